@@ -1,0 +1,258 @@
+"""CPU oracle for the KIVI flush, dequantize and dequantize-then-attend.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  The product
+(``kv_cache_quantization_quantize_amd``) never imports it, and it never imports
+the product: the two share no code.
+
+The arithmetic lives in ``kivi_oracle.c`` (plain single-threaded C, built with
+``-ffp-contract=off``); this module only marshals numpy arrays into it.
+
+Parity status of each function (what pins it is in ``tests/test_oracle_*.py``):
+  f16_to_f32 / f32_to_f16 ..... pinned (exhaustive against numpy's IEEE codec)
+  quantize_group .............. pinned (hand-worked groups, invariants, brute
+                                force against an exact-rational emulation)
+  quantize_keys / _values ..... pinned (layout fixtures, per-group reduction to
+                                quantize_group, axis-discriminating fixtures)
+  dequantize .................. pinned (hand-worked reconstructions, identity
+                                with the flush's own reconstruction)
+  decode_attend ............... pinned (closed forms: one token, equal scores,
+                                shift invariance; torch float64 SDPA when the
+                                store is empty)
+  flush_count ................. pinned (the flush/layer figures of the
+                                Generation 1 table)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+SRC_PATH = os.path.join(_HERE, "kivi_oracle.c")
+
+KEYS = 0
+VALUES = 1
+
+# -ffp-contract=off keeps a*b+c as two roundings; no -ffast-math anywhere.
+CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+          "-fPIC", "-shared", "-Wall", "-Wextra"]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile ``liboracle.so`` with gcc; always recompiles."""
+    cmd = ["gcc", *CFLAGS, "-o", LIB_PATH + ".tmp", SRC_PATH, "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(LIB_PATH + ".tmp", LIB_PATH)
+    return LIB_PATH
+
+
+_lib = None
+_u16p = ctypes.POINTER(ctypes.c_uint16)
+_u32p = ctypes.POINTER(ctypes.c_uint32)
+_u8p = ctypes.POINTER(ctypes.c_uint8)
+_f32p = ctypes.POINTER(ctypes.c_float)
+_f64p = ctypes.POINTER(ctypes.c_double)
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+
+
+def lib():
+    """Load the built oracle; build it only when nothing is built yet."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        L = ctypes.CDLL(LIB_PATH)
+        L.orc_f16_to_f32.argtypes = [ctypes.c_uint16]
+        L.orc_f16_to_f32.restype = ctypes.c_float
+        L.orc_f32_to_f16.argtypes = [ctypes.c_float]
+        L.orc_f32_to_f16.restype = ctypes.c_uint16
+        L.orc_f16_to_f32_array.argtypes = [_u16p, _f32p, _i64]
+        L.orc_f32_to_f16_array.argtypes = [_f32p, _u16p, _i64]
+        L.orc_quantize_group.argtypes = [_u16p, _int, _int, _f32p, _f32p, _u8p, _u16p]
+        L.orc_dequantize_one.argtypes = [ctypes.c_uint32, ctypes.c_float, ctypes.c_float]
+        L.orc_dequantize_one.restype = ctypes.c_uint16
+        flush_args = [_u16p, _i64, _i64, _i64, _i64, _int, _int,
+                      _u32p, _i64, _f32p, _f32p, _i64, _i64, _u16p, _i64]
+        L.orc_quantize_keys.argtypes = flush_args
+        L.orc_quantize_values.argtypes = flush_args
+        L.orc_quantize_keys.restype = _int
+        L.orc_quantize_values.restype = _int
+        L.orc_dequantize.argtypes = [_int, _u32p, _i64, _f32p, _f32p, _i64,
+                                     _i64, _i64, _int, _int, _i64, _i64, _u16p, _i64]
+        L.orc_dequantize.restype = _int
+        L.orc_decode_attend.argtypes = [
+            _u16p, _i64, _int, _int, _i64,
+            _u32p, _f32p, _f32p, _u32p, _f32p, _f32p,
+            _i64, _i64, _i64, _int, _int, _i64,
+            _u16p, _u16p, _i64, _i64, ctypes.c_double, _f64p]
+        L.orc_decode_attend.restype = _int
+        L.orc_flush_count.argtypes = [_i64, _i64, _i64]
+        L.orc_flush_count.restype = _i64
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray | None, ctype):
+    if a is None:
+        return ctypes.cast(None, ctypes.POINTER(ctype))
+    assert a.flags["C_CONTIGUOUS"] or a.ndim == 0
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def _as_u16(x) -> np.ndarray:
+    """fp16 bit patterns as a contiguous uint16 array (accepts float16)."""
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.float16:
+        x = x.view(np.uint16)
+    assert x.dtype == np.uint16, x.dtype
+    return x
+
+
+# ------------------------------------------------------------------ codec
+def f16_to_f32(h) -> np.ndarray:
+    h = _as_u16(h)
+    out = np.empty(h.shape, np.float32)
+    lib().orc_f16_to_f32_array(_ptr(h, ctypes.c_uint16), _ptr(out, ctypes.c_float), h.size)
+    return out
+
+
+def f32_to_f16(f) -> np.ndarray:
+    f = np.ascontiguousarray(f, dtype=np.float32)
+    out = np.empty(f.shape, np.uint16)
+    lib().orc_f32_to_f16_array(_ptr(f, ctypes.c_float), _ptr(out, ctypes.c_uint16), f.size)
+    return out
+
+
+# ------------------------------------------------------------------ groups
+def quantize_group(x, bits: int):
+    """-> (scale fp32, zero fp32, codes uint8[n], recon fp16 bits uint16[n])."""
+    x = _as_u16(x).reshape(-1)
+    n = x.size
+    sc = np.zeros(1, np.float32)
+    ze = np.zeros(1, np.float32)
+    q = np.zeros(n, np.uint8)
+    rec = np.zeros(n, np.uint16)
+    lib().orc_quantize_group(_ptr(x, ctypes.c_uint16), n, bits, _ptr(sc, ctypes.c_float),
+                             _ptr(ze, ctypes.c_float), _ptr(q, ctypes.c_uint8),
+                             _ptr(rec, ctypes.c_uint16))
+    return sc[0], ze[0], q, rec
+
+
+def dequantize_one(q: int, scale, zero) -> int:
+    return int(lib().orc_dequantize_one(int(q), float(np.float32(scale)), float(np.float32(zero))))
+
+
+# ------------------------------------------------------------------ store
+class Store:
+    """Host packed store in the documented layout (see kivi_oracle.h)."""
+
+    def __init__(self, kind: int, BH: int, cap: int, D: int = 128, bits: int = 4,
+                 G: int = 32, fill_codes: int = 0, fill_meta: float = 0.0):
+        assert kind in (KEYS, VALUES)
+        self.kind, self.BH, self.cap, self.D, self.bits, self.G = kind, BH, cap, D, bits, G
+        self.words = D * bits // 32
+        self.codes = np.full((BH, cap, self.words), fill_codes, np.uint32)
+        if kind == KEYS:
+            meta_shape = (BH, cap // G, D)
+        else:
+            meta_shape = (BH, cap, (D + G - 1) // G)
+        self.scale = np.full(meta_shape, fill_meta, np.float32)
+        self.zero = np.full(meta_shape, fill_meta, np.float32)
+
+    @property
+    def codes_bh_stride(self) -> int:
+        return self.codes.shape[1] * self.codes.shape[2]
+
+    @property
+    def meta_bh_stride(self) -> int:
+        return self.scale.shape[1] * self.scale.shape[2]
+
+
+def _flush(fn, x, store: Store, dst_token: int, want_recon: bool):
+    x = _as_u16(x)
+    BH, S, D = x.shape
+    assert BH == store.BH and D == store.D
+    recon = np.zeros((BH, S, D), np.uint16) if want_recon else None
+    rc = fn(_ptr(x, ctypes.c_uint16), BH, S, D, S * D, store.bits, store.G,
+            _ptr(store.codes, ctypes.c_uint32), store.codes_bh_stride,
+            _ptr(store.scale, ctypes.c_float), _ptr(store.zero, ctypes.c_float),
+            store.meta_bh_stride, dst_token,
+            _ptr(recon, ctypes.c_uint16), S * D)
+    if rc != 0:
+        raise ValueError("oracle rejected the flush arguments")
+    return recon
+
+
+def quantize_keys(x, store: Store, dst_token: int = 0, want_recon: bool = True):
+    """Per-channel key flush of x[BH][S][D] into ``store`` at ``dst_token``."""
+    assert store.kind == KEYS
+    return _flush(lib().orc_quantize_keys, x, store, dst_token, want_recon)
+
+
+def quantize_values(x, store: Store, dst_token: int = 0, want_recon: bool = True):
+    """Per-token value flush of x[BH][S][D] into ``store`` at ``dst_token``."""
+    assert store.kind == VALUES
+    return _flush(lib().orc_quantize_values, x, store, dst_token, want_recon)
+
+
+def dequantize(store: Store, t0: int, n: int) -> np.ndarray:
+    out = np.zeros((store.BH, n, store.D), np.uint16)
+    rc = lib().orc_dequantize(store.kind, _ptr(store.codes, ctypes.c_uint32),
+                              store.codes_bh_stride, _ptr(store.scale, ctypes.c_float),
+                              _ptr(store.zero, ctypes.c_float), store.meta_bh_stride,
+                              store.BH, store.D, store.bits, store.G, t0, n,
+                              _ptr(out, ctypes.c_uint16), n * store.D)
+    if rc != 0:
+        raise ValueError("oracle rejected the dequantize arguments")
+    return out
+
+
+def decode_attend(q, B: int, Hq: int, Hkv: int, kstore: Store | None, vstore: Store | None,
+                  n_quant: int, k_res, v_res, n_res: int,
+                  softmax_scale: float | None = None) -> np.ndarray:
+    """float64 [B][Hq][D] = softmax(q K^T * scale) V over store + residual.
+
+    ``k_res``/``v_res`` are fp16 [B*Hkv][R][D] with n_res <= R used rows."""
+    q = _as_u16(q).reshape(B, Hq, -1)
+    D = q.shape[2]
+    if softmax_scale is None:
+        softmax_scale = 1.0 / np.sqrt(D)
+    out = np.zeros((B, Hq, D), np.float64)
+    if n_quant > 0:
+        ks, vs = kstore, vstore
+        assert ks.codes_bh_stride == vs.codes_bh_stride and ks.bits == vs.bits
+        args = (_ptr(ks.codes, ctypes.c_uint32), _ptr(ks.scale, ctypes.c_float),
+                _ptr(ks.zero, ctypes.c_float), _ptr(vs.codes, ctypes.c_uint32),
+                _ptr(vs.scale, ctypes.c_float), _ptr(vs.zero, ctypes.c_float),
+                ks.codes_bh_stride, ks.meta_bh_stride, vs.meta_bh_stride, ks.bits, ks.G)
+    else:
+        z32, zf = np.zeros(1, np.uint32), np.zeros(1, np.float32)
+        args = (_ptr(z32, ctypes.c_uint32), _ptr(zf, ctypes.c_float), _ptr(zf, ctypes.c_float),
+                _ptr(z32, ctypes.c_uint32), _ptr(zf, ctypes.c_float), _ptr(zf, ctypes.c_float),
+                0, 0, 0, 4, 32)
+    if n_res > 0:
+        k_res = _as_u16(k_res)
+        v_res = _as_u16(v_res)
+        res_stride = k_res.shape[1] * k_res.shape[2]
+        assert v_res.shape == k_res.shape
+    else:
+        k_res = v_res = np.zeros(1, np.uint16)
+        res_stride = 0
+    rc = lib().orc_decode_attend(_ptr(q, ctypes.c_uint16), B, Hq, Hkv, D, *args, n_quant,
+                                 _ptr(k_res, ctypes.c_uint16), _ptr(v_res, ctypes.c_uint16),
+                                 res_stride, n_res, float(softmax_scale),
+                                 _ptr(out, ctypes.c_double))
+    if rc != 0:
+        raise ValueError("oracle rejected the attend arguments")
+    return out
+
+
+def flush_count(S: int, R: int, G: int) -> int:
+    return int(lib().orc_flush_count(S, R, G))
