@@ -1,0 +1,176 @@
+/*
+ * kivi.h -- C ABI of libkivi, the MI355X (gfx950) KIVI KV-cache
+ * quantization hot path.
+ *
+ * Sources, cited by page title and section:
+ *   [Metal post]  blog post "A 5.65x Metal Kernel That Made My LLM Exactly
+ *                 0% Faster" (VeloxQuant-MLX)
+ *   [Benchmarks]  VeloxQuant-MLX "Benchmarks" page
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every data pointer is a DEVICE pointer owned by the caller.  The
+ *    library never allocates, frees, copies between host and device or
+ *    synchronizes; each call validates its arguments on the host, enqueues
+ *    its kernels on `stream` and returns.
+ *  - Validation happens before anything is enqueued: a negative return
+ *    means nothing was launched.  A zero-sized call (S == 0, n_tokens == 0,
+ *    B == 0) succeeds without launching.
+ *  - fp16 tensors are passed as `uint16_t*` holding IEEE binary16 bits.
+ *  - Strides are in elements of the array they index.  Token rows inside a
+ *    bh slab are contiguous (row stride = head_dim).
+ *  - Inputs must not alias outputs.  Calls on different streams may run
+ *    concurrently if their outputs do not overlap.
+ *  - Faults inside a kernel surface at the caller's next synchronization.
+ *  - Supported parameters: bits in {2, 4}, group_size 32, head_dim 128.
+ *    Anything else returns KIVI_ERR_UNSUPPORTED (there is no fallback
+ *    path).
+ *
+ * Packed store layout (the pages fix none; [Metal post] "So why does the
+ * kernel ship?" asks for packed storage of the codes):
+ *   codes  uint32 [BH][cap][head_dim*bits/32]  token-major; the code of
+ *          channel d of token t sits in word (t, d / (32/bits)) at bit
+ *          offset bits * (d % (32/bits)), least significant first.
+ *   keys   scale, zero fp32 [BH][cap/G][head_dim]   one pair per
+ *          (token group, channel): per-channel quantization.
+ *   values scale, zero fp32 [BH][cap][head_dim/G]   one pair per
+ *          (token, channel group): per-token quantization.
+ *   zero is the group minimum (a float offset, not an integer zero point).
+ */
+#ifndef KIVI_H
+#define KIVI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* HIP's own stream handle type (identical typedef to hip_runtime_api.h). */
+typedef struct ihipStream_t* hipStream_t;
+
+enum {
+    KIVI_OK = 0,
+    KIVI_ERR_NULL = -1,        /* a required pointer is NULL                  */
+    KIVI_ERR_SHAPE = -2,       /* negative size, window outside the store,
+                                  misaligned key offset, Hq % Hkv != 0, ...   */
+    KIVI_ERR_UNSUPPORTED = -3, /* bits, group_size, head_dim or kind unsupported */
+    KIVI_ERR_ALIGN = -4,       /* pointer not 16-byte aligned or stride not a
+                                  multiple of 16 bytes                         */
+    KIVI_ERR_WORKSPACE = -5,   /* attend workspace NULL or too small          */
+    KIVI_ERR_HIP = -6          /* a HIP launch failed; see kivi_last_hip_error */
+};
+
+enum { KIVI_KEYS = 0, KIVI_VALUES = 1 };
+
+/* A packed store (see the layout above).  The struct itself lives in host
+ * memory and is only read during the call; the arrays are device memory. */
+typedef struct kivi_store {
+    uint32_t* codes;           /* [BH][cap][head_dim*bits/32]                 */
+    float*    scale;           /* keys [BH][cap/G][D]; values [BH][cap][D/G]  */
+    float*    zero;            /* same shape as scale                         */
+    int64_t   codes_bh_stride; /* uint32 words between bh slabs (>= cap*row) */
+    int64_t   meta_bh_stride;  /* floats between bh slabs                     */
+    int64_t   cap;             /* token capacity of each slab                 */
+    int32_t   bits;            /* 2 or 4                                      */
+    int32_t   group_size;      /* 32                                          */
+    int32_t   head_dim;        /* 128                                         */
+    int32_t   kind;            /* KIVI_KEYS or KIVI_VALUES                    */
+} kivi_store;
+
+/*
+ * Per-channel key flush.  [Metal post] "What we're actually optimizing":
+ * keys get one scale per channel computed across a group of tokens, with
+ * zero = min, scale = (max - min) / (2^bits - 1), q = round((x - zero) /
+ * scale) clipped to [0, 2^bits - 1]; "Kernel A": the group of channel d is
+ * tokens [g*G, min(g*G + G, S)) of that channel; "Three ways to be off by
+ * one bit": ties round to even, q*scale and +zero are rounded separately,
+ * a ragged last group behaves as if padded with its last real token.
+ * Arithmetic is IEEE binary32 (IEEE division, no contraction), bit-exact
+ * with the documented reading.  A group with max == min gets scale 0 and
+ * code 0.
+ *
+ *   x              fp16 [BH][S][head_dim], slab bh at x + bh*x_bh_stride
+ *   dst            key store (kind KIVI_KEYS); tokens [dst_token,
+ *                  dst_token + S) of every slab are written, nothing else
+ *   dst_token      multiple of group_size; dst_token + S <= dst->cap
+ *   recon          optional (NULL for none): fp16 [BH][S][head_dim]
+ *                  reconstruction q*scale + zero of every input element
+ *   recon_bh_stride  elements between recon slabs
+ * Returns KIVI_OK or a negative KIVI_ERR_* code.
+ */
+int kivi_quantize_keys(const uint16_t* x, int64_t BH, int64_t S, int64_t x_bh_stride,
+                       const kivi_store* dst, int64_t dst_token,
+                       uint16_t* recon, int64_t recon_bh_stride, hipStream_t stream);
+
+/*
+ * Per-token value flush.  [Metal post] "What we're actually optimizing":
+ * values get one scale per token computed across a group of channels;
+ * "Kernel B": the group of token s is channels [j*G, j*G + G) of that
+ * token.  Same element rule, arguments and write window as
+ * kivi_quantize_keys, except that dst_token may be any offset and dst has
+ * kind KIVI_VALUES.
+ */
+int kivi_quantize_values(const uint16_t* x, int64_t BH, int64_t S, int64_t x_bh_stride,
+                         const kivi_store* dst, int64_t dst_token,
+                         uint16_t* recon, int64_t recon_bh_stride, hipStream_t stream);
+
+/*
+ * Dequantize tokens [token_begin, token_begin + n_tokens) of every slab of
+ * a key or value store to fp16: out = fp16_rne(fl(fl(q*scale) + zero))
+ * ([Metal post] "Three ways to be off by one bit", item 1: no fused
+ * multiply-add; "So why does the kernel ship?": KIVI as shipped expands the
+ * store back to fp16).  Bit-exact with the reconstruction the flush writes.
+ *
+ *   src        store; src->kind selects the key or value metadata layout
+ *   BH         number of slabs to read (<= what the store holds)
+ *   out        fp16 [BH][n_tokens][head_dim], slab bh at out + bh*out_bh_stride
+ */
+int kivi_dequantize(const kivi_store* src, int64_t BH, int64_t token_begin, int64_t n_tokens,
+                    uint16_t* out, int64_t out_bh_stride, hipStream_t stream);
+
+/*
+ * Fused dequantize + attend for one new query token per sequence
+ * ([Benchmarks] "KV-Cache Kernel Roofline: What Actually Limits Decode":
+ * a decode+attend kernel that reads the packed state directly, measured
+ * against dequantize + SDPA on the same compressed state; [Metal post]
+ * "What we're actually optimizing": the newest residual_length tokens stay
+ * fp16).  For every sequence b and query head h (kv head h / (Hq/Hkv)):
+ *   out[b][h] = softmax(q[b][h] . K^T * softmax_scale) V
+ * over K, V = [store tokens 0..n_quant-1 dequantized ; residual tokens
+ * 0..n_res-1], accumulated in fp32 (the result is within 2e-3 max-abs of
+ * the float64 definition, not bit-exact).
+ *
+ *   q          fp16 [B][Hq][head_dim]
+ *   k, v       key and value stores whose slab b*Hkv + kv holds sequence b,
+ *              kv head kv (same bits, same cap >= n_quant)
+ *   k_res, v_res  fp16 residual windows [B*Hkv][..][head_dim], slab stride
+ *              res_bh_stride; may be NULL when n_res == 0
+ *   out        fp32 [B][Hq][head_dim]
+ *   workspace  device scratch of at least
+ *              kivi_decode_attend_workspace_bytes(B, Hq, Hkv, n_quant, n_res)
+ *              bytes, 256-byte aligned; its contents on entry do not matter
+ * n_quant + n_res must be > 0; Hq/Hkv must be in 1..8.
+ */
+int kivi_decode_attend(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
+                       const kivi_store* k, const kivi_store* v, int64_t n_quant,
+                       const uint16_t* k_res, const uint16_t* v_res, int64_t res_bh_stride,
+                       int64_t n_res, float softmax_scale, float* out,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes kivi_decode_attend needs for this shape (head_dim 128). */
+size_t kivi_decode_attend_workspace_bytes(int64_t B, int32_t Hq, int32_t Hkv,
+                                          int64_t n_quant, int64_t n_res);
+
+/* Static description of a status code. */
+const char* kivi_status_string(int status);
+
+/* hipError_t of the last KIVI_ERR_HIP returned on this host thread. */
+int kivi_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KIVI_H */

@@ -1,0 +1,184 @@
+// abi.cpp -- the C ABI of libkivi (declared in include/kivi.h and
+// include/kivi_calib.h): argument validation on the host, then kernel launch
+// on the caller's stream.  Validation never calls into HIP, so an error
+// return means nothing was enqueued.
+#include "kivi.h"
+#include "kivi_calib.h"
+#include "kivi_launch.h"
+
+#include <limits>
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int64_t kD = 128;
+constexpr int64_t kG = 32;
+constexpr int64_t kMaxBlocks = (int64_t{1} << 31) - 1;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int finish(hipError_t e) {
+    if (e == hipSuccess) return KIVI_OK;
+    g_last_hip_error = static_cast<int>(e);
+    return KIVI_ERR_HIP;
+}
+
+int64_t words_per_token(int bits) { return kD * bits / 32; }
+
+int64_t meta_rows(const kivi_store* st) {
+    return st->kind == KIVI_KEYS ? (st->cap + kG - 1) / kG * kD : st->cap * (kD / kG);
+}
+
+// Checks a store and that tokens [t0, t0 + n) of slabs [0, BH) lie inside it.
+int check_store(const kivi_store* st, int kind, int64_t BH, int64_t t0, int64_t n) {
+    if (!st) return KIVI_ERR_NULL;
+    if (st->kind != KIVI_KEYS && st->kind != KIVI_VALUES) return KIVI_ERR_UNSUPPORTED;
+    if (kind >= 0 && st->kind != kind) return KIVI_ERR_SHAPE;
+    if (st->bits != 2 && st->bits != 4) return KIVI_ERR_UNSUPPORTED;
+    if (st->group_size != kG || st->head_dim != kD) return KIVI_ERR_UNSUPPORTED;
+    if (!st->codes || !st->scale || !st->zero) return KIVI_ERR_NULL;
+    if (!aligned16(st->codes) || !aligned16(st->scale) || !aligned16(st->zero)) return KIVI_ERR_ALIGN;
+    if (st->codes_bh_stride % 4 != 0 || st->meta_bh_stride % 4 != 0) return KIVI_ERR_ALIGN;
+    if (st->cap < 0 || t0 < 0 || n < 0 || t0 > st->cap - n) return KIVI_ERR_SHAPE;
+    if (BH > 1) {
+        if (st->codes_bh_stride < st->cap * words_per_token(st->bits)) return KIVI_ERR_SHAPE;
+        if (st->meta_bh_stride < meta_rows(st)) return KIVI_ERR_SHAPE;
+    }
+    return KIVI_OK;
+}
+
+// fp16 [BH][S][128] tensor with slab stride `stride` elements.
+int check_f16_tensor(const void* p, int64_t BH, int64_t S, int64_t stride) {
+    if (!p) return KIVI_ERR_NULL;
+    if (!aligned16(p) || stride % 8 != 0) return KIVI_ERR_ALIGN;
+    if (BH > 1 && stride < S * kD) return KIVI_ERR_SHAPE;
+    return KIVI_OK;
+}
+
+int flush(bool keys, const uint16_t* x, int64_t BH, int64_t S, int64_t x_bh_stride,
+          const kivi_store* dst, int64_t dst_token, uint16_t* recon, int64_t recon_bh_stride,
+          hipStream_t stream) {
+    if (BH < 0 || S < 0) return KIVI_ERR_SHAPE;
+    int rc = check_store(dst, keys ? KIVI_KEYS : KIVI_VALUES, BH, dst_token, S);
+    if (rc != KIVI_OK) return rc;
+    if (keys && dst_token % kG != 0) return KIVI_ERR_SHAPE;
+    if (BH == 0 || S == 0) return KIVI_OK;
+    if ((rc = check_f16_tensor(x, BH, S, x_bh_stride)) != KIVI_OK) return rc;
+    if (recon && (rc = check_f16_tensor(recon, BH, S, recon_bh_stride)) != KIVI_OK) return rc;
+    const int64_t tiles = BH * ((S + 31) / 32);
+    if ((tiles + 3) / 4 > kMaxBlocks) return KIVI_ERR_SHAPE;
+
+    kivi::FlushArgs a;
+    a.x = x; a.BH = BH; a.S = S; a.x_bh_stride = x_bh_stride;
+    a.codes = dst->codes; a.codes_bh_stride = dst->codes_bh_stride;
+    a.scale = dst->scale; a.zero = dst->zero; a.meta_bh_stride = dst->meta_bh_stride;
+    a.dst_token = dst_token; a.recon = recon; a.recon_bh_stride = recon_bh_stride;
+    a.bits = dst->bits;
+    return finish(keys ? kivi::launch_key_flush(a, stream) : kivi::launch_value_flush(a, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int kivi_quantize_keys(const uint16_t* x, int64_t BH, int64_t S, int64_t x_bh_stride,
+                       const kivi_store* dst, int64_t dst_token,
+                       uint16_t* recon, int64_t recon_bh_stride, hipStream_t stream) {
+    return flush(true, x, BH, S, x_bh_stride, dst, dst_token, recon, recon_bh_stride, stream);
+}
+
+int kivi_quantize_values(const uint16_t* x, int64_t BH, int64_t S, int64_t x_bh_stride,
+                         const kivi_store* dst, int64_t dst_token,
+                         uint16_t* recon, int64_t recon_bh_stride, hipStream_t stream) {
+    return flush(false, x, BH, S, x_bh_stride, dst, dst_token, recon, recon_bh_stride, stream);
+}
+
+int kivi_dequantize(const kivi_store* src, int64_t BH, int64_t token_begin, int64_t n_tokens,
+                    uint16_t* out, int64_t out_bh_stride, hipStream_t stream) {
+    if (BH < 0 || n_tokens < 0) return KIVI_ERR_SHAPE;
+    int rc = check_store(src, -1, BH, token_begin, n_tokens);
+    if (rc != KIVI_OK) return rc;
+    if (BH == 0 || n_tokens == 0) return KIVI_OK;
+    if ((rc = check_f16_tensor(out, BH, n_tokens, out_bh_stride)) != KIVI_OK) return rc;
+    const int64_t tiles = BH * ((n_tokens + 31) / 32);
+    if ((tiles + 3) / 4 > kMaxBlocks) return KIVI_ERR_SHAPE;
+    kivi::DequantArgs a;
+    a.codes = src->codes; a.codes_bh_stride = src->codes_bh_stride;
+    a.scale = src->scale; a.zero = src->zero; a.meta_bh_stride = src->meta_bh_stride;
+    a.BH = BH; a.t0 = token_begin; a.n = n_tokens; a.out = out; a.out_bh_stride = out_bh_stride;
+    a.bits = src->bits; a.kind = src->kind;
+    return finish(kivi::launch_dequantize(a, stream));
+}
+
+size_t kivi_decode_attend_workspace_bytes(int64_t B, int32_t Hq, int32_t Hkv,
+                                          int64_t n_quant, int64_t n_res) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || n_quant < 0 || n_res < 0 || n_quant + n_res == 0) return 0;
+    return kivi::plan_attend(B, Hq, Hkv, n_quant, n_res).workspace_bytes;
+}
+
+int kivi_decode_attend(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
+                       const kivi_store* k, const kivi_store* v, int64_t n_quant,
+                       const uint16_t* k_res, const uint16_t* v_res, int64_t res_bh_stride,
+                       int64_t n_res, float softmax_scale, float* out,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || n_quant < 0 || n_res < 0) return KIVI_ERR_SHAPE;
+    if (Hq % Hkv != 0) return KIVI_ERR_SHAPE;
+    const int group = Hq / Hkv;
+    if (group != 1 && group != 2 && group != 4 && group != 8) return KIVI_ERR_UNSUPPORTED;
+    if (n_quant + n_res == 0) return KIVI_ERR_SHAPE;
+    const int64_t slabs = B * Hkv;
+    int rc = check_store(k, KIVI_KEYS, slabs, 0, n_quant);
+    if (rc != KIVI_OK) return rc;
+    if ((rc = check_store(v, KIVI_VALUES, slabs, 0, n_quant)) != KIVI_OK) return rc;
+    if (k->bits != v->bits) return KIVI_ERR_SHAPE;
+    if (B == 0) return KIVI_OK;
+    if (!q || !out) return KIVI_ERR_NULL;
+    if (!aligned16(q) || !aligned16(out)) return KIVI_ERR_ALIGN;
+    if (n_res > 0) {
+        if ((rc = check_f16_tensor(k_res, slabs, n_res, res_bh_stride)) != KIVI_OK) return rc;
+        if ((rc = check_f16_tensor(v_res, slabs, n_res, res_bh_stride)) != KIVI_OK) return rc;
+    }
+    const kivi::AttendPlan plan = kivi::plan_attend(B, Hq, Hkv, n_quant, n_res);
+    if (!workspace || workspace_bytes < plan.workspace_bytes) return KIVI_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KIVI_ERR_ALIGN;
+    if (plan.n_split > kMaxBlocks || slabs > 65535 || B * Hq > kMaxBlocks) return KIVI_ERR_SHAPE;
+
+    kivi::AttendArgs a;
+    a.q = q; a.B = B; a.Hq = Hq; a.Hkv = Hkv;
+    a.k_codes = k->codes; a.k_scale = k->scale; a.k_zero = k->zero;
+    a.v_codes = v->codes; a.v_scale = v->scale; a.v_zero = v->zero;
+    a.k_codes_bh_stride = k->codes_bh_stride; a.v_codes_bh_stride = v->codes_bh_stride;
+    a.k_meta_bh_stride = k->meta_bh_stride; a.v_meta_bh_stride = v->meta_bh_stride;
+    a.n_quant = n_quant;
+    a.k_res = n_res > 0 ? k_res : q;     // never read when n_res == 0
+    a.v_res = n_res > 0 ? v_res : q;
+    a.res_bh_stride = n_res > 0 ? res_bh_stride : 0;
+    a.n_res = n_res; a.softmax_scale = softmax_scale; a.out = out;
+    a.workspace = workspace; a.bits = k->bits;
+    return finish(kivi::launch_decode_attend(a, plan, stream));
+}
+
+const char* kivi_status_string(int status) {
+    switch (status) {
+        case KIVI_OK: return "ok";
+        case KIVI_ERR_NULL: return "a required pointer is NULL";
+        case KIVI_ERR_SHAPE: return "invalid shape, offset or window";
+        case KIVI_ERR_UNSUPPORTED: return "unsupported bits, group size, head dim, kind or head ratio";
+        case KIVI_ERR_ALIGN: return "pointer or stride not 16-byte aligned";
+        case KIVI_ERR_WORKSPACE: return "attend workspace missing or too small";
+        case KIVI_ERR_HIP: return "HIP launch failed (see kivi_last_hip_error)";
+        default: return "unknown status";
+    }
+}
+
+int kivi_last_hip_error(void) { return g_last_hip_error; }
+
+int kivi_calib_copy(const void* src, void* dst, size_t n_bytes, hipStream_t stream) {
+    if (!src || !dst) return KIVI_ERR_NULL;
+    if (!aligned16(src) || !aligned16(dst) || n_bytes % 16 != 0) return KIVI_ERR_ALIGN;
+    if (n_bytes == 0) return KIVI_OK;
+    return finish(kivi::launch_calib_copy(src, dst, n_bytes, stream));
+}
+
+}  // extern "C"

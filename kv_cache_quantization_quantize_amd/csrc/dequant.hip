@@ -1,0 +1,88 @@
+// dequant.hip -- expand a packed key or value store back to fp16 for a token
+// range: out = fp16_rne(fl(fl(q * scale) + zero)), the same two roundings as
+// the flush's reconstruction (blog post "A 5.65x Metal Kernel That Made My
+// LLM Exactly 0% Faster", "Three ways to be off by one bit", item 1; "So why
+// does the kernel ship?": the shipped cache expands to fp16 before
+// attention).
+//
+// One wave per 32-token x 128-channel tile with the lane mapping of
+// kivi_device.h: per token a lane reads one code word (4-bit) or half a word
+// (2-bit) and writes 16 contiguous bytes of fp16.
+#include "kivi_device.h"
+#include "kivi_launch.h"
+
+namespace kivi {
+
+template <int BITS, bool KEYS>
+__global__ __launch_bounds__(kBlock) void dequant_kernel(
+    const uint32_t* __restrict__ codes, int64_t codes_bh_stride,
+    const float* __restrict__ scale, const float* __restrict__ zero, int64_t meta_bh_stride,
+    int64_t t0, int64_t n, uint16_t* __restrict__ out, int64_t out_bh_stride,
+    int64_t tiles_per_bh, int64_t n_tiles)
+{
+    constexpr int kWords = kHeadDim * BITS / 32;
+    constexpr uint32_t kMask = (1u << BITS) - 1u;
+    constexpr int kMetaPerTok = kHeadDim / kGroup;
+    const int lane = threadIdx.x & 63;
+    const int64_t tile = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
+    if (tile >= n_tiles) return;
+
+    const int64_t bh = tile / tiles_per_bh;
+    const int64_t i0 = (tile - bh * tiles_per_bh) * 32;
+    const int c = lane & 15;
+    const int r = lane >> 4;
+    const uint32_t* cb = codes + bh * codes_bh_stride;
+    const float* scb = scale + bh * meta_bh_stride;
+    const float* zeb = zero + bh * meta_bh_stride;
+
+#pragma unroll
+    for (int i = 0; i < kTokPerLane; ++i) {
+        const int64_t k = i0 + r + kRowsPerWave * i;   // output row
+        if (k >= n) continue;
+        const int64_t t = t0 + k;                      // store token
+        uint32_t w;
+        if constexpr (BITS == 4) w = cb[t * kWords + c];
+        else w = cb[t * kWords + (c >> 1)] >> (16 * (c & 1));
+        float sc[8], ze[8];
+        if constexpr (KEYS) {
+            const float* sp = scb + (t / kGroup) * kHeadDim + c * 8;
+            const float* zp = zeb + (t / kGroup) * kHeadDim + c * 8;
+            const float4 s0 = *reinterpret_cast<const float4*>(sp);
+            const float4 s1 = *reinterpret_cast<const float4*>(sp + 4);
+            const float4 z0 = *reinterpret_cast<const float4*>(zp);
+            const float4 z1 = *reinterpret_cast<const float4*>(zp + 4);
+            sc[0] = s0.x; sc[1] = s0.y; sc[2] = s0.z; sc[3] = s0.w;
+            sc[4] = s1.x; sc[5] = s1.y; sc[6] = s1.z; sc[7] = s1.w;
+            ze[0] = z0.x; ze[1] = z0.y; ze[2] = z0.z; ze[3] = z0.w;
+            ze[4] = z1.x; ze[5] = z1.y; ze[6] = z1.z; ze[7] = z1.w;
+        } else {
+            const float s = scb[t * kMetaPerTok + (c >> 2)];
+            const float z = zeb[t * kMetaPerTok + (c >> 2)];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) { sc[j] = s; ze[j] = z; }
+        }
+        uint32_t h[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) h[j] = recon_f16((w >> (BITS * j)) & kMask, sc[j], ze[j]);
+        *reinterpret_cast<uint4*>(out + bh * out_bh_stride + k * kHeadDim + c * 8) = pack8(h);
+    }
+}
+
+template <int BITS, bool KEYS>
+static hipError_t launch_t(const DequantArgs& a, hipStream_t stream) {
+    const int64_t tiles_per_bh = (a.n + 31) / 32;
+    const int64_t n_tiles = a.BH * tiles_per_bh;
+    const int64_t blocks = (n_tiles + kWavesPerBlock - 1) / kWavesPerBlock;
+    hipLaunchKernelGGL((dequant_kernel<BITS, KEYS>), dim3(static_cast<uint32_t>(blocks)),
+                       dim3(kBlock), 0, stream, a.codes, a.codes_bh_stride, a.scale, a.zero,
+                       a.meta_bh_stride, a.t0, a.n, a.out, a.out_bh_stride, tiles_per_bh, n_tiles);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequantize(const DequantArgs& a, hipStream_t stream) {
+    const bool keys = a.kind == 0;
+    if (a.bits == 4) return keys ? launch_t<4, true>(a, stream) : launch_t<4, false>(a, stream);
+    return keys ? launch_t<2, true>(a, stream) : launch_t<2, false>(a, stream);
+}
+
+}  // namespace kivi

@@ -1,0 +1,240 @@
+// flush.hip -- the KIVI flush kernels for gfx950: per-channel keys and
+// per-token values, quantized to 2 or 4 bits, codes bit-packed into uint32,
+// one fp32 scale and zero per group, optional fused fp16 reconstruction.
+//
+// Sources, cited by page title and section:
+//   [Metal post] blog post "A 5.65x Metal Kernel That Made My LLM Exactly 0%
+//                Faster": "What we're actually optimizing" (the quantizer),
+//                "The layout problem that shapes everything", "Kernel A",
+//                "Kernel B", "Three ways to be off by one bit".
+//
+// Both kernels give one wave one tile of 32 tokens x 128 channels with the
+// lane mapping of kivi_device.h.  For keys the tile is exactly one token
+// group of every channel, so a lane's 8 tokens x 8 channels cover a quarter
+// of each of its 8 channel groups; the four quarters meet with two cross-row
+// exchanges and no LDS.  For values each token row's 128 channels are four
+// groups of 32, i.e. four lanes of 8; two quad exchanges finish them.  The
+// Metal kernels used a thread per strided key group and a 32-lane SIMD-group
+// per value group; on wave64 both layouts read the same coalesced tile.
+#include "kivi_device.h"
+#include "kivi_launch.h"
+
+namespace kivi {
+
+// ---------------------------------------------------------------------------
+// Keys: group = (bh, token group g, channel d) over tokens [32g, min(32g+32, S))
+// ---------------------------------------------------------------------------
+template <int BITS, bool RECON>
+__global__ __launch_bounds__(kBlock) void key_flush_kernel(
+    const uint16_t* __restrict__ x, int64_t S, int64_t x_bh_stride,
+    uint32_t* __restrict__ codes, int64_t codes_bh_stride,
+    float* __restrict__ scale, float* __restrict__ zero, int64_t meta_bh_stride,
+    int64_t dst_token, uint16_t* __restrict__ recon, int64_t recon_bh_stride,
+    int64_t n_groups, int64_t n_tiles)
+{
+    constexpr int kWords = kHeadDim * BITS / 32;   // code words per token row
+    const int lane = threadIdx.x & 63;
+    const int64_t tile = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
+    if (tile >= n_tiles) return;                   // uniform across the wave
+
+    const int64_t bh = tile / n_groups;
+    const int64_t g = tile - bh * n_groups;
+    const int c = lane & 15;                       // channels 8c .. 8c+7
+    const int r = lane >> 4;                       // token rows r, r+4, ...
+    const int64_t s0 = g * kGroup;
+
+    // Load 8 token rows x 8 channels.  Rows past the end of a ragged last
+    // group re-read the last real token, which is the edge padding of
+    // "Three ways to be off by one bit", item 3, and cannot move min or max.
+    const uint16_t* xb = x + bh * x_bh_stride + c * 8;
+    float f[kTokPerLane][8];
+#pragma unroll
+    for (int i = 0; i < kTokPerLane; ++i) {
+        int64_t s = s0 + r + kRowsPerWave * i;
+        s = s < S ? s : S - 1;
+        const uint4 v = *reinterpret_cast<const uint4*>(xb + s * kHeadDim);
+        unpack8(v, f[i]);
+    }
+
+    // Per-channel min/max over the lane's 8 rows, then over the 4 row lanes.
+    float mn[8], mx[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        mn[j] = f[0][j];
+        mx[j] = f[0][j];
+#pragma unroll
+        for (int i = 1; i < kTokPerLane; ++i) {
+            mn[j] = fminf(mn[j], f[i][j]);
+            mx[j] = fmaxf(mx[j], f[i][j]);
+        }
+        mn[j] = fminf(mn[j], __shfl_xor(mn[j], 16));
+        mx[j] = fmaxf(mx[j], __shfl_xor(mx[j], 16));
+        mn[j] = fminf(mn[j], __shfl_xor(mn[j], 32));
+        mx[j] = fmaxf(mx[j], __shfl_xor(mx[j], 32));
+    }
+
+    // zero = min, scale = (max - min) / (2^bits - 1), IEEE division.
+    constexpr float kLevels = static_cast<float>((1 << BITS) - 1);
+    float sc[8], ze[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        ze[j] = canon_zero(mn[j]);
+        const float range = canon_zero(mx[j]) - ze[j];
+        sc[j] = range / kLevels;
+    }
+
+    const int64_t meta_off = bh * meta_bh_stride + (dst_token / kGroup + g) * kHeadDim + c * 8;
+    if (r == 0) {
+        *reinterpret_cast<float4*>(scale + meta_off) = make_float4(sc[0], sc[1], sc[2], sc[3]);
+        *reinterpret_cast<float4*>(scale + meta_off + 4) = make_float4(sc[4], sc[5], sc[6], sc[7]);
+    } else if (r == 1) {
+        *reinterpret_cast<float4*>(zero + meta_off) = make_float4(ze[0], ze[1], ze[2], ze[3]);
+        *reinterpret_cast<float4*>(zero + meta_off + 4) = make_float4(ze[4], ze[5], ze[6], ze[7]);
+    }
+
+    uint32_t* cb = codes + bh * codes_bh_stride + dst_token * kWords;
+#pragma unroll
+    for (int i = 0; i < kTokPerLane; ++i) {
+        const int64_t s = s0 + r + kRowsPerWave * i;
+        uint32_t q[8];
+        uint32_t packed = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            q[j] = quant_code<BITS>(f[i][j], ze[j], sc[j]);
+            packed |= q[j] << (BITS * j);
+        }
+        if constexpr (BITS == 4) {
+            // the lane's 8 channels are exactly one word
+            if (s < S) cb[s * kWords + c] = packed;
+        } else {
+            // 16 channels per word: the even lane takes its odd neighbour's half
+            const uint32_t hi = __shfl_xor(packed, 1);
+            if (s < S && (c & 1) == 0) cb[s * kWords + (c >> 1)] = packed | (hi << 16);
+        }
+        if constexpr (RECON) {
+            uint32_t h[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) h[j] = recon_f16(q[j], sc[j], ze[j]);
+            if (s < S)
+                *reinterpret_cast<uint4*>(recon + bh * recon_bh_stride + s * kHeadDim + c * 8) = pack8(h);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Values: group = (bh, token s, channel group j) over channels [32j, 32j+32)
+// ---------------------------------------------------------------------------
+template <int BITS, bool RECON>
+__global__ __launch_bounds__(kBlock) void value_flush_kernel(
+    const uint16_t* __restrict__ x, int64_t S, int64_t x_bh_stride,
+    uint32_t* __restrict__ codes, int64_t codes_bh_stride,
+    float* __restrict__ scale, float* __restrict__ zero, int64_t meta_bh_stride,
+    int64_t dst_token, uint16_t* __restrict__ recon, int64_t recon_bh_stride,
+    int64_t tiles_per_bh, int64_t n_tiles)
+{
+    constexpr int kWords = kHeadDim * BITS / 32;
+    constexpr int kMetaPerTok = kHeadDim / kGroup;  // 4 groups per token
+    const int lane = threadIdx.x & 63;
+    const int64_t tile = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
+    if (tile >= n_tiles) return;                    // uniform across the wave
+
+    const int64_t bh = tile / tiles_per_bh;
+    const int64_t s0 = (tile - bh * tiles_per_bh) * 32;
+    const int c = lane & 15;
+    const int r = lane >> 4;
+    const int j = c >> 2;                           // channel group of this lane
+
+    const uint16_t* xb = x + bh * x_bh_stride + c * 8;
+    uint32_t* cb = codes + bh * codes_bh_stride + dst_token * kWords;
+    float* scb = scale + bh * meta_bh_stride + dst_token * kMetaPerTok;
+    float* zeb = zero + bh * meta_bh_stride + dst_token * kMetaPerTok;
+
+#pragma unroll
+    for (int i = 0; i < kTokPerLane; ++i) {
+        const int64_t s = s0 + r + kRowsPerWave * i;
+        const int64_t sl = s < S ? s : S - 1;       // keep every lane in the exchange
+        float f[8];
+        unpack8(*reinterpret_cast<const uint4*>(xb + sl * kHeadDim), f);
+        float mn = f[0], mx = f[0];
+#pragma unroll
+        for (int k = 1; k < 8; ++k) {
+            mn = fminf(mn, f[k]);
+            mx = fmaxf(mx, f[k]);
+        }
+        // the 4 lanes of one group are a DPP quad
+        mn = fminf(mn, __shfl_xor(mn, 1));
+        mx = fmaxf(mx, __shfl_xor(mx, 1));
+        mn = fminf(mn, __shfl_xor(mn, 2));
+        mx = fmaxf(mx, __shfl_xor(mx, 2));
+
+        constexpr float kLevels = static_cast<float>((1 << BITS) - 1);
+        const float ze = canon_zero(mn);
+        const float sc = (canon_zero(mx) - ze) / kLevels;
+
+        uint32_t q[8];
+        uint32_t packed = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            q[k] = quant_code<BITS>(f[k], ze, sc);
+            packed |= q[k] << (BITS * k);
+        }
+        if constexpr (BITS == 4) {
+            if (s < S) cb[s * kWords + c] = packed;
+        } else {
+            const uint32_t hi = __shfl_xor(packed, 1);
+            if (s < S && (c & 1) == 0) cb[s * kWords + (c >> 1)] = packed | (hi << 16);
+        }
+        if (s < S) {
+            if ((c & 3) == 0) scb[s * kMetaPerTok + j] = sc;
+            else if ((c & 3) == 1) zeb[s * kMetaPerTok + j] = ze;
+        }
+        if constexpr (RECON) {
+            uint32_t h[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) h[k] = recon_f16(q[k], sc, ze);
+            if (s < S)
+                *reinterpret_cast<uint4*>(recon + bh * recon_bh_stride + s * kHeadDim + c * 8) = pack8(h);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host launchers
+// ---------------------------------------------------------------------------
+template <int BITS, bool RECON>
+static hipError_t launch_keys_t(const FlushArgs& a, hipStream_t stream) {
+    const int64_t n_groups = (a.S + kGroup - 1) / kGroup;
+    const int64_t n_tiles = a.BH * n_groups;
+    const int64_t blocks = (n_tiles + kWavesPerBlock - 1) / kWavesPerBlock;
+    hipLaunchKernelGGL((key_flush_kernel<BITS, RECON>), dim3(static_cast<uint32_t>(blocks)),
+                       dim3(kBlock), 0, stream, a.x, a.S, a.x_bh_stride, a.codes,
+                       a.codes_bh_stride, a.scale, a.zero, a.meta_bh_stride, a.dst_token,
+                       a.recon, a.recon_bh_stride, n_groups, n_tiles);
+    return hipGetLastError();
+}
+
+template <int BITS, bool RECON>
+static hipError_t launch_values_t(const FlushArgs& a, hipStream_t stream) {
+    const int64_t tiles_per_bh = (a.S + 31) / 32;
+    const int64_t n_tiles = a.BH * tiles_per_bh;
+    const int64_t blocks = (n_tiles + kWavesPerBlock - 1) / kWavesPerBlock;
+    hipLaunchKernelGGL((value_flush_kernel<BITS, RECON>), dim3(static_cast<uint32_t>(blocks)),
+                       dim3(kBlock), 0, stream, a.x, a.S, a.x_bh_stride, a.codes,
+                       a.codes_bh_stride, a.scale, a.zero, a.meta_bh_stride, a.dst_token,
+                       a.recon, a.recon_bh_stride, tiles_per_bh, n_tiles);
+    return hipGetLastError();
+}
+
+hipError_t launch_key_flush(const FlushArgs& a, hipStream_t stream) {
+    const bool rec = a.recon != nullptr;
+    if (a.bits == 4) return rec ? launch_keys_t<4, true>(a, stream) : launch_keys_t<4, false>(a, stream);
+    return rec ? launch_keys_t<2, true>(a, stream) : launch_keys_t<2, false>(a, stream);
+}
+
+hipError_t launch_value_flush(const FlushArgs& a, hipStream_t stream) {
+    const bool rec = a.recon != nullptr;
+    if (a.bits == 4) return rec ? launch_values_t<4, true>(a, stream) : launch_values_t<4, false>(a, stream);
+    return rec ? launch_values_t<2, true>(a, stream) : launch_values_t<2, false>(a, stream);
+}
+
+}  // namespace kivi

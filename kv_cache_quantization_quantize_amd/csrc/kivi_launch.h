@@ -1,0 +1,77 @@
+// kivi_launch.h -- host launchers of the libkivi kernels (internal).  The
+// C ABI in abi.cpp validates every argument before calling these; they only
+// size grids and enqueue.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kivi {
+
+struct FlushArgs {
+    const uint16_t* x;
+    int64_t BH, S, x_bh_stride;
+    uint32_t* codes;
+    int64_t codes_bh_stride;
+    float* scale;
+    float* zero;
+    int64_t meta_bh_stride;
+    int64_t dst_token;
+    uint16_t* recon;               // may be null
+    int64_t recon_bh_stride;
+    int bits;
+};
+
+struct DequantArgs {
+    const uint32_t* codes;
+    int64_t codes_bh_stride;
+    const float* scale;
+    const float* zero;
+    int64_t meta_bh_stride;
+    int64_t BH, t0, n;
+    uint16_t* out;
+    int64_t out_bh_stride;
+    int bits;
+    int kind;                      // KIVI_KEYS or KIVI_VALUES
+};
+
+struct AttendArgs {
+    const uint16_t* q;
+    int64_t B;
+    int Hq, Hkv;
+    const uint32_t* k_codes;
+    const float* k_scale;
+    const float* k_zero;
+    const uint32_t* v_codes;
+    const float* v_scale;
+    const float* v_zero;
+    int64_t k_codes_bh_stride, v_codes_bh_stride;
+    int64_t k_meta_bh_stride, v_meta_bh_stride;
+    int64_t n_quant;
+    const uint16_t* k_res;
+    const uint16_t* v_res;
+    int64_t res_bh_stride;
+    int64_t n_res;
+    float softmax_scale;
+    float* out;
+    void* workspace;
+    int bits;
+};
+
+// Split of the token axis chosen for an attend shape; the workspace holds
+// one (m, l, o[128]) partial per (sequence, query head, split).
+struct AttendPlan {
+    int64_t chunk;                 // tokens per split, a multiple of 32
+    int64_t n_split;
+    size_t workspace_bytes;
+};
+AttendPlan plan_attend(int64_t B, int Hq, int Hkv, int64_t n_quant, int64_t n_res);
+
+hipError_t launch_key_flush(const FlushArgs& a, hipStream_t stream);
+hipError_t launch_value_flush(const FlushArgs& a, hipStream_t stream);
+hipError_t launch_dequantize(const DequantArgs& a, hipStream_t stream);
+hipError_t launch_decode_attend(const AttendArgs& a, const AttendPlan& p, hipStream_t stream);
+hipError_t launch_calib_copy(const void* src, void* dst, size_t n_bytes, hipStream_t stream);
+
+}  // namespace kivi

@@ -1,0 +1,215 @@
+"""Python binding of libkivi (argument marshalling only).
+
+Every call checks torch-level properties (dtype, device, strides), builds
+the C structs and calls the function of the same name in ``libkivi.so`` on
+torch's current HIP stream.  All arithmetic happens in the HIP kernels; if
+the library is missing this module raises instead of computing anything.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkivi.so")
+
+KIVI_KEYS = 0
+KIVI_VALUES = 1
+HEAD_DIM = 128
+GROUP = 32
+
+# symbols of include/kivi.h and include/kivi_calib.h
+EXPORTS = (
+    "kivi_quantize_keys", "kivi_quantize_values", "kivi_dequantize",
+    "kivi_decode_attend", "kivi_decode_attend_workspace_bytes",
+    "kivi_status_string", "kivi_last_hip_error", "kivi_calib_copy",
+)
+
+
+class KiviError(RuntimeError):
+    """A libkivi call returned a negative status."""
+
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+class CStore(ctypes.Structure):
+    _fields_ = [
+        ("codes", ctypes.c_void_p),
+        ("scale", ctypes.c_void_p),
+        ("zero", ctypes.c_void_p),
+        ("codes_bh_stride", ctypes.c_int64),
+        ("meta_bh_stride", ctypes.c_int64),
+        ("cap", ctypes.c_int64),
+        ("bits", ctypes.c_int32),
+        ("group_size", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("kind", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libkivi.so (built by ``__graft_entry__.build()``); never falls back."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+        sp = ctypes.POINTER(CStore)
+        L.kivi_quantize_keys.argtypes = [vp, i64, i64, i64, sp, i64, vp, i64, vp]
+        L.kivi_quantize_values.argtypes = [vp, i64, i64, i64, sp, i64, vp, i64, vp]
+        L.kivi_dequantize.argtypes = [sp, i64, i64, i64, vp, i64, vp]
+        L.kivi_decode_attend.argtypes = [vp, i64, i32, i32, sp, sp, i64, vp, vp, i64, i64,
+                                         ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
+        L.kivi_decode_attend_workspace_bytes.argtypes = [i64, i32, i32, i64, i64]
+        L.kivi_decode_attend_workspace_bytes.restype = ctypes.c_size_t
+        L.kivi_status_string.argtypes = [ctypes.c_int]
+        L.kivi_status_string.restype = ctypes.c_char_p
+        L.kivi_last_hip_error.argtypes = []
+        L.kivi_calib_copy.argtypes = [vp, vp, ctypes.c_size_t, vp]
+        for name in ("kivi_quantize_keys", "kivi_quantize_values", "kivi_dequantize",
+                     "kivi_decode_attend", "kivi_last_hip_error", "kivi_calib_copy"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().kivi_status_string(int(status)).decode()
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise KiviError(rc, what)
+
+
+def _stream(stream=None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def _need_f16(t: torch.Tensor, name: str) -> None:
+    if t.dtype != torch.float16:
+        raise TypeError(f"{name} must be float16, got {t.dtype}")
+    if not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if t.dim() != 3 or t.shape[2] != HEAD_DIM or t.stride(2) != 1 or t.stride(1) != HEAD_DIM:
+        raise ValueError(f"{name} must be [BH][S][{HEAD_DIM}] with contiguous token rows")
+
+
+class Store:
+    """A packed store in device memory (layout of include/kivi.h).
+
+    ``codes`` is int32 storage holding the uint32 code words."""
+
+    def __init__(self, kind: int, BH: int, cap: int, bits: int = 4, device="cuda",
+                 codes: torch.Tensor | None = None, scale: torch.Tensor | None = None,
+                 zero: torch.Tensor | None = None):
+        self.kind, self.BH, self.cap, self.bits = kind, BH, cap, bits
+        self.words = HEAD_DIM * bits // 32
+        meta = (BH, (cap + GROUP - 1) // GROUP, HEAD_DIM) if kind == KIVI_KEYS else \
+            (BH, cap, HEAD_DIM // GROUP)
+        self.codes = codes if codes is not None else torch.zeros((BH, cap, self.words),
+                                                                 dtype=torch.int32, device=device)
+        self.scale = scale if scale is not None else torch.zeros(meta, dtype=torch.float32, device=device)
+        self.zero = zero if zero is not None else torch.zeros(meta, dtype=torch.float32, device=device)
+
+    def c(self) -> CStore:
+        return CStore(self.codes.data_ptr(), self.scale.data_ptr(), self.zero.data_ptr(),
+                      self.codes.stride(0), self.scale.stride(0), self.cap, self.bits,
+                      GROUP, HEAD_DIM, self.kind)
+
+    def nbytes(self) -> int:
+        return (self.codes.numel() * 4 + self.scale.numel() * 4 + self.zero.numel() * 4)
+
+
+def _flush(fn_name, x: torch.Tensor, store: Store, dst_token: int, recon, stream):
+    _need_f16(x, "x")
+    if recon is not None:
+        _need_f16(recon, "recon")
+    st = store.c()
+    rc = getattr(lib(), fn_name)(
+        x.data_ptr(), x.shape[0], x.shape[1], x.stride(0), ctypes.byref(st), dst_token,
+        recon.data_ptr() if recon is not None else None,
+        recon.stride(0) if recon is not None else 0, _stream(stream))
+    _check(rc, fn_name)
+
+
+def quantize_keys(x: torch.Tensor, store: Store, dst_token: int = 0,
+                  recon: torch.Tensor | None = None, stream=None) -> None:
+    """kivi_quantize_keys: per-channel key flush of x[BH][S][128] into store."""
+    _flush("kivi_quantize_keys", x, store, dst_token, recon, stream)
+
+
+def quantize_values(x: torch.Tensor, store: Store, dst_token: int = 0,
+                    recon: torch.Tensor | None = None, stream=None) -> None:
+    """kivi_quantize_values: per-token value flush of x[BH][S][128] into store."""
+    _flush("kivi_quantize_values", x, store, dst_token, recon, stream)
+
+
+def dequantize(store: Store, token_begin: int, n_tokens: int, out: torch.Tensor | None = None,
+               BH: int | None = None, stream=None) -> torch.Tensor:
+    """kivi_dequantize: fp16 [BH][n_tokens][128] reconstruction of a token range."""
+    BH = store.BH if BH is None else BH
+    if out is None:
+        out = torch.empty((BH, n_tokens, HEAD_DIM), dtype=torch.float16, device=store.codes.device)
+    _need_f16(out, "out")
+    st = store.c()
+    rc = lib().kivi_dequantize(ctypes.byref(st), BH, token_begin, n_tokens, out.data_ptr(),
+                               out.stride(0), _stream(stream))
+    _check(rc, "kivi_dequantize")
+    return out
+
+
+def attend_workspace_bytes(B: int, Hq: int, Hkv: int, n_quant: int, n_res: int) -> int:
+    return int(lib().kivi_decode_attend_workspace_bytes(B, Hq, Hkv, n_quant, n_res))
+
+
+def decode_attend(q: torch.Tensor, k_store: Store, v_store: Store, n_quant: int,
+                  k_res: torch.Tensor | None, v_res: torch.Tensor | None, n_res: int,
+                  softmax_scale: float | None = None, out: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """kivi_decode_attend: fp32 [B][Hq][128] attention of one query token per
+    sequence over store tokens [0, n_quant) then residual tokens [0, n_res)."""
+    if q.dtype != torch.float16 or not q.is_cuda or q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous float16 device tensor [B][Hq][128]")
+    B, Hq, D = q.shape
+    Hkv = k_store.BH // B if B else 1
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if not (out.dtype == torch.float32 and out.is_contiguous() and tuple(out.shape) == (B, Hq, D)):
+        raise ValueError("out must be a contiguous float32 [B][Hq][128] tensor")
+    need = attend_workspace_bytes(B, Hq, Hkv, n_quant, n_res) if B else 0
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if n_res > 0:
+        _need_f16(k_res, "k_res")
+        _need_f16(v_res, "v_res")
+        if k_res.stride(0) != v_res.stride(0):
+            raise ValueError("k_res and v_res must share their slab stride")
+    ks, vs = k_store.c(), v_store.c()
+    rc = lib().kivi_decode_attend(
+        q.data_ptr(), B, Hq, Hkv, ctypes.byref(ks), ctypes.byref(vs), n_quant,
+        k_res.data_ptr() if n_res > 0 else None, v_res.data_ptr() if n_res > 0 else None,
+        k_res.stride(0) if n_res > 0 else 0, n_res, float(softmax_scale), out.data_ptr(),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc, "kivi_decode_attend")
+    return out
+
+
+def calib_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    """kivi_calib_copy: device-to-device streaming copy (bandwidth ceiling)."""
+    n = src.numel() * src.element_size()
+    assert dst.numel() * dst.element_size() >= n
+    _check(lib().kivi_calib_copy(src.data_ptr(), dst.data_ptr(), n, _stream(stream)), "kivi_calib_copy")
