@@ -13,231 +13,457 @@
 //                stay fp16) and "So why does the kernel ship?" (dequantize
 //                in registers inside attention).
 //
-// Design for MI355X: one workgroup per (sequence, kv head, token split).  The
-// workgroup serves every query head that shares the kv head, so each packed
+// Design for MI355X: one wave per (sequence, kv head, token split).  The
+// wave serves every query head that shares the kv head, so each packed
 // byte is read from HBM once; the token axis is split so the grid reaches
 // thousands of workgroups even at B=1 (which answers the occupancy limit the
 // pages measured).  Partials (m, l, o[128]) go to the workspace and a second
 // kernel merges them with the log-sum-exp rule.
 //
-// Arithmetic: scores and the weighted sum accumulate in fp32; K and V are the
-// exact fp16 reconstructions of the store (the same values kivi_dequantize
-// writes).
+// Arithmetic: QK^T and PV run on MFMA (fp16 operands, fp32 accumulation).  K
+// and V are dequantized in registers to fp16 with one mixed-precision FMA per
+// element (within one fp16 rounding of the stored reconstruction); q enters
+// exactly, softmax probabilities are rounded to fp16 for PV, and the online
+// softmax runs in fp32, base 2.
+//
+// Grid: one 64-lane wave per (sequence, kv head, split of the token axis);
+// each wave walks its split in 32-token steps, one key group per step, with
+// the step's key and value metadata staged through LDS.
 #include "kivi_device.h"
 #include "kivi_launch.h"
 
 namespace kivi {
 
-constexpr int kMaxChunk = 256;
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
 
+// 8 fp16 values in 4 VGPRs: one MFMA operand of one lane.
+union Frag {
+    half8_t h;
+    uint32_t u[4];
+};
+
+constexpr int kStep = 32;             // tokens per wave step (one key group)
+constexpr int kMaxStepsPerWave = 32;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr uint32_t kMagic = 0x64006400u;   // fp16 1024.0 in both halves
+
+// v_mfma_f32_16x16x32_f16 lane layout (gfx950, wave64), lane l = 16*q + n:
+//   A (16x32): lane l holds row m = n, columns 8q .. 8q+7 (slot s = column - 8q)
+//   B (32x16): lane l holds rows 8q .. 8q+7, column n
+//   D (16x16 fp32): lane l holds rows 4q .. 4q+3, column n
+// The product only pairs A slot s of lane (q, m) with B slot s of lane (q, n),
+// so any bijection channel <-> (q, slot) used on both sides is valid.
+//
+// Channel order inside an 8-channel unit: the codes of channels j and j+4
+// come out of one SIMD-within-register extraction, so slot 2j holds channel
+// j and slot 2j+1 channel j+4 (j = 0..3).  Key unit kb of lane group q is
+// channels 32q + 8kb .. 32q + 8kb + 7.
+
+// Four fp16 pairs (1024 + code[j], 1024 + code[j+4]), j = 0..3, from the 8
+// codes of one 8-channel unit.  4-bit: one code word.  2-bit: the unit's
+// half of a word, spread to bytes 0 and 2 first.
 template <int BITS>
-__device__ __forceinline__ void load_key8(const uint32_t* __restrict__ codes, const float* __restrict__ sc,
-                                          const float* __restrict__ ze, int64_t j, int c, float (&kf)[8]) {
-    constexpr int kWords = kHeadDim * BITS / 32;
-    constexpr uint32_t kMask = (1u << BITS) - 1u;
-    uint32_t w;
-    if constexpr (BITS == 4) w = codes[j * kWords + c];
-    else w = codes[j * kWords + (c >> 1)] >> (16 * (c & 1));
-    const float* sp = sc + (j / kGroup) * kHeadDim + c * 8;
-    const float* zp = ze + (j / kGroup) * kHeadDim + c * 8;
-    const float4 s0 = *reinterpret_cast<const float4*>(sp);
-    const float4 s1 = *reinterpret_cast<const float4*>(sp + 4);
-    const float4 z0 = *reinterpret_cast<const float4*>(zp);
-    const float4 z1 = *reinterpret_cast<const float4*>(zp + 4);
-    const float s[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-    const float z[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+__device__ __forceinline__ void code_pairs(uint32_t w, int half, uint32_t (&p)[4]) {
+    if constexpr (BITS == 4) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) kf[k] = f16_to_f32(recon_f16((w >> (BITS * k)) & kMask, s[k], z[k]));
+        for (int j = 0; j < 4; ++j) p[j] = ((w >> (4 * j)) & 0x000F000Fu) | kMagic;
+    } else {
+        const uint32_t sel = half ? 0x0C030C02u : 0x0C010C00u;
+        const uint32_t s = __builtin_amdgcn_perm(w, w, sel);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) p[j] = ((s >> (2 * j)) & 0x00030003u) | kMagic;
+    }
 }
 
+// code * scale + zero as one mixed-precision FMA with an fp16 result:
+// c16 = 1024 + code exactly and zp = RN32(zero - 1024 s), so the result is
+// code*s + zero up to 2^-24 (|zero| + 1024 s) plus the fp16 rounding (the
+// attend is checked against the float64 definition to 2e-3, not bit-exactly).
+__device__ __forceinline__ _Float16 deq(uint32_t pair, int hi, float s, float zp) {
+    const half2_t c = as_h2(pair);
+    return static_cast<_Float16>(__builtin_fmaf(static_cast<float>(hi ? c[1] : c[0]), s, zp));
+}
+
+__device__ __forceinline__ uint32_t pack_h2(_Float16 lo, _Float16 hi) {
+    half2_t v;
+    v[0] = lo;
+    v[1] = hi;
+    return as_u32(v);
+}
+
+// lane exchanges across the four 16-lane rows (see kivi_device.h)
+__device__ __forceinline__ float rows_max(float v) {
+    auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float rows_sum(float v) {
+    auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+// Global loads of one 32-token step of store tokens, issued one step ahead of
+// the compute that uses them.  Token indices are clamped into the store, so
+// every load is in bounds; lanes whose token is past n_quant ignore them.
 template <int BITS>
-__device__ __forceinline__ void load_value8(const uint32_t* __restrict__ codes, const float* __restrict__ sc,
-                                            const float* __restrict__ ze, int64_t j, int c, float (&vf)[8]) {
+struct StepLoad {
+    uint32_t kw[2][4];      // key codes of token t0 + 16*blk + n (lane's 32 channels)
+    float2 ks, kz;          // key scale / zero of channels 2l, 2l+1 of the step's group
+    float2 vs, vz;          // value scale / zero, token t0 + (l & 31), groups 2(l>>5), +1
+    uint32_t vw[8];         // value code word of the lane's 8 channels, its 8 tokens
+};
+
+// Token (within the step) of PV slot s for lane group q: the order in which
+// QK^T leaves each lane its scores (rows 4q .. 4q+3 of both 16-token blocks).
+__device__ __forceinline__ int pv_token(int q, int s) { return 16 * (s >> 2) + 4 * q + (s & 3); }
+
+template <int BITS>
+__device__ __forceinline__ void issue_step(StepLoad<BITS>& L, const AttendArgs& a, int64_t t0,
+                                           const uint32_t* kc, const float* ksc, const float* kze,
+                                           const uint32_t* vc, const float* vsc, const float* vze,
+                                           int l, int n, int q) {
     constexpr int kWords = kHeadDim * BITS / 32;
-    constexpr uint32_t kMask = (1u << BITS) - 1u;
     constexpr int kMetaPerTok = kHeadDim / kGroup;
-    uint32_t w;
-    if constexpr (BITS == 4) w = codes[j * kWords + c];
-    else w = codes[j * kWords + (c >> 1)] >> (16 * (c & 1));
-    const float s = sc[j * kMetaPerTok + (c >> 2)];
-    const float z = ze[j * kMetaPerTok + (c >> 2)];
+    if (t0 >= a.n_quant) return;                  // uniform: residual-only step
+    const int64_t last = a.n_quant - 1;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) vf[k] = f16_to_f32(recon_f16((w >> (BITS * k)) & kMask, s, z));
+    for (int blk = 0; blk < 2; ++blk) {
+        int64_t tok = t0 + 16 * blk + n;
+        tok = tok < last ? tok : last;
+        if constexpr (BITS == 4) {
+            const uint4 t = *reinterpret_cast<const uint4*>(kc + tok * kWords + 4 * q);
+            L.kw[blk][0] = t.x; L.kw[blk][1] = t.y; L.kw[blk][2] = t.z; L.kw[blk][3] = t.w;
+        } else {
+            const uint2 t = *reinterpret_cast<const uint2*>(kc + tok * kWords + 2 * q);
+            L.kw[blk][0] = t.x; L.kw[blk][1] = t.x; L.kw[blk][2] = t.y; L.kw[blk][3] = t.y;
+        }
+    }
+    const int64_t g = t0 / kGroup;
+    L.ks = *reinterpret_cast<const float2*>(ksc + g * kHeadDim + 2 * l);
+    L.kz = *reinterpret_cast<const float2*>(kze + g * kHeadDim + 2 * l);
+    int64_t tv = t0 + (l & 31);
+    tv = tv < last ? tv : last;
+    L.vs = *reinterpret_cast<const float2*>(vsc + tv * kMetaPerTok + 2 * (l >> 5));
+    L.vz = *reinterpret_cast<const float2*>(vze + tv * kMetaPerTok + 2 * (l >> 5));
+    const int word = BITS == 4 ? n : (n >> 1);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        int64_t tok = t0 + pv_token(q, s);
+        tok = tok < last ? tok : last;
+        L.vw[s] = vc[tok * kWords + word];
+    }
 }
 
-template <int BITS, int GQA>
-__global__ __launch_bounds__(kBlock) void attend_partial_kernel(const AttendArgs a, int64_t chunk,
-                                                                int64_t n_split, float* __restrict__ ws_o,
-                                                                float* __restrict__ ws_ml)
-{
-    __shared__ float q_s[GQA][kHeadDim];
-    __shared__ float p_s[GQA][kMaxChunk];
-    __shared__ float red[kWavesPerBlock][GQA][kHeadDim];
+// Keeps the compiler from moving LDS accesses across this point.  The
+// workgroup is one wave and a wave's LDS instructions execute in order, so
+// no hardware barrier is needed between a lane's write and another lane's
+// later read.
+__device__ __forceinline__ void lds_order() { __atomic_signal_fence(__ATOMIC_SEQ_CST); }
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
+struct Smem {
+    float ks[kHeadDim];                       // key scale of the step's group
+    float kz[kHeadDim];                       // key zero - 1024 * scale
+    float vs[kHeadDim / kGroup][kStep];       // value scale, [group][token]
+    float vz[kHeadDim / kGroup][kStep];       // value zero - 1024 * scale
+};
+
+// Online-softmax state of one lane: head n, channels 32q + 8r + i of acc_o[i][r].
+struct SoftState {
+    float m_run;
+    float l_part;
+    float4_t acc_o[8];
+};
+
+template <int BITS>
+__device__ __forceinline__ void process_step(const StepLoad<BITS>& L, Smem& sm, SoftState& st,
+                                             const Frag (&bq)[4], const AttendArgs& a, int64_t t0,
+                                             int64_t j1, const uint16_t* kr, const uint16_t* vr,
+                                             float c2, int l, int n, int q) {
+    const int64_t N = a.n_quant + a.n_res;
+    // ---- stage this step's metadata in LDS
+    if (t0 < a.n_quant) {
+        lds_order();
+        sm.ks[2 * l] = L.ks.x;
+        sm.ks[2 * l + 1] = L.ks.y;
+        sm.kz[2 * l] = __builtin_fmaf(-1024.0f, L.ks.x, L.kz.x);
+        sm.kz[2 * l + 1] = __builtin_fmaf(-1024.0f, L.ks.y, L.kz.y);
+        const int tt = l & 31;
+        const int gg = (l >> 5) * 2;
+        sm.vs[gg][tt] = L.vs.x;
+        sm.vs[gg + 1][tt] = L.vs.y;
+        sm.vz[gg][tt] = __builtin_fmaf(-1024.0f, L.vs.x, L.vz.x);
+        sm.vz[gg + 1][tt] = __builtin_fmaf(-1024.0f, L.vs.y, L.vz.y);
+        lds_order();
+    }
+
+    // ---- S^T = K Q^T for the two 16-token blocks (token t0 + 16*blk + n)
+    float4_t acc_s[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+        acc_s[blk] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        const int64_t tok = t0 + 16 * blk + n;
+        Frag ka[4];
+        if (tok < a.n_quant) {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                uint32_t pr[4];
+                code_pairs<BITS>(L.kw[blk][kb], kb & 1, pr);
+                const int cb = 32 * q + 8 * kb;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    ka[kb].u[j] = pack_h2(deq(pr[j], 0, sm.ks[cb + j], sm.kz[cb + j]),
+                                          deq(pr[j], 1, sm.ks[cb + j + 4], sm.kz[cb + j + 4]));
+            }
+        } else if (tok < N) {
+            const uint4* src = reinterpret_cast<const uint4*>(kr + (tok - a.n_quant) * kHeadDim + 32 * q);
+            uint32_t rn[16];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const uint4 t = src[v];
+                rn[4 * v] = t.x; rn[4 * v + 1] = t.y; rn[4 * v + 2] = t.z; rn[4 * v + 3] = t.w;
+            }
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int c0 = 8 * kb + j, c1 = 8 * kb + j + 4;
+                    const uint32_t s0 = (c0 & 1) ? 0x0302u : 0x0100u;
+                    const uint32_t s1 = (c1 & 1) ? 0x0706u : 0x0504u;
+                    ka[kb].u[j] = __builtin_amdgcn_perm(rn[c1 >> 1], rn[c0 >> 1], (s1 << 16) | s0);
+                }
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) ka[kb].u[j] = 0u;
+        }
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+            acc_s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[kb].h, bq[kb].h, acc_s[blk], 0, 0, 0);
+    }
+
+    // ---- online softmax (base 2).  Lane (q, n) holds head n's scores of
+    // tokens t0 + 16*blk + 4q + r, r = 0..3.
+    float sv[8];
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t tok = t0 + 16 * blk + 4 * q + r;
+            const float sc = tok < j1 ? acc_s[blk][r] * c2 : -INFINITY;
+            sv[4 * blk + r] = sc;
+            mloc = fmaxf(mloc, sc);
+        }
+    const float m_new = fmaxf(st.m_run, rows_max(mloc));
+    const float alpha = exp2f(st.m_run - m_new);
+    st.m_run = m_new;
+    float psum = 0.0f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        sv[s] = exp2f(sv[s] - m_new);
+        psum += sv[s];
+    }
+    st.l_part = __builtin_fmaf(st.l_part, alpha, psum);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st.acc_o[i] *= alpha;
+    // B operand of PV: P^T, slot s <-> token t0 + pv_token(q, s)
+    Frag bp;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        half2_t h;
+        h[0] = static_cast<_Float16>(sv[2 * j]);
+        h[1] = static_cast<_Float16>(sv[2 * j + 1]);
+        bp.u[j] = as_u32(h);
+    }
+
+    // ---- V rows: lane (q, m=n) takes channels 8n .. 8n+7 of its 8 tokens
+    Frag vrow[8];
+    const int vg = n >> 2;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        const int tl = pv_token(q, s);
+        const int64_t tok = t0 + tl;
+        if (tok < a.n_quant) {
+            uint32_t pr[4];
+            code_pairs<BITS>(L.vw[s], n & 1, pr);
+            const float sc = sm.vs[vg][tl];
+            const float zp = sm.vz[vg][tl];
+#pragma unroll
+            for (int v = 0; v < 4; ++v)               // natural order: channels 2v, 2v+1
+                vrow[s].u[v] = pack_h2(deq(pr[(2 * v) & 3], (2 * v) >> 2, sc, zp),
+                                       deq(pr[(2 * v + 1) & 3], (2 * v + 1) >> 2, sc, zp));
+        } else if (tok < N) {
+            const uint4 t = *reinterpret_cast<const uint4*>(vr + (tok - a.n_quant) * kHeadDim + 8 * n);
+            vrow[s].u[0] = t.x; vrow[s].u[1] = t.y; vrow[s].u[2] = t.z; vrow[s].u[3] = t.w;
+        } else {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) vrow[s].u[v] = 0u;
+        }
+    }
+    // ---- O^T += V^T P^T: MFMA i covers channels 8m + i, m = 0..15
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        Frag va;
+        const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            va.u[j] = __builtin_amdgcn_perm(vrow[2 * j + 1].u[i >> 1], vrow[2 * j].u[i >> 1], sel);
+        st.acc_o[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va.h, bp.h, st.acc_o[i], 0, 0, 0);
+    }
+}
+
+// One wave: sequence b, kv head kv, steps_per_wave 32-token steps starting at
+// split * steps_per_wave * 32 of [store tokens 0..n_quant-1 ; residual 0..n_res-1].
+template <int BITS, int GQA>
+__global__ __launch_bounds__(64) void attend_partial_kernel(const AttendArgs a, int64_t steps_per_wave,
+                                                            int64_t n_split, float* __restrict__ ws_o,
+                                                            float* __restrict__ ws_ml)
+{
+    __shared__ Smem sm;
+    const int l = threadIdx.x;
+    const int n = l & 15;
+    const int q = l >> 4;
     const int64_t split = blockIdx.x;
-    const int64_t bkv = blockIdx.y;                  // b * Hkv + kv
+    const int64_t bkv = blockIdx.y;
     const int64_t b = bkv / a.Hkv;
     const int kv = static_cast<int>(bkv - b * a.Hkv);
     const int64_t N = a.n_quant + a.n_res;
-    const int64_t j0 = split * chunk;
-    const int n_tok = static_cast<int>((j0 + chunk < N ? j0 + chunk : N) - j0);
+    const int64_t j0 = split * steps_per_wave * kStep;
+    const int64_t j1 = (j0 + steps_per_wave * kStep < N) ? j0 + steps_per_wave * kStep : N;
     const int64_t qrow0 = b * a.Hq + static_cast<int64_t>(kv) * GQA;
 
-    for (int idx = tid; idx < GQA * kHeadDim; idx += kBlock)
-        q_s[idx / kHeadDim][idx % kHeadDim] = f16_to_f32(a.q[qrow0 * kHeadDim + idx]);
-    __syncthreads();
-
-    const int c = tid & 15;                          // channels 8c .. 8c+7
-    const int row = tid >> 4;                        // 16 token rows per pass
     const uint32_t* kc = a.k_codes + bkv * a.k_codes_bh_stride;
-    const float* ks = a.k_scale + bkv * a.k_meta_bh_stride;
-    const float* kz = a.k_zero + bkv * a.k_meta_bh_stride;
+    const float* ksc = a.k_scale + bkv * a.k_meta_bh_stride;
+    const float* kze = a.k_zero + bkv * a.k_meta_bh_stride;
     const uint32_t* vc = a.v_codes + bkv * a.v_codes_bh_stride;
-    const float* vs = a.v_scale + bkv * a.v_meta_bh_stride;
-    const float* vz = a.v_zero + bkv * a.v_meta_bh_stride;
+    const float* vsc = a.v_scale + bkv * a.v_meta_bh_stride;
+    const float* vze = a.v_zero + bkv * a.v_meta_bh_stride;
     const uint16_t* kr = a.k_res + bkv * a.res_bh_stride;
     const uint16_t* vr = a.v_res + bkv * a.res_bh_stride;
 
-    // ---- scores s[h][t] = (q_h . k_t) * softmax_scale
-    float qreg[GQA][8];
-#pragma unroll
-    for (int h = 0; h < GQA; ++h)
-#pragma unroll
-        for (int k = 0; k < 8; ++k) qreg[h][k] = q_s[h][c * 8 + k];
+    StepLoad<BITS> bufA, bufB;
+    issue_step<BITS>(bufA, a, j0, kc, ksc, kze, vc, vsc, vze, l, n, q);
 
-    for (int t0 = 0; t0 < n_tok; t0 += 16) {         // uniform trip count
-        const int t = t0 + row;
-        const bool valid = t < n_tok;
-        const int64_t j = j0 + (valid ? t : 0);
-        float kf[8];
-        if (j < a.n_quant) {
-            load_key8<BITS>(kc, ks, kz, j, c, kf);
+    // B operand of QK^T: q of head n (zero for n >= GQA) in slot order.
+    Frag bq[4];
+    {
+        uint32_t qn[16];                      // channels 32q .. 32q+31, natural order
+        if (n < GQA) {
+            const uint4* src = reinterpret_cast<const uint4*>(a.q + (qrow0 + n) * kHeadDim + 32 * q);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const uint4 t = src[v];
+                qn[4 * v] = t.x; qn[4 * v + 1] = t.y; qn[4 * v + 2] = t.z; qn[4 * v + 3] = t.w;
+            }
         } else {
-            const uint4 v = *reinterpret_cast<const uint4*>(kr + (j - a.n_quant) * kHeadDim + c * 8);
-            unpack8(v, kf);
-        }
-        float part[GQA];
 #pragma unroll
-        for (int h = 0; h < GQA; ++h) {
-            float acc = 0.0f;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) acc = __builtin_fmaf(qreg[h][k], kf[k], acc);
-            acc += __shfl_xor(acc, 1);
-            acc += __shfl_xor(acc, 2);
-            acc += __shfl_xor(acc, 4);
-            acc += __shfl_xor(acc, 8);
-            part[h] = acc;
+            for (int v = 0; v < 16; ++v) qn[v] = 0u;
         }
-        if (valid && c == 0) {
 #pragma unroll
-            for (int h = 0; h < GQA; ++h) p_s[h][t] = part[h] * a.softmax_scale;
-        }
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                // slots (2j, 2j+1) = channels (8kb + j, 8kb + j + 4) of the lane's window
+                const int c0 = 8 * kb + j, c1 = 8 * kb + j + 4;
+                const uint32_t s0 = (c0 & 1) ? 0x0302u : 0x0100u;
+                const uint32_t s1 = (c1 & 1) ? 0x0706u : 0x0504u;
+                bq[kb].u[j] = __builtin_amdgcn_perm(qn[c1 >> 1], qn[c0 >> 1], (s1 << 16) | s0);
+            }
     }
-    __syncthreads();
 
-    // ---- softmax over the split: wave w owns heads w, w+4, ...
-    for (int h = wave; h < GQA; h += kWavesPerBlock) {
-        float m = -INFINITY;
-        for (int t = lane; t < n_tok; t += 64) m = fmaxf(m, p_s[h][t]);
+    const float c2 = a.softmax_scale * kLog2e;
+    SoftState st;
+    st.m_run = -INFINITY;
+    st.l_part = 0.0f;
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-        float l = 0.0f;
-        for (int t = lane; t < n_tok; t += 64) {
-            const float p = __expf(p_s[h][t] - m);
-            p_s[h][t] = p;
-            l += p;
-        }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
-        if (lane == 0) {
-            float* ml = ws_ml + ((qrow0 + h) * n_split + split) * 2;
-            ml[0] = m;
-            ml[1] = l;
-        }
-    }
-    __syncthreads();
+    for (int i = 0; i < 8; ++i) st.acc_o[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // ---- o[h][d] = sum_t p[h][t] * v[t][d]
-    float acc[GQA][8];
-#pragma unroll
-    for (int h = 0; h < GQA; ++h)
-#pragma unroll
-        for (int k = 0; k < 8; ++k) acc[h][k] = 0.0f;
+    // two buffers in flight: the loads of step t+32 overlap the compute of t
+    for (int64_t t0 = j0; t0 < j1; t0 += 2 * kStep) {
+        if (t0 + kStep < j1) issue_step<BITS>(bufB, a, t0 + kStep, kc, ksc, kze, vc, vsc, vze, l, n, q);
+        process_step<BITS>(bufA, sm, st, bq, a, t0, j1, kr, vr, c2, l, n, q);
+        if (t0 + kStep >= j1) break;
+        if (t0 + 2 * kStep < j1) issue_step<BITS>(bufA, a, t0 + 2 * kStep, kc, ksc, kze, vc, vsc, vze, l, n, q);
+        process_step<BITS>(bufB, sm, st, bq, a, t0 + kStep, j1, kr, vr, c2, l, n, q);
+    }
 
-    for (int t0 = 0; t0 < n_tok; t0 += 16) {
-        const int t = t0 + row;
-        const bool valid = t < n_tok;
-        const int64_t j = j0 + (valid ? t : 0);
-        float vf[8];
-        if (j < a.n_quant) {
-            load_value8<BITS>(vc, vs, vz, j, c, vf);
-        } else {
-            const uint4 v = *reinterpret_cast<const uint4*>(vr + (j - a.n_quant) * kHeadDim + c * 8);
-            unpack8(v, vf);
+    // ---- partial (m, l, o) of head n: lane (q, n) holds channels 32q + 8r + i
+    const float l_tot = rows_sum(st.l_part);
+    if (n < GQA) {
+        float* dst = ws_o + ((qrow0 + n) * n_split + split) * kHeadDim + 32 * q;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            *reinterpret_cast<float4*>(dst + 8 * r) =
+                make_float4(st.acc_o[0][r], st.acc_o[1][r], st.acc_o[2][r], st.acc_o[3][r]);
+            *reinterpret_cast<float4*>(dst + 8 * r + 4) =
+                make_float4(st.acc_o[4][r], st.acc_o[5][r], st.acc_o[6][r], st.acc_o[7][r]);
         }
-#pragma unroll
-        for (int h = 0; h < GQA; ++h) {
-            const float p = valid ? p_s[h][t] : 0.0f;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) acc[h][k] = __builtin_fmaf(p, vf[k], acc[h][k]);
+        if (q == 0) {
+            float* ml = ws_ml + ((qrow0 + n) * n_split + split) * 2;
+            ml[0] = st.m_run;
+            ml[1] = l_tot;
         }
-    }
-    // rows 4w .. 4w+3 of wave w meet in lanes 0..15
-#pragma unroll
-    for (int h = 0; h < GQA; ++h)
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            acc[h][k] += __shfl_xor(acc[h][k], 16);
-            acc[h][k] += __shfl_xor(acc[h][k], 32);
-        }
-    if (lane < 16) {
-#pragma unroll
-        for (int h = 0; h < GQA; ++h)
-#pragma unroll
-            for (int k = 0; k < 8; ++k) red[wave][h][c * 8 + k] = acc[h][k];
-    }
-    __syncthreads();
-    for (int idx = tid; idx < GQA * kHeadDim; idx += kBlock) {
-        const int h = idx / kHeadDim;
-        const int d = idx % kHeadDim;
-        const float o = (red[0][h][d] + red[1][h][d]) + (red[2][h][d] + red[3][h][d]);
-        ws_o[((qrow0 + h) * n_split + split) * kHeadDim + d] = o;
     }
 }
 
-// Merge the splits of one (sequence, query head): o = sum_i e^(m_i - M) o_i /
-// sum_i e^(m_i - M) l_i with M = max_i m_i.
+// Merge the splits of one (sequence, query head), base-2 log-sum-exp:
+// o = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i with M = max_i m_i.
 __global__ __launch_bounds__(kHeadDim) void attend_combine_kernel(const float* __restrict__ ws_o,
                                                                   const float* __restrict__ ws_ml,
                                                                   int64_t n_split, float* __restrict__ out)
 {
+    __shared__ float red[2];
     const int64_t row = blockIdx.x;                  // b * Hq + h
     const int d = threadIdx.x;
     const float* ml = ws_ml + row * n_split * 2;
     float M = -INFINITY;
-    for (int64_t i = 0; i < n_split; ++i) M = fmaxf(M, ml[2 * i]);
+    for (int64_t i = d; i < n_split; i += kHeadDim) M = fmaxf(M, ml[2 * i]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    if ((d & 63) == 0) red[d >> 6] = M;
+    __syncthreads();
+    M = fmaxf(red[0], red[1]);
     float L = 0.0f, acc = 0.0f;
-    for (int64_t i = 0; i < n_split; ++i) {
-        const float w = __expf(ml[2 * i] - M);
-        L = __builtin_fmaf(w, ml[2 * i + 1], L);
-        acc = __builtin_fmaf(w, ws_o[(row * n_split + i) * kHeadDim + d], acc);
+    const float* o = ws_o + row * n_split * kHeadDim + d;
+    int64_t i = 0;
+    for (; i + 4 <= n_split; i += 4) {
+        float w[4], lv[4], ov[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            w[u] = ml[2 * (i + u)];
+            lv[u] = ml[2 * (i + u) + 1];
+            ov[u] = o[(i + u) * kHeadDim];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float e = exp2f(w[u] - M);
+            L = __builtin_fmaf(e, lv[u], L);
+            acc = __builtin_fmaf(e, ov[u], acc);
+        }
+    }
+    for (; i < n_split; ++i) {
+        const float e = exp2f(ml[2 * i] - M);
+        L = __builtin_fmaf(e, ml[2 * i + 1], L);
+        acc = __builtin_fmaf(e, o[i * kHeadDim], acc);
     }
     out[row * kHeadDim + d] = acc / L;
 }
 
 AttendPlan plan_attend(int64_t B, int Hq, int Hkv, int64_t n_quant, int64_t n_res) {
-    (void)Hq;
     const int64_t N = n_quant + n_res;
     const int64_t pairs = B * Hkv;
-    int64_t chunk = kMaxChunk;
-    // smaller splits until the grid holds >= 4 workgroups per CU (256 CUs)
-    while (chunk > 32 && pairs * ((N + chunk - 1) / chunk) < 1024) chunk /= 2;
+    const int64_t steps = (N + kStep - 1) / kStep;
+    // enough waves for two per SIMD (1024 SIMDs) before lengthening them
+    int64_t spw = pairs * steps / 2048;
+    spw = spw < 1 ? 1 : (spw > kMaxStepsPerWave ? kMaxStepsPerWave : spw);
     AttendPlan p;
-    p.chunk = chunk;
-    p.n_split = (N + chunk - 1) / chunk;
+    p.chunk = spw * kStep;
+    p.n_split = (steps + spw - 1) / spw;
     const size_t rows = static_cast<size_t>(B) * static_cast<size_t>(Hq) * static_cast<size_t>(p.n_split);
     const size_t o_bytes = (rows * kHeadDim * sizeof(float) + 255) & ~static_cast<size_t>(255);
     p.workspace_bytes = o_bytes + rows * 2 * sizeof(float);
@@ -251,8 +477,8 @@ static hipError_t launch_t(const AttendArgs& a, const AttendPlan& p, hipStream_t
     const size_t o_bytes = (rows * kHeadDim * sizeof(float) + 255) & ~static_cast<size_t>(255);
     float* ws_ml = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + o_bytes);
     const dim3 grid(static_cast<uint32_t>(p.n_split), static_cast<uint32_t>(a.B * a.Hkv));
-    hipLaunchKernelGGL((attend_partial_kernel<BITS, GQA>), grid, dim3(kBlock), 0, stream, a,
-                       p.chunk, p.n_split, ws_o, ws_ml);
+    hipLaunchKernelGGL((attend_partial_kernel<BITS, GQA>), grid, dim3(64), 0, stream, a,
+                       p.chunk / kStep, p.n_split, ws_o, ws_ml);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(attend_combine_kernel, dim3(static_cast<uint32_t>(a.B * a.Hq)),

@@ -47,40 +47,43 @@ __global__ __launch_bounds__(kBlock) void key_flush_kernel(
     // group re-read the last real token, which is the edge padding of
     // "Three ways to be off by one bit", item 3, and cannot move min or max.
     const uint16_t* xb = x + bh * x_bh_stride + c * 8;
-    float f[kTokPerLane][8];
+    uint4 raw[kTokPerLane];
 #pragma unroll
     for (int i = 0; i < kTokPerLane; ++i) {
         int64_t s = s0 + r + kRowsPerWave * i;
         s = s < S ? s : S - 1;
-        const uint4 v = *reinterpret_cast<const uint4*>(xb + s * kHeadDim);
-        unpack8(v, f[i]);
+        raw[i] = *reinterpret_cast<const uint4*>(xb + s * kHeadDim);
     }
 
-    // Per-channel min/max over the lane's 8 rows, then over the 4 row lanes.
-    float mn[8], mx[8];
+    // Per-channel min/max in packed fp16 (exact: the conversion to fp32 is
+    // monotone), over the lane's 8 rows and then across the 4 row lanes.
+    half2_t mn[4], mx[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        mn[j] = f[0][j];
-        mx[j] = f[0][j];
+    for (int k = 0; k < 4; ++k) {
+        half2_t v[kTokPerLane];
 #pragma unroll
-        for (int i = 1; i < kTokPerLane; ++i) {
-            mn[j] = fminf(mn[j], f[i][j]);
-            mx[j] = fmaxf(mx[j], f[i][j]);
+        for (int i = 0; i < kTokPerLane; ++i) {
+            const uint32_t w = k == 0 ? raw[i].x : k == 1 ? raw[i].y : k == 2 ? raw[i].z : raw[i].w;
+            v[i] = as_h2(w);
         }
-        mn[j] = fminf(mn[j], __shfl_xor(mn[j], 16));
-        mx[j] = fmaxf(mx[j], __shfl_xor(mx[j], 16));
-        mn[j] = fminf(mn[j], __shfl_xor(mn[j], 32));
-        mx[j] = fmaxf(mx[j], __shfl_xor(mx[j], 32));
+        mn[k] = hmin3(hmin3(v[0], v[1], v[2]), hmin3(v[3], v[4], v[5]), hmin(v[6], v[7]));
+        mx[k] = hmax3(hmax3(v[0], v[1], v[2]), hmax3(v[3], v[4], v[5]), hmax(v[6], v[7]));
+        mn[k] = half_min(row_pair_min(mn[k]));
+        mx[k] = half_max(row_pair_max(mx[k]));
     }
 
-    // zero = min, scale = (max - min) / (2^bits - 1), IEEE division.
-    constexpr float kLevels = static_cast<float>((1 << BITS) - 1);
-    float sc[8], ze[8];
+    // zero = min, scale = RN((max - min) / (2^bits - 1)), r ~ 1/scale.
+    float ze[8], sc[8], rc[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        ze[j] = canon_zero(mn[j]);
-        const float range = canon_zero(mx[j]) - ze[j];
-        sc[j] = range / kLevels;
+    for (int k = 0; k < 4; ++k) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int j = 2 * k + h;
+            ze[j] = canon_zero(static_cast<float>(mn[k][h]));
+            const float range = canon_zero(static_cast<float>(mx[k][h])) - ze[j];
+            sc[j] = scale_of<BITS>(range);
+            rc[j] = recip_or_zero(sc[j]);
+        }
     }
 
     const int64_t meta_off = bh * meta_bh_stride + (dst_token / kGroup + g) * kHeadDim + c * 8;
@@ -96,19 +99,29 @@ __global__ __launch_bounds__(kBlock) void key_flush_kernel(
 #pragma unroll
     for (int i = 0; i < kTokPerLane; ++i) {
         const int64_t s = s0 + r + kRowsPerWave * i;
+        float f[8];
+        unpack8(raw[i], f);
         uint32_t q[8];
-        uint32_t packed = 0;
+        bool near = false;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            q[j] = quant_code<BITS>(f[i][j], ze[j], sc[j]);
-            packed |= q[j] << (BITS * j);
+            bool nj;
+            q[j] = quant_fast(f[j], ze[j], rc[j], nj);
+            near |= nj;
         }
+        if (near) {                                // rare: within 2^-16 of a tie
+#pragma unroll
+            for (int j = 0; j < 8; ++j) q[j] = quant_exact(f[j], ze[j], sc[j]);
+        }
+        uint32_t packed = q[0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) packed |= q[j] << (BITS * j);
         if constexpr (BITS == 4) {
             // the lane's 8 channels are exactly one word
             if (s < S) cb[s * kWords + c] = packed;
         } else {
             // 16 channels per word: the even lane takes its odd neighbour's half
-            const uint32_t hi = __shfl_xor(packed, 1);
+            const uint32_t hi = quad_xor1(packed);
             if (s < S && (c & 1) == 0) cb[s * kWords + (c >> 1)] = packed | (hi << 16);
         }
         if constexpr (RECON) {
@@ -149,39 +162,51 @@ __global__ __launch_bounds__(kBlock) void value_flush_kernel(
     float* scb = scale + bh * meta_bh_stride + dst_token * kMetaPerTok;
     float* zeb = zero + bh * meta_bh_stride + dst_token * kMetaPerTok;
 
+    uint4 raw[kTokPerLane];
 #pragma unroll
     for (int i = 0; i < kTokPerLane; ++i) {
         const int64_t s = s0 + r + kRowsPerWave * i;
         const int64_t sl = s < S ? s : S - 1;       // keep every lane in the exchange
-        float f[8];
-        unpack8(*reinterpret_cast<const uint4*>(xb + sl * kHeadDim), f);
-        float mn = f[0], mx = f[0];
+        raw[i] = *reinterpret_cast<const uint4*>(xb + sl * kHeadDim);
+    }
+
 #pragma unroll
-        for (int k = 1; k < 8; ++k) {
-            mn = fminf(mn, f[k]);
-            mx = fmaxf(mx, f[k]);
-        }
+    for (int i = 0; i < kTokPerLane; ++i) {
+        const int64_t s = s0 + r + kRowsPerWave * i;
+        const half2_t a = as_h2(raw[i].x), b = as_h2(raw[i].y), cc = as_h2(raw[i].z), d = as_h2(raw[i].w);
+        half2_t mn = hmin(hmin3(a, b, cc), d);
+        half2_t mx = hmax(hmax3(a, b, cc), d);
         // the 4 lanes of one group are a DPP quad
-        mn = fminf(mn, __shfl_xor(mn, 1));
-        mx = fmaxf(mx, __shfl_xor(mx, 1));
-        mn = fminf(mn, __shfl_xor(mn, 2));
-        mx = fmaxf(mx, __shfl_xor(mx, 2));
+        mn = hmin(mn, as_h2(quad_xor1(as_u32(mn))));
+        mx = hmax(mx, as_h2(quad_xor1(as_u32(mx))));
+        mn = hmin(mn, as_h2(quad_xor2(as_u32(mn))));
+        mx = hmax(mx, as_h2(quad_xor2(as_u32(mx))));
+        const float ze = canon_zero(fminf(static_cast<float>(mn[0]), static_cast<float>(mn[1])));
+        const float range = canon_zero(fmaxf(static_cast<float>(mx[0]), static_cast<float>(mx[1]))) - ze;
+        const float sc = scale_of<BITS>(range);
+        const float rc = recip_or_zero(sc);
 
-        constexpr float kLevels = static_cast<float>((1 << BITS) - 1);
-        const float ze = canon_zero(mn);
-        const float sc = (canon_zero(mx) - ze) / kLevels;
-
+        float f[8];
+        unpack8(raw[i], f);
         uint32_t q[8];
-        uint32_t packed = 0;
+        bool near = false;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            q[k] = quant_code<BITS>(f[k], ze, sc);
-            packed |= q[k] << (BITS * k);
+            bool nk;
+            q[k] = quant_fast(f[k], ze, rc, nk);
+            near |= nk;
         }
+        if (near) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) q[k] = quant_exact(f[k], ze, sc);
+        }
+        uint32_t packed = q[0];
+#pragma unroll
+        for (int k = 1; k < 8; ++k) packed |= q[k] << (BITS * k);
         if constexpr (BITS == 4) {
             if (s < S) cb[s * kWords + c] = packed;
         } else {
-            const uint32_t hi = __shfl_xor(packed, 1);
+            const uint32_t hi = quad_xor1(packed);
             if (s < S && (c & 1) == 0) cb[s * kWords + (c >> 1)] = packed | (hi << 16);
         }
         if (s < S) {

@@ -53,6 +53,99 @@ __device__ __forceinline__ uint4 pack8(const uint32_t (&h)[8]) {
     return v;
 }
 
+// Two fp16 values in one VGPR, for the packed min/max instructions.
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ half2_t as_h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
+__device__ __forceinline__ uint32_t as_u32(half2_t v) { return __builtin_bit_cast(uint32_t, v); }
+
+// IEEE 754-2019 minimum/maximum: exact on finite values, -0 < +0 (zeros are
+// canonicalized afterwards).  Three inputs map to v_pk_minimum3_f16 /
+// v_pk_maximum3_f16.
+__device__ __forceinline__ half2_t hmin(half2_t a, half2_t b) { return __builtin_elementwise_minimum(a, b); }
+__device__ __forceinline__ half2_t hmax(half2_t a, half2_t b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ half2_t hmin3(half2_t a, half2_t b, half2_t c) { return hmin(hmin(a, b), c); }
+__device__ __forceinline__ half2_t hmax3(half2_t a, half2_t b, half2_t c) { return hmax(hmax(a, b), c); }
+
+// Reductions across the four 16-lane rows of a wave with the gfx950 lane
+// swaps: permlane16_swap exchanges rows 0<->1 and 2<->3, permlane32_swap the
+// two halves, so min(a, b) of the two swapped copies combines row pairs.
+__device__ __forceinline__ half2_t row_pair_min(half2_t v) {
+    const auto p = __builtin_amdgcn_permlane16_swap(as_u32(v), as_u32(v), false, false);
+    return hmin(as_h2(p[0]), as_h2(p[1]));
+}
+__device__ __forceinline__ half2_t row_pair_max(half2_t v) {
+    const auto p = __builtin_amdgcn_permlane16_swap(as_u32(v), as_u32(v), false, false);
+    return hmax(as_h2(p[0]), as_h2(p[1]));
+}
+__device__ __forceinline__ half2_t half_min(half2_t v) {
+    const auto p = __builtin_amdgcn_permlane32_swap(as_u32(v), as_u32(v), false, false);
+    return hmin(as_h2(p[0]), as_h2(p[1]));
+}
+__device__ __forceinline__ half2_t half_max(half2_t v) {
+    const auto p = __builtin_amdgcn_permlane32_swap(as_u32(v), as_u32(v), false, false);
+    return hmax(as_h2(p[0]), as_h2(p[1]));
+}
+
+// DPP quad permutations (lane ^ 1, lane ^ 2 within each group of 4 lanes).
+__device__ __forceinline__ uint32_t quad_xor1(uint32_t v) {
+    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ uint32_t quad_xor2(uint32_t v) {
+    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x4E, 0xF, 0xF, false));
+}
+
+// scale = RN(range / (2^bits - 1)) in three operations: a product with the
+// rounded reciprocal of the constant, then one FMA correction step.  This
+// equals the IEEE quotient for every binary32 range in [2^-24, 2^18) and for
+// 0, checked exhaustively for both divisors (every range here is 0 or a
+// rounded difference of two fp16 values, so it lies in that set).
+template <int BITS>
+__device__ __forceinline__ float scale_of(float range) {
+    constexpr float kL = static_cast<float>((1 << BITS) - 1);
+    constexpr float kRL = 1.0f / kL;
+    const float q0 = range * kRL;
+    const float rho = __builtin_fmaf(-q0, kL, range);
+    return __builtin_fmaf(rho, kRL, q0);
+}
+
+// 1/s to within 2^-22 relative: hardware reciprocal r0 plus one Newton step
+// e = RN(1 - s*r0), r1 = RN(r0 + r0*e).  The step squares r0's relative
+// error (any r0 within 2^-12 leaves at most 2^-24) and its two roundings add
+// at most 2^-23.  0 for a constant group, so its quotients are exactly 0.
+__device__ __forceinline__ float recip_or_zero(float s) {
+    const float r0 = __builtin_amdgcn_rcpf(s);
+    const float e = __builtin_fmaf(-s, r0, 1.0f);
+    const float r1 = __builtin_fmaf(r0, e, r0);
+    return s == 0.0f ? 0.0f : r1;
+}
+
+// Code of one element on the fast path: rint(t * r) with t = x - zero.
+//
+// Why it equals rint(fl(t / s)) unless `near` is set.  With |r - 1/s| <=
+// 2^-22/s, y = RN(t*r) and z = t/s < 16:
+//   |y - z| <= z (2^-22 + 2^-24) (1 + 2^-22),  |fl(z) - z| <= z 2^-24,
+// so |y - fl(z)| < 16 * 1.51 * 2^-22 < 2^-17.  rint only changes value at
+// half-integers, so if y is farther than 2^-16 from every half-integer,
+// y and fl(z) round to the same integer; otherwise `near` is set and the
+// caller recomputes the code with the IEEE quotient.  (y - q is exact:
+// q = rint(y) is within half of y.)  The code needs no clip: 0 <= t <=
+// range (rounding is monotone) and s >= (range/L)(1 - 2^-24) bound y by
+// L (1 + 2^-21) < L + 1/2.
+__device__ __forceinline__ uint32_t quant_fast(float x, float zero, float r, bool& near) {
+    const float t = x - zero;
+    const float y = t * r;
+    const float q = __builtin_rintf(y);
+    near = __builtin_fabsf(y - q) > 0.5f - 0x1p-16f;
+    return static_cast<uint32_t>(q);
+}
+
+// The same code with the IEEE quotient (the oracle's exact steps).
+__device__ __forceinline__ uint32_t quant_exact(float x, float zero, float s) {
+    if (s == 0.0f) return 0u;
+    return static_cast<uint32_t>(__builtin_rintf((x - zero) / s));
+}
+
 // A zero extreme is stored as +0, so the result does not depend on which
 // signed zero a reduction kept.
 __device__ __forceinline__ float canon_zero(float v) { return v == 0.0f ? 0.0f : v; }

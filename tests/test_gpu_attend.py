@@ -113,3 +113,34 @@ def test_deterministic():
     a = _gpu(c)
     b = _gpu(c)
     assert np.array_equal(a, b)
+
+
+def test_graph_replays_match_eager():
+    """Flush + attend captured into one HIP graph: every replay (with eager
+    work and synchronizations in between) reproduces the eager bytes."""
+    c = _case(2, 32, 8, 1000, 64, 4, seed=6)
+    BH = 16
+    x_new = synth.kv_tensor(BH, 32, keys=True, seed=7, device="cuda")
+    ks2 = kivi.Store(kivi.KIVI_KEYS, BH, 64, 4)
+    out = torch.empty((2, 32, D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(kivi.attend_workspace_bytes(2, 32, 8, 1000, 64), dtype=torch.uint8, device="cuda")
+
+    def work():
+        kivi.quantize_keys(x_new, ks2, 32)
+        kivi.decode_attend(c["q"], c["ks"], c["vs"], 1000, c["kr"], c["vr"], 64, out=out, workspace=ws)
+
+    work()
+    torch.cuda.synchronize()
+    want_out, want_codes = out.clone(), ks2.codes.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        work()
+    for rep in range(4):
+        out.zero_()
+        ks2.codes.zero_()
+        _ = (c["kx"].float() * 2).sum()             # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, want_out), f"replay {rep}"
+        assert torch.equal(ks2.codes, want_codes), f"replay {rep}"
