@@ -63,7 +63,7 @@ __global__ __launch_bounds__(kBlock) void dequant_kernel(
         }
         uint32_t h[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) h[j] = recon_f16((w >> (BITS * j)) & kMask, sc[j], ze[j]);
+        for (int j = 0; j < 8; ++j) h[j] = recon_f16(static_cast<float>((w >> (BITS * j)) & kMask), sc[j], ze[j]);
         *reinterpret_cast<uint4*>(out + bh * out_bh_stride + k * kHeadDim + c * 8) = pack8(h);
     }
 }

@@ -24,35 +24,27 @@ namespace kivi {
 // ---------------------------------------------------------------------------
 // Keys: group = (bh, token group g, channel d) over tokens [32g, min(32g+32, S))
 // ---------------------------------------------------------------------------
-template <int BITS, bool RECON>
-__global__ __launch_bounds__(kBlock) void key_flush_kernel(
-    const uint16_t* __restrict__ x, int64_t S, int64_t x_bh_stride,
-    uint32_t* __restrict__ codes, int64_t codes_bh_stride,
-    float* __restrict__ scale, float* __restrict__ zero, int64_t meta_bh_stride,
-    int64_t dst_token, uint16_t* __restrict__ recon, int64_t recon_bh_stride,
-    int64_t n_groups, int64_t n_tiles)
+// One tile.  xt, ct, rt point at token s0 of the slab (input, codes, recon);
+// n_rows = min(32, S - s0) real rows.  RAGGED tiles clamp loads to the last
+// real row and guard stores; full tiles do neither.
+template <int BITS, bool RECON, bool RAGGED>
+__device__ __forceinline__ void key_tile(const uint16_t* __restrict__ xt, uint32_t* __restrict__ ct,
+                                         float* __restrict__ sct, float* __restrict__ zet,
+                                         uint16_t* __restrict__ rt, int n_rows, int lane, float one)
 {
     constexpr int kWords = kHeadDim * BITS / 32;   // code words per token row
-    const int lane = threadIdx.x & 63;
-    const int64_t tile = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
-    if (tile >= n_tiles) return;                   // uniform across the wave
-
-    const int64_t bh = tile / n_groups;
-    const int64_t g = tile - bh * n_groups;
     const int c = lane & 15;                       // channels 8c .. 8c+7
     const int r = lane >> 4;                       // token rows r, r+4, ...
-    const int64_t s0 = g * kGroup;
 
     // Load 8 token rows x 8 channels.  Rows past the end of a ragged last
     // group re-read the last real token, which is the edge padding of
     // "Three ways to be off by one bit", item 3, and cannot move min or max.
-    const uint16_t* xb = x + bh * x_bh_stride + c * 8;
     uint4 raw[kTokPerLane];
 #pragma unroll
     for (int i = 0; i < kTokPerLane; ++i) {
-        int64_t s = s0 + r + kRowsPerWave * i;
-        s = s < S ? s : S - 1;
-        raw[i] = *reinterpret_cast<const uint4*>(xb + s * kHeadDim);
+        int row = r + kRowsPerWave * i;
+        if constexpr (RAGGED) row = row < n_rows ? row : n_rows - 1;
+        raw[i] = *reinterpret_cast<const uint4*>(xt + row * kHeadDim + c * 8);
     }
 
     // Per-channel min/max in packed fp16 (exact: the conversion to fp32 is
@@ -72,155 +64,190 @@ __global__ __launch_bounds__(kBlock) void key_flush_kernel(
         mx[k] = half_max(row_pair_max(mx[k]));
     }
 
-    // zero = min, scale = RN((max - min) / (2^bits - 1)), r ~ 1/scale.
+    // zero = min, scale = RN((max - min) / (2^bits - 1)), r ~ 1/scale.  (The
+    // range needs no zero canonicalization: x - y is +0 for equal zeros.)
     float ze[8], sc[8], rc[8];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int j = 2 * k + h;
-            ze[j] = canon_zero(static_cast<float>(mn[k][h]));
-            const float range = canon_zero(static_cast<float>(mx[k][h])) - ze[j];
-            sc[j] = scale_of<BITS>(range);
-            rc[j] = recip_or_zero(sc[j]);
+            const float lo = static_cast<float>(mn[k][h]);
+            ze[j] = canon_zero(lo);
+            sc[j] = scale_of<BITS>(static_cast<float>(mx[k][h]) - lo);
+            rc[j] = recip_clamped(sc[j]);
         }
     }
 
-    const int64_t meta_off = bh * meta_bh_stride + (dst_token / kGroup + g) * kHeadDim + c * 8;
     if (r == 0) {
-        *reinterpret_cast<float4*>(scale + meta_off) = make_float4(sc[0], sc[1], sc[2], sc[3]);
-        *reinterpret_cast<float4*>(scale + meta_off + 4) = make_float4(sc[4], sc[5], sc[6], sc[7]);
+        *reinterpret_cast<float4*>(sct + c * 8) = make_float4(sc[0], sc[1], sc[2], sc[3]);
+        *reinterpret_cast<float4*>(sct + c * 8 + 4) = make_float4(sc[4], sc[5], sc[6], sc[7]);
     } else if (r == 1) {
-        *reinterpret_cast<float4*>(zero + meta_off) = make_float4(ze[0], ze[1], ze[2], ze[3]);
-        *reinterpret_cast<float4*>(zero + meta_off + 4) = make_float4(ze[4], ze[5], ze[6], ze[7]);
+        *reinterpret_cast<float4*>(zet + c * 8) = make_float4(ze[0], ze[1], ze[2], ze[3]);
+        *reinterpret_cast<float4*>(zet + c * 8 + 4) = make_float4(ze[4], ze[5], ze[6], ze[7]);
     }
 
-    uint32_t* cb = codes + bh * codes_bh_stride + dst_token * kWords;
 #pragma unroll
     for (int i = 0; i < kTokPerLane; ++i) {
-        const int64_t s = s0 + r + kRowsPerWave * i;
-        float f[8];
-        unpack8(raw[i], f);
-        uint32_t q[8];
-        bool near = false;
+        const int row = r + kRowsPerWave * i;
+        const half2_t hv[4] = {as_h2(raw[i].x), as_h2(raw[i].y), as_h2(raw[i].z), as_h2(raw[i].w)};
+        float t[8], qf[8];
+        float dev = 0.0f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            bool nj;
-            q[j] = quant_fast(f[j], ze[j], rc[j], nj);
-            near |= nj;
+            t[j] = sub_from_f16(hv[j >> 1][j & 1], one, ze[j]);
+            qf[j] = quant_fast(t[j], rc[j], dev);
         }
-        if (near) {                                // rare: within 2^-16 of a tie
+        if (dev > kNearTie) {                      // rare: within 2^-16 of a tie
 #pragma unroll
-            for (int j = 0; j < 8; ++j) q[j] = quant_exact(f[j], ze[j], sc[j]);
+            for (int j = 0; j < 8; ++j) qf[j] = quant_exact(t[j], sc[j]);
         }
-        uint32_t packed = q[0];
+        uint32_t packed = static_cast<uint32_t>(qf[0]);
 #pragma unroll
-        for (int j = 1; j < 8; ++j) packed |= q[j] << (BITS * j);
+        for (int j = 1; j < 8; ++j) packed |= static_cast<uint32_t>(qf[j]) << (BITS * j);
+        const bool live = !RAGGED || row < n_rows;
         if constexpr (BITS == 4) {
             // the lane's 8 channels are exactly one word
-            if (s < S) cb[s * kWords + c] = packed;
+            if (live) ct[row * kWords + c] = packed;
         } else {
             // 16 channels per word: the even lane takes its odd neighbour's half
             const uint32_t hi = quad_xor1(packed);
-            if (s < S && (c & 1) == 0) cb[s * kWords + (c >> 1)] = packed | (hi << 16);
+            if (live && (c & 1) == 0) ct[row * kWords + (c >> 1)] = packed | (hi << 16);
         }
         if constexpr (RECON) {
             uint32_t h[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) h[j] = recon_f16(q[j], sc[j], ze[j]);
-            if (s < S)
-                *reinterpret_cast<uint4*>(recon + bh * recon_bh_stride + s * kHeadDim + c * 8) = pack8(h);
+            for (int j = 0; j < 8; ++j) h[j] = recon_f16(qf[j], sc[j], ze[j]);
+            if (live) *reinterpret_cast<uint4*>(rt + row * kHeadDim + c * 8) = pack8(h);
         }
     }
+}
+
+template <int BITS, bool RECON>
+__global__ __launch_bounds__(kBlock) void key_flush_kernel(
+    const uint16_t* __restrict__ x, int64_t S, int64_t x_bh_stride,
+    uint32_t* __restrict__ codes, int64_t codes_bh_stride,
+    float* __restrict__ scale, float* __restrict__ zero, int64_t meta_bh_stride,
+    int64_t dst_token, uint16_t* __restrict__ recon, int64_t recon_bh_stride,
+    int64_t n_groups, int64_t n_tiles, float one)
+{
+    constexpr int kWords = kHeadDim * BITS / 32;
+    const int lane = threadIdx.x & 63;
+    const int64_t tile = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
+    if (tile >= n_tiles) return;                   // uniform across the wave
+    const int64_t bh = tile / n_groups;
+    const int64_t g = tile - bh * n_groups;
+    const int64_t s0 = g * kGroup;
+    const uint16_t* xt = x + bh * x_bh_stride + s0 * kHeadDim;
+    uint32_t* ct = codes + bh * codes_bh_stride + (dst_token + s0) * kWords;
+    const int64_t moff = bh * meta_bh_stride + (dst_token / kGroup + g) * kHeadDim;
+    uint16_t* rt = RECON ? recon + bh * recon_bh_stride + s0 * kHeadDim : nullptr;
+    const int64_t rows = S - s0;
+    if (rows >= kGroup)
+        key_tile<BITS, RECON, false>(xt, ct, scale + moff, zero + moff, rt, kGroup, lane, one);
+    else
+        key_tile<BITS, RECON, true>(xt, ct, scale + moff, zero + moff, rt, static_cast<int>(rows), lane, one);
 }
 
 // ---------------------------------------------------------------------------
 // Values: group = (bh, token s, channel group j) over channels [32j, 32j+32)
 // ---------------------------------------------------------------------------
+template <int BITS, bool RECON, bool RAGGED>
+__device__ __forceinline__ void value_tile(const uint16_t* __restrict__ xt, uint32_t* __restrict__ ct,
+                                           float* __restrict__ sct, float* __restrict__ zet,
+                                           uint16_t* __restrict__ rt, int n_rows, int lane, float one)
+{
+    constexpr int kWords = kHeadDim * BITS / 32;
+    constexpr int kMetaPerTok = kHeadDim / kGroup;  // 4 groups per token
+    const int c = lane & 15;
+    const int r = lane >> 4;
+    const int j = c >> 2;                           // channel group of this lane
+
+    uint4 raw[kTokPerLane];
+#pragma unroll
+    for (int i = 0; i < kTokPerLane; ++i) {
+        int row = r + kRowsPerWave * i;
+        if constexpr (RAGGED) row = row < n_rows ? row : n_rows - 1;   // keep every lane in the exchange
+        raw[i] = *reinterpret_cast<const uint4*>(xt + row * kHeadDim + c * 8);
+    }
+
+#pragma unroll
+    for (int i = 0; i < kTokPerLane; ++i) {
+        const int row = r + kRowsPerWave * i;
+        const half2_t hv[4] = {as_h2(raw[i].x), as_h2(raw[i].y), as_h2(raw[i].z), as_h2(raw[i].w)};
+        const half2_t mn2 = hmin(hmin3(hv[0], hv[1], hv[2]), hv[3]);
+        const half2_t mx2 = hmax(hmax3(hv[0], hv[1], hv[2]), hv[3]);
+        // (min, -max) of the lane in one register, then the 4 lanes of the
+        // group (a DPP quad) with min only
+        half2_t mm;
+        mm[0] = __builtin_elementwise_minimum(mn2[0], mn2[1]);
+        mm[1] = -__builtin_elementwise_maximum(mx2[0], mx2[1]);
+        mm = hmin(mm, as_h2(quad_xor1(as_u32(mm))));
+        mm = hmin(mm, as_h2(quad_xor2(as_u32(mm))));
+        const float lo = static_cast<float>(mm[0]);
+        const float hi = -static_cast<float>(mm[1]);
+        const float ze = canon_zero(lo);
+        const float sc = scale_of<BITS>(hi - lo);
+        const float rc = recip_clamped(sc);
+
+        float t[8], qf[8];
+        float dev = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            t[k] = sub_from_f16(hv[k >> 1][k & 1], one, ze);
+            qf[k] = quant_fast(t[k], rc, dev);
+        }
+        if (dev > kNearTie) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) qf[k] = quant_exact(t[k], sc);
+        }
+        uint32_t packed = static_cast<uint32_t>(qf[0]);
+#pragma unroll
+        for (int k = 1; k < 8; ++k) packed |= static_cast<uint32_t>(qf[k]) << (BITS * k);
+        const bool live = !RAGGED || row < n_rows;
+        if constexpr (BITS == 4) {
+            if (live) ct[row * kWords + c] = packed;
+        } else {
+            const uint32_t hw = quad_xor1(packed);
+            if (live && (c & 1) == 0) ct[row * kWords + (c >> 1)] = packed | (hw << 16);
+        }
+        if (live) {
+            if ((c & 3) == 0) sct[row * kMetaPerTok + j] = sc;
+            else if ((c & 3) == 1) zet[row * kMetaPerTok + j] = ze;
+        }
+        if constexpr (RECON) {
+            uint32_t h[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) h[k] = recon_f16(qf[k], sc, ze);
+            if (live) *reinterpret_cast<uint4*>(rt + row * kHeadDim + c * 8) = pack8(h);
+        }
+    }
+}
+
 template <int BITS, bool RECON>
 __global__ __launch_bounds__(kBlock) void value_flush_kernel(
     const uint16_t* __restrict__ x, int64_t S, int64_t x_bh_stride,
     uint32_t* __restrict__ codes, int64_t codes_bh_stride,
     float* __restrict__ scale, float* __restrict__ zero, int64_t meta_bh_stride,
     int64_t dst_token, uint16_t* __restrict__ recon, int64_t recon_bh_stride,
-    int64_t tiles_per_bh, int64_t n_tiles)
+    int64_t tiles_per_bh, int64_t n_tiles, float one)
 {
     constexpr int kWords = kHeadDim * BITS / 32;
-    constexpr int kMetaPerTok = kHeadDim / kGroup;  // 4 groups per token
+    constexpr int kMetaPerTok = kHeadDim / kGroup;
     const int lane = threadIdx.x & 63;
     const int64_t tile = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
     if (tile >= n_tiles) return;                    // uniform across the wave
-
     const int64_t bh = tile / tiles_per_bh;
     const int64_t s0 = (tile - bh * tiles_per_bh) * 32;
-    const int c = lane & 15;
-    const int r = lane >> 4;
-    const int j = c >> 2;                           // channel group of this lane
-
-    const uint16_t* xb = x + bh * x_bh_stride + c * 8;
-    uint32_t* cb = codes + bh * codes_bh_stride + dst_token * kWords;
-    float* scb = scale + bh * meta_bh_stride + dst_token * kMetaPerTok;
-    float* zeb = zero + bh * meta_bh_stride + dst_token * kMetaPerTok;
-
-    uint4 raw[kTokPerLane];
-#pragma unroll
-    for (int i = 0; i < kTokPerLane; ++i) {
-        const int64_t s = s0 + r + kRowsPerWave * i;
-        const int64_t sl = s < S ? s : S - 1;       // keep every lane in the exchange
-        raw[i] = *reinterpret_cast<const uint4*>(xb + sl * kHeadDim);
-    }
-
-#pragma unroll
-    for (int i = 0; i < kTokPerLane; ++i) {
-        const int64_t s = s0 + r + kRowsPerWave * i;
-        const half2_t a = as_h2(raw[i].x), b = as_h2(raw[i].y), cc = as_h2(raw[i].z), d = as_h2(raw[i].w);
-        half2_t mn = hmin(hmin3(a, b, cc), d);
-        half2_t mx = hmax(hmax3(a, b, cc), d);
-        // the 4 lanes of one group are a DPP quad
-        mn = hmin(mn, as_h2(quad_xor1(as_u32(mn))));
-        mx = hmax(mx, as_h2(quad_xor1(as_u32(mx))));
-        mn = hmin(mn, as_h2(quad_xor2(as_u32(mn))));
-        mx = hmax(mx, as_h2(quad_xor2(as_u32(mx))));
-        const float ze = canon_zero(fminf(static_cast<float>(mn[0]), static_cast<float>(mn[1])));
-        const float range = canon_zero(fmaxf(static_cast<float>(mx[0]), static_cast<float>(mx[1]))) - ze;
-        const float sc = scale_of<BITS>(range);
-        const float rc = recip_or_zero(sc);
-
-        float f[8];
-        unpack8(raw[i], f);
-        uint32_t q[8];
-        bool near = false;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            bool nk;
-            q[k] = quant_fast(f[k], ze, rc, nk);
-            near |= nk;
-        }
-        if (near) {
-#pragma unroll
-            for (int k = 0; k < 8; ++k) q[k] = quant_exact(f[k], ze, sc);
-        }
-        uint32_t packed = q[0];
-#pragma unroll
-        for (int k = 1; k < 8; ++k) packed |= q[k] << (BITS * k);
-        if constexpr (BITS == 4) {
-            if (s < S) cb[s * kWords + c] = packed;
-        } else {
-            const uint32_t hi = quad_xor1(packed);
-            if (s < S && (c & 1) == 0) cb[s * kWords + (c >> 1)] = packed | (hi << 16);
-        }
-        if (s < S) {
-            if ((c & 3) == 0) scb[s * kMetaPerTok + j] = sc;
-            else if ((c & 3) == 1) zeb[s * kMetaPerTok + j] = ze;
-        }
-        if constexpr (RECON) {
-            uint32_t h[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) h[k] = recon_f16(q[k], sc, ze);
-            if (s < S)
-                *reinterpret_cast<uint4*>(recon + bh * recon_bh_stride + s * kHeadDim + c * 8) = pack8(h);
-        }
-    }
+    const uint16_t* xt = x + bh * x_bh_stride + s0 * kHeadDim;
+    uint32_t* ct = codes + bh * codes_bh_stride + (dst_token + s0) * kWords;
+    const int64_t moff = bh * meta_bh_stride + (dst_token + s0) * kMetaPerTok;
+    uint16_t* rt = RECON ? recon + bh * recon_bh_stride + s0 * kHeadDim : nullptr;
+    const int64_t rows = S - s0;
+    if (rows >= 32)
+        value_tile<BITS, RECON, false>(xt, ct, scale + moff, zero + moff, rt, 32, lane, one);
+    else
+        value_tile<BITS, RECON, true>(xt, ct, scale + moff, zero + moff, rt, static_cast<int>(rows), lane, one);
 }
 
 // ---------------------------------------------------------------------------
@@ -234,7 +261,7 @@ static hipError_t launch_keys_t(const FlushArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((key_flush_kernel<BITS, RECON>), dim3(static_cast<uint32_t>(blocks)),
                        dim3(kBlock), 0, stream, a.x, a.S, a.x_bh_stride, a.codes,
                        a.codes_bh_stride, a.scale, a.zero, a.meta_bh_stride, a.dst_token,
-                       a.recon, a.recon_bh_stride, n_groups, n_tiles);
+                       a.recon, a.recon_bh_stride, n_groups, n_tiles, 1.0f);
     return hipGetLastError();
 }
 
@@ -246,7 +273,7 @@ static hipError_t launch_values_t(const FlushArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((value_flush_kernel<BITS, RECON>), dim3(static_cast<uint32_t>(blocks)),
                        dim3(kBlock), 0, stream, a.x, a.S, a.x_bh_stride, a.codes,
                        a.codes_bh_stride, a.scale, a.zero, a.meta_bh_stride, a.dst_token,
-                       a.recon, a.recon_bh_stride, tiles_per_bh, n_tiles);
+                       a.recon, a.recon_bh_stride, tiles_per_bh, n_tiles, 1.0f);
     return hipGetLastError();
 }
 

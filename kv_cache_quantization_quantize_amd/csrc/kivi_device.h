@@ -112,62 +112,58 @@ __device__ __forceinline__ float scale_of(float range) {
 // 1/s to within 2^-22 relative: hardware reciprocal r0 plus one Newton step
 // e = RN(1 - s*r0), r1 = RN(r0 + r0*e).  The step squares r0's relative
 // error (any r0 within 2^-12 leaves at most 2^-24) and its two roundings add
-// at most 2^-23.  0 for a constant group, so its quotients are exactly 0.
-__device__ __forceinline__ float recip_or_zero(float s) {
-    const float r0 = __builtin_amdgcn_rcpf(s);
-    const float e = __builtin_fmaf(-s, r0, 1.0f);
-    const float r1 = __builtin_fmaf(r0, e, r0);
-    return s == 0.0f ? 0.0f : r1;
+// at most 2^-23.  A constant group (s = 0) gets r = 2^126 from the clamp, and
+// all its t are 0, so its products are exactly 0 (no 0 * inf).  Every
+// non-zero scale is >= 2^-24/15 > 2^-126, so the clamp changes nothing else.
+__device__ __forceinline__ float recip_clamped(float s) {
+    const float sc = fmaxf(s, 0x1p-126f);
+    const float r0 = __builtin_amdgcn_rcpf(sc);
+    const float e = __builtin_fmaf(-sc, r0, 1.0f);
+    return __builtin_fmaf(r0, e, r0);
 }
 
-// Code of one element on the fast path: rint(t * r) with t = x - zero.
+// t = x - zero from the fp16 input in one mixed-precision FMA.  `one` is a
+// kernel argument equal to 1.0f: x*1 is exact, so this is the IEEE
+// subtraction of the widened input (the compiler would fold a literal 1.0
+// into a separate conversion and subtraction).
+__device__ __forceinline__ float sub_from_f16(_Float16 x, float one, float zero) {
+    return __builtin_fmaf(static_cast<float>(x), one, -zero);
+}
+
+// Code of one element on the fast path: q = rint(t * r), and |y - q| is folded
+// into `dev` (the largest distance of the row's quotients from their integer).
 //
-// Why it equals rint(fl(t / s)) unless `near` is set.  With |r - 1/s| <=
-// 2^-22/s, y = RN(t*r) and z = t/s < 16:
+// Why q equals rint(fl(t / s)) when every |y - q| <= 1/2 - 2^-16.  With
+// |r - 1/s| <= 2^-22/s, y = RN(t*r) and z = t/s < 16:
 //   |y - z| <= z (2^-22 + 2^-24) (1 + 2^-22),  |fl(z) - z| <= z 2^-24,
 // so |y - fl(z)| < 16 * 1.51 * 2^-22 < 2^-17.  rint only changes value at
 // half-integers, so if y is farther than 2^-16 from every half-integer,
-// y and fl(z) round to the same integer; otherwise `near` is set and the
-// caller recomputes the code with the IEEE quotient.  (y - q is exact:
-// q = rint(y) is within half of y.)  The code needs no clip: 0 <= t <=
-// range (rounding is monotone) and s >= (range/L)(1 - 2^-24) bound y by
-// L (1 + 2^-21) < L + 1/2.
-__device__ __forceinline__ uint32_t quant_fast(float x, float zero, float r, bool& near) {
-    const float t = x - zero;
+// y and fl(z) round to the same integer; otherwise the caller recomputes the
+// row with the IEEE quotient.  (y - q is exact: q = rint(y) is within half
+// of y.)  The code needs no clip: 0 <= t <= range (rounding is monotone) and
+// s >= (range/L)(1 - 2^-24) bound y by L (1 + 2^-21) < L + 1/2.
+__device__ __forceinline__ float quant_fast(float t, float r, float& dev) {
     const float y = t * r;
     const float q = __builtin_rintf(y);
-    near = __builtin_fabsf(y - q) > 0.5f - 0x1p-16f;
-    return static_cast<uint32_t>(q);
+    dev = fmaxf(dev, __builtin_fabsf(y - q));
+    return q;
 }
+constexpr float kNearTie = 0.5f - 0x1p-16f;
 
-// The same code with the IEEE quotient (the oracle's exact steps).
-__device__ __forceinline__ uint32_t quant_exact(float x, float zero, float s) {
-    if (s == 0.0f) return 0u;
-    return static_cast<uint32_t>(__builtin_rintf((x - zero) / s));
+// The same code with the IEEE quotient (the oracle's exact steps); t = x - zero.
+__device__ __forceinline__ float quant_exact(float t, float s) {
+    if (s == 0.0f) return 0.0f;
+    return __builtin_rintf(t / s);
 }
 
 // A zero extreme is stored as +0, so the result does not depend on which
-// signed zero a reduction kept.
-__device__ __forceinline__ float canon_zero(float v) { return v == 0.0f ? 0.0f : v; }
-
-// Code of one element: clip(rint((x - zero) / scale), 0, levels), with code 0
-// for a constant group (scale 0).  Two IEEE roundings (subtract, divide),
-// then round-half-even.
-template <int BITS>
-__device__ __forceinline__ uint32_t quant_code(float x, float zero, float scale) {
-    constexpr float kLevels = static_cast<float>((1 << BITS) - 1);
-    if (scale == 0.0f) return 0u;
-    const float t = x - zero;
-    const float u = t / scale;
-    float r = __builtin_rintf(u);
-    r = r < 0.0f ? 0.0f : r;
-    r = r > kLevels ? kLevels : r;
-    return static_cast<uint32_t>(r);
-}
+// signed zero a reduction kept: -0 + 0 = +0 in round-to-nearest, and v + 0 = v
+// for every other v.
+__device__ __forceinline__ float canon_zero(float v) { return v + 0.0f; }
 
 // Reconstruction fp16_rne(fl(fl(q * scale) + zero)) -- two roundings, no FMA.
-__device__ __forceinline__ uint32_t recon_f16(uint32_t q, float scale, float zero) {
-    const float prod = static_cast<float>(q) * scale;
+__device__ __forceinline__ uint32_t recon_f16(float q, float scale, float zero) {
+    const float prod = q * scale;
     const float sum = prod + zero;
     return f32_to_f16(sum);
 }
