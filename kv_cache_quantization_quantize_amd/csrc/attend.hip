@@ -43,6 +43,10 @@ union Frag {
     uint32_t u[4];
 };
 
+#ifndef KIVI_ATTEND_OCCUPANCY
+#define KIVI_ATTEND_OCCUPANCY
+#endif
+
 constexpr int kStep = 32;             // tokens per wave step (one key group)
 constexpr int kMaxStepsPerWave = 32;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -63,16 +67,21 @@ constexpr uint32_t kMagic = 0x64006400u;   // fp16 1024.0 in both halves
 // Four fp16 pairs (1024 + code[j], 1024 + code[j+4]), j = 0..3, from the 8
 // codes of one 8-channel unit.  4-bit: one code word.  2-bit: the unit's
 // half of a word, spread to bytes 0 and 2 first.
+// (x & mask) | magic in one v_bitop3_b32 (truth table 0xEA = (a & b) | c).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t magic) {
+    return __builtin_amdgcn_bitop3_b32(x, mask, magic, 0xEA);
+}
+
 template <int BITS>
 __device__ __forceinline__ void code_pairs(uint32_t w, int half, uint32_t (&p)[4]) {
     if constexpr (BITS == 4) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) p[j] = ((w >> (4 * j)) & 0x000F000Fu) | kMagic;
+        for (int j = 0; j < 4; ++j) p[j] = and_or(w >> (4 * j), 0x000F000Fu, kMagic);
     } else {
         const uint32_t sel = half ? 0x0C030C02u : 0x0C010C00u;
         const uint32_t s = __builtin_amdgcn_perm(w, w, sel);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) p[j] = ((s >> (2 * j)) & 0x00030003u) | kMagic;
+        for (int j = 0; j < 4; ++j) p[j] = and_or(s >> (2 * j), 0x00030003u, kMagic);
     }
 }
 
@@ -80,16 +89,16 @@ __device__ __forceinline__ void code_pairs(uint32_t w, int half, uint32_t (&p)[4
 // c16 = 1024 + code exactly and zp = RN32(zero - 1024 s), so the result is
 // code*s + zero up to 2^-24 (|zero| + 1024 s) plus the fp16 rounding (the
 // attend is checked against the float64 definition to 2e-3, not bit-exactly).
-__device__ __forceinline__ _Float16 deq(uint32_t pair, int hi, float s, float zp) {
+// Both halves of one fp16 pair register: lo = fma(c.lo, s0, z0), hi =
+// fma(c.hi, s1, z1), each rounded to fp16.  Written in C, not inline asm, so
+// the compiler sees the register writes and keeps the wait states an MFMA
+// needs after a VALU write of its operands.
+__device__ __forceinline__ uint32_t deq2(uint32_t pair, float s0, float z0, float s1, float z1) {
     const half2_t c = as_h2(pair);
-    return static_cast<_Float16>(__builtin_fmaf(static_cast<float>(hi ? c[1] : c[0]), s, zp));
-}
-
-__device__ __forceinline__ uint32_t pack_h2(_Float16 lo, _Float16 hi) {
-    half2_t v;
-    v[0] = lo;
-    v[1] = hi;
-    return as_u32(v);
+    half2_t r;
+    r[0] = static_cast<_Float16>(__builtin_fmaf(static_cast<float>(c[0]), s0, z0));
+    r[1] = static_cast<_Float16>(__builtin_fmaf(static_cast<float>(c[1]), s1, z1));
+    return as_u32(r);
 }
 
 // lane exchanges across the four 16-lane rows (see kivi_device.h)
@@ -107,14 +116,13 @@ __device__ __forceinline__ float rows_sum(float v) {
 }
 
 // Global loads of one 32-token step of store tokens, issued one step ahead of
-// the compute that uses them.  Token indices are clamped into the store, so
-// every load is in bounds; lanes whose token is past n_quant ignore them.
-template <int BITS>
+// the compute that uses them.  Token indices are clamped to the last store
+// token, so every load is in bounds; masked tokens get zero probability.
 struct StepLoad {
-    uint32_t kw[2][4];      // key codes of token t0 + 16*blk + n (lane's 32 channels)
+    uint32_t kw[2][4];      // key code words of token t0 + 16*blk + n (lane's 32 channels)
     float2 ks, kz;          // key scale / zero of channels 2l, 2l+1 of the step's group
-    float2 vs, vz;          // value scale / zero, token t0 + (l & 31), groups 2(l>>5), +1
-    uint32_t vw[8];         // value code word of the lane's 8 channels, its 8 tokens
+    float2 vs, vz;          // value scale / zero of token t0 + (l & 31), groups 2(l>>5), +1
+    uint32_t vw[8];         // value code word holding the lane's 8 channels, its 8 tokens
 };
 
 // Token (within the step) of PV slot s for lane group q: the order in which
@@ -122,18 +130,14 @@ struct StepLoad {
 __device__ __forceinline__ int pv_token(int q, int s) { return 16 * (s >> 2) + 4 * q + (s & 3); }
 
 template <int BITS>
-__device__ __forceinline__ void issue_step(StepLoad<BITS>& L, const AttendArgs& a, int64_t t0,
-                                           const uint32_t* kc, const float* ksc, const float* kze,
-                                           const uint32_t* vc, const float* vsc, const float* vze,
-                                           int l, int n, int q) {
+__device__ __forceinline__ void issue_step(StepLoad& L, int t0, int last, const uint32_t* kc,
+                                           const float* ksc, const float* kze, const uint32_t* vc,
+                                           const float* vsc, const float* vze, int l, int n, int q) {
     constexpr int kWords = kHeadDim * BITS / 32;
     constexpr int kMetaPerTok = kHeadDim / kGroup;
-    if (t0 >= a.n_quant) return;                  // uniform: residual-only step
-    const int64_t last = a.n_quant - 1;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-        int64_t tok = t0 + 16 * blk + n;
-        tok = tok < last ? tok : last;
+        const int tok = min(t0 + 16 * blk + n, last);
         if constexpr (BITS == 4) {
             const uint4 t = *reinterpret_cast<const uint4*>(kc + tok * kWords + 4 * q);
             L.kw[blk][0] = t.x; L.kw[blk][1] = t.y; L.kw[blk][2] = t.z; L.kw[blk][3] = t.w;
@@ -142,19 +146,19 @@ __device__ __forceinline__ void issue_step(StepLoad<BITS>& L, const AttendArgs& 
             L.kw[blk][0] = t.x; L.kw[blk][1] = t.x; L.kw[blk][2] = t.y; L.kw[blk][3] = t.y;
         }
     }
-    const int64_t g = t0 / kGroup;
+    const int g = t0 / kGroup;
     L.ks = *reinterpret_cast<const float2*>(ksc + g * kHeadDim + 2 * l);
     L.kz = *reinterpret_cast<const float2*>(kze + g * kHeadDim + 2 * l);
-    int64_t tv = t0 + (l & 31);
-    tv = tv < last ? tv : last;
+    const int tv = min(t0 + (l & 31), last);
     L.vs = *reinterpret_cast<const float2*>(vsc + tv * kMetaPerTok + 2 * (l >> 5));
     L.vz = *reinterpret_cast<const float2*>(vze + tv * kMetaPerTok + 2 * (l >> 5));
     const int word = BITS == 4 ? n : (n >> 1);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-        int64_t tok = t0 + pv_token(q, s);
-        tok = tok < last ? tok : last;
-        L.vw[s] = vc[tok * kWords + word];
+        const int tok = min(t0 + pv_token(q, s), last);
+        const uint32_t w = vc[tok * kWords + word];
+        // 2-bit: bring the lane's 8 channels (half of the word) to the low half
+        L.vw[s] = BITS == 4 ? w : (w >> (16 * (n & 1)));
     }
 }
 
@@ -164,11 +168,17 @@ __device__ __forceinline__ void issue_step(StepLoad<BITS>& L, const AttendArgs& 
 // later read.
 __device__ __forceinline__ void lds_order() { __atomic_signal_fence(__ATOMIC_SEQ_CST); }
 
+// Rows are padded so that lanes reading different channel windows or groups
+// in the same LDS cycle hit different banks.
+constexpr int kKPad = 4;                      // floats of padding per 32 channels
+constexpr int kVRow = kStep + 4;              // padded row of 32 tokens
+__device__ __forceinline__ int kidx(int ch) { return ch + kKPad * (ch >> 5); }
+
 struct Smem {
-    float ks[kHeadDim];                       // key scale of the step's group
-    float kz[kHeadDim];                       // key zero - 1024 * scale
-    float vs[kHeadDim / kGroup][kStep];       // value scale, [group][token]
-    float vz[kHeadDim / kGroup][kStep];       // value zero - 1024 * scale
+    alignas(16) float ks[kHeadDim + kKPad * 4];       // key scale of the step's group
+    alignas(16) float kz[kHeadDim + kKPad * 4];       // key zero - 1024 * scale
+    alignas(16) float vs[kHeadDim / kGroup][kVRow];   // value scale, [group][token]
+    alignas(16) float vz[kHeadDim / kGroup][kVRow];   // value zero - 1024 * scale
 };
 
 // Online-softmax state of one lane: head n, channels 32q + 8r + i of acc_o[i][r].
@@ -178,101 +188,45 @@ struct SoftState {
     float4_t acc_o[8];
 };
 
-template <int BITS>
-__device__ __forceinline__ void process_step(const StepLoad<BITS>& L, Smem& sm, SoftState& st,
-                                             const Frag (&bq)[4], const AttendArgs& a, int64_t t0,
-                                             int64_t j1, const uint16_t* kr, const uint16_t* vr,
-                                             float c2, int l, int n, int q) {
-    const int64_t N = a.n_quant + a.n_res;
-    // ---- stage this step's metadata in LDS
-    if (t0 < a.n_quant) {
-        lds_order();
-        sm.ks[2 * l] = L.ks.x;
-        sm.ks[2 * l + 1] = L.ks.y;
-        sm.kz[2 * l] = __builtin_fmaf(-1024.0f, L.ks.x, L.kz.x);
-        sm.kz[2 * l + 1] = __builtin_fmaf(-1024.0f, L.ks.y, L.kz.y);
-        const int tt = l & 31;
-        const int gg = (l >> 5) * 2;
-        sm.vs[gg][tt] = L.vs.x;
-        sm.vs[gg + 1][tt] = L.vs.y;
-        sm.vz[gg][tt] = __builtin_fmaf(-1024.0f, L.vs.x, L.vz.x);
-        sm.vz[gg + 1][tt] = __builtin_fmaf(-1024.0f, L.vs.y, L.vz.y);
-        lds_order();
-    }
+// The running max m only moves when a step's max exceeds it by more than
+// kSlack (base 2), so most steps skip rescaling the accumulators; the
+// unnormalized probabilities stay <= 2^kSlack = 256, exact enough in fp16
+// (relative precision is unchanged) and far from its range limit.
+constexpr float kSlack = 8.0f;
 
-    // ---- S^T = K Q^T for the two 16-token blocks (token t0 + 16*blk + n)
-    float4_t acc_s[2];
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-        acc_s[blk] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        const int64_t tok = t0 + 16 * blk + n;
-        Frag ka[4];
-        if (tok < a.n_quant) {
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                uint32_t pr[4];
-                code_pairs<BITS>(L.kw[blk][kb], kb & 1, pr);
-                const int cb = 32 * q + 8 * kb;
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    ka[kb].u[j] = pack_h2(deq(pr[j], 0, sm.ks[cb + j], sm.kz[cb + j]),
-                                          deq(pr[j], 1, sm.ks[cb + j + 4], sm.kz[cb + j + 4]));
-            }
-        } else if (tok < N) {
-            const uint4* src = reinterpret_cast<const uint4*>(kr + (tok - a.n_quant) * kHeadDim + 32 * q);
-            uint32_t rn[16];
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const uint4 t = src[v];
-                rn[4 * v] = t.x; rn[4 * v + 1] = t.y; rn[4 * v + 2] = t.z; rn[4 * v + 3] = t.w;
-            }
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int c0 = 8 * kb + j, c1 = 8 * kb + j + 4;
-                    const uint32_t s0 = (c0 & 1) ? 0x0302u : 0x0100u;
-                    const uint32_t s1 = (c1 & 1) ? 0x0706u : 0x0504u;
-                    ka[kb].u[j] = __builtin_amdgcn_perm(rn[c1 >> 1], rn[c0 >> 1], (s1 << 16) | s0);
-                }
-        } else {
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) ka[kb].u[j] = 0u;
-        }
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-            acc_s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[kb].h, bq[kb].h, acc_s[blk], 0, 0, 0);
-    }
-
-    // ---- online softmax (base 2).  Lane (q, n) holds head n's scores of
-    // tokens t0 + 16*blk + 4q + r, r = 0..3.
+// Online softmax over one step's scores (base 2) and the PV B operand.
+// Lane (q, n) holds head n's scores of step tokens 16*blk + 4q + r; with
+// MASK, tokens at or past `limit` (step-relative) get probability 0.
+template <bool MASK>
+__device__ __forceinline__ Frag softmax_step(const float4_t (&acc_s)[2], SoftState& st, float c2,
+                                             int limit, int q) {
     float sv[8];
     float mloc = -INFINITY;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int64_t tok = t0 + 16 * blk + 4 * q + r;
-            const float sc = tok < j1 ? acc_s[blk][r] * c2 : -INFINITY;
+            float sc = acc_s[blk][r] * c2;
+            if constexpr (MASK) sc = (16 * blk + 4 * q + r) < limit ? sc : -INFINITY;
             sv[4 * blk + r] = sc;
             mloc = fmaxf(mloc, sc);
         }
-    const float m_new = fmaxf(st.m_run, rows_max(mloc));
-    const float alpha = exp2f(st.m_run - m_new);
+    const float m_step = rows_max(mloc);
+    const float m_new = m_step > st.m_run + kSlack ? m_step : st.m_run;
+    const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);   // 1 when m did not move
     st.m_run = m_new;
     float psum = 0.0f;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-        sv[s] = exp2f(sv[s] - m_new);
+        sv[s] = __builtin_amdgcn_exp2f(sv[s] - m_new);
         psum += sv[s];
     }
     st.l_part = __builtin_fmaf(st.l_part, alpha, psum);
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) st.acc_o[i] *= alpha;
-    // B operand of PV: P^T, slot s <-> token t0 + pv_token(q, s)
-    Frag bp;
+        for (int i = 0; i < 8; ++i) st.acc_o[i] *= alpha;
+    }
+    Frag bp;                                  // P^T, slot s <-> step token pv_token(q, s)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         half2_t h;
@@ -280,74 +234,155 @@ __device__ __forceinline__ void process_step(const StepLoad<BITS>& L, Smem& sm, 
         h[1] = static_cast<_Float16>(sv[2 * j + 1]);
         bp.u[j] = as_u32(h);
     }
+    return bp;
+}
 
-    // ---- V rows: lane (q, m=n) takes channels 8n .. 8n+7 of its 8 tokens
-    Frag vrow[8];
-    const int vg = n >> 2;
+__device__ __forceinline__ Frag softmax_any(const float4_t (&acc_s)[2], SoftState& st, float c2,
+                                            int limit, int q) {
+    if (limit >= kStep) return softmax_step<false>(acc_s, st, c2, limit, q);
+    return softmax_step<true>(acc_s, st, c2, limit, q);
+}
+
+// One step of store tokens [t0, t0 + 32), tokens at or past n_quant masked.
+template <int BITS>
+__device__ __forceinline__ void store_step(const StepLoad& L, Smem& sm, SoftState& st,
+                                           const Frag (&bq)[4], int t0, int n_quant, float c2,
+                                           int l, int n, int q) {
+    // ---- stage this step's metadata in LDS (zero' = zero - 1024 * scale)
+    lds_order();
+    *reinterpret_cast<float2*>(&sm.ks[kidx(2 * l)]) = L.ks;
+    *reinterpret_cast<float2*>(&sm.kz[kidx(2 * l)]) =
+        make_float2(__builtin_fmaf(-1024.0f, L.ks.x, L.kz.x), __builtin_fmaf(-1024.0f, L.ks.y, L.kz.y));
+    {
+        const int tt = l & 31;
+        const int gg = (l >> 5) * 2;
+        sm.vs[gg][tt] = L.vs.x;
+        sm.vs[gg + 1][tt] = L.vs.y;
+        sm.vz[gg][tt] = __builtin_fmaf(-1024.0f, L.vs.x, L.vz.x);
+        sm.vz[gg + 1][tt] = __builtin_fmaf(-1024.0f, L.vs.y, L.vz.y);
+    }
+    lds_order();
+
+    // ---- S^T = K Q^T, token t0 + 16*blk + n, channel unit kb of group q
+    float4_t acc_s[2] = {float4_t{0.0f, 0.0f, 0.0f, 0.0f}, float4_t{0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-        const int tl = pv_token(q, s);
-        const int64_t tok = t0 + tl;
-        if (tok < a.n_quant) {
+    for (int kb = 0; kb < 4; ++kb) {
+        const int cb = kidx(32 * q + 8 * kb);
+        const float4 s0 = *reinterpret_cast<const float4*>(&sm.ks[cb]);
+        const float4 s1 = *reinterpret_cast<const float4*>(&sm.ks[cb + 4]);
+        const float4 z0 = *reinterpret_cast<const float4*>(&sm.kz[cb]);
+        const float4 z1 = *reinterpret_cast<const float4*>(&sm.kz[cb + 4]);
+        const float sl[4] = {s0.x, s0.y, s0.z, s0.w}, sh[4] = {s1.x, s1.y, s1.z, s1.w};
+        const float zl[4] = {z0.x, z0.y, z0.z, z0.w}, zh[4] = {z1.x, z1.y, z1.z, z1.w};
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
             uint32_t pr[4];
-            code_pairs<BITS>(L.vw[s], n & 1, pr);
-            const float sc = sm.vs[vg][tl];
-            const float zp = sm.vz[vg][tl];
+            code_pairs<BITS>(L.kw[blk][kb], kb & 1, pr);
+            Frag ka;
 #pragma unroll
-            for (int v = 0; v < 4; ++v)               // natural order: channels 2v, 2v+1
-                vrow[s].u[v] = pack_h2(deq(pr[(2 * v) & 3], (2 * v) >> 2, sc, zp),
-                                       deq(pr[(2 * v + 1) & 3], (2 * v + 1) >> 2, sc, zp));
-        } else if (tok < N) {
-            const uint4 t = *reinterpret_cast<const uint4*>(vr + (tok - a.n_quant) * kHeadDim + 8 * n);
-            vrow[s].u[0] = t.x; vrow[s].u[1] = t.y; vrow[s].u[2] = t.z; vrow[s].u[3] = t.w;
-        } else {
-#pragma unroll
-            for (int v = 0; v < 4; ++v) vrow[s].u[v] = 0u;
+            for (int j = 0; j < 4; ++j) ka.u[j] = deq2(pr[j], sl[j], zl[j], sh[j], zh[j]);
+            acc_s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka.h, bq[kb].h, acc_s[blk], 0, 0, 0);
         }
     }
-    // ---- O^T += V^T P^T: MFMA i covers channels 8m + i, m = 0..15
+
+    const Frag bp = softmax_any(acc_s, st, c2, n_quant - t0, q);
+
+    // ---- O^T += V^T P^T: MFMA i covers channels 8m + i, m = 0..15.  Slot s of
+    // lane (q, m) is channel 8m + i of step token pv_token(q, s).
+    const int vg = n >> 2;
+    const float4 vsa = *reinterpret_cast<const float4*>(&sm.vs[vg][4 * q]);
+    const float4 vsb = *reinterpret_cast<const float4*>(&sm.vs[vg][16 + 4 * q]);
+    const float4 vza = *reinterpret_cast<const float4*>(&sm.vz[vg][4 * q]);
+    const float4 vzb = *reinterpret_cast<const float4*>(&sm.vz[vg][16 + 4 * q]);
+    const float vsc[8] = {vsa.x, vsa.y, vsa.z, vsa.w, vsb.x, vsb.y, vsb.z, vsb.w};
+    const float vzp[8] = {vza.x, vza.y, vza.z, vza.w, vzb.x, vzb.y, vzb.z, vzb.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        // code of channel i of the lane's 8 (4-bit: nibble i; 2-bit: field i)
+        constexpr uint32_t kMask = BITS == 4 ? 0x000F000Fu : 0x00030003u;
+        const uint32_t byte = BITS == 4 ? (i >> 1) : (i >> 2);
+        const uint32_t shift = BITS == 4 ? 4 * (i & 1) : 2 * (i & 3);
+        const uint32_t sel = 0x0C000C00u | ((4u + byte) << 16) | byte;
+        Frag va;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t x = __builtin_amdgcn_perm(L.vw[2 * j + 1], L.vw[2 * j], sel);
+            const uint32_t pr = and_or(x >> shift, kMask, kMagic);
+            va.u[j] = deq2(pr, vsc[2 * j], vzp[2 * j], vsc[2 * j + 1], vzp[2 * j + 1]);
+        }
+        st.acc_o[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va.h, bp.h, st.acc_o[i], 0, 0, 0);
+    }
+}
+
+// One step of fp16 residual tokens [t0, t0 + 32), tokens at or past n_res masked.
+__device__ __forceinline__ void residual_step(const uint16_t* kr, const uint16_t* vr, SoftState& st,
+                                              const Frag (&bq)[4], int t0, int n_res, float c2,
+                                              int n, int q) {
+    const int last = n_res - 1;
+    float4_t acc_s[2] = {float4_t{0.0f, 0.0f, 0.0f, 0.0f}, float4_t{0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+        const int tok = min(t0 + 16 * blk + n, last);
+        const uint4* src = reinterpret_cast<const uint4*>(kr + tok * kHeadDim + 32 * q);
+        uint32_t rn[16];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const uint4 t = src[v];
+            rn[4 * v] = t.x; rn[4 * v + 1] = t.y; rn[4 * v + 2] = t.z; rn[4 * v + 3] = t.w;
+        }
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            Frag ka;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int c0 = 8 * kb + j, c1 = 8 * kb + j + 4;
+                const uint32_t s0 = (c0 & 1) ? 0x0302u : 0x0100u;
+                const uint32_t s1 = (c1 & 1) ? 0x0706u : 0x0504u;
+                ka.u[j] = __builtin_amdgcn_perm(rn[c1 >> 1], rn[c0 >> 1], (s1 << 16) | s0);
+            }
+            acc_s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka.h, bq[kb].h, acc_s[blk], 0, 0, 0);
+        }
+    }
+    const Frag bp = softmax_any(acc_s, st, c2, n_res - t0, q);
+    // V rows: lane (q, m=n) takes channels 8n .. 8n+7 of its 8 tokens
+    uint4 vrow[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        const int tok = min(t0 + pv_token(q, s), last);
+        vrow[s] = *reinterpret_cast<const uint4*>(vr + tok * kHeadDim + 8 * n);
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         Frag va;
         const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            va.u[j] = __builtin_amdgcn_perm(vrow[2 * j + 1].u[i >> 1], vrow[2 * j].u[i >> 1], sel);
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t* a0 = reinterpret_cast<const uint32_t*>(&vrow[2 * j]);
+            const uint32_t* a1 = reinterpret_cast<const uint32_t*>(&vrow[2 * j + 1]);
+            va.u[j] = __builtin_amdgcn_perm(a1[i >> 1], a0[i >> 1], sel);
+        }
         st.acc_o[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va.h, bp.h, st.acc_o[i], 0, 0, 0);
     }
 }
 
-// One wave: sequence b, kv head kv, steps_per_wave 32-token steps starting at
-// split * steps_per_wave * 32 of [store tokens 0..n_quant-1 ; residual 0..n_res-1].
+// One wave: sequence b, kv head kv, one split.  Splits [0, n_split_q) cover
+// store tokens [0, n_quant) in runs of spw_q steps of 32 tokens; the rest
+// cover residual tokens [0, n_res) in runs of spw_r steps.  Slab offsets fit
+// in 32 bits (the ABI bounds every slab below 2^31 elements).
 template <int BITS, int GQA>
-__global__ __launch_bounds__(64) void attend_partial_kernel(const AttendArgs a, int64_t steps_per_wave,
-                                                            int64_t n_split, float* __restrict__ ws_o,
+__global__ __launch_bounds__(64) KIVI_ATTEND_OCCUPANCY void attend_partial_kernel(const AttendArgs a, int spw_q, int n_split_q,
+                                                            int spw_r, int64_t n_split, float* __restrict__ ws_o,
                                                             float* __restrict__ ws_ml)
 {
     __shared__ Smem sm;
     const int l = threadIdx.x;
     const int n = l & 15;
     const int q = l >> 4;
-    const int64_t split = blockIdx.x;
+    const int split = blockIdx.x;
     const int64_t bkv = blockIdx.y;
     const int64_t b = bkv / a.Hkv;
     const int kv = static_cast<int>(bkv - b * a.Hkv);
-    const int64_t N = a.n_quant + a.n_res;
-    const int64_t j0 = split * steps_per_wave * kStep;
-    const int64_t j1 = (j0 + steps_per_wave * kStep < N) ? j0 + steps_per_wave * kStep : N;
     const int64_t qrow0 = b * a.Hq + static_cast<int64_t>(kv) * GQA;
-
-    const uint32_t* kc = a.k_codes + bkv * a.k_codes_bh_stride;
-    const float* ksc = a.k_scale + bkv * a.k_meta_bh_stride;
-    const float* kze = a.k_zero + bkv * a.k_meta_bh_stride;
-    const uint32_t* vc = a.v_codes + bkv * a.v_codes_bh_stride;
-    const float* vsc = a.v_scale + bkv * a.v_meta_bh_stride;
-    const float* vze = a.v_zero + bkv * a.v_meta_bh_stride;
-    const uint16_t* kr = a.k_res + bkv * a.res_bh_stride;
-    const uint16_t* vr = a.v_res + bkv * a.res_bh_stride;
-
-    StepLoad<BITS> bufA, bufB;
-    issue_step<BITS>(bufA, a, j0, kc, ksc, kze, vc, vsc, vze, l, n, q);
 
     // B operand of QK^T: q of head n (zero for n >= GQA) in slot order.
     Frag bq[4];
@@ -383,13 +418,33 @@ __global__ __launch_bounds__(64) void attend_partial_kernel(const AttendArgs a, 
 #pragma unroll
     for (int i = 0; i < 8; ++i) st.acc_o[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // two buffers in flight: the loads of step t+32 overlap the compute of t
-    for (int64_t t0 = j0; t0 < j1; t0 += 2 * kStep) {
-        if (t0 + kStep < j1) issue_step<BITS>(bufB, a, t0 + kStep, kc, ksc, kze, vc, vsc, vze, l, n, q);
-        process_step<BITS>(bufA, sm, st, bq, a, t0, j1, kr, vr, c2, l, n, q);
-        if (t0 + kStep >= j1) break;
-        if (t0 + 2 * kStep < j1) issue_step<BITS>(bufA, a, t0 + 2 * kStep, kc, ksc, kze, vc, vsc, vze, l, n, q);
-        process_step<BITS>(bufB, sm, st, bq, a, t0 + kStep, j1, kr, vr, c2, l, n, q);
+    if (split < n_split_q) {
+        const int nq = static_cast<int>(a.n_quant);
+        const int j0 = split * spw_q * kStep;
+        const int j1 = min(j0 + spw_q * kStep, nq);
+        const uint32_t* kc = a.k_codes + bkv * a.k_codes_bh_stride;
+        const float* ksc = a.k_scale + bkv * a.k_meta_bh_stride;
+        const float* kze = a.k_zero + bkv * a.k_meta_bh_stride;
+        const uint32_t* vc = a.v_codes + bkv * a.v_codes_bh_stride;
+        const float* vsc = a.v_scale + bkv * a.v_meta_bh_stride;
+        const float* vze = a.v_zero + bkv * a.v_meta_bh_stride;
+        StepLoad bufA, bufB;
+        issue_step<BITS>(bufA, j0, nq - 1, kc, ksc, kze, vc, vsc, vze, l, n, q);
+        // two buffers in flight: the loads of step t+32 overlap the compute of t
+        for (int t0 = j0; t0 < j1; t0 += 2 * kStep) {
+            if (t0 + kStep < j1) issue_step<BITS>(bufB, t0 + kStep, nq - 1, kc, ksc, kze, vc, vsc, vze, l, n, q);
+            store_step<BITS>(bufA, sm, st, bq, t0, j1, c2, l, n, q);
+            if (t0 + kStep >= j1) break;
+            if (t0 + 2 * kStep < j1) issue_step<BITS>(bufA, t0 + 2 * kStep, nq - 1, kc, ksc, kze, vc, vsc, vze, l, n, q);
+            store_step<BITS>(bufB, sm, st, bq, t0 + kStep, j1, c2, l, n, q);
+        }
+    } else {
+        const int nr = static_cast<int>(a.n_res);
+        const int r0 = (split - n_split_q) * spw_r * kStep;
+        const int r1 = min(r0 + spw_r * kStep, nr);
+        const uint16_t* kr = a.k_res + bkv * a.res_bh_stride;
+        const uint16_t* vr = a.v_res + bkv * a.res_bh_stride;
+        for (int t0 = r0; t0 < r1; t0 += kStep) residual_step(kr, vr, st, bq, t0, r1, c2, n, q);
     }
 
     // ---- partial (m, l, o) of head n: lane (q, n) holds channels 32q + 8r + i
@@ -455,15 +510,18 @@ __global__ __launch_bounds__(kHeadDim) void attend_combine_kernel(const float* _
 }
 
 AttendPlan plan_attend(int64_t B, int Hq, int Hkv, int64_t n_quant, int64_t n_res) {
-    const int64_t N = n_quant + n_res;
     const int64_t pairs = B * Hkv;
-    const int64_t steps = (N + kStep - 1) / kStep;
+    const int64_t steps_q = (n_quant + kStep - 1) / kStep;
+    const int64_t steps_r = (n_res + kStep - 1) / kStep;
     // enough waves for two per SIMD (1024 SIMDs) before lengthening them
-    int64_t spw = pairs * steps / 2048;
+    int64_t spw = pairs * (steps_q + steps_r) / 2048;
     spw = spw < 1 ? 1 : (spw > kMaxStepsPerWave ? kMaxStepsPerWave : spw);
     AttendPlan p;
+    p.steps_per_wave_q = spw;
+    p.n_split_q = (steps_q + spw - 1) / spw;
+    p.steps_per_wave_r = spw;
+    p.n_split = p.n_split_q + (steps_r + spw - 1) / spw;
     p.chunk = spw * kStep;
-    p.n_split = (steps + spw - 1) / spw;
     const size_t rows = static_cast<size_t>(B) * static_cast<size_t>(Hq) * static_cast<size_t>(p.n_split);
     const size_t o_bytes = (rows * kHeadDim * sizeof(float) + 255) & ~static_cast<size_t>(255);
     p.workspace_bytes = o_bytes + rows * 2 * sizeof(float);
@@ -478,7 +536,8 @@ static hipError_t launch_t(const AttendArgs& a, const AttendPlan& p, hipStream_t
     float* ws_ml = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + o_bytes);
     const dim3 grid(static_cast<uint32_t>(p.n_split), static_cast<uint32_t>(a.B * a.Hkv));
     hipLaunchKernelGGL((attend_partial_kernel<BITS, GQA>), grid, dim3(64), 0, stream, a,
-                       p.chunk / kStep, p.n_split, ws_o, ws_ml);
+                       static_cast<int>(p.steps_per_wave_q), static_cast<int>(p.n_split_q),
+                       static_cast<int>(p.steps_per_wave_r), p.n_split, ws_o, ws_ml);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(attend_combine_kernel, dim3(static_cast<uint32_t>(a.B * a.Hq)),

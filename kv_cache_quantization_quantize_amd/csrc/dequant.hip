@@ -13,38 +13,46 @@
 
 namespace kivi {
 
-template <int BITS, bool KEYS>
-__global__ __launch_bounds__(kBlock) void dequant_kernel(
-    const uint32_t* __restrict__ codes, int64_t codes_bh_stride,
-    const float* __restrict__ scale, const float* __restrict__ zero, int64_t meta_bh_stride,
-    int64_t t0, int64_t n, uint16_t* __restrict__ out, int64_t out_bh_stride,
-    int64_t tiles_per_bh, int64_t n_tiles)
+// Rows [0, n_rows) of one tile; row k is store token t_first + k, written to
+// ot + k*128.  ONE_GROUP (keys only): the 32 rows are exactly one key group,
+// so its scale and zero are loaded once for the tile.
+template <int BITS, bool KEYS, bool ONE_GROUP>
+__device__ __forceinline__ void dequant_tile(const uint32_t* __restrict__ cb, const float* __restrict__ scb,
+                                             const float* __restrict__ zeb, int64_t t_first, int n_rows,
+                                             uint16_t* __restrict__ ot, int lane)
 {
     constexpr int kWords = kHeadDim * BITS / 32;
     constexpr uint32_t kMask = (1u << BITS) - 1u;
     constexpr int kMetaPerTok = kHeadDim / kGroup;
-    const int lane = threadIdx.x & 63;
-    const int64_t tile = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
-    if (tile >= n_tiles) return;
-
-    const int64_t bh = tile / tiles_per_bh;
-    const int64_t i0 = (tile - bh * tiles_per_bh) * 32;
     const int c = lane & 15;
     const int r = lane >> 4;
-    const uint32_t* cb = codes + bh * codes_bh_stride;
-    const float* scb = scale + bh * meta_bh_stride;
-    const float* zeb = zero + bh * meta_bh_stride;
-
+    const uint32_t* ct = cb + t_first * kWords;
+    float gs[8], gz[8];
+    if constexpr (ONE_GROUP) {
+        const float* sp = scb + (t_first / kGroup) * kHeadDim + c * 8;
+        const float* zp = zeb + (t_first / kGroup) * kHeadDim + c * 8;
+        const float4 s0 = *reinterpret_cast<const float4*>(sp);
+        const float4 s1 = *reinterpret_cast<const float4*>(sp + 4);
+        const float4 z0 = *reinterpret_cast<const float4*>(zp);
+        const float4 z1 = *reinterpret_cast<const float4*>(zp + 4);
+        gs[0] = s0.x; gs[1] = s0.y; gs[2] = s0.z; gs[3] = s0.w;
+        gs[4] = s1.x; gs[5] = s1.y; gs[6] = s1.z; gs[7] = s1.w;
+        gz[0] = z0.x; gz[1] = z0.y; gz[2] = z0.z; gz[3] = z0.w;
+        gz[4] = z1.x; gz[5] = z1.y; gz[6] = z1.z; gz[7] = z1.w;
+    }
 #pragma unroll
     for (int i = 0; i < kTokPerLane; ++i) {
-        const int64_t k = i0 + r + kRowsPerWave * i;   // output row
-        if (k >= n) continue;
-        const int64_t t = t0 + k;                      // store token
+        const int k = r + kRowsPerWave * i;            // output row
+        if (!ONE_GROUP && k >= n_rows) continue;
         uint32_t w;
-        if constexpr (BITS == 4) w = cb[t * kWords + c];
-        else w = cb[t * kWords + (c >> 1)] >> (16 * (c & 1));
+        if constexpr (BITS == 4) w = ct[k * kWords + c];
+        else w = ct[k * kWords + (c >> 1)] >> (16 * (c & 1));
         float sc[8], ze[8];
-        if constexpr (KEYS) {
+        if constexpr (ONE_GROUP) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) { sc[j] = gs[j]; ze[j] = gz[j]; }
+        } else if constexpr (KEYS) {
+            const int64_t t = t_first + k;
             const float* sp = scb + (t / kGroup) * kHeadDim + c * 8;
             const float* zp = zeb + (t / kGroup) * kHeadDim + c * 8;
             const float4 s0 = *reinterpret_cast<const float4*>(sp);
@@ -56,6 +64,7 @@ __global__ __launch_bounds__(kBlock) void dequant_kernel(
             ze[0] = z0.x; ze[1] = z0.y; ze[2] = z0.z; ze[3] = z0.w;
             ze[4] = z1.x; ze[5] = z1.y; ze[6] = z1.z; ze[7] = z1.w;
         } else {
+            const int64_t t = t_first + k;
             const float s = scb[t * kMetaPerTok + (c >> 2)];
             const float z = zeb[t * kMetaPerTok + (c >> 2)];
 #pragma unroll
@@ -64,8 +73,32 @@ __global__ __launch_bounds__(kBlock) void dequant_kernel(
         uint32_t h[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) h[j] = recon_f16(static_cast<float>((w >> (BITS * j)) & kMask), sc[j], ze[j]);
-        *reinterpret_cast<uint4*>(out + bh * out_bh_stride + k * kHeadDim + c * 8) = pack8(h);
+        *reinterpret_cast<uint4*>(ot + k * kHeadDim + c * 8) = pack8(h);
     }
+}
+
+template <int BITS, bool KEYS>
+__global__ __launch_bounds__(kBlock) void dequant_kernel(
+    const uint32_t* __restrict__ codes, int64_t codes_bh_stride,
+    const float* __restrict__ scale, const float* __restrict__ zero, int64_t meta_bh_stride,
+    int64_t t0, int64_t n, uint16_t* __restrict__ out, int64_t out_bh_stride,
+    int64_t tiles_per_bh, int64_t n_tiles)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t tile = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
+    if (tile >= n_tiles) return;                   // uniform across the wave
+
+    const int64_t bh = tile / tiles_per_bh;
+    const int64_t i0 = (tile - bh * tiles_per_bh) * 32;
+    const int64_t rows = n - i0;
+    const uint32_t* cb = codes + bh * codes_bh_stride;
+    const float* scb = scale + bh * meta_bh_stride;
+    const float* zeb = zero + bh * meta_bh_stride;
+    uint16_t* ot = out + bh * out_bh_stride + i0 * kHeadDim;
+    if (KEYS && rows >= 32 && (t0 + i0) % kGroup == 0)
+        dequant_tile<BITS, KEYS, true>(cb, scb, zeb, t0 + i0, 32, ot, lane);
+    else
+        dequant_tile<BITS, KEYS, false>(cb, scb, zeb, t0 + i0, rows < 32 ? static_cast<int>(rows) : 32, ot, lane);
 }
 
 template <int BITS, bool KEYS>
