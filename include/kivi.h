@@ -151,7 +151,8 @@ int kivi_dequantize(const kivi_store* src, int64_t BH, int64_t token_begin, int6
  *   workspace  device scratch of at least
  *              kivi_decode_attend_workspace_bytes(B, Hq, Hkv, n_quant, n_res)
  *              bytes, 256-byte aligned; its contents on entry do not matter
- * n_quant + n_res must be > 0; Hq/Hkv must be in 1..8.
+ * n_quant + n_res must be > 0, n_quant and n_res below 2^24, Hq/Hkv one of
+ * 1, 2, 4, 8, and softmax_scale finite and > 0 (KIVI_ERR_SHAPE otherwise).
  */
 int kivi_decode_attend(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
                        const kivi_store* k, const kivi_store* v, int64_t n_quant,

@@ -26,6 +26,9 @@ HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-ffp-contract=off", "-Wall", "-Wno-unused-command-line-argument",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: the attend's accumulators live across a loop
+    # with a conditional rescale, and AGPR accumulators cost copies every step
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

@@ -2,6 +2,8 @@
 // include/kivi_calib.h): argument validation on the host, then kernel launch
 // on the caller's stream.  Validation never calls into HIP, so an error
 // return means nothing was enqueued.
+#include <cmath>
+
 #include "kivi.h"
 #include "kivi_calib.h"
 #include "kivi_launch.h"
@@ -15,6 +17,7 @@ thread_local int g_last_hip_error = 0;
 constexpr int64_t kD = 128;
 constexpr int64_t kG = 32;
 constexpr int64_t kMaxBlocks = (int64_t{1} << 31) - 1;
+constexpr int64_t kMaxAttendTokens = int64_t{1} << 24;   // attend offsets stay 32-bit
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -127,6 +130,8 @@ int kivi_decode_attend(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
     const int group = Hq / Hkv;
     if (group != 1 && group != 2 && group != 4 && group != 8) return KIVI_ERR_UNSUPPORTED;
     if (n_quant + n_res == 0) return KIVI_ERR_SHAPE;
+    if (n_quant >= kMaxAttendTokens || n_res >= kMaxAttendTokens) return KIVI_ERR_SHAPE;
+    if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) return KIVI_ERR_SHAPE;
     const int64_t slabs = B * Hkv;
     int rc = check_store(k, KIVI_KEYS, slabs, 0, n_quant);
     if (rc != KIVI_OK) return rc;

@@ -43,8 +43,9 @@ union Frag {
     uint32_t u[4];
 };
 
+// Two waves per SIMD: the register budget (256) holds three steps of loads.
 #ifndef KIVI_ATTEND_OCCUPANCY
-#define KIVI_ATTEND_OCCUPANCY
+#define KIVI_ATTEND_OCCUPANCY __attribute__((amdgpu_waves_per_eu(2)))
 #endif
 
 constexpr int kStep = 32;             // tokens per wave step (one key group)
@@ -64,25 +65,39 @@ constexpr uint32_t kMagic = 0x64006400u;   // fp16 1024.0 in both halves
 // j and slot 2j+1 channel j+4 (j = 0..3).  Key unit kb of lane group q is
 // channels 32q + 8kb .. 32q + 8kb + 7.
 
-// Four fp16 pairs (1024 + code[j], 1024 + code[j+4]), j = 0..3, from the 8
-// codes of one 8-channel unit.  4-bit: one code word.  2-bit: the unit's
-// half of a word, spread to bytes 0 and 2 first.
 // (x & mask) | magic in one v_bitop3_b32 (truth table 0xEA = (a & b) | c).
 __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t magic) {
     return __builtin_amdgcn_bitop3_b32(x, mask, magic, 0xEA);
 }
 
+// Four fp16 pairs from the 8 codes of one 8-channel unit: pair j holds the
+// codes of channels j and j+4.  A code masked in place at bit offset e of
+// the low mantissa byte under the exponent of 1024 reads as 1024 + 2^e code
+// exactly, so no shift is needed for e < 8; the factor 2^-e goes into the
+// staged scale (kscale_factor).  4-bit: one code word, e = 4 (j & 1) after
+// one shift by 8 for j >= 2.  2-bit: the unit's half of a word spread to
+// bytes 0 and 2 first, e = 2 j.
 template <int BITS>
 __device__ __forceinline__ void code_pairs(uint32_t w, int half, uint32_t (&p)[4]) {
     if constexpr (BITS == 4) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) p[j] = and_or(w >> (4 * j), 0x000F000Fu, kMagic);
+        const uint32_t w8 = w >> 8;
+        p[0] = and_or(w, 0x000F000Fu, kMagic);
+        p[1] = and_or(w, 0x00F000F0u, kMagic);
+        p[2] = and_or(w8, 0x000F000Fu, kMagic);
+        p[3] = and_or(w8, 0x00F000F0u, kMagic);
     } else {
         const uint32_t sel = half ? 0x0C030C02u : 0x0C010C00u;
-        const uint32_t s = __builtin_amdgcn_perm(w, w, sel);
+        const uint32_t x = __builtin_amdgcn_perm(w, w, sel);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) p[j] = and_or(s >> (2 * j), 0x00030003u, kMagic);
+        for (int j = 0; j < 4; ++j) p[j] = and_or(x, 0x00030003u << (2 * j), kMagic);
     }
+}
+
+// 2^-e for key channel c (c & 3 = j is its pair in the unit, see code_pairs).
+template <int BITS>
+__device__ __forceinline__ float kscale_factor(int c) {
+    if constexpr (BITS == 4) return (c & 1) ? 0.0625f : 1.0f;
+    else return __builtin_ldexpf(1.0f, -2 * (c & 3));
 }
 
 // code * scale + zero as one mixed-precision FMA with an fp16 result:
@@ -104,9 +119,9 @@ __device__ __forceinline__ uint32_t deq2(uint32_t pair, float s0, float z0, floa
 // lane exchanges across the four 16-lane rows (see kivi_device.h)
 __device__ __forceinline__ float rows_max(float v) {
     auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    v = __builtin_elementwise_maximum(__uint_as_float(p[0]), __uint_as_float(p[1]));
     p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    return __builtin_elementwise_maximum(__uint_as_float(p[0]), __uint_as_float(p[1]));
 }
 __device__ __forceinline__ float rows_sum(float v) {
     auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -115,9 +130,48 @@ __device__ __forceinline__ float rows_sum(float v) {
     return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
-// Global loads of one 32-token step of store tokens, issued one step ahead of
-// the compute that uses them.  Token indices are clamped to the last store
-// token, so every load is in bounds; masked tokens get zero probability.
+// The slab of one (sequence, kv head) as raw buffer resources whose extent
+// ends at store token n_quant: a load past the extent returns zero, so the
+// masked tokens of a partial last step read finite zeros and no load leaves
+// the slab.  Word 3 is the raw-buffer format of gfx9-family parts (32-bit
+// data format, no swizzle, no thread-id indexing).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kRsrcWord3);
+}
+
+// A step start whose every load lies past the buffers' extent: the ABI
+// keeps n_quant below 2^24 tokens, so the extents stay below 2^30 bytes of
+// codes and 2^28 of metadata, while this start puts code offsets at
+// 2^25 x 32 or 64 B and metadata offsets at 2^25 x 16 B (lane and
+// instruction offsets keep all of them below 2^32).
+constexpr uint32_t kFarToken = 1u << 25;
+
+struct StoreView {
+    rsrc_t kc, ks, kz;      // key codes, scale, zero
+    rsrc_t vc, vs, vz;      // value codes, scale, zero
+};
+
+// Byte offsets of a lane's loads at step t0 = 0; a step adds t0 times the
+// bytes per token (key metadata: t0 / 32 groups of 512 B = 16 t0).
+struct LaneOffsets {
+    uint32_t k;             // key codes of token n, the lane's 32 channels
+    uint32_t v;             // value code word of token 4q, the lane's 8 channels
+    uint32_t km;            // key scale / zero of channels 2l, 2l+1
+    uint32_t vm;            // value scale / zero of token l & 31, groups 2(l>>5), +1
+};
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float2 as_float2(u32x2 v) {
+    return make_float2(__uint_as_float(v.x), __uint_as_float(v.y));
+}
+
+// Loads of one 32-token step of store tokens, issued one step ahead of the
+// compute that uses them.
 struct StepLoad {
     uint32_t kw[2][4];      // key code words of token t0 + 16*blk + n (lane's 32 channels)
     float2 ks, kz;          // key scale / zero of channels 2l, 2l+1 of the step's group
@@ -130,33 +184,30 @@ struct StepLoad {
 __device__ __forceinline__ int pv_token(int q, int s) { return 16 * (s >> 2) + 4 * q + (s & 3); }
 
 template <int BITS>
-__device__ __forceinline__ void issue_step(StepLoad& L, int t0, int last, const uint32_t* kc,
-                                           const float* ksc, const float* kze, const uint32_t* vc,
-                                           const float* vsc, const float* vze, int l, int n, int q) {
-    constexpr int kWords = kHeadDim * BITS / 32;
-    constexpr int kMetaPerTok = kHeadDim / kGroup;
+__device__ __forceinline__ void issue_step(StepLoad& L, const StoreView& S, const LaneOffsets& O,
+                                           uint32_t t0, int n) {
+    constexpr uint32_t kRow = kHeadDim * BITS / 8;          // code bytes per token
+    const uint32_t ko = O.k + t0 * kRow;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-        const int tok = min(t0 + 16 * blk + n, last);
         if constexpr (BITS == 4) {
-            const uint4 t = *reinterpret_cast<const uint4*>(kc + tok * kWords + 4 * q);
+            const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(S.kc, ko + 16 * kRow * blk, 0, 0);
             L.kw[blk][0] = t.x; L.kw[blk][1] = t.y; L.kw[blk][2] = t.z; L.kw[blk][3] = t.w;
         } else {
-            const uint2 t = *reinterpret_cast<const uint2*>(kc + tok * kWords + 2 * q);
+            const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(S.kc, ko + 16 * kRow * blk, 0, 0);
             L.kw[blk][0] = t.x; L.kw[blk][1] = t.x; L.kw[blk][2] = t.y; L.kw[blk][3] = t.y;
         }
     }
-    const int g = t0 / kGroup;
-    L.ks = *reinterpret_cast<const float2*>(ksc + g * kHeadDim + 2 * l);
-    L.kz = *reinterpret_cast<const float2*>(kze + g * kHeadDim + 2 * l);
-    const int tv = min(t0 + (l & 31), last);
-    L.vs = *reinterpret_cast<const float2*>(vsc + tv * kMetaPerTok + 2 * (l >> 5));
-    L.vz = *reinterpret_cast<const float2*>(vze + tv * kMetaPerTok + 2 * (l >> 5));
-    const int word = BITS == 4 ? n : (n >> 1);
+    const uint32_t kmo = O.km + 16 * t0;
+    L.ks = as_float2(__builtin_amdgcn_raw_buffer_load_b64(S.ks, kmo, 0, 0));
+    L.kz = as_float2(__builtin_amdgcn_raw_buffer_load_b64(S.kz, kmo, 0, 0));
+    const uint32_t vmo = O.vm + 16 * t0;
+    L.vs = as_float2(__builtin_amdgcn_raw_buffer_load_b64(S.vs, vmo, 0, 0));
+    L.vz = as_float2(__builtin_amdgcn_raw_buffer_load_b64(S.vz, vmo, 0, 0));
+    const uint32_t vo = O.v + t0 * kRow;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-        const int tok = min(t0 + pv_token(q, s), last);
-        const uint32_t w = vc[tok * kWords + word];
+        const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(S.vc, vo + (16 * (s >> 2) + (s & 3)) * kRow, 0, 0);
         // 2-bit: bring the lane's 8 channels (half of the word) to the low half
         L.vw[s] = BITS == 4 ? w : (w >> (16 * (n & 1)));
     }
@@ -179,7 +230,17 @@ struct Smem {
     alignas(16) float kz[kHeadDim + kKPad * 4];       // key zero - 1024 * scale
     alignas(16) float vs[kHeadDim / kGroup][kVRow];   // value scale, [group][token]
     alignas(16) float vz[kHeadDim / kGroup][kVRow];   // value zero - 1024 * scale
+    alignas(16) uint4 bq[4][64];                       // QK^T B operand (queries), [unit][lane]
 };
+
+// The QK^T B operand of channel unit kb, kept in LDS rather than in 16
+// registers across the step loop (the registers hold the prefetched loads).
+__device__ __forceinline__ Frag query_frag(const Smem& sm, int kb, int l) {
+    const uint4 v = sm.bq[kb][l];
+    Frag f;
+    f.u[0] = v.x; f.u[1] = v.y; f.u[2] = v.z; f.u[3] = v.w;
+    return f;
+}
 
 // Online-softmax state of one lane: head n, channels 32q + 8r + i of acc_o[i][r].
 struct SoftState {
@@ -196,31 +257,33 @@ constexpr float kSlack = 8.0f;
 
 // Online softmax over one step's scores (base 2) and the PV B operand.
 // Lane (q, n) holds head n's scores of step tokens 16*blk + 4q + r; with
-// MASK, tokens at or past `limit` (step-relative) get probability 0.
+// MASK, tokens at or past `limit` (step-relative) get probability 0.  The
+// scale c2 = softmax_scale * log2(e) is positive, so the max is taken over
+// the raw scores and scaled once.
 template <bool MASK>
 __device__ __forceinline__ Frag softmax_step(const float4_t (&acc_s)[2], SoftState& st, float c2,
                                              int limit, int q) {
     float sv[8];
-    float mloc = -INFINITY;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            float sc = acc_s[blk][r] * c2;
+            float sc = acc_s[blk][r];
             if constexpr (MASK) sc = (16 * blk + 4 * q + r) < limit ? sc : -INFINITY;
             sv[4 * blk + r] = sc;
-            mloc = fmaxf(mloc, sc);
         }
-    const float m_step = rows_max(mloc);
+    float mloc = sv[0];
+#pragma unroll
+    for (int s = 1; s < 8; ++s) mloc = __builtin_elementwise_maximum(mloc, sv[s]);
+    const float m_step = rows_max(mloc) * c2;
     const float m_new = m_step > st.m_run + kSlack ? m_step : st.m_run;
     const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);   // 1 when m did not move
     st.m_run = m_new;
-    float psum = 0.0f;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-        sv[s] = __builtin_amdgcn_exp2f(sv[s] - m_new);
-        psum += sv[s];
-    }
+    for (int s = 0; s < 8; ++s) sv[s] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[s], c2, -m_new));
+    float psum = sv[0];
+#pragma unroll
+    for (int s = 1; s < 8; ++s) psum += sv[s];
     st.l_part = __builtin_fmaf(st.l_part, alpha, psum);
     if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
@@ -246,13 +309,18 @@ __device__ __forceinline__ Frag softmax_any(const float4_t (&acc_s)[2], SoftStat
 // One step of store tokens [t0, t0 + 32), tokens at or past n_quant masked.
 template <int BITS>
 __device__ __forceinline__ void store_step(const StepLoad& L, Smem& sm, SoftState& st,
-                                           const Frag (&bq)[4], int t0, int n_quant, float c2,
+                                           int t0, int n_quant, float c2,
                                            int l, int n, int q) {
-    // ---- stage this step's metadata in LDS (zero' = zero - 1024 * scale)
+    // ---- stage this step's metadata in LDS (zero' = zero - 1024 * scale')
     lds_order();
-    *reinterpret_cast<float2*>(&sm.ks[kidx(2 * l)]) = L.ks;
-    *reinterpret_cast<float2*>(&sm.kz[kidx(2 * l)]) =
-        make_float2(__builtin_fmaf(-1024.0f, L.ks.x, L.kz.x), __builtin_fmaf(-1024.0f, L.ks.y, L.kz.y));
+    {
+        // key scale times 2^-e of its channel's code position (code_pairs)
+        const float s0 = L.ks.x * kscale_factor<BITS>(2 * l);
+        const float s1 = L.ks.y * kscale_factor<BITS>(2 * l + 1);
+        *reinterpret_cast<float2*>(&sm.ks[kidx(2 * l)]) = make_float2(s0, s1);
+        *reinterpret_cast<float2*>(&sm.kz[kidx(2 * l)]) =
+            make_float2(__builtin_fmaf(-1024.0f, s0, L.kz.x), __builtin_fmaf(-1024.0f, s1, L.kz.y));
+    }
     {
         const int tt = l & 31;
         const int gg = (l >> 5) * 2;
@@ -274,6 +342,7 @@ __device__ __forceinline__ void store_step(const StepLoad& L, Smem& sm, SoftStat
         const float4 z1 = *reinterpret_cast<const float4*>(&sm.kz[cb + 4]);
         const float sl[4] = {s0.x, s0.y, s0.z, s0.w}, sh[4] = {s1.x, s1.y, s1.z, s1.w};
         const float zl[4] = {z0.x, z0.y, z0.z, z0.w}, zh[4] = {z1.x, z1.y, z1.z, z1.w};
+        const Frag bq = query_frag(sm, kb, l);
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
             uint32_t pr[4];
@@ -281,7 +350,7 @@ __device__ __forceinline__ void store_step(const StepLoad& L, Smem& sm, SoftStat
             Frag ka;
 #pragma unroll
             for (int j = 0; j < 4; ++j) ka.u[j] = deq2(pr[j], sl[j], zl[j], sh[j], zh[j]);
-            acc_s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka.h, bq[kb].h, acc_s[blk], 0, 0, 0);
+            acc_s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka.h, bq.h, acc_s[blk], 0, 0, 0);
         }
     }
 
@@ -315,9 +384,9 @@ __device__ __forceinline__ void store_step(const StepLoad& L, Smem& sm, SoftStat
 }
 
 // One step of fp16 residual tokens [t0, t0 + 32), tokens at or past n_res masked.
-__device__ __forceinline__ void residual_step(const uint16_t* kr, const uint16_t* vr, SoftState& st,
-                                              const Frag (&bq)[4], int t0, int n_res, float c2,
-                                              int n, int q) {
+__device__ __forceinline__ void residual_step(const uint16_t* kr, const uint16_t* vr, const Smem& sm,
+                                              SoftState& st, int t0, int n_res, float c2,
+                                              int l, int n, int q) {
     const int last = n_res - 1;
     float4_t acc_s[2] = {float4_t{0.0f, 0.0f, 0.0f, 0.0f}, float4_t{0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
@@ -340,7 +409,7 @@ __device__ __forceinline__ void residual_step(const uint16_t* kr, const uint16_t
                 const uint32_t s1 = (c1 & 1) ? 0x0706u : 0x0504u;
                 ka.u[j] = __builtin_amdgcn_perm(rn[c1 >> 1], rn[c0 >> 1], (s1 << 16) | s0);
             }
-            acc_s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka.h, bq[kb].h, acc_s[blk], 0, 0, 0);
+            acc_s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka.h, query_frag(sm, kb, l).h, acc_s[blk], 0, 0, 0);
         }
     }
     const Frag bp = softmax_any(acc_s, st, c2, n_res - t0, q);
@@ -367,8 +436,8 @@ __device__ __forceinline__ void residual_step(const uint16_t* kr, const uint16_t
 
 // One wave: sequence b, kv head kv, one split.  Splits [0, n_split_q) cover
 // store tokens [0, n_quant) in runs of spw_q steps of 32 tokens; the rest
-// cover residual tokens [0, n_res) in runs of spw_r steps.  Slab offsets fit
-// in 32 bits (the ABI bounds every slab below 2^31 elements).
+// cover residual tokens [0, n_res) in runs of spw_r steps.  Offsets within a
+// slab fit in 32 bits: the ABI keeps n_quant and n_res below 2^24 tokens.
 template <int BITS, int GQA>
 __global__ __launch_bounds__(64) KIVI_ATTEND_OCCUPANCY void attend_partial_kernel(const AttendArgs a, int spw_q, int n_split_q,
                                                             int spw_r, int64_t n_split, float* __restrict__ ws_o,
@@ -409,6 +478,9 @@ __global__ __launch_bounds__(64) KIVI_ATTEND_OCCUPANCY void attend_partial_kerne
                 const uint32_t s1 = (c1 & 1) ? 0x0706u : 0x0504u;
                 bq[kb].u[j] = __builtin_amdgcn_perm(qn[c1 >> 1], qn[c0 >> 1], (s1 << 16) | s0);
             }
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) sm.bq[kb][l] = make_uint4(bq[kb].u[0], bq[kb].u[1], bq[kb].u[2], bq[kb].u[3]);
+        lds_order();
     }
 
     const float c2 = a.softmax_scale * kLog2e;
@@ -422,21 +494,39 @@ __global__ __launch_bounds__(64) KIVI_ATTEND_OCCUPANCY void attend_partial_kerne
         const int nq = static_cast<int>(a.n_quant);
         const int j0 = split * spw_q * kStep;
         const int j1 = min(j0 + spw_q * kStep, nq);
-        const uint32_t* kc = a.k_codes + bkv * a.k_codes_bh_stride;
-        const float* ksc = a.k_scale + bkv * a.k_meta_bh_stride;
-        const float* kze = a.k_zero + bkv * a.k_meta_bh_stride;
-        const uint32_t* vc = a.v_codes + bkv * a.v_codes_bh_stride;
-        const float* vsc = a.v_scale + bkv * a.v_meta_bh_stride;
-        const float* vze = a.v_zero + bkv * a.v_meta_bh_stride;
-        StepLoad bufA, bufB;
-        issue_step<BITS>(bufA, j0, nq - 1, kc, ksc, kze, vc, vsc, vze, l, n, q);
-        // two buffers in flight: the loads of step t+32 overlap the compute of t
-        for (int t0 = j0; t0 < j1; t0 += 2 * kStep) {
-            if (t0 + kStep < j1) issue_step<BITS>(bufB, t0 + kStep, nq - 1, kc, ksc, kze, vc, vsc, vze, l, n, q);
-            store_step<BITS>(bufA, sm, st, bq, t0, j1, c2, l, n, q);
+        constexpr int kWords = kHeadDim * BITS / 32;
+        constexpr int kMetaPerTok = kHeadDim / kGroup;
+        const uint32_t n_groups = static_cast<uint32_t>((nq + kGroup - 1) / kGroup);
+        StoreView S;
+        S.kc = make_rsrc(a.k_codes + bkv * a.k_codes_bh_stride, static_cast<uint32_t>(nq) * kWords * 4u);
+        S.ks = make_rsrc(a.k_scale + bkv * a.k_meta_bh_stride, n_groups * kHeadDim * 4u);
+        S.kz = make_rsrc(a.k_zero + bkv * a.k_meta_bh_stride, n_groups * kHeadDim * 4u);
+        S.vc = make_rsrc(a.v_codes + bkv * a.v_codes_bh_stride, static_cast<uint32_t>(nq) * kWords * 4u);
+        S.vs = make_rsrc(a.v_scale + bkv * a.v_meta_bh_stride, static_cast<uint32_t>(nq) * kMetaPerTok * 4u);
+        S.vz = make_rsrc(a.v_zero + bkv * a.v_meta_bh_stride, static_cast<uint32_t>(nq) * kMetaPerTok * 4u);
+        LaneOffsets O;
+        O.k = static_cast<uint32_t>(n * kWords + (BITS == 4 ? 4 * q : 2 * q)) * 4u;
+        O.v = static_cast<uint32_t>(4 * q * kWords + (BITS == 4 ? n : (n >> 1))) * 4u;
+        O.km = static_cast<uint32_t>(l) * 8u;
+        O.vm = static_cast<uint32_t>(l & 31) * 16u + static_cast<uint32_t>(l >> 5) * 8u;
+        // Three buffers: the loads of steps t+32 and t+64 are in flight while
+        // step t computes.  Every prefetch is issued, also past the split's
+        // end (to a token far outside the buffers' extent, which the buffer
+        // unit answers with zeros and no memory access): a conditional issue
+        // makes the compiler wait for all outstanding loads at the join.
+        const auto pref = [j1](int t) { return t < j1 ? static_cast<uint32_t>(t) : kFarToken; };
+        StepLoad bufA, bufB, bufC;
+        issue_step<BITS>(bufA, S, O, j0, n);
+        issue_step<BITS>(bufB, S, O, pref(j0 + kStep), n);
+        for (int t0 = j0; t0 < j1; t0 += 3 * kStep) {
+            issue_step<BITS>(bufC, S, O, pref(t0 + 2 * kStep), n);
+            store_step<BITS>(bufA, sm, st, t0, j1, c2, l, n, q);
             if (t0 + kStep >= j1) break;
-            if (t0 + 2 * kStep < j1) issue_step<BITS>(bufA, t0 + 2 * kStep, nq - 1, kc, ksc, kze, vc, vsc, vze, l, n, q);
-            store_step<BITS>(bufB, sm, st, bq, t0 + kStep, j1, c2, l, n, q);
+            issue_step<BITS>(bufA, S, O, pref(t0 + 3 * kStep), n);
+            store_step<BITS>(bufB, sm, st, t0 + kStep, j1, c2, l, n, q);
+            if (t0 + 2 * kStep >= j1) break;
+            issue_step<BITS>(bufB, S, O, pref(t0 + 4 * kStep), n);
+            store_step<BITS>(bufC, sm, st, t0 + 2 * kStep, j1, c2, l, n, q);
         }
     } else {
         const int nr = static_cast<int>(a.n_res);
@@ -444,7 +534,7 @@ __global__ __launch_bounds__(64) KIVI_ATTEND_OCCUPANCY void attend_partial_kerne
         const int r1 = min(r0 + spw_r * kStep, nr);
         const uint16_t* kr = a.k_res + bkv * a.res_bh_stride;
         const uint16_t* vr = a.v_res + bkv * a.res_bh_stride;
-        for (int t0 = r0; t0 < r1; t0 += kStep) residual_step(kr, vr, st, bq, t0, r1, c2, n, q);
+        for (int t0 = r0; t0 < r1; t0 += kStep) residual_step(kr, vr, sm, st, t0, r1, c2, l, n, q);
     }
 
     // ---- partial (m, l, o) of head n: lane (q, n) holds channels 32q + 8r + i

@@ -130,12 +130,17 @@ def test_attend_validation():
     assert ws > 0
     assert kivi.attend_workspace_bytes(1, 32, 8, 0, 0) == 0
 
-    def call(Hq=32, Hkv=8, nq=64, nr=16, kk=k, vv=v, q=FAKE, wsb=ws, wsp=FAKE):
+    def call(Hq=32, Hkv=8, nq=64, nr=16, kk=k, vv=v, q=FAKE, wsb=ws, wsp=FAKE, scale=0.088):
         return L.kivi_decode_attend(q, 1, Hq, Hkv, ctypes.byref(kk), ctypes.byref(vv), nq,
-                                    FAKE, FAKE, 16 * 128, nr, 0.088, FAKE, wsp, wsb, None)
+                                    FAKE, FAKE, 16 * 128, nr, scale, FAKE, wsp, wsb, None)
     assert call(Hq=30) == -2                      # Hq % Hkv
     assert call(Hq=24) == -3                      # 3 query heads per kv head
     assert call(nq=0, nr=0) == -2                 # nothing to attend to
+    assert call(nq=1 << 24) == -2                 # attend token bound (before the capacity check)
+    assert call(scale=0.0) == -2                  # the scale must be finite and positive
+    assert call(scale=-0.088) == -2
+    assert call(scale=float("inf")) == -2
+    assert call(scale=float("nan")) == -2
     assert call(nq=65) == -2                      # past the store capacity
     assert call(kk=v) == -2                       # kinds swapped
     assert call(vv=_store(kivi.KIVI_VALUES, bits=2, cap=64)) == -2
