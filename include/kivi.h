@@ -160,6 +160,34 @@ int kivi_decode_attend(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
                        int64_t n_res, float softmax_scale, float* out,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * kivi_decode_attend over a batch of sequences of different lengths, in one
+ * launch ([Benchmarks] "KV-Cache Kernel Roofline: What Actually Limits
+ * Decode": several concurrent requests routed through one fused decode
+ * kernel, the way to fill the GPU at decode).  Sequence b attends over store
+ * tokens [0, n_quant[b]) then residual tokens [0, n_res[b]) of its own slabs
+ * b*Hkv + kv, exactly as kivi_decode_attend does for a batch of one.
+ *
+ *   n_quant, n_res  DEVICE int32 [B], 4-byte aligned, read by the kernel
+ *              (so the lengths can change between replays of a captured
+ *              graph).  A value is clamped to [0, max_n_quant] /
+ *              [0, max_n_res]; the host cannot see them, so the clamp is what
+ *              keeps every load inside the store and residual bounds below.
+ *   max_n_quant, max_n_res  host bounds on the lengths: the grid, the
+ *              workspace (kivi_decode_attend_workspace_bytes(B, Hq, Hkv,
+ *              max_n_quant, max_n_res)) and the store/residual validation use
+ *              them.  max_n_quant + max_n_res must be > 0.
+ * A sequence whose clamped lengths are both 0 gets an all-zero output row.
+ * Every other argument and every error is as for kivi_decode_attend.
+ */
+int kivi_decode_attend_varlen(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
+                              const kivi_store* k, const kivi_store* v,
+                              const int32_t* n_quant, int64_t max_n_quant,
+                              const uint16_t* k_res, const uint16_t* v_res, int64_t res_bh_stride,
+                              const int32_t* n_res, int64_t max_n_res, float softmax_scale,
+                              float* out, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
 /* Workspace bytes kivi_decode_attend needs for this shape (head_dim 128). */
 size_t kivi_decode_attend_workspace_bytes(int64_t B, int32_t Hq, int32_t Hkv,
                                           int64_t n_quant, int64_t n_res);

@@ -120,11 +120,18 @@ size_t kivi_decode_attend_workspace_bytes(int64_t B, int32_t Hq, int32_t Hkv,
     return kivi::plan_attend(B, Hq, Hkv, n_quant, n_res).workspace_bytes;
 }
 
-int kivi_decode_attend(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
-                       const kivi_store* k, const kivi_store* v, int64_t n_quant,
-                       const uint16_t* k_res, const uint16_t* v_res, int64_t res_bh_stride,
-                       int64_t n_res, float softmax_scale, float* out,
-                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared validation and launch of the uniform and variable-length attends;
+// n_quant / n_res are the uniform counts or the per-sequence bounds.
+int decode_attend(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
+                  const kivi_store* k, const kivi_store* v, int64_t n_quant,
+                  const uint16_t* k_res, const uint16_t* v_res, int64_t res_bh_stride,
+                  int64_t n_res, const int32_t* seq_n_quant, const int32_t* seq_n_res,
+                  float softmax_scale, float* out, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream) {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || n_quant < 0 || n_res < 0) return KIVI_ERR_SHAPE;
     if (Hq % Hkv != 0) return KIVI_ERR_SHAPE;
     const int group = Hq / Hkv;
@@ -159,9 +166,38 @@ int kivi_decode_attend(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
     a.k_res = n_res > 0 ? k_res : q;     // never read when n_res == 0
     a.v_res = n_res > 0 ? v_res : q;
     a.res_bh_stride = n_res > 0 ? res_bh_stride : 0;
-    a.n_res = n_res; a.softmax_scale = softmax_scale; a.out = out;
+    a.n_res = n_res;
+    a.seq_n_quant = seq_n_quant; a.seq_n_res = seq_n_res;
+    a.softmax_scale = softmax_scale; a.out = out;
     a.workspace = workspace; a.bits = k->bits;
     return finish(kivi::launch_decode_attend(a, plan, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int kivi_decode_attend(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
+                       const kivi_store* k, const kivi_store* v, int64_t n_quant,
+                       const uint16_t* k_res, const uint16_t* v_res, int64_t res_bh_stride,
+                       int64_t n_res, float softmax_scale, float* out,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return decode_attend(q, B, Hq, Hkv, k, v, n_quant, k_res, v_res, res_bh_stride, n_res,
+                         nullptr, nullptr, softmax_scale, out, workspace, workspace_bytes, stream);
+}
+
+int kivi_decode_attend_varlen(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
+                              const kivi_store* k, const kivi_store* v,
+                              const int32_t* n_quant, int64_t max_n_quant,
+                              const uint16_t* k_res, const uint16_t* v_res, int64_t res_bh_stride,
+                              const int32_t* n_res, int64_t max_n_res, float softmax_scale,
+                              float* out, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+    if (B > 0 && (!n_quant || !n_res)) return KIVI_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(n_quant) & 3u) != 0 ||
+        (reinterpret_cast<uintptr_t>(n_res) & 3u) != 0) return KIVI_ERR_ALIGN;
+    return decode_attend(q, B, Hq, Hkv, k, v, max_n_quant, k_res, v_res, res_bh_stride, max_n_res,
+                         n_quant, n_res, softmax_scale, out, workspace, workspace_bytes, stream);
 }
 
 const char* kivi_status_string(int status) {

@@ -490,8 +490,16 @@ __global__ __launch_bounds__(64) KIVI_ATTEND_OCCUPANCY void attend_partial_kerne
 #pragma unroll
     for (int i = 0; i < 8; ++i) st.acc_o[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    if (split < n_split_q) {
-        const int nq = static_cast<int>(a.n_quant);
+    // Token counts of this sequence: the uniform bounds, or the per-sequence
+    // lengths clamped to them (so no load can leave the bounded slab).
+    int nq = static_cast<int>(a.n_quant);
+    int nr = static_cast<int>(a.n_res);
+    if (a.seq_n_quant) {
+        nq = min(max(a.seq_n_quant[b], 0), nq);
+        nr = min(max(a.seq_n_res[b], 0), nr);
+    }
+
+    if (split < n_split_q && split * spw_q * kStep < nq) {
         const int j0 = split * spw_q * kStep;
         const int j1 = min(j0 + spw_q * kStep, nq);
         constexpr int kWords = kHeadDim * BITS / 32;
@@ -528,8 +536,7 @@ __global__ __launch_bounds__(64) KIVI_ATTEND_OCCUPANCY void attend_partial_kerne
             issue_step<BITS>(bufB, S, O, pref(t0 + 4 * kStep), n);
             store_step<BITS>(bufC, sm, st, t0 + 2 * kStep, j1, c2, l, n, q);
         }
-    } else {
-        const int nr = static_cast<int>(a.n_res);
+    } else if (split >= n_split_q) {
         const int r0 = (split - n_split_q) * spw_r * kStep;
         const int r1 = min(r0 + spw_r * kStep, nr);
         const uint16_t* kr = a.k_res + bkv * a.res_bh_stride;
@@ -573,6 +580,8 @@ __global__ __launch_bounds__(kHeadDim) void attend_combine_kernel(const float* _
     if ((d & 63) == 0) red[d >> 6] = M;
     __syncthreads();
     M = fmaxf(red[0], red[1]);
+    // every split empty: keep the weights 2^(m_i - M) finite (they are 0)
+    if (M == -INFINITY) M = 0.0f;
     float L = 0.0f, acc = 0.0f;
     const float* o = ws_o + row * n_split * kHeadDim + d;
     int64_t i = 0;
@@ -596,7 +605,9 @@ __global__ __launch_bounds__(kHeadDim) void attend_combine_kernel(const float* _
         L = __builtin_fmaf(e, ml[2 * i + 1], L);
         acc = __builtin_fmaf(e, o[i * kHeadDim], acc);
     }
-    out[row * kHeadDim + d] = acc / L;
+    // A sequence with no tokens at all (only possible in a variable-length
+    // batch) has every partial empty (m = -inf, l = 0): its output is zero.
+    out[row * kHeadDim + d] = L > 0.0f ? acc / L : 0.0f;
 }
 
 AttendPlan plan_attend(int64_t B, int Hq, int Hkv, int64_t n_quant, int64_t n_res) {

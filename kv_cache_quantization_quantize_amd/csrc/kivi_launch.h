@@ -48,11 +48,15 @@ struct AttendArgs {
     const float* v_zero;
     int64_t k_codes_bh_stride, v_codes_bh_stride;
     int64_t k_meta_bh_stride, v_meta_bh_stride;
-    int64_t n_quant;
+    int64_t n_quant;               // store tokens (varlen: the per-sequence bound)
     const uint16_t* k_res;
     const uint16_t* v_res;
     int64_t res_bh_stride;
-    int64_t n_res;
+    int64_t n_res;                 // residual tokens (varlen: the per-sequence bound)
+    // Variable-length batches: device int32 [B] per-sequence lengths, each
+    // clamped to [0, n_quant] / [0, n_res]; both null for a uniform batch.
+    const int32_t* seq_n_quant;
+    const int32_t* seq_n_res;
     float softmax_scale;
     float* out;
     void* workspace;

@@ -24,7 +24,7 @@ GROUP = 32
 # symbols of include/kivi.h and include/kivi_calib.h
 EXPORTS = (
     "kivi_quantize_keys", "kivi_quantize_values", "kivi_dequantize",
-    "kivi_decode_attend", "kivi_decode_attend_workspace_bytes",
+    "kivi_decode_attend", "kivi_decode_attend_varlen", "kivi_decode_attend_workspace_bytes",
     "kivi_status_string", "kivi_last_hip_error", "kivi_calib_copy",
 )
 
@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
         L.kivi_dequantize.argtypes = [sp, i64, i64, i64, vp, i64, vp]
         L.kivi_decode_attend.argtypes = [vp, i64, i32, i32, sp, sp, i64, vp, vp, i64, i64,
                                          ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
+        L.kivi_decode_attend_varlen.argtypes = [vp, i64, i32, i32, sp, sp, vp, i64, vp, vp, i64,
+                                                vp, i64, ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
         L.kivi_decode_attend_workspace_bytes.argtypes = [i64, i32, i32, i64, i64]
         L.kivi_decode_attend_workspace_bytes.restype = ctypes.c_size_t
         L.kivi_status_string.argtypes = [ctypes.c_int]
@@ -77,7 +79,8 @@ def lib() -> ctypes.CDLL:
         L.kivi_last_hip_error.argtypes = []
         L.kivi_calib_copy.argtypes = [vp, vp, ctypes.c_size_t, vp]
         for name in ("kivi_quantize_keys", "kivi_quantize_values", "kivi_dequantize",
-                     "kivi_decode_attend", "kivi_last_hip_error", "kivi_calib_copy"):
+                     "kivi_decode_attend", "kivi_decode_attend_varlen", "kivi_last_hip_error",
+                     "kivi_calib_copy"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -205,6 +208,45 @@ def decode_attend(q: torch.Tensor, k_store: Store, v_store: Store, n_quant: int,
         k_res.stride(0) if n_res > 0 else 0, n_res, float(softmax_scale), out.data_ptr(),
         workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream))
     _check(rc, "kivi_decode_attend")
+    return out
+
+
+def decode_attend_varlen(q: torch.Tensor, k_store: Store, v_store: Store, n_quant: torch.Tensor,
+                         max_n_quant: int, k_res: torch.Tensor | None, v_res: torch.Tensor | None,
+                         n_res: torch.Tensor, max_n_res: int, softmax_scale: float | None = None,
+                         out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                         stream=None) -> torch.Tensor:
+    """kivi_decode_attend_varlen: like decode_attend, with device int32 [B]
+    per-sequence lengths n_quant[b] <= max_n_quant and n_res[b] <= max_n_res."""
+    if q.dtype != torch.float16 or not q.is_cuda or q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous float16 device tensor [B][Hq][128]")
+    B, Hq, D = q.shape
+    for t, name in ((n_quant, "n_quant"), (n_res, "n_res")):
+        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous() or t.numel() != B:
+            raise ValueError(f"{name} must be a contiguous int32 device tensor of B elements")
+    Hkv = k_store.BH // B if B else 1
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if not (out.dtype == torch.float32 and out.is_contiguous() and tuple(out.shape) == (B, Hq, D)):
+        raise ValueError("out must be a contiguous float32 [B][Hq][128] tensor")
+    need = attend_workspace_bytes(B, Hq, Hkv, max_n_quant, max_n_res) if B else 0
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if max_n_res > 0:
+        _need_f16(k_res, "k_res")
+        _need_f16(v_res, "v_res")
+        if k_res.stride(0) != v_res.stride(0):
+            raise ValueError("k_res and v_res must share their slab stride")
+    ks, vs = k_store.c(), v_store.c()
+    rc = lib().kivi_decode_attend_varlen(
+        q.data_ptr(), B, Hq, Hkv, ctypes.byref(ks), ctypes.byref(vs), n_quant.data_ptr(), max_n_quant,
+        k_res.data_ptr() if max_n_res > 0 else None, v_res.data_ptr() if max_n_res > 0 else None,
+        k_res.stride(0) if max_n_res > 0 else 0, n_res.data_ptr(), max_n_res, float(softmax_scale),
+        out.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        _stream(stream))
+    _check(rc, "kivi_decode_attend_varlen")
     return out
 
 

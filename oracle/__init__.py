@@ -19,6 +19,9 @@ Parity status of each function (what pins it is in ``tests/test_oracle_*.py``):
   decode_attend ............... pinned (closed forms: one token, equal scores,
                                 shift invariance; torch float64 SDPA when the
                                 store is empty)
+  decode_attend_varlen ........ pinned (equal lengths reproduce decode_attend;
+                                each sequence equals its own batch of one and
+                                does not depend on the others; empty -> 0)
   flush_count ................. pinned (the flush/layer figures of the
                                 Generation 1 table)
 """
@@ -166,6 +169,15 @@ class Store:
         self.scale = np.full(meta_shape, fill_meta, np.float32)
         self.zero = np.full(meta_shape, fill_meta, np.float32)
 
+    def slabs(self, lo: int, hi: int) -> "Store":
+        """Slabs [lo, hi) as a store of their own (views, not copies)."""
+        sub = Store.__new__(Store)
+        sub.kind, sub.BH, sub.cap, sub.D, sub.bits, sub.G = self.kind, hi - lo, self.cap, self.D, \
+            self.bits, self.G
+        sub.words = self.words
+        sub.codes, sub.scale, sub.zero = self.codes[lo:hi], self.scale[lo:hi], self.zero[lo:hi]
+        return sub
+
     @property
     def codes_bh_stride(self) -> int:
         return self.codes.shape[1] * self.codes.shape[2]
@@ -251,6 +263,31 @@ def decode_attend(q, B: int, Hq: int, Hkv: int, kstore: Store | None, vstore: St
                                  _ptr(out, ctypes.c_double))
     if rc != 0:
         raise ValueError("oracle rejected the attend arguments")
+    return out
+
+
+def decode_attend_varlen(q, B: int, Hq: int, Hkv: int, kstore: Store | None,
+                         vstore: Store | None, n_quant, max_n_quant: int, k_res, v_res,
+                         n_res, max_n_res: int, softmax_scale: float | None = None) -> np.ndarray:
+    """float64 [B][Hq][D]: sequence b is ``decode_attend`` of a batch of one over
+    its own slabs b*Hkv .. b*Hkv + Hkv - 1, with n_quant[b] store tokens and
+    n_res[b] residual tokens, each clamped to [0, max]; a sequence left with no
+    token gets zeros (attention over an empty set is undefined)."""
+    q = _as_u16(q).reshape(B, Hq, -1)
+    out = np.zeros((B, Hq, q.shape[2]), np.float64)
+    if max_n_res > 0:
+        k_res, v_res = _as_u16(k_res), _as_u16(v_res)
+    for b in range(B):
+        nq = min(max(int(n_quant[b]), 0), max_n_quant)
+        nr = min(max(int(n_res[b]), 0), max_n_res)
+        if nq + nr == 0:
+            continue
+        lo, hi = b * Hkv, (b + 1) * Hkv
+        out[b] = decode_attend(q[b:b + 1], 1, Hq, Hkv,
+                               kstore.slabs(lo, hi) if nq else None,
+                               vstore.slabs(lo, hi) if nq else None, nq,
+                               k_res[lo:hi] if nr else None, v_res[lo:hi] if nr else None, nr,
+                               softmax_scale)[0]
     return out
 
 

@@ -144,3 +144,162 @@ def test_graph_replays_match_eager():
         torch.cuda.synchronize()
         assert torch.equal(out, want_out), f"replay {rep}"
         assert torch.equal(ks2.codes, want_codes), f"replay {rep}"
+
+
+# ---------------------------------------------------------------- varlen
+def _varlen_case(B, Hq, Hkv, cap, R, bits, seed, nq, nr):
+    c = _case(B, Hq, Hkv, cap, R, bits, seed)
+    c["nq_seq"] = np.asarray(nq, np.int32)
+    c["nr_seq"] = np.asarray(nr, np.int32)
+    return c
+
+
+def _varlen_gpu(c, max_nq=None, max_nr=None):
+    max_nq = c["nq"] if max_nq is None else max_nq
+    max_nr = c["nr"] if max_nr is None else max_nr
+    note(f"attend varlen B={c['B']} Hq={c['Hq']} max_n_quant={max_nq} max_n_res={max_nr} "
+         f"n_quant={c['nq_seq'].tolist()} n_res={c['nr_seq'].tolist()}")
+    nq_t = torch.from_numpy(c["nq_seq"]).cuda()
+    nr_t = torch.from_numpy(c["nr_seq"]).cuda()
+    out = kivi.decode_attend_varlen(c["q"], c["ks"], c["vs"], nq_t, max_nq, c["kr"], c["vr"],
+                                    nr_t, max_nr)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+def _varlen_oracle(c, seqs, max_nq, max_nr):
+    Hkv, bits, cap = c["Hkv"], c["bits"], c["cap"]
+    res = {}
+    for b in seqs:
+        sl = slice(b * Hkv, (b + 1) * Hkv)
+        ks = oracle.Store(oracle.KEYS, Hkv, cap, D, bits)
+        vs = oracle.Store(oracle.VALUES, Hkv, cap, D, bits)
+        oracle.quantize_keys(u16(c["kx"][sl]), ks, 0, want_recon=False)
+        oracle.quantize_values(u16(c["vx"][sl]), vs, 0, want_recon=False)
+        res[b] = oracle.decode_attend_varlen(u16(c["q"][b:b + 1]), 1, c["Hq"], Hkv, ks, vs,
+                                             c["nq_seq"][b:b + 1], max_nq, u16(c["kr"][sl]),
+                                             u16(c["vr"][sl]), c["nr_seq"][b:b + 1], max_nr)[0]
+    return res
+
+
+def _varlen_compare(c, seqs, max_nq=None, max_nr=None):
+    max_nq = c["nq"] if max_nq is None else max_nq
+    max_nr = c["nr"] if max_nr is None else max_nr
+    got = _varlen_gpu(c, max_nq, max_nr)
+    assert np.all(np.isfinite(got))
+    worst = 0.0
+    for b, ref in _varlen_oracle(c, seqs, max_nq, max_nr).items():
+        if not np.any(ref):
+            assert np.all(got[b] == 0.0), f"sequence {b} has no tokens: output must be 0"
+            continue
+        err = float(np.max(np.abs(got[b] - ref)))
+        worst = max(worst, err)
+        assert err <= TOL, f"sequence {b}: max-abs error {err:.3e}"
+    return worst
+
+
+def test_varlen_mixed_lengths_all_sequences():
+    """Ragged store lengths (not multiples of 32), empty store, empty residual,
+    an empty sequence, and lengths above the bound (clamped)."""
+    nq = [1000, 0, 33, 1024, 1, 517, 0, 999999, 64, 31, 2, 700]
+    nr = [128, 128, 5, 0, 1, 77, 0, 128, -3, 128, 0, 1000]
+    c = _varlen_case(12, 32, 8, 1024, 128, 4, 11, nq, nr)
+    _varlen_compare(c, range(12))
+
+
+def test_varlen_2bit_gqa8():
+    nq = [300, 0, 129, 64]
+    nr = [17, 40, 0, 3]
+    c = _varlen_case(4, 64, 8, 320, 40, 2, 12, nq, nr)
+    _varlen_compare(c, range(4))
+
+
+def test_varlen_batch32_long_context_sampled():
+    """B=32 requests of 1..16384 store tokens and 0..128 residual tokens."""
+    rng = np.random.default_rng(13)
+    nq = rng.integers(1, 16385, size=32)
+    nr = rng.integers(0, 129, size=32)
+    nq[0], nq[1] = 16384, 1
+    c = _varlen_case(32, 32, 8, 16384, 128, 4, 13, nq, nr)
+    _varlen_compare(c, [0, 1, 7, 31])
+
+
+def test_varlen_equal_lengths_match_uniform_call():
+    c = _case(4, 32, 8, 3000, 128, 4, seed=14)
+    c["nq_seq"] = np.full(4, 3000, np.int32)
+    c["nr_seq"] = np.full(4, 128, np.int32)
+    assert np.array_equal(_varlen_gpu(c), _gpu(c))
+
+
+def test_varlen_graph_replays_follow_device_lengths():
+    """A captured varlen call reads the lengths at replay time: after the
+    length tensors change between replays, each replay equals the eager call
+    with the new lengths."""
+    c = _case(4, 32, 8, 2048, 64, 4, seed=15)
+    nq_t = torch.zeros(4, dtype=torch.int32, device="cuda")
+    nr_t = torch.zeros(4, dtype=torch.int32, device="cuda")
+    out = torch.empty((4, 32, D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(kivi.attend_workspace_bytes(4, 32, 8, 2048, 64), dtype=torch.uint8, device="cuda")
+
+    def call(o):
+        kivi.decode_attend_varlen(c["q"], c["ks"], c["vs"], nq_t, 2048, c["kr"], c["vr"], nr_t, 64,
+                                  out=o, workspace=ws)
+
+    nq_t.copy_(torch.tensor([2048, 100, 0, 1500], dtype=torch.int32))
+    nr_t.copy_(torch.tensor([64, 10, 5, 0], dtype=torch.int32))
+    call(out)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(out)
+    for rep, (a, r) in enumerate([([2048, 100, 0, 1500], [64, 10, 5, 0]),
+                                  ([7, 2000, 33, 0], [0, 64, 1, 9]),
+                                  ([2048, 2048, 2048, 2048], [64, 64, 64, 64])]):
+        nq_t.copy_(torch.tensor(a, dtype=torch.int32))
+        nr_t.copy_(torch.tensor(r, dtype=torch.int32))
+        want = torch.empty_like(out)
+        call(want)
+        torch.cuda.synchronize()
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, want), f"replay {rep}"
+
+
+def test_varlen_rejects_missing_lengths():
+    c = _case(1, 32, 8, 64, 8, 4, seed=16)
+    nq = torch.tensor([64], dtype=torch.int32, device="cuda")
+    ks, vs = c["ks"].c(), c["vs"].c()
+    ws = torch.empty(kivi.attend_workspace_bytes(1, 32, 8, 64, 8), dtype=torch.uint8, device="cuda")
+    out = torch.empty((1, 32, D), dtype=torch.float32, device="cuda")
+    import ctypes
+    rc = kivi.lib().kivi_decode_attend_varlen(
+        c["q"].data_ptr(), 1, 32, 8, ctypes.byref(ks), ctypes.byref(vs), nq.data_ptr(), 64,
+        c["kr"].data_ptr(), c["vr"].data_ptr(), c["kr"].stride(0), None, 8, 0.088, out.data_ptr(),
+        ws.data_ptr(), ws.numel(), None)
+    assert rc == -1        # KIVI_ERR_NULL: nothing launched
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_two_pass_decode_once_matches_oracle(bits):
+    """The two-pass variant: kivi_dequantize of both stores into fp16 buffers
+    whose tails hold the residual window, then the attend over fp16 tokens
+    only (n_quant = 0, thousands of residual-path tokens) -- the same
+    definition as the fused call, so the same oracle and tolerance."""
+    B, S_kv, NR = 2, 4096 + 40, 128
+    c = _case(B, 32, 8, S_kv, NR, bits, seed=17)
+    BH = B * 8
+    kf = torch.empty((BH, S_kv + NR, D), dtype=torch.float16, device="cuda")
+    vf = torch.empty_like(kf)
+    kivi.dequantize(c["ks"], 0, S_kv, out=kf[:, :S_kv])
+    kivi.dequantize(c["vs"], 0, S_kv, out=vf[:, :S_kv])
+    kf[:, S_kv:] = c["kr"]
+    vf[:, S_kv:] = c["vr"]
+    note(f"two-pass attend B={B} n_res={S_kv + NR} bits={bits}")
+    got = kivi.decode_attend(c["q"], c["ks"], c["vs"], 0, kf, vf, S_kv + NR)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy().astype(np.float64)
+    for b in range(B):
+        err = float(np.max(np.abs(got[b] - _oracle(c, b))))
+        assert err <= TOL, f"sequence {b}: max-abs error {err:.3e}"

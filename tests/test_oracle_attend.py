@@ -110,3 +110,53 @@ def test_common_key_shift_leaves_output_unchanged(orc):
     o1 = orc.decode_attend(q, 1, 4, 1, None, None, 0, _f16(k), v, N)
     o2 = orc.decode_attend(q, 1, 4, 1, None, None, 0, _f16(k + a), v, N)
     assert np.max(np.abs(o1 - o2)) < 1e-12
+
+
+def test_varlen_matches_torch_sdpa_per_sequence(orc):
+    """Each sequence attends over its own prefix of the store and of the
+    residual window: torch's float64 SDPA on exactly those rows."""
+    rng = np.random.default_rng(7)
+    B, Hq, Hkv, cap, R = 4, 8, 2, 96, 24
+    ks, vs = _stores(orc, rng, B * Hkv, cap)
+    q = _f16(rng.standard_normal((B, Hq, D)))
+    kr = _f16(rng.standard_normal((B * Hkv, R, D)))
+    vr = _f16(rng.standard_normal((B * Hkv, R, D)))
+    nq = np.array([96, 0, 33, 70], np.int32)
+    nr = np.array([0, 24, 7, 24], np.int32)
+    got = orc.decode_attend_varlen(q, B, Hq, Hkv, ks, vs, nq, cap, kr, vr, nr, R)
+    kd, vd = _w(orc.dequantize(ks, 0, cap)), _w(orc.dequantize(vs, 0, cap))
+    for b in range(B):
+        sl = slice(b * Hkv, (b + 1) * Hkv)
+        kk = np.concatenate([kd[sl, :nq[b]], _w(kr[sl, :nr[b]])], axis=1)
+        vv = np.concatenate([vd[sl, :nq[b]], _w(vr[sl, :nr[b]])], axis=1)
+        want = _sdpa(_w(q[b:b + 1]), kk, vv, Hq // Hkv)[0]
+        assert np.max(np.abs(got[b] - want)) < 1e-12, b
+
+
+def test_varlen_equal_lengths_is_the_uniform_call(orc):
+    rng = np.random.default_rng(8)
+    B, Hq, Hkv, nq, nr = 3, 8, 2, 64, 9
+    ks, vs = _stores(orc, rng, B * Hkv, nq)
+    q = _f16(rng.standard_normal((B, Hq, D)))
+    kr = _f16(rng.standard_normal((B * Hkv, 16, D)))
+    vr = _f16(rng.standard_normal((B * Hkv, 16, D)))
+    want = orc.decode_attend(q, B, Hq, Hkv, ks, vs, nq, kr, vr, nr)
+    got = orc.decode_attend_varlen(q, B, Hq, Hkv, ks, vs, np.full(B, nq), nq, kr, vr,
+                                   np.full(B, nr), 16)
+    assert np.array_equal(got, want)
+
+
+def test_varlen_clamps_lengths_and_zeroes_empty_sequences(orc):
+    """Lengths are clamped to [0, max]; a sequence left empty outputs 0."""
+    rng = np.random.default_rng(9)
+    B, Hq, Hkv, cap = 3, 4, 1, 64
+    ks, vs = _stores(orc, rng, B * Hkv, cap)
+    q = _f16(rng.standard_normal((B, Hq, D)))
+    kr = _f16(rng.standard_normal((B * Hkv, 8, D)))
+    vr = _f16(rng.standard_normal((B * Hkv, 8, D)))
+    got = orc.decode_attend_varlen(q, B, Hq, Hkv, ks, vs, np.array([1000, -5, 0]), 40, kr, vr,
+                                   np.array([3, 99, -1]), 8)
+    want = orc.decode_attend_varlen(q, B, Hq, Hkv, ks, vs, np.array([40, 0, 0]), 40, kr, vr,
+                                    np.array([3, 8, 0]), 8)
+    assert np.array_equal(got, want)
+    assert np.all(got[2] == 0.0) and np.all(np.abs(got[0]) > 0)
