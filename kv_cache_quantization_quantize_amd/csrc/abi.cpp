@@ -11,8 +11,18 @@
 #include <limits>
 
 namespace {
-
 thread_local int g_last_hip_error = 0;
+}  // namespace
+
+namespace kivi {
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return KIVI_OK;
+    g_last_hip_error = static_cast<int>(e);
+    return KIVI_ERR_HIP;
+}
+}  // namespace kivi
+
+namespace {
 
 constexpr int64_t kD = 128;
 constexpr int64_t kG = 32;
@@ -21,11 +31,7 @@ constexpr int64_t kMaxAttendTokens = int64_t{1} << 24;   // attend offsets stay 
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int finish(hipError_t e) {
-    if (e == hipSuccess) return KIVI_OK;
-    g_last_hip_error = static_cast<int>(e);
-    return KIVI_ERR_HIP;
-}
+int finish(hipError_t e) { return kivi::hip_status(e); }
 
 int64_t words_per_token(int bits) { return kD * bits / 32; }
 
@@ -122,16 +128,19 @@ size_t kivi_decode_attend_workspace_bytes(int64_t B, int32_t Hq, int32_t Hkv,
 
 }  // extern "C"
 
-namespace {
+namespace kivi {
 
-// Shared validation and launch of the uniform and variable-length attends;
-// n_quant / n_res are the uniform counts or the per-sequence bounds.
-int decode_attend(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
-                  const kivi_store* k, const kivi_store* v, int64_t n_quant,
-                  const uint16_t* k_res, const uint16_t* v_res, int64_t res_bh_stride,
-                  int64_t n_res, const int32_t* seq_n_quant, const int32_t* seq_n_res,
-                  float softmax_scale, float* out, void* workspace, size_t workspace_bytes,
-                  hipStream_t stream) {
+// Shared validation and launch of the uniform and variable-length attends
+// and of the cache's attend; n_quant / n_res are the uniform counts or the
+// per-sequence bounds.  res_ring == 0 means a linear residual window;
+// otherwise residual token i of a slab is row (res_head + i) mod res_ring.
+int decode_attend_entry(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
+                        const kivi_store* k, const kivi_store* v, int64_t n_quant,
+                        const uint16_t* k_res, const uint16_t* v_res, int64_t res_bh_stride,
+                        int64_t n_res, int64_t res_head, int64_t res_ring,
+                        const int32_t* seq_n_quant, const int32_t* seq_n_res,
+                        float softmax_scale, float* out, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || n_quant < 0 || n_res < 0) return KIVI_ERR_SHAPE;
     if (Hq % Hkv != 0) return KIVI_ERR_SHAPE;
     const int group = Hq / Hkv;
@@ -147,9 +156,12 @@ int decode_attend(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
     if (B == 0) return KIVI_OK;
     if (!q || !out) return KIVI_ERR_NULL;
     if (!aligned16(q) || !aligned16(out)) return KIVI_ERR_ALIGN;
+    if (res_ring < 0 || res_head < 0 || (res_ring > 0 && (res_head >= res_ring || n_res > res_ring)) ||
+        (res_ring == 0 && res_head != 0) || res_ring >= kMaxAttendTokens) return KIVI_ERR_SHAPE;
     if (n_res > 0) {
-        if ((rc = check_f16_tensor(k_res, slabs, n_res, res_bh_stride)) != KIVI_OK) return rc;
-        if ((rc = check_f16_tensor(v_res, slabs, n_res, res_bh_stride)) != KIVI_OK) return rc;
+        const int64_t rows = res_ring > 0 ? res_ring : n_res;
+        if ((rc = check_f16_tensor(k_res, slabs, rows, res_bh_stride)) != KIVI_OK) return rc;
+        if ((rc = check_f16_tensor(v_res, slabs, rows, res_bh_stride)) != KIVI_OK) return rc;
     }
     const kivi::AttendPlan plan = kivi::plan_attend(B, Hq, Hkv, n_quant, n_res);
     if (!workspace || workspace_bytes < plan.workspace_bytes) return KIVI_ERR_WORKSPACE;
@@ -167,13 +179,15 @@ int decode_attend(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
     a.v_res = n_res > 0 ? v_res : q;
     a.res_bh_stride = n_res > 0 ? res_bh_stride : 0;
     a.n_res = n_res;
+    a.res_head = static_cast<int32_t>(res_head);
+    a.res_ring = res_ring > 0 ? static_cast<int32_t>(res_ring) : (1 << 30);
     a.seq_n_quant = seq_n_quant; a.seq_n_res = seq_n_res;
     a.softmax_scale = softmax_scale; a.out = out;
     a.workspace = workspace; a.bits = k->bits;
     return finish(kivi::launch_decode_attend(a, plan, stream));
 }
 
-}  // namespace
+}  // namespace kivi
 
 extern "C" {
 
@@ -182,8 +196,9 @@ int kivi_decode_attend(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
                        const uint16_t* k_res, const uint16_t* v_res, int64_t res_bh_stride,
                        int64_t n_res, float softmax_scale, float* out,
                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    return decode_attend(q, B, Hq, Hkv, k, v, n_quant, k_res, v_res, res_bh_stride, n_res,
-                         nullptr, nullptr, softmax_scale, out, workspace, workspace_bytes, stream);
+    return kivi::decode_attend_entry(q, B, Hq, Hkv, k, v, n_quant, k_res, v_res, res_bh_stride,
+                                     n_res, 0, 0, nullptr, nullptr, softmax_scale, out, workspace,
+                                     workspace_bytes, stream);
 }
 
 int kivi_decode_attend_varlen(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
@@ -196,8 +211,9 @@ int kivi_decode_attend_varlen(const uint16_t* q, int64_t B, int32_t Hq, int32_t 
     if (B > 0 && (!n_quant || !n_res)) return KIVI_ERR_NULL;
     if ((reinterpret_cast<uintptr_t>(n_quant) & 3u) != 0 ||
         (reinterpret_cast<uintptr_t>(n_res) & 3u) != 0) return KIVI_ERR_ALIGN;
-    return decode_attend(q, B, Hq, Hkv, k, v, max_n_quant, k_res, v_res, res_bh_stride, max_n_res,
-                         n_quant, n_res, softmax_scale, out, workspace, workspace_bytes, stream);
+    return kivi::decode_attend_entry(q, B, Hq, Hkv, k, v, max_n_quant, k_res, v_res,
+                                     res_bh_stride, max_n_res, 0, 0, n_quant, n_res,
+                                     softmax_scale, out, workspace, workspace_bytes, stream);
 }
 
 const char* kivi_status_string(int status) {

@@ -384,14 +384,20 @@ __device__ __forceinline__ void store_step(const StepLoad& L, Smem& sm, SoftStat
 }
 
 // One step of fp16 residual tokens [t0, t0 + 32), tokens at or past n_res masked.
+// Residual token i of the slab is row (head + i) mod ring (head < ring).
+__device__ __forceinline__ int ring_row(int tok, int head, int ring) {
+    const int r = tok + head;
+    return r >= ring ? r - ring : r;
+}
+
 __device__ __forceinline__ void residual_step(const uint16_t* kr, const uint16_t* vr, const Smem& sm,
                                               SoftState& st, int t0, int n_res, float c2,
-                                              int l, int n, int q) {
+                                              int l, int n, int q, int head, int ring) {
     const int last = n_res - 1;
     float4_t acc_s[2] = {float4_t{0.0f, 0.0f, 0.0f, 0.0f}, float4_t{0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-        const int tok = min(t0 + 16 * blk + n, last);
+        const int tok = ring_row(min(t0 + 16 * blk + n, last), head, ring);
         const uint4* src = reinterpret_cast<const uint4*>(kr + tok * kHeadDim + 32 * q);
         uint32_t rn[16];
 #pragma unroll
@@ -417,7 +423,7 @@ __device__ __forceinline__ void residual_step(const uint16_t* kr, const uint16_t
     uint4 vrow[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-        const int tok = min(t0 + pv_token(q, s), last);
+        const int tok = ring_row(min(t0 + pv_token(q, s), last), head, ring);
         vrow[s] = *reinterpret_cast<const uint4*>(vr + tok * kHeadDim + 8 * n);
     }
 #pragma unroll
@@ -541,7 +547,8 @@ __global__ __launch_bounds__(64) KIVI_ATTEND_OCCUPANCY void attend_partial_kerne
         const int r1 = min(r0 + spw_r * kStep, nr);
         const uint16_t* kr = a.k_res + bkv * a.res_bh_stride;
         const uint16_t* vr = a.v_res + bkv * a.res_bh_stride;
-        for (int t0 = r0; t0 < r1; t0 += kStep) residual_step(kr, vr, sm, st, t0, r1, c2, l, n, q);
+        for (int t0 = r0; t0 < r1; t0 += kStep)
+            residual_step(kr, vr, sm, st, t0, r1, c2, l, n, q, a.res_head, a.res_ring);
     }
 
     // ---- partial (m, l, o) of head n: lane (q, n) holds channels 32q + 8r + i

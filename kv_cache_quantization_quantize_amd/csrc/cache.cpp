@@ -1,0 +1,240 @@
+// cache.cpp -- the KV cache of include/kivi_cache.h: layout of the stores and
+// fp16 residual rings in one caller-owned device buffer, the flush rule, and
+// the per-step append / attend / end-of-step calls.  Host code only; the
+// kernels are the flush and attend kernels of the library plus the row copy
+// in cache.hip.  Every call validates everything before its first launch.
+#include <hip/hip_runtime.h>
+
+#include "kivi.h"
+#include "kivi_cache.h"
+#include "kivi_launch.h"
+
+namespace {
+
+constexpr int64_t kD = 128;
+constexpr int64_t kG = 32;
+constexpr int64_t kMaxTokens = int64_t{1} << 24;      // the attend's 32-bit offsets
+constexpr int64_t kMaxSlabs = int64_t{1} << 31;
+
+int64_t align256(int64_t x) { return (x + 255) & ~int64_t{255}; }
+
+struct Layout {
+    int64_t slabs, ring, words;
+    int64_t kc, ks, kz, vc, vs, vz, kr, vr, total;    // byte offsets / size
+};
+
+bool valid(const kivi_cache_config* c) {
+    if (!c) return false;
+    if (c->layers < 1 || c->layers > KIVI_CACHE_MAX_LAYERS || c->batch < 1 || c->kv_heads < 1) return false;
+    if (c->bits != 2 && c->bits != 4) return false;
+    if (c->head_dim != kD || c->group_size != kG) return false;
+    if (c->flush_tokens <= 0 || c->flush_tokens % kG != 0) return false;
+    if (c->residual_length < 0 || c->residual_length % c->flush_tokens != 0) return false;
+    if (c->store_capacity < 0 || c->store_capacity % c->flush_tokens != 0) return false;
+    if (c->store_capacity >= kMaxTokens) return false;
+    if (int64_t{c->residual_length} + c->flush_tokens >= kMaxTokens) return false;
+    const int64_t slabs = int64_t{c->layers} * c->batch * c->kv_heads;
+    return slabs < kMaxSlabs;
+}
+
+Layout layout(const kivi_cache_config& c) {
+    Layout L;
+    L.slabs = int64_t{c.layers} * c.batch * c.kv_heads;
+    L.ring = int64_t{c.residual_length} + c.flush_tokens;
+    L.words = kD * c.bits / 32;
+    const int64_t cap = c.store_capacity;
+    int64_t off = 0;
+    auto take = [&off](int64_t bytes) { const int64_t at = off; off = align256(off + bytes); return at; };
+    L.kc = take(L.slabs * cap * L.words * 4);
+    L.ks = take(L.slabs * (cap / kG) * kD * 4);
+    L.kz = take(L.slabs * (cap / kG) * kD * 4);
+    L.vc = take(L.slabs * cap * L.words * 4);
+    L.vs = take(L.slabs * cap * (kD / kG) * 4);
+    L.vz = take(L.slabs * cap * (kD / kG) * 4);
+    L.kr = take(L.slabs * L.ring * kD * 2);
+    L.vr = take(L.slabs * L.ring * kD * 2);
+    L.total = off;
+    return L;
+}
+
+int64_t seq_slabs(const kivi_cache* c) { return int64_t{c->cfg.batch} * c->cfg.kv_heads; }
+
+bool appended(const kivi_cache* c, int layer) { return (c->appended[layer >> 6] >> (layer & 63)) & 1u; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int finish(hipError_t e) { return kivi::hip_status(e); }
+
+// The slabs of one layer as a store of their own.
+kivi_store layer_store(const kivi_store& s, int64_t slab0) {
+    kivi_store r = s;
+    r.codes = s.codes + slab0 * s.codes_bh_stride;
+    r.scale = s.scale + slab0 * s.meta_bh_stride;
+    r.zero = s.zero + slab0 * s.meta_bh_stride;
+    return r;
+}
+
+// Quantized tokens of a sequence of S tokens: the whole flush units older
+// than the newest R tokens.
+int64_t quantized_tokens(const kivi_cache_config& c, int64_t S) {
+    if (S < c.residual_length) return 0;
+    return (S - c.residual_length) / c.flush_tokens * c.flush_tokens;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kivi_cache_device_bytes(const kivi_cache_config* cfg) {
+    if (!valid(cfg)) return 0;
+    return static_cast<size_t>(layout(*cfg).total);
+}
+
+int kivi_cache_init(kivi_cache* cache, const kivi_cache_config* cfg, void* device, size_t bytes) {
+    if (!cache || !cfg || !device) return KIVI_ERR_NULL;
+    if (!valid(cfg)) return KIVI_ERR_UNSUPPORTED;
+    if ((reinterpret_cast<uintptr_t>(device) & 255u) != 0) return KIVI_ERR_ALIGN;
+    const Layout L = layout(*cfg);
+    if (bytes < static_cast<size_t>(L.total)) return KIVI_ERR_WORKSPACE;
+    char* base = static_cast<char*>(device);
+    kivi_cache c = {};
+    c.cfg = *cfg;
+    const int64_t cap = cfg->store_capacity;
+    c.k_store = {reinterpret_cast<uint32_t*>(base + L.kc), reinterpret_cast<float*>(base + L.ks),
+                 reinterpret_cast<float*>(base + L.kz), cap * L.words, (cap / kG) * kD, cap,
+                 cfg->bits, cfg->group_size, cfg->head_dim, KIVI_KEYS};
+    c.v_store = {reinterpret_cast<uint32_t*>(base + L.vc), reinterpret_cast<float*>(base + L.vs),
+                 reinterpret_cast<float*>(base + L.vz), cap * L.words, cap * (kD / kG), cap,
+                 cfg->bits, cfg->group_size, cfg->head_dim, KIVI_VALUES};
+    c.k_ring = reinterpret_cast<uint16_t*>(base + L.kr);
+    c.v_ring = reinterpret_cast<uint16_t*>(base + L.vr);
+    c.ring = L.ring;
+    *cache = c;
+    return KIVI_OK;
+}
+
+int kivi_cache_prefill(kivi_cache* cache, const uint16_t* k, const uint16_t* v,
+                       int64_t x_bh_stride, int64_t S, hipStream_t stream) {
+    if (!cache) return KIVI_ERR_NULL;
+    if (!valid(&cache->cfg)) return KIVI_ERR_UNSUPPORTED;
+    if (S < 0 || cache->length != 0) return KIVI_ERR_SHAPE;
+    for (uint64_t w : cache->appended)
+        if (w) return KIVI_ERR_SHAPE;                  // a step is in progress
+    const int64_t Q = quantized_tokens(cache->cfg, S);
+    const int64_t nres = S - Q;
+    if (Q > cache->cfg.store_capacity || nres > cache->ring) return KIVI_ERR_SHAPE;
+    if (S == 0) return KIVI_OK;
+    const int64_t slabs = layout(cache->cfg).slabs;
+    if (!k || !v) return KIVI_ERR_NULL;
+    if (!aligned16(k) || !aligned16(v) || x_bh_stride % 8 != 0) return KIVI_ERR_ALIGN;
+    if (slabs > 1 && x_bh_stride < S * kD) return KIVI_ERR_SHAPE;
+    if ((slabs * ((Q + 31) / 32) + 3) / 4 >= kMaxSlabs) return KIVI_ERR_SHAPE;
+    if (slabs * nres * (kD * 2 / 16) / 256 >= kMaxSlabs) return KIVI_ERR_SHAPE;
+
+    int rc = KIVI_OK;
+    if (Q > 0) {
+        rc = kivi_quantize_keys(k, slabs, Q, x_bh_stride, &cache->k_store, 0, nullptr, 0, stream);
+        if (rc == KIVI_OK)
+            rc = kivi_quantize_values(v, slabs, Q, x_bh_stride, &cache->v_store, 0, nullptr, 0, stream);
+        if (rc != KIVI_OK) return rc;
+    }
+    if (nres > 0) {
+        const kivi::RowCopy kc = {k + Q * kD, x_bh_stride, cache->k_ring, cache->ring * kD};
+        const kivi::RowCopy vc = {v + Q * kD, x_bh_stride, cache->v_ring, cache->ring * kD};
+        rc = finish(kivi::launch_copy_rows(kc, vc, slabs, nres, stream));
+        if (rc != KIVI_OK) return rc;
+    }
+    cache->length = S;
+    cache->n_quant = Q;
+    cache->n_res = nres;
+    cache->head = 0;
+    return KIVI_OK;
+}
+
+int kivi_cache_append(kivi_cache* cache, int32_t layer, const uint16_t* k_new,
+                      const uint16_t* v_new, hipStream_t stream) {
+    if (!cache) return KIVI_ERR_NULL;
+    if (!valid(&cache->cfg)) return KIVI_ERR_UNSUPPORTED;
+    if (layer < 0 || layer >= cache->cfg.layers || appended(cache, layer)) return KIVI_ERR_SHAPE;
+    if (cache->n_res >= cache->ring) return KIVI_ERR_SHAPE;        // no free ring row
+    if (!k_new || !v_new) return KIVI_ERR_NULL;
+    if (!aligned16(k_new) || !aligned16(v_new)) return KIVI_ERR_ALIGN;
+    const int64_t slab0 = layer * seq_slabs(cache);
+    int64_t row = cache->head + cache->n_res;
+    if (row >= cache->ring) row -= cache->ring;
+    const int64_t rs = cache->ring * kD;
+    const kivi::RowCopy kc = {k_new, kD, cache->k_ring + slab0 * rs + row * kD, rs};
+    const kivi::RowCopy vc = {v_new, kD, cache->v_ring + slab0 * rs + row * kD, rs};
+    const int rc = finish(kivi::launch_copy_rows(kc, vc, seq_slabs(cache), 1, stream));
+    if (rc != KIVI_OK) return rc;
+    cache->appended[layer >> 6] |= uint64_t{1} << (layer & 63);
+    return KIVI_OK;
+}
+
+int kivi_cache_attend(const kivi_cache* cache, int32_t layer, const uint16_t* q, int32_t Hq,
+                      float softmax_scale, float* out, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+    if (!cache) return KIVI_ERR_NULL;
+    if (!valid(&cache->cfg)) return KIVI_ERR_UNSUPPORTED;
+    if (layer < 0 || layer >= cache->cfg.layers || !appended(cache, layer)) return KIVI_ERR_SHAPE;
+    const int64_t slab0 = layer * seq_slabs(cache);
+    const kivi_store ks = layer_store(cache->k_store, slab0);
+    const kivi_store vs = layer_store(cache->v_store, slab0);
+    const int64_t rs = cache->ring * kD;
+    return kivi::decode_attend_entry(q, cache->cfg.batch, Hq, cache->cfg.kv_heads, &ks, &vs,
+                                     cache->n_quant, cache->k_ring + slab0 * rs,
+                                     cache->v_ring + slab0 * rs, rs, cache->n_res + 1, cache->head,
+                                     cache->ring, nullptr, nullptr, softmax_scale, out, workspace,
+                                     workspace_bytes, stream);
+}
+
+size_t kivi_cache_attend_workspace_bytes(const kivi_cache* cache, int32_t Hq) {
+    if (!cache || !valid(&cache->cfg) || Hq <= 0) return 0;
+    // the largest need over every (quantized, fp16) split the cache can reach
+    size_t need = 0;
+    const int64_t F = cache->cfg.flush_tokens;
+    for (int64_t nq = 0; nq <= cache->cfg.store_capacity; nq += F)
+        for (int64_t nr = 1; nr <= cache->ring; ++nr) {
+            const size_t b = kivi_decode_attend_workspace_bytes(cache->cfg.batch, Hq, cache->cfg.kv_heads,
+                                                                nq, nr);
+            need = b > need ? b : need;
+        }
+    return need;
+}
+
+int kivi_cache_end_step(kivi_cache* cache, hipStream_t stream) {
+    if (!cache) return KIVI_ERR_NULL;
+    if (!valid(&cache->cfg)) return KIVI_ERR_UNSUPPORTED;
+    for (int l = 0; l < cache->cfg.layers; ++l)
+        if (!appended(cache, l)) return KIVI_ERR_SHAPE;
+    const int64_t F = cache->cfg.flush_tokens;
+    const int64_t n_res = cache->n_res + 1;
+    const bool flush = n_res == cache->ring;
+    if (flush && cache->n_quant + F > cache->cfg.store_capacity) return KIVI_ERR_SHAPE;
+    int launches = 0;
+    if (flush) {
+        // the oldest F fp16 tokens of every slab of every layer: ring rows
+        // head .. head + F - 1 (head and the ring length are multiples of F)
+        const int64_t slabs = layout(cache->cfg).slabs;
+        const int64_t rs = cache->ring * kD;
+        int rc = kivi_quantize_keys(cache->k_ring + cache->head * kD, slabs, F, rs, &cache->k_store,
+                                    cache->n_quant, nullptr, 0, stream);
+        if (rc == KIVI_OK)
+            rc = kivi_quantize_values(cache->v_ring + cache->head * kD, slabs, F, rs, &cache->v_store,
+                                      cache->n_quant, nullptr, 0, stream);
+        if (rc != KIVI_OK) return rc;
+        launches = 2;
+    }
+    cache->length += 1;
+    cache->n_res = n_res;
+    if (flush) {
+        cache->n_quant += F;
+        cache->n_res -= F;
+        cache->head += F;
+        if (cache->head == cache->ring) cache->head = 0;
+    }
+    for (uint64_t& w : cache->appended) w = 0;
+    return launches;
+}
+
+}  // extern "C"

@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "kivi.h"
+
 namespace kivi {
 
 struct FlushArgs {
@@ -53,6 +55,10 @@ struct AttendArgs {
     const uint16_t* v_res;
     int64_t res_bh_stride;
     int64_t n_res;                 // residual tokens (varlen: the per-sequence bound)
+    // Residual token i of a slab sits in row (res_head + i) mod res_ring of
+    // the slab (a ring of res_ring rows); a linear window has res_head = 0
+    // and res_ring >= n_res.
+    int32_t res_head, res_ring;
     // Variable-length batches: device int32 [B] per-sequence lengths, each
     // clamped to [0, n_quant] / [0, n_res]; both null for a uniform batch.
     const int32_t* seq_n_quant;
@@ -79,6 +85,30 @@ hipError_t launch_key_flush(const FlushArgs& a, hipStream_t stream);
 hipError_t launch_value_flush(const FlushArgs& a, hipStream_t stream);
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t stream);
 hipError_t launch_decode_attend(const AttendArgs& a, const AttendPlan& p, hipStream_t stream);
+// Copies n_rows token rows (head_dim fp16 each) of every slab from src to
+// dst for keys and values at once (one launch).
+struct RowCopy {
+    const uint16_t* src;
+    int64_t src_bh_stride;         // elements between slabs
+    uint16_t* dst;
+    int64_t dst_bh_stride;
+};
+hipError_t launch_copy_rows(const RowCopy& k, const RowCopy& v, int64_t slabs, int64_t n_rows,
+                            hipStream_t stream);
+
+// The attend entry point behind kivi_decode_attend(_varlen) and the cache:
+// validates on the host, then launches (see abi.cpp).
+int decode_attend_entry(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
+                        const kivi_store* k, const kivi_store* v, int64_t n_quant,
+                        const uint16_t* k_res, const uint16_t* v_res, int64_t res_bh_stride,
+                        int64_t n_res, int64_t res_head, int64_t res_ring,
+                        const int32_t* seq_n_quant, const int32_t* seq_n_res,
+                        float softmax_scale, float* out, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+// KIVI_OK, or KIVI_ERR_HIP after recording e for kivi_last_hip_error.
+int hip_status(hipError_t e);
+
 hipError_t launch_calib_copy(const void* src, void* dst, size_t n_bytes, hipStream_t stream);
 
 }  // namespace kivi

@@ -21,12 +21,15 @@ KIVI_VALUES = 1
 HEAD_DIM = 128
 GROUP = 32
 
-# symbols of include/kivi.h and include/kivi_calib.h
+# symbols of include/kivi.h, include/kivi_cache.h and include/kivi_calib.h
 EXPORTS = (
     "kivi_quantize_keys", "kivi_quantize_values", "kivi_dequantize",
     "kivi_decode_attend", "kivi_decode_attend_varlen", "kivi_decode_attend_workspace_bytes",
     "kivi_status_string", "kivi_last_hip_error", "kivi_calib_copy",
+    "kivi_cache_device_bytes", "kivi_cache_init", "kivi_cache_prefill", "kivi_cache_append",
+    "kivi_cache_attend", "kivi_cache_attend_workspace_bytes", "kivi_cache_end_step",
 )
+CACHE_MAX_LAYERS = 256
 
 
 class KiviError(RuntimeError):
@@ -49,6 +52,24 @@ class CStore(ctypes.Structure):
         ("group_size", ctypes.c_int32),
         ("head_dim", ctypes.c_int32),
         ("kind", ctypes.c_int32),
+    ]
+
+
+class CCacheConfig(ctypes.Structure):
+    _fields_ = [
+        ("layers", ctypes.c_int32), ("batch", ctypes.c_int32), ("kv_heads", ctypes.c_int32),
+        ("bits", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("group_size", ctypes.c_int32),
+        ("residual_length", ctypes.c_int32), ("flush_tokens", ctypes.c_int32),
+        ("store_capacity", ctypes.c_int64),
+    ]
+
+
+class CCache(ctypes.Structure):
+    _fields_ = [
+        ("cfg", CCacheConfig), ("k_store", CStore), ("v_store", CStore),
+        ("k_ring", ctypes.c_void_p), ("v_ring", ctypes.c_void_p), ("ring", ctypes.c_int64),
+        ("length", ctypes.c_int64), ("n_quant", ctypes.c_int64), ("n_res", ctypes.c_int64),
+        ("head", ctypes.c_int64), ("appended", ctypes.c_uint64 * (CACHE_MAX_LAYERS // 64)),
     ]
 
 
@@ -78,9 +99,20 @@ def lib() -> ctypes.CDLL:
         L.kivi_status_string.restype = ctypes.c_char_p
         L.kivi_last_hip_error.argtypes = []
         L.kivi_calib_copy.argtypes = [vp, vp, ctypes.c_size_t, vp]
+        cp, cfgp = ctypes.POINTER(CCache), ctypes.POINTER(CCacheConfig)
+        L.kivi_cache_device_bytes.argtypes = [cfgp]
+        L.kivi_cache_device_bytes.restype = ctypes.c_size_t
+        L.kivi_cache_init.argtypes = [cp, cfgp, vp, ctypes.c_size_t]
+        L.kivi_cache_prefill.argtypes = [cp, vp, vp, i64, i64, vp]
+        L.kivi_cache_append.argtypes = [cp, i32, vp, vp, vp]
+        L.kivi_cache_attend.argtypes = [cp, i32, vp, i32, ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
+        L.kivi_cache_attend_workspace_bytes.argtypes = [cp, i32]
+        L.kivi_cache_attend_workspace_bytes.restype = ctypes.c_size_t
+        L.kivi_cache_end_step.argtypes = [cp, vp]
         for name in ("kivi_quantize_keys", "kivi_quantize_values", "kivi_dequantize",
                      "kivi_decode_attend", "kivi_decode_attend_varlen", "kivi_last_hip_error",
-                     "kivi_calib_copy"):
+                     "kivi_calib_copy", "kivi_cache_init", "kivi_cache_prefill", "kivi_cache_append",
+                     "kivi_cache_attend", "kivi_cache_end_step"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -255,3 +287,104 @@ def calib_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
     n = src.numel() * src.element_size()
     assert dst.numel() * dst.element_size() >= n
     _check(lib().kivi_calib_copy(src.data_ptr(), dst.data_ptr(), n, _stream(stream)), "kivi_calib_copy")
+
+
+class Cache:
+    """kivi_cache (include/kivi_cache.h): every layer's stores and fp16
+    residual rings in one device buffer, with the per-step calls.  The
+    device buffer is a torch uint8 tensor this object owns; all state
+    changes happen in the C calls."""
+
+    def __init__(self, layers: int, batch: int, kv_heads: int, store_capacity: int, bits: int = 4,
+                 residual_length: int = 128, flush_tokens: int = GROUP, device="cuda"):
+        self.cfg = CCacheConfig(layers, batch, kv_heads, bits, HEAD_DIM, GROUP, residual_length,
+                                flush_tokens, store_capacity)
+        n = int(lib().kivi_cache_device_bytes(ctypes.byref(self.cfg)))
+        if n == 0:
+            raise KiviError(-3, "kivi_cache_device_bytes")
+        self.buffer = torch.empty(n + 256, dtype=torch.uint8, device=device)
+        pad = (-self.buffer.data_ptr()) % 256
+        self.buffer = self.buffer[pad:pad + n]
+        self.c = CCache()
+        _check(lib().kivi_cache_init(ctypes.byref(self.c), ctypes.byref(self.cfg),
+                                     self.buffer.data_ptr(), n), "kivi_cache_init")
+        self.slabs = layers * batch * kv_heads
+
+    # ---- state (read from the C struct)
+    length = property(lambda self: self.c.length)
+    n_quant = property(lambda self: self.c.n_quant)
+    n_res = property(lambda self: self.c.n_res)
+    head = property(lambda self: self.c.head)
+    ring = property(lambda self: self.c.ring)
+
+    def _view(self, ptr: int, dtype, shape):
+        off = ptr - self.buffer.data_ptr()
+        n = 1
+        for d in shape:
+            n *= d
+        nbytes = n * torch.empty((), dtype=dtype).element_size()
+        return self.buffer[off:off + nbytes].view(dtype).view(shape)
+
+    def stores(self) -> tuple[Store, Store]:
+        """The key and value stores of all layers (torch views of the buffer)."""
+        out = []
+        for cs, kind in ((self.c.k_store, KIVI_KEYS), (self.c.v_store, KIVI_VALUES)):
+            cap, words = cs.cap, HEAD_DIM * cs.bits // 32
+            meta = (self.slabs, cap // GROUP, HEAD_DIM) if kind == KIVI_KEYS else \
+                (self.slabs, cap, HEAD_DIM // GROUP)
+            out.append(Store(kind, self.slabs, cap, cs.bits,
+                             codes=self._view(cs.codes, torch.int32, (self.slabs, cap, words)),
+                             scale=self._view(cs.scale, torch.float32, meta),
+                             zero=self._view(cs.zero, torch.float32, meta)))
+        return out[0], out[1]
+
+    def rings(self) -> tuple[torch.Tensor, torch.Tensor]:
+        """fp16 [slabs][ring][128] residual rings (torch views of the buffer)."""
+        shape = (self.slabs, self.c.ring, HEAD_DIM)
+        return (self._view(self.c.k_ring, torch.float16, shape),
+                self._view(self.c.v_ring, torch.float16, shape))
+
+    # ---- calls
+    def prefill(self, k: torch.Tensor, v: torch.Tensor, stream=None) -> None:
+        _need_f16(k, "k")
+        _need_f16(v, "v")
+        if k.stride(0) != v.stride(0) or k.shape != v.shape:
+            raise ValueError("k and v must have one shape and slab stride")
+        _check(lib().kivi_cache_prefill(ctypes.byref(self.c), k.data_ptr(), v.data_ptr(), k.stride(0),
+                                        k.shape[1], _stream(stream)), "kivi_cache_prefill")
+
+    def append(self, layer: int, k_new: torch.Tensor, v_new: torch.Tensor, stream=None) -> None:
+        for t, name in ((k_new, "k_new"), (v_new, "v_new")):
+            if t.dtype != torch.float16 or not t.is_cuda or not t.is_contiguous() or \
+                    t.numel() != self.cfg.batch * self.cfg.kv_heads * HEAD_DIM:
+                raise ValueError(f"{name} must be contiguous float16 [batch*kv_heads][128]")
+        _check(lib().kivi_cache_append(ctypes.byref(self.c), layer, k_new.data_ptr(), v_new.data_ptr(),
+                                       _stream(stream)), "kivi_cache_append")
+
+    def attend_workspace_bytes(self, Hq: int) -> int:
+        return int(lib().kivi_cache_attend_workspace_bytes(ctypes.byref(self.c), Hq))
+
+    def attend(self, layer: int, q: torch.Tensor, out: torch.Tensor | None = None,
+               workspace: torch.Tensor | None = None, softmax_scale: float | None = None,
+               stream=None) -> torch.Tensor:
+        if q.dtype != torch.float16 or not q.is_cuda or q.dim() != 3 or not q.is_contiguous():
+            raise ValueError("q must be a contiguous float16 device tensor [B][Hq][128]")
+        B, Hq, D = q.shape
+        if softmax_scale is None:
+            softmax_scale = 1.0 / math.sqrt(D)
+        if out is None:
+            out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+        if workspace is None:
+            workspace = torch.empty(max(self.attend_workspace_bytes(Hq), 256), dtype=torch.uint8,
+                                    device=q.device)
+        _check(lib().kivi_cache_attend(ctypes.byref(self.c), layer, q.data_ptr(), Hq, float(softmax_scale),
+                                       out.data_ptr(), workspace.data_ptr(),
+                                       workspace.numel() * workspace.element_size(), _stream(stream)),
+               "kivi_cache_attend")
+        return out
+
+    def end_step(self, stream=None) -> int:
+        rc = lib().kivi_cache_end_step(ctypes.byref(self.c), _stream(stream))
+        if rc < 0:
+            raise KiviError(rc, "kivi_cache_end_step")
+        return rc

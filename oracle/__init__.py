@@ -24,6 +24,9 @@ Parity status of each function (what pins it is in ``tests/test_oracle_*.py``):
                                 does not depend on the others; empty -> 0)
   flush_count ................. pinned (the flush/layer figures of the
                                 Generation 1 table)
+  CacheModel .................. pinned (incremental stores equal one flush of
+                                the same prefix; token split per step checked
+                                with torch float64 SDPA; counts follow the rule)
 """
 from __future__ import annotations
 
@@ -293,3 +296,61 @@ def decode_attend_varlen(q, B: int, Hq: int, Hkv: int, kstore: Store | None,
 
 def flush_count(S: int, R: int, G: int) -> int:
     return int(lib().orc_flush_count(S, R, G))
+
+
+class CacheModel:
+    """The decode loop's cache as a plain model: every slab keeps all of its
+    fp16 tokens in order; after the prompt and after every step the oldest
+    flush_count(S, R, F) tokens of a sequence of S tokens are in the stores
+    (whole units of F older than the newest R, the rule of ``flush_count``
+    with F in place of G), flushed by ``quantize_keys`` / ``quantize_values``
+    as they cross that line.  A step's attention (``decode_attend``) sees the
+    store tokens and every later token, the step's own one included, in
+    order.  Slab s = (layer * batch + b) * kv_heads + h."""
+
+    def __init__(self, layers: int, batch: int, kv_heads: int, capacity: int, bits: int = 4,
+                 R: int = 128, F: int = 32, D: int = 128):
+        self.layers, self.batch, self.kv_heads, self.R, self.F, self.D = layers, batch, kv_heads, R, F, D
+        self.slabs = layers * batch * kv_heads
+        self.kstore = Store(KEYS, self.slabs, capacity, D, bits)
+        self.vstore = Store(VALUES, self.slabs, capacity, D, bits)
+        self.k = np.zeros((self.slabs, 0, D), np.uint16)
+        self.v = np.zeros((self.slabs, 0, D), np.uint16)
+        self.n_quant = 0
+
+    @property
+    def length(self) -> int:
+        return self.k.shape[1]
+
+    def _flush_to_rule(self):
+        Q = flush_count(self.length, self.R, self.F)
+        if Q > self.n_quant:
+            quantize_keys(np.ascontiguousarray(self.k[:, self.n_quant:Q]), self.kstore, self.n_quant,
+                          want_recon=False)
+            quantize_values(np.ascontiguousarray(self.v[:, self.n_quant:Q]), self.vstore, self.n_quant,
+                            want_recon=False)
+            self.n_quant = Q
+
+    def prefill(self, k, v):
+        """k, v fp16 [slabs][S][D]: the prompt of every layer and sequence."""
+        self.k, self.v = _as_u16(k).copy(), _as_u16(v).copy()
+        self._flush_to_rule()
+
+    def step(self, k_new, v_new, q, Hq: int) -> np.ndarray:
+        """k_new, v_new fp16 [slabs][D] (this step's token of every slab);
+        q fp16 [layers][batch][Hq][D].  Returns float64 [layers][batch][Hq][D]."""
+        self.k = np.concatenate([self.k, _as_u16(k_new)[:, None, :]], axis=1)
+        self.v = np.concatenate([self.v, _as_u16(v_new)[:, None, :]], axis=1)
+        q = _as_u16(q)
+        per = self.batch * self.kv_heads
+        out = np.zeros((self.layers, self.batch, Hq, self.D), np.float64)
+        nq, nr = self.n_quant, self.length - self.n_quant
+        for layer in range(self.layers):
+            lo, hi = layer * per, (layer + 1) * per
+            out[layer] = decode_attend(q[layer], self.batch, Hq, self.kv_heads,
+                                       self.kstore.slabs(lo, hi) if nq else None,
+                                       self.vstore.slabs(lo, hi) if nq else None, nq,
+                                       np.ascontiguousarray(self.k[lo:hi, nq:]),
+                                       np.ascontiguousarray(self.v[lo:hi, nq:]), nr)
+        self._flush_to_rule()
+        return out

@@ -148,3 +148,42 @@ def test_attend_validation():
     assert call(wsb=ws - 4) == -5
     assert call(wsp=None) == -5
     assert call(wsp=FAKE + 16) == -4
+
+
+# ---------------------------------------------------------------- cache
+def test_cache_rejects_bad_configs():
+    L = kivi.lib()
+    ok = kivi.CCacheConfig(2, 2, 8, 4, 128, 32, 128, 32, 4096)
+    assert L.kivi_cache_device_bytes(ctypes.byref(ok)) > 0
+    for field, bad in (("layers", 0), ("layers", 257), ("bits", 3), ("head_dim", 64),
+                       ("group_size", 64), ("flush_tokens", 48), ("residual_length", 100),
+                       ("store_capacity", 4100), ("batch", 0)):
+        cfg = kivi.CCacheConfig(2, 2, 8, 4, 128, 32, 128, 32, 4096)
+        setattr(cfg, field, bad)
+        assert L.kivi_cache_device_bytes(ctypes.byref(cfg)) == 0, field
+        c = kivi.CCache()
+        assert L.kivi_cache_init(ctypes.byref(c), ctypes.byref(cfg), FAKE, 1 << 40) == -3, field
+
+
+def test_cache_init_checks_buffer_and_step_order():
+    """Host-only paths: alignment and size of the buffer, and the step order
+    (attend and end_step before any append) are refused without a launch."""
+    L = kivi.lib()
+    cfg = kivi.CCacheConfig(2, 1, 2, 4, 128, 32, 64, 32, 256)
+    need = L.kivi_cache_device_bytes(ctypes.byref(cfg))
+    c = kivi.CCache()
+    assert L.kivi_cache_init(ctypes.byref(c), ctypes.byref(cfg), FAKE + 16, need) == -4
+    assert L.kivi_cache_init(ctypes.byref(c), ctypes.byref(cfg), FAKE, need - 1) == -5
+    assert L.kivi_cache_init(ctypes.byref(c), ctypes.byref(cfg), FAKE, need) == 0
+    assert (c.length, c.n_quant, c.n_res, c.head, c.ring) == (0, 0, 0, 0, 96)
+    assert c.k_store.cap == 256 and c.k_store.codes_bh_stride == 256 * 16
+    assert c.k_store.meta_bh_stride == 8 * 128 and c.v_store.meta_bh_stride == 256 * 4
+    assert L.kivi_cache_end_step(ctypes.byref(c), None) == -2
+    assert L.kivi_cache_attend(ctypes.byref(c), 0, FAKE, 4, 0.088, FAKE, FAKE, 1 << 20, None) == -2
+    assert L.kivi_cache_append(ctypes.byref(c), 2, FAKE, FAKE, None) == -2       # no layer 2
+    # a prompt whose quantized part exceeds the capacity: Q(400) = 320 > 256
+    assert L.kivi_cache_prefill(ctypes.byref(c), FAKE, FAKE, 400 * 128, 400, None) == -2
+    assert L.kivi_cache_prefill(ctypes.byref(c), FAKE + 8, FAKE, 300 * 128, 300, None) == -4
+    assert c.length == 0
+    assert L.kivi_cache_attend_workspace_bytes(ctypes.byref(c), 8) >= \
+        L.kivi_decode_attend_workspace_bytes(1, 8, 2, 256, 96)
