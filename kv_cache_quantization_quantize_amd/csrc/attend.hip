@@ -43,13 +43,16 @@ union Frag {
     uint32_t u[4];
 };
 
-// Two waves per SIMD: the register budget (256) holds three steps of loads.
+// Three waves per SIMD (at most 168 VGPRs, which hold three steps of loads
+// in flight without spilling; four would need 128 and spill), so the chip
+// holds 256 CUs x 4 SIMDs x 3 = 3072 of these waves at once.
 #ifndef KIVI_ATTEND_OCCUPANCY
-#define KIVI_ATTEND_OCCUPANCY __attribute__((amdgpu_waves_per_eu(2)))
+#define KIVI_ATTEND_OCCUPANCY __attribute__((amdgpu_waves_per_eu(3)))
 #endif
+constexpr int64_t kWaveSlots = 3072;
 
 constexpr int kStep = 32;             // tokens per wave step (one key group)
-constexpr int kMaxStepsPerWave = 32;
+constexpr int64_t kMaxStepsPerWave = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr uint32_t kMagic = 0x64006400u;   // fp16 1024.0 in both halves
 
@@ -440,13 +443,15 @@ __device__ __forceinline__ void residual_step(const uint16_t* kr, const uint16_t
     }
 }
 
-// One wave: sequence b, kv head kv, one split.  Splits [0, n_split_q) cover
-// store tokens [0, n_quant) in runs of spw_q steps of 32 tokens; the rest
-// cover residual tokens [0, n_res) in runs of spw_r steps.  Offsets within a
-// slab fit in 32 bits: the ABI keeps n_quant and n_res below 2^24 tokens.
+// One wave: sequence b, kv head kv, one split.  The token axis of a slab is
+// the store tokens [0, n_quant) in steps_q 32-token steps followed by the
+// residual tokens [0, n_res); split s covers the steps [s*spw, (s+1)*spw) of
+// that axis, so one wave may finish the store and start the residual.
+// Offsets within a slab fit in 32 bits: the ABI keeps n_quant and n_res
+// below 2^24 tokens.
 template <int BITS, int GQA>
-__global__ __launch_bounds__(64) KIVI_ATTEND_OCCUPANCY void attend_partial_kernel(const AttendArgs a, int spw_q, int n_split_q,
-                                                            int spw_r, int64_t n_split, float* __restrict__ ws_o,
+__global__ __launch_bounds__(64) KIVI_ATTEND_OCCUPANCY void attend_partial_kernel(const AttendArgs a, int spw, int steps_q,
+                                                            int64_t n_split, float* __restrict__ ws_o,
                                                             float* __restrict__ ws_ml)
 {
     __shared__ Smem sm;
@@ -459,9 +464,52 @@ __global__ __launch_bounds__(64) KIVI_ATTEND_OCCUPANCY void attend_partial_kerne
     const int kv = static_cast<int>(bkv - b * a.Hkv);
     const int64_t qrow0 = b * a.Hq + static_cast<int64_t>(kv) * GQA;
 
+    // Token counts of this sequence: the uniform bounds, or the per-sequence
+    // lengths clamped to them (so no load can leave the bounded slab).
+    int nq = static_cast<int>(a.n_quant);
+    int nr = static_cast<int>(a.n_res);
+    if (a.seq_n_quant) {
+        nq = min(max(a.seq_n_quant[b], 0), nq);
+        nr = min(max(a.seq_n_res[b], 0), nr);
+    }
+    const int s0 = split * spw, s1 = s0 + spw;
+    const int j0 = s0 * kStep;                                  // store tokens [j0, j1)
+    const int j1 = min(min(s1, steps_q) * kStep, nq);
+    const int r0 = max(s0 - steps_q, 0) * kStep;                // residual tokens [r0, r1)
+    const int r1 = min(max(s1 - steps_q, 0) * kStep, nr);
+    const bool has_store = j0 < j1;
+
+    // Store part: buffer views and the first two steps' loads, issued before
+    // the query so the two HBM latencies overlap.
+    constexpr int kWords = kHeadDim * BITS / 32;
+    constexpr int kMetaPerTok = kHeadDim / kGroup;
+    StoreView S;
+    LaneOffsets O;
+    StepLoad bufA, bufB, bufC;
+    // Every prefetch is issued, also past the split's end (to a token far
+    // outside the buffers' extent, which the buffer unit answers with zeros
+    // and no memory access): a conditional issue makes the compiler wait for
+    // all outstanding loads at the join.
+    const auto pref = [j1](int t) { return t < j1 ? static_cast<uint32_t>(t) : kFarToken; };
+    if (has_store) {
+        const uint32_t n_groups = static_cast<uint32_t>((nq + kGroup - 1) / kGroup);
+        S.kc = make_rsrc(a.k_codes + bkv * a.k_codes_bh_stride, static_cast<uint32_t>(nq) * kWords * 4u);
+        S.ks = make_rsrc(a.k_scale + bkv * a.k_meta_bh_stride, n_groups * kHeadDim * 4u);
+        S.kz = make_rsrc(a.k_zero + bkv * a.k_meta_bh_stride, n_groups * kHeadDim * 4u);
+        S.vc = make_rsrc(a.v_codes + bkv * a.v_codes_bh_stride, static_cast<uint32_t>(nq) * kWords * 4u);
+        S.vs = make_rsrc(a.v_scale + bkv * a.v_meta_bh_stride, static_cast<uint32_t>(nq) * kMetaPerTok * 4u);
+        S.vz = make_rsrc(a.v_zero + bkv * a.v_meta_bh_stride, static_cast<uint32_t>(nq) * kMetaPerTok * 4u);
+        O.k = static_cast<uint32_t>(n * kWords + (BITS == 4 ? 4 * q : 2 * q)) * 4u;
+        O.v = static_cast<uint32_t>(4 * q * kWords + (BITS == 4 ? n : (n >> 1))) * 4u;
+        O.km = static_cast<uint32_t>(l) * 8u;
+        O.vm = static_cast<uint32_t>(l & 31) * 16u + static_cast<uint32_t>(l >> 5) * 8u;
+        issue_step<BITS>(bufA, S, O, j0, n);
+        issue_step<BITS>(bufB, S, O, pref(j0 + kStep), n);
+    }
+
     // B operand of QK^T: q of head n (zero for n >= GQA) in slot order.
-    Frag bq[4];
     {
+        Frag bq[4];
         uint32_t qn[16];                      // channels 32q .. 32q+31, natural order
         if (n < GQA) {
             const uint4* src = reinterpret_cast<const uint4*>(a.q + (qrow0 + n) * kHeadDim + 32 * q);
@@ -496,42 +544,9 @@ __global__ __launch_bounds__(64) KIVI_ATTEND_OCCUPANCY void attend_partial_kerne
 #pragma unroll
     for (int i = 0; i < 8; ++i) st.acc_o[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // Token counts of this sequence: the uniform bounds, or the per-sequence
-    // lengths clamped to them (so no load can leave the bounded slab).
-    int nq = static_cast<int>(a.n_quant);
-    int nr = static_cast<int>(a.n_res);
-    if (a.seq_n_quant) {
-        nq = min(max(a.seq_n_quant[b], 0), nq);
-        nr = min(max(a.seq_n_res[b], 0), nr);
-    }
-
-    if (split < n_split_q && split * spw_q * kStep < nq) {
-        const int j0 = split * spw_q * kStep;
-        const int j1 = min(j0 + spw_q * kStep, nq);
-        constexpr int kWords = kHeadDim * BITS / 32;
-        constexpr int kMetaPerTok = kHeadDim / kGroup;
-        const uint32_t n_groups = static_cast<uint32_t>((nq + kGroup - 1) / kGroup);
-        StoreView S;
-        S.kc = make_rsrc(a.k_codes + bkv * a.k_codes_bh_stride, static_cast<uint32_t>(nq) * kWords * 4u);
-        S.ks = make_rsrc(a.k_scale + bkv * a.k_meta_bh_stride, n_groups * kHeadDim * 4u);
-        S.kz = make_rsrc(a.k_zero + bkv * a.k_meta_bh_stride, n_groups * kHeadDim * 4u);
-        S.vc = make_rsrc(a.v_codes + bkv * a.v_codes_bh_stride, static_cast<uint32_t>(nq) * kWords * 4u);
-        S.vs = make_rsrc(a.v_scale + bkv * a.v_meta_bh_stride, static_cast<uint32_t>(nq) * kMetaPerTok * 4u);
-        S.vz = make_rsrc(a.v_zero + bkv * a.v_meta_bh_stride, static_cast<uint32_t>(nq) * kMetaPerTok * 4u);
-        LaneOffsets O;
-        O.k = static_cast<uint32_t>(n * kWords + (BITS == 4 ? 4 * q : 2 * q)) * 4u;
-        O.v = static_cast<uint32_t>(4 * q * kWords + (BITS == 4 ? n : (n >> 1))) * 4u;
-        O.km = static_cast<uint32_t>(l) * 8u;
-        O.vm = static_cast<uint32_t>(l & 31) * 16u + static_cast<uint32_t>(l >> 5) * 8u;
+    if (has_store) {
         // Three buffers: the loads of steps t+32 and t+64 are in flight while
-        // step t computes.  Every prefetch is issued, also past the split's
-        // end (to a token far outside the buffers' extent, which the buffer
-        // unit answers with zeros and no memory access): a conditional issue
-        // makes the compiler wait for all outstanding loads at the join.
-        const auto pref = [j1](int t) { return t < j1 ? static_cast<uint32_t>(t) : kFarToken; };
-        StepLoad bufA, bufB, bufC;
-        issue_step<BITS>(bufA, S, O, j0, n);
-        issue_step<BITS>(bufB, S, O, pref(j0 + kStep), n);
+        // step t computes.
         for (int t0 = j0; t0 < j1; t0 += 3 * kStep) {
             issue_step<BITS>(bufC, S, O, pref(t0 + 2 * kStep), n);
             store_step<BITS>(bufA, sm, st, t0, j1, c2, l, n, q);
@@ -542,9 +557,8 @@ __global__ __launch_bounds__(64) KIVI_ATTEND_OCCUPANCY void attend_partial_kerne
             issue_step<BITS>(bufB, S, O, pref(t0 + 4 * kStep), n);
             store_step<BITS>(bufC, sm, st, t0 + 2 * kStep, j1, c2, l, n, q);
         }
-    } else if (split >= n_split_q) {
-        const int r0 = (split - n_split_q) * spw_r * kStep;
-        const int r1 = min(r0 + spw_r * kStep, nr);
+    }
+    if (r0 < r1) {
         const uint16_t* kr = a.k_res + bkv * a.res_bh_stride;
         const uint16_t* vr = a.v_res + bkv * a.res_bh_stride;
         for (int t0 = r0; t0 < r1; t0 += kStep)
@@ -572,64 +586,103 @@ __global__ __launch_bounds__(64) KIVI_ATTEND_OCCUPANCY void attend_partial_kerne
 
 // Merge the splits of one (sequence, query head), base-2 log-sum-exp:
 // o = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i with M = max_i m_i.
-__global__ __launch_bounds__(kHeadDim) void attend_combine_kernel(const float* __restrict__ ws_o,
-                                                                  const float* __restrict__ ws_ml,
-                                                                  int64_t n_split, float* __restrict__ out)
+// Four waves per row: wave w takes splits w, w + 4, ..., lane l channels
+// 2l and 2l + 1; the waves' sums meet in LDS.
+constexpr int kCombineWaves = 4;
+
+__global__ __launch_bounds__(64 * kCombineWaves) void attend_combine_kernel(const float* __restrict__ ws_o,
+                                                                           const float* __restrict__ ws_ml,
+                                                                           int64_t n_split, float* __restrict__ out)
 {
-    __shared__ float red[2];
+    __shared__ float red_m[kCombineWaves];
+    __shared__ float red_l[kCombineWaves];
+    __shared__ float2 red_o[kCombineWaves][64];
     const int64_t row = blockIdx.x;                  // b * Hq + h
-    const int d = threadIdx.x;
+    const int t = threadIdx.x;
+    const int w = t >> 6;
+    const int l = t & 63;
     const float* ml = ws_ml + row * n_split * 2;
+    const float2* o = reinterpret_cast<const float2*>(ws_o + row * n_split * kHeadDim) + l;
+
     float M = -INFINITY;
-    for (int64_t i = d; i < n_split; i += kHeadDim) M = fmaxf(M, ml[2 * i]);
+    for (int64_t i = t; i < n_split; i += 64 * kCombineWaves) M = fmaxf(M, ml[2 * i]);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    if ((d & 63) == 0) red[d >> 6] = M;
+    if (l == 0) red_m[w] = M;
     __syncthreads();
-    M = fmaxf(red[0], red[1]);
-    // every split empty: keep the weights 2^(m_i - M) finite (they are 0)
+    M = red_m[0];
+#pragma unroll
+    for (int i = 1; i < kCombineWaves; ++i) M = fmaxf(M, red_m[i]);
+    // every split empty (a sequence with no tokens): keep the weights finite (0)
     if (M == -INFINITY) M = 0.0f;
-    float L = 0.0f, acc = 0.0f;
-    const float* o = ws_o + row * n_split * kHeadDim + d;
-    int64_t i = 0;
-    for (; i + 4 <= n_split; i += 4) {
-        float w[4], lv[4], ov[4];
+
+    float L = 0.0f;
+    float2 acc = make_float2(0.0f, 0.0f);
+    int64_t i = w;
+    constexpr int kU = 4;
+    for (; i + (kU - 1) * kCombineWaves < n_split; i += kU * kCombineWaves) {
+        float2 mv[kU];
+        float2 ov[kU];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            w[u] = ml[2 * (i + u)];
-            lv[u] = ml[2 * (i + u) + 1];
-            ov[u] = o[(i + u) * kHeadDim];
+        for (int u = 0; u < kU; ++u) {
+            const int64_t s = i + u * kCombineWaves;
+            mv[u] = *reinterpret_cast<const float2*>(ml + 2 * s);
+            ov[u] = o[s * (kHeadDim / 2)];
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const float e = exp2f(w[u] - M);
-            L = __builtin_fmaf(e, lv[u], L);
-            acc = __builtin_fmaf(e, ov[u], acc);
+        for (int u = 0; u < kU; ++u) {
+            const float e = exp2f(mv[u].x - M);
+            L = __builtin_fmaf(e, mv[u].y, L);
+            acc.x = __builtin_fmaf(e, ov[u].x, acc.x);
+            acc.y = __builtin_fmaf(e, ov[u].y, acc.y);
         }
     }
-    for (; i < n_split; ++i) {
-        const float e = exp2f(ml[2 * i] - M);
-        L = __builtin_fmaf(e, ml[2 * i + 1], L);
-        acc = __builtin_fmaf(e, o[i * kHeadDim], acc);
+    for (; i < n_split; i += kCombineWaves) {
+        const float2 mv = *reinterpret_cast<const float2*>(ml + 2 * i);
+        const float2 ov = o[i * (kHeadDim / 2)];
+        const float e = exp2f(mv.x - M);
+        L = __builtin_fmaf(e, mv.y, L);
+        acc.x = __builtin_fmaf(e, ov.x, acc.x);
+        acc.y = __builtin_fmaf(e, ov.y, acc.y);
     }
-    // A sequence with no tokens at all (only possible in a variable-length
-    // batch) has every partial empty (m = -inf, l = 0): its output is zero.
-    out[row * kHeadDim + d] = L > 0.0f ? acc / L : 0.0f;
+    red_o[w][l] = acc;
+    if (l == 0) red_l[w] = L;
+    __syncthreads();
+    if (w == 0) {
+        float Lt = red_l[0];
+        float2 at = red_o[0][l];
+#pragma unroll
+        for (int v = 1; v < kCombineWaves; ++v) {
+            Lt += red_l[v];
+            at.x += red_o[v][l].x;
+            at.y += red_o[v][l].y;
+        }
+        // a sequence with no tokens at all (only possible in a variable-length
+        // batch) has every partial empty (m = -inf, l = 0): its output is zero
+        const float2 r = Lt > 0.0f ? make_float2(at.x / Lt, at.y / Lt) : make_float2(0.0f, 0.0f);
+        reinterpret_cast<float2*>(out + row * kHeadDim)[l] = r;
+    }
 }
 
+// Split of the token axis.  Small problems (no more 32-token steps than the
+// chip holds waves) get one step per wave: everything is in flight at once.
+// Larger ones get as few whole rounds of kWaveSlots waves as keep a wave at
+// most kMaxStepsPerWave steps, with the steps spread evenly, so the last
+// round is not a short tail.
 AttendPlan plan_attend(int64_t B, int Hq, int Hkv, int64_t n_quant, int64_t n_res) {
     const int64_t pairs = B * Hkv;
     const int64_t steps_q = (n_quant + kStep - 1) / kStep;
-    const int64_t steps_r = (n_res + kStep - 1) / kStep;
-    // enough waves for two per SIMD (1024 SIMDs) before lengthening them
-    int64_t spw = pairs * (steps_q + steps_r) / 2048;
-    spw = spw < 1 ? 1 : (spw > kMaxStepsPerWave ? kMaxStepsPerWave : spw);
+    const int64_t steps = steps_q + (n_res + kStep - 1) / kStep;
+    const int64_t total = pairs * steps;
+    int64_t spw = 1;
+    if (total > kWaveSlots) {
+        const int64_t rounds = (total + kWaveSlots * kMaxStepsPerWave - 1) / (kWaveSlots * kMaxStepsPerWave);
+        spw = (total + rounds * kWaveSlots - 1) / (rounds * kWaveSlots);
+    }
     AttendPlan p;
-    p.steps_per_wave_q = spw;
-    p.n_split_q = (steps_q + spw - 1) / spw;
-    p.steps_per_wave_r = spw;
-    p.n_split = p.n_split_q + (steps_r + spw - 1) / spw;
-    p.chunk = spw * kStep;
+    p.steps_q = steps_q;
+    p.steps_per_wave = spw;
+    p.n_split = (steps + spw - 1) / spw;
     const size_t rows = static_cast<size_t>(B) * static_cast<size_t>(Hq) * static_cast<size_t>(p.n_split);
     const size_t o_bytes = (rows * kHeadDim * sizeof(float) + 255) & ~static_cast<size_t>(255);
     p.workspace_bytes = o_bytes + rows * 2 * sizeof(float);
@@ -644,12 +697,12 @@ static hipError_t launch_t(const AttendArgs& a, const AttendPlan& p, hipStream_t
     float* ws_ml = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + o_bytes);
     const dim3 grid(static_cast<uint32_t>(p.n_split), static_cast<uint32_t>(a.B * a.Hkv));
     hipLaunchKernelGGL((attend_partial_kernel<BITS, GQA>), grid, dim3(64), 0, stream, a,
-                       static_cast<int>(p.steps_per_wave_q), static_cast<int>(p.n_split_q),
-                       static_cast<int>(p.steps_per_wave_r), p.n_split, ws_o, ws_ml);
+                       static_cast<int>(p.steps_per_wave), static_cast<int>(p.steps_q), p.n_split,
+                       ws_o, ws_ml);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(attend_combine_kernel, dim3(static_cast<uint32_t>(a.B * a.Hq)),
-                       dim3(kHeadDim), 0, stream, ws_o, ws_ml, p.n_split, a.out);
+                       dim3(64 * kCombineWaves), 0, stream, ws_o, ws_ml, p.n_split, a.out);
     return hipGetLastError();
 }
 

@@ -72,11 +72,9 @@ struct AttendArgs {
 // Split of the token axis chosen for an attend shape; the workspace holds
 // one (m, l, o[128]) partial per (sequence, query head, split).
 struct AttendPlan {
-    int64_t chunk;                 // tokens per split, a multiple of 32
-    int64_t steps_per_wave_q;      // 32-token steps per store-token split
-    int64_t n_split_q;             // splits over store tokens [0, n_quant)
-    int64_t steps_per_wave_r;      // 32-token steps per residual split
-    int64_t n_split;               // store splits + residual splits
+    int64_t steps_q;               // 32-token steps over store tokens [0, n_quant)
+    int64_t steps_per_wave;        // consecutive steps of store-then-residual per wave
+    int64_t n_split;               // waves per (sequence, kv head)
     size_t workspace_bytes;
 };
 AttendPlan plan_attend(int64_t B, int Hq, int Hkv, int64_t n_quant, int64_t n_res);
