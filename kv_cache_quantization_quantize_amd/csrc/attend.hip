@@ -45,11 +45,17 @@ union Frag {
 
 // Three waves per SIMD (at most 168 VGPRs, which hold three steps of loads
 // in flight without spilling; four would need 128 and spill), so the chip
-// holds 256 CUs x 4 SIMDs x 3 = 3072 of these waves at once.
-#ifndef KIVI_ATTEND_OCCUPANCY
-#define KIVI_ATTEND_OCCUPANCY __attribute__((amdgpu_waves_per_eu(3)))
+// holds 256 CUs x 4 SIMDs x 3 = 3072 of these waves at once.  Each wave
+// keeps KIVI_ATTEND_NBUF - 1 steps of loads in flight while it computes one.
+#ifndef KIVI_ATTEND_WAVES_PER_SIMD
+#define KIVI_ATTEND_WAVES_PER_SIMD 3
 #endif
-constexpr int64_t kWaveSlots = 3072;
+#ifndef KIVI_ATTEND_NBUF
+#define KIVI_ATTEND_NBUF 3
+#endif
+#define KIVI_ATTEND_OCCUPANCY __attribute__((amdgpu_waves_per_eu(KIVI_ATTEND_WAVES_PER_SIMD)))
+constexpr int64_t kWaveSlots = 256 * 4 * KIVI_ATTEND_WAVES_PER_SIMD;
+constexpr int kNBuf = KIVI_ATTEND_NBUF;
 
 constexpr int kStep = 32;             // tokens per wave step (one key group)
 constexpr int64_t kMaxStepsPerWave = 64;
@@ -485,7 +491,7 @@ __global__ __launch_bounds__(64) KIVI_ATTEND_OCCUPANCY void attend_partial_kerne
     constexpr int kMetaPerTok = kHeadDim / kGroup;
     StoreView S;
     LaneOffsets O;
-    StepLoad bufA, bufB, bufC;
+    StepLoad buf[kNBuf];
     // Every prefetch is issued, also past the split's end (to a token far
     // outside the buffers' extent, which the buffer unit answers with zeros
     // and no memory access): a conditional issue makes the compiler wait for
@@ -503,8 +509,8 @@ __global__ __launch_bounds__(64) KIVI_ATTEND_OCCUPANCY void attend_partial_kerne
         O.v = static_cast<uint32_t>(4 * q * kWords + (BITS == 4 ? n : (n >> 1))) * 4u;
         O.km = static_cast<uint32_t>(l) * 8u;
         O.vm = static_cast<uint32_t>(l & 31) * 16u + static_cast<uint32_t>(l >> 5) * 8u;
-        issue_step<BITS>(bufA, S, O, j0, n);
-        issue_step<BITS>(bufB, S, O, pref(j0 + kStep), n);
+#pragma unroll
+        for (int u = 0; u + 1 < kNBuf; ++u) issue_step<BITS>(buf[u], S, O, pref(j0 + u * kStep), n);
     }
 
     // B operand of QK^T: q of head n (zero for n >= GQA) in slot order.
@@ -545,18 +551,17 @@ __global__ __launch_bounds__(64) KIVI_ATTEND_OCCUPANCY void attend_partial_kerne
     for (int i = 0; i < 8; ++i) st.acc_o[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
     if (has_store) {
-        // Three buffers: the loads of steps t+32 and t+64 are in flight while
-        // step t computes.
-        for (int t0 = j0; t0 < j1; t0 += 3 * kStep) {
-            issue_step<BITS>(bufC, S, O, pref(t0 + 2 * kStep), n);
-            store_step<BITS>(bufA, sm, st, t0, j1, c2, l, n, q);
-            if (t0 + kStep >= j1) break;
-            issue_step<BITS>(bufA, S, O, pref(t0 + 3 * kStep), n);
-            store_step<BITS>(bufB, sm, st, t0 + kStep, j1, c2, l, n, q);
-            if (t0 + 2 * kStep >= j1) break;
-            issue_step<BITS>(bufB, S, O, pref(t0 + 4 * kStep), n);
-            store_step<BITS>(bufC, sm, st, t0 + 2 * kStep, j1, c2, l, n, q);
+        // kNBuf buffers in rotation: while step t computes, the loads of the
+        // next kNBuf - 1 steps are in flight.
+        for (int t0 = j0; t0 < j1; t0 += kNBuf * kStep) {
+#pragma unroll
+            for (int u = 0; u < kNBuf; ++u) {
+                issue_step<BITS>(buf[(u + kNBuf - 1) % kNBuf], S, O, pref(t0 + (u + kNBuf - 1) * kStep), n);
+                store_step<BITS>(buf[u], sm, st, t0 + u * kStep, j1, c2, l, n, q);
+                if (t0 + (u + 1) * kStep >= j1) goto store_done;
+            }
         }
+    store_done:;
     }
     if (r0 < r1) {
         const uint16_t* kr = a.k_res + bkv * a.res_bh_stride;
@@ -586,17 +591,17 @@ __global__ __launch_bounds__(64) KIVI_ATTEND_OCCUPANCY void attend_partial_kerne
 
 // Merge the splits of one (sequence, query head), base-2 log-sum-exp:
 // o = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i with M = max_i m_i.
-// Four waves per row: wave w takes splits w, w + 4, ..., lane l channels
-// 2l and 2l + 1; the waves' sums meet in LDS.
-constexpr int kCombineWaves = 4;
-
-__global__ __launch_bounds__(64 * kCombineWaves) void attend_combine_kernel(const float* __restrict__ ws_o,
-                                                                           const float* __restrict__ ws_ml,
-                                                                           int64_t n_split, float* __restrict__ out)
+// WAVES waves per row: wave w takes splits w, w + WAVES, ..., lane l
+// channels 2l and 2l + 1; the waves' sums meet in LDS.  Many splits (small
+// batches, long contexts) get 16 waves, so each walks only a few of them.
+template <int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void attend_combine_kernel(const float* __restrict__ ws_o,
+                                                                   const float* __restrict__ ws_ml,
+                                                                   int64_t n_split, float* __restrict__ out)
 {
-    __shared__ float red_m[kCombineWaves];
-    __shared__ float red_l[kCombineWaves];
-    __shared__ float2 red_o[kCombineWaves][64];
+    __shared__ float red_m[WAVES];
+    __shared__ float red_l[WAVES];
+    __shared__ float2 red_o[WAVES][64];
     const int64_t row = blockIdx.x;                  // b * Hq + h
     const int t = threadIdx.x;
     const int w = t >> 6;
@@ -605,14 +610,14 @@ __global__ __launch_bounds__(64 * kCombineWaves) void attend_combine_kernel(cons
     const float2* o = reinterpret_cast<const float2*>(ws_o + row * n_split * kHeadDim) + l;
 
     float M = -INFINITY;
-    for (int64_t i = t; i < n_split; i += 64 * kCombineWaves) M = fmaxf(M, ml[2 * i]);
+    for (int64_t i = t; i < n_split; i += 64 * WAVES) M = fmaxf(M, ml[2 * i]);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
     if (l == 0) red_m[w] = M;
     __syncthreads();
     M = red_m[0];
 #pragma unroll
-    for (int i = 1; i < kCombineWaves; ++i) M = fmaxf(M, red_m[i]);
+    for (int i = 1; i < WAVES; ++i) M = fmaxf(M, red_m[i]);
     // every split empty (a sequence with no tokens): keep the weights finite (0)
     if (M == -INFINITY) M = 0.0f;
 
@@ -620,12 +625,12 @@ __global__ __launch_bounds__(64 * kCombineWaves) void attend_combine_kernel(cons
     float2 acc = make_float2(0.0f, 0.0f);
     int64_t i = w;
     constexpr int kU = 4;
-    for (; i + (kU - 1) * kCombineWaves < n_split; i += kU * kCombineWaves) {
+    for (; i + (kU - 1) * WAVES < n_split; i += kU * WAVES) {
         float2 mv[kU];
         float2 ov[kU];
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
-            const int64_t s = i + u * kCombineWaves;
+            const int64_t s = i + u * WAVES;
             mv[u] = *reinterpret_cast<const float2*>(ml + 2 * s);
             ov[u] = o[s * (kHeadDim / 2)];
         }
@@ -637,7 +642,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void attend_combine_kernel(cons
             acc.y = __builtin_fmaf(e, ov[u].y, acc.y);
         }
     }
-    for (; i < n_split; i += kCombineWaves) {
+    for (; i < n_split; i += WAVES) {
         const float2 mv = *reinterpret_cast<const float2*>(ml + 2 * i);
         const float2 ov = o[i * (kHeadDim / 2)];
         const float e = exp2f(mv.x - M);
@@ -652,7 +657,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void attend_combine_kernel(cons
         float Lt = red_l[0];
         float2 at = red_o[0][l];
 #pragma unroll
-        for (int v = 1; v < kCombineWaves; ++v) {
+        for (int v = 1; v < WAVES; ++v) {
             Lt += red_l[v];
             at.x += red_o[v][l].x;
             at.y += red_o[v][l].y;
@@ -701,8 +706,12 @@ static hipError_t launch_t(const AttendArgs& a, const AttendPlan& p, hipStream_t
                        ws_o, ws_ml);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attend_combine_kernel, dim3(static_cast<uint32_t>(a.B * a.Hq)),
-                       dim3(64 * kCombineWaves), 0, stream, ws_o, ws_ml, p.n_split, a.out);
+    if (p.n_split >= 48)
+        hipLaunchKernelGGL(attend_combine_kernel<16>, dim3(static_cast<uint32_t>(a.B * a.Hq)), dim3(64 * 16), 0,
+                           stream, ws_o, ws_ml, p.n_split, a.out);
+    else
+        hipLaunchKernelGGL(attend_combine_kernel<4>, dim3(static_cast<uint32_t>(a.B * a.Hq)), dim3(64 * 4), 0,
+                           stream, ws_o, ws_ml, p.n_split, a.out);
     return hipGetLastError();
 }
 
