@@ -10,10 +10,14 @@ The arithmetic lives in ``kivi_oracle.c`` (plain single-threaded C, built with
 
 Parity status of each function (what pins it is in ``tests/test_oracle_*.py``):
   f16_to_f32 / f32_to_f16 ..... pinned (exhaustive against numpy's IEEE codec)
+  bf16_to_f32 / f32_to_bf16 ... pinned (all 65536 patterns and whole fp32
+                                exponents against torch's bfloat16 codec)
   quantize_group .............. pinned (hand-worked groups, invariants, brute
                                 force against an exact-rational emulation)
   quantize_keys / _values ..... pinned (layout fixtures, per-group reduction to
-                                quantize_group, axis-discriminating fixtures)
+                                quantize_group, axis-discriminating fixtures);
+                                bf16 inputs: hand-worked groups and brute force
+                                against the exact-rational emulation
   dequantize .................. pinned (hand-worked reconstructions, identity
                                 with the flush's own reconstruction)
   decode_attend ............... pinned (closed forms: one token, equal scores,
@@ -42,6 +46,7 @@ SRC_PATH = os.path.join(_HERE, "kivi_oracle.c")
 
 KEYS = 0
 VALUES = 1
+FMT = {"f16": 0, "bf16": 1}        # 16-bit storage format of inputs and reconstructions
 
 # -ffp-contract=off keeps a*b+c as two roundings; no -ffast-math anywhere.
 CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
@@ -81,6 +86,15 @@ def lib():
         L.orc_f32_to_f16.restype = ctypes.c_uint16
         L.orc_f16_to_f32_array.argtypes = [_u16p, _f32p, _i64]
         L.orc_f32_to_f16_array.argtypes = [_f32p, _u16p, _i64]
+        L.orc_bf16_to_f32.argtypes = [ctypes.c_uint16]
+        L.orc_bf16_to_f32.restype = ctypes.c_float
+        L.orc_f32_to_bf16.argtypes = [ctypes.c_float]
+        L.orc_f32_to_bf16.restype = ctypes.c_uint16
+        L.orc_bf16_to_f32_array.argtypes = [_u16p, _f32p, _i64]
+        L.orc_f32_to_bf16_array.argtypes = [_f32p, _u16p, _i64]
+        L.orc_quantize_group_fmt.argtypes = [_u16p, _int, _int, _int, _f32p, _f32p, _u8p, _u16p]
+        L.orc_dequantize_one_fmt.argtypes = [ctypes.c_uint32, ctypes.c_float, ctypes.c_float, _int]
+        L.orc_dequantize_one_fmt.restype = ctypes.c_uint16
         L.orc_quantize_group.argtypes = [_u16p, _int, _int, _f32p, _f32p, _u8p, _u16p]
         L.orc_dequantize_one.argtypes = [ctypes.c_uint32, ctypes.c_float, ctypes.c_float]
         L.orc_dequantize_one.restype = ctypes.c_uint16
@@ -90,9 +104,15 @@ def lib():
         L.orc_quantize_values.argtypes = flush_args
         L.orc_quantize_keys.restype = _int
         L.orc_quantize_values.restype = _int
+        L.orc_quantize_keys_fmt.argtypes = flush_args + [_int]
+        L.orc_quantize_values_fmt.argtypes = flush_args + [_int]
+        L.orc_quantize_keys_fmt.restype = _int
+        L.orc_quantize_values_fmt.restype = _int
         L.orc_dequantize.argtypes = [_int, _u32p, _i64, _f32p, _f32p, _i64,
                                      _i64, _i64, _int, _int, _i64, _i64, _u16p, _i64]
         L.orc_dequantize.restype = _int
+        L.orc_dequantize_fmt.argtypes = L.orc_dequantize.argtypes + [_int]
+        L.orc_dequantize_fmt.restype = _int
         L.orc_decode_attend.argtypes = [
             _u16p, _i64, _int, _int, _i64,
             _u32p, _f32p, _f32p, _u32p, _f32p, _f32p,
@@ -136,23 +156,39 @@ def f32_to_f16(f) -> np.ndarray:
     return out
 
 
+def bf16_to_f32(h) -> np.ndarray:
+    h = _as_u16(h)
+    out = np.empty(h.shape, np.float32)
+    lib().orc_bf16_to_f32_array(_ptr(h, ctypes.c_uint16), _ptr(out, ctypes.c_float), h.size)
+    return out
+
+
+def f32_to_bf16(f) -> np.ndarray:
+    f = np.ascontiguousarray(f, dtype=np.float32)
+    out = np.empty(f.shape, np.uint16)
+    lib().orc_f32_to_bf16_array(_ptr(f, ctypes.c_float), _ptr(out, ctypes.c_uint16), f.size)
+    return out
+
+
 # ------------------------------------------------------------------ groups
-def quantize_group(x, bits: int):
-    """-> (scale fp32, zero fp32, codes uint8[n], recon fp16 bits uint16[n])."""
+def quantize_group(x, bits: int, fmt: str = "f16"):
+    """-> (scale fp32, zero fp32, codes uint8[n], recon bits uint16[n]) for
+    n values stored as fp16 or bf16 bit patterns (``fmt``)."""
     x = _as_u16(x).reshape(-1)
     n = x.size
     sc = np.zeros(1, np.float32)
     ze = np.zeros(1, np.float32)
     q = np.zeros(n, np.uint8)
     rec = np.zeros(n, np.uint16)
-    lib().orc_quantize_group(_ptr(x, ctypes.c_uint16), n, bits, _ptr(sc, ctypes.c_float),
-                             _ptr(ze, ctypes.c_float), _ptr(q, ctypes.c_uint8),
-                             _ptr(rec, ctypes.c_uint16))
+    lib().orc_quantize_group_fmt(_ptr(x, ctypes.c_uint16), n, bits, FMT[fmt], _ptr(sc, ctypes.c_float),
+                                 _ptr(ze, ctypes.c_float), _ptr(q, ctypes.c_uint8),
+                                 _ptr(rec, ctypes.c_uint16))
     return sc[0], ze[0], q, rec
 
 
-def dequantize_one(q: int, scale, zero) -> int:
-    return int(lib().orc_dequantize_one(int(q), float(np.float32(scale)), float(np.float32(zero))))
+def dequantize_one(q: int, scale, zero, fmt: str = "f16") -> int:
+    return int(lib().orc_dequantize_one_fmt(int(q), float(np.float32(scale)), float(np.float32(zero)),
+                                            FMT[fmt]))
 
 
 # ------------------------------------------------------------------ store
@@ -190,7 +226,7 @@ class Store:
         return self.scale.shape[1] * self.scale.shape[2]
 
 
-def _flush(fn, x, store: Store, dst_token: int, want_recon: bool):
+def _flush(fn, x, store: Store, dst_token: int, want_recon: bool, fmt: str):
     x = _as_u16(x)
     BH, S, D = x.shape
     assert BH == store.BH and D == store.D
@@ -199,31 +235,34 @@ def _flush(fn, x, store: Store, dst_token: int, want_recon: bool):
             _ptr(store.codes, ctypes.c_uint32), store.codes_bh_stride,
             _ptr(store.scale, ctypes.c_float), _ptr(store.zero, ctypes.c_float),
             store.meta_bh_stride, dst_token,
-            _ptr(recon, ctypes.c_uint16), S * D)
+            _ptr(recon, ctypes.c_uint16), S * D, FMT[fmt])
     if rc != 0:
         raise ValueError("oracle rejected the flush arguments")
     return recon
 
 
-def quantize_keys(x, store: Store, dst_token: int = 0, want_recon: bool = True):
-    """Per-channel key flush of x[BH][S][D] into ``store`` at ``dst_token``."""
+def quantize_keys(x, store: Store, dst_token: int = 0, want_recon: bool = True, fmt: str = "f16"):
+    """Per-channel key flush of x[BH][S][D] (fp16 or bf16 bits, ``fmt``) into
+    ``store`` at ``dst_token``; the reconstruction comes back in ``fmt``."""
     assert store.kind == KEYS
-    return _flush(lib().orc_quantize_keys, x, store, dst_token, want_recon)
+    return _flush(lib().orc_quantize_keys_fmt, x, store, dst_token, want_recon, fmt)
 
 
-def quantize_values(x, store: Store, dst_token: int = 0, want_recon: bool = True):
-    """Per-token value flush of x[BH][S][D] into ``store`` at ``dst_token``."""
+def quantize_values(x, store: Store, dst_token: int = 0, want_recon: bool = True, fmt: str = "f16"):
+    """Per-token value flush of x[BH][S][D] (fp16 or bf16 bits, ``fmt``) into
+    ``store`` at ``dst_token``; the reconstruction comes back in ``fmt``."""
     assert store.kind == VALUES
-    return _flush(lib().orc_quantize_values, x, store, dst_token, want_recon)
+    return _flush(lib().orc_quantize_values_fmt, x, store, dst_token, want_recon, fmt)
 
 
-def dequantize(store: Store, t0: int, n: int) -> np.ndarray:
+def dequantize(store: Store, t0: int, n: int, fmt: str = "f16") -> np.ndarray:
+    """Reconstruction of tokens [t0, t0 + n) as fp16 or bf16 bits (``fmt``)."""
     out = np.zeros((store.BH, n, store.D), np.uint16)
-    rc = lib().orc_dequantize(store.kind, _ptr(store.codes, ctypes.c_uint32),
-                              store.codes_bh_stride, _ptr(store.scale, ctypes.c_float),
-                              _ptr(store.zero, ctypes.c_float), store.meta_bh_stride,
-                              store.BH, store.D, store.bits, store.G, t0, n,
-                              _ptr(out, ctypes.c_uint16), n * store.D)
+    rc = lib().orc_dequantize_fmt(store.kind, _ptr(store.codes, ctypes.c_uint32),
+                                  store.codes_bh_stride, _ptr(store.scale, ctypes.c_float),
+                                  _ptr(store.zero, ctypes.c_float), store.meta_bh_stride,
+                                  store.BH, store.D, store.bits, store.G, t0, n,
+                                  _ptr(out, ctypes.c_uint16), n * store.D, FMT[fmt])
     if rc != 0:
         raise ValueError("oracle rejected the dequantize arguments")
     return out

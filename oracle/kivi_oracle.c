@@ -89,6 +89,72 @@ uint16_t orc_f32_to_f16(float f)
     return (uint16_t)(sign | enc);
 }
 
+/* ------------------------------------------------------------------ */
+/* bfloat16 codec, written from the format's definition: 1 sign bit,  */
+/* 8 exponent bits (bias 127), 7 fraction bits -- binary32 with the   */
+/* low 16 fraction bits dropped.                                      */
+/* ------------------------------------------------------------------ */
+
+float orc_bf16_to_f32(uint16_t b)
+{
+    const int sign = (b >> 15) & 1;
+    const int expo = (b >> 7) & 0xff;
+    const int frac = b & 0x7f;
+    float mag;
+    if (expo == 0) {
+        /* zero or subnormal: frac * 2^-133 (exact in binary32) */
+        mag = ldexpf((float)frac, -133);
+    } else if (expo == 255) {
+        mag = frac ? NAN : INFINITY;
+    } else {
+        /* normal: (128 + frac) * 2^(expo - 134) (exact in binary32) */
+        mag = ldexpf((float)(128 + frac), expo - 134);
+    }
+    return sign ? -mag : mag;
+}
+
+uint16_t orc_f32_to_bf16(float f)
+{
+    uint32_t bits;
+    memcpy(&bits, &f, sizeof bits);
+    const uint16_t sign = (uint16_t)((bits >> 16) & 0x8000u);
+    if ((bits & 0x7fffffffu) > 0x7f800000u) return (uint16_t)(sign | 0x7fc0u); /* NaN */
+    if ((bits & 0x7fffffffu) == 0x7f800000u) return (uint16_t)(sign | 0x7f80u);
+    const double a = fabs((double)f);     /* exact */
+    /* from (2 - 2^-8) * 2^127, half an ulp above the largest finite bfloat16,
+       the nearest-even result is infinity (the tie goes to the even 2^128) */
+    if (a >= ldexp(2.0 - ldexp(1.0, -8), 127)) return (uint16_t)(sign | 0x7f80u);
+    if (a < ldexp(1.0, -126)) {
+        /* subnormal range: quantum 2^-133; a result of 128 is the smallest
+           normal, whose encoding is the same integer */
+        const double r = round_half_even(ldexp(a, 133));
+        return (uint16_t)(sign | (uint16_t)r);
+    }
+    int k;
+    (void)frexp(a, &k);                   /* a = m * 2^k, m in [0.5, 1) */
+    const int e = k - 1;                  /* 2^e <= a < 2^(e+1), -126 <= e <= 127 */
+    const double r = round_half_even(ldexp(a, 7 - e));  /* in [128, 256] */
+    /* r == 256 carries into the exponent field, which this sum does */
+    const uint32_t enc = ((uint32_t)(e + 127) << 7) + ((uint32_t)r - 128u);
+    return (uint16_t)(sign | enc);
+}
+
+void orc_bf16_to_f32_array(const uint16_t *h, float *f, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) f[i] = orc_bf16_to_f32(h[i]);
+}
+
+void orc_f32_to_bf16_array(const float *f, uint16_t *h, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) h[i] = orc_f32_to_bf16(f[i]);
+}
+
+/* the 16-bit storage format of inputs and reconstructions */
+typedef float (*widen_fn)(uint16_t);
+typedef uint16_t (*narrow_fn)(float);
+static widen_fn widen_of(int fmt) { return fmt == ORC_BF16 ? orc_bf16_to_f32 : orc_f16_to_f32; }
+static narrow_fn narrow_of(int fmt) { return fmt == ORC_BF16 ? orc_f32_to_bf16 : orc_f32_to_f16; }
+
 void orc_f16_to_f32_array(const uint16_t *h, float *f, int64_t n)
 {
     for (int64_t i = 0; i < n; ++i) f[i] = orc_f16_to_f32(h[i]);
@@ -108,15 +174,16 @@ void orc_f32_to_f16_array(const float *f, uint16_t *h, int64_t n)
 /* multiply, add, in that order, each as its own fp32 operation.      */
 /* ------------------------------------------------------------------ */
 
-void orc_quantize_group(const uint16_t *x, int n, int bits,
-                        float *scale_out, float *zero_out, uint8_t *q, uint16_t *recon)
+void orc_quantize_group_fmt(const uint16_t *x, int n, int bits, int fmt,
+                            float *scale_out, float *zero_out, uint8_t *q, uint16_t *recon)
 {
+    const widen_fn widen = widen_of(fmt);
     /* widen exactly to fp32 (the Metal kernels read float(x[...]),
        [Metal post] "Kernel A" and "Kernel B") */
-    float mn = orc_f16_to_f32(x[0]);
+    float mn = widen(x[0]);
     float mx = mn;
     for (int i = 1; i < n; ++i) {
-        const float v = orc_f16_to_f32(x[i]);
+        const float v = widen(x[i]);
         if (v < mn) mn = v;
         if (v > mx) mx = v;
     }
@@ -133,7 +200,7 @@ void orc_quantize_group(const uint16_t *x, int n, int bits,
     *zero_out = zero;
 
     for (int i = 0; i < n; ++i) {
-        const float v = orc_f16_to_f32(x[i]);
+        const float v = widen(x[i]);
         int code;
         if (scale == 0.0f) {
             /* constant group: the quotient would be 0/0; every element
@@ -150,18 +217,29 @@ void orc_quantize_group(const uint16_t *x, int n, int bits,
             code = (int)r;
         }
         q[i] = (uint8_t)code;
-        if (recon) recon[i] = orc_dequantize_one((uint32_t)code, scale, zero);
+        if (recon) recon[i] = orc_dequantize_one_fmt((uint32_t)code, scale, zero, fmt);
     }
 }
 
+void orc_quantize_group(const uint16_t *x, int n, int bits,
+                        float *scale_out, float *zero_out, uint8_t *q, uint16_t *recon)
+{
+    orc_quantize_group_fmt(x, n, bits, ORC_F16, scale_out, zero_out, q, recon);
+}
+
 /* [Metal post], "Three ways to be off by one bit", item 1: the product is
-   rounded before the add (no fused multiply-add); the cast to fp16 rounds
-   to nearest even. */
-uint16_t orc_dequantize_one(uint32_t q, float scale, float zero)
+   rounded before the add (no fused multiply-add); the cast to the 16-bit
+   format rounds to nearest even. */
+uint16_t orc_dequantize_one_fmt(uint32_t q, float scale, float zero, int fmt)
 {
     const float prod = (float)q * scale;
     const float sum = prod + zero;
-    return orc_f32_to_f16(sum);
+    return narrow_of(fmt)(sum);
+}
+
+uint16_t orc_dequantize_one(uint32_t q, float scale, float zero)
+{
+    return orc_dequantize_one_fmt(q, scale, zero, ORC_F16);
 }
 
 /* ------------------------------------------------------------------ */
@@ -190,12 +268,12 @@ static void put_code(uint32_t *row_words, int64_t d, int bits, uint32_t code)
    group uses its real tokens only; "Three ways to be off by one bit", item 3,
    pads it with copies of the last real token, which leaves min and max --
    and so every result -- unchanged. */
-int orc_quantize_keys(const uint16_t *x, int64_t BH, int64_t S, int64_t D,
-                      int64_t x_bh_stride, int bits, int G,
-                      uint32_t *codes, int64_t codes_bh_stride,
-                      float *scale, float *zero, int64_t meta_bh_stride,
-                      int64_t dst_token,
-                      uint16_t *recon, int64_t recon_bh_stride)
+int orc_quantize_keys_fmt(const uint16_t *x, int64_t BH, int64_t S, int64_t D,
+                          int64_t x_bh_stride, int bits, int G,
+                          uint32_t *codes, int64_t codes_bh_stride,
+                          float *scale, float *zero, int64_t meta_bh_stride,
+                          int64_t dst_token,
+                          uint16_t *recon, int64_t recon_bh_stride, int fmt)
 {
     if (check_common(BH, S, D, bits, G) != 0) return -1;
     if (dst_token < 0 || dst_token % G != 0) return -1;
@@ -220,7 +298,7 @@ int orc_quantize_keys(const uint16_t *x, int64_t BH, int64_t S, int64_t D,
                 for (int i = 0; i < n; ++i)
                     grp[i] = x[bh * x_bh_stride + (s0 + i) * D + d];
                 float sc, ze;
-                orc_quantize_group(grp, n, bits, &sc, &ze, q, recon ? rec : NULL);
+                orc_quantize_group_fmt(grp, n, bits, fmt, &sc, &ze, q, recon ? rec : NULL);
                 scale[bh * meta_bh_stride + meta_row * D + d] = sc;
                 zero[bh * meta_bh_stride + meta_row * D + d] = ze;
                 for (int i = 0; i < n; ++i) {
@@ -238,12 +316,12 @@ int orc_quantize_keys(const uint16_t *x, int64_t BH, int64_t S, int64_t D,
 /* Values, per token: [Metal post] "What we're actually optimizing" (values
    get one scale per token over a group of channels) and "Kernel B" (the
    group of token s is channels [j*G, min(j*G+G, D)) of that token). */
-int orc_quantize_values(const uint16_t *x, int64_t BH, int64_t S, int64_t D,
-                        int64_t x_bh_stride, int bits, int G,
-                        uint32_t *codes, int64_t codes_bh_stride,
-                        float *scale, float *zero, int64_t meta_bh_stride,
-                        int64_t dst_token,
-                        uint16_t *recon, int64_t recon_bh_stride)
+int orc_quantize_values_fmt(const uint16_t *x, int64_t BH, int64_t S, int64_t D,
+                            int64_t x_bh_stride, int bits, int G,
+                            uint32_t *codes, int64_t codes_bh_stride,
+                            float *scale, float *zero, int64_t meta_bh_stride,
+                            int64_t dst_token,
+                            uint16_t *recon, int64_t recon_bh_stride, int fmt)
 {
     if (check_common(BH, S, D, bits, G) != 0) return -1;
     if (dst_token < 0) return -1;
@@ -263,7 +341,7 @@ int orc_quantize_values(const uint16_t *x, int64_t BH, int64_t S, int64_t D,
                 const int64_t d1 = (d0 + G < D) ? d0 + G : D;
                 const int n = (int)(d1 - d0);
                 float sc, ze;
-                orc_quantize_group(xrow + d0, n, bits, &sc, &ze, q, recon ? rec : NULL);
+                orc_quantize_group_fmt(xrow + d0, n, bits, fmt, &sc, &ze, q, recon ? rec : NULL);
                 scale[bh * meta_bh_stride + (dst_token + s) * NGD + j] = sc;
                 zero[bh * meta_bh_stride + (dst_token + s) * NGD + j] = ze;
                 for (int i = 0; i < n; ++i) {
@@ -277,6 +355,30 @@ int orc_quantize_values(const uint16_t *x, int64_t BH, int64_t S, int64_t D,
     return 0;
 }
 
+int orc_quantize_keys(const uint16_t *x, int64_t BH, int64_t S, int64_t D,
+                      int64_t x_bh_stride, int bits, int G,
+                      uint32_t *codes, int64_t codes_bh_stride,
+                      float *scale, float *zero, int64_t meta_bh_stride,
+                      int64_t dst_token,
+                      uint16_t *recon, int64_t recon_bh_stride)
+{
+    return orc_quantize_keys_fmt(x, BH, S, D, x_bh_stride, bits, G, codes, codes_bh_stride,
+                                 scale, zero, meta_bh_stride, dst_token, recon, recon_bh_stride,
+                                 ORC_F16);
+}
+
+int orc_quantize_values(const uint16_t *x, int64_t BH, int64_t S, int64_t D,
+                        int64_t x_bh_stride, int bits, int G,
+                        uint32_t *codes, int64_t codes_bh_stride,
+                        float *scale, float *zero, int64_t meta_bh_stride,
+                        int64_t dst_token,
+                        uint16_t *recon, int64_t recon_bh_stride)
+{
+    return orc_quantize_values_fmt(x, BH, S, D, x_bh_stride, bits, G, codes, codes_bh_stride,
+                                   scale, zero, meta_bh_stride, dst_token, recon, recon_bh_stride,
+                                   ORC_F16);
+}
+
 static uint32_t get_code(const uint32_t *row_words, int64_t d, int bits)
 {
     const int64_t per_word = 32 / bits;
@@ -288,11 +390,11 @@ static uint32_t get_code(const uint32_t *row_words, int64_t d, int bits)
 /* Dequantization, [Metal post] "So why does the kernel ship?" (the packed
    store is expanded back to fp16) with the element rule of
    orc_dequantize_one. */
-int orc_dequantize(int kind, const uint32_t *codes, int64_t codes_bh_stride,
-                   const float *scale, const float *zero, int64_t meta_bh_stride,
-                   int64_t BH, int64_t D, int bits, int G,
-                   int64_t t0, int64_t n,
-                   uint16_t *out, int64_t out_bh_stride)
+int orc_dequantize_fmt(int kind, const uint32_t *codes, int64_t codes_bh_stride,
+                       const float *scale, const float *zero, int64_t meta_bh_stride,
+                       int64_t BH, int64_t D, int bits, int G,
+                       int64_t t0, int64_t n,
+                       uint16_t *out, int64_t out_bh_stride, int fmt)
 {
     if (check_common(BH, n, D, bits, G) != 0) return -1;
     if (t0 < 0 || (kind != ORC_KEYS && kind != ORC_VALUES)) return -1;
@@ -307,11 +409,21 @@ int orc_dequantize(int kind, const uint32_t *codes, int64_t codes_bh_stride,
                 if (kind == ORC_KEYS) m = bh * meta_bh_stride + (t / G) * D + d;
                 else                  m = bh * meta_bh_stride + t * NGD + d / G;
                 out[bh * out_bh_stride + i * D + d] =
-                    orc_dequantize_one(get_code(row, d, bits), scale[m], zero[m]);
+                    orc_dequantize_one_fmt(get_code(row, d, bits), scale[m], zero[m], fmt);
             }
         }
     }
     return 0;
+}
+
+int orc_dequantize(int kind, const uint32_t *codes, int64_t codes_bh_stride,
+                   const float *scale, const float *zero, int64_t meta_bh_stride,
+                   int64_t BH, int64_t D, int bits, int G,
+                   int64_t t0, int64_t n,
+                   uint16_t *out, int64_t out_bh_stride)
+{
+    return orc_dequantize_fmt(kind, codes, codes_bh_stride, scale, zero, meta_bh_stride, BH, D,
+                              bits, G, t0, n, out, out_bh_stride, ORC_F16);
 }
 
 /* ------------------------------------------------------------------ */

@@ -34,6 +34,39 @@ uint16_t orc_f32_to_f16(float f);
 void     orc_f16_to_f32_array(const uint16_t *h, float *f, int64_t n);
 void     orc_f32_to_f16_array(const float *f, uint16_t *h, int64_t n);
 
+/* bfloat16 <-> binary32 (binary32 with the low 16 fraction bits dropped),
+   round to nearest even, with subnormals. */
+float    orc_bf16_to_f32(uint16_t b);
+uint16_t orc_f32_to_bf16(float f);
+void     orc_bf16_to_f32_array(const uint16_t *h, float *f, int64_t n);
+void     orc_f32_to_bf16_array(const float *f, uint16_t *h, int64_t n);
+
+/* 16-bit storage format of inputs and reconstructions for the _fmt calls. */
+enum { ORC_F16 = 0, ORC_BF16 = 1 };
+
+/* The calls below without _fmt read and write fp16; their _fmt twins take
+   the format as their last (or, for the group, fourth) argument. */
+void orc_quantize_group_fmt(const uint16_t *x, int n, int bits, int fmt,
+                            float *scale, float *zero, uint8_t *q, uint16_t *recon);
+uint16_t orc_dequantize_one_fmt(uint32_t q, float scale, float zero, int fmt);
+int orc_quantize_keys_fmt(const uint16_t *x, int64_t BH, int64_t S, int64_t D,
+                          int64_t x_bh_stride, int bits, int G,
+                          uint32_t *codes, int64_t codes_bh_stride,
+                          float *scale, float *zero, int64_t meta_bh_stride,
+                          int64_t dst_token,
+                          uint16_t *recon, int64_t recon_bh_stride, int fmt);
+int orc_quantize_values_fmt(const uint16_t *x, int64_t BH, int64_t S, int64_t D,
+                            int64_t x_bh_stride, int bits, int G,
+                            uint32_t *codes, int64_t codes_bh_stride,
+                            float *scale, float *zero, int64_t meta_bh_stride,
+                            int64_t dst_token,
+                            uint16_t *recon, int64_t recon_bh_stride, int fmt);
+int orc_dequantize_fmt(int kind, const uint32_t *codes, int64_t codes_bh_stride,
+                       const float *scale, const float *zero, int64_t meta_bh_stride,
+                       int64_t BH, int64_t D, int bits, int G,
+                       int64_t t0, int64_t n,
+                       uint16_t *out, int64_t out_bh_stride, int fmt);
+
 /* One quantization group of n fp16 values.  Writes scale, zero, the n codes
    and the n fp16 reconstructions (recon may be NULL). */
 void orc_quantize_group(const uint16_t *x, int n, int bits,

@@ -88,6 +88,43 @@ def rnd16_bits(r: Fraction) -> int:
     return bits | 0x8000 if r < 0 else bits
 
 
+def rndbf16(r: Fraction) -> Fraction:
+    return _round(Fraction(r), 7, -126)
+
+
+def bf16_value(bits: int) -> Fraction:
+    bits = int(bits)
+    sign = -1 if bits & 0x8000 else 1
+    e = (bits >> 7) & 0xFF
+    f = bits & 0x7F
+    assert e != 255, "finite inputs only"
+    if e == 0:
+        return sign * Fraction(f) * Fraction(2) ** -133
+    return sign * Fraction(128 + f) * Fraction(2) ** (e - 134)
+
+
+def bf16_bits(v: Fraction) -> int:
+    """Encode a value already on the bfloat16 grid."""
+    sign = 0x8000 if v < 0 else 0
+    a = abs(v)
+    if a == 0:
+        return sign
+    if a < Fraction(2) ** -126:
+        n = a * Fraction(2) ** 133
+        assert n.denominator == 1
+        return sign | int(n)
+    e = _floor_log2(a)
+    n = a / Fraction(2) ** (e - 7)
+    assert n.denominator == 1 and 128 <= n < 256
+    return sign | ((e + 127) << 7) | (int(n) - 128)
+
+
+def rndbf16_bits(r: Fraction) -> int:
+    r = Fraction(r)
+    bits = bf16_bits(abs(rndbf16(r)))
+    return bits | 0x8000 if r < 0 else bits
+
+
 def f32_bits(v: Fraction) -> int:
     """Bit pattern of a value already on the binary32 grid."""
     f = float(v)  # exact: v is representable in binary32, hence in binary64
@@ -95,7 +132,7 @@ def f32_bits(v: Fraction) -> int:
 
 
 def quantize_group(xbits, bits: int, *, ties="even", quotient="fp32",
-                   recon_fma=False):
+                   recon_fma=False, fmt="f16"):
     """Emulate one group.  The keyword arguments select deliberately wrong
     variants (used to show that a fixture discriminates):
       ties="away"          round half away from zero instead of half to even
@@ -103,8 +140,10 @@ def quantize_group(xbits, bits: int, *, ties="even", quotient="fp32",
                            binary32 rounding
       quotient="rcp"       binary32 (x-zero) * binary32(1/scale)
       recon_fma=True       one rounding for q*scale+zero (a fused multiply-add)
+      fmt="bf16"           inputs and reconstructions in bfloat16
     Returns (scale, zero, codes, recon_bits) with scale/zero as Fractions."""
-    xs = [f16_value(b) for b in xbits]
+    value, to_bits = (f16_value, rnd16_bits) if fmt == "f16" else (bf16_value, rndbf16_bits)
+    xs = [value(b) for b in xbits]
     mn, mx = min(xs), max(xs)
     levels = (1 << bits) - 1
     rng = rnd32(mx - mn)
@@ -134,5 +173,5 @@ def quantize_group(xbits, bits: int, *, ties="even", quotient="fp32",
         else:
             r = rnd32(rnd32(q * scale) + zero)
         codes.append(q)
-        recon.append(rnd16_bits(r))
+        recon.append(to_bits(r))
     return scale, zero, codes, recon
