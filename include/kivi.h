@@ -16,7 +16,8 @@
  *  - Validation happens before anything is enqueued: a negative return
  *    means nothing was launched.  A zero-sized call (S == 0, n_tokens == 0,
  *    B == 0) succeeds without launching.
- *  - fp16 tensors are passed as `uint16_t*` holding IEEE binary16 bits.
+ *  - fp16 tensors are passed as `uint16_t*` holding IEEE binary16 bits (the
+ *    _bf16 calls take bfloat16 bits instead).
  *  - Strides are in elements of the array they index.  Token rows inside a
  *    bh slab are contiguous (row stride = head_dim).
  *  - Inputs must not alias outputs.  Calls on different streams may run
@@ -117,6 +118,21 @@ int kivi_quantize_values(const uint16_t* x, int64_t BH, int64_t S, int64_t x_bh_
                          uint16_t* recon, int64_t recon_bh_stride, hipStream_t stream);
 
 /*
+ * The same flushes for bfloat16 caches: x (and recon, if given) hold
+ * bfloat16 bit patterns, widened exactly to fp32 (bfloat16 is binary32 with
+ * the low 16 fraction bits dropped); every later step is the same fp32
+ * arithmetic, and the reconstruction is rounded to bfloat16 (nearest even).
+ * The packed store is identical to the one the fp16 calls write.  Inputs
+ * must be finite with a finite max - min in every group.
+ */
+int kivi_quantize_keys_bf16(const uint16_t* x, int64_t BH, int64_t S, int64_t x_bh_stride,
+                            const kivi_store* dst, int64_t dst_token,
+                            uint16_t* recon, int64_t recon_bh_stride, hipStream_t stream);
+int kivi_quantize_values_bf16(const uint16_t* x, int64_t BH, int64_t S, int64_t x_bh_stride,
+                              const kivi_store* dst, int64_t dst_token,
+                              uint16_t* recon, int64_t recon_bh_stride, hipStream_t stream);
+
+/*
  * Dequantize tokens [token_begin, token_begin + n_tokens) of every slab of
  * a key or value store to fp16: out = fp16_rne(fl(fl(q*scale) + zero))
  * ([Metal post] "Three ways to be off by one bit", item 1: no fused
@@ -129,6 +145,11 @@ int kivi_quantize_values(const uint16_t* x, int64_t BH, int64_t S, int64_t x_bh_
  */
 int kivi_dequantize(const kivi_store* src, int64_t BH, int64_t token_begin, int64_t n_tokens,
                     uint16_t* out, int64_t out_bh_stride, hipStream_t stream);
+
+/* kivi_dequantize with a bfloat16 output: out = bf16_rne(fl(fl(q*scale) +
+ * zero)), bit-exact with the reconstruction the bfloat16 flushes write. */
+int kivi_dequantize_bf16(const kivi_store* src, int64_t BH, int64_t token_begin, int64_t n_tokens,
+                         uint16_t* out, int64_t out_bh_stride, hipStream_t stream);
 
 /*
  * Fused dequantize + attend for one new query token per sequence

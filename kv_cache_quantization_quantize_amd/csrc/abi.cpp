@@ -65,7 +65,7 @@ int check_f16_tensor(const void* p, int64_t BH, int64_t S, int64_t stride) {
     return KIVI_OK;
 }
 
-int flush(bool keys, const uint16_t* x, int64_t BH, int64_t S, int64_t x_bh_stride,
+int flush(bool keys, bool bf16, const uint16_t* x, int64_t BH, int64_t S, int64_t x_bh_stride,
           const kivi_store* dst, int64_t dst_token, uint16_t* recon, int64_t recon_bh_stride,
           hipStream_t stream) {
     if (BH < 0 || S < 0) return KIVI_ERR_SHAPE;
@@ -84,6 +84,7 @@ int flush(bool keys, const uint16_t* x, int64_t BH, int64_t S, int64_t x_bh_stri
     a.scale = dst->scale; a.zero = dst->zero; a.meta_bh_stride = dst->meta_bh_stride;
     a.dst_token = dst_token; a.recon = recon; a.recon_bh_stride = recon_bh_stride;
     a.bits = dst->bits;
+    a.bf16 = bf16;
     return finish(keys ? kivi::launch_key_flush(a, stream) : kivi::launch_value_flush(a, stream));
 }
 
@@ -94,17 +95,29 @@ extern "C" {
 int kivi_quantize_keys(const uint16_t* x, int64_t BH, int64_t S, int64_t x_bh_stride,
                        const kivi_store* dst, int64_t dst_token,
                        uint16_t* recon, int64_t recon_bh_stride, hipStream_t stream) {
-    return flush(true, x, BH, S, x_bh_stride, dst, dst_token, recon, recon_bh_stride, stream);
+    return flush(true, false, x, BH, S, x_bh_stride, dst, dst_token, recon, recon_bh_stride, stream);
+}
+
+int kivi_quantize_keys_bf16(const uint16_t* x, int64_t BH, int64_t S, int64_t x_bh_stride,
+                            const kivi_store* dst, int64_t dst_token,
+                            uint16_t* recon, int64_t recon_bh_stride, hipStream_t stream) {
+    return flush(true, true, x, BH, S, x_bh_stride, dst, dst_token, recon, recon_bh_stride, stream);
 }
 
 int kivi_quantize_values(const uint16_t* x, int64_t BH, int64_t S, int64_t x_bh_stride,
                          const kivi_store* dst, int64_t dst_token,
                          uint16_t* recon, int64_t recon_bh_stride, hipStream_t stream) {
-    return flush(false, x, BH, S, x_bh_stride, dst, dst_token, recon, recon_bh_stride, stream);
+    return flush(false, false, x, BH, S, x_bh_stride, dst, dst_token, recon, recon_bh_stride, stream);
 }
 
-int kivi_dequantize(const kivi_store* src, int64_t BH, int64_t token_begin, int64_t n_tokens,
-                    uint16_t* out, int64_t out_bh_stride, hipStream_t stream) {
+int kivi_quantize_values_bf16(const uint16_t* x, int64_t BH, int64_t S, int64_t x_bh_stride,
+                              const kivi_store* dst, int64_t dst_token,
+                              uint16_t* recon, int64_t recon_bh_stride, hipStream_t stream) {
+    return flush(false, true, x, BH, S, x_bh_stride, dst, dst_token, recon, recon_bh_stride, stream);
+}
+
+static int dequantize(bool bf16, const kivi_store* src, int64_t BH, int64_t token_begin, int64_t n_tokens,
+                      uint16_t* out, int64_t out_bh_stride, hipStream_t stream) {
     if (BH < 0 || n_tokens < 0) return KIVI_ERR_SHAPE;
     int rc = check_store(src, -1, BH, token_begin, n_tokens);
     if (rc != KIVI_OK) return rc;
@@ -116,8 +129,18 @@ int kivi_dequantize(const kivi_store* src, int64_t BH, int64_t token_begin, int6
     a.codes = src->codes; a.codes_bh_stride = src->codes_bh_stride;
     a.scale = src->scale; a.zero = src->zero; a.meta_bh_stride = src->meta_bh_stride;
     a.BH = BH; a.t0 = token_begin; a.n = n_tokens; a.out = out; a.out_bh_stride = out_bh_stride;
-    a.bits = src->bits; a.kind = src->kind;
+    a.bits = src->bits; a.kind = src->kind; a.bf16 = bf16;
     return finish(kivi::launch_dequantize(a, stream));
+}
+
+int kivi_dequantize(const kivi_store* src, int64_t BH, int64_t token_begin, int64_t n_tokens,
+                    uint16_t* out, int64_t out_bh_stride, hipStream_t stream) {
+    return dequantize(false, src, BH, token_begin, n_tokens, out, out_bh_stride, stream);
+}
+
+int kivi_dequantize_bf16(const kivi_store* src, int64_t BH, int64_t token_begin, int64_t n_tokens,
+                         uint16_t* out, int64_t out_bh_stride, hipStream_t stream) {
+    return dequantize(true, src, BH, token_begin, n_tokens, out, out_bh_stride, stream);
 }
 
 size_t kivi_decode_attend_workspace_bytes(int64_t B, int32_t Hq, int32_t Hkv,

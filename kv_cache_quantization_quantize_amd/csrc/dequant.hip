@@ -1,5 +1,6 @@
-// dequant.hip -- expand a packed key or value store back to fp16 for a token
-// range: out = fp16_rne(fl(fl(q * scale) + zero)), the same two roundings as
+// dequant.hip -- expand a packed key or value store back to fp16 (or
+// bfloat16) for a token range: out = rne(fl(fl(q * scale) + zero)), the same
+// two roundings as
 // the flush's reconstruction (blog post "A 5.65x Metal Kernel That Made My
 // LLM Exactly 0% Faster", "Three ways to be off by one bit", item 1; "So why
 // does the kernel ship?": the shipped cache expands to fp16 before
@@ -16,7 +17,7 @@ namespace kivi {
 // Rows [0, n_rows) of one tile; row k is store token t_first + k, written to
 // ot + k*128.  ONE_GROUP (keys only): the 32 rows are exactly one key group,
 // so its scale and zero are loaded once for the tile.
-template <int BITS, bool KEYS, bool ONE_GROUP>
+template <int BITS, bool KEYS, bool ONE_GROUP, bool BF16>
 __device__ __forceinline__ void dequant_tile(const uint32_t* __restrict__ cb, const float* __restrict__ scb,
                                              const float* __restrict__ zeb, int64_t t_first, int n_rows,
                                              uint16_t* __restrict__ ot, int lane)
@@ -72,12 +73,12 @@ __device__ __forceinline__ void dequant_tile(const uint32_t* __restrict__ cb, co
         }
         uint32_t h[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) h[j] = recon_f16(static_cast<float>((w >> (BITS * j)) & kMask), sc[j], ze[j]);
+        for (int j = 0; j < 8; ++j) h[j] = recon_out<BF16>(static_cast<float>((w >> (BITS * j)) & kMask), sc[j], ze[j]);
         *reinterpret_cast<uint4*>(ot + k * kHeadDim + c * 8) = pack8(h);
     }
 }
 
-template <int BITS, bool KEYS>
+template <int BITS, bool KEYS, bool BF16>
 __global__ __launch_bounds__(kBlock) void dequant_kernel(
     const uint32_t* __restrict__ codes, int64_t codes_bh_stride,
     const float* __restrict__ scale, const float* __restrict__ zero, int64_t meta_bh_stride,
@@ -96,26 +97,31 @@ __global__ __launch_bounds__(kBlock) void dequant_kernel(
     const float* zeb = zero + bh * meta_bh_stride;
     uint16_t* ot = out + bh * out_bh_stride + i0 * kHeadDim;
     if (KEYS && rows >= 32 && (t0 + i0) % kGroup == 0)
-        dequant_tile<BITS, KEYS, true>(cb, scb, zeb, t0 + i0, 32, ot, lane);
+        dequant_tile<BITS, KEYS, true, BF16>(cb, scb, zeb, t0 + i0, 32, ot, lane);
     else
-        dequant_tile<BITS, KEYS, false>(cb, scb, zeb, t0 + i0, rows < 32 ? static_cast<int>(rows) : 32, ot, lane);
+        dequant_tile<BITS, KEYS, false, BF16>(cb, scb, zeb, t0 + i0, rows < 32 ? static_cast<int>(rows) : 32, ot, lane);
 }
 
-template <int BITS, bool KEYS>
+template <int BITS, bool KEYS, bool BF16>
 static hipError_t launch_t(const DequantArgs& a, hipStream_t stream) {
     const int64_t tiles_per_bh = (a.n + 31) / 32;
     const int64_t n_tiles = a.BH * tiles_per_bh;
     const int64_t blocks = (n_tiles + kWavesPerBlock - 1) / kWavesPerBlock;
-    hipLaunchKernelGGL((dequant_kernel<BITS, KEYS>), dim3(static_cast<uint32_t>(blocks)),
+    hipLaunchKernelGGL((dequant_kernel<BITS, KEYS, BF16>), dim3(static_cast<uint32_t>(blocks)),
                        dim3(kBlock), 0, stream, a.codes, a.codes_bh_stride, a.scale, a.zero,
                        a.meta_bh_stride, a.t0, a.n, a.out, a.out_bh_stride, tiles_per_bh, n_tiles);
     return hipGetLastError();
 }
 
-hipError_t launch_dequantize(const DequantArgs& a, hipStream_t stream) {
+template <bool BF16>
+static hipError_t launch_fmt(const DequantArgs& a, hipStream_t stream) {
     const bool keys = a.kind == 0;
-    if (a.bits == 4) return keys ? launch_t<4, true>(a, stream) : launch_t<4, false>(a, stream);
-    return keys ? launch_t<2, true>(a, stream) : launch_t<2, false>(a, stream);
+    if (a.bits == 4) return keys ? launch_t<4, true, BF16>(a, stream) : launch_t<4, false, BF16>(a, stream);
+    return keys ? launch_t<2, true, BF16>(a, stream) : launch_t<2, false, BF16>(a, stream);
+}
+
+hipError_t launch_dequantize(const DequantArgs& a, hipStream_t stream) {
+    return a.bf16 ? launch_fmt<true>(a, stream) : launch_fmt<false>(a, stream);
 }
 
 }  // namespace kivi

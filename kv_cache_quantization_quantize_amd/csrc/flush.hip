@@ -27,7 +27,7 @@ namespace kivi {
 // One tile.  xt, ct, rt point at token s0 of the slab (input, codes, recon);
 // n_rows = min(32, S - s0) real rows.  RAGGED tiles clamp loads to the last
 // real row and guard stores; full tiles do neither.
-template <int BITS, bool RECON, bool RAGGED>
+template <int BITS, bool RECON, bool RAGGED, bool BF16>
 __device__ __forceinline__ void key_tile(const uint16_t* __restrict__ xt, uint32_t* __restrict__ ct,
                                          float* __restrict__ sct, float* __restrict__ zet,
                                          uint16_t* __restrict__ rt, int n_rows, int lane, float one)
@@ -47,36 +47,49 @@ __device__ __forceinline__ void key_tile(const uint16_t* __restrict__ xt, uint32
         raw[i] = *reinterpret_cast<const uint4*>(xt + row * kHeadDim + c * 8);
     }
 
-    // Per-channel min/max in packed fp16 (exact: the conversion to fp32 is
-    // monotone), over the lane's 8 rows and then across the 4 row lanes.
-    half2_t mn[4], mx[4];
+    // Per-channel min/max over the lane's 8 rows and then across the 4 row
+    // lanes: fp16 in packed fp16 (exact: the conversion to fp32 is
+    // monotone), bfloat16 widened exactly to fp32 (no packed bfloat16 form).
+    float mnf[8], mxf[8];
+    if constexpr (!BF16) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        half2_t v[kTokPerLane];
+        for (int k = 0; k < 4; ++k) {
+            half2_t v[kTokPerLane];
 #pragma unroll
-        for (int i = 0; i < kTokPerLane; ++i) {
-            const uint32_t w = k == 0 ? raw[i].x : k == 1 ? raw[i].y : k == 2 ? raw[i].z : raw[i].w;
-            v[i] = as_h2(w);
+            for (int i = 0; i < kTokPerLane; ++i) v[i] = as_h2(word_of(raw[i], k));
+            half2_t mn = hmin3(hmin3(v[0], v[1], v[2]), hmin3(v[3], v[4], v[5]), hmin(v[6], v[7]));
+            half2_t mx = hmax3(hmax3(v[0], v[1], v[2]), hmax3(v[3], v[4], v[5]), hmax(v[6], v[7]));
+            mn = half_min(row_pair_min(mn));
+            mx = half_max(row_pair_max(mx));
+            mnf[2 * k] = static_cast<float>(mn[0]); mnf[2 * k + 1] = static_cast<float>(mn[1]);
+            mxf[2 * k] = static_cast<float>(mx[0]); mxf[2 * k + 1] = static_cast<float>(mx[1]);
         }
-        mn[k] = hmin3(hmin3(v[0], v[1], v[2]), hmin3(v[3], v[4], v[5]), hmin(v[6], v[7]));
-        mx[k] = hmax3(hmax3(v[0], v[1], v[2]), hmax3(v[3], v[4], v[5]), hmax(v[6], v[7]));
-        mn[k] = half_min(row_pair_min(mn[k]));
-        mx[k] = half_max(row_pair_max(mx[k]));
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            float v[kTokPerLane];
+#pragma unroll
+            for (int i = 0; i < kTokPerLane; ++i) {
+                const uint32_t w = word_of(raw[i], j >> 1);
+                v[i] = (j & 1) ? bf16_hi(w) : bf16_lo(w);
+            }
+            const float mn = fmin3(fmin3(v[0], v[1], v[2]), fmin3(v[3], v[4], v[5]), fminimum(v[6], v[7]));
+            const float mx = fmax3(fmax3(v[0], v[1], v[2]), fmax3(v[3], v[4], v[5]), fmaximum(v[6], v[7]));
+            mnf[j] = rows_min_f32(mn);
+            mxf[j] = rows_max_f32(mx);
+        }
     }
 
     // zero = min, scale = RN((max - min) / (2^bits - 1)), r ~ 1/scale.  (The
     // range needs no zero canonicalization: x - y is +0 for equal zeros.)
     float ze[8], sc[8], rc[8];
+    bool slow = false;                              // a scale off the fast path (bfloat16 only)
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int j = 2 * k + h;
-            const float lo = static_cast<float>(mn[k][h]);
-            ze[j] = canon_zero(lo);
-            sc[j] = scale_of<BITS>(static_cast<float>(mx[k][h]) - lo);
-            rc[j] = recip_clamped(sc[j]);
-        }
+    for (int j = 0; j < 8; ++j) {
+        ze[j] = canon_zero(mnf[j]);
+        sc[j] = BF16 ? scale_div<BITS>(mxf[j] - mnf[j]) : scale_of<BITS>(mxf[j] - mnf[j]);
+        rc[j] = recip_clamped(sc[j]);
+        if constexpr (BF16) slow |= !fast_scale(sc[j]);
     }
 
     if (r == 0) {
@@ -90,17 +103,16 @@ __device__ __forceinline__ void key_tile(const uint16_t* __restrict__ xt, uint32
 #pragma unroll
     for (int i = 0; i < kTokPerLane; ++i) {
         const int row = r + kRowsPerWave * i;
-        const half2_t hv[4] = {as_h2(raw[i].x), as_h2(raw[i].y), as_h2(raw[i].z), as_h2(raw[i].w)};
         float t[8], qf[8];
         float dev = 0.0f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            t[j] = sub_from_f16(hv[j >> 1][j & 1], one, ze[j]);
+            t[j] = sub_elem<BF16>(raw[i], j, one, ze[j]);
             qf[j] = quant_fast(t[j], rc[j], dev);
         }
-        if (dev > kNearTie) {                      // rare: within 2^-16 of a tie
+        if (dev > kNearTie || slow) {              // rare: within 2^-16 of a tie
 #pragma unroll
-            for (int j = 0; j < 8; ++j) qf[j] = quant_exact(t[j], sc[j]);
+            for (int j = 0; j < 8; ++j) qf[j] = quant_exact(t[j], sc[j], static_cast<float>((1 << BITS) - 1));
         }
         uint32_t packed = static_cast<uint32_t>(qf[0]);
 #pragma unroll
@@ -117,13 +129,13 @@ __device__ __forceinline__ void key_tile(const uint16_t* __restrict__ xt, uint32
         if constexpr (RECON) {
             uint32_t h[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) h[j] = recon_f16(qf[j], sc[j], ze[j]);
+            for (int j = 0; j < 8; ++j) h[j] = recon_out<BF16>(qf[j], sc[j], ze[j]);
             if (live) *reinterpret_cast<uint4*>(rt + row * kHeadDim + c * 8) = pack8(h);
         }
     }
 }
 
-template <int BITS, bool RECON>
+template <int BITS, bool RECON, bool BF16>
 __global__ __launch_bounds__(kBlock) void key_flush_kernel(
     const uint16_t* __restrict__ x, int64_t S, int64_t x_bh_stride,
     uint32_t* __restrict__ codes, int64_t codes_bh_stride,
@@ -144,15 +156,15 @@ __global__ __launch_bounds__(kBlock) void key_flush_kernel(
     uint16_t* rt = RECON ? recon + bh * recon_bh_stride + s0 * kHeadDim : nullptr;
     const int64_t rows = S - s0;
     if (rows >= kGroup)
-        key_tile<BITS, RECON, false>(xt, ct, scale + moff, zero + moff, rt, kGroup, lane, one);
+        key_tile<BITS, RECON, false, BF16>(xt, ct, scale + moff, zero + moff, rt, kGroup, lane, one);
     else
-        key_tile<BITS, RECON, true>(xt, ct, scale + moff, zero + moff, rt, static_cast<int>(rows), lane, one);
+        key_tile<BITS, RECON, true, BF16>(xt, ct, scale + moff, zero + moff, rt, static_cast<int>(rows), lane, one);
 }
 
 // ---------------------------------------------------------------------------
 // Values: group = (bh, token s, channel group j) over channels [32j, 32j+32)
 // ---------------------------------------------------------------------------
-template <int BITS, bool RECON, bool RAGGED>
+template <int BITS, bool RECON, bool RAGGED, bool BF16>
 __device__ __forceinline__ void value_tile(const uint16_t* __restrict__ xt, uint32_t* __restrict__ ct,
                                            float* __restrict__ sct, float* __restrict__ zet,
                                            uint16_t* __restrict__ rt, int n_rows, int lane, float one)
@@ -174,32 +186,50 @@ __device__ __forceinline__ void value_tile(const uint16_t* __restrict__ xt, uint
 #pragma unroll
     for (int i = 0; i < kTokPerLane; ++i) {
         const int row = r + kRowsPerWave * i;
-        const half2_t hv[4] = {as_h2(raw[i].x), as_h2(raw[i].y), as_h2(raw[i].z), as_h2(raw[i].w)};
-        const half2_t mn2 = hmin(hmin3(hv[0], hv[1], hv[2]), hv[3]);
-        const half2_t mx2 = hmax(hmax3(hv[0], hv[1], hv[2]), hv[3]);
-        // (min, -max) of the lane in one register, then the 4 lanes of the
-        // group (a DPP quad) with min only
-        half2_t mm;
-        mm[0] = __builtin_elementwise_minimum(mn2[0], mn2[1]);
-        mm[1] = -__builtin_elementwise_maximum(mx2[0], mx2[1]);
-        mm = hmin(mm, as_h2(quad_xor1(as_u32(mm))));
-        mm = hmin(mm, as_h2(quad_xor2(as_u32(mm))));
-        const float lo = static_cast<float>(mm[0]);
-        const float hi = -static_cast<float>(mm[1]);
+        float lo, hi;
+        if constexpr (!BF16) {
+            const half2_t hv[4] = {as_h2(raw[i].x), as_h2(raw[i].y), as_h2(raw[i].z), as_h2(raw[i].w)};
+            const half2_t mn2 = hmin(hmin3(hv[0], hv[1], hv[2]), hv[3]);
+            const half2_t mx2 = hmax(hmax3(hv[0], hv[1], hv[2]), hv[3]);
+            // (min, -max) of the lane in one register, then the 4 lanes of the
+            // group (a DPP quad) with min only
+            half2_t mm;
+            mm[0] = __builtin_elementwise_minimum(mn2[0], mn2[1]);
+            mm[1] = -__builtin_elementwise_maximum(mx2[0], mx2[1]);
+            mm = hmin(mm, as_h2(quad_xor1(as_u32(mm))));
+            mm = hmin(mm, as_h2(quad_xor2(as_u32(mm))));
+            lo = static_cast<float>(mm[0]);
+            hi = -static_cast<float>(mm[1]);
+        } else {
+            float v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const uint32_t w = word_of(raw[i], k >> 1);
+                v[k] = (k & 1) ? bf16_hi(w) : bf16_lo(w);
+            }
+            lo = fminimum(fmin3(v[0], v[1], v[2]), fmin3(v[3], v[4], v[5]));
+            lo = fmin3(lo, v[6], v[7]);
+            hi = fmaximum(fmax3(v[0], v[1], v[2]), fmax3(v[3], v[4], v[5]));
+            hi = fmax3(hi, v[6], v[7]);
+            lo = fminimum(lo, __uint_as_float(quad_xor1(__float_as_uint(lo))));
+            hi = fmaximum(hi, __uint_as_float(quad_xor1(__float_as_uint(hi))));
+            lo = fminimum(lo, __uint_as_float(quad_xor2(__float_as_uint(lo))));
+            hi = fmaximum(hi, __uint_as_float(quad_xor2(__float_as_uint(hi))));
+        }
         const float ze = canon_zero(lo);
-        const float sc = scale_of<BITS>(hi - lo);
+        const float sc = BF16 ? scale_div<BITS>(hi - lo) : scale_of<BITS>(hi - lo);
         const float rc = recip_clamped(sc);
 
         float t[8], qf[8];
         float dev = 0.0f;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            t[k] = sub_from_f16(hv[k >> 1][k & 1], one, ze);
+            t[k] = sub_elem<BF16>(raw[i], k, one, ze);
             qf[k] = quant_fast(t[k], rc, dev);
         }
-        if (dev > kNearTie) {
+        if (dev > kNearTie || (BF16 && !fast_scale(sc))) {
 #pragma unroll
-            for (int k = 0; k < 8; ++k) qf[k] = quant_exact(t[k], sc);
+            for (int k = 0; k < 8; ++k) qf[k] = quant_exact(t[k], sc, static_cast<float>((1 << BITS) - 1));
         }
         uint32_t packed = static_cast<uint32_t>(qf[0]);
 #pragma unroll
@@ -218,13 +248,13 @@ __device__ __forceinline__ void value_tile(const uint16_t* __restrict__ xt, uint
         if constexpr (RECON) {
             uint32_t h[8];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) h[k] = recon_f16(qf[k], sc, ze);
+            for (int k = 0; k < 8; ++k) h[k] = recon_out<BF16>(qf[k], sc, ze);
             if (live) *reinterpret_cast<uint4*>(rt + row * kHeadDim + c * 8) = pack8(h);
         }
     }
 }
 
-template <int BITS, bool RECON>
+template <int BITS, bool RECON, bool BF16>
 __global__ __launch_bounds__(kBlock) void value_flush_kernel(
     const uint16_t* __restrict__ x, int64_t S, int64_t x_bh_stride,
     uint32_t* __restrict__ codes, int64_t codes_bh_stride,
@@ -245,48 +275,58 @@ __global__ __launch_bounds__(kBlock) void value_flush_kernel(
     uint16_t* rt = RECON ? recon + bh * recon_bh_stride + s0 * kHeadDim : nullptr;
     const int64_t rows = S - s0;
     if (rows >= 32)
-        value_tile<BITS, RECON, false>(xt, ct, scale + moff, zero + moff, rt, 32, lane, one);
+        value_tile<BITS, RECON, false, BF16>(xt, ct, scale + moff, zero + moff, rt, 32, lane, one);
     else
-        value_tile<BITS, RECON, true>(xt, ct, scale + moff, zero + moff, rt, static_cast<int>(rows), lane, one);
+        value_tile<BITS, RECON, true, BF16>(xt, ct, scale + moff, zero + moff, rt, static_cast<int>(rows), lane, one);
 }
 
 // ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
-template <int BITS, bool RECON>
+template <int BITS, bool RECON, bool BF16>
 static hipError_t launch_keys_t(const FlushArgs& a, hipStream_t stream) {
     const int64_t n_groups = (a.S + kGroup - 1) / kGroup;
     const int64_t n_tiles = a.BH * n_groups;
     const int64_t blocks = (n_tiles + kWavesPerBlock - 1) / kWavesPerBlock;
-    hipLaunchKernelGGL((key_flush_kernel<BITS, RECON>), dim3(static_cast<uint32_t>(blocks)),
+    hipLaunchKernelGGL((key_flush_kernel<BITS, RECON, BF16>), dim3(static_cast<uint32_t>(blocks)),
                        dim3(kBlock), 0, stream, a.x, a.S, a.x_bh_stride, a.codes,
                        a.codes_bh_stride, a.scale, a.zero, a.meta_bh_stride, a.dst_token,
                        a.recon, a.recon_bh_stride, n_groups, n_tiles, 1.0f);
     return hipGetLastError();
 }
 
-template <int BITS, bool RECON>
+template <int BITS, bool RECON, bool BF16>
 static hipError_t launch_values_t(const FlushArgs& a, hipStream_t stream) {
     const int64_t tiles_per_bh = (a.S + 31) / 32;
     const int64_t n_tiles = a.BH * tiles_per_bh;
     const int64_t blocks = (n_tiles + kWavesPerBlock - 1) / kWavesPerBlock;
-    hipLaunchKernelGGL((value_flush_kernel<BITS, RECON>), dim3(static_cast<uint32_t>(blocks)),
+    hipLaunchKernelGGL((value_flush_kernel<BITS, RECON, BF16>), dim3(static_cast<uint32_t>(blocks)),
                        dim3(kBlock), 0, stream, a.x, a.S, a.x_bh_stride, a.codes,
                        a.codes_bh_stride, a.scale, a.zero, a.meta_bh_stride, a.dst_token,
                        a.recon, a.recon_bh_stride, tiles_per_bh, n_tiles, 1.0f);
     return hipGetLastError();
 }
 
-hipError_t launch_key_flush(const FlushArgs& a, hipStream_t stream) {
+template <bool BF16>
+static hipError_t launch_key_flush_fmt(const FlushArgs& a, hipStream_t stream) {
     const bool rec = a.recon != nullptr;
-    if (a.bits == 4) return rec ? launch_keys_t<4, true>(a, stream) : launch_keys_t<4, false>(a, stream);
-    return rec ? launch_keys_t<2, true>(a, stream) : launch_keys_t<2, false>(a, stream);
+    if (a.bits == 4) return rec ? launch_keys_t<4, true, BF16>(a, stream) : launch_keys_t<4, false, BF16>(a, stream);
+    return rec ? launch_keys_t<2, true, BF16>(a, stream) : launch_keys_t<2, false, BF16>(a, stream);
+}
+
+template <bool BF16>
+static hipError_t launch_value_flush_fmt(const FlushArgs& a, hipStream_t stream) {
+    const bool rec = a.recon != nullptr;
+    if (a.bits == 4) return rec ? launch_values_t<4, true, BF16>(a, stream) : launch_values_t<4, false, BF16>(a, stream);
+    return rec ? launch_values_t<2, true, BF16>(a, stream) : launch_values_t<2, false, BF16>(a, stream);
+}
+
+hipError_t launch_key_flush(const FlushArgs& a, hipStream_t stream) {
+    return a.bf16 ? launch_key_flush_fmt<true>(a, stream) : launch_key_flush_fmt<false>(a, stream);
 }
 
 hipError_t launch_value_flush(const FlushArgs& a, hipStream_t stream) {
-    const bool rec = a.recon != nullptr;
-    if (a.bits == 4) return rec ? launch_values_t<4, true>(a, stream) : launch_values_t<4, false>(a, stream);
-    return rec ? launch_values_t<2, true>(a, stream) : launch_values_t<2, false>(a, stream);
+    return a.bf16 ? launch_value_flush_fmt<true>(a, stream) : launch_value_flush_fmt<false>(a, stream);
 }
 
 }  // namespace kivi

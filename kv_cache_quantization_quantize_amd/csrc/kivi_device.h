@@ -32,6 +32,11 @@ __device__ __forceinline__ float f16_to_f32(uint32_t bits16) {
     return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)));
 }
 
+// Exact widening of the low / high bfloat16 of a 32-bit word (bfloat16 is
+// binary32 with the low 16 fraction bits dropped).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
 // fp32 -> fp16, round to nearest even (the default rounding mode).
 __device__ __forceinline__ uint32_t f32_to_f16(float f) {
     return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
@@ -85,6 +90,30 @@ __device__ __forceinline__ half2_t half_min(half2_t v) {
 __device__ __forceinline__ half2_t half_max(half2_t v) {
     const auto p = __builtin_amdgcn_permlane32_swap(as_u32(v), as_u32(v), false, false);
     return hmax(as_h2(p[0]), as_h2(p[1]));
+}
+
+// fp32 forms of the same: IEEE minimum/maximum (v_minimum3_f32 /
+// v_maximum3_f32 for three inputs) and the reduction over the four rows.
+__device__ __forceinline__ float fminimum(float a, float b) { return __builtin_elementwise_minimum(a, b); }
+__device__ __forceinline__ float fmaximum(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float fmin3(float a, float b, float c) { return fminimum(fminimum(a, b), c); }
+__device__ __forceinline__ float fmax3(float a, float b, float c) { return fmaximum(fmaximum(a, b), c); }
+__device__ __forceinline__ float rows_min_f32(float v) {
+    auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fminimum(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fminimum(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float rows_max_f32(float v) {
+    auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaximum(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaximum(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+
+// Word k (0..3) of a 16-byte load: channels 2k and 2k+1 of the lane's 8.
+__device__ __forceinline__ uint32_t word_of(const uint4& v, int k) {
+    return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
 }
 
 // DPP quad permutations (lane ^ 1, lane ^ 2 within each group of 4 lanes).
@@ -151,9 +180,24 @@ __device__ __forceinline__ float quant_fast(float t, float r, float& dev) {
 constexpr float kNearTie = 0.5f - 0x1p-16f;
 
 // The same code with the IEEE quotient (the oracle's exact steps); t = x - zero.
-__device__ __forceinline__ float quant_exact(float t, float s) {
+// The clip to [0, 2^bits - 1] is a no-op (see quant_fast: 0 <= t <= range
+// and s is the rounded range/L); it is kept so these are the oracle's steps
+// for every input, fp16 or bfloat16.
+__device__ __forceinline__ float quant_exact(float t, float s, float levels) {
     if (s == 0.0f) return 0.0f;
-    return __builtin_rintf(t / s);
+    return fminf(fmaxf(__builtin_rintf(t / s), 0.0f), levels);
+}
+
+// t = x - zero for element j (0..7) of a lane's 16-byte row: fp16 through
+// sub_from_f16, bfloat16 widened exactly and subtracted in fp32.
+template <bool BF16>
+__device__ __forceinline__ float sub_elem(const uint4& raw, int j, float one, float zero) {
+    const uint32_t w = word_of(raw, j >> 1);
+    if constexpr (BF16) {
+        return ((j & 1) ? bf16_hi(w) : bf16_lo(w)) - zero;
+    } else {
+        return sub_from_f16(as_h2(w)[j & 1], one, zero);
+    }
 }
 
 // A zero extreme is stored as +0, so the result does not depend on which
@@ -167,5 +211,44 @@ __device__ __forceinline__ uint32_t recon_f16(float q, float scale, float zero) 
     const float sum = prod + zero;
     return f32_to_f16(sum);
 }
+
+// ---------------------------------------------------------------------------
+// bfloat16 storage: binary32 with the low 16 fraction bits dropped.
+// ---------------------------------------------------------------------------
+
+// fp32 -> bfloat16, round to nearest even on the bit pattern: adding
+// 0x7fff plus the lowest kept bit rounds the dropped half up past the
+// midpoint, and at the midpoint only when that would make the kept part
+// even; a carry moves into the exponent (up to infinity), which is the
+// correct rounding too.  Exact for every finite input, subnormals included.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Reconstruction bf16_rne(fl(fl(q * scale) + zero)).
+__device__ __forceinline__ uint32_t recon_bf16(float q, float scale, float zero) {
+    const float prod = q * scale;
+    const float sum = prod + zero;
+    return f32_to_bf16(sum);
+}
+
+template <bool BF16>
+__device__ __forceinline__ uint32_t recon_out(float q, float scale, float zero) {
+    if constexpr (BF16) return recon_bf16(q, scale, zero);
+    else return recon_f16(q, scale, zero);
+}
+
+// The scale for bfloat16 inputs: the plain IEEE quotient.  (The shortcut of
+// scale_of is proven only for the ranges fp16 inputs can produce; bfloat16
+// ranges span the whole binary32 exponent range.)
+template <int BITS>
+__device__ __forceinline__ float scale_div(float range) {
+    return range / static_cast<float>((1 << BITS) - 1);
+}
+
+// The reciprocal fast path of quant_fast needs a normal scale with a normal
+// reciprocal; any other scale (zero included) takes the IEEE quotient.
+__device__ __forceinline__ bool fast_scale(float s) { return s >= 0x1p-126f && s < 0x1p126f; }
 
 }  // namespace kivi

@@ -23,6 +23,7 @@ struct FlushArgs {
     uint16_t* recon;               // may be null
     int64_t recon_bh_stride;
     int bits;
+    bool bf16;                     // x and recon hold bfloat16 (else fp16)
 };
 
 struct DequantArgs {
@@ -36,6 +37,7 @@ struct DequantArgs {
     int64_t out_bh_stride;
     int bits;
     int kind;                      // KIVI_KEYS or KIVI_VALUES
+    bool bf16;                     // out holds bfloat16 (else fp16)
 };
 
 struct AttendArgs {

@@ -24,6 +24,7 @@ GROUP = 32
 # symbols of include/kivi.h, include/kivi_cache.h and include/kivi_calib.h
 EXPORTS = (
     "kivi_quantize_keys", "kivi_quantize_values", "kivi_dequantize",
+    "kivi_quantize_keys_bf16", "kivi_quantize_values_bf16", "kivi_dequantize_bf16",
     "kivi_decode_attend", "kivi_decode_attend_varlen", "kivi_decode_attend_workspace_bytes",
     "kivi_status_string", "kivi_last_hip_error", "kivi_calib_copy",
     "kivi_cache_device_bytes", "kivi_cache_init", "kivi_cache_prefill", "kivi_cache_append",
@@ -89,6 +90,9 @@ def lib() -> ctypes.CDLL:
         L.kivi_quantize_keys.argtypes = [vp, i64, i64, i64, sp, i64, vp, i64, vp]
         L.kivi_quantize_values.argtypes = [vp, i64, i64, i64, sp, i64, vp, i64, vp]
         L.kivi_dequantize.argtypes = [sp, i64, i64, i64, vp, i64, vp]
+        L.kivi_quantize_keys_bf16.argtypes = L.kivi_quantize_keys.argtypes
+        L.kivi_quantize_values_bf16.argtypes = L.kivi_quantize_values.argtypes
+        L.kivi_dequantize_bf16.argtypes = L.kivi_dequantize.argtypes
         L.kivi_decode_attend.argtypes = [vp, i64, i32, i32, sp, sp, i64, vp, vp, i64, i64,
                                          ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
         L.kivi_decode_attend_varlen.argtypes = [vp, i64, i32, i32, sp, sp, vp, i64, vp, vp, i64,
@@ -110,6 +114,7 @@ def lib() -> ctypes.CDLL:
         L.kivi_cache_attend_workspace_bytes.restype = ctypes.c_size_t
         L.kivi_cache_end_step.argtypes = [cp, vp]
         for name in ("kivi_quantize_keys", "kivi_quantize_values", "kivi_dequantize",
+                     "kivi_quantize_keys_bf16", "kivi_quantize_values_bf16", "kivi_dequantize_bf16",
                      "kivi_decode_attend", "kivi_decode_attend_varlen", "kivi_last_hip_error",
                      "kivi_calib_copy", "kivi_cache_init", "kivi_cache_prefill", "kivi_cache_append",
                      "kivi_cache_attend", "kivi_cache_end_step"):
@@ -132,9 +137,9 @@ def _stream(stream=None) -> int:
     return int(s.cuda_stream)
 
 
-def _need_f16(t: torch.Tensor, name: str) -> None:
-    if t.dtype != torch.float16:
-        raise TypeError(f"{name} must be float16, got {t.dtype}")
+def _need_f16(t: torch.Tensor, name: str, allow_bf16: bool = False) -> None:
+    if t.dtype != torch.float16 and not (allow_bf16 and t.dtype == torch.bfloat16):
+        raise TypeError(f"{name} must be float16{' or bfloat16' if allow_bf16 else ''}, got {t.dtype}")
     if not t.is_cuda:
         raise TypeError(f"{name} must be a device tensor")
     if t.dim() != 3 or t.shape[2] != HEAD_DIM or t.stride(2) != 1 or t.stride(1) != HEAD_DIM:
@@ -168,9 +173,13 @@ class Store:
 
 
 def _flush(fn_name, x: torch.Tensor, store: Store, dst_token: int, recon, stream):
-    _need_f16(x, "x")
+    _need_f16(x, "x", allow_bf16=True)
     if recon is not None:
-        _need_f16(recon, "recon")
+        _need_f16(recon, "recon", allow_bf16=True)
+        if recon.dtype != x.dtype:
+            raise TypeError("recon must have the dtype of x")
+    if x.dtype == torch.bfloat16:
+        fn_name += "_bf16"
     st = store.c()
     rc = getattr(lib(), fn_name)(
         x.data_ptr(), x.shape[0], x.shape[1], x.stride(0), ctypes.byref(st), dst_token,
@@ -181,27 +190,31 @@ def _flush(fn_name, x: torch.Tensor, store: Store, dst_token: int, recon, stream
 
 def quantize_keys(x: torch.Tensor, store: Store, dst_token: int = 0,
                   recon: torch.Tensor | None = None, stream=None) -> None:
-    """kivi_quantize_keys: per-channel key flush of x[BH][S][128] into store."""
+    """kivi_quantize_keys: per-channel key flush of x[BH][S][128] into store
+    (kivi_quantize_keys_bf16 when x is bfloat16)."""
     _flush("kivi_quantize_keys", x, store, dst_token, recon, stream)
 
 
 def quantize_values(x: torch.Tensor, store: Store, dst_token: int = 0,
                     recon: torch.Tensor | None = None, stream=None) -> None:
-    """kivi_quantize_values: per-token value flush of x[BH][S][128] into store."""
+    """kivi_quantize_values: per-token value flush of x[BH][S][128] into store
+    (kivi_quantize_values_bf16 when x is bfloat16)."""
     _flush("kivi_quantize_values", x, store, dst_token, recon, stream)
 
 
 def dequantize(store: Store, token_begin: int, n_tokens: int, out: torch.Tensor | None = None,
-               BH: int | None = None, stream=None) -> torch.Tensor:
-    """kivi_dequantize: fp16 [BH][n_tokens][128] reconstruction of a token range."""
+               BH: int | None = None, stream=None, dtype=torch.float16) -> torch.Tensor:
+    """kivi_dequantize: fp16 [BH][n_tokens][128] reconstruction of a token range
+    (kivi_dequantize_bf16 for a bfloat16 ``out`` / ``dtype``)."""
     BH = store.BH if BH is None else BH
     if out is None:
-        out = torch.empty((BH, n_tokens, HEAD_DIM), dtype=torch.float16, device=store.codes.device)
-    _need_f16(out, "out")
+        out = torch.empty((BH, n_tokens, HEAD_DIM), dtype=dtype, device=store.codes.device)
+    _need_f16(out, "out", allow_bf16=True)
+    name = "kivi_dequantize_bf16" if out.dtype == torch.bfloat16 else "kivi_dequantize"
     st = store.c()
-    rc = lib().kivi_dequantize(ctypes.byref(st), BH, token_begin, n_tokens, out.data_ptr(),
-                               out.stride(0), _stream(stream))
-    _check(rc, "kivi_dequantize")
+    rc = getattr(lib(), name)(ctypes.byref(st), BH, token_begin, n_tokens, out.data_ptr(),
+                              out.stride(0), _stream(stream))
+    _check(rc, name)
     return out
 
 

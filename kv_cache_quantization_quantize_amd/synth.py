@@ -46,11 +46,12 @@ def outlier_channels(BH: int, D: int, seed: int, n_outliers: int = 4) -> torch.T
 def kv_tensor(BH: int, S: int, D: int = 128, *, keys: bool, seed: int,
               n_outliers: int = 4, outlier_scale: float = 10.0,
               device="cpu", tensor_id: int | None = None,
-              slab_chunk: int = 8) -> torch.Tensor:
-    """fp16 [BH][S][D].  Drawn slab-chunk by slab-chunk to bound the float32
-    temporary (the long-context cache is 1.2e9 elements per tensor)."""
+              slab_chunk: int = 8, dtype=torch.float16) -> torch.Tensor:
+    """fp16 (or ``dtype``, e.g. bfloat16) [BH][S][D].  Drawn slab-chunk by
+    slab-chunk to bound the float32 temporary (the long-context cache is
+    1.2e9 elements per tensor)."""
     tid = tensor_id if tensor_id is not None else (KEY_TENSOR if keys else VALUE_TENSOR)
-    out = torch.empty((BH, S, D), dtype=torch.float16, device=device)
+    out = torch.empty((BH, S, D), dtype=dtype, device=device)
     g = _gen(device, seed * 1_000_003 + tid)
     outl = outlier_channels(BH, D, seed, n_outliers) if (keys and n_outliers) else None
     for b0 in range(0, BH, slab_chunk):
