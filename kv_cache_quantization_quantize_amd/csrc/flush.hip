@@ -87,7 +87,7 @@ __device__ __forceinline__ void key_tile(const uint16_t* __restrict__ xt, uint32
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         ze[j] = canon_zero(mnf[j]);
-        sc[j] = BF16 ? scale_div<BITS>(mxf[j] - mnf[j]) : scale_of<BITS>(mxf[j] - mnf[j]);
+        sc[j] = BF16 ? scale_wide<BITS>(mxf[j] - mnf[j]) : scale_of<BITS>(mxf[j] - mnf[j]);
         rc[j] = recip_clamped(sc[j]);
         if constexpr (BF16) slow |= !fast_scale(sc[j]);
     }
@@ -217,7 +217,7 @@ __device__ __forceinline__ void value_tile(const uint16_t* __restrict__ xt, uint
             hi = fmaximum(hi, __uint_as_float(quad_xor2(__float_as_uint(hi))));
         }
         const float ze = canon_zero(lo);
-        const float sc = BF16 ? scale_div<BITS>(hi - lo) : scale_of<BITS>(hi - lo);
+        const float sc = BF16 ? scale_wide<BITS>(hi - lo) : scale_of<BITS>(hi - lo);
         const float rc = recip_clamped(sc);
 
         float t[8], qf[8];

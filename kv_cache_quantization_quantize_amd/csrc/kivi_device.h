@@ -239,11 +239,15 @@ __device__ __forceinline__ uint32_t recon_out(float q, float scale, float zero) 
     else return recon_f16(q, scale, zero);
 }
 
-// The scale for bfloat16 inputs: the plain IEEE quotient.  (The shortcut of
-// scale_of is proven only for the ranges fp16 inputs can produce; bfloat16
-// ranges span the whole binary32 exponent range.)
+// The scale for bfloat16 inputs.  scale_of is proven equal to the IEEE
+// quotient for every binary32 range in {0} and [2^-24, 2^18); bfloat16
+// ranges can lie anywhere in the binary32 exponent range, so a wave takes
+// the plain IEEE quotient whenever one of its lanes has a range outside
+// that set (the branch is uniform, and not taken for ordinary caches).
 template <int BITS>
-__device__ __forceinline__ float scale_div(float range) {
+__device__ __forceinline__ float scale_wide(float range) {
+    const bool proven = range == 0.0f || (range >= 0x1p-24f && range < 0x1p18f);
+    if (__builtin_amdgcn_ballot_w64(!proven) == 0) return scale_of<BITS>(range);
     return range / static_cast<float>((1 << BITS) - 1);
 }
 

@@ -79,7 +79,7 @@ struct AttendPlan {
     int64_t n_split;               // waves per (sequence, kv head)
     size_t workspace_bytes;
 };
-AttendPlan plan_attend(int64_t B, int Hq, int Hkv, int64_t n_quant, int64_t n_res);
+AttendPlan plan_attend(int64_t B, int Hq, int Hkv, int64_t n_quant, int64_t n_res, bool varlen);
 
 hipError_t launch_key_flush(const FlushArgs& a, hipStream_t stream);
 hipError_t launch_value_flush(const FlushArgs& a, hipStream_t stream);

@@ -225,10 +225,19 @@ def test_varlen_batch32_long_context_sampled():
 
 
 def test_varlen_equal_lengths_match_uniform_call():
+    """Equal lengths give the uniform call's result.  The variable-length
+    plan splits the token axis more finely; each split rounds its
+    probabilities to fp16 relative to its own running max and sums in fp32,
+    so the two calls differ by that rounding (about 2e-4 here), and both
+    meet the oracle's tolerance."""
     c = _case(4, 32, 8, 3000, 128, 4, seed=14)
     c["nq_seq"] = np.full(4, 3000, np.int32)
     c["nr_seq"] = np.full(4, 128, np.int32)
-    assert np.array_equal(_varlen_gpu(c), _gpu(c))
+    a, u = _varlen_gpu(c), _gpu(c)
+    assert np.max(np.abs(a - u)) <= TOL
+    for b in range(4):
+        ref = _oracle(c, b)
+        assert np.max(np.abs(a[b] - ref)) <= TOL and np.max(np.abs(u[b] - ref)) <= TOL
 
 
 def test_varlen_graph_replays_follow_device_lengths():
