@@ -36,8 +36,13 @@ int finish(hipError_t e) { return kivi::hip_status(e); }
 int64_t words_per_token(int bits) { return kD * bits / 32; }
 
 int64_t meta_rows(const kivi_store* st) {
-    return st->kind == KIVI_KEYS ? (st->cap + kG - 1) / kG * kD : st->cap * (kD / kG);
+    const int64_t G = st->group_size;
+    return st->kind == KIVI_KEYS ? (st->cap + G - 1) / G * kD : st->cap * (kD / G);
 }
+
+// The flush and dequantize take groups of 32, 64 or 128; the attend and the
+// decode-loop cache take 32.
+bool flush_group_ok(int32_t G) { return G == 32 || G == 64 || G == 128; }
 
 // Checks a store and that tokens [t0, t0 + n) of slabs [0, BH) lie inside it.
 int check_store(const kivi_store* st, int kind, int64_t BH, int64_t t0, int64_t n) {
@@ -45,7 +50,7 @@ int check_store(const kivi_store* st, int kind, int64_t BH, int64_t t0, int64_t 
     if (st->kind != KIVI_KEYS && st->kind != KIVI_VALUES) return KIVI_ERR_UNSUPPORTED;
     if (kind >= 0 && st->kind != kind) return KIVI_ERR_SHAPE;
     if (st->bits != 2 && st->bits != 4) return KIVI_ERR_UNSUPPORTED;
-    if (st->group_size != kG || st->head_dim != kD) return KIVI_ERR_UNSUPPORTED;
+    if (!flush_group_ok(st->group_size) || st->head_dim != kD) return KIVI_ERR_UNSUPPORTED;
     if (!st->codes || !st->scale || !st->zero) return KIVI_ERR_NULL;
     if (!aligned16(st->codes) || !aligned16(st->scale) || !aligned16(st->zero)) return KIVI_ERR_ALIGN;
     if (st->codes_bh_stride % 4 != 0 || st->meta_bh_stride % 4 != 0) return KIVI_ERR_ALIGN;
@@ -71,7 +76,7 @@ int flush(bool keys, bool bf16, const uint16_t* x, int64_t BH, int64_t S, int64_
     if (BH < 0 || S < 0) return KIVI_ERR_SHAPE;
     int rc = check_store(dst, keys ? KIVI_KEYS : KIVI_VALUES, BH, dst_token, S);
     if (rc != KIVI_OK) return rc;
-    if (keys && dst_token % kG != 0) return KIVI_ERR_SHAPE;
+    if (keys && dst_token % dst->group_size != 0) return KIVI_ERR_SHAPE;
     if (BH == 0 || S == 0) return KIVI_OK;
     if ((rc = check_f16_tensor(x, BH, S, x_bh_stride)) != KIVI_OK) return rc;
     if (recon && (rc = check_f16_tensor(recon, BH, S, recon_bh_stride)) != KIVI_OK) return rc;
@@ -84,6 +89,7 @@ int flush(bool keys, bool bf16, const uint16_t* x, int64_t BH, int64_t S, int64_
     a.scale = dst->scale; a.zero = dst->zero; a.meta_bh_stride = dst->meta_bh_stride;
     a.dst_token = dst_token; a.recon = recon; a.recon_bh_stride = recon_bh_stride;
     a.bits = dst->bits;
+    a.group = dst->group_size;
     a.bf16 = bf16;
     return finish(keys ? kivi::launch_key_flush(a, stream) : kivi::launch_value_flush(a, stream));
 }
@@ -129,7 +135,7 @@ static int dequantize(bool bf16, const kivi_store* src, int64_t BH, int64_t toke
     a.codes = src->codes; a.codes_bh_stride = src->codes_bh_stride;
     a.scale = src->scale; a.zero = src->zero; a.meta_bh_stride = src->meta_bh_stride;
     a.BH = BH; a.t0 = token_begin; a.n = n_tokens; a.out = out; a.out_bh_stride = out_bh_stride;
-    a.bits = src->bits; a.kind = src->kind; a.bf16 = bf16;
+    a.bits = src->bits; a.kind = src->kind; a.group = src->group_size; a.bf16 = bf16;
     return finish(kivi::launch_dequantize(a, stream));
 }
 
@@ -180,6 +186,7 @@ int decode_attend_entry(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
     if (rc != KIVI_OK) return rc;
     if ((rc = check_store(v, KIVI_VALUES, slabs, 0, n_quant)) != KIVI_OK) return rc;
     if (k->bits != v->bits) return KIVI_ERR_SHAPE;
+    if (k->group_size != kG || v->group_size != kG) return KIVI_ERR_UNSUPPORTED;
     if (B == 0) return KIVI_OK;
     if (!q || !out) return KIVI_ERR_NULL;
     if (!aligned16(q) || !aligned16(out)) return KIVI_ERR_ALIGN;

@@ -17,21 +17,21 @@ namespace kivi {
 // Rows [0, n_rows) of one tile; row k is store token t_first + k, written to
 // ot + k*128.  ONE_GROUP (keys only): the 32 rows are exactly one key group,
 // so its scale and zero are loaded once for the tile.
-template <int BITS, bool KEYS, bool ONE_GROUP, bool BF16>
+template <int BITS, bool KEYS, bool ONE_GROUP, bool BF16, int G>
 __device__ __forceinline__ void dequant_tile(const uint32_t* __restrict__ cb, const float* __restrict__ scb,
                                              const float* __restrict__ zeb, int64_t t_first, int n_rows,
                                              uint16_t* __restrict__ ot, int lane)
 {
     constexpr int kWords = kHeadDim * BITS / 32;
     constexpr uint32_t kMask = (1u << BITS) - 1u;
-    constexpr int kMetaPerTok = kHeadDim / kGroup;
+    constexpr int kMetaPerTok = kHeadDim / G;
     const int c = lane & 15;
     const int r = lane >> 4;
     const uint32_t* ct = cb + t_first * kWords;
     float gs[8], gz[8];
     if constexpr (ONE_GROUP) {
-        const float* sp = scb + (t_first / kGroup) * kHeadDim + c * 8;
-        const float* zp = zeb + (t_first / kGroup) * kHeadDim + c * 8;
+        const float* sp = scb + (t_first / G) * kHeadDim + c * 8;
+        const float* zp = zeb + (t_first / G) * kHeadDim + c * 8;
         const float4 s0 = *reinterpret_cast<const float4*>(sp);
         const float4 s1 = *reinterpret_cast<const float4*>(sp + 4);
         const float4 z0 = *reinterpret_cast<const float4*>(zp);
@@ -54,8 +54,8 @@ __device__ __forceinline__ void dequant_tile(const uint32_t* __restrict__ cb, co
             for (int j = 0; j < 8; ++j) { sc[j] = gs[j]; ze[j] = gz[j]; }
         } else if constexpr (KEYS) {
             const int64_t t = t_first + k;
-            const float* sp = scb + (t / kGroup) * kHeadDim + c * 8;
-            const float* zp = zeb + (t / kGroup) * kHeadDim + c * 8;
+            const float* sp = scb + (t / G) * kHeadDim + c * 8;
+            const float* zp = zeb + (t / G) * kHeadDim + c * 8;
             const float4 s0 = *reinterpret_cast<const float4*>(sp);
             const float4 s1 = *reinterpret_cast<const float4*>(sp + 4);
             const float4 z0 = *reinterpret_cast<const float4*>(zp);
@@ -66,8 +66,8 @@ __device__ __forceinline__ void dequant_tile(const uint32_t* __restrict__ cb, co
             ze[4] = z1.x; ze[5] = z1.y; ze[6] = z1.z; ze[7] = z1.w;
         } else {
             const int64_t t = t_first + k;
-            const float s = scb[t * kMetaPerTok + (c >> 2)];
-            const float z = zeb[t * kMetaPerTok + (c >> 2)];
+            const float s = scb[t * kMetaPerTok + c / (G / 8)];
+            const float z = zeb[t * kMetaPerTok + c / (G / 8)];
 #pragma unroll
             for (int j = 0; j < 8; ++j) { sc[j] = s; ze[j] = z; }
         }
@@ -78,7 +78,7 @@ __device__ __forceinline__ void dequant_tile(const uint32_t* __restrict__ cb, co
     }
 }
 
-template <int BITS, bool KEYS, bool BF16>
+template <int BITS, bool KEYS, bool BF16, int G>
 __global__ __launch_bounds__(kBlock) void dequant_kernel(
     const uint32_t* __restrict__ codes, int64_t codes_bh_stride,
     const float* __restrict__ scale, const float* __restrict__ zero, int64_t meta_bh_stride,
@@ -96,28 +96,38 @@ __global__ __launch_bounds__(kBlock) void dequant_kernel(
     const float* scb = scale + bh * meta_bh_stride;
     const float* zeb = zero + bh * meta_bh_stride;
     uint16_t* ot = out + bh * out_bh_stride + i0 * kHeadDim;
-    if (KEYS && rows >= 32 && (t0 + i0) % kGroup == 0)
-        dequant_tile<BITS, KEYS, true, BF16>(cb, scb, zeb, t0 + i0, 32, ot, lane);
+    // a full tile inside one key group loads the group's scale and zero once
+    if (KEYS && rows >= 32 && (t0 + i0) % G + 32 <= G)
+        dequant_tile<BITS, KEYS, true, BF16, G>(cb, scb, zeb, t0 + i0, 32, ot, lane);
     else
-        dequant_tile<BITS, KEYS, false, BF16>(cb, scb, zeb, t0 + i0, rows < 32 ? static_cast<int>(rows) : 32, ot, lane);
+        dequant_tile<BITS, KEYS, false, BF16, G>(cb, scb, zeb, t0 + i0, rows < 32 ? static_cast<int>(rows) : 32, ot, lane);
 }
 
-template <int BITS, bool KEYS, bool BF16>
+template <int BITS, bool KEYS, bool BF16, int G>
 static hipError_t launch_t(const DequantArgs& a, hipStream_t stream) {
     const int64_t tiles_per_bh = (a.n + 31) / 32;
     const int64_t n_tiles = a.BH * tiles_per_bh;
     const int64_t blocks = (n_tiles + kWavesPerBlock - 1) / kWavesPerBlock;
-    hipLaunchKernelGGL((dequant_kernel<BITS, KEYS, BF16>), dim3(static_cast<uint32_t>(blocks)),
+    hipLaunchKernelGGL((dequant_kernel<BITS, KEYS, BF16, G>), dim3(static_cast<uint32_t>(blocks)),
                        dim3(kBlock), 0, stream, a.codes, a.codes_bh_stride, a.scale, a.zero,
                        a.meta_bh_stride, a.t0, a.n, a.out, a.out_bh_stride, tiles_per_bh, n_tiles);
     return hipGetLastError();
 }
 
+template <bool BF16, int G>
+static hipError_t launch_g(const DequantArgs& a, hipStream_t stream) {
+    const bool keys = a.kind == 0;
+    if (a.bits == 4) return keys ? launch_t<4, true, BF16, G>(a, stream) : launch_t<4, false, BF16, G>(a, stream);
+    return keys ? launch_t<2, true, BF16, G>(a, stream) : launch_t<2, false, BF16, G>(a, stream);
+}
+
 template <bool BF16>
 static hipError_t launch_fmt(const DequantArgs& a, hipStream_t stream) {
-    const bool keys = a.kind == 0;
-    if (a.bits == 4) return keys ? launch_t<4, true, BF16>(a, stream) : launch_t<4, false, BF16>(a, stream);
-    return keys ? launch_t<2, true, BF16>(a, stream) : launch_t<2, false, BF16>(a, stream);
+    switch (a.group) {
+        case 64: return launch_g<BF16, 64>(a, stream);
+        case 128: return launch_g<BF16, 128>(a, stream);
+        default: return launch_g<BF16, 32>(a, stream);
+    }
 }
 
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t stream) {

@@ -8,12 +8,14 @@
 //                "The layout problem that shapes everything", "Kernel A",
 //                "Kernel B", "Three ways to be off by one bit".
 //
-// Both kernels give one wave one tile of 32 tokens x 128 channels with the
-// lane mapping of kivi_device.h.  For keys the tile is exactly one token
-// group of every channel, so a lane's 8 tokens x 8 channels cover a quarter
-// of each of its 8 channel groups; the four quarters meet with two cross-row
-// exchanges and no LDS.  For values each token row's 128 channels are four
-// groups of 32, i.e. four lanes of 8; two quad exchanges finish them.  The
+// Both kernels give one wave one tile of tokens x 128 channels with the lane
+// mapping of kivi_device.h.  For keys the tile is exactly one token group of
+// every channel (G = 32, 64 or 128 tokens), so a lane's G/4 tokens x 8
+// channels cover a quarter of each of its 8 channel groups; the four
+// quarters meet with two cross-row exchanges and no LDS.  For values the
+// tile is 32 tokens and each token row's 128 channels are groups of G
+// channels, i.e. G/8 lanes of 8; two quad exchanges finish a group of 32,
+// a half-row mirror one of 64 and a row mirror one of 128.  The
 // Metal kernels used a thread per strided key group and a 32-lane SIMD-group
 // per value group; on wave64 both layouts read the same coalesced tile.
 #include "kivi_device.h"
@@ -27,7 +29,7 @@ namespace kivi {
 // One tile.  xt, ct, rt point at token s0 of the slab (input, codes, recon);
 // n_rows = min(32, S - s0) real rows.  RAGGED tiles clamp loads to the last
 // real row and guard stores; full tiles do neither.
-template <int BITS, bool RECON, bool RAGGED, bool BF16>
+template <int BITS, bool RECON, bool RAGGED, bool BF16, int G>
 __device__ __forceinline__ void key_tile(const uint16_t* __restrict__ xt, uint32_t* __restrict__ ct,
                                          float* __restrict__ sct, float* __restrict__ zet,
                                          uint16_t* __restrict__ rt, int n_rows, int lane, float one)
@@ -39,26 +41,35 @@ __device__ __forceinline__ void key_tile(const uint16_t* __restrict__ xt, uint32
     // Load 8 token rows x 8 channels.  Rows past the end of a ragged last
     // group re-read the last real token, which is the edge padding of
     // "Three ways to be off by one bit", item 3, and cannot move min or max.
-    uint4 raw[kTokPerLane];
+    constexpr int kRows = G / kRowsPerWave;        // token rows per lane: the tile is one group
+    uint4 raw[kRows];
 #pragma unroll
-    for (int i = 0; i < kTokPerLane; ++i) {
+    for (int i = 0; i < kRows; ++i) {
         int row = r + kRowsPerWave * i;
         if constexpr (RAGGED) row = row < n_rows ? row : n_rows - 1;
         raw[i] = *reinterpret_cast<const uint4*>(xt + row * kHeadDim + c * 8);
     }
 
-    // Per-channel min/max over the lane's 8 rows and then across the 4 row
+    // Per-channel min/max over the lane's rows and then across the 4 row
     // lanes: fp16 in packed fp16 (exact: the conversion to fp32 is
     // monotone), bfloat16 widened exactly to fp32 (no packed bfloat16 form).
     float mnf[8], mxf[8];
     if constexpr (!BF16) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            half2_t v[kTokPerLane];
+            half2_t mn = as_h2(word_of(raw[0], k)), mx = mn;
 #pragma unroll
-            for (int i = 0; i < kTokPerLane; ++i) v[i] = as_h2(word_of(raw[i], k));
-            half2_t mn = hmin3(hmin3(v[0], v[1], v[2]), hmin3(v[3], v[4], v[5]), hmin(v[6], v[7]));
-            half2_t mx = hmax3(hmax3(v[0], v[1], v[2]), hmax3(v[3], v[4], v[5]), hmax(v[6], v[7]));
+            for (int i = 1; i < kRows; i += 2) {
+                const half2_t a = as_h2(word_of(raw[i], k));
+                if (i + 1 < kRows) {
+                    const half2_t b = as_h2(word_of(raw[i + 1], k));
+                    mn = hmin3(mn, a, b);
+                    mx = hmax3(mx, a, b);
+                } else {
+                    mn = hmin(mn, a);
+                    mx = hmax(mx, a);
+                }
+            }
             mn = half_min(row_pair_min(mn));
             mx = half_max(row_pair_max(mx));
             mnf[2 * k] = static_cast<float>(mn[0]); mnf[2 * k + 1] = static_cast<float>(mn[1]);
@@ -67,14 +78,23 @@ __device__ __forceinline__ void key_tile(const uint16_t* __restrict__ xt, uint32
     } else {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            float v[kTokPerLane];
-#pragma unroll
-            for (int i = 0; i < kTokPerLane; ++i) {
+            const auto val = [&](int i) {
                 const uint32_t w = word_of(raw[i], j >> 1);
-                v[i] = (j & 1) ? bf16_hi(w) : bf16_lo(w);
+                return (j & 1) ? bf16_hi(w) : bf16_lo(w);
+            };
+            float mn = val(0), mx = mn;
+#pragma unroll
+            for (int i = 1; i < kRows; i += 2) {
+                const float a = val(i);
+                if (i + 1 < kRows) {
+                    const float b = val(i + 1);
+                    mn = fmin3(mn, a, b);
+                    mx = fmax3(mx, a, b);
+                } else {
+                    mn = fminimum(mn, a);
+                    mx = fmaximum(mx, a);
+                }
             }
-            const float mn = fmin3(fmin3(v[0], v[1], v[2]), fmin3(v[3], v[4], v[5]), fminimum(v[6], v[7]));
-            const float mx = fmax3(fmax3(v[0], v[1], v[2]), fmax3(v[3], v[4], v[5]), fmaximum(v[6], v[7]));
             mnf[j] = rows_min_f32(mn);
             mxf[j] = rows_max_f32(mx);
         }
@@ -101,7 +121,7 @@ __device__ __forceinline__ void key_tile(const uint16_t* __restrict__ xt, uint32
     }
 
 #pragma unroll
-    for (int i = 0; i < kTokPerLane; ++i) {
+    for (int i = 0; i < kRows; ++i) {
         const int row = r + kRowsPerWave * i;
         float t[8], qf[8];
         float dev = 0.0f;
@@ -135,7 +155,7 @@ __device__ __forceinline__ void key_tile(const uint16_t* __restrict__ xt, uint32
     }
 }
 
-template <int BITS, bool RECON, bool BF16>
+template <int BITS, bool RECON, bool BF16, int G>
 __global__ __launch_bounds__(kBlock) void key_flush_kernel(
     const uint16_t* __restrict__ x, int64_t S, int64_t x_bh_stride,
     uint32_t* __restrict__ codes, int64_t codes_bh_stride,
@@ -149,31 +169,32 @@ __global__ __launch_bounds__(kBlock) void key_flush_kernel(
     if (tile >= n_tiles) return;                   // uniform across the wave
     const int64_t bh = tile / n_groups;
     const int64_t g = tile - bh * n_groups;
-    const int64_t s0 = g * kGroup;
+    const int64_t s0 = g * G;
     const uint16_t* xt = x + bh * x_bh_stride + s0 * kHeadDim;
     uint32_t* ct = codes + bh * codes_bh_stride + (dst_token + s0) * kWords;
-    const int64_t moff = bh * meta_bh_stride + (dst_token / kGroup + g) * kHeadDim;
+    const int64_t moff = bh * meta_bh_stride + (dst_token / G + g) * kHeadDim;
     uint16_t* rt = RECON ? recon + bh * recon_bh_stride + s0 * kHeadDim : nullptr;
     const int64_t rows = S - s0;
-    if (rows >= kGroup)
-        key_tile<BITS, RECON, false, BF16>(xt, ct, scale + moff, zero + moff, rt, kGroup, lane, one);
+    if (rows >= G)
+        key_tile<BITS, RECON, false, BF16, G>(xt, ct, scale + moff, zero + moff, rt, G, lane, one);
     else
-        key_tile<BITS, RECON, true, BF16>(xt, ct, scale + moff, zero + moff, rt, static_cast<int>(rows), lane, one);
+        key_tile<BITS, RECON, true, BF16, G>(xt, ct, scale + moff, zero + moff, rt, static_cast<int>(rows), lane, one);
 }
 
 // ---------------------------------------------------------------------------
 // Values: group = (bh, token s, channel group j) over channels [32j, 32j+32)
 // ---------------------------------------------------------------------------
-template <int BITS, bool RECON, bool RAGGED, bool BF16>
+template <int BITS, bool RECON, bool RAGGED, bool BF16, int G>
 __device__ __forceinline__ void value_tile(const uint16_t* __restrict__ xt, uint32_t* __restrict__ ct,
                                            float* __restrict__ sct, float* __restrict__ zet,
                                            uint16_t* __restrict__ rt, int n_rows, int lane, float one)
 {
     constexpr int kWords = kHeadDim * BITS / 32;
-    constexpr int kMetaPerTok = kHeadDim / kGroup;  // 4 groups per token
+    constexpr int kMetaPerTok = kHeadDim / G;       // channel groups per token
+    constexpr int kLanesPerGroup = G / 8;           // 4, 8 or 16 lanes of 8 channels
     const int c = lane & 15;
     const int r = lane >> 4;
-    const int j = c >> 2;                           // channel group of this lane
+    const int j = c / kLanesPerGroup;               // channel group of this lane
 
     uint4 raw[kTokPerLane];
 #pragma unroll
@@ -198,6 +219,8 @@ __device__ __forceinline__ void value_tile(const uint16_t* __restrict__ xt, uint
             mm[1] = -__builtin_elementwise_maximum(mx2[0], mx2[1]);
             mm = hmin(mm, as_h2(quad_xor1(as_u32(mm))));
             mm = hmin(mm, as_h2(quad_xor2(as_u32(mm))));
+            if constexpr (G >= 64) mm = hmin(mm, as_h2(half_row_mirror(as_u32(mm))));
+            if constexpr (G >= 128) mm = hmin(mm, as_h2(row_mirror(as_u32(mm))));
             lo = static_cast<float>(mm[0]);
             hi = -static_cast<float>(mm[1]);
         } else {
@@ -215,6 +238,14 @@ __device__ __forceinline__ void value_tile(const uint16_t* __restrict__ xt, uint
             hi = fmaximum(hi, __uint_as_float(quad_xor1(__float_as_uint(hi))));
             lo = fminimum(lo, __uint_as_float(quad_xor2(__float_as_uint(lo))));
             hi = fmaximum(hi, __uint_as_float(quad_xor2(__float_as_uint(hi))));
+            if constexpr (G >= 64) {
+                lo = fminimum(lo, __uint_as_float(half_row_mirror(__float_as_uint(lo))));
+                hi = fmaximum(hi, __uint_as_float(half_row_mirror(__float_as_uint(hi))));
+            }
+            if constexpr (G >= 128) {
+                lo = fminimum(lo, __uint_as_float(row_mirror(__float_as_uint(lo))));
+                hi = fmaximum(hi, __uint_as_float(row_mirror(__float_as_uint(hi))));
+            }
         }
         const float ze = canon_zero(lo);
         const float sc = BF16 ? scale_wide<BITS>(hi - lo) : scale_of<BITS>(hi - lo);
@@ -242,8 +273,8 @@ __device__ __forceinline__ void value_tile(const uint16_t* __restrict__ xt, uint
             if (live && (c & 1) == 0) ct[row * kWords + (c >> 1)] = packed | (hw << 16);
         }
         if (live) {
-            if ((c & 3) == 0) sct[row * kMetaPerTok + j] = sc;
-            else if ((c & 3) == 1) zet[row * kMetaPerTok + j] = ze;
+            if (c % kLanesPerGroup == 0) sct[row * kMetaPerTok + j] = sc;
+            else if (c % kLanesPerGroup == 1) zet[row * kMetaPerTok + j] = ze;
         }
         if constexpr (RECON) {
             uint32_t h[8];
@@ -254,7 +285,7 @@ __device__ __forceinline__ void value_tile(const uint16_t* __restrict__ xt, uint
     }
 }
 
-template <int BITS, bool RECON, bool BF16>
+template <int BITS, bool RECON, bool BF16, int G>
 __global__ __launch_bounds__(kBlock) void value_flush_kernel(
     const uint16_t* __restrict__ x, int64_t S, int64_t x_bh_stride,
     uint32_t* __restrict__ codes, int64_t codes_bh_stride,
@@ -263,7 +294,7 @@ __global__ __launch_bounds__(kBlock) void value_flush_kernel(
     int64_t tiles_per_bh, int64_t n_tiles, float one)
 {
     constexpr int kWords = kHeadDim * BITS / 32;
-    constexpr int kMetaPerTok = kHeadDim / kGroup;
+    constexpr int kMetaPerTok = kHeadDim / G;
     const int lane = threadIdx.x & 63;
     const int64_t tile = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
     if (tile >= n_tiles) return;                    // uniform across the wave
@@ -275,58 +306,66 @@ __global__ __launch_bounds__(kBlock) void value_flush_kernel(
     uint16_t* rt = RECON ? recon + bh * recon_bh_stride + s0 * kHeadDim : nullptr;
     const int64_t rows = S - s0;
     if (rows >= 32)
-        value_tile<BITS, RECON, false, BF16>(xt, ct, scale + moff, zero + moff, rt, 32, lane, one);
+        value_tile<BITS, RECON, false, BF16, G>(xt, ct, scale + moff, zero + moff, rt, 32, lane, one);
     else
-        value_tile<BITS, RECON, true, BF16>(xt, ct, scale + moff, zero + moff, rt, static_cast<int>(rows), lane, one);
+        value_tile<BITS, RECON, true, BF16, G>(xt, ct, scale + moff, zero + moff, rt, static_cast<int>(rows), lane, one);
 }
 
 // ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
-template <int BITS, bool RECON, bool BF16>
+template <int BITS, bool RECON, bool BF16, int G>
 static hipError_t launch_keys_t(const FlushArgs& a, hipStream_t stream) {
-    const int64_t n_groups = (a.S + kGroup - 1) / kGroup;
+    const int64_t n_groups = (a.S + G - 1) / G;
     const int64_t n_tiles = a.BH * n_groups;
     const int64_t blocks = (n_tiles + kWavesPerBlock - 1) / kWavesPerBlock;
-    hipLaunchKernelGGL((key_flush_kernel<BITS, RECON, BF16>), dim3(static_cast<uint32_t>(blocks)),
+    hipLaunchKernelGGL((key_flush_kernel<BITS, RECON, BF16, G>), dim3(static_cast<uint32_t>(blocks)),
                        dim3(kBlock), 0, stream, a.x, a.S, a.x_bh_stride, a.codes,
                        a.codes_bh_stride, a.scale, a.zero, a.meta_bh_stride, a.dst_token,
                        a.recon, a.recon_bh_stride, n_groups, n_tiles, 1.0f);
     return hipGetLastError();
 }
 
-template <int BITS, bool RECON, bool BF16>
+template <int BITS, bool RECON, bool BF16, int G>
 static hipError_t launch_values_t(const FlushArgs& a, hipStream_t stream) {
     const int64_t tiles_per_bh = (a.S + 31) / 32;
     const int64_t n_tiles = a.BH * tiles_per_bh;
     const int64_t blocks = (n_tiles + kWavesPerBlock - 1) / kWavesPerBlock;
-    hipLaunchKernelGGL((value_flush_kernel<BITS, RECON, BF16>), dim3(static_cast<uint32_t>(blocks)),
+    hipLaunchKernelGGL((value_flush_kernel<BITS, RECON, BF16, G>), dim3(static_cast<uint32_t>(blocks)),
                        dim3(kBlock), 0, stream, a.x, a.S, a.x_bh_stride, a.codes,
                        a.codes_bh_stride, a.scale, a.zero, a.meta_bh_stride, a.dst_token,
                        a.recon, a.recon_bh_stride, tiles_per_bh, n_tiles, 1.0f);
     return hipGetLastError();
 }
 
-template <bool BF16>
-static hipError_t launch_key_flush_fmt(const FlushArgs& a, hipStream_t stream) {
+// One instantiation per (bits, reconstruction, input format, group size).
+template <bool KEYS, bool BF16, int G>
+static hipError_t launch_flush_g(const FlushArgs& a, hipStream_t stream) {
     const bool rec = a.recon != nullptr;
-    if (a.bits == 4) return rec ? launch_keys_t<4, true, BF16>(a, stream) : launch_keys_t<4, false, BF16>(a, stream);
-    return rec ? launch_keys_t<2, true, BF16>(a, stream) : launch_keys_t<2, false, BF16>(a, stream);
+    if constexpr (KEYS) {
+        if (a.bits == 4) return rec ? launch_keys_t<4, true, BF16, G>(a, stream) : launch_keys_t<4, false, BF16, G>(a, stream);
+        return rec ? launch_keys_t<2, true, BF16, G>(a, stream) : launch_keys_t<2, false, BF16, G>(a, stream);
+    } else {
+        if (a.bits == 4) return rec ? launch_values_t<4, true, BF16, G>(a, stream) : launch_values_t<4, false, BF16, G>(a, stream);
+        return rec ? launch_values_t<2, true, BF16, G>(a, stream) : launch_values_t<2, false, BF16, G>(a, stream);
+    }
 }
 
-template <bool BF16>
-static hipError_t launch_value_flush_fmt(const FlushArgs& a, hipStream_t stream) {
-    const bool rec = a.recon != nullptr;
-    if (a.bits == 4) return rec ? launch_values_t<4, true, BF16>(a, stream) : launch_values_t<4, false, BF16>(a, stream);
-    return rec ? launch_values_t<2, true, BF16>(a, stream) : launch_values_t<2, false, BF16>(a, stream);
+template <bool KEYS, bool BF16>
+static hipError_t launch_flush_fmt(const FlushArgs& a, hipStream_t stream) {
+    switch (a.group) {
+        case 64: return launch_flush_g<KEYS, BF16, 64>(a, stream);
+        case 128: return launch_flush_g<KEYS, BF16, 128>(a, stream);
+        default: return launch_flush_g<KEYS, BF16, 32>(a, stream);
+    }
 }
 
 hipError_t launch_key_flush(const FlushArgs& a, hipStream_t stream) {
-    return a.bf16 ? launch_key_flush_fmt<true>(a, stream) : launch_key_flush_fmt<false>(a, stream);
+    return a.bf16 ? launch_flush_fmt<true, true>(a, stream) : launch_flush_fmt<true, false>(a, stream);
 }
 
 hipError_t launch_value_flush(const FlushArgs& a, hipStream_t stream) {
-    return a.bf16 ? launch_value_flush_fmt<true>(a, stream) : launch_value_flush_fmt<false>(a, stream);
+    return a.bf16 ? launch_flush_fmt<false, true>(a, stream) : launch_flush_fmt<false, false>(a, stream);
 }
 
 }  // namespace kivi

@@ -1,9 +1,10 @@
 // kivi_device.h -- device-side helpers shared by the libkivi kernels
 // (internal to the library; not part of the C ABI).
 //
-// Fixed geometry of every kernel here: head_dim 128, group_size 32, wave64.
-// A "tile" is 32 consecutive tokens x 128 channels of one bh slab (8 KiB of
-// fp16).  Lane l of the wave that owns a tile holds channels 8*(l%16) ..
+// Fixed geometry of every kernel here: head_dim 128, wave64; group_size 32
+// (the flush and dequantize also take 64 and 128).  A "tile" is 32
+// consecutive tokens x 128 channels of one bh slab (8 KiB of fp16; a key
+// flush tile is one whole group of G tokens).  Lane l of the wave that owns a tile holds channels 8*(l%16) ..
 // 8*(l%16)+7 of tokens tile_start + (l/16) + 4*i, i = 0..7: each token row
 // of the tile is read by 16 lanes as one contiguous 256-byte segment, so the
 // wave reads the tile as 8 fully coalesced 1 KiB loads.
@@ -122,6 +123,16 @@ __device__ __forceinline__ uint32_t quad_xor1(uint32_t v) {
 }
 __device__ __forceinline__ uint32_t quad_xor2(uint32_t v) {
     return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x4E, 0xF, 0xF, false));
+}
+// DPP mirrors within each half-row of 8 lanes (lane i <- 7 - i) and within
+// each row of 16 (lane i <- 15 - i): after the quad exchanges every lane of a
+// quad holds the quad's value, so one mirror joins two quads (8 lanes) and a
+// second joins two half-rows (16 lanes).
+__device__ __forceinline__ uint32_t half_row_mirror(uint32_t v) {
+    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x141, 0xF, 0xF, false));
+}
+__device__ __forceinline__ uint32_t row_mirror(uint32_t v) {
+    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x140, 0xF, 0xF, false));
 }
 
 // scale = RN(range / (2^bits - 1)) in three operations: a product with the

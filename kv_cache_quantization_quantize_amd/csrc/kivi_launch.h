@@ -23,6 +23,7 @@ struct FlushArgs {
     uint16_t* recon;               // may be null
     int64_t recon_bh_stride;
     int bits;
+    int group;                     // 32, 64 or 128
     bool bf16;                     // x and recon hold bfloat16 (else fp16)
 };
 
@@ -37,6 +38,7 @@ struct DequantArgs {
     int64_t out_bh_stride;
     int bits;
     int kind;                      // KIVI_KEYS or KIVI_VALUES
+    int group;                     // 32, 64 or 128
     bool bf16;                     // out holds bfloat16 (else fp16)
 };
 

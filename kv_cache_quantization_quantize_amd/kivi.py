@@ -153,11 +153,11 @@ class Store:
 
     def __init__(self, kind: int, BH: int, cap: int, bits: int = 4, device="cuda",
                  codes: torch.Tensor | None = None, scale: torch.Tensor | None = None,
-                 zero: torch.Tensor | None = None):
-        self.kind, self.BH, self.cap, self.bits = kind, BH, cap, bits
+                 zero: torch.Tensor | None = None, group: int = GROUP):
+        self.kind, self.BH, self.cap, self.bits, self.group = kind, BH, cap, bits, group
         self.words = HEAD_DIM * bits // 32
-        meta = (BH, (cap + GROUP - 1) // GROUP, HEAD_DIM) if kind == KIVI_KEYS else \
-            (BH, cap, HEAD_DIM // GROUP)
+        meta = (BH, (cap + group - 1) // group, HEAD_DIM) if kind == KIVI_KEYS else \
+            (BH, cap, HEAD_DIM // group)
         self.codes = codes if codes is not None else torch.zeros((BH, cap, self.words),
                                                                  dtype=torch.int32, device=device)
         self.scale = scale if scale is not None else torch.zeros(meta, dtype=torch.float32, device=device)
@@ -166,7 +166,7 @@ class Store:
     def c(self) -> CStore:
         return CStore(self.codes.data_ptr(), self.scale.data_ptr(), self.zero.data_ptr(),
                       self.codes.stride(0), self.scale.stride(0), self.cap, self.bits,
-                      GROUP, HEAD_DIM, self.kind)
+                      self.group, HEAD_DIM, self.kind)
 
     def nbytes(self) -> int:
         return (self.codes.numel() * 4 + self.scale.numel() * 4 + self.zero.numel() * 4)

@@ -60,7 +60,8 @@ def _keys(st, x=FAKE, BH=2, S=32, x_stride=32 * 128, off=0, recon=None, rstride=
 
 
 @pytest.mark.parametrize("case,want", [
-    ("null_store", -1), ("bits3", -3), ("bits8", -3), ("group64", -3), ("dim64", -3),
+    ("null_store", -1), ("bits3", -3), ("bits8", -3), ("group48", -3), ("group256", -3),
+    ("dim64", -3), ("group64_offset32", -2), ("group64", 0),
     ("kind_values", -2), ("offset_not_group", -2), ("window_past_cap", -2),
     ("misaligned_x", -4), ("odd_stride", -4), ("null_x", -1), ("neg_S", -2),
     ("slab_overlap", -2), ("misaligned_codes", -4),
@@ -74,8 +75,16 @@ def test_key_flush_validation(case, want):
         st = _store(bits=3)
     elif case == "bits8":
         st = _store(bits=8)
+    elif case == "group48":
+        st = _store(G=48)
+    elif case == "group256":
+        st = _store(G=256)
+    elif case == "group64_offset32":
+        st = _store(G=64, cap=128)
+        kw = dict(off=32)                          # key groups of 64 start at multiples of 64
     elif case == "group64":
         st = _store(G=64)
+        kw = dict(S=0)                             # valid: a zero-sized call launches nothing
     elif case == "dim64":
         st = _store(D=64)
     elif case == "kind_values":
@@ -148,6 +157,8 @@ def test_attend_validation():
     assert call(wsb=ws - 4) == -5
     assert call(wsp=None) == -5
     assert call(wsp=FAKE + 16) == -4
+    # the attend reads groups of 32 only (the flush and dequantize take 64 and 128 too)
+    assert call(kk=_store(kivi.KIVI_KEYS, cap=64, G=64), vv=_store(kivi.KIVI_VALUES, cap=64, G=64)) == -3
 
 
 # ---------------------------------------------------------------- cache

@@ -1,0 +1,56 @@
+"""Pins for the oracle's flushes with groups of 64 and 128 (the pages' cache
+takes `group_size` as a parameter; the benchmark workloads use 32).
+
+Each tensor-level group reduces to the group function on exactly its
+elements: keys over G consecutive tokens of one channel (a ragged last group
+over its real tokens), values over G consecutive channels of one token.  The
+group function itself is pinned in test_oracle_groups.py."""
+import numpy as np
+import pytest
+
+D = 128
+
+
+def _f16(a):
+    return np.asarray(a, np.float32).astype(np.float16).view(np.uint16)
+
+
+@pytest.mark.parametrize("G", [64, 128])
+@pytest.mark.parametrize("bits", [2, 4])
+def test_wide_groups_reduce_to_the_group_function(orc, G, bits):
+    rng = np.random.default_rng(G + bits)
+    BH, S = 2, 2 * G + 37                          # two whole key groups and a ragged one
+    x = _f16(rng.standard_normal((BH, S, D)) * np.where(rng.random(D) < 0.05, 10, 1))
+    cap = 3 * G
+    ks = orc.Store(orc.KEYS, BH, cap, D, bits, G)
+    vs = orc.Store(orc.VALUES, BH, cap, D, bits, G)
+    rk = orc.quantize_keys(x, ks, 0)
+    rv = orc.quantize_values(x, vs, 0)
+    assert ks.scale.shape == (BH, 3, D) and vs.scale.shape == (BH, cap, D // G)
+    for bh in range(BH):
+        for g in range(3):
+            s0, s1 = G * g, min(G * g + G, S)
+            for d in (0, 63, 127):
+                sc, ze, q, rec = orc.quantize_group(x[bh, s0:s1, d], bits)
+                assert ks.scale[bh, g, d] == sc and ks.zero[bh, g, d] == ze
+                assert np.array_equal(rk[bh, s0:s1, d], rec)
+        for s in (0, G, S - 1):
+            for j in range(D // G):
+                sc, ze, q, rec = orc.quantize_group(x[bh, s, G * j:G * j + G], bits)
+                assert vs.scale[bh, s, j] == sc and vs.zero[bh, s, j] == ze
+                assert np.array_equal(rv[bh, s, G * j:G * j + G], rec)
+    assert np.array_equal(orc.dequantize(ks, 0, S), rk)
+    assert np.array_equal(orc.dequantize(vs, 0, S), rv)
+
+
+def test_group_of_128_values_is_the_whole_row(orc):
+    """With G = D every token has one value group: its scale is the row's
+    (max - min) / (2^bits - 1)."""
+    rng = np.random.default_rng(5)
+    x = _f16(rng.standard_normal((1, 3, D)))
+    vs = orc.Store(orc.VALUES, 1, 32, D, 4, 128)
+    orc.quantize_values(x, vs, 0)
+    w = x.view(np.float16).astype(np.float32)
+    for s in range(3):
+        assert vs.zero[0, s, 0] == w[0, s].min()
+        assert vs.scale[0, s, 0] == np.float32(np.float32(w[0, s].max() - w[0, s].min()) / np.float32(15))
