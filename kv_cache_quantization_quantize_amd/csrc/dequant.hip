@@ -74,7 +74,7 @@ __device__ __forceinline__ void dequant_tile(const uint32_t* __restrict__ cb, co
         uint32_t h[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) h[j] = recon_out<BF16>(static_cast<float>((w >> (BITS * j)) & kMask), sc[j], ze[j]);
-        *reinterpret_cast<uint4*>(ot + k * kHeadDim + c * 8) = pack8(h);
+        store_stream(ot + k * kHeadDim + c * 8, pack8(h));
     }
 }
 

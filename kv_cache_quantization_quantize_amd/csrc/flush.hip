@@ -47,7 +47,7 @@ __device__ __forceinline__ void key_tile(const uint16_t* __restrict__ xt, uint32
     for (int i = 0; i < kRows; ++i) {
         int row = r + kRowsPerWave * i;
         if constexpr (RAGGED) row = row < n_rows ? row : n_rows - 1;
-        raw[i] = *reinterpret_cast<const uint4*>(xt + row * kHeadDim + c * 8);
+        raw[i] = load_stream(xt + row * kHeadDim + c * 8);
     }
 
     // Per-channel min/max over the lane's rows and then across the 4 row
@@ -113,11 +113,11 @@ __device__ __forceinline__ void key_tile(const uint16_t* __restrict__ xt, uint32
     }
 
     if (r == 0) {
-        *reinterpret_cast<float4*>(sct + c * 8) = make_float4(sc[0], sc[1], sc[2], sc[3]);
-        *reinterpret_cast<float4*>(sct + c * 8 + 4) = make_float4(sc[4], sc[5], sc[6], sc[7]);
+        store_stream4(sct + c * 8, sc[0], sc[1], sc[2], sc[3]);
+        store_stream4(sct + c * 8 + 4, sc[4], sc[5], sc[6], sc[7]);
     } else if (r == 1) {
-        *reinterpret_cast<float4*>(zet + c * 8) = make_float4(ze[0], ze[1], ze[2], ze[3]);
-        *reinterpret_cast<float4*>(zet + c * 8 + 4) = make_float4(ze[4], ze[5], ze[6], ze[7]);
+        store_stream4(zet + c * 8, ze[0], ze[1], ze[2], ze[3]);
+        store_stream4(zet + c * 8 + 4, ze[4], ze[5], ze[6], ze[7]);
     }
 
 #pragma unroll
@@ -140,17 +140,17 @@ __device__ __forceinline__ void key_tile(const uint16_t* __restrict__ xt, uint32
         const bool live = !RAGGED || row < n_rows;
         if constexpr (BITS == 4) {
             // the lane's 8 channels are exactly one word
-            if (live) ct[row * kWords + c] = packed;
+            if (live) store_stream(&ct[row * kWords + c], packed);
         } else {
             // 16 channels per word: the even lane takes its odd neighbour's half
             const uint32_t hi = quad_xor1(packed);
-            if (live && (c & 1) == 0) ct[row * kWords + (c >> 1)] = packed | (hi << 16);
+            if (live && (c & 1) == 0) store_stream(&ct[row * kWords + (c >> 1)], packed | (hi << 16));
         }
         if constexpr (RECON) {
             uint32_t h[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) h[j] = recon_out<BF16>(qf[j], sc[j], ze[j]);
-            if (live) *reinterpret_cast<uint4*>(rt + row * kHeadDim + c * 8) = pack8(h);
+            if (live) store_stream(rt + row * kHeadDim + c * 8, pack8(h));
         }
     }
 }
@@ -201,7 +201,7 @@ __device__ __forceinline__ void value_tile(const uint16_t* __restrict__ xt, uint
     for (int i = 0; i < kTokPerLane; ++i) {
         int row = r + kRowsPerWave * i;
         if constexpr (RAGGED) row = row < n_rows ? row : n_rows - 1;   // keep every lane in the exchange
-        raw[i] = *reinterpret_cast<const uint4*>(xt + row * kHeadDim + c * 8);
+        raw[i] = load_stream(xt + row * kHeadDim + c * 8);
     }
 
 #pragma unroll
@@ -267,12 +267,15 @@ __device__ __forceinline__ void value_tile(const uint16_t* __restrict__ xt, uint
         for (int k = 1; k < 8; ++k) packed |= static_cast<uint32_t>(qf[k]) << (BITS * k);
         const bool live = !RAGGED || row < n_rows;
         if constexpr (BITS == 4) {
-            if (live) ct[row * kWords + c] = packed;
+            if (live) store_stream(&ct[row * kWords + c], packed);
         } else {
             const uint32_t hw = quad_xor1(packed);
-            if (live && (c & 1) == 0) ct[row * kWords + (c >> 1)] = packed | (hw << 16);
+            if (live && (c & 1) == 0) store_stream(&ct[row * kWords + (c >> 1)], packed | (hw << 16));
         }
         if (live) {
+            // plain stores: one instruction writes 16-64 B of a line, which the
+            // L2 merges (with the nontemporal hint they reached HBM as partial
+            // lines: 8% more write traffic and a slower flush)
             if (c % kLanesPerGroup == 0) sct[row * kMetaPerTok + j] = sc;
             else if (c % kLanesPerGroup == 1) zet[row * kMetaPerTok + j] = ze;
         }
@@ -280,7 +283,7 @@ __device__ __forceinline__ void value_tile(const uint16_t* __restrict__ xt, uint
             uint32_t h[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k) h[k] = recon_out<BF16>(qf[k], sc, ze);
-            if (live) *reinterpret_cast<uint4*>(rt + row * kHeadDim + c * 8) = pack8(h);
+            if (live) store_stream(rt + row * kHeadDim + c * 8, pack8(h));
         }
     }
 }
