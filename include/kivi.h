@@ -23,7 +23,8 @@
  *  - Inputs must not alias outputs.  Calls on different streams may run
  *    concurrently if their outputs do not overlap.
  *  - Faults inside a kernel surface at the caller's next synchronization.
- *  - Supported parameters: bits in {2, 4}, group_size 32, head_dim 128.
+ *  - Supported parameters: bits in {2, 4}, group_size in {32, 64, 128}
+ *    (the key and value stores of one attend share it), head_dim 128.
  *    Anything else returns KIVI_ERR_UNSUPPORTED (there is no fallback
  *    path).
  *
@@ -75,7 +76,7 @@ typedef struct kivi_store {
     int64_t   meta_bh_stride;  /* floats between bh slabs                     */
     int64_t   cap;             /* token capacity of each slab                 */
     int32_t   bits;            /* 2 or 4                                      */
-    int32_t   group_size;      /* 32                                          */
+    int32_t   group_size;      /* 32, 64 or 128                               */
     int32_t   head_dim;        /* 128                                         */
     int32_t   kind;            /* KIVI_KEYS or KIVI_VALUES                    */
 } kivi_store;

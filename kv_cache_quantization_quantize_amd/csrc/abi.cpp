@@ -25,7 +25,6 @@ int hip_status(hipError_t e) {
 namespace {
 
 constexpr int64_t kD = 128;
-constexpr int64_t kG = 32;
 constexpr int64_t kMaxBlocks = (int64_t{1} << 31) - 1;
 constexpr int64_t kMaxAttendTokens = int64_t{1} << 24;   // attend offsets stay 32-bit
 
@@ -40,8 +39,8 @@ int64_t meta_rows(const kivi_store* st) {
     return st->kind == KIVI_KEYS ? (st->cap + G - 1) / G * kD : st->cap * (kD / G);
 }
 
-// The flush and dequantize take groups of 32, 64 or 128; the attend and the
-// decode-loop cache take 32.
+// Stores take groups of 32, 64 or 128 tokens (keys) or channels (values);
+// the decode-loop cache uses 32.
 bool flush_group_ok(int32_t G) { return G == 32 || G == 64 || G == 128; }
 
 // Checks a store and that tokens [t0, t0 + n) of slabs [0, BH) lie inside it.
@@ -186,7 +185,7 @@ int decode_attend_entry(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
     if (rc != KIVI_OK) return rc;
     if ((rc = check_store(v, KIVI_VALUES, slabs, 0, n_quant)) != KIVI_OK) return rc;
     if (k->bits != v->bits) return KIVI_ERR_SHAPE;
-    if (k->group_size != kG || v->group_size != kG) return KIVI_ERR_UNSUPPORTED;
+    if (k->group_size != v->group_size) return KIVI_ERR_UNSUPPORTED;
     if (B == 0) return KIVI_OK;
     if (!q || !out) return KIVI_ERR_NULL;
     if (!aligned16(q) || !aligned16(out)) return KIVI_ERR_ALIGN;
@@ -217,7 +216,7 @@ int decode_attend_entry(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
     a.res_ring = res_ring > 0 ? static_cast<int32_t>(res_ring) : (1 << 30);
     a.seq_n_quant = seq_n_quant; a.seq_n_res = seq_n_res;
     a.softmax_scale = softmax_scale; a.out = out;
-    a.workspace = workspace; a.bits = k->bits;
+    a.workspace = workspace; a.bits = k->bits; a.group = k->group_size;
     return finish(kivi::launch_decode_attend(a, plan, stream));
 }
 

@@ -173,7 +173,8 @@ struct LaneOffsets {
     uint32_t k;             // key codes of token n, the lane's 32 channels
     uint32_t v;             // value code word of token 4q, the lane's 8 channels
     uint32_t km;            // key scale / zero of channels 2l, 2l+1
-    uint32_t vm;            // value scale / zero of token l & 31, groups 2(l>>5), +1
+    uint32_t vm;            // value scale / zero of token l & 31: groups 2(l>>5), +1 (G = 32),
+                            // groups 0, 1 (G = 64) or group 0 (G = 128)
 };
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -196,7 +197,7 @@ struct StepLoad {
 // QK^T leaves each lane its scores (rows 4q .. 4q+3 of both 16-token blocks).
 __device__ __forceinline__ int pv_token(int q, int s) { return 16 * (s >> 2) + 4 * q + (s & 3); }
 
-template <int BITS>
+template <int BITS, int G>
 __device__ __forceinline__ void issue_step(StepLoad& L, const StoreView& S, const LaneOffsets& O,
                                            uint32_t t0, int n) {
     constexpr uint32_t kRow = kHeadDim * BITS / 8;          // code bytes per token
@@ -211,12 +212,19 @@ __device__ __forceinline__ void issue_step(StepLoad& L, const StoreView& S, cons
             L.kw[blk][0] = t.x; L.kw[blk][1] = t.x; L.kw[blk][2] = t.y; L.kw[blk][3] = t.y;
         }
     }
-    const uint32_t kmo = O.km + 16 * t0;
+    // key metadata of the step's group (a 32-token step never crosses one)
+    const uint32_t kmo = O.km + (t0 / G) * (kHeadDim * 4);
     L.ks = as_float2(__builtin_amdgcn_raw_buffer_load_b64(S.ks, kmo, 0, kStreamLoad));
     L.kz = as_float2(__builtin_amdgcn_raw_buffer_load_b64(S.kz, kmo, 0, kStreamLoad));
-    const uint32_t vmo = O.vm + 16 * t0;
-    L.vs = as_float2(__builtin_amdgcn_raw_buffer_load_b64(S.vs, vmo, 0, kStreamLoad));
-    L.vz = as_float2(__builtin_amdgcn_raw_buffer_load_b64(S.vz, vmo, 0, kStreamLoad));
+    // value metadata: 128/G floats per token
+    const uint32_t vmo = O.vm + (kHeadDim * 4 / G) * t0;
+    if constexpr (G == 128) {
+        L.vs = make_float2(__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(S.vs, vmo, 0, kStreamLoad)), 0.0f);
+        L.vz = make_float2(__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(S.vz, vmo, 0, kStreamLoad)), 0.0f);
+    } else {
+        L.vs = as_float2(__builtin_amdgcn_raw_buffer_load_b64(S.vs, vmo, 0, kStreamLoad));
+        L.vz = as_float2(__builtin_amdgcn_raw_buffer_load_b64(S.vz, vmo, 0, kStreamLoad));
+    }
     const uint32_t vo = O.v + t0 * kRow;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
@@ -320,7 +328,7 @@ __device__ __forceinline__ Frag softmax_any(const float4_t (&acc_s)[2], SoftStat
 }
 
 // One step of store tokens [t0, t0 + 32), tokens at or past n_quant masked.
-template <int BITS>
+template <int BITS, int G>
 __device__ __forceinline__ void store_step(const StepLoad& L, Smem& sm, SoftState& st,
                                            int t0, int n_quant, float c2,
                                            int l, int n, int q) {
@@ -335,12 +343,16 @@ __device__ __forceinline__ void store_step(const StepLoad& L, Smem& sm, SoftStat
             make_float2(__builtin_fmaf(-1024.0f, s0, L.kz.x), __builtin_fmaf(-1024.0f, s1, L.kz.y));
     }
     {
+        // lanes l and l + 32 hold the same token; for G = 64 and 128 they
+        // hold the same groups too and write the same values
         const int tt = l & 31;
-        const int gg = (l >> 5) * 2;
+        const int gg = G == 32 ? (l >> 5) * 2 : 0;
         sm.vs[gg][tt] = L.vs.x;
-        sm.vs[gg + 1][tt] = L.vs.y;
         sm.vz[gg][tt] = __builtin_fmaf(-1024.0f, L.vs.x, L.vz.x);
-        sm.vz[gg + 1][tt] = __builtin_fmaf(-1024.0f, L.vs.y, L.vz.y);
+        if constexpr (G != 128) {
+            sm.vs[gg + 1][tt] = L.vs.y;
+            sm.vz[gg + 1][tt] = __builtin_fmaf(-1024.0f, L.vs.y, L.vz.y);
+        }
     }
     lds_order();
 
@@ -371,7 +383,7 @@ __device__ __forceinline__ void store_step(const StepLoad& L, Smem& sm, SoftStat
 
     // ---- O^T += V^T P^T: MFMA i covers channels 8m + i, m = 0..15.  Slot s of
     // lane (q, m) is channel 8m + i of step token pv_token(q, s).
-    const int vg = n >> 2;
+    const int vg = n / (G / 8);                 // value group of the lane's channels 8n .. 8n+7
     const float4 vsa = *reinterpret_cast<const float4*>(&sm.vs[vg][4 * q]);
     const float4 vsb = *reinterpret_cast<const float4*>(&sm.vs[vg][16 + 4 * q]);
     const float4 vza = *reinterpret_cast<const float4*>(&sm.vz[vg][4 * q]);
@@ -459,7 +471,7 @@ __device__ __forceinline__ void residual_step(const uint16_t* kr, const uint16_t
 // that axis, so one wave may finish the store and start the residual.
 // Offsets within a slab fit in 32 bits: the ABI keeps n_quant and n_res
 // below 2^24 tokens.
-template <int BITS, int GQA>
+template <int BITS, int GQA, int G>
 __global__ __launch_bounds__(64) KIVI_ATTEND_OCCUPANCY void attend_partial_kernel(const AttendArgs a, int spw, int steps_q,
                                                             int64_t n_split, float* __restrict__ ws_o,
                                                             float* __restrict__ ws_ml)
@@ -492,7 +504,7 @@ __global__ __launch_bounds__(64) KIVI_ATTEND_OCCUPANCY void attend_partial_kerne
     // Store part: buffer views and the first two steps' loads, issued before
     // the query so the two HBM latencies overlap.
     constexpr int kWords = kHeadDim * BITS / 32;
-    constexpr int kMetaPerTok = kHeadDim / kGroup;
+    constexpr int kMetaPerTok = kHeadDim / G;
     StoreView S;
     LaneOffsets O;
     StepLoad buf[kNBuf];
@@ -502,7 +514,7 @@ __global__ __launch_bounds__(64) KIVI_ATTEND_OCCUPANCY void attend_partial_kerne
     // all outstanding loads at the join.
     const auto pref = [j1](int t) { return t < j1 ? static_cast<uint32_t>(t) : kFarToken; };
     if (has_store) {
-        const uint32_t n_groups = static_cast<uint32_t>((nq + kGroup - 1) / kGroup);
+        const uint32_t n_groups = static_cast<uint32_t>((nq + G - 1) / G);
         S.kc = make_rsrc(a.k_codes + bkv * a.k_codes_bh_stride, static_cast<uint32_t>(nq) * kWords * 4u);
         S.ks = make_rsrc(a.k_scale + bkv * a.k_meta_bh_stride, n_groups * kHeadDim * 4u);
         S.kz = make_rsrc(a.k_zero + bkv * a.k_meta_bh_stride, n_groups * kHeadDim * 4u);
@@ -512,9 +524,10 @@ __global__ __launch_bounds__(64) KIVI_ATTEND_OCCUPANCY void attend_partial_kerne
         O.k = static_cast<uint32_t>(n * kWords + (BITS == 4 ? 4 * q : 2 * q)) * 4u;
         O.v = static_cast<uint32_t>(4 * q * kWords + (BITS == 4 ? n : (n >> 1))) * 4u;
         O.km = static_cast<uint32_t>(l) * 8u;
-        O.vm = static_cast<uint32_t>(l & 31) * 16u + static_cast<uint32_t>(l >> 5) * 8u;
+        O.vm = G == 32 ? static_cast<uint32_t>(l & 31) * 16u + static_cast<uint32_t>(l >> 5) * 8u
+                       : static_cast<uint32_t>(l & 31) * (kMetaPerTok * 4u);
 #pragma unroll
-        for (int u = 0; u + 1 < kNBuf; ++u) issue_step<BITS>(buf[u], S, O, pref(j0 + u * kStep), n);
+        for (int u = 0; u + 1 < kNBuf; ++u) issue_step<BITS, G>(buf[u], S, O, pref(j0 + u * kStep), n);
     }
 
     // B operand of QK^T: q of head n (zero for n >= GQA) in slot order.
@@ -560,8 +573,8 @@ __global__ __launch_bounds__(64) KIVI_ATTEND_OCCUPANCY void attend_partial_kerne
         for (int t0 = j0; t0 < j1; t0 += kNBuf * kStep) {
 #pragma unroll
             for (int u = 0; u < kNBuf; ++u) {
-                issue_step<BITS>(buf[(u + kNBuf - 1) % kNBuf], S, O, pref(t0 + (u + kNBuf - 1) * kStep), n);
-                store_step<BITS>(buf[u], sm, st, t0 + u * kStep, j1, c2, l, n, q);
+                issue_step<BITS, G>(buf[(u + kNBuf - 1) % kNBuf], S, O, pref(t0 + (u + kNBuf - 1) * kStep), n);
+                store_step<BITS, G>(buf[u], sm, st, t0 + u * kStep, j1, c2, l, n, q);
                 if (t0 + (u + 1) * kStep >= j1) goto store_done;
             }
         }
@@ -703,14 +716,14 @@ AttendPlan plan_attend(int64_t B, int Hq, int Hkv, int64_t n_quant, int64_t n_re
     return p;
 }
 
-template <int BITS, int GQA>
+template <int BITS, int GQA, int G>
 static hipError_t launch_t(const AttendArgs& a, const AttendPlan& p, hipStream_t stream) {
     float* ws_o = static_cast<float*>(a.workspace);
     const size_t rows = static_cast<size_t>(a.B) * a.Hq * p.n_split;
     const size_t o_bytes = (rows * kHeadDim * sizeof(float) + 255) & ~static_cast<size_t>(255);
     float* ws_ml = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + o_bytes);
     const dim3 grid(static_cast<uint32_t>(p.n_split), static_cast<uint32_t>(a.B * a.Hkv));
-    hipLaunchKernelGGL((attend_partial_kernel<BITS, GQA>), grid, dim3(64), 0, stream, a,
+    hipLaunchKernelGGL((attend_partial_kernel<BITS, GQA, G>), grid, dim3(64), 0, stream, a,
                        static_cast<int>(p.steps_per_wave), static_cast<int>(p.steps_q), p.n_split,
                        ws_o, ws_ml);
     hipError_t e = hipGetLastError();
@@ -724,13 +737,22 @@ static hipError_t launch_t(const AttendArgs& a, const AttendPlan& p, hipStream_t
     return hipGetLastError();
 }
 
+template <int BITS, int G>
+static hipError_t launch_gqa(const AttendArgs& a, const AttendPlan& p, hipStream_t stream) {
+    switch (a.Hq / a.Hkv) {
+        case 1: return launch_t<BITS, 1, G>(a, p, stream);
+        case 2: return launch_t<BITS, 2, G>(a, p, stream);
+        case 4: return launch_t<BITS, 4, G>(a, p, stream);
+        default: return launch_t<BITS, 8, G>(a, p, stream);
+    }
+}
+
 template <int BITS>
 static hipError_t launch_bits(const AttendArgs& a, const AttendPlan& p, hipStream_t stream) {
-    switch (a.Hq / a.Hkv) {
-        case 1: return launch_t<BITS, 1>(a, p, stream);
-        case 2: return launch_t<BITS, 2>(a, p, stream);
-        case 4: return launch_t<BITS, 4>(a, p, stream);
-        default: return launch_t<BITS, 8>(a, p, stream);
+    switch (a.group) {
+        case 64: return launch_gqa<BITS, 64>(a, p, stream);
+        case 128: return launch_gqa<BITS, 128>(a, p, stream);
+        default: return launch_gqa<BITS, 32>(a, p, stream);
     }
 }
 

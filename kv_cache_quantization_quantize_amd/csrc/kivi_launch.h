@@ -71,6 +71,7 @@ struct AttendArgs {
     float* out;
     void* workspace;
     int bits;
+    int group;                     // 32, 64 or 128 (keys and values alike)
 };
 
 // Split of the token axis chosen for an attend shape; the workspace holds

@@ -157,8 +157,9 @@ def test_attend_validation():
     assert call(wsb=ws - 4) == -5
     assert call(wsp=None) == -5
     assert call(wsp=FAKE + 16) == -4
-    # the attend reads groups of 32 only (the flush and dequantize take 64 and 128 too)
-    assert call(kk=_store(kivi.KIVI_KEYS, cap=64, G=64), vv=_store(kivi.KIVI_VALUES, cap=64, G=64)) == -3
+    # key and value stores must share their group size (32, 64 or 128)
+    assert call(kk=_store(kivi.KIVI_KEYS, cap=64, G=64), vv=_store(kivi.KIVI_VALUES, cap=64, G=32)) == -3
+    assert call(kk=_store(kivi.KIVI_KEYS, cap=64, G=48), vv=_store(kivi.KIVI_VALUES, cap=64, G=48)) == -3
 
 
 # ---------------------------------------------------------------- cache

@@ -79,3 +79,46 @@ def test_dequantize_ranges_inside_wide_key_groups():
         out = kivi.dequantize(st, t0, n)
         torch.cuda.synchronize()
         assert_u16_equal(u16(out), oracle.dequantize(hs, t0, n), f"[{t0}, {t0 + n})")
+
+
+ATTEND = [
+    # B, Hq, Hkv, n_quant, n_res, bits
+    (2, 32, 8, 1000, 37, 4),
+    (1, 32, 8, 4096 + 64, 128, 4),
+    (3, 64, 8, 300, 5, 2),
+    (2, 32, 8, 0, 64, 4),
+]
+
+
+@pytest.mark.parametrize("G", [64, 128])
+@pytest.mark.parametrize("case", ATTEND, ids=lambda c: "B%d-Hq%d-nq%d-nr%d-b%d" % (c[0], c[1], c[3], c[4], c[5]))
+def test_attend_over_wide_group_stores(case, G):
+    B, Hq, Hkv, nq, nr, bits = case
+    BH = B * Hkv
+    cap = max(G, ((nq + G - 1) // G) * G)
+    seed = 9100 + nq + G
+    kx = synth.kv_tensor(BH, max(nq, 1), keys=True, seed=seed, device="cuda")[:, :nq]
+    vx = synth.kv_tensor(BH, max(nq, 1), keys=False, seed=seed, device="cuda")[:, :nq]
+    kr = synth.residual(BH, max(nr, 1), keys=True, seed=seed, device="cuda")
+    vr = synth.residual(BH, max(nr, 1), keys=False, seed=seed, device="cuda")
+    q = synth.query(B, Hq, seed=seed, device="cuda")
+    ks = kivi.Store(kivi.KIVI_KEYS, BH, cap, bits, group=G)
+    vs = kivi.Store(kivi.KIVI_VALUES, BH, cap, bits, group=G)
+    note(f"attend over G={G} stores B={B} Hq={Hq} n_quant={nq} n_res={nr} bits={bits}")
+    if nq:
+        kivi.quantize_keys(kx, ks, 0)
+        kivi.quantize_values(vx, vs, 0)
+    out = kivi.decode_attend(q, ks, vs, nq, kr, vr, nr)
+    nq_t = torch.full((B,), nq, dtype=torch.int32, device="cuda")
+    nr_t = torch.full((B,), nr, dtype=torch.int32, device="cuda")
+    out_v = kivi.decode_attend_varlen(q, ks, vs, nq_t, nq, kr, vr, nr_t, nr)
+    torch.cuda.synchronize()
+    hk = oracle.Store(oracle.KEYS, BH, cap, D, bits, G)
+    hv = oracle.Store(oracle.VALUES, BH, cap, D, bits, G)
+    if nq:
+        oracle.quantize_keys(u16(kx), hk, 0, want_recon=False)
+        oracle.quantize_values(u16(vx), hv, 0, want_recon=False)
+    ref = oracle.decode_attend(u16(q), B, Hq, Hkv, hk, hv, nq, u16(kr), u16(vr), nr)
+    for got in (out, out_v):
+        err = float(np.max(np.abs(got.cpu().numpy().astype(np.float64) - ref)))
+        assert err <= 2e-3, f"max-abs error {err:.3e}"

@@ -54,3 +54,34 @@ def test_group_of_128_values_is_the_whole_row(orc):
     for s in range(3):
         assert vs.zero[0, s, 0] == w[0, s].min()
         assert vs.scale[0, s, 0] == np.float32(np.float32(w[0, s].max() - w[0, s].min()) / np.float32(15))
+
+
+@pytest.mark.parametrize("G", [64, 128])
+def test_attend_over_wide_group_stores_matches_torch_sdpa(orc, G):
+    """The attend over stores with groups of G is the definition over their
+    dequantized tokens (torch float64 SDPA, a library routine)."""
+    import torch
+    rng = np.random.default_rng(G)
+    B, Hq, Hkv, nq, nr = 2, 8, 2, 150, 11
+    cap = ((nq + G - 1) // G) * G
+    k = _f16(rng.standard_normal((B * Hkv, nq, D)) * np.where(rng.random(D) < 0.05, 10, 1))
+    v = _f16(rng.standard_normal((B * Hkv, nq, D)))
+    ks = orc.Store(orc.KEYS, B * Hkv, cap, D, 4, G)
+    vs = orc.Store(orc.VALUES, B * Hkv, cap, D, 4, G)
+    orc.quantize_keys(k, ks)
+    orc.quantize_values(v, vs)
+    q = _f16(rng.standard_normal((B, Hq, D)))
+    kr = _f16(rng.standard_normal((B * Hkv, 16, D)))
+    vr = _f16(rng.standard_normal((B * Hkv, 16, D)))
+    got = orc.decode_attend(q, B, Hq, Hkv, ks, vs, nq, kr, vr, nr)
+
+    def w(u):
+        return u.view(np.float16).astype(np.float64)
+    kk = np.concatenate([w(orc.dequantize(ks, 0, nq)), w(kr[:, :nr])], axis=1)
+    vv = np.concatenate([w(orc.dequantize(vs, 0, nq)), w(vr[:, :nr])], axis=1)
+    g = Hq // Hkv
+    kt = torch.from_numpy(kk.reshape(B, Hkv, -1, D)).repeat_interleave(g, dim=1)
+    vt = torch.from_numpy(vv.reshape(B, Hkv, -1, D)).repeat_interleave(g, dim=1)
+    qt = torch.from_numpy(w(q)).reshape(B, Hq, 1, D)
+    want = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt).reshape(B, Hq, D).numpy()
+    assert np.max(np.abs(got - want)) < 1e-12
