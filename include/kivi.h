@@ -23,8 +23,9 @@
  *  - Inputs must not alias outputs.  Calls on different streams may run
  *    concurrently if their outputs do not overlap.
  *  - Faults inside a kernel surface at the caller's next synchronization.
- *  - Supported parameters: bits in {2, 4}, group_size in {32, 64, 128}
- *    (the key and value stores of one attend share it), head_dim 128.
+ *  - Supported parameters: bits in {2, 4}; head_dim 128 with group_size
+ *    32, 64 or 128, or head_dim 64 or 256 with group_size 32.  The attend
+ *    takes head_dim 128, and its key and value stores share the group size.
  *    Anything else returns KIVI_ERR_UNSUPPORTED (there is no fallback
  *    path).
  *
@@ -77,7 +78,7 @@ typedef struct kivi_store {
     int64_t   cap;             /* token capacity of each slab                 */
     int32_t   bits;            /* 2 or 4                                      */
     int32_t   group_size;      /* 32, 64 or 128                               */
-    int32_t   head_dim;        /* 128                                         */
+    int32_t   head_dim;        /* 64, 128 or 256                              */
     int32_t   kind;            /* KIVI_KEYS or KIVI_VALUES                    */
 } kivi_store;
 

@@ -32,16 +32,20 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int finish(hipError_t e) { return kivi::hip_status(e); }
 
-int64_t words_per_token(int bits) { return kD * bits / 32; }
+int64_t words_per_token(const kivi_store* st) { return int64_t{st->head_dim} * st->bits / 32; }
 
 int64_t meta_rows(const kivi_store* st) {
-    const int64_t G = st->group_size;
-    return st->kind == KIVI_KEYS ? (st->cap + G - 1) / G * kD : st->cap * (kD / G);
+    const int64_t G = st->group_size, D = st->head_dim;
+    return st->kind == KIVI_KEYS ? (st->cap + G - 1) / G * D : st->cap * (D / G);
 }
 
-// Stores take groups of 32, 64 or 128 tokens (keys) or channels (values);
-// the decode-loop cache uses 32.
-bool flush_group_ok(int32_t G) { return G == 32 || G == 64 || G == 128; }
+// Stores take head_dim 128 with groups of 32, 64 or 128 tokens (keys) or
+// channels (values), and head_dim 64 or 256 with groups of 32.  The attend
+// and the decode-loop cache take head_dim 128.
+bool geometry_ok(int32_t D, int32_t G) {
+    if (D == 128) return G == 32 || G == 64 || G == 128;
+    return (D == 64 || D == 256) && G == 32;
+}
 
 // Checks a store and that tokens [t0, t0 + n) of slabs [0, BH) lie inside it.
 int check_store(const kivi_store* st, int kind, int64_t BH, int64_t t0, int64_t n) {
@@ -49,23 +53,23 @@ int check_store(const kivi_store* st, int kind, int64_t BH, int64_t t0, int64_t 
     if (st->kind != KIVI_KEYS && st->kind != KIVI_VALUES) return KIVI_ERR_UNSUPPORTED;
     if (kind >= 0 && st->kind != kind) return KIVI_ERR_SHAPE;
     if (st->bits != 2 && st->bits != 4) return KIVI_ERR_UNSUPPORTED;
-    if (!flush_group_ok(st->group_size) || st->head_dim != kD) return KIVI_ERR_UNSUPPORTED;
+    if (!geometry_ok(st->head_dim, st->group_size)) return KIVI_ERR_UNSUPPORTED;
     if (!st->codes || !st->scale || !st->zero) return KIVI_ERR_NULL;
     if (!aligned16(st->codes) || !aligned16(st->scale) || !aligned16(st->zero)) return KIVI_ERR_ALIGN;
     if (st->codes_bh_stride % 4 != 0 || st->meta_bh_stride % 4 != 0) return KIVI_ERR_ALIGN;
     if (st->cap < 0 || t0 < 0 || n < 0 || t0 > st->cap - n) return KIVI_ERR_SHAPE;
     if (BH > 1) {
-        if (st->codes_bh_stride < st->cap * words_per_token(st->bits)) return KIVI_ERR_SHAPE;
+        if (st->codes_bh_stride < st->cap * words_per_token(st)) return KIVI_ERR_SHAPE;
         if (st->meta_bh_stride < meta_rows(st)) return KIVI_ERR_SHAPE;
     }
     return KIVI_OK;
 }
 
-// fp16 [BH][S][128] tensor with slab stride `stride` elements.
-int check_f16_tensor(const void* p, int64_t BH, int64_t S, int64_t stride) {
+// 16-bit [BH][S][D] tensor with slab stride `stride` elements.
+int check_f16_tensor(const void* p, int64_t BH, int64_t S, int64_t stride, int64_t D = kD) {
     if (!p) return KIVI_ERR_NULL;
     if (!aligned16(p) || stride % 8 != 0) return KIVI_ERR_ALIGN;
-    if (BH > 1 && stride < S * kD) return KIVI_ERR_SHAPE;
+    if (BH > 1 && stride < S * D) return KIVI_ERR_SHAPE;
     return KIVI_OK;
 }
 
@@ -77,8 +81,8 @@ int flush(bool keys, bool bf16, const uint16_t* x, int64_t BH, int64_t S, int64_
     if (rc != KIVI_OK) return rc;
     if (keys && dst_token % dst->group_size != 0) return KIVI_ERR_SHAPE;
     if (BH == 0 || S == 0) return KIVI_OK;
-    if ((rc = check_f16_tensor(x, BH, S, x_bh_stride)) != KIVI_OK) return rc;
-    if (recon && (rc = check_f16_tensor(recon, BH, S, recon_bh_stride)) != KIVI_OK) return rc;
+    if ((rc = check_f16_tensor(x, BH, S, x_bh_stride, dst->head_dim)) != KIVI_OK) return rc;
+    if (recon && (rc = check_f16_tensor(recon, BH, S, recon_bh_stride, dst->head_dim)) != KIVI_OK) return rc;
     const int64_t tiles = BH * ((S + 31) / 32);
     if ((tiles + 3) / 4 > kMaxBlocks) return KIVI_ERR_SHAPE;
 
@@ -89,6 +93,7 @@ int flush(bool keys, bool bf16, const uint16_t* x, int64_t BH, int64_t S, int64_
     a.dst_token = dst_token; a.recon = recon; a.recon_bh_stride = recon_bh_stride;
     a.bits = dst->bits;
     a.group = dst->group_size;
+    a.head_dim = dst->head_dim;
     a.bf16 = bf16;
     return finish(keys ? kivi::launch_key_flush(a, stream) : kivi::launch_value_flush(a, stream));
 }
@@ -127,14 +132,15 @@ static int dequantize(bool bf16, const kivi_store* src, int64_t BH, int64_t toke
     int rc = check_store(src, -1, BH, token_begin, n_tokens);
     if (rc != KIVI_OK) return rc;
     if (BH == 0 || n_tokens == 0) return KIVI_OK;
-    if ((rc = check_f16_tensor(out, BH, n_tokens, out_bh_stride)) != KIVI_OK) return rc;
+    if ((rc = check_f16_tensor(out, BH, n_tokens, out_bh_stride, src->head_dim)) != KIVI_OK) return rc;
     const int64_t tiles = BH * ((n_tokens + 31) / 32);
     if ((tiles + 3) / 4 > kMaxBlocks) return KIVI_ERR_SHAPE;
     kivi::DequantArgs a;
     a.codes = src->codes; a.codes_bh_stride = src->codes_bh_stride;
     a.scale = src->scale; a.zero = src->zero; a.meta_bh_stride = src->meta_bh_stride;
     a.BH = BH; a.t0 = token_begin; a.n = n_tokens; a.out = out; a.out_bh_stride = out_bh_stride;
-    a.bits = src->bits; a.kind = src->kind; a.group = src->group_size; a.bf16 = bf16;
+    a.bits = src->bits; a.kind = src->kind; a.group = src->group_size; a.head_dim = src->head_dim;
+    a.bf16 = bf16;
     return finish(kivi::launch_dequantize(a, stream));
 }
 
@@ -186,6 +192,7 @@ int decode_attend_entry(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
     if ((rc = check_store(v, KIVI_VALUES, slabs, 0, n_quant)) != KIVI_OK) return rc;
     if (k->bits != v->bits) return KIVI_ERR_SHAPE;
     if (k->group_size != v->group_size) return KIVI_ERR_UNSUPPORTED;
+    if (k->head_dim != kD || v->head_dim != kD) return KIVI_ERR_UNSUPPORTED;
     if (B == 0) return KIVI_OK;
     if (!q || !out) return KIVI_ERR_NULL;
     if (!aligned16(q) || !aligned16(out)) return KIVI_ERR_ALIGN;

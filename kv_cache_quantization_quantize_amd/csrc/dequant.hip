@@ -17,21 +17,23 @@ namespace kivi {
 // Rows [0, n_rows) of one tile; row k is store token t_first + k, written to
 // ot + k*128.  ONE_GROUP (keys only): the 32 rows are exactly one key group,
 // so its scale and zero are loaded once for the tile.
-template <int BITS, bool KEYS, bool ONE_GROUP, bool BF16, int G>
+template <int BITS, bool KEYS, bool ONE_GROUP, bool BF16, int G, int D>
 __device__ __forceinline__ void dequant_tile(const uint32_t* __restrict__ cb, const float* __restrict__ scb,
                                              const float* __restrict__ zeb, int64_t t_first, int n_rows,
                                              uint16_t* __restrict__ ot, int lane)
 {
-    constexpr int kWords = kHeadDim * BITS / 32;
+    constexpr int kWords = D * BITS / 32;
     constexpr uint32_t kMask = (1u << BITS) - 1u;
-    constexpr int kMetaPerTok = kHeadDim / G;
-    const int c = lane & 15;
-    const int r = lane >> 4;
+    constexpr int kMetaPerTok = D / G;
+    constexpr int kLPR = RowGeo<D>::kLanesPerRow;
+    constexpr int kRPW = RowGeo<D>::kRowsPerWave;
+    const int c = lane % kLPR;
+    const int r = lane / kLPR;
     const uint32_t* ct = cb + t_first * kWords;
     float gs[8], gz[8];
     if constexpr (ONE_GROUP) {
-        const float* sp = scb + (t_first / G) * kHeadDim + c * 8;
-        const float* zp = zeb + (t_first / G) * kHeadDim + c * 8;
+        const float* sp = scb + (t_first / G) * D + c * 8;
+        const float* zp = zeb + (t_first / G) * D + c * 8;
         const float4 s0 = *reinterpret_cast<const float4*>(sp);
         const float4 s1 = *reinterpret_cast<const float4*>(sp + 4);
         const float4 z0 = *reinterpret_cast<const float4*>(zp);
@@ -42,8 +44,8 @@ __device__ __forceinline__ void dequant_tile(const uint32_t* __restrict__ cb, co
         gz[4] = z1.x; gz[5] = z1.y; gz[6] = z1.z; gz[7] = z1.w;
     }
 #pragma unroll
-    for (int i = 0; i < kTokPerLane; ++i) {
-        const int k = r + kRowsPerWave * i;            // output row
+    for (int i = 0; i < 32 / kRPW; ++i) {
+        const int k = r + kRPW * i;                    // output row
         if (!ONE_GROUP && k >= n_rows) continue;
         uint32_t w;
         if constexpr (BITS == 4) w = ct[k * kWords + c];
@@ -54,8 +56,8 @@ __device__ __forceinline__ void dequant_tile(const uint32_t* __restrict__ cb, co
             for (int j = 0; j < 8; ++j) { sc[j] = gs[j]; ze[j] = gz[j]; }
         } else if constexpr (KEYS) {
             const int64_t t = t_first + k;
-            const float* sp = scb + (t / G) * kHeadDim + c * 8;
-            const float* zp = zeb + (t / G) * kHeadDim + c * 8;
+            const float* sp = scb + (t / G) * D + c * 8;
+            const float* zp = zeb + (t / G) * D + c * 8;
             const float4 s0 = *reinterpret_cast<const float4*>(sp);
             const float4 s1 = *reinterpret_cast<const float4*>(sp + 4);
             const float4 z0 = *reinterpret_cast<const float4*>(zp);
@@ -74,11 +76,11 @@ __device__ __forceinline__ void dequant_tile(const uint32_t* __restrict__ cb, co
         uint32_t h[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) h[j] = recon_out<BF16>(static_cast<float>((w >> (BITS * j)) & kMask), sc[j], ze[j]);
-        store_stream(ot + k * kHeadDim + c * 8, pack8(h));
+        store_stream(ot + k * D + c * 8, pack8(h));
     }
 }
 
-template <int BITS, bool KEYS, bool BF16, int G>
+template <int BITS, bool KEYS, bool BF16, int G, int D>
 __global__ __launch_bounds__(kBlock) void dequant_kernel(
     const uint32_t* __restrict__ codes, int64_t codes_bh_stride,
     const float* __restrict__ scale, const float* __restrict__ zero, int64_t meta_bh_stride,
@@ -95,38 +97,41 @@ __global__ __launch_bounds__(kBlock) void dequant_kernel(
     const uint32_t* cb = codes + bh * codes_bh_stride;
     const float* scb = scale + bh * meta_bh_stride;
     const float* zeb = zero + bh * meta_bh_stride;
-    uint16_t* ot = out + bh * out_bh_stride + i0 * kHeadDim;
+    uint16_t* ot = out + bh * out_bh_stride + i0 * D;
     // a full tile inside one key group loads the group's scale and zero once
     if (KEYS && rows >= 32 && (t0 + i0) % G + 32 <= G)
-        dequant_tile<BITS, KEYS, true, BF16, G>(cb, scb, zeb, t0 + i0, 32, ot, lane);
+        dequant_tile<BITS, KEYS, true, BF16, G, D>(cb, scb, zeb, t0 + i0, 32, ot, lane);
     else
-        dequant_tile<BITS, KEYS, false, BF16, G>(cb, scb, zeb, t0 + i0, rows < 32 ? static_cast<int>(rows) : 32, ot, lane);
+        dequant_tile<BITS, KEYS, false, BF16, G, D>(cb, scb, zeb, t0 + i0, rows < 32 ? static_cast<int>(rows) : 32, ot, lane);
 }
 
-template <int BITS, bool KEYS, bool BF16, int G>
+template <int BITS, bool KEYS, bool BF16, int G, int D>
 static hipError_t launch_t(const DequantArgs& a, hipStream_t stream) {
     const int64_t tiles_per_bh = (a.n + 31) / 32;
     const int64_t n_tiles = a.BH * tiles_per_bh;
     const int64_t blocks = (n_tiles + kWavesPerBlock - 1) / kWavesPerBlock;
-    hipLaunchKernelGGL((dequant_kernel<BITS, KEYS, BF16, G>), dim3(static_cast<uint32_t>(blocks)),
+    hipLaunchKernelGGL((dequant_kernel<BITS, KEYS, BF16, G, D>), dim3(static_cast<uint32_t>(blocks)),
                        dim3(kBlock), 0, stream, a.codes, a.codes_bh_stride, a.scale, a.zero,
                        a.meta_bh_stride, a.t0, a.n, a.out, a.out_bh_stride, tiles_per_bh, n_tiles);
     return hipGetLastError();
 }
 
-template <bool BF16, int G>
+template <bool BF16, int G, int D>
 static hipError_t launch_g(const DequantArgs& a, hipStream_t stream) {
     const bool keys = a.kind == 0;
-    if (a.bits == 4) return keys ? launch_t<4, true, BF16, G>(a, stream) : launch_t<4, false, BF16, G>(a, stream);
-    return keys ? launch_t<2, true, BF16, G>(a, stream) : launch_t<2, false, BF16, G>(a, stream);
+    if (a.bits == 4) return keys ? launch_t<4, true, BF16, G, D>(a, stream) : launch_t<4, false, BF16, G, D>(a, stream);
+    return keys ? launch_t<2, true, BF16, G, D>(a, stream) : launch_t<2, false, BF16, G, D>(a, stream);
 }
 
+// head_dim 128 with groups of 32, 64 or 128; head_dim 64 and 256 with groups of 32
 template <bool BF16>
 static hipError_t launch_fmt(const DequantArgs& a, hipStream_t stream) {
+    if (a.head_dim == 64) return launch_g<BF16, 32, 64>(a, stream);
+    if (a.head_dim == 256) return launch_g<BF16, 32, 256>(a, stream);
     switch (a.group) {
-        case 64: return launch_g<BF16, 64>(a, stream);
-        case 128: return launch_g<BF16, 128>(a, stream);
-        default: return launch_g<BF16, 32>(a, stream);
+        case 64: return launch_g<BF16, 64, 128>(a, stream);
+        case 128: return launch_g<BF16, 128, 128>(a, stream);
+        default: return launch_g<BF16, 32, 128>(a, stream);
     }
 }
 

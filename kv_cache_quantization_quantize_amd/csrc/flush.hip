@@ -29,25 +29,27 @@ namespace kivi {
 // One tile.  xt, ct, rt point at token s0 of the slab (input, codes, recon);
 // n_rows = min(32, S - s0) real rows.  RAGGED tiles clamp loads to the last
 // real row and guard stores; full tiles do neither.
-template <int BITS, bool RECON, bool RAGGED, bool BF16, int G>
+template <int BITS, bool RECON, bool RAGGED, bool BF16, int G, int D>
 __device__ __forceinline__ void key_tile(const uint16_t* __restrict__ xt, uint32_t* __restrict__ ct,
                                          float* __restrict__ sct, float* __restrict__ zet,
                                          uint16_t* __restrict__ rt, int n_rows, int lane, float one)
 {
-    constexpr int kWords = kHeadDim * BITS / 32;   // code words per token row
-    const int c = lane & 15;                       // channels 8c .. 8c+7
-    const int r = lane >> 4;                       // token rows r, r+4, ...
+    constexpr int kWords = D * BITS / 32;          // code words per token row
+    constexpr int kLPR = RowGeo<D>::kLanesPerRow;
+    constexpr int kRPW = RowGeo<D>::kRowsPerWave;
+    const int c = lane % kLPR;                     // channels 8c .. 8c+7
+    const int r = lane / kLPR;                     // token rows r, r + kRPW, ...
 
     // Load 8 token rows x 8 channels.  Rows past the end of a ragged last
     // group re-read the last real token, which is the edge padding of
     // "Three ways to be off by one bit", item 3, and cannot move min or max.
-    constexpr int kRows = G / kRowsPerWave;        // token rows per lane: the tile is one group
+    constexpr int kRows = G / kRPW;                // token rows per lane: the tile is one group
     uint4 raw[kRows];
 #pragma unroll
     for (int i = 0; i < kRows; ++i) {
-        int row = r + kRowsPerWave * i;
+        int row = r + kRPW * i;
         if constexpr (RAGGED) row = row < n_rows ? row : n_rows - 1;
-        raw[i] = load_stream(xt + row * kHeadDim + c * 8);
+        raw[i] = load_stream(xt + row * D + c * 8);
     }
 
     // Per-channel min/max over the lane's rows and then across the 4 row
@@ -70,8 +72,8 @@ __device__ __forceinline__ void key_tile(const uint16_t* __restrict__ xt, uint32
                     mx = hmax(mx, a);
                 }
             }
-            mn = half_min(row_pair_min(mn));
-            mx = half_max(row_pair_max(mx));
+            mn = cross_rows_min<D>(mn);
+            mx = cross_rows_max<D>(mx);
             mnf[2 * k] = static_cast<float>(mn[0]); mnf[2 * k + 1] = static_cast<float>(mn[1]);
             mxf[2 * k] = static_cast<float>(mx[0]); mxf[2 * k + 1] = static_cast<float>(mx[1]);
         }
@@ -95,8 +97,8 @@ __device__ __forceinline__ void key_tile(const uint16_t* __restrict__ xt, uint32
                     mx = fmaximum(mx, a);
                 }
             }
-            mnf[j] = rows_min_f32(mn);
-            mxf[j] = rows_max_f32(mx);
+            mnf[j] = cross_rows_min_f32<D>(mn);
+            mxf[j] = cross_rows_max_f32<D>(mx);
         }
     }
 
@@ -122,7 +124,7 @@ __device__ __forceinline__ void key_tile(const uint16_t* __restrict__ xt, uint32
 
 #pragma unroll
     for (int i = 0; i < kRows; ++i) {
-        const int row = r + kRowsPerWave * i;
+        const int row = r + kRPW * i;
         float t[8], qf[8];
         float dev = 0.0f;
 #pragma unroll
@@ -150,12 +152,12 @@ __device__ __forceinline__ void key_tile(const uint16_t* __restrict__ xt, uint32
             uint32_t h[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) h[j] = recon_out<BF16>(qf[j], sc[j], ze[j]);
-            if (live) store_stream(rt + row * kHeadDim + c * 8, pack8(h));
+            if (live) store_stream(rt + row * D + c * 8, pack8(h));
         }
     }
 }
 
-template <int BITS, bool RECON, bool BF16, int G>
+template <int BITS, bool RECON, bool BF16, int G, int D>
 __global__ __launch_bounds__(kBlock) void key_flush_kernel(
     const uint16_t* __restrict__ x, int64_t S, int64_t x_bh_stride,
     uint32_t* __restrict__ codes, int64_t codes_bh_stride,
@@ -163,50 +165,53 @@ __global__ __launch_bounds__(kBlock) void key_flush_kernel(
     int64_t dst_token, uint16_t* __restrict__ recon, int64_t recon_bh_stride,
     int64_t n_groups, int64_t n_tiles, float one)
 {
-    constexpr int kWords = kHeadDim * BITS / 32;
+    constexpr int kWords = D * BITS / 32;
     const int lane = threadIdx.x & 63;
     const int64_t tile = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
     if (tile >= n_tiles) return;                   // uniform across the wave
     const int64_t bh = tile / n_groups;
     const int64_t g = tile - bh * n_groups;
     const int64_t s0 = g * G;
-    const uint16_t* xt = x + bh * x_bh_stride + s0 * kHeadDim;
+    const uint16_t* xt = x + bh * x_bh_stride + s0 * D;
     uint32_t* ct = codes + bh * codes_bh_stride + (dst_token + s0) * kWords;
-    const int64_t moff = bh * meta_bh_stride + (dst_token / G + g) * kHeadDim;
-    uint16_t* rt = RECON ? recon + bh * recon_bh_stride + s0 * kHeadDim : nullptr;
+    const int64_t moff = bh * meta_bh_stride + (dst_token / G + g) * D;
+    uint16_t* rt = RECON ? recon + bh * recon_bh_stride + s0 * D : nullptr;
     const int64_t rows = S - s0;
     if (rows >= G)
-        key_tile<BITS, RECON, false, BF16, G>(xt, ct, scale + moff, zero + moff, rt, G, lane, one);
+        key_tile<BITS, RECON, false, BF16, G, D>(xt, ct, scale + moff, zero + moff, rt, G, lane, one);
     else
-        key_tile<BITS, RECON, true, BF16, G>(xt, ct, scale + moff, zero + moff, rt, static_cast<int>(rows), lane, one);
+        key_tile<BITS, RECON, true, BF16, G, D>(xt, ct, scale + moff, zero + moff, rt, static_cast<int>(rows), lane, one);
 }
 
 // ---------------------------------------------------------------------------
 // Values: group = (bh, token s, channel group j) over channels [32j, 32j+32)
 // ---------------------------------------------------------------------------
-template <int BITS, bool RECON, bool RAGGED, bool BF16, int G>
+template <int BITS, bool RECON, bool RAGGED, bool BF16, int G, int D>
 __device__ __forceinline__ void value_tile(const uint16_t* __restrict__ xt, uint32_t* __restrict__ ct,
                                            float* __restrict__ sct, float* __restrict__ zet,
                                            uint16_t* __restrict__ rt, int n_rows, int lane, float one)
 {
-    constexpr int kWords = kHeadDim * BITS / 32;
-    constexpr int kMetaPerTok = kHeadDim / G;       // channel groups per token
+    constexpr int kWords = D * BITS / 32;
+    constexpr int kMetaPerTok = D / G;              // channel groups per token
     constexpr int kLanesPerGroup = G / 8;           // 4, 8 or 16 lanes of 8 channels
-    const int c = lane & 15;
-    const int r = lane >> 4;
+    constexpr int kLPR = RowGeo<D>::kLanesPerRow;
+    constexpr int kRPW = RowGeo<D>::kRowsPerWave;
+    constexpr int kRows = 32 / kRPW;                // token rows per lane in a 32-token tile
+    const int c = lane % kLPR;
+    const int r = lane / kLPR;
     const int j = c / kLanesPerGroup;               // channel group of this lane
 
-    uint4 raw[kTokPerLane];
+    uint4 raw[kRows];
 #pragma unroll
-    for (int i = 0; i < kTokPerLane; ++i) {
-        int row = r + kRowsPerWave * i;
+    for (int i = 0; i < kRows; ++i) {
+        int row = r + kRPW * i;
         if constexpr (RAGGED) row = row < n_rows ? row : n_rows - 1;   // keep every lane in the exchange
-        raw[i] = load_stream(xt + row * kHeadDim + c * 8);
+        raw[i] = load_stream(xt + row * D + c * 8);
     }
 
 #pragma unroll
-    for (int i = 0; i < kTokPerLane; ++i) {
-        const int row = r + kRowsPerWave * i;
+    for (int i = 0; i < kRows; ++i) {
+        const int row = r + kRPW * i;
         float lo, hi;
         if constexpr (!BF16) {
             const half2_t hv[4] = {as_h2(raw[i].x), as_h2(raw[i].y), as_h2(raw[i].z), as_h2(raw[i].w)};
@@ -283,12 +288,12 @@ __device__ __forceinline__ void value_tile(const uint16_t* __restrict__ xt, uint
             uint32_t h[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k) h[k] = recon_out<BF16>(qf[k], sc, ze);
-            if (live) store_stream(rt + row * kHeadDim + c * 8, pack8(h));
+            if (live) store_stream(rt + row * D + c * 8, pack8(h));
         }
     }
 }
 
-template <int BITS, bool RECON, bool BF16, int G>
+template <int BITS, bool RECON, bool BF16, int G, int D>
 __global__ __launch_bounds__(kBlock) void value_flush_kernel(
     const uint16_t* __restrict__ x, int64_t S, int64_t x_bh_stride,
     uint32_t* __restrict__ codes, int64_t codes_bh_stride,
@@ -296,70 +301,74 @@ __global__ __launch_bounds__(kBlock) void value_flush_kernel(
     int64_t dst_token, uint16_t* __restrict__ recon, int64_t recon_bh_stride,
     int64_t tiles_per_bh, int64_t n_tiles, float one)
 {
-    constexpr int kWords = kHeadDim * BITS / 32;
-    constexpr int kMetaPerTok = kHeadDim / G;
+    constexpr int kWords = D * BITS / 32;
+    constexpr int kMetaPerTok = D / G;
     const int lane = threadIdx.x & 63;
     const int64_t tile = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
     if (tile >= n_tiles) return;                    // uniform across the wave
     const int64_t bh = tile / tiles_per_bh;
     const int64_t s0 = (tile - bh * tiles_per_bh) * 32;
-    const uint16_t* xt = x + bh * x_bh_stride + s0 * kHeadDim;
+    const uint16_t* xt = x + bh * x_bh_stride + s0 * D;
     uint32_t* ct = codes + bh * codes_bh_stride + (dst_token + s0) * kWords;
     const int64_t moff = bh * meta_bh_stride + (dst_token + s0) * kMetaPerTok;
-    uint16_t* rt = RECON ? recon + bh * recon_bh_stride + s0 * kHeadDim : nullptr;
+    uint16_t* rt = RECON ? recon + bh * recon_bh_stride + s0 * D : nullptr;
     const int64_t rows = S - s0;
     if (rows >= 32)
-        value_tile<BITS, RECON, false, BF16, G>(xt, ct, scale + moff, zero + moff, rt, 32, lane, one);
+        value_tile<BITS, RECON, false, BF16, G, D>(xt, ct, scale + moff, zero + moff, rt, 32, lane, one);
     else
-        value_tile<BITS, RECON, true, BF16, G>(xt, ct, scale + moff, zero + moff, rt, static_cast<int>(rows), lane, one);
+        value_tile<BITS, RECON, true, BF16, G, D>(xt, ct, scale + moff, zero + moff, rt, static_cast<int>(rows), lane, one);
 }
 
 // ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
-template <int BITS, bool RECON, bool BF16, int G>
+template <int BITS, bool RECON, bool BF16, int G, int D>
 static hipError_t launch_keys_t(const FlushArgs& a, hipStream_t stream) {
     const int64_t n_groups = (a.S + G - 1) / G;
     const int64_t n_tiles = a.BH * n_groups;
     const int64_t blocks = (n_tiles + kWavesPerBlock - 1) / kWavesPerBlock;
-    hipLaunchKernelGGL((key_flush_kernel<BITS, RECON, BF16, G>), dim3(static_cast<uint32_t>(blocks)),
+    hipLaunchKernelGGL((key_flush_kernel<BITS, RECON, BF16, G, D>), dim3(static_cast<uint32_t>(blocks)),
                        dim3(kBlock), 0, stream, a.x, a.S, a.x_bh_stride, a.codes,
                        a.codes_bh_stride, a.scale, a.zero, a.meta_bh_stride, a.dst_token,
                        a.recon, a.recon_bh_stride, n_groups, n_tiles, 1.0f);
     return hipGetLastError();
 }
 
-template <int BITS, bool RECON, bool BF16, int G>
+template <int BITS, bool RECON, bool BF16, int G, int D>
 static hipError_t launch_values_t(const FlushArgs& a, hipStream_t stream) {
     const int64_t tiles_per_bh = (a.S + 31) / 32;
     const int64_t n_tiles = a.BH * tiles_per_bh;
     const int64_t blocks = (n_tiles + kWavesPerBlock - 1) / kWavesPerBlock;
-    hipLaunchKernelGGL((value_flush_kernel<BITS, RECON, BF16, G>), dim3(static_cast<uint32_t>(blocks)),
+    hipLaunchKernelGGL((value_flush_kernel<BITS, RECON, BF16, G, D>), dim3(static_cast<uint32_t>(blocks)),
                        dim3(kBlock), 0, stream, a.x, a.S, a.x_bh_stride, a.codes,
                        a.codes_bh_stride, a.scale, a.zero, a.meta_bh_stride, a.dst_token,
                        a.recon, a.recon_bh_stride, tiles_per_bh, n_tiles, 1.0f);
     return hipGetLastError();
 }
 
-// One instantiation per (bits, reconstruction, input format, group size).
-template <bool KEYS, bool BF16, int G>
+// One instantiation per (bits, reconstruction, input format, group size, head_dim).
+template <bool KEYS, bool BF16, int G, int D>
 static hipError_t launch_flush_g(const FlushArgs& a, hipStream_t stream) {
     const bool rec = a.recon != nullptr;
     if constexpr (KEYS) {
-        if (a.bits == 4) return rec ? launch_keys_t<4, true, BF16, G>(a, stream) : launch_keys_t<4, false, BF16, G>(a, stream);
-        return rec ? launch_keys_t<2, true, BF16, G>(a, stream) : launch_keys_t<2, false, BF16, G>(a, stream);
+        if (a.bits == 4) return rec ? launch_keys_t<4, true, BF16, G, D>(a, stream) : launch_keys_t<4, false, BF16, G, D>(a, stream);
+        return rec ? launch_keys_t<2, true, BF16, G, D>(a, stream) : launch_keys_t<2, false, BF16, G, D>(a, stream);
     } else {
-        if (a.bits == 4) return rec ? launch_values_t<4, true, BF16, G>(a, stream) : launch_values_t<4, false, BF16, G>(a, stream);
-        return rec ? launch_values_t<2, true, BF16, G>(a, stream) : launch_values_t<2, false, BF16, G>(a, stream);
+        if (a.bits == 4) return rec ? launch_values_t<4, true, BF16, G, D>(a, stream) : launch_values_t<4, false, BF16, G, D>(a, stream);
+        return rec ? launch_values_t<2, true, BF16, G, D>(a, stream) : launch_values_t<2, false, BF16, G, D>(a, stream);
     }
 }
 
+// head_dim 128 with groups of 32, 64 or 128; head_dim 64 and 256 with groups
+// of 32 (the ABI admits no other pair).
 template <bool KEYS, bool BF16>
 static hipError_t launch_flush_fmt(const FlushArgs& a, hipStream_t stream) {
+    if (a.head_dim == 64) return launch_flush_g<KEYS, BF16, 32, 64>(a, stream);
+    if (a.head_dim == 256) return launch_flush_g<KEYS, BF16, 32, 256>(a, stream);
     switch (a.group) {
-        case 64: return launch_flush_g<KEYS, BF16, 64>(a, stream);
-        case 128: return launch_flush_g<KEYS, BF16, 128>(a, stream);
-        default: return launch_flush_g<KEYS, BF16, 32>(a, stream);
+        case 64: return launch_flush_g<KEYS, BF16, 64, 128>(a, stream);
+        case 128: return launch_flush_g<KEYS, BF16, 128, 128>(a, stream);
+        default: return launch_flush_g<KEYS, BF16, 32, 128>(a, stream);
     }
 }
 

@@ -135,6 +135,55 @@ __device__ __forceinline__ uint32_t word_of(const uint4& v, int k) {
     return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
 }
 
+// Row geometry of the flush and dequantize for head_dim D: a token row is
+// D/8 lanes of 8 channels, so one wave covers 64/(D/8) rows per load (8, 4
+// or 2 for D = 64, 128, 256).  The lanes that hold the same 8 channels of
+// different rows are lane ^ 8 (D = 64 only), ^ 16 (D <= 128) and ^ 32.
+template <int D>
+struct RowGeo {
+    static constexpr int kLanesPerRow = D / 8;
+    static constexpr int kRowsPerWave = 64 / kLanesPerRow;
+};
+
+// lane ^ 8 within each row of 16: DPP row_ror:8
+__device__ __forceinline__ uint32_t lane_xor8(uint32_t v) {
+    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x128, 0xF, 0xF, false));
+}
+
+// min / max over the rows of a wave for each lane's channel block
+template <int D>
+__device__ __forceinline__ half2_t cross_rows_min(half2_t v) {
+    if constexpr (D == 64) v = hmin(v, as_h2(lane_xor8(as_u32(v))));
+    if constexpr (D <= 128) v = row_pair_min(v);
+    return half_min(v);
+}
+template <int D>
+__device__ __forceinline__ half2_t cross_rows_max(half2_t v) {
+    if constexpr (D == 64) v = hmax(v, as_h2(lane_xor8(as_u32(v))));
+    if constexpr (D <= 128) v = row_pair_max(v);
+    return half_max(v);
+}
+template <int D>
+__device__ __forceinline__ float cross_rows_min_f32(float v) {
+    if constexpr (D == 64) v = fminimum(v, __uint_as_float(lane_xor8(__float_as_uint(v))));
+    if constexpr (D <= 128) {
+        const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = fminimum(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    }
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fminimum(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+template <int D>
+__device__ __forceinline__ float cross_rows_max_f32(float v) {
+    if constexpr (D == 64) v = fmaximum(v, __uint_as_float(lane_xor8(__float_as_uint(v))));
+    if constexpr (D <= 128) {
+        const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = fmaximum(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    }
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaximum(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+
 // DPP quad permutations (lane ^ 1, lane ^ 2 within each group of 4 lanes).
 __device__ __forceinline__ uint32_t quad_xor1(uint32_t v) {
     return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0xB1, 0xF, 0xF, false));

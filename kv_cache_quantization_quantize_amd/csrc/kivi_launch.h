@@ -24,6 +24,7 @@ struct FlushArgs {
     int64_t recon_bh_stride;
     int bits;
     int group;                     // 32, 64 or 128
+    int head_dim;                  // 64, 128 or 256
     bool bf16;                     // x and recon hold bfloat16 (else fp16)
 };
 
@@ -39,6 +40,7 @@ struct DequantArgs {
     int bits;
     int kind;                      // KIVI_KEYS or KIVI_VALUES
     int group;                     // 32, 64 or 128
+    int head_dim;                  // 64, 128 or 256
     bool bf16;                     // out holds bfloat16 (else fp16)
 };
 

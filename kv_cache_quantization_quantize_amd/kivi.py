@@ -137,13 +137,13 @@ def _stream(stream=None) -> int:
     return int(s.cuda_stream)
 
 
-def _need_f16(t: torch.Tensor, name: str, allow_bf16: bool = False) -> None:
+def _need_f16(t: torch.Tensor, name: str, allow_bf16: bool = False, D: int = HEAD_DIM) -> None:
     if t.dtype != torch.float16 and not (allow_bf16 and t.dtype == torch.bfloat16):
         raise TypeError(f"{name} must be float16{' or bfloat16' if allow_bf16 else ''}, got {t.dtype}")
     if not t.is_cuda:
         raise TypeError(f"{name} must be a device tensor")
-    if t.dim() != 3 or t.shape[2] != HEAD_DIM or t.stride(2) != 1 or t.stride(1) != HEAD_DIM:
-        raise ValueError(f"{name} must be [BH][S][{HEAD_DIM}] with contiguous token rows")
+    if t.dim() != 3 or t.shape[2] != D or t.stride(2) != 1 or t.stride(1) != D:
+        raise ValueError(f"{name} must be [BH][S][{D}] with contiguous token rows")
 
 
 class Store:
@@ -153,11 +153,12 @@ class Store:
 
     def __init__(self, kind: int, BH: int, cap: int, bits: int = 4, device="cuda",
                  codes: torch.Tensor | None = None, scale: torch.Tensor | None = None,
-                 zero: torch.Tensor | None = None, group: int = GROUP):
+                 zero: torch.Tensor | None = None, group: int = GROUP, head_dim: int = HEAD_DIM):
         self.kind, self.BH, self.cap, self.bits, self.group = kind, BH, cap, bits, group
-        self.words = HEAD_DIM * bits // 32
-        meta = (BH, (cap + group - 1) // group, HEAD_DIM) if kind == KIVI_KEYS else \
-            (BH, cap, HEAD_DIM // group)
+        self.head_dim = head_dim
+        self.words = head_dim * bits // 32
+        meta = (BH, (cap + group - 1) // group, head_dim) if kind == KIVI_KEYS else \
+            (BH, cap, head_dim // group)
         self.codes = codes if codes is not None else torch.zeros((BH, cap, self.words),
                                                                  dtype=torch.int32, device=device)
         self.scale = scale if scale is not None else torch.zeros(meta, dtype=torch.float32, device=device)
@@ -166,16 +167,16 @@ class Store:
     def c(self) -> CStore:
         return CStore(self.codes.data_ptr(), self.scale.data_ptr(), self.zero.data_ptr(),
                       self.codes.stride(0), self.scale.stride(0), self.cap, self.bits,
-                      self.group, HEAD_DIM, self.kind)
+                      self.group, self.head_dim, self.kind)
 
     def nbytes(self) -> int:
         return (self.codes.numel() * 4 + self.scale.numel() * 4 + self.zero.numel() * 4)
 
 
 def _flush(fn_name, x: torch.Tensor, store: Store, dst_token: int, recon, stream):
-    _need_f16(x, "x", allow_bf16=True)
+    _need_f16(x, "x", allow_bf16=True, D=store.head_dim)
     if recon is not None:
-        _need_f16(recon, "recon", allow_bf16=True)
+        _need_f16(recon, "recon", allow_bf16=True, D=store.head_dim)
         if recon.dtype != x.dtype:
             raise TypeError("recon must have the dtype of x")
     if x.dtype == torch.bfloat16:
@@ -208,8 +209,8 @@ def dequantize(store: Store, token_begin: int, n_tokens: int, out: torch.Tensor 
     (kivi_dequantize_bf16 for a bfloat16 ``out`` / ``dtype``)."""
     BH = store.BH if BH is None else BH
     if out is None:
-        out = torch.empty((BH, n_tokens, HEAD_DIM), dtype=dtype, device=store.codes.device)
-    _need_f16(out, "out", allow_bf16=True)
+        out = torch.empty((BH, n_tokens, store.head_dim), dtype=dtype, device=store.codes.device)
+    _need_f16(out, "out", allow_bf16=True, D=store.head_dim)
     name = "kivi_dequantize_bf16" if out.dtype == torch.bfloat16 else "kivi_dequantize"
     st = store.c()
     rc = getattr(lib(), name)(ctypes.byref(st), BH, token_begin, n_tokens, out.data_ptr(),

@@ -61,7 +61,7 @@ def _keys(st, x=FAKE, BH=2, S=32, x_stride=32 * 128, off=0, recon=None, rstride=
 
 @pytest.mark.parametrize("case,want", [
     ("null_store", -1), ("bits3", -3), ("bits8", -3), ("group48", -3), ("group256", -3),
-    ("dim64", -3), ("group64_offset32", -2), ("group64", 0),
+    ("dim96", -3), ("dim64_group64", -3), ("dim64", 0), ("group64_offset32", -2), ("group64", 0),
     ("kind_values", -2), ("offset_not_group", -2), ("window_past_cap", -2),
     ("misaligned_x", -4), ("odd_stride", -4), ("null_x", -1), ("neg_S", -2),
     ("slab_overlap", -2), ("misaligned_codes", -4),
@@ -85,8 +85,13 @@ def test_key_flush_validation(case, want):
     elif case == "group64":
         st = _store(G=64)
         kw = dict(S=0)                             # valid: a zero-sized call launches nothing
+    elif case == "dim96":
+        st = _store(D=96)
+    elif case == "dim64_group64":
+        st = _store(D=64, G=64)
     elif case == "dim64":
         st = _store(D=64)
+        kw = dict(S=0)                             # valid: head_dim 64 with groups of 32
     elif case == "kind_values":
         st = _store(kind=kivi.KIVI_VALUES)
     elif case == "offset_not_group":
@@ -157,6 +162,8 @@ def test_attend_validation():
     assert call(wsb=ws - 4) == -5
     assert call(wsp=None) == -5
     assert call(wsp=FAKE + 16) == -4
+    # the attend reads head_dim 128 only
+    assert call(kk=_store(kivi.KIVI_KEYS, cap=64, D=64), vv=_store(kivi.KIVI_VALUES, cap=64, D=64)) == -3
     # key and value stores must share their group size (32, 64 or 128)
     assert call(kk=_store(kivi.KIVI_KEYS, cap=64, G=64), vv=_store(kivi.KIVI_VALUES, cap=64, G=32)) == -3
     assert call(kk=_store(kivi.KIVI_KEYS, cap=64, G=48), vv=_store(kivi.KIVI_VALUES, cap=64, G=48)) == -3

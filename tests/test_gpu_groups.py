@@ -122,3 +122,39 @@ def test_attend_over_wide_group_stores(case, G):
     for got in (out, out_v):
         err = float(np.max(np.abs(got.cpu().numpy().astype(np.float64) - ref)))
         assert err <= 2e-3, f"max-abs error {err:.3e}"
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("kind", ["keys", "values"])
+@pytest.mark.parametrize("Dh", [64, 256])
+@pytest.mark.parametrize("shape", [(3, 101, 160, 32, 7), (1, 64, 64, 0, 0), (2, 1, 64, 32, 1)],
+                         ids=lambda c: "BH%d-S%d-dst%d" % (c[0], c[1], c[3]))
+def test_other_head_dims(shape, Dh, kind, bits, fmt):
+    """head_dim 64 and 256 with groups of 32: flush (with fused
+    reconstruction) and dequantize bit-exact against the oracle."""
+    BH, S, cap, dst_k, dst_v = shape
+    dst = dst_k if kind == "keys" else dst_v
+    dtype = torch.bfloat16 if fmt == "bf16" else torch.float16
+    x = synth.kv_tensor(BH, S, Dh, keys=(kind == "keys"), seed=8500 + Dh + S, device="cuda", dtype=dtype)
+    k = KINDS[kind]
+    st = kivi.Store(k, BH, cap, bits, head_dim=Dh)
+    st.codes.fill_(CODE_SENTINEL)
+    st.scale.fill_(META_SENTINEL)
+    st.zero.fill_(META_SENTINEL)
+    okind = oracle.KEYS if k == kivi.KIVI_KEYS else oracle.VALUES
+    hs = oracle.Store(okind, BH, cap, Dh, bits, 32, fill_codes=CODE_SENTINEL, fill_meta=META_SENTINEL)
+    recon_full = torch.full((BH, S + 8, Dh), SENTINEL16, dtype=torch.int16, device="cuda").view(dtype)
+    note(f"head_dim {Dh} {fmt} flush {kind} bits={bits} BH={BH} S={S} cap={cap} dst={dst}")
+    (kivi.quantize_keys if kind == "keys" else kivi.quantize_values)(x, st, dst, recon_full[:, :S])
+    torch.cuda.synchronize()
+    ofn = oracle.quantize_keys if kind == "keys" else oracle.quantize_values
+    hrec = ofn(u16(x), hs, dst, want_recon=True, fmt=fmt)
+    what = f"D={Dh} {fmt} {kind} bits={bits} S={S} dst={dst}"
+    assert_store_equal(st, hs, what=what)
+    r = u16(recon_full)
+    assert_u16_equal(r[:, :S], hrec, what + " recon")
+    assert np.all(r[:, S:] == SENTINEL16), "recon written past the window"
+    out = kivi.dequantize(st, dst, S, dtype=dtype)
+    torch.cuda.synchronize()
+    assert_u16_equal(u16(out), hrec, what + " dequantize")

@@ -85,3 +85,32 @@ def test_attend_over_wide_group_stores_matches_torch_sdpa(orc, G):
     qt = torch.from_numpy(w(q)).reshape(B, Hq, 1, D)
     want = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt).reshape(B, Hq, D).numpy()
     assert np.max(np.abs(got - want)) < 1e-12
+
+
+@pytest.mark.parametrize("Dh", [64, 256])
+@pytest.mark.parametrize("bits", [2, 4])
+def test_other_head_dims_reduce_to_the_group_function(orc, Dh, bits):
+    """head_dim 64 and 256 with groups of 32: keys over 32 tokens of one of
+    the Dh channels, values over 32 channels of a token (Dh/32 groups)."""
+    rng = np.random.default_rng(Dh + bits)
+    BH, S, G = 2, 70, 32
+    x = _f16(rng.standard_normal((BH, S, Dh)) * np.where(rng.random(Dh) < 0.05, 10, 1))
+    ks = orc.Store(orc.KEYS, BH, 96, Dh, bits, G)
+    vs = orc.Store(orc.VALUES, BH, 96, Dh, bits, G)
+    rk = orc.quantize_keys(x, ks, 0)
+    rv = orc.quantize_values(x, vs, 0)
+    assert ks.codes.shape == (BH, 96, Dh * bits // 32) and vs.scale.shape == (BH, 96, Dh // G)
+    for bh in range(BH):
+        for g in range(3):
+            s0, s1 = G * g, min(G * g + G, S)
+            for d in (0, Dh // 2 + 1, Dh - 1):
+                sc, ze, q, rec = orc.quantize_group(x[bh, s0:s1, d], bits)
+                assert ks.scale[bh, g, d] == sc and ks.zero[bh, g, d] == ze
+                assert np.array_equal(rk[bh, s0:s1, d], rec)
+        for s in (0, 33, S - 1):
+            for j in range(Dh // G):
+                sc, ze, q, rec = orc.quantize_group(x[bh, s, G * j:G * j + G], bits)
+                assert vs.scale[bh, s, j] == sc and vs.zero[bh, s, j] == ze
+                assert np.array_equal(rv[bh, s, G * j:G * j + G], rec)
+    assert np.array_equal(orc.dequantize(ks, 0, S), rk)
+    assert np.array_equal(orc.dequantize(vs, 0, S), rv)
