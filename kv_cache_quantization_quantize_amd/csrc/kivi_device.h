@@ -1,13 +1,13 @@
 // kivi_device.h -- device-side helpers shared by the libkivi kernels
 // (internal to the library; not part of the C ABI).
 //
-// Fixed geometry of every kernel here: head_dim 128, wave64; group_size 32
-// (the flush and dequantize also take 64 and 128).  A "tile" is 32
-// consecutive tokens x 128 channels of one bh slab (8 KiB of fp16; a key
-// flush tile is one whole group of G tokens).  Lane l of the wave that owns a tile holds channels 8*(l%16) ..
-// 8*(l%16)+7 of tokens tile_start + (l/16) + 4*i, i = 0..7: each token row
-// of the tile is read by 16 lanes as one contiguous 256-byte segment, so the
-// wave reads the tile as 8 fully coalesced 1 KiB loads.
+// Geometry of the flush and dequantize (wave64): a "tile" is 32 consecutive
+// tokens (a key flush tile: one whole group of G tokens) x D channels of one
+// bh slab.  A token row is D/8 lanes of 8 channels (RowGeo below), so lane l
+// holds channels 8*(l % (D/8)) .. +7 of tokens tile_start + l/(D/8) + i*64/(D/8):
+// each token row is read as one contiguous segment of 2*D bytes and every
+// load instruction of the wave covers 1 KiB of consecutive rows.  At the
+// default head_dim 128 that is 16 lanes per row and 4 rows per load.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -17,21 +17,10 @@
 
 namespace kivi {
 
-constexpr int kHeadDim = 128;
-constexpr int kGroup = 32;
-constexpr int kLanesPerRow = 16;   // lanes covering one 128-channel token row
-constexpr int kRowsPerWave = 4;    // token rows covered by one wave at a time
-constexpr int kTokPerLane = 8;     // token rows held by one lane per tile
+constexpr int kHeadDim = 128;      // the attend's and the cache's head_dim
+constexpr int kGroup = 32;         // the cache's group size; the attend's smallest
 constexpr int kWavesPerBlock = 4;
 constexpr int kBlock = 64 * kWavesPerBlock;
-
-struct h8 {                        // 8 fp16 values as raw bits (one 16 B load)
-    uint4 v;
-};
-
-__device__ __forceinline__ float f16_to_f32(uint32_t bits16) {
-    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)));
-}
 
 // Exact widening of the low / high bfloat16 of a 32-bit word (bfloat16 is
 // binary32 with the low 16 fraction bits dropped).
@@ -41,13 +30,6 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // fp32 -> fp16, round to nearest even (the default rounding mode).
 __device__ __forceinline__ uint32_t f32_to_f16(float f) {
     return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
-}
-
-__device__ __forceinline__ void unpack8(const uint4 v, float (&f)[8]) {
-    f[0] = f16_to_f32(v.x & 0xffffu); f[1] = f16_to_f32(v.x >> 16);
-    f[2] = f16_to_f32(v.y & 0xffffu); f[3] = f16_to_f32(v.y >> 16);
-    f[4] = f16_to_f32(v.z & 0xffffu); f[5] = f16_to_f32(v.z >> 16);
-    f[6] = f16_to_f32(v.w & 0xffffu); f[7] = f16_to_f32(v.w >> 16);
 }
 
 // Streaming accesses: the flush and dequantize read their inputs and write
@@ -112,24 +94,11 @@ __device__ __forceinline__ half2_t half_max(half2_t v) {
 }
 
 // fp32 forms of the same: IEEE minimum/maximum (v_minimum3_f32 /
-// v_maximum3_f32 for three inputs) and the reduction over the four rows.
+// v_maximum3_f32 for three inputs).
 __device__ __forceinline__ float fminimum(float a, float b) { return __builtin_elementwise_minimum(a, b); }
 __device__ __forceinline__ float fmaximum(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 __device__ __forceinline__ float fmin3(float a, float b, float c) { return fminimum(fminimum(a, b), c); }
 __device__ __forceinline__ float fmax3(float a, float b, float c) { return fmaximum(fmaximum(a, b), c); }
-__device__ __forceinline__ float rows_min_f32(float v) {
-    auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = fminimum(__uint_as_float(p[0]), __uint_as_float(p[1]));
-    p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fminimum(__uint_as_float(p[0]), __uint_as_float(p[1]));
-}
-__device__ __forceinline__ float rows_max_f32(float v) {
-    auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = fmaximum(__uint_as_float(p[0]), __uint_as_float(p[1]));
-    p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fmaximum(__uint_as_float(p[0]), __uint_as_float(p[1]));
-}
-
 // Word k (0..3) of a 16-byte load: channels 2k and 2k+1 of the lane's 8.
 __device__ __forceinline__ uint32_t word_of(const uint4& v, int k) {
     return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
