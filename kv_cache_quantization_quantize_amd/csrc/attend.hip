@@ -29,6 +29,8 @@
 // Grid: one 64-lane wave per (sequence, kv head, split of the token axis);
 // each wave walks its split in 32-token steps, one key group per step, with
 // the step's key and value metadata staged through LDS.
+#include <algorithm>
+
 #include "kivi_device.h"
 #include "kivi_launch.h"
 
@@ -706,6 +708,15 @@ AttendPlan plan_attend(int64_t B, int Hq, int Hkv, int64_t n_quant, int64_t n_re
         const int64_t rounds = (total + per_round * kMaxStepsPerWave - 1) / (per_round * kMaxStepsPerWave);
         spw = (total + rounds * per_round - 1) / (rounds * per_round);
     }
+    // Small and mid-size calls take fewer, longer waves: each wave pays a
+    // fixed cost (query load, LDS setup, its partial and its share of the
+    // combine), and about 700 waves with two steps of loads in flight each
+    // already keep these sizes at their best.  Measured per call on MI355X
+    // (steps per wave -> us): B=1 x 16384 tokens 2 -> 19.1, 6 -> 16.1;
+    // B=4 x 2048: 1 -> 13.3, 3 -> 11.9; B=16 x 2048: 3 -> 23.0, 9 -> 19.9;
+    // B=4 x 16384: 6 -> 31.2, 9 -> 30.3; B=32 x 2048: 6 -> 31.7, 9 -> 31.4.
+    const int64_t longer = (total + 699) / 700;
+    spw = std::max(spw, std::min<int64_t>(9, longer));
     AttendPlan p;
     p.steps_q = steps_q;
     p.steps_per_wave = spw;
