@@ -47,6 +47,7 @@ SRC_PATH = os.path.join(_HERE, "kivi_oracle.c")
 KEYS = 0
 VALUES = 1
 FMT = {"f16": 0, "bf16": 1}        # 16-bit storage format of inputs and reconstructions
+META = {"f32": 0, "f16": 1}       # storage format of a store's scale and zero
 
 # -ffp-contract=off keeps a*b+c as two roundings; no -ffast-math anywhere.
 CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
@@ -104,6 +105,12 @@ def lib():
         L.orc_quantize_values.argtypes = flush_args
         L.orc_quantize_keys.restype = _int
         L.orc_quantize_values.restype = _int
+        L.orc_quantize_group_meta.argtypes = [_u16p, _int, _int, _int, _int, _f32p, _f32p, _u8p,
+                                              _u16p]
+        L.orc_quantize_keys_meta.argtypes = flush_args + [_int, _int]
+        L.orc_quantize_values_meta.argtypes = flush_args + [_int, _int]
+        L.orc_quantize_keys_meta.restype = _int
+        L.orc_quantize_values_meta.restype = _int
         L.orc_quantize_keys_fmt.argtypes = flush_args + [_int]
         L.orc_quantize_values_fmt.argtypes = flush_args + [_int]
         L.orc_quantize_keys_fmt.restype = _int
@@ -171,18 +178,21 @@ def f32_to_bf16(f) -> np.ndarray:
 
 
 # ------------------------------------------------------------------ groups
-def quantize_group(x, bits: int, fmt: str = "f16"):
+def quantize_group(x, bits: int, fmt: str = "f16", meta: str = "f32"):
     """-> (scale fp32, zero fp32, codes uint8[n], recon bits uint16[n]) for
-    n values stored as fp16 or bf16 bit patterns (``fmt``)."""
+    n values stored as fp16 or bf16 bit patterns (``fmt``).  With ``meta``
+    "f16" the scale and zero are the binary16-rounded values (widened) that
+    the codes and the reconstruction were taken with."""
     x = _as_u16(x).reshape(-1)
     n = x.size
+    assert meta == "f32" or fmt == "f16", "binary16 metadata is for fp16 inputs"
     sc = np.zeros(1, np.float32)
     ze = np.zeros(1, np.float32)
     q = np.zeros(n, np.uint8)
     rec = np.zeros(n, np.uint16)
-    lib().orc_quantize_group_fmt(_ptr(x, ctypes.c_uint16), n, bits, FMT[fmt], _ptr(sc, ctypes.c_float),
-                                 _ptr(ze, ctypes.c_float), _ptr(q, ctypes.c_uint8),
-                                 _ptr(rec, ctypes.c_uint16))
+    lib().orc_quantize_group_meta(_ptr(x, ctypes.c_uint16), n, bits, FMT[fmt], META[meta],
+                                  _ptr(sc, ctypes.c_float), _ptr(ze, ctypes.c_float),
+                                  _ptr(q, ctypes.c_uint8), _ptr(rec, ctypes.c_uint16))
     return sc[0], ze[0], q, rec
 
 
@@ -193,12 +203,17 @@ def dequantize_one(q: int, scale, zero, fmt: str = "f16") -> int:
 
 # ------------------------------------------------------------------ store
 class Store:
-    """Host packed store in the documented layout (see kivi_oracle.h)."""
+    """Host packed store in the documented layout (see kivi_oracle.h).
+
+    ``meta`` is the storage format of scale and zero ("f32" or "f16"); the
+    arrays are float32 either way, holding the binary16 values widened for
+    "f16" (``meta_bits`` gives their bit patterns)."""
 
     def __init__(self, kind: int, BH: int, cap: int, D: int = 128, bits: int = 4,
-                 G: int = 32, fill_codes: int = 0, fill_meta: float = 0.0):
-        assert kind in (KEYS, VALUES)
+                 G: int = 32, fill_codes: int = 0, fill_meta: float = 0.0, meta: str = "f32"):
+        assert kind in (KEYS, VALUES) and meta in META
         self.kind, self.BH, self.cap, self.D, self.bits, self.G = kind, BH, cap, D, bits, G
+        self.meta = meta
         self.words = D * bits // 32
         self.codes = np.full((BH, cap, self.words), fill_codes, np.uint32)
         if kind == KEYS:
@@ -213,6 +228,7 @@ class Store:
         sub = Store.__new__(Store)
         sub.kind, sub.BH, sub.cap, sub.D, sub.bits, sub.G = self.kind, hi - lo, self.cap, self.D, \
             self.bits, self.G
+        sub.meta = self.meta
         sub.words = self.words
         sub.codes, sub.scale, sub.zero = self.codes[lo:hi], self.scale[lo:hi], self.zero[lo:hi]
         return sub
@@ -225,6 +241,11 @@ class Store:
     def meta_bh_stride(self) -> int:
         return self.scale.shape[1] * self.scale.shape[2]
 
+    def meta_bits(self):
+        """(scale, zero) as binary16 bit patterns (exact for an "f16" store)."""
+        assert self.meta == "f16"
+        return f32_to_f16(self.scale), f32_to_f16(self.zero)
+
 
 def _flush(fn, x, store: Store, dst_token: int, want_recon: bool, fmt: str):
     x = _as_u16(x)
@@ -235,7 +256,7 @@ def _flush(fn, x, store: Store, dst_token: int, want_recon: bool, fmt: str):
             _ptr(store.codes, ctypes.c_uint32), store.codes_bh_stride,
             _ptr(store.scale, ctypes.c_float), _ptr(store.zero, ctypes.c_float),
             store.meta_bh_stride, dst_token,
-            _ptr(recon, ctypes.c_uint16), S * D, FMT[fmt])
+            _ptr(recon, ctypes.c_uint16), S * D, FMT[fmt], META[store.meta])
     if rc != 0:
         raise ValueError("oracle rejected the flush arguments")
     return recon
@@ -245,14 +266,14 @@ def quantize_keys(x, store: Store, dst_token: int = 0, want_recon: bool = True, 
     """Per-channel key flush of x[BH][S][D] (fp16 or bf16 bits, ``fmt``) into
     ``store`` at ``dst_token``; the reconstruction comes back in ``fmt``."""
     assert store.kind == KEYS
-    return _flush(lib().orc_quantize_keys_fmt, x, store, dst_token, want_recon, fmt)
+    return _flush(lib().orc_quantize_keys_meta, x, store, dst_token, want_recon, fmt)
 
 
 def quantize_values(x, store: Store, dst_token: int = 0, want_recon: bool = True, fmt: str = "f16"):
     """Per-token value flush of x[BH][S][D] (fp16 or bf16 bits, ``fmt``) into
     ``store`` at ``dst_token``; the reconstruction comes back in ``fmt``."""
     assert store.kind == VALUES
-    return _flush(lib().orc_quantize_values_fmt, x, store, dst_token, want_recon, fmt)
+    return _flush(lib().orc_quantize_values_meta, x, store, dst_token, want_recon, fmt)
 
 
 def dequantize(store: Store, t0: int, n: int, fmt: str = "f16") -> np.ndarray:

@@ -174,8 +174,8 @@ void orc_f32_to_f16_array(const float *f, uint16_t *h, int64_t n)
 /* multiply, add, in that order, each as its own fp32 operation.      */
 /* ------------------------------------------------------------------ */
 
-void orc_quantize_group_fmt(const uint16_t *x, int n, int bits, int fmt,
-                            float *scale_out, float *zero_out, uint8_t *q, uint16_t *recon)
+void orc_quantize_group_meta(const uint16_t *x, int n, int bits, int fmt, int meta,
+                             float *scale_out, float *zero_out, uint8_t *q, uint16_t *recon)
 {
     const widen_fn widen = widen_of(fmt);
     /* widen exactly to fp32 (the Metal kernels read float(x[...]),
@@ -194,8 +194,17 @@ void orc_quantize_group_fmt(const uint16_t *x, int n, int bits, int fmt,
 
     const float levels = (float)((1 << bits) - 1);
     const float range = mx - mn;
-    const float scale = range / levels;
-    const float zero = mn;
+    float scale = range / levels;
+    float zero = mn;
+    if (meta == ORC_META_F16) {
+        /* Binary16 metadata: the pair is stored rounded to nearest even
+           binary16, and the codes and the reconstruction use the stored
+           values, so that a reader of the store reproduces them.  (The zero
+           of an fp16 group is an fp16 value already; a scale below 2^-25
+           becomes 0 and the group codes as constant.) */
+        scale = orc_f16_to_f32(orc_f32_to_f16(scale));
+        zero = orc_f16_to_f32(orc_f32_to_f16(zero));
+    }
     *scale_out = scale;
     *zero_out = zero;
 
@@ -219,6 +228,12 @@ void orc_quantize_group_fmt(const uint16_t *x, int n, int bits, int fmt,
         q[i] = (uint8_t)code;
         if (recon) recon[i] = orc_dequantize_one_fmt((uint32_t)code, scale, zero, fmt);
     }
+}
+
+void orc_quantize_group_fmt(const uint16_t *x, int n, int bits, int fmt,
+                            float *scale_out, float *zero_out, uint8_t *q, uint16_t *recon)
+{
+    orc_quantize_group_meta(x, n, bits, fmt, ORC_META_F32, scale_out, zero_out, q, recon);
 }
 
 void orc_quantize_group(const uint16_t *x, int n, int bits,
@@ -268,14 +283,15 @@ static void put_code(uint32_t *row_words, int64_t d, int bits, uint32_t code)
    group uses its real tokens only; "Three ways to be off by one bit", item 3,
    pads it with copies of the last real token, which leaves min and max --
    and so every result -- unchanged. */
-int orc_quantize_keys_fmt(const uint16_t *x, int64_t BH, int64_t S, int64_t D,
-                          int64_t x_bh_stride, int bits, int G,
-                          uint32_t *codes, int64_t codes_bh_stride,
-                          float *scale, float *zero, int64_t meta_bh_stride,
-                          int64_t dst_token,
-                          uint16_t *recon, int64_t recon_bh_stride, int fmt)
+int orc_quantize_keys_meta(const uint16_t *x, int64_t BH, int64_t S, int64_t D,
+                           int64_t x_bh_stride, int bits, int G,
+                           uint32_t *codes, int64_t codes_bh_stride,
+                           float *scale, float *zero, int64_t meta_bh_stride,
+                           int64_t dst_token,
+                           uint16_t *recon, int64_t recon_bh_stride, int fmt, int meta)
 {
     if (check_common(BH, S, D, bits, G) != 0) return -1;
+    if (meta != ORC_META_F32 && (meta != ORC_META_F16 || fmt != ORC_F16)) return -1;
     if (dst_token < 0 || dst_token % G != 0) return -1;
     const int64_t words = D * bits / 32;
     const int64_t NG = (S + G - 1) / G;
@@ -298,7 +314,7 @@ int orc_quantize_keys_fmt(const uint16_t *x, int64_t BH, int64_t S, int64_t D,
                 for (int i = 0; i < n; ++i)
                     grp[i] = x[bh * x_bh_stride + (s0 + i) * D + d];
                 float sc, ze;
-                orc_quantize_group_fmt(grp, n, bits, fmt, &sc, &ze, q, recon ? rec : NULL);
+                orc_quantize_group_meta(grp, n, bits, fmt, meta, &sc, &ze, q, recon ? rec : NULL);
                 scale[bh * meta_bh_stride + meta_row * D + d] = sc;
                 zero[bh * meta_bh_stride + meta_row * D + d] = ze;
                 for (int i = 0; i < n; ++i) {
@@ -316,14 +332,15 @@ int orc_quantize_keys_fmt(const uint16_t *x, int64_t BH, int64_t S, int64_t D,
 /* Values, per token: [Metal post] "What we're actually optimizing" (values
    get one scale per token over a group of channels) and "Kernel B" (the
    group of token s is channels [j*G, min(j*G+G, D)) of that token). */
-int orc_quantize_values_fmt(const uint16_t *x, int64_t BH, int64_t S, int64_t D,
-                            int64_t x_bh_stride, int bits, int G,
-                            uint32_t *codes, int64_t codes_bh_stride,
-                            float *scale, float *zero, int64_t meta_bh_stride,
-                            int64_t dst_token,
-                            uint16_t *recon, int64_t recon_bh_stride, int fmt)
+int orc_quantize_values_meta(const uint16_t *x, int64_t BH, int64_t S, int64_t D,
+                             int64_t x_bh_stride, int bits, int G,
+                             uint32_t *codes, int64_t codes_bh_stride,
+                             float *scale, float *zero, int64_t meta_bh_stride,
+                             int64_t dst_token,
+                             uint16_t *recon, int64_t recon_bh_stride, int fmt, int meta)
 {
     if (check_common(BH, S, D, bits, G) != 0) return -1;
+    if (meta != ORC_META_F32 && (meta != ORC_META_F16 || fmt != ORC_F16)) return -1;
     if (dst_token < 0) return -1;
     const int64_t words = D * bits / 32;
     const int64_t NGD = (D + G - 1) / G;
@@ -341,7 +358,7 @@ int orc_quantize_values_fmt(const uint16_t *x, int64_t BH, int64_t S, int64_t D,
                 const int64_t d1 = (d0 + G < D) ? d0 + G : D;
                 const int n = (int)(d1 - d0);
                 float sc, ze;
-                orc_quantize_group_fmt(xrow + d0, n, bits, fmt, &sc, &ze, q, recon ? rec : NULL);
+                orc_quantize_group_meta(xrow + d0, n, bits, fmt, meta, &sc, &ze, q, recon ? rec : NULL);
                 scale[bh * meta_bh_stride + (dst_token + s) * NGD + j] = sc;
                 zero[bh * meta_bh_stride + (dst_token + s) * NGD + j] = ze;
                 for (int i = 0; i < n; ++i) {
@@ -353,6 +370,30 @@ int orc_quantize_values_fmt(const uint16_t *x, int64_t BH, int64_t S, int64_t D,
     }
     free(q); free(rec);
     return 0;
+}
+
+int orc_quantize_keys_fmt(const uint16_t *x, int64_t BH, int64_t S, int64_t D,
+                          int64_t x_bh_stride, int bits, int G,
+                          uint32_t *codes, int64_t codes_bh_stride,
+                          float *scale, float *zero, int64_t meta_bh_stride,
+                          int64_t dst_token,
+                          uint16_t *recon, int64_t recon_bh_stride, int fmt)
+{
+    return orc_quantize_keys_meta(x, BH, S, D, x_bh_stride, bits, G, codes, codes_bh_stride,
+                                  scale, zero, meta_bh_stride, dst_token, recon, recon_bh_stride,
+                                  fmt, ORC_META_F32);
+}
+
+int orc_quantize_values_fmt(const uint16_t *x, int64_t BH, int64_t S, int64_t D,
+                            int64_t x_bh_stride, int bits, int G,
+                            uint32_t *codes, int64_t codes_bh_stride,
+                            float *scale, float *zero, int64_t meta_bh_stride,
+                            int64_t dst_token,
+                            uint16_t *recon, int64_t recon_bh_stride, int fmt)
+{
+    return orc_quantize_values_meta(x, BH, S, D, x_bh_stride, bits, G, codes, codes_bh_stride,
+                                    scale, zero, meta_bh_stride, dst_token, recon, recon_bh_stride,
+                                    fmt, ORC_META_F32);
 }
 
 int orc_quantize_keys(const uint16_t *x, int64_t BH, int64_t S, int64_t D,

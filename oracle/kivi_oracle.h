@@ -67,6 +67,27 @@ int orc_dequantize_fmt(int kind, const uint32_t *codes, int64_t codes_bh_stride,
                        int64_t t0, int64_t n,
                        uint16_t *out, int64_t out_bh_stride, int fmt);
 
+/* Storage format of a store's scale and zero for the _meta calls: binary32,
+   or binary16 (fp16 inputs only).  The store arrays stay float either way:
+   with ORC_META_F16 they hold the binary16 values widened (exactly), and
+   the codes and reconstructions are taken with those rounded values. */
+enum { ORC_META_F32 = 0, ORC_META_F16 = 1 };
+
+void orc_quantize_group_meta(const uint16_t *x, int n, int bits, int fmt, int meta,
+                             float *scale, float *zero, uint8_t *q, uint16_t *recon);
+int orc_quantize_keys_meta(const uint16_t *x, int64_t BH, int64_t S, int64_t D,
+                           int64_t x_bh_stride, int bits, int G,
+                           uint32_t *codes, int64_t codes_bh_stride,
+                           float *scale, float *zero, int64_t meta_bh_stride,
+                           int64_t dst_token,
+                           uint16_t *recon, int64_t recon_bh_stride, int fmt, int meta);
+int orc_quantize_values_meta(const uint16_t *x, int64_t BH, int64_t S, int64_t D,
+                             int64_t x_bh_stride, int bits, int G,
+                             uint32_t *codes, int64_t codes_bh_stride,
+                             float *scale, float *zero, int64_t meta_bh_stride,
+                             int64_t dst_token,
+                             uint16_t *recon, int64_t recon_bh_stride, int fmt, int meta);
+
 /* One quantization group of n fp16 values.  Writes scale, zero, the n codes
    and the n fp16 reconstructions (recon may be NULL). */
 void orc_quantize_group(const uint16_t *x, int n, int bits,

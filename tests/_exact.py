@@ -132,7 +132,7 @@ def f32_bits(v: Fraction) -> int:
 
 
 def quantize_group(xbits, bits: int, *, ties="even", quotient="fp32",
-                   recon_fma=False, fmt="f16"):
+                   recon_fma=False, fmt="f16", meta="f32"):
     """Emulate one group.  The keyword arguments select deliberately wrong
     variants (used to show that a fixture discriminates):
       ties="away"          round half away from zero instead of half to even
@@ -141,6 +141,10 @@ def quantize_group(xbits, bits: int, *, ties="even", quotient="fp32",
       quotient="rcp"       binary32 (x-zero) * binary32(1/scale)
       recon_fma=True       one rounding for q*scale+zero (a fused multiply-add)
       fmt="bf16"           inputs and reconstructions in bfloat16
+      meta="f16"           scale and zero stored as binary16 (the reading:
+                           codes and reconstruction use the stored values)
+      meta="f16_store_only"  wrong: codes from the binary32 scale, only the
+                           reconstruction from the binary16 one
     Returns (scale, zero, codes, recon_bits) with scale/zero as Fractions."""
     value, to_bits = (f16_value, rnd16_bits) if fmt == "f16" else (bf16_value, rndbf16_bits)
     xs = [value(b) for b in xbits]
@@ -149,18 +153,22 @@ def quantize_group(xbits, bits: int, *, ties="even", quotient="fp32",
     rng = rnd32(mx - mn)
     scale = rnd32(rng / levels)
     zero = mn
+    code_scale = scale
+    if meta in ("f16", "f16_store_only"):
+        scale, zero = rnd16(scale), rnd16(zero)
+        code_scale = scale if meta == "f16" else code_scale
     codes, recon = [], []
     for x in xs:
-        if scale == 0:
+        if code_scale == 0:
             q = 0
         else:
             t = rnd32(x - zero)
             if quotient == "fp32":
-                u = rnd32(t / scale)
+                u = rnd32(t / code_scale)
             elif quotient == "exact":
-                u = t / scale
+                u = t / code_scale
             elif quotient == "rcp":
-                u = rnd32(t * rnd32(1 / scale))
+                u = rnd32(t * rnd32(1 / code_scale))
             else:
                 raise ValueError(quotient)
             if ties == "even":
