@@ -34,11 +34,21 @@
  *   codes  uint32 [BH][cap][head_dim*bits/32]  token-major; the code of
  *          channel d of token t sits in word (t, d / (32/bits)) at bit
  *          offset bits * (d % (32/bits)), least significant first.
- *   keys   scale, zero fp32 [BH][cap/G][head_dim]   one pair per
+ *   keys   scale, zero [BH][cap/G][head_dim]   one pair per
  *          (token group, channel): per-channel quantization.
- *   values scale, zero fp32 [BH][cap][head_dim/G]   one pair per
+ *   values scale, zero [BH][cap][head_dim/G]   one pair per
  *          (token, channel group): per-token quantization.
  *   zero is the group minimum (a float offset, not an integer zero point).
+ *   scale and zero are binary32 (meta_format KIVI_META_F32, the default)
+ *   or binary16 (KIVI_META_F16).  The pages leave this precision open;
+ *   [Benchmarks] "KV-Cache Kernel Roofline" reports KV-compression ratios,
+ *   which depend on it.  A binary16 store holds the binary32 scale and zero
+ *   rounded to nearest even, and its codes and reconstructions are taken
+ *   with those stored values (so a reader of the store reproduces them
+ *   exactly); a scale that rounds to 0 codes its group as constant, and a
+ *   code past 2^bits - 1 is clipped.  It halves the metadata bytes (4-bit,
+ *   groups of 32: 5 bits per element instead of 6) and is supported for
+ *   fp16 caches at head_dim 128, by the flush, dequantize and attend calls.
  */
 #ifndef KIVI_H
 #define KIVI_H
@@ -66,20 +76,23 @@ enum {
 };
 
 enum { KIVI_KEYS = 0, KIVI_VALUES = 1 };
+enum { KIVI_META_F32 = 0, KIVI_META_F16 = 1 };
 
 /* A packed store (see the layout above).  The struct itself lives in host
  * memory and is only read during the call; the arrays are device memory. */
 typedef struct kivi_store {
     uint32_t* codes;           /* [BH][cap][head_dim*bits/32]                 */
-    float*    scale;           /* keys [BH][cap/G][D]; values [BH][cap][D/G]  */
-    float*    zero;            /* same shape as scale                         */
+    void*     scale;           /* keys [BH][cap/G][D]; values [BH][cap][D/G];
+                                  float, or binary16 bits (meta_format)       */
+    void*     zero;            /* same shape and format as scale              */
     int64_t   codes_bh_stride; /* uint32 words between bh slabs (>= cap*row) */
-    int64_t   meta_bh_stride;  /* floats between bh slabs                     */
+    int64_t   meta_bh_stride;  /* scale elements between bh slabs             */
     int64_t   cap;             /* token capacity of each slab                 */
     int32_t   bits;            /* 2 or 4                                      */
     int32_t   group_size;      /* 32, 64 or 128                               */
     int32_t   head_dim;        /* 64, 128 or 256                              */
     int32_t   kind;            /* KIVI_KEYS or KIVI_VALUES                    */
+    int32_t   meta_format;     /* KIVI_META_F32 or KIVI_META_F16              */
 } kivi_store;
 
 /*

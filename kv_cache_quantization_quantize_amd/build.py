@@ -10,10 +10,12 @@ Always recompiles.  Flags that decide what the kernels compute:
 """
 from __future__ import annotations
 
+import concurrent.futures
 import glob
 import os
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -23,7 +25,7 @@ LIB_PATH = os.path.join(PKG, "libkivi.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-ffp-contract=off", "-Wall", "-Wno-unused-command-line-argument",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # MFMA accumulators in VGPRs: the attend's accumulators live across a loop
@@ -37,13 +39,28 @@ def sources() -> list[str]:
 
 
 def build(verbose: bool = False, extra: list[str] | None = None) -> str:
+    """Compiles every source to an object in parallel (one compiler process
+    per file), then links the shared library."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, *(extra or []), "-I", INCLUDE, "-I", CSRC,
-           "-o", tmp, *sources()]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
+    srcs = sources()
+    with tempfile.TemporaryDirectory(prefix="kivi_build_") as obj_dir:
+        objs = [os.path.join(obj_dir, os.path.basename(src) + ".o") for src in srcs]
+        cmds = [[hipcc, *HIPCC_FLAGS, *(extra or []), "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
+                for src, obj in zip(srcs, objs)]
+        if verbose:
+            for cmd in cmds:
+                print(" ".join(cmd), flush=True)
+        jobs = max(1, min(len(cmds), os.cpu_count() or 1, 16))
+        with concurrent.futures.ThreadPoolExecutor(jobs) as pool:
+            codes = list(pool.map(lambda c: subprocess.run(c).returncode, cmds))
+        failed = [src for src, rc in zip(srcs, codes) if rc != 0]
+        if failed:
+            raise subprocess.CalledProcessError(1, "hipcc -c " + " ".join(failed))
+        link = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+        if verbose:
+            print(" ".join(link), flush=True)
+        subprocess.run(link, check=True)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

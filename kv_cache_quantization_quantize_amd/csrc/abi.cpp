@@ -47,16 +47,22 @@ bool geometry_ok(int32_t D, int32_t G) {
     return (D == 64 || D == 256) && G == 32;
 }
 
+bool meta16(const kivi_store* st) { return st->meta_format == KIVI_META_F16; }
+
 // Checks a store and that tokens [t0, t0 + n) of slabs [0, BH) lie inside it.
+// Binary16 scale/zero are supported at head_dim 128.
 int check_store(const kivi_store* st, int kind, int64_t BH, int64_t t0, int64_t n) {
     if (!st) return KIVI_ERR_NULL;
     if (st->kind != KIVI_KEYS && st->kind != KIVI_VALUES) return KIVI_ERR_UNSUPPORTED;
     if (kind >= 0 && st->kind != kind) return KIVI_ERR_SHAPE;
     if (st->bits != 2 && st->bits != 4) return KIVI_ERR_UNSUPPORTED;
     if (!geometry_ok(st->head_dim, st->group_size)) return KIVI_ERR_UNSUPPORTED;
+    if (st->meta_format != KIVI_META_F32 && st->meta_format != KIVI_META_F16) return KIVI_ERR_UNSUPPORTED;
+    if (meta16(st) && st->head_dim != kD) return KIVI_ERR_UNSUPPORTED;
     if (!st->codes || !st->scale || !st->zero) return KIVI_ERR_NULL;
     if (!aligned16(st->codes) || !aligned16(st->scale) || !aligned16(st->zero)) return KIVI_ERR_ALIGN;
-    if (st->codes_bh_stride % 4 != 0 || st->meta_bh_stride % 4 != 0) return KIVI_ERR_ALIGN;
+    // slab strides of whole 16-byte units
+    if (st->codes_bh_stride % 4 != 0 || st->meta_bh_stride % (meta16(st) ? 8 : 4) != 0) return KIVI_ERR_ALIGN;
     if (st->cap < 0 || t0 < 0 || n < 0 || t0 > st->cap - n) return KIVI_ERR_SHAPE;
     if (BH > 1) {
         if (st->codes_bh_stride < st->cap * words_per_token(st)) return KIVI_ERR_SHAPE;
@@ -80,6 +86,7 @@ int flush(bool keys, bool bf16, const uint16_t* x, int64_t BH, int64_t S, int64_
     int rc = check_store(dst, keys ? KIVI_KEYS : KIVI_VALUES, BH, dst_token, S);
     if (rc != KIVI_OK) return rc;
     if (keys && dst_token % dst->group_size != 0) return KIVI_ERR_SHAPE;
+    if (bf16 && meta16(dst)) return KIVI_ERR_UNSUPPORTED;     // binary16 metadata is for fp16 caches
     if (BH == 0 || S == 0) return KIVI_OK;
     if ((rc = check_f16_tensor(x, BH, S, x_bh_stride, dst->head_dim)) != KIVI_OK) return rc;
     if (recon && (rc = check_f16_tensor(recon, BH, S, recon_bh_stride, dst->head_dim)) != KIVI_OK) return rc;
@@ -95,6 +102,7 @@ int flush(bool keys, bool bf16, const uint16_t* x, int64_t BH, int64_t S, int64_
     a.group = dst->group_size;
     a.head_dim = dst->head_dim;
     a.bf16 = bf16;
+    a.meta16 = meta16(dst);
     return finish(keys ? kivi::launch_key_flush(a, stream) : kivi::launch_value_flush(a, stream));
 }
 
@@ -131,6 +139,7 @@ static int dequantize(bool bf16, const kivi_store* src, int64_t BH, int64_t toke
     if (BH < 0 || n_tokens < 0) return KIVI_ERR_SHAPE;
     int rc = check_store(src, -1, BH, token_begin, n_tokens);
     if (rc != KIVI_OK) return rc;
+    if (bf16 && meta16(src)) return KIVI_ERR_UNSUPPORTED;
     if (BH == 0 || n_tokens == 0) return KIVI_OK;
     if ((rc = check_f16_tensor(out, BH, n_tokens, out_bh_stride, src->head_dim)) != KIVI_OK) return rc;
     const int64_t tiles = BH * ((n_tokens + 31) / 32);
@@ -141,6 +150,7 @@ static int dequantize(bool bf16, const kivi_store* src, int64_t BH, int64_t toke
     a.BH = BH; a.t0 = token_begin; a.n = n_tokens; a.out = out; a.out_bh_stride = out_bh_stride;
     a.bits = src->bits; a.kind = src->kind; a.group = src->group_size; a.head_dim = src->head_dim;
     a.bf16 = bf16;
+    a.meta16 = meta16(src);
     return finish(kivi::launch_dequantize(a, stream));
 }
 
@@ -191,7 +201,7 @@ int decode_attend_entry(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
     if (rc != KIVI_OK) return rc;
     if ((rc = check_store(v, KIVI_VALUES, slabs, 0, n_quant)) != KIVI_OK) return rc;
     if (k->bits != v->bits) return KIVI_ERR_SHAPE;
-    if (k->group_size != v->group_size) return KIVI_ERR_UNSUPPORTED;
+    if (k->group_size != v->group_size || k->meta_format != v->meta_format) return KIVI_ERR_UNSUPPORTED;
     if (k->head_dim != kD || v->head_dim != kD) return KIVI_ERR_UNSUPPORTED;
     if (B == 0) return KIVI_OK;
     if (!q || !out) return KIVI_ERR_NULL;
@@ -224,6 +234,7 @@ int decode_attend_entry(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
     a.seq_n_quant = seq_n_quant; a.seq_n_res = seq_n_res;
     a.softmax_scale = softmax_scale; a.out = out;
     a.workspace = workspace; a.bits = k->bits; a.group = k->group_size;
+    a.meta16 = meta16(k);
     return finish(kivi::launch_decode_attend(a, plan, stream));
 }
 

@@ -158,10 +158,11 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 }
 
 // A step start whose every load lies past the buffers' extent: the ABI
-// keeps n_quant below 2^24 tokens, so the extents stay below 2^30 bytes of
-// codes and 2^28 of metadata, while this start puts code offsets at
-// 2^25 x 32 or 64 B and metadata offsets at 2^25 x 16 B (lane and
-// instruction offsets keep all of them below 2^32).
+// keeps n_quant below 2^24 tokens, and every buffer's offset for token t is
+// t times its bytes per token (key metadata: per token of the group), so a
+// start at 2^25 lands at twice any buffer's extent.  The largest such
+// offsets are 2^25 x 64 B of codes and 2^25 x 16 B of binary32 metadata;
+// lane and instruction offsets keep all of them below 2^32.
 constexpr uint32_t kFarToken = 1u << 25;
 
 struct StoreView {
@@ -170,7 +171,7 @@ struct StoreView {
 };
 
 // Byte offsets of a lane's loads at step t0 = 0; a step adds t0 times the
-// bytes per token (key metadata: t0 / 32 groups of 512 B = 16 t0).
+// bytes per token (key metadata: t0 / G groups of 128 pairs).
 struct LaneOffsets {
     uint32_t k;             // key codes of token n, the lane's 32 channels
     uint32_t v;             // value code word of token 4q, the lane's 8 channels
@@ -182,24 +183,32 @@ struct LaneOffsets {
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ float2 as_float2(u32x2 v) {
-    return make_float2(__uint_as_float(v.x), __uint_as_float(v.y));
-}
-
 // Loads of one 32-token step of store tokens, issued one step ahead of the
 // compute that uses them.
+// Scale and zero stay as loaded (binary32 pairs, or binary16 pairs in the
+// low word) until the step that uses them, so that issuing a prefetch never
+// waits on an earlier load.
 struct StepLoad {
     uint32_t kw[2][4];      // key code words of token t0 + 16*blk + n (lane's 32 channels)
-    float2 ks, kz;          // key scale / zero of channels 2l, 2l+1 of the step's group
-    float2 vs, vz;          // value scale / zero of token t0 + (l & 31), groups 2(l>>5), +1
+    u32x2 ks, kz;           // key scale / zero of channels 2l, 2l+1 of the step's group
+    u32x2 vs, vz;           // value scale / zero of token t0 + (l & 31), groups 2(l>>5), +1
     uint32_t vw[8];         // value code word holding the lane's 8 channels, its 8 tokens
 };
+
+// The pair of a StepLoad field as floats: MB = 4 bytes (binary32) or 2
+// (binary16, widened exactly).
+template <int MB>
+__device__ __forceinline__ float2 meta_pair(u32x2 v) {
+    if constexpr (MB == 4) return make_float2(__uint_as_float(v.x), __uint_as_float(v.y));
+    const half2_t h = as_h2(v.x);
+    return make_float2(static_cast<float>(h[0]), static_cast<float>(h[1]));
+}
 
 // Token (within the step) of PV slot s for lane group q: the order in which
 // QK^T leaves each lane its scores (rows 4q .. 4q+3 of both 16-token blocks).
 __device__ __forceinline__ int pv_token(int q, int s) { return 16 * (s >> 2) + 4 * q + (s & 3); }
 
-template <int BITS, int G>
+template <int BITS, int G, int MB>
 __device__ __forceinline__ void issue_step(StepLoad& L, const StoreView& S, const LaneOffsets& O,
                                            uint32_t t0, int n) {
     constexpr uint32_t kRow = kHeadDim * BITS / 8;          // code bytes per token
@@ -214,18 +223,31 @@ __device__ __forceinline__ void issue_step(StepLoad& L, const StoreView& S, cons
             L.kw[blk][0] = t.x; L.kw[blk][1] = t.x; L.kw[blk][2] = t.y; L.kw[blk][3] = t.y;
         }
     }
-    // key metadata of the step's group (a 32-token step never crosses one)
-    const uint32_t kmo = O.km + (t0 / G) * (kHeadDim * 4);
-    L.ks = as_float2(__builtin_amdgcn_raw_buffer_load_b64(S.ks, kmo, 0, kStreamLoad));
-    L.kz = as_float2(__builtin_amdgcn_raw_buffer_load_b64(S.kz, kmo, 0, kStreamLoad));
-    // value metadata: 128/G floats per token
-    const uint32_t vmo = O.vm + (kHeadDim * 4 / G) * t0;
-    if constexpr (G == 128) {
-        L.vs = make_float2(__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(S.vs, vmo, 0, kStreamLoad)), 0.0f);
-        L.vz = make_float2(__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(S.vz, vmo, 0, kStreamLoad)), 0.0f);
+    // key metadata of the step's group (a 32-token step never crosses one):
+    // two channels' pairs, 2 * MB bytes
+    const uint32_t kmo = O.km + (t0 / G) * (kHeadDim * MB);
+    // value metadata: 128/G pairs per token; the lane's one or two groups
+    const uint32_t vmo = O.vm + (kHeadDim * MB / G) * t0;
+    if constexpr (MB == 4) {
+        L.ks = __builtin_amdgcn_raw_buffer_load_b64(S.ks, kmo, 0, kStreamLoad);
+        L.kz = __builtin_amdgcn_raw_buffer_load_b64(S.kz, kmo, 0, kStreamLoad);
+        if constexpr (G == 128) {
+            L.vs = u32x2{__builtin_amdgcn_raw_buffer_load_b32(S.vs, vmo, 0, kStreamLoad), 0u};
+            L.vz = u32x2{__builtin_amdgcn_raw_buffer_load_b32(S.vz, vmo, 0, kStreamLoad), 0u};
+        } else {
+            L.vs = __builtin_amdgcn_raw_buffer_load_b64(S.vs, vmo, 0, kStreamLoad);
+            L.vz = __builtin_amdgcn_raw_buffer_load_b64(S.vz, vmo, 0, kStreamLoad);
+        }
     } else {
-        L.vs = as_float2(__builtin_amdgcn_raw_buffer_load_b64(S.vs, vmo, 0, kStreamLoad));
-        L.vz = as_float2(__builtin_amdgcn_raw_buffer_load_b64(S.vz, vmo, 0, kStreamLoad));
+        L.ks = u32x2{__builtin_amdgcn_raw_buffer_load_b32(S.ks, kmo, 0, kStreamLoad), 0u};
+        L.kz = u32x2{__builtin_amdgcn_raw_buffer_load_b32(S.kz, kmo, 0, kStreamLoad), 0u};
+        if constexpr (G == 128) {
+            L.vs = u32x2{static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(S.vs, vmo, 0, kStreamLoad)), 0u};
+            L.vz = u32x2{static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(S.vz, vmo, 0, kStreamLoad)), 0u};
+        } else {
+            L.vs = u32x2{__builtin_amdgcn_raw_buffer_load_b32(S.vs, vmo, 0, kStreamLoad), 0u};
+            L.vz = u32x2{__builtin_amdgcn_raw_buffer_load_b32(S.vz, vmo, 0, kStreamLoad), 0u};
+        }
     }
     const uint32_t vo = O.v + t0 * kRow;
 #pragma unroll
@@ -330,7 +352,7 @@ __device__ __forceinline__ Frag softmax_any(const float4_t (&acc_s)[2], SoftStat
 }
 
 // One step of store tokens [t0, t0 + 32), tokens at or past n_quant masked.
-template <int BITS, int G>
+template <int BITS, int G, int MB>
 __device__ __forceinline__ void store_step(const StepLoad& L, Smem& sm, SoftState& st,
                                            int t0, int n_quant, float c2,
                                            int l, int n, int q) {
@@ -338,22 +360,24 @@ __device__ __forceinline__ void store_step(const StepLoad& L, Smem& sm, SoftStat
     lds_order();
     {
         // key scale times 2^-e of its channel's code position (code_pairs)
-        const float s0 = L.ks.x * kscale_factor<BITS>(2 * l);
-        const float s1 = L.ks.y * kscale_factor<BITS>(2 * l + 1);
+        const float2 ks = meta_pair<MB>(L.ks), kz = meta_pair<MB>(L.kz);
+        const float s0 = ks.x * kscale_factor<BITS>(2 * l);
+        const float s1 = ks.y * kscale_factor<BITS>(2 * l + 1);
         *reinterpret_cast<float2*>(&sm.ks[kidx(2 * l)]) = make_float2(s0, s1);
         *reinterpret_cast<float2*>(&sm.kz[kidx(2 * l)]) =
-            make_float2(__builtin_fmaf(-1024.0f, s0, L.kz.x), __builtin_fmaf(-1024.0f, s1, L.kz.y));
+            make_float2(__builtin_fmaf(-1024.0f, s0, kz.x), __builtin_fmaf(-1024.0f, s1, kz.y));
     }
     {
         // lanes l and l + 32 hold the same token; for G = 64 and 128 they
         // hold the same groups too and write the same values
+        const float2 vs = meta_pair<MB>(L.vs), vz = meta_pair<MB>(L.vz);
         const int tt = l & 31;
         const int gg = G == 32 ? (l >> 5) * 2 : 0;
-        sm.vs[gg][tt] = L.vs.x;
-        sm.vz[gg][tt] = __builtin_fmaf(-1024.0f, L.vs.x, L.vz.x);
+        sm.vs[gg][tt] = vs.x;
+        sm.vz[gg][tt] = __builtin_fmaf(-1024.0f, vs.x, vz.x);
         if constexpr (G != 128) {
-            sm.vs[gg + 1][tt] = L.vs.y;
-            sm.vz[gg + 1][tt] = __builtin_fmaf(-1024.0f, L.vs.y, L.vz.y);
+            sm.vs[gg + 1][tt] = vs.y;
+            sm.vz[gg + 1][tt] = __builtin_fmaf(-1024.0f, vs.y, vz.y);
         }
     }
     lds_order();
@@ -473,7 +497,7 @@ __device__ __forceinline__ void residual_step(const uint16_t* kr, const uint16_t
 // that axis, so one wave may finish the store and start the residual.
 // Offsets within a slab fit in 32 bits: the ABI keeps n_quant and n_res
 // below 2^24 tokens.
-template <int BITS, int GQA, int G>
+template <int BITS, int GQA, int G, int MB>
 __global__ __launch_bounds__(64) KIVI_ATTEND_OCCUPANCY void attend_partial_kernel(const AttendArgs a, int spw, int steps_q,
                                                             int64_t n_split, float* __restrict__ ws_o,
                                                             float* __restrict__ ws_ml)
@@ -518,18 +542,22 @@ __global__ __launch_bounds__(64) KIVI_ATTEND_OCCUPANCY void attend_partial_kerne
     if (has_store) {
         const uint32_t n_groups = static_cast<uint32_t>((nq + G - 1) / G);
         S.kc = make_rsrc(a.k_codes + bkv * a.k_codes_bh_stride, static_cast<uint32_t>(nq) * kWords * 4u);
-        S.ks = make_rsrc(a.k_scale + bkv * a.k_meta_bh_stride, n_groups * kHeadDim * 4u);
-        S.kz = make_rsrc(a.k_zero + bkv * a.k_meta_bh_stride, n_groups * kHeadDim * 4u);
+        const char* kmeta_s = static_cast<const char*>(a.k_scale) + bkv * a.k_meta_bh_stride * MB;
+        const char* kmeta_z = static_cast<const char*>(a.k_zero) + bkv * a.k_meta_bh_stride * MB;
+        const char* vmeta_s = static_cast<const char*>(a.v_scale) + bkv * a.v_meta_bh_stride * MB;
+        const char* vmeta_z = static_cast<const char*>(a.v_zero) + bkv * a.v_meta_bh_stride * MB;
+        S.ks = make_rsrc(kmeta_s, n_groups * kHeadDim * MB);
+        S.kz = make_rsrc(kmeta_z, n_groups * kHeadDim * MB);
         S.vc = make_rsrc(a.v_codes + bkv * a.v_codes_bh_stride, static_cast<uint32_t>(nq) * kWords * 4u);
-        S.vs = make_rsrc(a.v_scale + bkv * a.v_meta_bh_stride, static_cast<uint32_t>(nq) * kMetaPerTok * 4u);
-        S.vz = make_rsrc(a.v_zero + bkv * a.v_meta_bh_stride, static_cast<uint32_t>(nq) * kMetaPerTok * 4u);
+        S.vs = make_rsrc(vmeta_s, static_cast<uint32_t>(nq) * kMetaPerTok * MB);
+        S.vz = make_rsrc(vmeta_z, static_cast<uint32_t>(nq) * kMetaPerTok * MB);
         O.k = static_cast<uint32_t>(n * kWords + (BITS == 4 ? 4 * q : 2 * q)) * 4u;
         O.v = static_cast<uint32_t>(4 * q * kWords + (BITS == 4 ? n : (n >> 1))) * 4u;
-        O.km = static_cast<uint32_t>(l) * 8u;
-        O.vm = G == 32 ? static_cast<uint32_t>(l & 31) * 16u + static_cast<uint32_t>(l >> 5) * 8u
-                       : static_cast<uint32_t>(l & 31) * (kMetaPerTok * 4u);
+        O.km = static_cast<uint32_t>(l) * (2u * MB);
+        O.vm = G == 32 ? static_cast<uint32_t>(l & 31) * (4u * MB) + static_cast<uint32_t>(l >> 5) * (2u * MB)
+                       : static_cast<uint32_t>(l & 31) * (kMetaPerTok * MB);
 #pragma unroll
-        for (int u = 0; u + 1 < kNBuf; ++u) issue_step<BITS, G>(buf[u], S, O, pref(j0 + u * kStep), n);
+        for (int u = 0; u + 1 < kNBuf; ++u) issue_step<BITS, G, MB>(buf[u], S, O, pref(j0 + u * kStep), n);
     }
 
     // B operand of QK^T: q of head n (zero for n >= GQA) in slot order.
@@ -575,8 +603,8 @@ __global__ __launch_bounds__(64) KIVI_ATTEND_OCCUPANCY void attend_partial_kerne
         for (int t0 = j0; t0 < j1; t0 += kNBuf * kStep) {
 #pragma unroll
             for (int u = 0; u < kNBuf; ++u) {
-                issue_step<BITS, G>(buf[(u + kNBuf - 1) % kNBuf], S, O, pref(t0 + (u + kNBuf - 1) * kStep), n);
-                store_step<BITS, G>(buf[u], sm, st, t0 + u * kStep, j1, c2, l, n, q);
+                issue_step<BITS, G, MB>(buf[(u + kNBuf - 1) % kNBuf], S, O, pref(t0 + (u + kNBuf - 1) * kStep), n);
+                store_step<BITS, G, MB>(buf[u], sm, st, t0 + u * kStep, j1, c2, l, n, q);
                 if (t0 + (u + 1) * kStep >= j1) goto store_done;
             }
         }
@@ -727,14 +755,14 @@ AttendPlan plan_attend(int64_t B, int Hq, int Hkv, int64_t n_quant, int64_t n_re
     return p;
 }
 
-template <int BITS, int GQA, int G>
+template <int BITS, int GQA, int G, int MB>
 static hipError_t launch_t(const AttendArgs& a, const AttendPlan& p, hipStream_t stream) {
     float* ws_o = static_cast<float*>(a.workspace);
     const size_t rows = static_cast<size_t>(a.B) * a.Hq * p.n_split;
     const size_t o_bytes = (rows * kHeadDim * sizeof(float) + 255) & ~static_cast<size_t>(255);
     float* ws_ml = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + o_bytes);
     const dim3 grid(static_cast<uint32_t>(p.n_split), static_cast<uint32_t>(a.B * a.Hkv));
-    hipLaunchKernelGGL((attend_partial_kernel<BITS, GQA, G>), grid, dim3(64), 0, stream, a,
+    hipLaunchKernelGGL((attend_partial_kernel<BITS, GQA, G, MB>), grid, dim3(64), 0, stream, a,
                        static_cast<int>(p.steps_per_wave), static_cast<int>(p.steps_q), p.n_split,
                        ws_o, ws_ml);
     hipError_t e = hipGetLastError();
@@ -748,27 +776,30 @@ static hipError_t launch_t(const AttendArgs& a, const AttendPlan& p, hipStream_t
     return hipGetLastError();
 }
 
-template <int BITS, int G>
+template <int BITS, int G, int MB>
 static hipError_t launch_gqa(const AttendArgs& a, const AttendPlan& p, hipStream_t stream) {
     switch (a.Hq / a.Hkv) {
-        case 1: return launch_t<BITS, 1, G>(a, p, stream);
-        case 2: return launch_t<BITS, 2, G>(a, p, stream);
-        case 4: return launch_t<BITS, 4, G>(a, p, stream);
-        default: return launch_t<BITS, 8, G>(a, p, stream);
+        case 1: return launch_t<BITS, 1, G, MB>(a, p, stream);
+        case 2: return launch_t<BITS, 2, G, MB>(a, p, stream);
+        case 4: return launch_t<BITS, 4, G, MB>(a, p, stream);
+        default: return launch_t<BITS, 8, G, MB>(a, p, stream);
     }
 }
 
-template <int BITS>
+template <int BITS, int MB>
 static hipError_t launch_bits(const AttendArgs& a, const AttendPlan& p, hipStream_t stream) {
     switch (a.group) {
-        case 64: return launch_gqa<BITS, 64>(a, p, stream);
-        case 128: return launch_gqa<BITS, 128>(a, p, stream);
-        default: return launch_gqa<BITS, 32>(a, p, stream);
+        case 64: return launch_gqa<BITS, 64, MB>(a, p, stream);
+        case 128: return launch_gqa<BITS, 128, MB>(a, p, stream);
+        default: return launch_gqa<BITS, 32, MB>(a, p, stream);
     }
 }
 
+// One instantiation per (bits, query heads per kv head, group size, bytes of
+// a scale/zero entry).
 hipError_t launch_decode_attend(const AttendArgs& a, const AttendPlan& p, hipStream_t stream) {
-    return a.bits == 4 ? launch_bits<4>(a, p, stream) : launch_bits<2>(a, p, stream);
+    if (a.meta16) return a.bits == 4 ? launch_bits<4, 2>(a, p, stream) : launch_bits<2, 2>(a, p, stream);
+    return a.bits == 4 ? launch_bits<4, 4>(a, p, stream) : launch_bits<2, 4>(a, p, stream);
 }
 
 }  // namespace kivi

@@ -68,9 +68,10 @@ int finish(hipError_t e) { return kivi::hip_status(e); }
 // The slabs of one layer as a store of their own.
 kivi_store layer_store(const kivi_store& s, int64_t slab0) {
     kivi_store r = s;
+    const int64_t meta_bytes = (s.meta_format == KIVI_META_F16 ? 2 : 4) * slab0 * s.meta_bh_stride;
     r.codes = s.codes + slab0 * s.codes_bh_stride;
-    r.scale = s.scale + slab0 * s.meta_bh_stride;
-    r.zero = s.zero + slab0 * s.meta_bh_stride;
+    r.scale = static_cast<char*>(s.scale) + meta_bytes;
+    r.zero = static_cast<char*>(s.zero) + meta_bytes;
     return r;
 }
 

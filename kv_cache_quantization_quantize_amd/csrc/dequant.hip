@@ -14,12 +14,33 @@
 
 namespace kivi {
 
+// Eight consecutive scale (or zero) entries as floats: binary32, or binary16
+// widened exactly.  p is 16-byte aligned (the ABI's slab stride and head_dim
+// rows keep it so).
+__device__ __forceinline__ void load_meta8(const float* p, float (&v)[8]) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void load_meta8(const uint16_t* p, float (&v)[8]) {
+    const uint4 a = *reinterpret_cast<const uint4*>(p);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const half2_t h = as_h2(word_of(a, k));
+        v[2 * k] = static_cast<float>(h[0]);
+        v[2 * k + 1] = static_cast<float>(h[1]);
+    }
+}
+__device__ __forceinline__ float meta_value(float m) { return m; }
+__device__ __forceinline__ float meta_value(uint16_t m) { return static_cast<float>(__builtin_bit_cast(_Float16, m)); }
+
 // Rows [0, n_rows) of one tile; row k is store token t_first + k, written to
 // ot + k*128.  ONE_GROUP (keys only): the 32 rows are exactly one key group,
 // so its scale and zero are loaded once for the tile.
-template <int BITS, bool KEYS, bool ONE_GROUP, bool BF16, int G, int D>
-__device__ __forceinline__ void dequant_tile(const uint32_t* __restrict__ cb, const float* __restrict__ scb,
-                                             const float* __restrict__ zeb, int64_t t_first, int n_rows,
+template <int BITS, bool KEYS, bool ONE_GROUP, bool BF16, int G, int D, typename MT>
+__device__ __forceinline__ void dequant_tile(const uint32_t* __restrict__ cb, const MT* __restrict__ scb,
+                                             const MT* __restrict__ zeb, int64_t t_first, int n_rows,
                                              uint16_t* __restrict__ ot, int lane)
 {
     constexpr int kWords = D * BITS / 32;
@@ -32,16 +53,8 @@ __device__ __forceinline__ void dequant_tile(const uint32_t* __restrict__ cb, co
     const uint32_t* ct = cb + t_first * kWords;
     float gs[8], gz[8];
     if constexpr (ONE_GROUP) {
-        const float* sp = scb + (t_first / G) * D + c * 8;
-        const float* zp = zeb + (t_first / G) * D + c * 8;
-        const float4 s0 = *reinterpret_cast<const float4*>(sp);
-        const float4 s1 = *reinterpret_cast<const float4*>(sp + 4);
-        const float4 z0 = *reinterpret_cast<const float4*>(zp);
-        const float4 z1 = *reinterpret_cast<const float4*>(zp + 4);
-        gs[0] = s0.x; gs[1] = s0.y; gs[2] = s0.z; gs[3] = s0.w;
-        gs[4] = s1.x; gs[5] = s1.y; gs[6] = s1.z; gs[7] = s1.w;
-        gz[0] = z0.x; gz[1] = z0.y; gz[2] = z0.z; gz[3] = z0.w;
-        gz[4] = z1.x; gz[5] = z1.y; gz[6] = z1.z; gz[7] = z1.w;
+        load_meta8(scb + (t_first / G) * D + c * 8, gs);
+        load_meta8(zeb + (t_first / G) * D + c * 8, gz);
     }
 #pragma unroll
     for (int i = 0; i < 32 / kRPW; ++i) {
@@ -56,20 +69,12 @@ __device__ __forceinline__ void dequant_tile(const uint32_t* __restrict__ cb, co
             for (int j = 0; j < 8; ++j) { sc[j] = gs[j]; ze[j] = gz[j]; }
         } else if constexpr (KEYS) {
             const int64_t t = t_first + k;
-            const float* sp = scb + (t / G) * D + c * 8;
-            const float* zp = zeb + (t / G) * D + c * 8;
-            const float4 s0 = *reinterpret_cast<const float4*>(sp);
-            const float4 s1 = *reinterpret_cast<const float4*>(sp + 4);
-            const float4 z0 = *reinterpret_cast<const float4*>(zp);
-            const float4 z1 = *reinterpret_cast<const float4*>(zp + 4);
-            sc[0] = s0.x; sc[1] = s0.y; sc[2] = s0.z; sc[3] = s0.w;
-            sc[4] = s1.x; sc[5] = s1.y; sc[6] = s1.z; sc[7] = s1.w;
-            ze[0] = z0.x; ze[1] = z0.y; ze[2] = z0.z; ze[3] = z0.w;
-            ze[4] = z1.x; ze[5] = z1.y; ze[6] = z1.z; ze[7] = z1.w;
+            load_meta8(scb + (t / G) * D + c * 8, sc);
+            load_meta8(zeb + (t / G) * D + c * 8, ze);
         } else {
             const int64_t t = t_first + k;
-            const float s = scb[t * kMetaPerTok + c / (G / 8)];
-            const float z = zeb[t * kMetaPerTok + c / (G / 8)];
+            const float s = meta_value(scb[t * kMetaPerTok + c / (G / 8)]);
+            const float z = meta_value(zeb[t * kMetaPerTok + c / (G / 8)]);
 #pragma unroll
             for (int j = 0; j < 8; ++j) { sc[j] = s; ze[j] = z; }
         }
@@ -80,10 +85,10 @@ __device__ __forceinline__ void dequant_tile(const uint32_t* __restrict__ cb, co
     }
 }
 
-template <int BITS, bool KEYS, bool BF16, int G, int D>
+template <int BITS, bool KEYS, bool BF16, int G, int D, typename MT>
 __global__ __launch_bounds__(kBlock) void dequant_kernel(
     const uint32_t* __restrict__ codes, int64_t codes_bh_stride,
-    const float* __restrict__ scale, const float* __restrict__ zero, int64_t meta_bh_stride,
+    const MT* __restrict__ scale, const MT* __restrict__ zero, int64_t meta_bh_stride,
     int64_t t0, int64_t n, uint16_t* __restrict__ out, int64_t out_bh_stride,
     int64_t tiles_per_bh, int64_t n_tiles)
 {
@@ -95,39 +100,50 @@ __global__ __launch_bounds__(kBlock) void dequant_kernel(
     const int64_t i0 = (tile - bh * tiles_per_bh) * 32;
     const int64_t rows = n - i0;
     const uint32_t* cb = codes + bh * codes_bh_stride;
-    const float* scb = scale + bh * meta_bh_stride;
-    const float* zeb = zero + bh * meta_bh_stride;
+    const MT* scb = scale + bh * meta_bh_stride;
+    const MT* zeb = zero + bh * meta_bh_stride;
     uint16_t* ot = out + bh * out_bh_stride + i0 * D;
     // a full tile inside one key group loads the group's scale and zero once
     if (KEYS && rows >= 32 && (t0 + i0) % G + 32 <= G)
-        dequant_tile<BITS, KEYS, true, BF16, G, D>(cb, scb, zeb, t0 + i0, 32, ot, lane);
+        dequant_tile<BITS, KEYS, true, BF16, G, D, MT>(cb, scb, zeb, t0 + i0, 32, ot, lane);
     else
-        dequant_tile<BITS, KEYS, false, BF16, G, D>(cb, scb, zeb, t0 + i0, rows < 32 ? static_cast<int>(rows) : 32, ot, lane);
+        dequant_tile<BITS, KEYS, false, BF16, G, D, MT>(cb, scb, zeb, t0 + i0, rows < 32 ? static_cast<int>(rows) : 32, ot, lane);
 }
 
-template <int BITS, bool KEYS, bool BF16, int G, int D>
+template <int BITS, bool KEYS, bool BF16, int G, int D, typename MT>
 static hipError_t launch_t(const DequantArgs& a, hipStream_t stream) {
     const int64_t tiles_per_bh = (a.n + 31) / 32;
     const int64_t n_tiles = a.BH * tiles_per_bh;
     const int64_t blocks = (n_tiles + kWavesPerBlock - 1) / kWavesPerBlock;
-    hipLaunchKernelGGL((dequant_kernel<BITS, KEYS, BF16, G, D>), dim3(static_cast<uint32_t>(blocks)),
-                       dim3(kBlock), 0, stream, a.codes, a.codes_bh_stride, a.scale, a.zero,
+    hipLaunchKernelGGL((dequant_kernel<BITS, KEYS, BF16, G, D, MT>), dim3(static_cast<uint32_t>(blocks)),
+                       dim3(kBlock), 0, stream, a.codes, a.codes_bh_stride,
+                       static_cast<const MT*>(a.scale), static_cast<const MT*>(a.zero),
                        a.meta_bh_stride, a.t0, a.n, a.out, a.out_bh_stride, tiles_per_bh, n_tiles);
     return hipGetLastError();
 }
 
-template <bool BF16, int G, int D>
+template <bool BF16, int G, int D, typename MT = float>
 static hipError_t launch_g(const DequantArgs& a, hipStream_t stream) {
     const bool keys = a.kind == 0;
-    if (a.bits == 4) return keys ? launch_t<4, true, BF16, G, D>(a, stream) : launch_t<4, false, BF16, G, D>(a, stream);
-    return keys ? launch_t<2, true, BF16, G, D>(a, stream) : launch_t<2, false, BF16, G, D>(a, stream);
+    if (a.bits == 4) return keys ? launch_t<4, true, BF16, G, D, MT>(a, stream) : launch_t<4, false, BF16, G, D, MT>(a, stream);
+    return keys ? launch_t<2, true, BF16, G, D, MT>(a, stream) : launch_t<2, false, BF16, G, D, MT>(a, stream);
 }
 
-// head_dim 128 with groups of 32, 64 or 128; head_dim 64 and 256 with groups of 32
+// head_dim 128 with groups of 32, 64 or 128; head_dim 64 and 256 with groups
+// of 32.  Binary16 metadata: fp16 output at head_dim 128.
 template <bool BF16>
 static hipError_t launch_fmt(const DequantArgs& a, hipStream_t stream) {
     if (a.head_dim == 64) return launch_g<BF16, 32, 64>(a, stream);
     if (a.head_dim == 256) return launch_g<BF16, 32, 256>(a, stream);
+    if constexpr (!BF16) {
+        if (a.meta16) {
+            switch (a.group) {
+                case 64: return launch_g<false, 64, 128, uint16_t>(a, stream);
+                case 128: return launch_g<false, 128, 128, uint16_t>(a, stream);
+                default: return launch_g<false, 32, 128, uint16_t>(a, stream);
+            }
+        }
+    }
     switch (a.group) {
         case 64: return launch_g<BF16, 64, 128>(a, stream);
         case 128: return launch_g<BF16, 128, 128>(a, stream);

@@ -1,6 +1,7 @@
 // flush.hip -- the KIVI flush kernels for gfx950: per-channel keys and
 // per-token values, quantized to 2 or 4 bits, codes bit-packed into uint32,
-// one fp32 scale and zero per group, optional fused fp16 reconstruction.
+// one scale and zero per group (binary32, or binary16 for fp16 caches),
+// optional fused fp16 reconstruction.
 //
 // Sources, cited by page title and section:
 //   [Metal post] blog post "A 5.65x Metal Kernel That Made My LLM Exactly 0%
@@ -29,11 +30,12 @@ namespace kivi {
 // One tile.  xt, ct, rt point at token s0 of the slab (input, codes, recon);
 // n_rows = min(32, S - s0) real rows.  RAGGED tiles clamp loads to the last
 // real row and guard stores; full tiles do neither.
-template <int BITS, bool RECON, bool RAGGED, bool BF16, int G, int D>
+template <int BITS, bool RECON, bool RAGGED, bool BF16, int G, int D, typename MT>
 __device__ __forceinline__ void key_tile(const uint16_t* __restrict__ xt, uint32_t* __restrict__ ct,
-                                         float* __restrict__ sct, float* __restrict__ zet,
+                                         MT* __restrict__ sct, MT* __restrict__ zet,
                                          uint16_t* __restrict__ rt, int n_rows, int lane, float one)
 {
+    constexpr bool MH = sizeof(MT) == 2;            // binary16 scale/zero
     constexpr int kWords = D * BITS / 32;          // code words per token row
     constexpr int kLPR = RowGeo<D>::kLanesPerRow;
     constexpr int kRPW = RowGeo<D>::kRowsPerWave;
@@ -105,21 +107,38 @@ __device__ __forceinline__ void key_tile(const uint16_t* __restrict__ xt, uint32
     // zero = min, scale = RN((max - min) / (2^bits - 1)), r ~ 1/scale.  (The
     // range needs no zero canonicalization: x - y is +0 for equal zeros.)
     float ze[8], sc[8], rc[8];
-    bool slow = false;                              // a scale off the fast path (bfloat16 only)
+    bool slow = false;                              // a scale off the fast path (bfloat16, binary16 metadata)
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         ze[j] = canon_zero(mnf[j]);
         sc[j] = BF16 ? scale_wide<BITS>(mxf[j] - mnf[j]) : scale_of<BITS>(mxf[j] - mnf[j]);
+        if constexpr (MH) {
+            sc[j] = round_to_f16(sc[j]);
+            slow |= slow_scale16(sc[j], mxf[j] - mnf[j]);
+        }
         rc[j] = recip_clamped(sc[j]);
         if constexpr (BF16) slow |= !fast_scale(sc[j]);
     }
 
-    if (r == 0) {
-        store_stream4(sct + c * 8, sc[0], sc[1], sc[2], sc[3]);
-        store_stream4(sct + c * 8 + 4, sc[4], sc[5], sc[6], sc[7]);
-    } else if (r == 1) {
-        store_stream4(zet + c * 8, ze[0], ze[1], ze[2], ze[3]);
-        store_stream4(zet + c * 8 + 4, ze[4], ze[5], ze[6], ze[7]);
+    if constexpr (MH) {
+        uint32_t h[8];
+        if (r == 0) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) h[j] = f32_to_f16(sc[j]);
+            store_stream(sct + c * 8, pack8(h));
+        } else if (r == 1) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) h[j] = f32_to_f16(ze[j]);
+            store_stream(zet + c * 8, pack8(h));
+        }
+    } else {
+        if (r == 0) {
+            store_stream4(sct + c * 8, sc[0], sc[1], sc[2], sc[3]);
+            store_stream4(sct + c * 8 + 4, sc[4], sc[5], sc[6], sc[7]);
+        } else if (r == 1) {
+            store_stream4(zet + c * 8, ze[0], ze[1], ze[2], ze[3]);
+            store_stream4(zet + c * 8 + 4, ze[4], ze[5], ze[6], ze[7]);
+        }
     }
 
 #pragma unroll
@@ -157,11 +176,11 @@ __device__ __forceinline__ void key_tile(const uint16_t* __restrict__ xt, uint32
     }
 }
 
-template <int BITS, bool RECON, bool BF16, int G, int D>
+template <int BITS, bool RECON, bool BF16, int G, int D, typename MT>
 __global__ __launch_bounds__(kBlock) void key_flush_kernel(
     const uint16_t* __restrict__ x, int64_t S, int64_t x_bh_stride,
     uint32_t* __restrict__ codes, int64_t codes_bh_stride,
-    float* __restrict__ scale, float* __restrict__ zero, int64_t meta_bh_stride,
+    MT* __restrict__ scale, MT* __restrict__ zero, int64_t meta_bh_stride,
     int64_t dst_token, uint16_t* __restrict__ recon, int64_t recon_bh_stride,
     int64_t n_groups, int64_t n_tiles, float one)
 {
@@ -178,19 +197,20 @@ __global__ __launch_bounds__(kBlock) void key_flush_kernel(
     uint16_t* rt = RECON ? recon + bh * recon_bh_stride + s0 * D : nullptr;
     const int64_t rows = S - s0;
     if (rows >= G)
-        key_tile<BITS, RECON, false, BF16, G, D>(xt, ct, scale + moff, zero + moff, rt, G, lane, one);
+        key_tile<BITS, RECON, false, BF16, G, D, MT>(xt, ct, scale + moff, zero + moff, rt, G, lane, one);
     else
-        key_tile<BITS, RECON, true, BF16, G, D>(xt, ct, scale + moff, zero + moff, rt, static_cast<int>(rows), lane, one);
+        key_tile<BITS, RECON, true, BF16, G, D, MT>(xt, ct, scale + moff, zero + moff, rt, static_cast<int>(rows), lane, one);
 }
 
 // ---------------------------------------------------------------------------
 // Values: group = (bh, token s, channel group j) over channels [32j, 32j+32)
 // ---------------------------------------------------------------------------
-template <int BITS, bool RECON, bool RAGGED, bool BF16, int G, int D>
+template <int BITS, bool RECON, bool RAGGED, bool BF16, int G, int D, typename MT>
 __device__ __forceinline__ void value_tile(const uint16_t* __restrict__ xt, uint32_t* __restrict__ ct,
-                                           float* __restrict__ sct, float* __restrict__ zet,
+                                           MT* __restrict__ sct, MT* __restrict__ zet,
                                            uint16_t* __restrict__ rt, int n_rows, int lane, float one)
 {
+    constexpr bool MH = sizeof(MT) == 2;            // binary16 scale/zero
     constexpr int kWords = D * BITS / 32;
     constexpr int kMetaPerTok = D / G;              // channel groups per token
     constexpr int kLanesPerGroup = G / 8;           // 4, 8 or 16 lanes of 8 channels
@@ -253,7 +273,8 @@ __device__ __forceinline__ void value_tile(const uint16_t* __restrict__ xt, uint
             }
         }
         const float ze = canon_zero(lo);
-        const float sc = BF16 ? scale_wide<BITS>(hi - lo) : scale_of<BITS>(hi - lo);
+        float sc = BF16 ? scale_wide<BITS>(hi - lo) : scale_of<BITS>(hi - lo);
+        if constexpr (MH) sc = round_to_f16(sc);
         const float rc = recip_clamped(sc);
 
         float t[8], qf[8];
@@ -263,7 +284,7 @@ __device__ __forceinline__ void value_tile(const uint16_t* __restrict__ xt, uint
             t[k] = sub_elem<BF16>(raw[i], k, one, ze);
             qf[k] = quant_fast(t[k], rc, dev);
         }
-        if (dev > kNearTie || (BF16 && !fast_scale(sc))) {
+        if (dev > kNearTie || (BF16 && !fast_scale(sc)) || (MH && slow_scale16(sc, hi - lo))) {
 #pragma unroll
             for (int k = 0; k < 8; ++k) qf[k] = quant_exact(t[k], sc, static_cast<float>((1 << BITS) - 1));
         }
@@ -281,8 +302,13 @@ __device__ __forceinline__ void value_tile(const uint16_t* __restrict__ xt, uint
             // plain stores: one instruction writes 16-64 B of a line, which the
             // L2 merges (with the nontemporal hint they reached HBM as partial
             // lines: 8% more write traffic and a slower flush)
-            if (c % kLanesPerGroup == 0) sct[row * kMetaPerTok + j] = sc;
-            else if (c % kLanesPerGroup == 1) zet[row * kMetaPerTok + j] = ze;
+            if constexpr (MH) {
+                if (c % kLanesPerGroup == 0) sct[row * kMetaPerTok + j] = static_cast<uint16_t>(f32_to_f16(sc));
+                else if (c % kLanesPerGroup == 1) zet[row * kMetaPerTok + j] = static_cast<uint16_t>(f32_to_f16(ze));
+            } else {
+                if (c % kLanesPerGroup == 0) sct[row * kMetaPerTok + j] = sc;
+                else if (c % kLanesPerGroup == 1) zet[row * kMetaPerTok + j] = ze;
+            }
         }
         if constexpr (RECON) {
             uint32_t h[8];
@@ -293,11 +319,11 @@ __device__ __forceinline__ void value_tile(const uint16_t* __restrict__ xt, uint
     }
 }
 
-template <int BITS, bool RECON, bool BF16, int G, int D>
+template <int BITS, bool RECON, bool BF16, int G, int D, typename MT>
 __global__ __launch_bounds__(kBlock) void value_flush_kernel(
     const uint16_t* __restrict__ x, int64_t S, int64_t x_bh_stride,
     uint32_t* __restrict__ codes, int64_t codes_bh_stride,
-    float* __restrict__ scale, float* __restrict__ zero, int64_t meta_bh_stride,
+    MT* __restrict__ scale, MT* __restrict__ zero, int64_t meta_bh_stride,
     int64_t dst_token, uint16_t* __restrict__ recon, int64_t recon_bh_stride,
     int64_t tiles_per_bh, int64_t n_tiles, float one)
 {
@@ -314,57 +340,70 @@ __global__ __launch_bounds__(kBlock) void value_flush_kernel(
     uint16_t* rt = RECON ? recon + bh * recon_bh_stride + s0 * D : nullptr;
     const int64_t rows = S - s0;
     if (rows >= 32)
-        value_tile<BITS, RECON, false, BF16, G, D>(xt, ct, scale + moff, zero + moff, rt, 32, lane, one);
+        value_tile<BITS, RECON, false, BF16, G, D, MT>(xt, ct, scale + moff, zero + moff, rt, 32, lane, one);
     else
-        value_tile<BITS, RECON, true, BF16, G, D>(xt, ct, scale + moff, zero + moff, rt, static_cast<int>(rows), lane, one);
+        value_tile<BITS, RECON, true, BF16, G, D, MT>(xt, ct, scale + moff, zero + moff, rt, static_cast<int>(rows), lane, one);
 }
 
 // ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
-template <int BITS, bool RECON, bool BF16, int G, int D>
+template <int BITS, bool RECON, bool BF16, int G, int D, typename MT>
 static hipError_t launch_keys_t(const FlushArgs& a, hipStream_t stream) {
     const int64_t n_groups = (a.S + G - 1) / G;
     const int64_t n_tiles = a.BH * n_groups;
     const int64_t blocks = (n_tiles + kWavesPerBlock - 1) / kWavesPerBlock;
-    hipLaunchKernelGGL((key_flush_kernel<BITS, RECON, BF16, G, D>), dim3(static_cast<uint32_t>(blocks)),
+    hipLaunchKernelGGL((key_flush_kernel<BITS, RECON, BF16, G, D, MT>), dim3(static_cast<uint32_t>(blocks)),
                        dim3(kBlock), 0, stream, a.x, a.S, a.x_bh_stride, a.codes,
-                       a.codes_bh_stride, a.scale, a.zero, a.meta_bh_stride, a.dst_token,
+                       a.codes_bh_stride, static_cast<MT*>(a.scale), static_cast<MT*>(a.zero),
+                       a.meta_bh_stride, a.dst_token,
                        a.recon, a.recon_bh_stride, n_groups, n_tiles, 1.0f);
     return hipGetLastError();
 }
 
-template <int BITS, bool RECON, bool BF16, int G, int D>
+template <int BITS, bool RECON, bool BF16, int G, int D, typename MT>
 static hipError_t launch_values_t(const FlushArgs& a, hipStream_t stream) {
     const int64_t tiles_per_bh = (a.S + 31) / 32;
     const int64_t n_tiles = a.BH * tiles_per_bh;
     const int64_t blocks = (n_tiles + kWavesPerBlock - 1) / kWavesPerBlock;
-    hipLaunchKernelGGL((value_flush_kernel<BITS, RECON, BF16, G, D>), dim3(static_cast<uint32_t>(blocks)),
+    hipLaunchKernelGGL((value_flush_kernel<BITS, RECON, BF16, G, D, MT>), dim3(static_cast<uint32_t>(blocks)),
                        dim3(kBlock), 0, stream, a.x, a.S, a.x_bh_stride, a.codes,
-                       a.codes_bh_stride, a.scale, a.zero, a.meta_bh_stride, a.dst_token,
+                       a.codes_bh_stride, static_cast<MT*>(a.scale), static_cast<MT*>(a.zero),
+                       a.meta_bh_stride, a.dst_token,
                        a.recon, a.recon_bh_stride, tiles_per_bh, n_tiles, 1.0f);
     return hipGetLastError();
 }
 
-// One instantiation per (bits, reconstruction, input format, group size, head_dim).
-template <bool KEYS, bool BF16, int G, int D>
+// One instantiation per (bits, reconstruction, input format, group size,
+// head_dim, metadata format).
+template <bool KEYS, bool BF16, int G, int D, typename MT = float>
 static hipError_t launch_flush_g(const FlushArgs& a, hipStream_t stream) {
     const bool rec = a.recon != nullptr;
     if constexpr (KEYS) {
-        if (a.bits == 4) return rec ? launch_keys_t<4, true, BF16, G, D>(a, stream) : launch_keys_t<4, false, BF16, G, D>(a, stream);
-        return rec ? launch_keys_t<2, true, BF16, G, D>(a, stream) : launch_keys_t<2, false, BF16, G, D>(a, stream);
+        if (a.bits == 4) return rec ? launch_keys_t<4, true, BF16, G, D, MT>(a, stream) : launch_keys_t<4, false, BF16, G, D, MT>(a, stream);
+        return rec ? launch_keys_t<2, true, BF16, G, D, MT>(a, stream) : launch_keys_t<2, false, BF16, G, D, MT>(a, stream);
     } else {
-        if (a.bits == 4) return rec ? launch_values_t<4, true, BF16, G, D>(a, stream) : launch_values_t<4, false, BF16, G, D>(a, stream);
-        return rec ? launch_values_t<2, true, BF16, G, D>(a, stream) : launch_values_t<2, false, BF16, G, D>(a, stream);
+        if (a.bits == 4) return rec ? launch_values_t<4, true, BF16, G, D, MT>(a, stream) : launch_values_t<4, false, BF16, G, D, MT>(a, stream);
+        return rec ? launch_values_t<2, true, BF16, G, D, MT>(a, stream) : launch_values_t<2, false, BF16, G, D, MT>(a, stream);
     }
 }
 
 // head_dim 128 with groups of 32, 64 or 128; head_dim 64 and 256 with groups
-// of 32 (the ABI admits no other pair).
+// of 32 (the ABI admits no other pair).  Binary16 metadata: fp16 input at
+// head_dim 128.
 template <bool KEYS, bool BF16>
 static hipError_t launch_flush_fmt(const FlushArgs& a, hipStream_t stream) {
     if (a.head_dim == 64) return launch_flush_g<KEYS, BF16, 32, 64>(a, stream);
     if (a.head_dim == 256) return launch_flush_g<KEYS, BF16, 32, 256>(a, stream);
+    if constexpr (!BF16) {
+        if (a.meta16) {
+            switch (a.group) {
+                case 64: return launch_flush_g<KEYS, false, 64, 128, uint16_t>(a, stream);
+                case 128: return launch_flush_g<KEYS, false, 128, 128, uint16_t>(a, stream);
+                default: return launch_flush_g<KEYS, false, 32, 128, uint16_t>(a, stream);
+            }
+        }
+    }
     switch (a.group) {
         case 64: return launch_flush_g<KEYS, BF16, 64, 128>(a, stream);
         case 128: return launch_flush_g<KEYS, BF16, 128, 128>(a, stream);

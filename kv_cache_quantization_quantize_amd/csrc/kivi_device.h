@@ -302,4 +302,19 @@ __device__ __forceinline__ float scale_wide(float range) {
 // reciprocal; any other scale (zero included) takes the IEEE quotient.
 __device__ __forceinline__ bool fast_scale(float s) { return s >= 0x1p-126f && s < 0x1p126f; }
 
+// ---------------------------------------------------------------------------
+// Binary16 scale/zero: the binary32 scale rounded to nearest even binary16
+// is what the store holds and what the codes and reconstruction use.  (The
+// zero of an fp16 group is an fp16 value and needs no rounding.)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float round_to_f16(float s) { return static_cast<float>(static_cast<_Float16>(s)); }
+
+// quant_fast's bounds hold for a normal binary16 scale: it is within 2^-11
+// (relative) of the binary32 one, so t / s <= L (1 + 2^-10) stays below
+// L + 1/2 and below 16, and no clip is needed.  A non-constant group whose
+// scale rounded to a subnormal or to 0 takes quant_exact (IEEE quotient and
+// clip; code 0 for a zero scale).  A constant group keeps the fast path: its
+// t are all 0.
+__device__ __forceinline__ bool slow_scale16(float s, float range) { return range != 0.0f && s < 0x1p-14f; }
+
 }  // namespace kivi

@@ -16,8 +16,8 @@ struct FlushArgs {
     int64_t BH, S, x_bh_stride;
     uint32_t* codes;
     int64_t codes_bh_stride;
-    float* scale;
-    float* zero;
+    void* scale;                   // float, or binary16 bits when meta16
+    void* zero;
     int64_t meta_bh_stride;
     int64_t dst_token;
     uint16_t* recon;               // may be null
@@ -26,13 +26,14 @@ struct FlushArgs {
     int group;                     // 32, 64 or 128
     int head_dim;                  // 64, 128 or 256
     bool bf16;                     // x and recon hold bfloat16 (else fp16)
+    bool meta16;                   // binary16 scale/zero (fp16 x, head_dim 128)
 };
 
 struct DequantArgs {
     const uint32_t* codes;
     int64_t codes_bh_stride;
-    const float* scale;
-    const float* zero;
+    const void* scale;             // float, or binary16 bits when meta16
+    const void* zero;
     int64_t meta_bh_stride;
     int64_t BH, t0, n;
     uint16_t* out;
@@ -42,6 +43,7 @@ struct DequantArgs {
     int group;                     // 32, 64 or 128
     int head_dim;                  // 64, 128 or 256
     bool bf16;                     // out holds bfloat16 (else fp16)
+    bool meta16;                   // binary16 scale/zero (head_dim 128)
 };
 
 struct AttendArgs {
@@ -49,11 +51,11 @@ struct AttendArgs {
     int64_t B;
     int Hq, Hkv;
     const uint32_t* k_codes;
-    const float* k_scale;
-    const float* k_zero;
+    const void* k_scale;           // float, or binary16 bits when meta16
+    const void* k_zero;
     const uint32_t* v_codes;
-    const float* v_scale;
-    const float* v_zero;
+    const void* v_scale;
+    const void* v_zero;
     int64_t k_codes_bh_stride, v_codes_bh_stride;
     int64_t k_meta_bh_stride, v_meta_bh_stride;
     int64_t n_quant;               // store tokens (varlen: the per-sequence bound)
@@ -74,6 +76,7 @@ struct AttendArgs {
     void* workspace;
     int bits;
     int group;                     // 32, 64 or 128 (keys and values alike)
+    bool meta16;                   // binary16 scale/zero (keys and values alike)
 };
 
 // Split of the token axis chosen for an attend shape; the workspace holds

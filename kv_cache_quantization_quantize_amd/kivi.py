@@ -18,6 +18,8 @@ LIB_PATH = os.path.join(_PKG, "libkivi.so")
 
 KIVI_KEYS = 0
 KIVI_VALUES = 1
+KIVI_META_F32 = 0
+KIVI_META_F16 = 1
 HEAD_DIM = 128
 GROUP = 32
 
@@ -53,6 +55,7 @@ class CStore(ctypes.Structure):
         ("group_size", ctypes.c_int32),
         ("head_dim", ctypes.c_int32),
         ("kind", ctypes.c_int32),
+        ("meta_format", ctypes.c_int32),
     ]
 
 
@@ -149,28 +152,39 @@ def _need_f16(t: torch.Tensor, name: str, allow_bf16: bool = False, D: int = HEA
 class Store:
     """A packed store in device memory (layout of include/kivi.h).
 
-    ``codes`` is int32 storage holding the uint32 code words."""
+    ``codes`` is int32 storage holding the uint32 code words.  ``meta`` is
+    the format of scale and zero: "f32" (float32 tensors) or "f16" (float16
+    tensors holding binary16, KIVI_META_F16)."""
 
     def __init__(self, kind: int, BH: int, cap: int, bits: int = 4, device="cuda",
                  codes: torch.Tensor | None = None, scale: torch.Tensor | None = None,
-                 zero: torch.Tensor | None = None, group: int = GROUP, head_dim: int = HEAD_DIM):
+                 zero: torch.Tensor | None = None, group: int = GROUP, head_dim: int = HEAD_DIM,
+                 meta: str = "f32"):
+        if meta not in ("f32", "f16"):
+            raise ValueError("meta must be 'f32' or 'f16'")
         self.kind, self.BH, self.cap, self.bits, self.group = kind, BH, cap, bits, group
         self.head_dim = head_dim
+        self.meta = meta
         self.words = head_dim * bits // 32
-        meta = (BH, (cap + group - 1) // group, head_dim) if kind == KIVI_KEYS else \
+        shape = (BH, (cap + group - 1) // group, head_dim) if kind == KIVI_KEYS else \
             (BH, cap, head_dim // group)
+        mdt = torch.float32 if meta == "f32" else torch.float16
         self.codes = codes if codes is not None else torch.zeros((BH, cap, self.words),
                                                                  dtype=torch.int32, device=device)
-        self.scale = scale if scale is not None else torch.zeros(meta, dtype=torch.float32, device=device)
-        self.zero = zero if zero is not None else torch.zeros(meta, dtype=torch.float32, device=device)
+        self.scale = scale if scale is not None else torch.zeros(shape, dtype=mdt, device=device)
+        self.zero = zero if zero is not None else torch.zeros(shape, dtype=mdt, device=device)
+        if self.scale.dtype != mdt or self.zero.dtype != mdt:
+            raise TypeError("scale and zero must be %s for meta=%r" % (mdt, meta))
 
     def c(self) -> CStore:
         return CStore(self.codes.data_ptr(), self.scale.data_ptr(), self.zero.data_ptr(),
                       self.codes.stride(0), self.scale.stride(0), self.cap, self.bits,
-                      self.group, self.head_dim, self.kind)
+                      self.group, self.head_dim, self.kind,
+                      KIVI_META_F16 if self.meta == "f16" else KIVI_META_F32)
 
     def nbytes(self) -> int:
-        return (self.codes.numel() * 4 + self.scale.numel() * 4 + self.zero.numel() * 4)
+        return (self.codes.numel() * 4 + self.scale.numel() * self.scale.element_size()
+                + self.zero.numel() * self.zero.element_size())
 
 
 def _flush(fn_name, x: torch.Tensor, store: Store, dst_token: int, recon, stream):

@@ -52,12 +52,21 @@ def assert_store_equal(gpu: kivi.Store, host: oracle.Store, slabs=None, what="")
         bad = np.argwhere(codes != hc)
         raise AssertionError(f"{what}: {len(bad)} code words differ, first at {bad[0].tolist()}: "
                              f"gpu {codes[tuple(bad[0])]:#010x} oracle {hc[tuple(bad[0])]:#010x}")
-    # compare metadata as bit patterns (the sentinel and +0 must match exactly)
-    if not np.array_equal(scale.view(np.uint32), hs.view(np.uint32)):
-        bad = np.argwhere(scale.view(np.uint32) != hs.view(np.uint32))
-        raise AssertionError(f"{what}: {len(bad)} scales differ, first at {bad[0].tolist()}")
-    if not np.array_equal(zero.view(np.uint32), hz.view(np.uint32)):
-        bad = np.argwhere(zero.view(np.uint32) != hz.view(np.uint32))
+    # compare metadata as bit patterns (the sentinel and +0 must match
+    # exactly); a binary16 host store holds binary16 values, so its
+    # conversion to binary16 bits is exact
+    if getattr(gpu, "meta", "f32") == "f16":
+        assert host.meta == "f16"
+        gs, gz = scale.view(np.uint16), zero.view(np.uint16)
+        hs, hz = oracle.f32_to_f16(hs), oracle.f32_to_f16(hz)
+    else:
+        gs, gz, hs, hz = scale.view(np.uint32), zero.view(np.uint32), hs.view(np.uint32), hz.view(np.uint32)
+    if not np.array_equal(gs, hs):
+        bad = np.argwhere(gs != hs)
+        raise AssertionError(f"{what}: {len(bad)} scales differ, first at {bad[0].tolist()}: "
+                             f"gpu {gs[tuple(bad[0])]:#x} oracle {hs[tuple(bad[0])]:#x}")
+    if not np.array_equal(gz, hz):
+        bad = np.argwhere(gz != hz)
         raise AssertionError(f"{what}: {len(bad)} zeros differ, first at {bad[0].tolist()}")
 
 

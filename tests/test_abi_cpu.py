@@ -47,11 +47,13 @@ def test_status_strings():
 FAKE = 0x10000   # an aligned address that is never dereferenced
 
 
-def _store(kind=kivi.KIVI_KEYS, bits=4, cap=64, G=32, D=128, codes=FAKE, stride=None):
+def _store(kind=kivi.KIVI_KEYS, bits=4, cap=64, G=32, D=128, codes=FAKE, stride=None,
+           meta_format=kivi.KIVI_META_F32, meta_stride=None):
     words = D * bits // 32
     meta = ((cap + 31) // 32) * D if kind == kivi.KIVI_KEYS else cap * 4
     return kivi.CStore(codes, FAKE, FAKE, stride if stride is not None else cap * words,
-                       meta, cap, bits, G, D, kind)
+                       meta_stride if meta_stride is not None else meta, cap, bits, G, D, kind,
+                       meta_format)
 
 
 def _keys(st, x=FAKE, BH=2, S=32, x_stride=32 * 128, off=0, recon=None, rstride=0):
@@ -113,6 +115,25 @@ def test_key_flush_validation(case, want):
     assert _keys(st, **kw) == want
 
 
+def test_binary16_metadata_validation():
+    L = kivi.lib()
+    F16 = kivi.KIVI_META_F16
+    # valid (zero-sized calls validate fully and launch nothing)
+    assert _keys(_store(meta_format=F16), S=0) == 0
+    assert _keys(_store(meta_format=F16, G=128, cap=128), S=0) == 0
+    assert L.kivi_dequantize(ctypes.byref(_store(meta_format=F16)), 2, 0, 0, FAKE, 0, None) == 0
+    # an unknown format, and binary16 metadata off head_dim 128
+    assert _keys(_store(meta_format=2), S=0) == -3
+    assert _keys(_store(meta_format=F16, D=64), S=0) == -3
+    # bfloat16 caches keep binary32 metadata, for the flush and the dequantize
+    st = _store(meta_format=F16)
+    assert L.kivi_quantize_keys_bf16(FAKE, 2, 0, 4096, ctypes.byref(st), 0, None, 0, None) == -3
+    assert L.kivi_dequantize_bf16(ctypes.byref(st), 2, 0, 0, FAKE, 0, None) == -3
+    # binary16 slab strides must be whole 16-byte units (8 entries)
+    assert _keys(_store(meta_format=F16, meta_stride=2 * 128 + 4)) == -4
+    assert _keys(_store(meta_stride=2 * 128 + 2)) == -4              # binary32: 4 entries
+
+
 def test_value_flush_accepts_unaligned_token_offset_but_checks_window():
     st = _store(kind=kivi.KIVI_VALUES, cap=40)
     L = kivi.lib()
@@ -167,6 +188,8 @@ def test_attend_validation():
     # key and value stores must share their group size (32, 64 or 128)
     assert call(kk=_store(kivi.KIVI_KEYS, cap=64, G=64), vv=_store(kivi.KIVI_VALUES, cap=64, G=32)) == -3
     assert call(kk=_store(kivi.KIVI_KEYS, cap=64, G=48), vv=_store(kivi.KIVI_VALUES, cap=64, G=48)) == -3
+    # and their scale/zero format
+    assert call(kk=_store(kivi.KIVI_KEYS, cap=64, meta_format=kivi.KIVI_META_F16)) == -3
 
 
 # ---------------------------------------------------------------- cache
