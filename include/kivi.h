@@ -138,7 +138,9 @@ int kivi_quantize_values(const uint16_t* x, int64_t BH, int64_t S, int64_t x_bh_
  * the low 16 fraction bits dropped); every later step is the same fp32
  * arithmetic, and the reconstruction is rounded to bfloat16 (nearest even).
  * The packed store is identical to the one the fp16 calls write.  Inputs
- * must be finite with a finite max - min in every group.
+ * must be finite with a finite max - min in every group.  A store with
+ * binary16 scale/zero returns KIVI_ERR_UNSUPPORTED (a bfloat16 minimum need
+ * not be a binary16 value).
  */
 int kivi_quantize_keys_bf16(const uint16_t* x, int64_t BH, int64_t S, int64_t x_bh_stride,
                             const kivi_store* dst, int64_t dst_token,
@@ -162,7 +164,8 @@ int kivi_dequantize(const kivi_store* src, int64_t BH, int64_t token_begin, int6
                     uint16_t* out, int64_t out_bh_stride, hipStream_t stream);
 
 /* kivi_dequantize with a bfloat16 output: out = bf16_rne(fl(fl(q*scale) +
- * zero)), bit-exact with the reconstruction the bfloat16 flushes write. */
+ * zero)), bit-exact with the reconstruction the bfloat16 flushes write.
+ * Stores with binary32 scale/zero only (KIVI_ERR_UNSUPPORTED otherwise). */
 int kivi_dequantize_bf16(const kivi_store* src, int64_t BH, int64_t token_begin, int64_t n_tokens,
                          uint16_t* out, int64_t out_bh_stride, hipStream_t stream);
 

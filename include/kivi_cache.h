@@ -34,6 +34,7 @@
  * Device layout (kivi_cache_device_bytes bytes at `device`, 256-byte aligned
  * sections, slab s = (layer * batch + b) * kv_heads + h):
  *   key store, value store   as in kivi.h with cap = store_capacity tokens
+ *                            and the configuration's scale/zero format
  *   key ring, value ring     fp16 [slabs][R + F][head_dim]
  *
  * The library never allocates: the caller allocates the device buffer and
@@ -65,6 +66,8 @@ typedef struct kivi_cache_config {
     int32_t residual_length;  /* R >= 0, a multiple of flush_tokens            */
     int32_t flush_tokens;     /* F > 0, a multiple of group_size               */
     int64_t store_capacity;   /* quantized tokens per sequence, a multiple of F */
+    int32_t meta_format;      /* scale/zero of the stores: KIVI_META_F32 (0) or
+                                 KIVI_META_F16 (1), as in kivi.h                */
 } kivi_cache_config;
 
 /* Host-side state of a cache.  Filled by kivi_cache_init; the fields are

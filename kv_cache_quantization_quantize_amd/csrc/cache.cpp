@@ -31,6 +31,7 @@ bool valid(const kivi_cache_config* c) {
     if (c->flush_tokens <= 0 || c->flush_tokens % kG != 0) return false;
     if (c->residual_length < 0 || c->residual_length % c->flush_tokens != 0) return false;
     if (c->store_capacity < 0 || c->store_capacity % c->flush_tokens != 0) return false;
+    if (c->meta_format != KIVI_META_F32 && c->meta_format != KIVI_META_F16) return false;
     if (c->store_capacity >= kMaxTokens) return false;
     if (int64_t{c->residual_length} + c->flush_tokens >= kMaxTokens) return false;
     const int64_t slabs = int64_t{c->layers} * c->batch * c->kv_heads;
@@ -43,14 +44,15 @@ Layout layout(const kivi_cache_config& c) {
     L.ring = int64_t{c.residual_length} + c.flush_tokens;
     L.words = kD * c.bits / 32;
     const int64_t cap = c.store_capacity;
+    const int64_t mb = c.meta_format == KIVI_META_F16 ? 2 : 4;     // bytes per scale/zero entry
     int64_t off = 0;
     auto take = [&off](int64_t bytes) { const int64_t at = off; off = align256(off + bytes); return at; };
     L.kc = take(L.slabs * cap * L.words * 4);
-    L.ks = take(L.slabs * (cap / kG) * kD * 4);
-    L.kz = take(L.slabs * (cap / kG) * kD * 4);
+    L.ks = take(L.slabs * (cap / kG) * kD * mb);
+    L.kz = take(L.slabs * (cap / kG) * kD * mb);
     L.vc = take(L.slabs * cap * L.words * 4);
-    L.vs = take(L.slabs * cap * (kD / kG) * 4);
-    L.vz = take(L.slabs * cap * (kD / kG) * 4);
+    L.vs = take(L.slabs * cap * (kD / kG) * mb);
+    L.vz = take(L.slabs * cap * (kD / kG) * mb);
     L.kr = take(L.slabs * L.ring * kD * 2);
     L.vr = take(L.slabs * L.ring * kD * 2);
     L.total = off;
@@ -101,12 +103,12 @@ int kivi_cache_init(kivi_cache* cache, const kivi_cache_config* cfg, void* devic
     kivi_cache c = {};
     c.cfg = *cfg;
     const int64_t cap = cfg->store_capacity;
-    c.k_store = {reinterpret_cast<uint32_t*>(base + L.kc), reinterpret_cast<float*>(base + L.ks),
-                 reinterpret_cast<float*>(base + L.kz), cap * L.words, (cap / kG) * kD, cap,
-                 cfg->bits, cfg->group_size, cfg->head_dim, KIVI_KEYS};
-    c.v_store = {reinterpret_cast<uint32_t*>(base + L.vc), reinterpret_cast<float*>(base + L.vs),
-                 reinterpret_cast<float*>(base + L.vz), cap * L.words, cap * (kD / kG), cap,
-                 cfg->bits, cfg->group_size, cfg->head_dim, KIVI_VALUES};
+    c.k_store = {reinterpret_cast<uint32_t*>(base + L.kc), base + L.ks, base + L.kz,
+                 cap * L.words, (cap / kG) * kD, cap,
+                 cfg->bits, cfg->group_size, cfg->head_dim, KIVI_KEYS, cfg->meta_format};
+    c.v_store = {reinterpret_cast<uint32_t*>(base + L.vc), base + L.vs, base + L.vz,
+                 cap * L.words, cap * (kD / kG), cap,
+                 cfg->bits, cfg->group_size, cfg->head_dim, KIVI_VALUES, cfg->meta_format};
     c.k_ring = reinterpret_cast<uint16_t*>(base + L.kr);
     c.v_ring = reinterpret_cast<uint16_t*>(base + L.vr);
     c.ring = L.ring;

@@ -64,7 +64,7 @@ class CCacheConfig(ctypes.Structure):
         ("layers", ctypes.c_int32), ("batch", ctypes.c_int32), ("kv_heads", ctypes.c_int32),
         ("bits", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("group_size", ctypes.c_int32),
         ("residual_length", ctypes.c_int32), ("flush_tokens", ctypes.c_int32),
-        ("store_capacity", ctypes.c_int64),
+        ("store_capacity", ctypes.c_int64), ("meta_format", ctypes.c_int32),
     ]
 
 
@@ -324,9 +324,14 @@ class Cache:
     changes happen in the C calls."""
 
     def __init__(self, layers: int, batch: int, kv_heads: int, store_capacity: int, bits: int = 4,
-                 residual_length: int = 128, flush_tokens: int = GROUP, device="cuda"):
+                 residual_length: int = 128, flush_tokens: int = GROUP, device="cuda",
+                 meta: str = "f32"):
+        if meta not in ("f32", "f16"):
+            raise ValueError("meta must be 'f32' or 'f16'")
+        self.meta = meta
         self.cfg = CCacheConfig(layers, batch, kv_heads, bits, HEAD_DIM, GROUP, residual_length,
-                                flush_tokens, store_capacity)
+                                flush_tokens, store_capacity,
+                                KIVI_META_F16 if meta == "f16" else KIVI_META_F32)
         n = int(lib().kivi_cache_device_bytes(ctypes.byref(self.cfg)))
         if n == 0:
             raise KiviError(-3, "kivi_cache_device_bytes")
@@ -360,10 +365,11 @@ class Cache:
             cap, words = cs.cap, HEAD_DIM * cs.bits // 32
             meta = (self.slabs, cap // GROUP, HEAD_DIM) if kind == KIVI_KEYS else \
                 (self.slabs, cap, HEAD_DIM // GROUP)
+            mdt = torch.float16 if self.meta == "f16" else torch.float32
             out.append(Store(kind, self.slabs, cap, cs.bits,
                              codes=self._view(cs.codes, torch.int32, (self.slabs, cap, words)),
-                             scale=self._view(cs.scale, torch.float32, meta),
-                             zero=self._view(cs.zero, torch.float32, meta)))
+                             scale=self._view(cs.scale, mdt, meta),
+                             zero=self._view(cs.zero, mdt, meta), meta=self.meta))
         return out[0], out[1]
 
     def rings(self) -> tuple[torch.Tensor, torch.Tensor]:

@@ -199,7 +199,7 @@ def test_cache_rejects_bad_configs():
     assert L.kivi_cache_device_bytes(ctypes.byref(ok)) > 0
     for field, bad in (("layers", 0), ("layers", 257), ("bits", 3), ("head_dim", 64),
                        ("group_size", 64), ("flush_tokens", 48), ("residual_length", 100),
-                       ("store_capacity", 4100), ("batch", 0)):
+                       ("store_capacity", 4100), ("batch", 0), ("meta_format", 2)):
         cfg = kivi.CCacheConfig(2, 2, 8, 4, 128, 32, 128, 32, 4096)
         setattr(cfg, field, bad)
         assert L.kivi_cache_device_bytes(ctypes.byref(cfg)) == 0, field
@@ -229,3 +229,18 @@ def test_cache_init_checks_buffer_and_step_order():
     assert c.length == 0
     assert L.kivi_cache_attend_workspace_bytes(ctypes.byref(c), 8) >= \
         L.kivi_decode_attend_workspace_bytes(1, 8, 2, 256, 96)
+
+
+def test_cache_with_binary16_metadata_halves_the_metadata_sections():
+    L = kivi.lib()
+    f32 = kivi.CCacheConfig(2, 1, 2, 4, 128, 32, 64, 32, 256)
+    f16 = kivi.CCacheConfig(2, 1, 2, 4, 128, 32, 64, 32, 256, kivi.KIVI_META_F16)
+    n32 = L.kivi_cache_device_bytes(ctypes.byref(f32))
+    n16 = L.kivi_cache_device_bytes(ctypes.byref(f16))
+    slabs, cap = 4, 256
+    meta32 = 2 * (slabs * (cap // 32) * 128 * 4) + 2 * (slabs * cap * 4 * 4)
+    assert n32 - n16 == meta32 // 2
+    c = kivi.CCache()
+    assert L.kivi_cache_init(ctypes.byref(c), ctypes.byref(f16), FAKE, n16) == 0
+    assert c.k_store.meta_format == kivi.KIVI_META_F16 == c.v_store.meta_format
+    assert c.k_store.meta_bh_stride == 8 * 128 and c.v_store.meta_bh_stride == 256 * 4

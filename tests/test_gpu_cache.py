@@ -18,26 +18,37 @@ D = 128
 TOL = 2e-3
 
 CASES = [
-    # layers, batch, kv_heads, Hq, bits, R, F, capacity, prompt, steps
-    (2, 2, 2, 8, 4, 64, 32, 512, 150, 100),       # F = G
-    (1, 2, 8, 32, 4, 128, 128, 512, 200, 200),    # 128-token flushes (F = R)
-    (2, 1, 2, 4, 2, 0, 32, 256, 31, 70),          # no fp16 window kept (R = 0), 2-bit
-    (3, 1, 1, 8, 4, 64, 32, 256, 10, 120),        # prompt shorter than R
-    (1, 3, 2, 16, 4, 32, 32, 256, 0, 90),         # empty prompt
+    # layers, batch, kv_heads, Hq, bits, R, F, capacity, prompt, steps, scale/zero format
+    (2, 2, 2, 8, 4, 64, 32, 512, 150, 100, "f32"),       # F = G
+    (1, 2, 8, 32, 4, 128, 128, 512, 200, 200, "f32"),    # 128-token flushes (F = R)
+    (2, 1, 2, 4, 2, 0, 32, 256, 31, 70, "f32"),          # no fp16 window kept (R = 0), 2-bit
+    (3, 1, 1, 8, 4, 64, 32, 256, 10, 120, "f32"),        # prompt shorter than R
+    (1, 3, 2, 16, 4, 32, 32, 256, 0, 90, "f32"),         # empty prompt
+    (2, 2, 2, 8, 4, 64, 32, 512, 150, 100, "f16"),       # binary16 scale/zero
+    (2, 1, 2, 4, 2, 0, 32, 256, 31, 70, "f16"),
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=lambda c: "L%d-B%d-H%d-q%d-b%d-R%d-F%d-S%d" % (
-    c[0], c[1], c[2], c[3], c[4], c[5], c[6], c[8]))
+def _meta_equal(gpu: torch.Tensor, host: np.ndarray) -> bool:
+    """Metadata equal as bit patterns (binary16 stores: the host holds the
+    binary16 values widened, so their conversion is exact)."""
+    g = gpu.cpu().numpy()
+    if g.dtype == np.float16:
+        return np.array_equal(g.view(np.uint16), oracle.f32_to_f16(host))
+    return np.array_equal(g.view(np.uint32), np.ascontiguousarray(host).view(np.uint32))
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "L%d-B%d-H%d-q%d-b%d-R%d-F%d-S%d-%s" % (
+    c[0], c[1], c[2], c[3], c[4], c[5], c[6], c[8], c[10]))
 def test_decode_loop_matches_model(case):
-    layers, batch, kvh, Hq, bits, R, F, cap, S0, steps = case
+    layers, batch, kvh, Hq, bits, R, F, cap, S0, steps, meta = case
     seed = 9000 + S0 + R
     slabs = layers * batch * kvh
     per = batch * kvh
     note(f"cache loop layers={layers} batch={batch} kv_heads={kvh} Hq={Hq} bits={bits} R={R} F={F} "
-         f"capacity={cap} prompt={S0} steps={steps}")
-    c = kivi.Cache(layers, batch, kvh, cap, bits, R, F)
-    m = oracle.CacheModel(layers, batch, kvh, cap, bits, R, F)
+         f"capacity={cap} prompt={S0} steps={steps} meta={meta}")
+    c = kivi.Cache(layers, batch, kvh, cap, bits, R, F, meta=meta)
+    m = oracle.CacheModel(layers, batch, kvh, cap, bits, R, F, meta=meta)
     if S0:
         k0 = synth.kv_tensor(slabs, S0, keys=True, seed=seed, device="cuda")
         v0 = synth.kv_tensor(slabs, S0, keys=False, seed=seed, device="cuda")
@@ -70,10 +81,10 @@ def test_decode_loop_matches_model(case):
     g = Q // 32
     assert np.array_equal(ks.codes[:, :Q].cpu().numpy().view(np.uint32), m.kstore.codes[:, :Q])
     assert np.array_equal(vs.codes[:, :Q].cpu().numpy().view(np.uint32), m.vstore.codes[:, :Q])
-    assert np.array_equal(ks.scale[:, :g].cpu().numpy(), m.kstore.scale[:, :g])
-    assert np.array_equal(ks.zero[:, :g].cpu().numpy(), m.kstore.zero[:, :g])
-    assert np.array_equal(vs.scale[:, :Q].cpu().numpy(), m.vstore.scale[:, :Q])
-    assert np.array_equal(vs.zero[:, :Q].cpu().numpy(), m.vstore.zero[:, :Q])
+    assert _meta_equal(ks.scale[:, :g], m.kstore.scale[:, :g])
+    assert _meta_equal(ks.zero[:, :g], m.kstore.zero[:, :g])
+    assert _meta_equal(vs.scale[:, :Q], m.vstore.scale[:, :Q])
+    assert _meta_equal(vs.zero[:, :Q], m.vstore.zero[:, :Q])
     kr, vr = c.rings()
     rows = [(c.head + i) % c.ring for i in range(c.n_res)]
     assert c.n_res == m.length - Q
