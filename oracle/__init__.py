@@ -126,6 +126,8 @@ def lib():
             _i64, _i64, _i64, _int, _int, _i64,
             _u16p, _u16p, _i64, _i64, ctypes.c_double, _f64p]
         L.orc_decode_attend.restype = _int
+        L.orc_decode_attend_fmt.argtypes = L.orc_decode_attend.argtypes + [_int]
+        L.orc_decode_attend_fmt.restype = _int
         L.orc_flush_count.argtypes = [_i64, _i64, _i64]
         L.orc_flush_count.restype = _i64
         _lib = L
@@ -291,10 +293,11 @@ def dequantize(store: Store, t0: int, n: int, fmt: str = "f16") -> np.ndarray:
 
 def decode_attend(q, B: int, Hq: int, Hkv: int, kstore: Store | None, vstore: Store | None,
                   n_quant: int, k_res, v_res, n_res: int,
-                  softmax_scale: float | None = None) -> np.ndarray:
+                  softmax_scale: float | None = None, fmt: str = "f16") -> np.ndarray:
     """float64 [B][Hq][D] = softmax(q K^T * scale) V over store + residual.
 
-    ``k_res``/``v_res`` are fp16 [B*Hkv][R][D] with n_res <= R used rows."""
+    ``k_res``/``v_res`` are [B*Hkv][R][D] with n_res <= R used rows; q, the
+    residual and the store's reconstruction are fp16 or bf16 (``fmt``)."""
     q = _as_u16(q).reshape(B, Hq, -1)
     D = q.shape[2]
     if softmax_scale is None:
@@ -320,10 +323,10 @@ def decode_attend(q, B: int, Hq: int, Hkv: int, kstore: Store | None, vstore: St
     else:
         k_res = v_res = np.zeros(1, np.uint16)
         res_stride = 0
-    rc = lib().orc_decode_attend(_ptr(q, ctypes.c_uint16), B, Hq, Hkv, D, *args, n_quant,
-                                 _ptr(k_res, ctypes.c_uint16), _ptr(v_res, ctypes.c_uint16),
-                                 res_stride, n_res, float(softmax_scale),
-                                 _ptr(out, ctypes.c_double))
+    rc = lib().orc_decode_attend_fmt(_ptr(q, ctypes.c_uint16), B, Hq, Hkv, D, *args, n_quant,
+                                     _ptr(k_res, ctypes.c_uint16), _ptr(v_res, ctypes.c_uint16),
+                                     res_stride, n_res, float(softmax_scale),
+                                     _ptr(out, ctypes.c_double), FMT[fmt])
     if rc != 0:
         raise ValueError("oracle rejected the attend arguments")
     return out
@@ -331,7 +334,8 @@ def decode_attend(q, B: int, Hq: int, Hkv: int, kstore: Store | None, vstore: St
 
 def decode_attend_varlen(q, B: int, Hq: int, Hkv: int, kstore: Store | None,
                          vstore: Store | None, n_quant, max_n_quant: int, k_res, v_res,
-                         n_res, max_n_res: int, softmax_scale: float | None = None) -> np.ndarray:
+                         n_res, max_n_res: int, softmax_scale: float | None = None,
+                         fmt: str = "f16") -> np.ndarray:
     """float64 [B][Hq][D]: sequence b is ``decode_attend`` of a batch of one over
     its own slabs b*Hkv .. b*Hkv + Hkv - 1, with n_quant[b] store tokens and
     n_res[b] residual tokens, each clamped to [0, max]; a sequence left with no
@@ -350,7 +354,7 @@ def decode_attend_varlen(q, B: int, Hq: int, Hkv: int, kstore: Store | None,
                                kstore.slabs(lo, hi) if nq else None,
                                vstore.slabs(lo, hi) if nq else None, nq,
                                k_res[lo:hi] if nr else None, v_res[lo:hi] if nr else None, nr,
-                               softmax_scale)[0]
+                               softmax_scale, fmt)[0]
     return out
 
 

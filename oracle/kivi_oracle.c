@@ -476,15 +476,16 @@ int orc_dequantize(int kind, const uint32_t *codes, int64_t codes_bh_stride,
 /* dequantize + SDPA on the same compressed state).                   */
 /* ------------------------------------------------------------------ */
 
-int orc_decode_attend(const uint16_t *q, int64_t B, int Hq, int Hkv, int64_t D,
-                      const uint32_t *k_codes, const float *k_scale, const float *k_zero,
-                      const uint32_t *v_codes, const float *v_scale, const float *v_zero,
-                      int64_t codes_bh_stride, int64_t k_meta_bh_stride,
-                      int64_t v_meta_bh_stride, int bits, int G, int64_t n_quant,
-                      const uint16_t *k_res, const uint16_t *v_res,
-                      int64_t res_bh_stride, int64_t n_res,
-                      double softmax_scale, double *out)
+int orc_decode_attend_fmt(const uint16_t *q, int64_t B, int Hq, int Hkv, int64_t D,
+                          const uint32_t *k_codes, const float *k_scale, const float *k_zero,
+                          const uint32_t *v_codes, const float *v_scale, const float *v_zero,
+                          int64_t codes_bh_stride, int64_t k_meta_bh_stride,
+                          int64_t v_meta_bh_stride, int bits, int G, int64_t n_quant,
+                          const uint16_t *k_res, const uint16_t *v_res,
+                          int64_t res_bh_stride, int64_t n_res,
+                          double softmax_scale, double *out, int fmt)
 {
+    const widen_fn widen = widen_of(fmt);
     if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || n_quant < 0 || n_res < 0) return -1;
     if (n_quant > 0 && check_common(1, n_quant, D, bits, G) != 0) return -1;
     const int64_t N = n_quant + n_res;
@@ -502,17 +503,17 @@ int orc_decode_attend(const uint16_t *q, int64_t B, int Hq, int Hkv, int64_t D,
     for (int64_t b = 0; b < B; ++b) {
         for (int kv = 0; kv < Hkv; ++kv) {
             const int64_t bh = b * Hkv + kv;
-            /* K-hat and V-hat: the store's fp16 reconstruction, then the
-               residual rows, all widened exactly */
+            /* K-hat and V-hat: the store's 16-bit reconstruction (fp16 or
+               bfloat16, `fmt`), then the residual rows, all widened exactly */
             if (n_quant > 0) {
-                orc_dequantize(ORC_KEYS, k_codes + bh * codes_bh_stride, 0,
-                               k_scale + bh * k_meta_bh_stride,
-                               k_zero + bh * k_meta_bh_stride, 0,
-                               1, D, bits, G, 0, n_quant, kq, 0);
-                orc_dequantize(ORC_VALUES, v_codes + bh * codes_bh_stride, 0,
-                               v_scale + bh * v_meta_bh_stride,
-                               v_zero + bh * v_meta_bh_stride, 0,
-                               1, D, bits, G, 0, n_quant, vq, 0);
+                orc_dequantize_fmt(ORC_KEYS, k_codes + bh * codes_bh_stride, 0,
+                                   k_scale + bh * k_meta_bh_stride,
+                                   k_zero + bh * k_meta_bh_stride, 0,
+                                   1, D, bits, G, 0, n_quant, kq, 0, fmt);
+                orc_dequantize_fmt(ORC_VALUES, v_codes + bh * codes_bh_stride, 0,
+                                   v_scale + bh * v_meta_bh_stride,
+                                   v_zero + bh * v_meta_bh_stride, 0,
+                                   1, D, bits, G, 0, n_quant, vq, 0, fmt);
             }
             for (int64_t j = 0; j < N; ++j) {
                 for (int64_t d = 0; d < D; ++d) {
@@ -524,8 +525,8 @@ int orc_decode_attend(const uint16_t *q, int64_t B, int Hq, int Hkv, int64_t D,
                         kh = k_res[bh * res_bh_stride + (j - n_quant) * D + d];
                         vh = v_res[bh * res_bh_stride + (j - n_quant) * D + d];
                     }
-                    kk[j * D + d] = (double)orc_f16_to_f32(kh);
-                    vv[j * D + d] = (double)orc_f16_to_f32(vh);
+                    kk[j * D + d] = (double)widen(kh);
+                    vv[j * D + d] = (double)widen(vh);
                 }
             }
             for (int h = kv * group; h < (kv + 1) * group; ++h) {
@@ -534,7 +535,7 @@ int orc_decode_attend(const uint16_t *q, int64_t B, int Hq, int Hkv, int64_t D,
                 for (int64_t j = 0; j < N; ++j) {
                     double s = 0.0;
                     for (int64_t d = 0; d < D; ++d)
-                        s += (double)orc_f16_to_f32(qrow[d]) * kk[j * D + d];
+                        s += (double)widen(qrow[d]) * kk[j * D + d];
                     sc[j] = s * softmax_scale;
                     if (sc[j] > m) m = sc[j];
                 }
@@ -561,6 +562,21 @@ int orc_decode_attend(const uint16_t *q, int64_t B, int Hq, int Hkv, int64_t D,
    record", Generation 1 (flush/layer 512, 2016, 8160 for prompts of 559,
    2059, 8209 tokens with R = G = 32): whole groups of G among the tokens
    older than the newest R. */
+int orc_decode_attend(const uint16_t *q, int64_t B, int Hq, int Hkv, int64_t D,
+                      const uint32_t *k_codes, const float *k_scale, const float *k_zero,
+                      const uint32_t *v_codes, const float *v_scale, const float *v_zero,
+                      int64_t codes_bh_stride, int64_t k_meta_bh_stride,
+                      int64_t v_meta_bh_stride, int bits, int G, int64_t n_quant,
+                      const uint16_t *k_res, const uint16_t *v_res,
+                      int64_t res_bh_stride, int64_t n_res,
+                      double softmax_scale, double *out)
+{
+    return orc_decode_attend_fmt(q, B, Hq, Hkv, D, k_codes, k_scale, k_zero, v_codes, v_scale,
+                                 v_zero, codes_bh_stride, k_meta_bh_stride, v_meta_bh_stride,
+                                 bits, G, n_quant, k_res, v_res, res_bh_stride, n_res,
+                                 softmax_scale, out, ORC_F16);
+}
+
 int64_t orc_flush_count(int64_t S, int64_t R, int64_t G)
 {
     if (S <= R) return 0;

@@ -138,6 +138,17 @@ int orc_decode_attend(const uint16_t *q, int64_t B, int Hq, int Hkv, int64_t D,
                       int64_t res_bh_stride, int64_t n_res,
                       double softmax_scale, double *out);
 
+/* orc_decode_attend for bfloat16 (fmt ORC_BF16) or fp16 (ORC_F16): q, the
+   residual rows and the store's reconstruction are in that format. */
+int orc_decode_attend_fmt(const uint16_t *q, int64_t B, int Hq, int Hkv, int64_t D,
+                          const uint32_t *k_codes, const float *k_scale, const float *k_zero,
+                          const uint32_t *v_codes, const float *v_scale, const float *v_zero,
+                          int64_t codes_bh_stride, int64_t k_meta_bh_stride,
+                          int64_t v_meta_bh_stride, int bits, int G, int64_t n_quant,
+                          const uint16_t *k_res, const uint16_t *v_res,
+                          int64_t res_bh_stride, int64_t n_res,
+                          double softmax_scale, double *out, int fmt);
+
 /* Number of the oldest tokens of an S-token prefix that a flush quantizes
    when the newest R stay fp16 and only whole groups of G are flushed. */
 int64_t orc_flush_count(int64_t S, int64_t R, int64_t G);

@@ -9,7 +9,10 @@ bfloat16 instead of fp16; the packed store is the same).
   * brute force: random groups against the exact-rational emulation in
     _exact.py with bfloat16 rounding (it shares no arithmetic with the C
     oracle), including values outside fp16's range;
-  * the tensor flushes reduce to the group function on every group.
+  * the tensor flushes reduce to the group function on every group;
+  * the bfloat16 attend equals torch's float64 scaled_dot_product_attention
+    (a library routine) over the bfloat16 reconstruction of the store and
+    the bfloat16 residual, and a single token returns its value.
 """
 import numpy as np
 import pytest
@@ -127,3 +130,47 @@ def test_bf16_flushes_reduce_to_the_group_function(orc):
                 assert np.array_equal(rv[bh, s, 32 * j:32 * j + 32], rec)
     assert np.array_equal(orc.dequantize(ks, 0, S, fmt="bf16"), rk)
     assert np.array_equal(orc.dequantize(vs, 0, S, fmt="bf16"), rv)
+
+
+def _bf16_tensor(rng, shape, scale=1.0):
+    return _torch_f32_to_bf16((rng.standard_normal(shape) * scale).astype(np.float32))
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_bf16_attend_matches_torch_sdpa(orc, bits):
+    rng = np.random.default_rng(60 + bits)
+    B, Hq, Hkv, nq, nr = 2, 8, 2, 70, 9
+    BH = B * Hkv
+    k = _bf16_tensor(rng, (BH, nq, D), 3.0)
+    v = _bf16_tensor(rng, (BH, nq, D))
+    kr = _bf16_tensor(rng, (BH, 16, D), 3.0)
+    vr = _bf16_tensor(rng, (BH, 16, D))
+    q = _bf16_tensor(rng, (B, Hq, D))
+    ks = orc.Store(orc.KEYS, BH, 96, D, bits)
+    vs = orc.Store(orc.VALUES, BH, 96, D, bits)
+    orc.quantize_keys(k, ks, fmt="bf16", want_recon=False)
+    orc.quantize_values(v, vs, fmt="bf16", want_recon=False)
+    out = orc.decode_attend(q, B, Hq, Hkv, ks, vs, nq, kr, vr, nr, fmt="bf16")
+    K = np.concatenate([orc.dequantize(ks, 0, nq, fmt="bf16"), kr[:, :nr]], axis=1)
+    V = np.concatenate([orc.dequantize(vs, 0, nq, fmt="bf16"), vr[:, :nr]], axis=1)
+    K = _torch_bf16_to_f32(K).astype(np.float64).reshape(B, Hkv, nq + nr, D)
+    V = _torch_bf16_to_f32(V).astype(np.float64).reshape(B, Hkv, nq + nr, D)
+    g = Hq // Hkv
+    qt = torch.from_numpy(_torch_bf16_to_f32(q).astype(np.float64)).reshape(B, Hq, 1, D)
+    want = torch.nn.functional.scaled_dot_product_attention(
+        qt, torch.from_numpy(K).repeat_interleave(g, dim=1),
+        torch.from_numpy(V).repeat_interleave(g, dim=1)).reshape(B, Hq, D).numpy()
+    assert np.allclose(out, want, rtol=1e-12, atol=1e-12)
+    # the same bit patterns read as fp16 give a different result: the format
+    # reaches every input
+    assert not np.allclose(orc.decode_attend(q, B, Hq, Hkv, ks, vs, nq, kr, vr, nr), want)
+
+
+def test_bf16_attend_single_token_returns_its_value(orc):
+    rng = np.random.default_rng(3)
+    vr = _bf16_tensor(rng, (1, 1, D), 1e20)           # outside fp16's range
+    kr = _bf16_tensor(rng, (1, 1, D))
+    q = _bf16_tensor(rng, (1, 4, D))
+    out = orc.decode_attend(q, 1, 4, 1, None, None, 0, kr, vr, 1, fmt="bf16")
+    for h in range(4):
+        assert np.array_equal(out[0, h], _torch_bf16_to_f32(vr[0, 0]).astype(np.float64))
