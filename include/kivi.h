@@ -227,6 +227,30 @@ int kivi_decode_attend_varlen(const uint16_t* q, int64_t B, int32_t Hq, int32_t 
                               float* out, void* workspace, size_t workspace_bytes,
                               hipStream_t stream);
 
+/*
+ * The same two attends for bfloat16 caches: q, k_res and v_res hold
+ * bfloat16 bit patterns, and the stores (written by the _bf16 flushes, with
+ * binary32 scale/zero) are reconstructed to bfloat16 in registers, as
+ * kivi_dequantize_bf16 would.  QK^T and PV run on bfloat16 MFMA operands
+ * with fp32 accumulation; the softmax probabilities are rounded to bfloat16
+ * for PV (about 2^-9 relative), so the result is within 2e-3 + 2^-8 max|v|
+ * of the float64 definition over the bfloat16 reconstruction.  A store with
+ * binary16 scale/zero returns KIVI_ERR_UNSUPPORTED; everything else is as
+ * for kivi_decode_attend and kivi_decode_attend_varlen (same workspace).
+ */
+int kivi_decode_attend_bf16(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
+                            const kivi_store* k, const kivi_store* v, int64_t n_quant,
+                            const uint16_t* k_res, const uint16_t* v_res, int64_t res_bh_stride,
+                            int64_t n_res, float softmax_scale, float* out,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+int kivi_decode_attend_varlen_bf16(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
+                                   const kivi_store* k, const kivi_store* v,
+                                   const int32_t* n_quant, int64_t max_n_quant,
+                                   const uint16_t* k_res, const uint16_t* v_res,
+                                   int64_t res_bh_stride, const int32_t* n_res, int64_t max_n_res,
+                                   float softmax_scale, float* out, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
+
 /* Workspace bytes kivi_decode_attend needs for this shape (head_dim 128). */
 size_t kivi_decode_attend_workspace_bytes(int64_t B, int32_t Hq, int32_t Hkv,
                                           int64_t n_quant, int64_t n_res);

@@ -188,7 +188,7 @@ int decode_attend_entry(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
                         int64_t n_res, int64_t res_head, int64_t res_ring,
                         const int32_t* seq_n_quant, const int32_t* seq_n_res,
                         float softmax_scale, float* out, void* workspace, size_t workspace_bytes,
-                        hipStream_t stream) {
+                        hipStream_t stream, bool bf16) {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || n_quant < 0 || n_res < 0) return KIVI_ERR_SHAPE;
     if (Hq % Hkv != 0) return KIVI_ERR_SHAPE;
     const int group = Hq / Hkv;
@@ -203,6 +203,7 @@ int decode_attend_entry(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
     if (k->bits != v->bits) return KIVI_ERR_SHAPE;
     if (k->group_size != v->group_size || k->meta_format != v->meta_format) return KIVI_ERR_UNSUPPORTED;
     if (k->head_dim != kD || v->head_dim != kD) return KIVI_ERR_UNSUPPORTED;
+    if (bf16 && meta16(k)) return KIVI_ERR_UNSUPPORTED;        // bfloat16 stores keep binary32 metadata
     if (B == 0) return KIVI_OK;
     if (!q || !out) return KIVI_ERR_NULL;
     if (!aligned16(q) || !aligned16(out)) return KIVI_ERR_ALIGN;
@@ -235,6 +236,7 @@ int decode_attend_entry(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
     a.softmax_scale = softmax_scale; a.out = out;
     a.workspace = workspace; a.bits = k->bits; a.group = k->group_size;
     a.meta16 = meta16(k);
+    a.bf16 = bf16;
     return finish(kivi::launch_decode_attend(a, plan, stream));
 }
 
@@ -265,6 +267,31 @@ int kivi_decode_attend_varlen(const uint16_t* q, int64_t B, int32_t Hq, int32_t 
     return kivi::decode_attend_entry(q, B, Hq, Hkv, k, v, max_n_quant, k_res, v_res,
                                      res_bh_stride, max_n_res, 0, 0, n_quant, n_res,
                                      softmax_scale, out, workspace, workspace_bytes, stream);
+}
+
+int kivi_decode_attend_bf16(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
+                            const kivi_store* k, const kivi_store* v, int64_t n_quant,
+                            const uint16_t* k_res, const uint16_t* v_res, int64_t res_bh_stride,
+                            int64_t n_res, float softmax_scale, float* out,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return kivi::decode_attend_entry(q, B, Hq, Hkv, k, v, n_quant, k_res, v_res, res_bh_stride,
+                                     n_res, 0, 0, nullptr, nullptr, softmax_scale, out, workspace,
+                                     workspace_bytes, stream, true);
+}
+
+int kivi_decode_attend_varlen_bf16(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
+                                   const kivi_store* k, const kivi_store* v,
+                                   const int32_t* n_quant, int64_t max_n_quant,
+                                   const uint16_t* k_res, const uint16_t* v_res,
+                                   int64_t res_bh_stride, const int32_t* n_res, int64_t max_n_res,
+                                   float softmax_scale, float* out, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+    if (B > 0 && (!n_quant || !n_res)) return KIVI_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(n_quant) & 3u) != 0 ||
+        (reinterpret_cast<uintptr_t>(n_res) & 3u) != 0) return KIVI_ERR_ALIGN;
+    return kivi::decode_attend_entry(q, B, Hq, Hkv, k, v, max_n_quant, k_res, v_res,
+                                     res_bh_stride, max_n_res, 0, 0, n_quant, n_res,
+                                     softmax_scale, out, workspace, workspace_bytes, stream, true);
 }
 
 const char* kivi_status_string(int status) {

@@ -1,640 +1,11 @@
-// attend.hip -- fused dequantize + attend for one new query token per
-// sequence over a packed 2/4-bit store plus an fp16 residual window.
-//
-// Sources, cited by page title and section:
-//   [Benchmarks] VeloxQuant-MLX "Benchmarks" page, "KV-Cache Kernel Roofline:
-//                What Actually Limits Decode": the Metal decode+attend kernel
-//                ran one threadgroup per (batch, head) and was bound by how
-//                few threadgroups that dispatches (8 at B=1, H=8), not by
-//                bandwidth; head-packing K/V across query heads cut the
-//                threadgroup count further and lost.
-//   [Metal post] blog post "A 5.65x Metal Kernel That Made My LLM Exactly 0%
-//                Faster", "What we're actually optimizing" (the newest tokens
-//                stay fp16) and "So why does the kernel ship?" (dequantize
-//                in registers inside attention).
-//
-// Design for MI355X: one wave per (sequence, kv head, token split).  The
-// wave serves every query head that shares the kv head, so each packed
-// byte is read from HBM once; the token axis is split so the grid reaches
-// thousands of workgroups even at B=1 (which answers the occupancy limit the
-// pages measured).  Partials (m, l, o[128]) go to the workspace and a second
-// kernel merges them with the log-sum-exp rule.
-//
-// Arithmetic: QK^T and PV run on MFMA (fp16 operands, fp32 accumulation).  K
-// and V are dequantized in registers to fp16 with one mixed-precision FMA per
-// element (within one fp16 rounding of the stored reconstruction); q enters
-// exactly, softmax probabilities are rounded to fp16 for PV, and the online
-// softmax runs in fp32, base 2.
-//
-// Grid: one 64-lane wave per (sequence, kv head, split of the token axis);
-// each wave walks its split in 32-token steps, one key group per step, with
-// the step's key and value metadata staged through LDS.
+// attend.hip -- the decode attend for fp16 caches (the partial kernel of
+// attend_device.h), the split plan, and the log-sum-exp combine kernel that
+// both the fp16 and the bfloat16 attends finish with.
 #include <algorithm>
 
-#include "kivi_device.h"
-#include "kivi_launch.h"
+#include "attend_device.h"
 
 namespace kivi {
-
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef float float4_t __attribute__((ext_vector_type(4)));
-
-// 8 fp16 values in 4 VGPRs: one MFMA operand of one lane.
-union Frag {
-    half8_t h;
-    uint32_t u[4];
-};
-
-// Three waves per SIMD (at most 168 VGPRs, which hold three steps of loads
-// in flight without spilling; four would need 128 and spill), so the chip
-// holds 256 CUs x 4 SIMDs x 3 = 3072 of these waves at once.  Each wave
-// keeps KIVI_ATTEND_NBUF - 1 steps of loads in flight while it computes one.
-#ifndef KIVI_ATTEND_WAVES_PER_SIMD
-#define KIVI_ATTEND_WAVES_PER_SIMD 3
-#endif
-#ifndef KIVI_ATTEND_NBUF
-#define KIVI_ATTEND_NBUF 3
-#endif
-#define KIVI_ATTEND_OCCUPANCY __attribute__((amdgpu_waves_per_eu(KIVI_ATTEND_WAVES_PER_SIMD)))
-constexpr int64_t kWaveSlots = 256 * 4 * KIVI_ATTEND_WAVES_PER_SIMD;
-constexpr int kNBuf = KIVI_ATTEND_NBUF;
-
-constexpr int kStep = 32;             // tokens per wave step (one key group)
-constexpr int64_t kMaxStepsPerWave = 64;
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr uint32_t kMagic = 0x64006400u;   // fp16 1024.0 in both halves
-
-// v_mfma_f32_16x16x32_f16 lane layout (gfx950, wave64), lane l = 16*q + n:
-//   A (16x32): lane l holds row m = n, columns 8q .. 8q+7 (slot s = column - 8q)
-//   B (32x16): lane l holds rows 8q .. 8q+7, column n
-//   D (16x16 fp32): lane l holds rows 4q .. 4q+3, column n
-// The product only pairs A slot s of lane (q, m) with B slot s of lane (q, n),
-// so any bijection channel <-> (q, slot) used on both sides is valid.
-//
-// Channel order inside an 8-channel unit: the codes of channels j and j+4
-// come out of one SIMD-within-register extraction, so slot 2j holds channel
-// j and slot 2j+1 channel j+4 (j = 0..3).  Key unit kb of lane group q is
-// channels 32q + 8kb .. 32q + 8kb + 7.
-
-// (x & mask) | magic in one v_bitop3_b32 (truth table 0xEA = (a & b) | c).
-__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t magic) {
-    return __builtin_amdgcn_bitop3_b32(x, mask, magic, 0xEA);
-}
-
-// Four fp16 pairs from the 8 codes of one 8-channel unit: pair j holds the
-// codes of channels j and j+4.  A code masked in place at bit offset e of
-// the low mantissa byte under the exponent of 1024 reads as 1024 + 2^e code
-// exactly, so no shift is needed for e < 8; the factor 2^-e goes into the
-// staged scale (kscale_factor).  4-bit: one code word, e = 4 (j & 1) after
-// one shift by 8 for j >= 2.  2-bit: the unit's half of a word spread to
-// bytes 0 and 2 first, e = 2 j.
-template <int BITS>
-__device__ __forceinline__ void code_pairs(uint32_t w, int half, uint32_t (&p)[4]) {
-    if constexpr (BITS == 4) {
-        const uint32_t w8 = w >> 8;
-        p[0] = and_or(w, 0x000F000Fu, kMagic);
-        p[1] = and_or(w, 0x00F000F0u, kMagic);
-        p[2] = and_or(w8, 0x000F000Fu, kMagic);
-        p[3] = and_or(w8, 0x00F000F0u, kMagic);
-    } else {
-        const uint32_t sel = half ? 0x0C030C02u : 0x0C010C00u;
-        const uint32_t x = __builtin_amdgcn_perm(w, w, sel);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) p[j] = and_or(x, 0x00030003u << (2 * j), kMagic);
-    }
-}
-
-// 2^-e for key channel c (c & 3 = j is its pair in the unit, see code_pairs).
-template <int BITS>
-__device__ __forceinline__ float kscale_factor(int c) {
-    if constexpr (BITS == 4) return (c & 1) ? 0.0625f : 1.0f;
-    else return __builtin_ldexpf(1.0f, -2 * (c & 3));
-}
-
-// code * scale + zero as one mixed-precision FMA with an fp16 result:
-// c16 = 1024 + code exactly and zp = RN32(zero - 1024 s), so the result is
-// code*s + zero up to 2^-24 (|zero| + 1024 s) plus the fp16 rounding (the
-// attend is checked against the float64 definition to 2e-3, not bit-exactly).
-// Both halves of one fp16 pair register: lo = fma(c.lo, s0, z0), hi =
-// fma(c.hi, s1, z1), each rounded to fp16.  Written in C, not inline asm, so
-// the compiler sees the register writes and keeps the wait states an MFMA
-// needs after a VALU write of its operands.
-__device__ __forceinline__ uint32_t deq2(uint32_t pair, float s0, float z0, float s1, float z1) {
-    const half2_t c = as_h2(pair);
-    half2_t r;
-    r[0] = static_cast<_Float16>(__builtin_fmaf(static_cast<float>(c[0]), s0, z0));
-    r[1] = static_cast<_Float16>(__builtin_fmaf(static_cast<float>(c[1]), s1, z1));
-    return as_u32(r);
-}
-
-// lane exchanges across the four 16-lane rows (see kivi_device.h)
-__device__ __forceinline__ float rows_max(float v) {
-    auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = __builtin_elementwise_maximum(__uint_as_float(p[0]), __uint_as_float(p[1]));
-    p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __builtin_elementwise_maximum(__uint_as_float(p[0]), __uint_as_float(p[1]));
-}
-__device__ __forceinline__ float rows_sum(float v) {
-    auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
-    p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
-}
-
-// The slab of one (sequence, kv head) as raw buffer resources whose extent
-// ends at store token n_quant: a load past the extent returns zero, so the
-// masked tokens of a partial last step read finite zeros and no load leaves
-// the slab.  Word 3 is the raw-buffer format of gfx9-family parts (32-bit
-// data format, no swizzle, no thread-id indexing).
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-constexpr int kRsrcWord3 = 0x00020000;
-// Cache-policy operand of the store loads: the nontemporal hint (`nt` on
-// gfx950).  A call reads each packed byte once; with the hint the B=32,
-// 16384-token attend ran 7-8% faster in a side-by-side run.
-constexpr int kStreamLoad = 2;
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kRsrcWord3);
-}
-
-// A step start whose every load lies past the buffers' extent: the ABI
-// keeps n_quant below 2^24 tokens, and every buffer's offset for token t is
-// t times its bytes per token (key metadata: per token of the group), so a
-// start at 2^25 lands at twice any buffer's extent.  The largest such
-// offsets are 2^25 x 64 B of codes and 2^25 x 16 B of binary32 metadata;
-// lane and instruction offsets keep all of them below 2^32.
-constexpr uint32_t kFarToken = 1u << 25;
-
-struct StoreView {
-    rsrc_t kc, ks, kz;      // key codes, scale, zero
-    rsrc_t vc, vs, vz;      // value codes, scale, zero
-};
-
-// Byte offsets of a lane's loads at step t0 = 0; a step adds t0 times the
-// bytes per token (key metadata: t0 / G groups of 128 pairs).
-struct LaneOffsets {
-    uint32_t k;             // key codes of token n, the lane's 32 channels
-    uint32_t v;             // value code word of token 4q, the lane's 8 channels
-    uint32_t km;            // key scale / zero of channels 2l, 2l+1
-    uint32_t vm;            // value scale / zero of token l & 31: groups 2(l>>5), +1 (G = 32),
-                            // groups 0, 1 (G = 64) or group 0 (G = 128)
-};
-
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// Loads of one 32-token step of store tokens, issued one step ahead of the
-// compute that uses them.
-// Scale and zero stay as loaded (binary32 pairs, or binary16 pairs in the
-// low word) until the step that uses them, so that issuing a prefetch never
-// waits on an earlier load.
-struct StepLoad {
-    uint32_t kw[2][4];      // key code words of token t0 + 16*blk + n (lane's 32 channels)
-    u32x2 ks, kz;           // key scale / zero of channels 2l, 2l+1 of the step's group
-    u32x2 vs, vz;           // value scale / zero of token t0 + (l & 31), groups 2(l>>5), +1
-    uint32_t vw[8];         // value code word holding the lane's 8 channels, its 8 tokens
-};
-
-// The pair of a StepLoad field as floats: MB = 4 bytes (binary32) or 2
-// (binary16, widened exactly).
-template <int MB>
-__device__ __forceinline__ float2 meta_pair(u32x2 v) {
-    if constexpr (MB == 4) return make_float2(__uint_as_float(v.x), __uint_as_float(v.y));
-    const half2_t h = as_h2(v.x);
-    return make_float2(static_cast<float>(h[0]), static_cast<float>(h[1]));
-}
-
-// Token (within the step) of PV slot s for lane group q: the order in which
-// QK^T leaves each lane its scores (rows 4q .. 4q+3 of both 16-token blocks).
-__device__ __forceinline__ int pv_token(int q, int s) { return 16 * (s >> 2) + 4 * q + (s & 3); }
-
-template <int BITS, int G, int MB>
-__device__ __forceinline__ void issue_step(StepLoad& L, const StoreView& S, const LaneOffsets& O,
-                                           uint32_t t0, int n) {
-    constexpr uint32_t kRow = kHeadDim * BITS / 8;          // code bytes per token
-    const uint32_t ko = O.k + t0 * kRow;
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-        if constexpr (BITS == 4) {
-            const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(S.kc, ko + 16 * kRow * blk, 0, kStreamLoad);
-            L.kw[blk][0] = t.x; L.kw[blk][1] = t.y; L.kw[blk][2] = t.z; L.kw[blk][3] = t.w;
-        } else {
-            const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(S.kc, ko + 16 * kRow * blk, 0, kStreamLoad);
-            L.kw[blk][0] = t.x; L.kw[blk][1] = t.x; L.kw[blk][2] = t.y; L.kw[blk][3] = t.y;
-        }
-    }
-    // key metadata of the step's group (a 32-token step never crosses one):
-    // two channels' pairs, 2 * MB bytes
-    const uint32_t kmo = O.km + (t0 / G) * (kHeadDim * MB);
-    // value metadata: 128/G pairs per token; the lane's one or two groups
-    const uint32_t vmo = O.vm + (kHeadDim * MB / G) * t0;
-    if constexpr (MB == 4) {
-        L.ks = __builtin_amdgcn_raw_buffer_load_b64(S.ks, kmo, 0, kStreamLoad);
-        L.kz = __builtin_amdgcn_raw_buffer_load_b64(S.kz, kmo, 0, kStreamLoad);
-        if constexpr (G == 128) {
-            L.vs = u32x2{__builtin_amdgcn_raw_buffer_load_b32(S.vs, vmo, 0, kStreamLoad), 0u};
-            L.vz = u32x2{__builtin_amdgcn_raw_buffer_load_b32(S.vz, vmo, 0, kStreamLoad), 0u};
-        } else {
-            L.vs = __builtin_amdgcn_raw_buffer_load_b64(S.vs, vmo, 0, kStreamLoad);
-            L.vz = __builtin_amdgcn_raw_buffer_load_b64(S.vz, vmo, 0, kStreamLoad);
-        }
-    } else {
-        L.ks = u32x2{__builtin_amdgcn_raw_buffer_load_b32(S.ks, kmo, 0, kStreamLoad), 0u};
-        L.kz = u32x2{__builtin_amdgcn_raw_buffer_load_b32(S.kz, kmo, 0, kStreamLoad), 0u};
-        if constexpr (G == 128) {
-            L.vs = u32x2{static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(S.vs, vmo, 0, kStreamLoad)), 0u};
-            L.vz = u32x2{static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(S.vz, vmo, 0, kStreamLoad)), 0u};
-        } else {
-            L.vs = u32x2{__builtin_amdgcn_raw_buffer_load_b32(S.vs, vmo, 0, kStreamLoad), 0u};
-            L.vz = u32x2{__builtin_amdgcn_raw_buffer_load_b32(S.vz, vmo, 0, kStreamLoad), 0u};
-        }
-    }
-    const uint32_t vo = O.v + t0 * kRow;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-        const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(S.vc, vo + (16 * (s >> 2) + (s & 3)) * kRow, 0, kStreamLoad);
-        // 2-bit: bring the lane's 8 channels (half of the word) to the low half
-        L.vw[s] = BITS == 4 ? w : (w >> (16 * (n & 1)));
-    }
-}
-
-// Keeps the compiler from moving LDS accesses across this point.  The
-// workgroup is one wave and a wave's LDS instructions execute in order, so
-// no hardware barrier is needed between a lane's write and another lane's
-// later read.
-__device__ __forceinline__ void lds_order() { __atomic_signal_fence(__ATOMIC_SEQ_CST); }
-
-// Rows are padded so that lanes reading different channel windows or groups
-// in the same LDS cycle hit different banks.
-constexpr int kKPad = 4;                      // floats of padding per 32 channels
-constexpr int kVRow = kStep + 4;              // padded row of 32 tokens
-__device__ __forceinline__ int kidx(int ch) { return ch + kKPad * (ch >> 5); }
-
-struct Smem {
-    alignas(16) float ks[kHeadDim + kKPad * 4];       // key scale of the step's group
-    alignas(16) float kz[kHeadDim + kKPad * 4];       // key zero - 1024 * scale
-    alignas(16) float vs[kHeadDim / kGroup][kVRow];   // value scale, [group][token]
-    alignas(16) float vz[kHeadDim / kGroup][kVRow];   // value zero - 1024 * scale
-    alignas(16) uint4 bq[4][64];                       // QK^T B operand (queries), [unit][lane]
-};
-
-// The QK^T B operand of channel unit kb, kept in LDS rather than in 16
-// registers across the step loop (the registers hold the prefetched loads).
-__device__ __forceinline__ Frag query_frag(const Smem& sm, int kb, int l) {
-    const uint4 v = sm.bq[kb][l];
-    Frag f;
-    f.u[0] = v.x; f.u[1] = v.y; f.u[2] = v.z; f.u[3] = v.w;
-    return f;
-}
-
-// Online-softmax state of one lane: head n, channels 32q + 8r + i of acc_o[i][r].
-struct SoftState {
-    float m_run;
-    float l_part;
-    float4_t acc_o[8];
-};
-
-// The running max m only moves when a step's max exceeds it by more than
-// kSlack (base 2), so most steps skip rescaling the accumulators; the
-// unnormalized probabilities stay <= 2^kSlack = 256, exact enough in fp16
-// (relative precision is unchanged) and far from its range limit.
-constexpr float kSlack = 8.0f;
-
-// Online softmax over one step's scores (base 2) and the PV B operand.
-// Lane (q, n) holds head n's scores of step tokens 16*blk + 4q + r; with
-// MASK, tokens at or past `limit` (step-relative) get probability 0.  The
-// scale c2 = softmax_scale * log2(e) is positive, so the max is taken over
-// the raw scores and scaled once.
-template <bool MASK>
-__device__ __forceinline__ Frag softmax_step(const float4_t (&acc_s)[2], SoftState& st, float c2,
-                                             int limit, int q) {
-    float sv[8];
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float sc = acc_s[blk][r];
-            if constexpr (MASK) sc = (16 * blk + 4 * q + r) < limit ? sc : -INFINITY;
-            sv[4 * blk + r] = sc;
-        }
-    float mloc = sv[0];
-#pragma unroll
-    for (int s = 1; s < 8; ++s) mloc = __builtin_elementwise_maximum(mloc, sv[s]);
-    const float m_step = rows_max(mloc) * c2;
-    const float m_new = m_step > st.m_run + kSlack ? m_step : st.m_run;
-    const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);   // 1 when m did not move
-    st.m_run = m_new;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) sv[s] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[s], c2, -m_new));
-    float psum = sv[0];
-#pragma unroll
-    for (int s = 1; s < 8; ++s) psum += sv[s];
-    st.l_part = __builtin_fmaf(st.l_part, alpha, psum);
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) st.acc_o[i] *= alpha;
-    }
-    Frag bp;                                  // P^T, slot s <-> step token pv_token(q, s)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        half2_t h;
-        h[0] = static_cast<_Float16>(sv[2 * j]);
-        h[1] = static_cast<_Float16>(sv[2 * j + 1]);
-        bp.u[j] = as_u32(h);
-    }
-    return bp;
-}
-
-__device__ __forceinline__ Frag softmax_any(const float4_t (&acc_s)[2], SoftState& st, float c2,
-                                            int limit, int q) {
-    if (limit >= kStep) return softmax_step<false>(acc_s, st, c2, limit, q);
-    return softmax_step<true>(acc_s, st, c2, limit, q);
-}
-
-// One step of store tokens [t0, t0 + 32), tokens at or past n_quant masked.
-template <int BITS, int G, int MB>
-__device__ __forceinline__ void store_step(const StepLoad& L, Smem& sm, SoftState& st,
-                                           int t0, int n_quant, float c2,
-                                           int l, int n, int q) {
-    // ---- stage this step's metadata in LDS (zero' = zero - 1024 * scale')
-    lds_order();
-    {
-        // key scale times 2^-e of its channel's code position (code_pairs)
-        const float2 ks = meta_pair<MB>(L.ks), kz = meta_pair<MB>(L.kz);
-        const float s0 = ks.x * kscale_factor<BITS>(2 * l);
-        const float s1 = ks.y * kscale_factor<BITS>(2 * l + 1);
-        *reinterpret_cast<float2*>(&sm.ks[kidx(2 * l)]) = make_float2(s0, s1);
-        *reinterpret_cast<float2*>(&sm.kz[kidx(2 * l)]) =
-            make_float2(__builtin_fmaf(-1024.0f, s0, kz.x), __builtin_fmaf(-1024.0f, s1, kz.y));
-    }
-    {
-        // lanes l and l + 32 hold the same token; for G = 64 and 128 they
-        // hold the same groups too and write the same values
-        const float2 vs = meta_pair<MB>(L.vs), vz = meta_pair<MB>(L.vz);
-        const int tt = l & 31;
-        const int gg = G == 32 ? (l >> 5) * 2 : 0;
-        sm.vs[gg][tt] = vs.x;
-        sm.vz[gg][tt] = __builtin_fmaf(-1024.0f, vs.x, vz.x);
-        if constexpr (G != 128) {
-            sm.vs[gg + 1][tt] = vs.y;
-            sm.vz[gg + 1][tt] = __builtin_fmaf(-1024.0f, vs.y, vz.y);
-        }
-    }
-    lds_order();
-
-    // ---- S^T = K Q^T, token t0 + 16*blk + n, channel unit kb of group q
-    float4_t acc_s[2] = {float4_t{0.0f, 0.0f, 0.0f, 0.0f}, float4_t{0.0f, 0.0f, 0.0f, 0.0f}};
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-        const int cb = kidx(32 * q + 8 * kb);
-        const float4 s0 = *reinterpret_cast<const float4*>(&sm.ks[cb]);
-        const float4 s1 = *reinterpret_cast<const float4*>(&sm.ks[cb + 4]);
-        const float4 z0 = *reinterpret_cast<const float4*>(&sm.kz[cb]);
-        const float4 z1 = *reinterpret_cast<const float4*>(&sm.kz[cb + 4]);
-        const float sl[4] = {s0.x, s0.y, s0.z, s0.w}, sh[4] = {s1.x, s1.y, s1.z, s1.w};
-        const float zl[4] = {z0.x, z0.y, z0.z, z0.w}, zh[4] = {z1.x, z1.y, z1.z, z1.w};
-        const Frag bq = query_frag(sm, kb, l);
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-            uint32_t pr[4];
-            code_pairs<BITS>(L.kw[blk][kb], kb & 1, pr);
-            Frag ka;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) ka.u[j] = deq2(pr[j], sl[j], zl[j], sh[j], zh[j]);
-            acc_s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka.h, bq.h, acc_s[blk], 0, 0, 0);
-        }
-    }
-
-    const Frag bp = softmax_any(acc_s, st, c2, n_quant - t0, q);
-
-    // ---- O^T += V^T P^T: MFMA i covers channels 8m + i, m = 0..15.  Slot s of
-    // lane (q, m) is channel 8m + i of step token pv_token(q, s).
-    const int vg = n / (G / 8);                 // value group of the lane's channels 8n .. 8n+7
-    const float4 vsa = *reinterpret_cast<const float4*>(&sm.vs[vg][4 * q]);
-    const float4 vsb = *reinterpret_cast<const float4*>(&sm.vs[vg][16 + 4 * q]);
-    const float4 vza = *reinterpret_cast<const float4*>(&sm.vz[vg][4 * q]);
-    const float4 vzb = *reinterpret_cast<const float4*>(&sm.vz[vg][16 + 4 * q]);
-    const float vsc[8] = {vsa.x, vsa.y, vsa.z, vsa.w, vsb.x, vsb.y, vsb.z, vsb.w};
-    const float vzp[8] = {vza.x, vza.y, vza.z, vza.w, vzb.x, vzb.y, vzb.z, vzb.w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        // code of channel i of the lane's 8 (4-bit: nibble i; 2-bit: field i)
-        constexpr uint32_t kMask = BITS == 4 ? 0x000F000Fu : 0x00030003u;
-        const uint32_t byte = BITS == 4 ? (i >> 1) : (i >> 2);
-        const uint32_t shift = BITS == 4 ? 4 * (i & 1) : 2 * (i & 3);
-        const uint32_t sel = 0x0C000C00u | ((4u + byte) << 16) | byte;
-        Frag va;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t x = __builtin_amdgcn_perm(L.vw[2 * j + 1], L.vw[2 * j], sel);
-            const uint32_t pr = and_or(x >> shift, kMask, kMagic);
-            va.u[j] = deq2(pr, vsc[2 * j], vzp[2 * j], vsc[2 * j + 1], vzp[2 * j + 1]);
-        }
-        st.acc_o[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va.h, bp.h, st.acc_o[i], 0, 0, 0);
-    }
-}
-
-// One step of fp16 residual tokens [t0, t0 + 32), tokens at or past n_res masked.
-// Residual token i of the slab is row (head + i) mod ring (head < ring).
-__device__ __forceinline__ int ring_row(int tok, int head, int ring) {
-    const int r = tok + head;
-    return r >= ring ? r - ring : r;
-}
-
-__device__ __forceinline__ void residual_step(const uint16_t* kr, const uint16_t* vr, const Smem& sm,
-                                              SoftState& st, int t0, int n_res, float c2,
-                                              int l, int n, int q, int head, int ring) {
-    const int last = n_res - 1;
-    float4_t acc_s[2] = {float4_t{0.0f, 0.0f, 0.0f, 0.0f}, float4_t{0.0f, 0.0f, 0.0f, 0.0f}};
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-        const int tok = ring_row(min(t0 + 16 * blk + n, last), head, ring);
-        const uint4* src = reinterpret_cast<const uint4*>(kr + tok * kHeadDim + 32 * q);
-        uint32_t rn[16];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const uint4 t = src[v];
-            rn[4 * v] = t.x; rn[4 * v + 1] = t.y; rn[4 * v + 2] = t.z; rn[4 * v + 3] = t.w;
-        }
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            Frag ka;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int c0 = 8 * kb + j, c1 = 8 * kb + j + 4;
-                const uint32_t s0 = (c0 & 1) ? 0x0302u : 0x0100u;
-                const uint32_t s1 = (c1 & 1) ? 0x0706u : 0x0504u;
-                ka.u[j] = __builtin_amdgcn_perm(rn[c1 >> 1], rn[c0 >> 1], (s1 << 16) | s0);
-            }
-            acc_s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka.h, query_frag(sm, kb, l).h, acc_s[blk], 0, 0, 0);
-        }
-    }
-    const Frag bp = softmax_any(acc_s, st, c2, n_res - t0, q);
-    // V rows: lane (q, m=n) takes channels 8n .. 8n+7 of its 8 tokens
-    uint4 vrow[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-        const int tok = ring_row(min(t0 + pv_token(q, s), last), head, ring);
-        vrow[s] = *reinterpret_cast<const uint4*>(vr + tok * kHeadDim + 8 * n);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        Frag va;
-        const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t* a0 = reinterpret_cast<const uint32_t*>(&vrow[2 * j]);
-            const uint32_t* a1 = reinterpret_cast<const uint32_t*>(&vrow[2 * j + 1]);
-            va.u[j] = __builtin_amdgcn_perm(a1[i >> 1], a0[i >> 1], sel);
-        }
-        st.acc_o[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va.h, bp.h, st.acc_o[i], 0, 0, 0);
-    }
-}
-
-// One wave: sequence b, kv head kv, one split.  The token axis of a slab is
-// the store tokens [0, n_quant) in steps_q 32-token steps followed by the
-// residual tokens [0, n_res); split s covers the steps [s*spw, (s+1)*spw) of
-// that axis, so one wave may finish the store and start the residual.
-// Offsets within a slab fit in 32 bits: the ABI keeps n_quant and n_res
-// below 2^24 tokens.
-template <int BITS, int GQA, int G, int MB>
-__global__ __launch_bounds__(64) KIVI_ATTEND_OCCUPANCY void attend_partial_kernel(const AttendArgs a, int spw, int steps_q,
-                                                            int64_t n_split, float* __restrict__ ws_o,
-                                                            float* __restrict__ ws_ml)
-{
-    __shared__ Smem sm;
-    const int l = threadIdx.x;
-    const int n = l & 15;
-    const int q = l >> 4;
-    const int split = blockIdx.x;
-    const int64_t bkv = blockIdx.y;
-    const int64_t b = bkv / a.Hkv;
-    const int kv = static_cast<int>(bkv - b * a.Hkv);
-    const int64_t qrow0 = b * a.Hq + static_cast<int64_t>(kv) * GQA;
-
-    // Token counts of this sequence: the uniform bounds, or the per-sequence
-    // lengths clamped to them (so no load can leave the bounded slab).
-    int nq = static_cast<int>(a.n_quant);
-    int nr = static_cast<int>(a.n_res);
-    if (a.seq_n_quant) {
-        nq = min(max(a.seq_n_quant[b], 0), nq);
-        nr = min(max(a.seq_n_res[b], 0), nr);
-    }
-    const int s0 = split * spw, s1 = s0 + spw;
-    const int j0 = s0 * kStep;                                  // store tokens [j0, j1)
-    const int j1 = min(min(s1, steps_q) * kStep, nq);
-    const int r0 = max(s0 - steps_q, 0) * kStep;                // residual tokens [r0, r1)
-    const int r1 = min(max(s1 - steps_q, 0) * kStep, nr);
-    const bool has_store = j0 < j1;
-
-    // Store part: buffer views and the first two steps' loads, issued before
-    // the query so the two HBM latencies overlap.
-    constexpr int kWords = kHeadDim * BITS / 32;
-    constexpr int kMetaPerTok = kHeadDim / G;
-    StoreView S;
-    LaneOffsets O;
-    StepLoad buf[kNBuf];
-    // Every prefetch is issued, also past the split's end (to a token far
-    // outside the buffers' extent, which the buffer unit answers with zeros
-    // and no memory access): a conditional issue makes the compiler wait for
-    // all outstanding loads at the join.
-    const auto pref = [j1](int t) { return t < j1 ? static_cast<uint32_t>(t) : kFarToken; };
-    if (has_store) {
-        const uint32_t n_groups = static_cast<uint32_t>((nq + G - 1) / G);
-        S.kc = make_rsrc(a.k_codes + bkv * a.k_codes_bh_stride, static_cast<uint32_t>(nq) * kWords * 4u);
-        const char* kmeta_s = static_cast<const char*>(a.k_scale) + bkv * a.k_meta_bh_stride * MB;
-        const char* kmeta_z = static_cast<const char*>(a.k_zero) + bkv * a.k_meta_bh_stride * MB;
-        const char* vmeta_s = static_cast<const char*>(a.v_scale) + bkv * a.v_meta_bh_stride * MB;
-        const char* vmeta_z = static_cast<const char*>(a.v_zero) + bkv * a.v_meta_bh_stride * MB;
-        S.ks = make_rsrc(kmeta_s, n_groups * kHeadDim * MB);
-        S.kz = make_rsrc(kmeta_z, n_groups * kHeadDim * MB);
-        S.vc = make_rsrc(a.v_codes + bkv * a.v_codes_bh_stride, static_cast<uint32_t>(nq) * kWords * 4u);
-        S.vs = make_rsrc(vmeta_s, static_cast<uint32_t>(nq) * kMetaPerTok * MB);
-        S.vz = make_rsrc(vmeta_z, static_cast<uint32_t>(nq) * kMetaPerTok * MB);
-        O.k = static_cast<uint32_t>(n * kWords + (BITS == 4 ? 4 * q : 2 * q)) * 4u;
-        O.v = static_cast<uint32_t>(4 * q * kWords + (BITS == 4 ? n : (n >> 1))) * 4u;
-        O.km = static_cast<uint32_t>(l) * (2u * MB);
-        O.vm = G == 32 ? static_cast<uint32_t>(l & 31) * (4u * MB) + static_cast<uint32_t>(l >> 5) * (2u * MB)
-                       : static_cast<uint32_t>(l & 31) * (kMetaPerTok * MB);
-#pragma unroll
-        for (int u = 0; u + 1 < kNBuf; ++u) issue_step<BITS, G, MB>(buf[u], S, O, pref(j0 + u * kStep), n);
-    }
-
-    // B operand of QK^T: q of head n (zero for n >= GQA) in slot order.
-    {
-        Frag bq[4];
-        uint32_t qn[16];                      // channels 32q .. 32q+31, natural order
-        if (n < GQA) {
-            const uint4* src = reinterpret_cast<const uint4*>(a.q + (qrow0 + n) * kHeadDim + 32 * q);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const uint4 t = src[v];
-                qn[4 * v] = t.x; qn[4 * v + 1] = t.y; qn[4 * v + 2] = t.z; qn[4 * v + 3] = t.w;
-            }
-        } else {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) qn[v] = 0u;
-        }
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                // slots (2j, 2j+1) = channels (8kb + j, 8kb + j + 4) of the lane's window
-                const int c0 = 8 * kb + j, c1 = 8 * kb + j + 4;
-                const uint32_t s0 = (c0 & 1) ? 0x0302u : 0x0100u;
-                const uint32_t s1 = (c1 & 1) ? 0x0706u : 0x0504u;
-                bq[kb].u[j] = __builtin_amdgcn_perm(qn[c1 >> 1], qn[c0 >> 1], (s1 << 16) | s0);
-            }
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) sm.bq[kb][l] = make_uint4(bq[kb].u[0], bq[kb].u[1], bq[kb].u[2], bq[kb].u[3]);
-        lds_order();
-    }
-
-    const float c2 = a.softmax_scale * kLog2e;
-    SoftState st;
-    st.m_run = -INFINITY;
-    st.l_part = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) st.acc_o[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-
-    if (has_store) {
-        // kNBuf buffers in rotation: while step t computes, the loads of the
-        // next kNBuf - 1 steps are in flight.
-        for (int t0 = j0; t0 < j1; t0 += kNBuf * kStep) {
-#pragma unroll
-            for (int u = 0; u < kNBuf; ++u) {
-                issue_step<BITS, G, MB>(buf[(u + kNBuf - 1) % kNBuf], S, O, pref(t0 + (u + kNBuf - 1) * kStep), n);
-                store_step<BITS, G, MB>(buf[u], sm, st, t0 + u * kStep, j1, c2, l, n, q);
-                if (t0 + (u + 1) * kStep >= j1) goto store_done;
-            }
-        }
-    store_done:;
-    }
-    if (r0 < r1) {
-        const uint16_t* kr = a.k_res + bkv * a.res_bh_stride;
-        const uint16_t* vr = a.v_res + bkv * a.res_bh_stride;
-        for (int t0 = r0; t0 < r1; t0 += kStep)
-            residual_step(kr, vr, sm, st, t0, r1, c2, l, n, q, a.res_head, a.res_ring);
-    }
-
-    // ---- partial (m, l, o) of head n: lane (q, n) holds channels 32q + 8r + i
-    const float l_tot = rows_sum(st.l_part);
-    if (n < GQA) {
-        float* dst = ws_o + ((qrow0 + n) * n_split + split) * kHeadDim + 32 * q;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            *reinterpret_cast<float4*>(dst + 8 * r) =
-                make_float4(st.acc_o[0][r], st.acc_o[1][r], st.acc_o[2][r], st.acc_o[3][r]);
-            *reinterpret_cast<float4*>(dst + 8 * r + 4) =
-                make_float4(st.acc_o[4][r], st.acc_o[5][r], st.acc_o[6][r], st.acc_o[7][r]);
-        }
-        if (q == 0) {
-            float* ml = ws_ml + ((qrow0 + n) * n_split + split) * 2;
-            ml[0] = st.m_run;
-            ml[1] = l_tot;
-        }
-    }
-}
 
 // Merge the splits of one (sequence, query head), base-2 log-sum-exp:
 // o = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i with M = max_i m_i.
@@ -755,17 +126,17 @@ AttendPlan plan_attend(int64_t B, int Hq, int Hkv, int64_t n_quant, int64_t n_re
     return p;
 }
 
-template <int BITS, int GQA, int G, int MB>
-static hipError_t launch_t(const AttendArgs& a, const AttendPlan& p, hipStream_t stream) {
+// The partial kernel, then the combine.  The workspace holds the o rows
+// (256-byte aligned), then the (m, l) pairs.
+hipError_t launch_decode_attend(const AttendArgs& a, const AttendPlan& p, hipStream_t stream) {
     float* ws_o = static_cast<float*>(a.workspace);
     const size_t rows = static_cast<size_t>(a.B) * a.Hq * p.n_split;
     const size_t o_bytes = (rows * kHeadDim * sizeof(float) + 255) & ~static_cast<size_t>(255);
     float* ws_ml = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + o_bytes);
-    const dim3 grid(static_cast<uint32_t>(p.n_split), static_cast<uint32_t>(a.B * a.Hkv));
-    hipLaunchKernelGGL((attend_partial_kernel<BITS, GQA, G, MB>), grid, dim3(64), 0, stream, a,
-                       static_cast<int>(p.steps_per_wave), static_cast<int>(p.steps_q), p.n_split,
-                       ws_o, ws_ml);
-    hipError_t e = hipGetLastError();
+    hipError_t e;
+    if (a.bf16) e = launch_attend_partial_bf16(a, p, ws_o, ws_ml, stream);
+    else if (a.meta16) e = launch_partials<2, false>(a, p, ws_o, ws_ml, stream);
+    else e = launch_partials<4, false>(a, p, ws_o, ws_ml, stream);
     if (e != hipSuccess) return e;
     if (p.n_split >= 48)
         hipLaunchKernelGGL(attend_combine_kernel<16>, dim3(static_cast<uint32_t>(a.B * a.Hq)), dim3(64 * 16), 0,
@@ -774,32 +145,6 @@ static hipError_t launch_t(const AttendArgs& a, const AttendPlan& p, hipStream_t
         hipLaunchKernelGGL(attend_combine_kernel<4>, dim3(static_cast<uint32_t>(a.B * a.Hq)), dim3(64 * 4), 0,
                            stream, ws_o, ws_ml, p.n_split, a.out);
     return hipGetLastError();
-}
-
-template <int BITS, int G, int MB>
-static hipError_t launch_gqa(const AttendArgs& a, const AttendPlan& p, hipStream_t stream) {
-    switch (a.Hq / a.Hkv) {
-        case 1: return launch_t<BITS, 1, G, MB>(a, p, stream);
-        case 2: return launch_t<BITS, 2, G, MB>(a, p, stream);
-        case 4: return launch_t<BITS, 4, G, MB>(a, p, stream);
-        default: return launch_t<BITS, 8, G, MB>(a, p, stream);
-    }
-}
-
-template <int BITS, int MB>
-static hipError_t launch_bits(const AttendArgs& a, const AttendPlan& p, hipStream_t stream) {
-    switch (a.group) {
-        case 64: return launch_gqa<BITS, 64, MB>(a, p, stream);
-        case 128: return launch_gqa<BITS, 128, MB>(a, p, stream);
-        default: return launch_gqa<BITS, 32, MB>(a, p, stream);
-    }
-}
-
-// One instantiation per (bits, query heads per kv head, group size, bytes of
-// a scale/zero entry).
-hipError_t launch_decode_attend(const AttendArgs& a, const AttendPlan& p, hipStream_t stream) {
-    if (a.meta16) return a.bits == 4 ? launch_bits<4, 2>(a, p, stream) : launch_bits<2, 2>(a, p, stream);
-    return a.bits == 4 ? launch_bits<4, 4>(a, p, stream) : launch_bits<2, 4>(a, p, stream);
 }
 
 }  // namespace kivi

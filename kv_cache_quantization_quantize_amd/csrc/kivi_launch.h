@@ -77,6 +77,7 @@ struct AttendArgs {
     int bits;
     int group;                     // 32, 64 or 128 (keys and values alike)
     bool meta16;                   // binary16 scale/zero (keys and values alike)
+    bool bf16;                     // q, residual and the reconstruction in bfloat16
 };
 
 // Split of the token axis chosen for an attend shape; the workspace holds
@@ -112,7 +113,7 @@ int decode_attend_entry(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
                         int64_t n_res, int64_t res_head, int64_t res_ring,
                         const int32_t* seq_n_quant, const int32_t* seq_n_res,
                         float softmax_scale, float* out, void* workspace, size_t workspace_bytes,
-                        hipStream_t stream);
+                        hipStream_t stream, bool bf16 = false);
 
 // KIVI_OK, or KIVI_ERR_HIP after recording e for kivi_last_hip_error.
 int hip_status(hipError_t e);

@@ -28,6 +28,7 @@ EXPORTS = (
     "kivi_quantize_keys", "kivi_quantize_values", "kivi_dequantize",
     "kivi_quantize_keys_bf16", "kivi_quantize_values_bf16", "kivi_dequantize_bf16",
     "kivi_decode_attend", "kivi_decode_attend_varlen", "kivi_decode_attend_workspace_bytes",
+    "kivi_decode_attend_bf16", "kivi_decode_attend_varlen_bf16",
     "kivi_status_string", "kivi_last_hip_error", "kivi_calib_copy",
     "kivi_cache_device_bytes", "kivi_cache_init", "kivi_cache_prefill", "kivi_cache_append",
     "kivi_cache_attend", "kivi_cache_attend_workspace_bytes", "kivi_cache_end_step",
@@ -100,6 +101,8 @@ def lib() -> ctypes.CDLL:
                                          ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
         L.kivi_decode_attend_varlen.argtypes = [vp, i64, i32, i32, sp, sp, vp, i64, vp, vp, i64,
                                                 vp, i64, ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
+        L.kivi_decode_attend_bf16.argtypes = L.kivi_decode_attend.argtypes
+        L.kivi_decode_attend_varlen_bf16.argtypes = L.kivi_decode_attend_varlen.argtypes
         L.kivi_decode_attend_workspace_bytes.argtypes = [i64, i32, i32, i64, i64]
         L.kivi_decode_attend_workspace_bytes.restype = ctypes.c_size_t
         L.kivi_status_string.argtypes = [ctypes.c_int]
@@ -119,6 +122,7 @@ def lib() -> ctypes.CDLL:
         for name in ("kivi_quantize_keys", "kivi_quantize_values", "kivi_dequantize",
                      "kivi_quantize_keys_bf16", "kivi_quantize_values_bf16", "kivi_dequantize_bf16",
                      "kivi_decode_attend", "kivi_decode_attend_varlen", "kivi_last_hip_error",
+                     "kivi_decode_attend_bf16", "kivi_decode_attend_varlen_bf16",
                      "kivi_calib_copy", "kivi_cache_init", "kivi_cache_prefill", "kivi_cache_append",
                      "kivi_cache_attend", "kivi_cache_end_step"):
             getattr(L, name).restype = ctypes.c_int
@@ -147,6 +151,21 @@ def _need_f16(t: torch.Tensor, name: str, allow_bf16: bool = False, D: int = HEA
         raise TypeError(f"{name} must be a device tensor")
     if t.dim() != 3 or t.shape[2] != D or t.stride(2) != 1 or t.stride(1) != D:
         raise ValueError(f"{name} must be [BH][S][{D}] with contiguous token rows")
+
+
+def _need_query(q: torch.Tensor) -> None:
+    if q.dtype not in (torch.float16, torch.bfloat16) or not q.is_cuda or q.dim() != 3 \
+            or not q.is_contiguous():
+        raise ValueError("q must be a contiguous float16 or bfloat16 device tensor [B][Hq][128]")
+
+
+def _need_residual(q: torch.Tensor, k_res: torch.Tensor, v_res: torch.Tensor) -> None:
+    _need_f16(k_res, "k_res", allow_bf16=True)
+    _need_f16(v_res, "v_res", allow_bf16=True)
+    if k_res.dtype != q.dtype or v_res.dtype != q.dtype:
+        raise TypeError("k_res and v_res must have the dtype of q")
+    if k_res.stride(0) != v_res.stride(0):
+        raise ValueError("k_res and v_res must share their slab stride")
 
 
 class Store:
@@ -242,9 +261,9 @@ def decode_attend(q: torch.Tensor, k_store: Store, v_store: Store, n_quant: int,
                   softmax_scale: float | None = None, out: torch.Tensor | None = None,
                   workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """kivi_decode_attend: fp32 [B][Hq][128] attention of one query token per
-    sequence over store tokens [0, n_quant) then residual tokens [0, n_res)."""
-    if q.dtype != torch.float16 or not q.is_cuda or q.dim() != 3 or not q.is_contiguous():
-        raise ValueError("q must be a contiguous float16 device tensor [B][Hq][128]")
+    sequence over store tokens [0, n_quant) then residual tokens [0, n_res)
+    (kivi_decode_attend_bf16 when q is bfloat16; the residual then is too)."""
+    _need_query(q)
     B, Hq, D = q.shape
     Hkv = k_store.BH // B if B else 1
     if softmax_scale is None:
@@ -257,17 +276,15 @@ def decode_attend(q: torch.Tensor, k_store: Store, v_store: Store, n_quant: int,
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     if n_res > 0:
-        _need_f16(k_res, "k_res")
-        _need_f16(v_res, "v_res")
-        if k_res.stride(0) != v_res.stride(0):
-            raise ValueError("k_res and v_res must share their slab stride")
+        _need_residual(q, k_res, v_res)
     ks, vs = k_store.c(), v_store.c()
-    rc = lib().kivi_decode_attend(
+    name = "kivi_decode_attend_bf16" if q.dtype == torch.bfloat16 else "kivi_decode_attend"
+    rc = getattr(lib(), name)(
         q.data_ptr(), B, Hq, Hkv, ctypes.byref(ks), ctypes.byref(vs), n_quant,
         k_res.data_ptr() if n_res > 0 else None, v_res.data_ptr() if n_res > 0 else None,
         k_res.stride(0) if n_res > 0 else 0, n_res, float(softmax_scale), out.data_ptr(),
         workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream))
-    _check(rc, "kivi_decode_attend")
+    _check(rc, name)
     return out
 
 
@@ -277,9 +294,9 @@ def decode_attend_varlen(q: torch.Tensor, k_store: Store, v_store: Store, n_quan
                          out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
                          stream=None) -> torch.Tensor:
     """kivi_decode_attend_varlen: like decode_attend, with device int32 [B]
-    per-sequence lengths n_quant[b] <= max_n_quant and n_res[b] <= max_n_res."""
-    if q.dtype != torch.float16 or not q.is_cuda or q.dim() != 3 or not q.is_contiguous():
-        raise ValueError("q must be a contiguous float16 device tensor [B][Hq][128]")
+    per-sequence lengths n_quant[b] <= max_n_quant and n_res[b] <= max_n_res
+    (kivi_decode_attend_varlen_bf16 when q is bfloat16)."""
+    _need_query(q)
     B, Hq, D = q.shape
     for t, name in ((n_quant, "n_quant"), (n_res, "n_res")):
         if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous() or t.numel() != B:
@@ -295,18 +312,16 @@ def decode_attend_varlen(q: torch.Tensor, k_store: Store, v_store: Store, n_quan
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     if max_n_res > 0:
-        _need_f16(k_res, "k_res")
-        _need_f16(v_res, "v_res")
-        if k_res.stride(0) != v_res.stride(0):
-            raise ValueError("k_res and v_res must share their slab stride")
+        _need_residual(q, k_res, v_res)
     ks, vs = k_store.c(), v_store.c()
-    rc = lib().kivi_decode_attend_varlen(
+    name = "kivi_decode_attend_varlen_bf16" if q.dtype == torch.bfloat16 else "kivi_decode_attend_varlen"
+    rc = getattr(lib(), name)(
         q.data_ptr(), B, Hq, Hkv, ctypes.byref(ks), ctypes.byref(vs), n_quant.data_ptr(), max_n_quant,
         k_res.data_ptr() if max_n_res > 0 else None, v_res.data_ptr() if max_n_res > 0 else None,
         k_res.stride(0) if max_n_res > 0 else 0, n_res.data_ptr(), max_n_res, float(softmax_scale),
         out.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
         _stream(stream))
-    _check(rc, "kivi_decode_attend_varlen")
+    _check(rc, name)
     return out
 
 

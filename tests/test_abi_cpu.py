@@ -190,6 +190,20 @@ def test_attend_validation():
     assert call(kk=_store(kivi.KIVI_KEYS, cap=64, G=48), vv=_store(kivi.KIVI_VALUES, cap=64, G=48)) == -3
     # and their scale/zero format
     assert call(kk=_store(kivi.KIVI_KEYS, cap=64, meta_format=kivi.KIVI_META_F16)) == -3
+    # the bfloat16 attends validate alike, and refuse binary16 metadata
+    k16 = _store(kivi.KIVI_KEYS, cap=64, meta_format=kivi.KIVI_META_F16)
+    v16 = _store(kivi.KIVI_VALUES, cap=64, meta_format=kivi.KIVI_META_F16)
+    for fn in (L.kivi_decode_attend_bf16,):
+        assert fn(FAKE, 1, 30, 8, ctypes.byref(k), ctypes.byref(v), 64, FAKE, FAKE, 2048, 16,
+                  0.088, FAKE, FAKE, ws, None) == -2
+        assert fn(FAKE, 1, 32, 8, ctypes.byref(k16), ctypes.byref(v16), 64, FAKE, FAKE, 2048, 16,
+                  0.088, FAKE, FAKE, ws, None) == -3
+        assert fn(FAKE, 1, 32, 8, ctypes.byref(k), ctypes.byref(v), 64, FAKE, FAKE, 2048, 16,
+                  0.088, FAKE, FAKE, ws - 4, None) == -5
+    nq = nr = FAKE
+    assert L.kivi_decode_attend_varlen_bf16(FAKE, 1, 32, 8, ctypes.byref(k16), ctypes.byref(v16),
+                                            nq, 64, FAKE, FAKE, 2048, nr, 16, 0.088, FAKE, FAKE,
+                                            ws, None) == -3
 
 
 # ---------------------------------------------------------------- cache

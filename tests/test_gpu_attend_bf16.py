@@ -1,0 +1,147 @@
+"""GPU parity of the bfloat16 decode attends (kivi_decode_attend_bf16 and
+kivi_decode_attend_varlen_bf16) against the oracle's bfloat16 attend over the
+same stores (written by the bfloat16 flushes) and the same bfloat16 query and
+residual rows.
+
+Tolerance: the fp16 attend's 2e-3 plus 2^-8 max|v|.  The kernel rounds the
+softmax probabilities to bfloat16 for PV (relative error at most 2^-9, so at
+most 2^-9 max|v| on an output that is a convex combination of values), and
+its in-register reconstruction can differ from the stored one by one
+bfloat16 rounding where the two roundings straddle a boundary."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import note, u16
+from kv_cache_quantization_quantize_amd import kivi, synth
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+D = 128
+
+CASES = [
+    # B, Hq, Hkv, n_quant, n_res, bits, G
+    (2, 32, 8, 1000, 37, 4, 32),
+    (1, 32, 8, 4096 + 64, 128, 4, 32),
+    (3, 64, 8, 300, 5, 2, 32),
+    (2, 32, 8, 0, 64, 4, 32),
+    (2, 16, 16, 640, 0, 4, 64),
+    (2, 32, 16, 500, 20, 2, 128),
+    (1, 8, 2, 2048, 100, 4, 32),
+    (4, 8, 8, 96, 3, 2, 64),
+]
+
+
+def _bf16(t):
+    return t.to(torch.bfloat16).contiguous()
+
+
+def _tol(vx, vr, nq, nr):
+    vmax = 0.0
+    if nq:
+        vmax = max(vmax, float(vx.float().abs().max()))
+    if nr:
+        vmax = max(vmax, float(vr[:, :nr].float().abs().max()))
+    return 2e-3 + 2.0 ** -8 * vmax
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B%d-Hq%d-Hkv%d-nq%d-nr%d-b%d-G%d" % c)
+def test_bf16_attend(case):
+    B, Hq, Hkv, nq, nr, bits, G = case
+    BH = B * Hkv
+    cap = max(G, ((nq + G - 1) // G) * G)
+    seed = 14100 + nq + G + bits
+    kx = _bf16(synth.kv_tensor(BH, max(nq, 1), keys=True, seed=seed, device="cuda", dtype=torch.bfloat16)[:, :nq])
+    vx = _bf16(synth.kv_tensor(BH, max(nq, 1), keys=False, seed=seed, device="cuda", dtype=torch.bfloat16)[:, :nq])
+    kr = _bf16(synth.residual(BH, max(nr, 1), keys=True, seed=seed, device="cuda"))
+    vr = _bf16(synth.residual(BH, max(nr, 1), keys=False, seed=seed, device="cuda"))
+    q = _bf16(synth.query(B, Hq, seed=seed, device="cuda"))
+    ks = kivi.Store(kivi.KIVI_KEYS, BH, cap, bits, group=G)
+    vs = kivi.Store(kivi.KIVI_VALUES, BH, cap, bits, group=G)
+    note(f"bf16 attend B={B} Hq={Hq} Hkv={Hkv} n_quant={nq} n_res={nr} bits={bits} G={G}")
+    if nq:
+        kivi.quantize_keys(kx, ks, 0)
+        kivi.quantize_values(vx, vs, 0)
+    out = kivi.decode_attend(q, ks, vs, nq, kr, vr, nr)
+    rng = np.random.default_rng(seed)
+    nq_h = rng.integers(0, nq + 1, size=B).astype(np.int32)
+    nr_h = rng.integers(0, nr + 1, size=B).astype(np.int32)
+    empty = (nq_h + nr_h) == 0
+    nq_h[empty], nr_h[empty] = nq, nr
+    out_v = kivi.decode_attend_varlen(q, ks, vs, torch.from_numpy(nq_h).cuda(), nq, kr, vr,
+                                      torch.from_numpy(nr_h).cuda(), nr)
+    torch.cuda.synchronize()
+    hk = oracle.Store(oracle.KEYS, BH, cap, D, bits, G)
+    hv = oracle.Store(oracle.VALUES, BH, cap, D, bits, G)
+    if nq:
+        oracle.quantize_keys(u16(kx), hk, 0, want_recon=False, fmt="bf16")
+        oracle.quantize_values(u16(vx), hv, 0, want_recon=False, fmt="bf16")
+    tol = _tol(vx, vr, nq, nr)
+    ref = oracle.decode_attend(u16(q), B, Hq, Hkv, hk, hv, nq, u16(kr), u16(vr), nr, fmt="bf16")
+    err = float(np.max(np.abs(out.cpu().numpy().astype(np.float64) - ref)))
+    print(f"{case}: max-abs error {err:.2e} (tolerance {tol:.2e})")
+    assert err <= tol, f"max-abs error {err:.3e} > {tol:.3e}"
+    ref_v = oracle.decode_attend_varlen(u16(q), B, Hq, Hkv, hk, hv, nq_h, nq, u16(kr), u16(vr),
+                                        nr_h, nr, fmt="bf16")
+    err = float(np.max(np.abs(out_v.cpu().numpy().astype(np.float64) - ref_v)))
+    assert err <= tol, f"varlen max-abs error {err:.3e} > {tol:.3e}"
+
+
+def test_bf16_values_outside_fp16_range():
+    """A bfloat16 cache whose values exceed fp16's range (1e6): the attend
+    stays in bfloat16 throughout, so the result is finite and matches."""
+    B, Hq, Hkv, nq, nr = 1, 8, 2, 256, 16
+    BH = B * Hkv
+    kx = _bf16(synth.kv_tensor(BH, nq, keys=True, seed=5, device="cuda", dtype=torch.bfloat16))
+    vx = _bf16(synth.kv_tensor(BH, nq, keys=False, seed=5, device="cuda", dtype=torch.bfloat16).float() * 1e6)
+    kr = _bf16(synth.residual(BH, nr, keys=True, seed=5, device="cuda"))
+    vr = _bf16(synth.residual(BH, nr, keys=False, seed=5, device="cuda").float() * 1e6)
+    q = _bf16(synth.query(B, Hq, seed=5, device="cuda"))
+    ks = kivi.Store(kivi.KIVI_KEYS, BH, nq, 4)
+    vs = kivi.Store(kivi.KIVI_VALUES, BH, nq, 4)
+    note("bf16 attend with values of magnitude 1e6")
+    kivi.quantize_keys(kx, ks, 0)
+    kivi.quantize_values(vx, vs, 0)
+    out = kivi.decode_attend(q, ks, vs, nq, kr, vr, nr)
+    torch.cuda.synchronize()
+    hk = oracle.Store(oracle.KEYS, BH, nq, D, 4, 32)
+    hv = oracle.Store(oracle.VALUES, BH, nq, D, 4, 32)
+    oracle.quantize_keys(u16(kx), hk, 0, want_recon=False, fmt="bf16")
+    oracle.quantize_values(u16(vx), hv, 0, want_recon=False, fmt="bf16")
+    ref = oracle.decode_attend(u16(q), B, Hq, Hkv, hk, hv, nq, u16(kr), u16(vr), nr, fmt="bf16")
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got))
+    tol = _tol(vx, vr, nq, nr)
+    assert float(np.max(np.abs(got - ref))) <= tol
+
+
+def test_full_size_bf16_attend_sampled():
+    """32 sequences x 32 query heads over 8 kv heads, 16384 store tokens + 128
+    residual, 4-bit: four sampled sequences against the oracle."""
+    B, Hq, Hkv, nq, nr = 32, 32, 8, 16384, 128
+    BH = B * Hkv
+    kx = synth.kv_tensor(BH, nq, keys=True, seed=91, device="cuda", dtype=torch.bfloat16)
+    vx = synth.kv_tensor(BH, nq, keys=False, seed=92, device="cuda", dtype=torch.bfloat16)
+    kr = _bf16(synth.residual(BH, nr, keys=True, seed=91, device="cuda"))
+    vr = _bf16(synth.residual(BH, nr, keys=False, seed=91, device="cuda"))
+    q = _bf16(synth.query(B, Hq, seed=91, device="cuda"))
+    ks = kivi.Store(kivi.KIVI_KEYS, BH, nq, 4)
+    vs = kivi.Store(kivi.KIVI_VALUES, BH, nq, 4)
+    note("bf16 attend full size B=32 n_quant=16384")
+    kivi.quantize_keys(kx, ks, 0)
+    kivi.quantize_values(vx, vs, 0)
+    out = kivi.decode_attend(q, ks, vs, nq, kr, vr, nr)
+    torch.cuda.synchronize()
+    for b in (0, 13, 31):
+        sl = slice(b * Hkv, (b + 1) * Hkv)
+        hk = oracle.Store(oracle.KEYS, Hkv, nq, D, 4, 32)
+        hv = oracle.Store(oracle.VALUES, Hkv, nq, D, 4, 32)
+        oracle.quantize_keys(u16(kx[sl]), hk, 0, want_recon=False, fmt="bf16")
+        oracle.quantize_values(u16(vx[sl]), hv, 0, want_recon=False, fmt="bf16")
+        ref = oracle.decode_attend(u16(q[b:b + 1]), 1, Hq, Hkv, hk, hv, nq, u16(kr[sl]), u16(vr[sl]), nr,
+                                   fmt="bf16")
+        tol = _tol(vx[sl], vr[sl], nq, nr)
+        err = float(np.max(np.abs(out[b:b + 1].cpu().numpy().astype(np.float64) - ref)))
+        assert err <= tol, f"sequence {b}: max-abs error {err:.3e} > {tol:.3e}"
