@@ -36,15 +36,16 @@ int64_t words_per_token(const kivi_store* st) { return int64_t{st->head_dim} * s
 
 int64_t meta_rows(const kivi_store* st) {
     const int64_t G = st->group_size, D = st->head_dim;
-    return st->kind == KIVI_KEYS ? (st->cap + G - 1) / G * D : st->cap * (D / G);
+    return st->kind == KIVI_KEYS ? (st->cap + G - 1) / G * D : st->cap * ((D + G - 1) / G);
 }
 
 // Stores take head_dim 128 with groups of 32, 64 or 128 tokens (keys) or
-// channels (values), and head_dim 64 or 256 with groups of 32.  The attend
-// and the decode-loop cache take head_dim 128.
+// channels (values), and any other multiple of 16 from 16 to 256 with groups
+// of 32 (a token's last value group is ragged when 32 does not divide
+// head_dim).  The attend and the decode-loop cache take head_dim 128.
 bool geometry_ok(int32_t D, int32_t G) {
     if (D == 128) return G == 32 || G == 64 || G == 128;
-    return (D == 64 || D == 256) && G == 32;
+    return D >= 16 && D <= 256 && D % 16 == 0 && G == 32;
 }
 
 bool meta16(const kivi_store* st) { return st->meta_format == KIVI_META_F16; }

@@ -152,6 +152,7 @@ static hipError_t launch_fmt(const DequantArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t stream) {
+    if (a.head_dim != 64 && a.head_dim != 128 && a.head_dim != 256) return launch_dequant_ragged(a, stream);
     return a.bf16 ? launch_fmt<true>(a, stream) : launch_fmt<false>(a, stream);
 }
 

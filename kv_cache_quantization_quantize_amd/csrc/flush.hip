@@ -411,11 +411,15 @@ static hipError_t launch_flush_fmt(const FlushArgs& a, hipStream_t stream) {
     }
 }
 
+static bool tiled_head_dim(int D) { return D == 64 || D == 128 || D == 256; }
+
 hipError_t launch_key_flush(const FlushArgs& a, hipStream_t stream) {
+    if (!tiled_head_dim(a.head_dim)) return launch_flush_ragged(true, a, stream);
     return a.bf16 ? launch_flush_fmt<true, true>(a, stream) : launch_flush_fmt<true, false>(a, stream);
 }
 
 hipError_t launch_value_flush(const FlushArgs& a, hipStream_t stream) {
+    if (!tiled_head_dim(a.head_dim)) return launch_flush_ragged(false, a, stream);
     return a.bf16 ? launch_flush_fmt<false, true>(a, stream) : launch_flush_fmt<false, false>(a, stream);
 }
 

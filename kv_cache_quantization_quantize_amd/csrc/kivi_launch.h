@@ -94,6 +94,9 @@ hipError_t launch_key_flush(const FlushArgs& a, hipStream_t stream);
 hipError_t launch_value_flush(const FlushArgs& a, hipStream_t stream);
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t stream);
 hipError_t launch_decode_attend(const AttendArgs& a, const AttendPlan& p, hipStream_t stream);
+// head_dims other than 64, 128 and 256 (multiples of 16 up to 256, groups of 32)
+hipError_t launch_flush_ragged(bool keys, const FlushArgs& a, hipStream_t stream);
+hipError_t launch_dequant_ragged(const DequantArgs& a, hipStream_t stream);
 // Copies n_rows token rows (head_dim fp16 each) of every slab from src to
 // dst for keys and values at once (one launch).
 struct RowCopy {

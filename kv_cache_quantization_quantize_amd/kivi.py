@@ -186,7 +186,7 @@ class Store:
         self.meta = meta
         self.words = head_dim * bits // 32
         shape = (BH, (cap + group - 1) // group, head_dim) if kind == KIVI_KEYS else \
-            (BH, cap, head_dim // group)
+            (BH, cap, (head_dim + group - 1) // group)
         mdt = torch.float32 if meta == "f32" else torch.float16
         self.codes = codes if codes is not None else torch.zeros((BH, cap, self.words),
                                                                  dtype=torch.int32, device=device)

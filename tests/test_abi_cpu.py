@@ -63,7 +63,8 @@ def _keys(st, x=FAKE, BH=2, S=32, x_stride=32 * 128, off=0, recon=None, rstride=
 
 @pytest.mark.parametrize("case,want", [
     ("null_store", -1), ("bits3", -3), ("bits8", -3), ("group48", -3), ("group256", -3),
-    ("dim96", -3), ("dim64_group64", -3), ("dim64", 0), ("group64_offset32", -2), ("group64", 0),
+    ("dim96", 0), ("dim72", -3), ("dim272", -3), ("dim96_group64", -3), ("dim64_group64", -3),
+    ("dim64", 0), ("group64_offset32", -2), ("group64", 0),
     ("kind_values", -2), ("offset_not_group", -2), ("window_past_cap", -2),
     ("misaligned_x", -4), ("odd_stride", -4), ("null_x", -1), ("neg_S", -2),
     ("slab_overlap", -2), ("misaligned_codes", -4),
@@ -89,6 +90,13 @@ def test_key_flush_validation(case, want):
         kw = dict(S=0)                             # valid: a zero-sized call launches nothing
     elif case == "dim96":
         st = _store(D=96)
+        kw = dict(S=0)                             # valid: a ragged head_dim with groups of 32
+    elif case == "dim72":
+        st = _store(D=72)
+    elif case == "dim272":
+        st = _store(D=272)
+    elif case == "dim96_group64":
+        st = _store(D=96, G=64)
     elif case == "dim64_group64":
         st = _store(D=64, G=64)
     elif case == "dim64":

@@ -158,3 +158,49 @@ def test_other_head_dims(shape, Dh, kind, bits, fmt):
     out = kivi.dequantize(st, dst, S, dtype=dtype)
     torch.cuda.synchronize()
     assert_u16_equal(u16(out), hrec, what + " dequantize")
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("kind", ["keys", "values"])
+@pytest.mark.parametrize("Dh", [16, 48, 80, 96, 112, 160, 240])
+@pytest.mark.parametrize("shape", [(3, 101, 160, 32, 7), (2, 64, 64, 0, 0), (1, 1, 64, 32, 1)],
+                         ids=lambda c: "BH%d-S%d-dst%d" % (c[0], c[1], c[3]))
+def test_ragged_head_dims(shape, Dh, kind, bits, fmt):
+    """head_dims other than 64, 128 and 256 (the generic kernels; a token's
+    last value group has 16 channels when 32 does not divide head_dim):
+    flush with fused reconstruction, and dequantize, bit-exact against the
+    oracle, sentinel-filled outputs checking the write window."""
+    BH, S, cap, dst_k, dst_v = shape
+    dst = dst_k if kind == "keys" else dst_v
+    dtype = torch.bfloat16 if fmt == "bf16" else torch.float16
+    x = synth.kv_tensor(BH, S, Dh, keys=(kind == "keys"), seed=8700 + Dh + S, device="cuda", dtype=dtype)
+    k = KINDS[kind]
+    st = kivi.Store(k, BH, cap, bits, head_dim=Dh)
+    st.codes.fill_(CODE_SENTINEL)
+    st.scale.fill_(META_SENTINEL)
+    st.zero.fill_(META_SENTINEL)
+    okind = oracle.KEYS if k == kivi.KIVI_KEYS else oracle.VALUES
+    hs = oracle.Store(okind, BH, cap, Dh, bits, 32, fill_codes=CODE_SENTINEL, fill_meta=META_SENTINEL)
+    recon_full = torch.full((BH, S + 8, Dh), SENTINEL16, dtype=torch.int16, device="cuda").view(dtype)
+    note(f"ragged head_dim {Dh} {fmt} flush {kind} bits={bits} BH={BH} S={S} cap={cap} dst={dst}")
+    (kivi.quantize_keys if kind == "keys" else kivi.quantize_values)(x, st, dst, recon_full[:, :S])
+    torch.cuda.synchronize()
+    ofn = oracle.quantize_keys if kind == "keys" else oracle.quantize_values
+    hrec = ofn(u16(x), hs, dst, want_recon=True, fmt=fmt)
+    what = f"D={Dh} {fmt} {kind} bits={bits} S={S} dst={dst}"
+    assert_store_equal(st, hs, what=what)
+    r = u16(recon_full)
+    assert_u16_equal(r[:, :S], hrec, what + " recon")
+    assert np.all(r[:, S:] == SENTINEL16), "recon written past the window"
+    out = kivi.dequantize(st, dst, S, dtype=dtype)
+    torch.cuda.synchronize()
+    assert_u16_equal(u16(out), hrec, what + " dequantize")
+    # the same flush without the fused reconstruction writes the same store
+    st2 = kivi.Store(k, BH, cap, bits, head_dim=Dh)
+    st2.codes.fill_(CODE_SENTINEL)
+    st2.scale.fill_(META_SENTINEL)
+    st2.zero.fill_(META_SENTINEL)
+    (kivi.quantize_keys if kind == "keys" else kivi.quantize_values)(x, st2, dst)
+    torch.cuda.synchronize()
+    assert_store_equal(st2, hs, what=what + " (no recon)")

@@ -114,3 +114,41 @@ def test_other_head_dims_reduce_to_the_group_function(orc, Dh, bits):
                 assert np.array_equal(rv[bh, s, G * j:G * j + G], rec)
     assert np.array_equal(orc.dequantize(ks, 0, S), rk)
     assert np.array_equal(orc.dequantize(vs, 0, S), rv)
+
+
+@pytest.mark.parametrize("D", [48, 80, 96, 112])
+@pytest.mark.parametrize("bits", [2, 4])
+def test_ragged_head_dims_reduce_to_the_group_function(orc, D, bits):
+    """head_dims that 32 does not divide (or that are not 64, 128 or 256):
+    every value group, the last one of 16 channels included, and every key
+    group is the one-group quantizer on exactly its elements ([Metal post]
+    "Kernel B": a token's group j is channels [32j, min(32j + 32, D)))."""
+    rng = np.random.default_rng(D + bits)
+    BH, S, G = 2, 45, 32
+    x = (rng.standard_normal((BH, S, D)) * 2).astype(np.float16)
+    xb = x.view(np.uint16)
+    L = (1 << bits) - 1
+    vs = orc.Store(orc.VALUES, BH, 64, D, bits, G)
+    vrec = orc.quantize_values(xb, vs)
+    assert vs.scale.shape == (BH, 64, (D + G - 1) // G)
+    for bh in range(BH):
+        for t in (0, 17, 44):
+            for j in range((D + G - 1) // G):
+                d0, d1 = G * j, min(G * j + G, D)
+                sc, ze, q, rec = orc.quantize_group(xb[bh, t, d0:d1], bits)
+                assert vs.scale[bh, t, j] == sc and vs.zero[bh, t, j] == ze
+                got = [(int(vs.codes[bh, t, d * bits // 32]) >> ((d % (32 // bits)) * bits)) & L
+                       for d in range(d0, d1)]
+                assert got == list(q)
+                assert np.array_equal(vrec[bh, t, d0:d1], rec)
+    ks = orc.Store(orc.KEYS, BH, 64, D, bits, G)
+    krec = orc.quantize_keys(xb, ks)
+    for bh in range(BH):
+        for g in range(2):
+            t1 = min(G * g + G, S)
+            for d in (0, D // 2, D - 1):
+                sc, ze, q, rec = orc.quantize_group(xb[bh, G * g:t1, d], bits)
+                assert ks.scale[bh, g, d] == sc and ks.zero[bh, g, d] == ze
+                assert np.array_equal(krec[bh, G * g:t1, d], rec)
+    assert np.array_equal(orc.dequantize(vs, 0, S), vrec)
+    assert np.array_equal(orc.dequantize(ks, 0, S), krec)
