@@ -24,10 +24,12 @@
  *    concurrently if their outputs do not overlap.
  *  - Faults inside a kernel surface at the caller's next synchronization.
  *  - Supported parameters: bits in {2, 4}; head_dim 128 with group_size
- *    32, 64 or 128, or head_dim 64 or 256 with group_size 32.  The attend
- *    takes head_dim 128, and its key and value stores share the group size.
- *    Anything else returns KIVI_ERR_UNSUPPORTED (there is no fallback
- *    path).
+ *    32, 64 or 128, or any other multiple of 16 from 16 to 256 with
+ *    group_size 32 (when 32 does not divide head_dim, a token's last value
+ *    group holds the remaining 16 channels: [Metal post] "Kernel B" cuts a
+ *    row's last group at the row's end).  The attend takes head_dim 128,
+ *    and its key and value stores share the group size.  Anything else
+ *    returns KIVI_ERR_UNSUPPORTED.
  *
  * Packed store layout (the pages fix none; [Metal post] "So why does the
  * kernel ship?" asks for packed storage of the codes):
@@ -36,7 +38,7 @@
  *          offset bits * (d % (32/bits)), least significant first.
  *   keys   scale, zero [BH][cap/G][head_dim]   one pair per
  *          (token group, channel): per-channel quantization.
- *   values scale, zero [BH][cap][head_dim/G]   one pair per
+ *   values scale, zero [BH][cap][ceil(head_dim/G)]   one pair per
  *          (token, channel group): per-token quantization.
  *   zero is the group minimum (a float offset, not an integer zero point).
  *   scale and zero are binary32 (meta_format KIVI_META_F32, the default)
@@ -82,7 +84,7 @@ enum { KIVI_META_F32 = 0, KIVI_META_F16 = 1 };
  * memory and is only read during the call; the arrays are device memory. */
 typedef struct kivi_store {
     uint32_t* codes;           /* [BH][cap][head_dim*bits/32]                 */
-    void*     scale;           /* keys [BH][cap/G][D]; values [BH][cap][D/G];
+    void*     scale;           /* keys [BH][cap/G][D]; values [BH][cap][ceil(D/G)];
                                   float, or binary16 bits (meta_format)       */
     void*     zero;            /* same shape and format as scale              */
     int64_t   codes_bh_stride; /* uint32 words between bh slabs (>= cap*row) */
@@ -90,7 +92,7 @@ typedef struct kivi_store {
     int64_t   cap;             /* token capacity of each slab                 */
     int32_t   bits;            /* 2 or 4                                      */
     int32_t   group_size;      /* 32, 64 or 128                               */
-    int32_t   head_dim;        /* 64, 128 or 256                              */
+    int32_t   head_dim;        /* a multiple of 16 from 16 to 256             */
     int32_t   kind;            /* KIVI_KEYS or KIVI_VALUES                    */
     int32_t   meta_format;     /* KIVI_META_F32 or KIVI_META_F16              */
 } kivi_store;
