@@ -16,9 +16,10 @@
 // chunks of 8 channels (16 B); lane = r * nC + c takes chunk c of rows
 // r, r + nR, ... with nR = 64 / nC row phases (lanes past nR * nC only take
 // part in the exchanges).  Partial min/max meet in the wave's own LDS
-// region.  Every step is the IEEE operation the oracle performs (scale by
-// division, code by division and rint, clip), so no shortcut needs a proof
-// for these shapes; they are not the measured workloads.
+// region.  The arithmetic is that of the tiled kernels (kivi_device.h): the
+// scale shortcut, the reciprocal code with its near-tie fallback to the IEEE
+// quotient, and the bfloat16 guards; their proofs are per group and per
+// element, so they hold at any head_dim.
 #include "kivi_device.h"
 #include "kivi_launch.h"
 
@@ -28,6 +29,10 @@ namespace {
 
 constexpr int kG = 32;
 constexpr int kMaxD = 256;
+// rows per lane: 32 / (64 / (head_dim / 8)) rounded up, at most 16 (head_dim
+// 256 has two row phases); loops run to this bound under a wave-uniform
+// guard, so a lane issues all its loads before it waits on the first
+constexpr int kMaxIters = 16;
 
 // The wave's LDS: per-phase min/max of every channel (keys) or per-row
 // min/max of every chunk (values), then the tile's scale and zero.
@@ -82,17 +87,23 @@ __global__ __launch_bounds__(kBlock) void key_flush_ragged_kernel(
     const uint16_t* xt = x + bh * x_bh_stride + s0 * D;
     const int iters = (kG + nR - 1) / nR;
 
-    // per-lane min/max over its rows (rows past the end re-read the last one)
+    // per-lane min/max over its rows; a row past the group's real rows (or
+    // past 32) re-reads the last real row, which cannot move min or max
+    uint4 raw[kMaxIters];
+#pragma unroll
+    for (int i = 0; i < kMaxIters; ++i) {
+        const int row = r + nR * i;
+        if (i < iters) raw[i] = load_stream(xt + (row < n_rows ? row : n_rows - 1) * D + c * 8);
+    }
     float mn[8], mx[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) { mn[j] = INFINITY; mx[j] = -INFINITY; }
-    for (int i = 0; i < iters; ++i) {
-        const int row = r + nR * i;
-        if (!on || row >= kG) continue;
-        const uint4 raw = load_stream(xt + (row < n_rows ? row : n_rows - 1) * D + c * 8);
+    for (int j = 0; j < 8; ++j) { mn[j] = widen(raw[0], j, BF16); mx[j] = mn[j]; }
+#pragma unroll
+    for (int i = 1; i < kMaxIters; ++i) {
+        if (i >= iters) continue;                   // wave-uniform
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const float v = widen(raw, j, BF16);
+            const float v = widen(raw[i], j, BF16);
             mn[j] = fminimum(mn[j], v);
             mx[j] = fmaximum(mx[j], v);
         }
@@ -103,7 +114,7 @@ __global__ __launch_bounds__(kBlock) void key_flush_ragged_kernel(
         for (int j = 0; j < 8; ++j) { sm.mn[r * D + c * 8 + j] = mn[j]; sm.mx[r * D + c * 8 + j] = mx[j]; }
     }
     lds_fence();
-    // phase 0 finishes its chunk: zero = min, scale = (max - min) / L
+    // phase 0 finishes its chunk: zero = min, scale = RN((max - min) / L)
     if (on && r == 0) {
         float sc[8], ze[8];
 #pragma unroll
@@ -114,7 +125,7 @@ __global__ __launch_bounds__(kBlock) void key_flush_ragged_kernel(
                 b = fmaximum(b, sm.mx[p * D + c * 8 + j]);
             }
             ze[j] = canon_zero(a);
-            sc[j] = (b - a) / kL;
+            sc[j] = BF16 ? scale_wide<BITS>(b - a) : scale_of<BITS>(b - a);
             sm.sc[c * 8 + j] = sc[j];
             sm.ze[c * 8 + j] = ze[j];
         }
@@ -125,19 +136,34 @@ __global__ __launch_bounds__(kBlock) void key_flush_ragged_kernel(
         store_stream4(zero + moff + 4, ze[4], ze[5], ze[6], ze[7]);
     }
     lds_fence();
-    float sc[8], ze[8];
+    float sc[8], ze[8], rc[8];
+    bool slow = false;                                 // a bfloat16 scale off the fast path
 #pragma unroll
-    for (int j = 0; j < 8; ++j) { sc[j] = sm.sc[c * 8 + j]; ze[j] = sm.ze[c * 8 + j]; }
+    for (int j = 0; j < 8; ++j) {
+        sc[j] = sm.sc[c * 8 + j];
+        ze[j] = sm.ze[c * 8 + j];
+        rc[j] = recip_clamped(sc[j]);
+        if constexpr (BF16) slow |= !fast_scale(sc[j]);
+    }
 
     uint32_t* ct = codes + bh * codes_bh_stride + (dst_token + s0) * kWords;
     uint16_t* rt = RECON ? recon + bh * recon_bh_stride + s0 * D : nullptr;
-    for (int i = 0; i < iters; ++i) {                  // the same trip count on every lane
+#pragma unroll
+    for (int i = 0; i < kMaxIters; ++i) {               // the same trip count on every lane
+        if (i >= iters) continue;                   // wave-uniform
         const int row = r + nR * i;
         const bool live = on && row < n_rows;
-        const uint4 raw = load_stream(xt + (live ? row : 0) * D + c * 8);
-        float qf[8];
+        float t[8], qf[8];
+        float dev = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) qf[j] = quant_exact(sub_elem<BF16>(raw, j, one, ze[j]), sc[j], kL);
+        for (int j = 0; j < 8; ++j) {
+            t[j] = sub_elem<BF16>(raw[i], j, one, ze[j]);
+            qf[j] = quant_fast(t[j], rc[j], dev);
+        }
+        if (dev > kNearTie || slow) {                   // rare: within 2^-16 of a tie
+#pragma unroll
+            for (int j = 0; j < 8; ++j) qf[j] = quant_exact(t[j], sc[j], kL);
+        }
         uint32_t packed = static_cast<uint32_t>(qf[0]);
 #pragma unroll
         for (int j = 1; j < 8; ++j) packed |= static_cast<uint32_t>(qf[j]) << (BITS * j);
@@ -187,16 +213,23 @@ __global__ __launch_bounds__(kBlock) void value_flush_ragged_kernel(
     const uint16_t* xt = x + bh * x_bh_stride + s0 * D;
     const int iters = (kG + nR - 1) / nR;
 
-    // chunk min/max of every row into LDS
-    for (int i = 0; i < iters; ++i) {
+    // every row's chunk min/max into LDS (rows past the tile re-read row 0
+    // and are never used)
+    uint4 raw[kMaxIters];
+#pragma unroll
+    for (int i = 0; i < kMaxIters; ++i) {
         const int row = r + nR * i;
-        const bool live = on && row < n_rows;
-        if (live) {
-            const uint4 raw = load_stream(xt + row * D + c * 8);
-            float a = widen(raw, 0, BF16), b = a;
+        if (i < iters) raw[i] = load_stream(xt + (on && row < n_rows ? row : 0) * D + c * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < kMaxIters; ++i) {
+        if (i >= iters) continue;                   // wave-uniform
+        const int row = r + nR * i;
+        if (on && row < n_rows) {
+            float a = widen(raw[i], 0, BF16), b = a;
 #pragma unroll
             for (int k = 1; k < 8; ++k) {
-                const float v = widen(raw, k, BF16);
+                const float v = widen(raw[i], k, BF16);
                 a = fminimum(a, v);
                 b = fmaximum(b, v);
             }
@@ -207,7 +240,9 @@ __global__ __launch_bounds__(kBlock) void value_flush_ragged_kernel(
     lds_fence();
     uint32_t* ct = codes + bh * codes_bh_stride + (dst_token + s0) * kWords;
     uint16_t* rt = RECON ? recon + bh * recon_bh_stride + s0 * D : nullptr;
-    for (int i = 0; i < iters; ++i) {                  // the same trip count on every lane
+#pragma unroll
+    for (int i = 0; i < kMaxIters; ++i) {               // the same trip count on every lane
+        if (i >= iters) continue;                   // wave-uniform
         const int row = r + nR * i;
         const bool live = on && row < n_rows;
         float lo = 0.0f, hi = 0.0f;
@@ -220,11 +255,19 @@ __global__ __launch_bounds__(kBlock) void value_flush_ragged_kernel(
             }
         }
         const float ze = canon_zero(lo);
-        const float sc = (hi - lo) / kL;
-        const uint4 raw = load_stream(xt + (live ? row : 0) * D + c * 8);   // read again: no register array
-        float qf[8];
+        const float sc = BF16 ? scale_wide<BITS>(hi - lo) : scale_of<BITS>(hi - lo);
+        const float rc = recip_clamped(sc);
+        float t[8], qf[8];
+        float dev = 0.0f;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) qf[k] = quant_exact(sub_elem<BF16>(raw, k, one, ze), sc, kL);
+        for (int k = 0; k < 8; ++k) {
+            t[k] = sub_elem<BF16>(raw[i], k, one, ze);
+            qf[k] = quant_fast(t[k], rc, dev);
+        }
+        if (dev > kNearTie || (BF16 && !fast_scale(sc))) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) qf[k] = quant_exact(t[k], sc, kL);
+        }
         uint32_t packed = static_cast<uint32_t>(qf[0]);
 #pragma unroll
         for (int k = 1; k < 8; ++k) packed |= static_cast<uint32_t>(qf[k]) << (BITS * k);
