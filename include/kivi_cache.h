@@ -35,7 +35,8 @@
  * sections, slab s = (layer * batch + b) * kv_heads + h):
  *   key store, value store   as in kivi.h with cap = store_capacity tokens
  *                            and the configuration's scale/zero format
- *   key ring, value ring     fp16 [slabs][R + F][head_dim]
+ *   key ring, value ring     16-bit [slabs][R + F][head_dim] (fp16, or
+ *                            bfloat16 for a bfloat16 cache)
  *
  * The library never allocates: the caller allocates the device buffer and
  * the kivi_cache struct.  Every call validates on the host before it enqueues
@@ -68,6 +69,9 @@ typedef struct kivi_cache_config {
     int64_t store_capacity;   /* quantized tokens per sequence, a multiple of F */
     int32_t meta_format;      /* scale/zero of the stores: KIVI_META_F32 (0) or
                                  KIVI_META_F16 (1), as in kivi.h                */
+    int32_t bf16;             /* 0: fp16 cache; 1: bfloat16 cache (prompt, new
+                                 rows, rings and queries in bfloat16, the _bf16
+                                 flushes and attend; binary32 scale/zero)     */
 } kivi_cache_config;
 
 /* Host-side state of a cache.  Filled by kivi_cache_init; the fields are

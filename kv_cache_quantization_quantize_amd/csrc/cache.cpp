@@ -32,6 +32,8 @@ bool valid(const kivi_cache_config* c) {
     if (c->residual_length < 0 || c->residual_length % c->flush_tokens != 0) return false;
     if (c->store_capacity < 0 || c->store_capacity % c->flush_tokens != 0) return false;
     if (c->meta_format != KIVI_META_F32 && c->meta_format != KIVI_META_F16) return false;
+    if (c->bf16 != 0 && c->bf16 != 1) return false;
+    if (c->bf16 && c->meta_format != KIVI_META_F32) return false;    // as for the _bf16 flushes
     if (c->store_capacity >= kMaxTokens) return false;
     if (int64_t{c->residual_length} + c->flush_tokens >= kMaxTokens) return false;
     const int64_t slabs = int64_t{c->layers} * c->batch * c->kv_heads;
@@ -75,6 +77,18 @@ kivi_store layer_store(const kivi_store& s, int64_t slab0) {
     r.scale = static_cast<char*>(s.scale) + meta_bytes;
     r.zero = static_cast<char*>(s.zero) + meta_bytes;
     return r;
+}
+
+// The flushes of the cache's format.
+int flush_keys(const kivi_cache* c, const uint16_t* x, int64_t BH, int64_t S, int64_t stride,
+               int64_t dst, hipStream_t stream) {
+    return (c->cfg.bf16 ? kivi_quantize_keys_bf16 : kivi_quantize_keys)(x, BH, S, stride, &c->k_store,
+                                                                       dst, nullptr, 0, stream);
+}
+int flush_values(const kivi_cache* c, const uint16_t* x, int64_t BH, int64_t S, int64_t stride,
+                 int64_t dst, hipStream_t stream) {
+    return (c->cfg.bf16 ? kivi_quantize_values_bf16 : kivi_quantize_values)(x, BH, S, stride, &c->v_store,
+                                                                           dst, nullptr, 0, stream);
 }
 
 // Quantized tokens of a sequence of S tokens: the whole flush units older
@@ -136,9 +150,8 @@ int kivi_cache_prefill(kivi_cache* cache, const uint16_t* k, const uint16_t* v,
 
     int rc = KIVI_OK;
     if (Q > 0) {
-        rc = kivi_quantize_keys(k, slabs, Q, x_bh_stride, &cache->k_store, 0, nullptr, 0, stream);
-        if (rc == KIVI_OK)
-            rc = kivi_quantize_values(v, slabs, Q, x_bh_stride, &cache->v_store, 0, nullptr, 0, stream);
+        rc = flush_keys(cache, k, slabs, Q, x_bh_stride, 0, stream);
+        if (rc == KIVI_OK) rc = flush_values(cache, v, slabs, Q, x_bh_stride, 0, stream);
         if (rc != KIVI_OK) return rc;
     }
     if (nres > 0) {
@@ -188,7 +201,7 @@ int kivi_cache_attend(const kivi_cache* cache, int32_t layer, const uint16_t* q,
                                      cache->n_quant, cache->k_ring + slab0 * rs,
                                      cache->v_ring + slab0 * rs, rs, cache->n_res + 1, cache->head,
                                      cache->ring, nullptr, nullptr, softmax_scale, out, workspace,
-                                     workspace_bytes, stream);
+                                     workspace_bytes, stream, cache->cfg.bf16 != 0);
 }
 
 size_t kivi_cache_attend_workspace_bytes(const kivi_cache* cache, int32_t Hq) {
@@ -220,11 +233,9 @@ int kivi_cache_end_step(kivi_cache* cache, hipStream_t stream) {
         // head .. head + F - 1 (head and the ring length are multiples of F)
         const int64_t slabs = layout(cache->cfg).slabs;
         const int64_t rs = cache->ring * kD;
-        int rc = kivi_quantize_keys(cache->k_ring + cache->head * kD, slabs, F, rs, &cache->k_store,
-                                    cache->n_quant, nullptr, 0, stream);
+        int rc = flush_keys(cache, cache->k_ring + cache->head * kD, slabs, F, rs, cache->n_quant, stream);
         if (rc == KIVI_OK)
-            rc = kivi_quantize_values(cache->v_ring + cache->head * kD, slabs, F, rs, &cache->v_store,
-                                      cache->n_quant, nullptr, 0, stream);
+            rc = flush_values(cache, cache->v_ring + cache->head * kD, slabs, F, rs, cache->n_quant, stream);
         if (rc != KIVI_OK) return rc;
         launches = 2;
     }

@@ -66,6 +66,7 @@ class CCacheConfig(ctypes.Structure):
         ("bits", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("group_size", ctypes.c_int32),
         ("residual_length", ctypes.c_int32), ("flush_tokens", ctypes.c_int32),
         ("store_capacity", ctypes.c_int64), ("meta_format", ctypes.c_int32),
+        ("bf16", ctypes.c_int32),
     ]
 
 
@@ -340,13 +341,16 @@ class Cache:
 
     def __init__(self, layers: int, batch: int, kv_heads: int, store_capacity: int, bits: int = 4,
                  residual_length: int = 128, flush_tokens: int = GROUP, device="cuda",
-                 meta: str = "f32"):
+                 meta: str = "f32", dtype=torch.float16):
         if meta not in ("f32", "f16"):
             raise ValueError("meta must be 'f32' or 'f16'")
-        self.meta = meta
+        if dtype not in (torch.float16, torch.bfloat16):
+            raise ValueError("dtype must be torch.float16 or torch.bfloat16")
+        self.meta, self.dtype = meta, dtype
         self.cfg = CCacheConfig(layers, batch, kv_heads, bits, HEAD_DIM, GROUP, residual_length,
                                 flush_tokens, store_capacity,
-                                KIVI_META_F16 if meta == "f16" else KIVI_META_F32)
+                                KIVI_META_F16 if meta == "f16" else KIVI_META_F32,
+                                1 if dtype == torch.bfloat16 else 0)
         n = int(lib().kivi_cache_device_bytes(ctypes.byref(self.cfg)))
         if n == 0:
             raise KiviError(-3, "kivi_cache_device_bytes")
@@ -388,15 +392,22 @@ class Cache:
         return out[0], out[1]
 
     def rings(self) -> tuple[torch.Tensor, torch.Tensor]:
-        """fp16 [slabs][ring][128] residual rings (torch views of the buffer)."""
+        """[slabs][ring][128] residual rings in the cache's dtype (torch views
+        of the buffer)."""
         shape = (self.slabs, self.c.ring, HEAD_DIM)
-        return (self._view(self.c.k_ring, torch.float16, shape),
-                self._view(self.c.v_ring, torch.float16, shape))
+        return (self._view(self.c.k_ring, self.dtype, shape),
+                self._view(self.c.v_ring, self.dtype, shape))
 
     # ---- calls
+    def _need_dtype(self, t: torch.Tensor, name: str) -> None:
+        if t.dtype != self.dtype:
+            raise TypeError(f"{name} must be {self.dtype} for this cache, got {t.dtype}")
+
     def prefill(self, k: torch.Tensor, v: torch.Tensor, stream=None) -> None:
-        _need_f16(k, "k")
-        _need_f16(v, "v")
+        _need_f16(k, "k", allow_bf16=True)
+        _need_f16(v, "v", allow_bf16=True)
+        self._need_dtype(k, "k")
+        self._need_dtype(v, "v")
         if k.stride(0) != v.stride(0) or k.shape != v.shape:
             raise ValueError("k and v must have one shape and slab stride")
         _check(lib().kivi_cache_prefill(ctypes.byref(self.c), k.data_ptr(), v.data_ptr(), k.stride(0),
@@ -404,9 +415,10 @@ class Cache:
 
     def append(self, layer: int, k_new: torch.Tensor, v_new: torch.Tensor, stream=None) -> None:
         for t, name in ((k_new, "k_new"), (v_new, "v_new")):
-            if t.dtype != torch.float16 or not t.is_cuda or not t.is_contiguous() or \
+            self._need_dtype(t, name)
+            if not t.is_cuda or not t.is_contiguous() or \
                     t.numel() != self.cfg.batch * self.cfg.kv_heads * HEAD_DIM:
-                raise ValueError(f"{name} must be contiguous float16 [batch*kv_heads][128]")
+                raise ValueError(f"{name} must be a contiguous device tensor [batch*kv_heads][128]")
         _check(lib().kivi_cache_append(ctypes.byref(self.c), layer, k_new.data_ptr(), v_new.data_ptr(),
                                        _stream(stream)), "kivi_cache_append")
 
@@ -416,8 +428,8 @@ class Cache:
     def attend(self, layer: int, q: torch.Tensor, out: torch.Tensor | None = None,
                workspace: torch.Tensor | None = None, softmax_scale: float | None = None,
                stream=None) -> torch.Tensor:
-        if q.dtype != torch.float16 or not q.is_cuda or q.dim() != 3 or not q.is_contiguous():
-            raise ValueError("q must be a contiguous float16 device tensor [B][Hq][128]")
+        _need_query(q)
+        self._need_dtype(q, "q")
         B, Hq, D = q.shape
         if softmax_scale is None:
             softmax_scale = 1.0 / math.sqrt(D)

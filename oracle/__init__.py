@@ -373,8 +373,9 @@ class CacheModel:
     order.  Slab s = (layer * batch + b) * kv_heads + h."""
 
     def __init__(self, layers: int, batch: int, kv_heads: int, capacity: int, bits: int = 4,
-                 R: int = 128, F: int = 32, D: int = 128, meta: str = "f32"):
+                 R: int = 128, F: int = 32, D: int = 128, meta: str = "f32", fmt: str = "f16"):
         self.layers, self.batch, self.kv_heads, self.R, self.F, self.D = layers, batch, kv_heads, R, F, D
+        self.fmt = fmt
         self.slabs = layers * batch * kv_heads
         self.kstore = Store(KEYS, self.slabs, capacity, D, bits, meta=meta)
         self.vstore = Store(VALUES, self.slabs, capacity, D, bits, meta=meta)
@@ -390,9 +391,9 @@ class CacheModel:
         Q = flush_count(self.length, self.R, self.F)
         if Q > self.n_quant:
             quantize_keys(np.ascontiguousarray(self.k[:, self.n_quant:Q]), self.kstore, self.n_quant,
-                          want_recon=False)
+                          want_recon=False, fmt=self.fmt)
             quantize_values(np.ascontiguousarray(self.v[:, self.n_quant:Q]), self.vstore, self.n_quant,
-                            want_recon=False)
+                            want_recon=False, fmt=self.fmt)
             self.n_quant = Q
 
     def prefill(self, k, v):
@@ -401,8 +402,9 @@ class CacheModel:
         self._flush_to_rule()
 
     def step(self, k_new, v_new, q, Hq: int) -> np.ndarray:
-        """k_new, v_new fp16 [slabs][D] (this step's token of every slab);
-        q fp16 [layers][batch][Hq][D].  Returns float64 [layers][batch][Hq][D]."""
+        """k_new, v_new [slabs][D] (this step's token of every slab) and q
+        [layers][batch][Hq][D], 16-bit in the model's format.  Returns float64
+        [layers][batch][Hq][D]."""
         self.k = np.concatenate([self.k, _as_u16(k_new)[:, None, :]], axis=1)
         self.v = np.concatenate([self.v, _as_u16(v_new)[:, None, :]], axis=1)
         q = _as_u16(q)
@@ -415,6 +417,6 @@ class CacheModel:
                                        self.kstore.slabs(lo, hi) if nq else None,
                                        self.vstore.slabs(lo, hi) if nq else None, nq,
                                        np.ascontiguousarray(self.k[lo:hi, nq:]),
-                                       np.ascontiguousarray(self.v[lo:hi, nq:]), nr)
+                                       np.ascontiguousarray(self.v[lo:hi, nq:]), nr, fmt=self.fmt)
         self._flush_to_rule()
         return out

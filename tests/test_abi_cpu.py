@@ -221,7 +221,7 @@ def test_cache_rejects_bad_configs():
     assert L.kivi_cache_device_bytes(ctypes.byref(ok)) > 0
     for field, bad in (("layers", 0), ("layers", 257), ("bits", 3), ("head_dim", 64),
                        ("group_size", 64), ("flush_tokens", 48), ("residual_length", 100),
-                       ("store_capacity", 4100), ("batch", 0), ("meta_format", 2)):
+                       ("store_capacity", 4100), ("batch", 0), ("meta_format", 2), ("bf16", 2)):
         cfg = kivi.CCacheConfig(2, 2, 8, 4, 128, 32, 128, 32, 4096)
         setattr(cfg, field, bad)
         assert L.kivi_cache_device_bytes(ctypes.byref(cfg)) == 0, field
@@ -251,6 +251,16 @@ def test_cache_init_checks_buffer_and_step_order():
     assert c.length == 0
     assert L.kivi_cache_attend_workspace_bytes(ctypes.byref(c), 8) >= \
         L.kivi_decode_attend_workspace_bytes(1, 8, 2, 256, 96)
+
+
+def test_bf16_cache_config():
+    L = kivi.lib()
+    ok = kivi.CCacheConfig(2, 1, 2, 4, 128, 32, 64, 32, 256, kivi.KIVI_META_F32, 1)
+    assert L.kivi_cache_device_bytes(ctypes.byref(ok)) == \
+        L.kivi_cache_device_bytes(ctypes.byref(kivi.CCacheConfig(2, 1, 2, 4, 128, 32, 64, 32, 256)))
+    # a bfloat16 cache keeps binary32 scale/zero, as the _bf16 flushes do
+    bad = kivi.CCacheConfig(2, 1, 2, 4, 128, 32, 64, 32, 256, kivi.KIVI_META_F16, 1)
+    assert L.kivi_cache_device_bytes(ctypes.byref(bad)) == 0
 
 
 def test_cache_with_binary16_metadata_halves_the_metadata_sections():

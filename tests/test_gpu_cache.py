@@ -26,6 +26,8 @@ CASES = [
     (1, 3, 2, 16, 4, 32, 32, 256, 0, 90, "f32"),         # empty prompt
     (2, 2, 2, 8, 4, 64, 32, 512, 150, 100, "f16"),       # binary16 scale/zero
     (2, 1, 2, 4, 2, 0, 32, 256, 31, 70, "f16"),
+    (2, 2, 2, 8, 4, 64, 32, 512, 150, 100, "bf16"),      # a bfloat16 cache
+    (1, 2, 8, 32, 2, 128, 128, 512, 200, 140, "bf16"),
 ]
 
 
@@ -41,26 +43,39 @@ def _meta_equal(gpu: torch.Tensor, host: np.ndarray) -> bool:
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "L%d-B%d-H%d-q%d-b%d-R%d-F%d-S%d-%s" % (
     c[0], c[1], c[2], c[3], c[4], c[5], c[6], c[8], c[10]))
 def test_decode_loop_matches_model(case):
-    layers, batch, kvh, Hq, bits, R, F, cap, S0, steps, meta = case
+    """The last field is the scale/zero format ("f32", "f16") or "bf16" for a
+    bfloat16 cache (binary32 scale/zero; tolerance as for the bfloat16
+    attend: 2e-3 + 2^-8 max|v|)."""
+    layers, batch, kvh, Hq, bits, R, F, cap, S0, steps, variant = case
+    bf16 = variant == "bf16"
+    meta = "f32" if bf16 else variant
+    dtype = torch.bfloat16 if bf16 else torch.float16
+    fmt = "bf16" if bf16 else "f16"
     seed = 9000 + S0 + R
     slabs = layers * batch * kvh
     per = batch * kvh
     note(f"cache loop layers={layers} batch={batch} kv_heads={kvh} Hq={Hq} bits={bits} R={R} F={F} "
          f"capacity={cap} prompt={S0} steps={steps} meta={meta}")
-    c = kivi.Cache(layers, batch, kvh, cap, bits, R, F, meta=meta)
-    m = oracle.CacheModel(layers, batch, kvh, cap, bits, R, F, meta=meta)
+    c = kivi.Cache(layers, batch, kvh, cap, bits, R, F, meta=meta, dtype=dtype)
+    m = oracle.CacheModel(layers, batch, kvh, cap, bits, R, F, meta=meta, fmt=fmt)
+    vmax = 0.0
     if S0:
-        k0 = synth.kv_tensor(slabs, S0, keys=True, seed=seed, device="cuda")
-        v0 = synth.kv_tensor(slabs, S0, keys=False, seed=seed, device="cuda")
+        k0 = synth.kv_tensor(slabs, S0, keys=True, seed=seed, device="cuda", dtype=dtype)
+        v0 = synth.kv_tensor(slabs, S0, keys=False, seed=seed, device="cuda", dtype=dtype)
+        vmax = float(v0.float().abs().max())
         c.prefill(k0, v0)
         m.prefill(u16(k0), u16(v0))
     assert (c.length, c.n_quant) == (m.length, m.n_quant)
     ws = torch.empty(c.attend_workspace_bytes(Hq), dtype=torch.uint8, device="cuda")
     worst = 0.0
     for step in range(steps):
-        kn = synth.kv_tensor(slabs, 1, keys=True, seed=seed * 1000 + step, device="cuda")[:, 0].contiguous()
-        vn = synth.kv_tensor(slabs, 1, keys=False, seed=seed * 1000 + step, device="cuda")[:, 0].contiguous()
-        q = synth.query(layers * batch, Hq, seed=seed * 1000 + step, device="cuda").view(layers, batch, Hq, D)
+        kn = synth.kv_tensor(slabs, 1, keys=True, seed=seed * 1000 + step, device="cuda",
+                             dtype=dtype)[:, 0].contiguous()
+        vn = synth.kv_tensor(slabs, 1, keys=False, seed=seed * 1000 + step, device="cuda",
+                             dtype=dtype)[:, 0].contiguous()
+        vmax = max(vmax, float(vn.float().abs().max()))
+        q = synth.query(layers * batch, Hq, seed=seed * 1000 + step, device="cuda").to(dtype) \
+            .view(layers, batch, Hq, D)
         outs = []
         for layer in range(layers):
             c.append(layer, kn[layer * per:(layer + 1) * per], vn[layer * per:(layer + 1) * per])
@@ -74,7 +89,8 @@ def test_decode_loop_matches_model(case):
         for layer in range(layers):
             err = float(np.max(np.abs(outs[layer].cpu().numpy().astype(np.float64) - ref[layer])))
             worst = max(worst, err)
-            assert err <= TOL, f"step {step} layer {layer}: max-abs error {err:.3e}"
+            tol = TOL + (2.0 ** -8 * vmax if bf16 else 0.0)
+            assert err <= tol, f"step {step} layer {layer}: max-abs error {err:.3e}"
     Q = c.n_quant
     ks, vs = c.stores()
     torch.cuda.synchronize()
