@@ -203,7 +203,9 @@ int decode_attend_entry(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
     if ((rc = check_store(v, KIVI_VALUES, slabs, 0, n_quant)) != KIVI_OK) return rc;
     if (k->bits != v->bits) return KIVI_ERR_SHAPE;
     if (k->group_size != v->group_size || k->meta_format != v->meta_format) return KIVI_ERR_UNSUPPORTED;
-    if (k->head_dim != kD || v->head_dim != kD) return KIVI_ERR_UNSUPPORTED;
+    // head_dim 128, or 64 with groups of 32 (binary32 scale/zero: meta16 stores are head_dim 128)
+    const int32_t D = k->head_dim;
+    if (v->head_dim != D || !(D == kD || (D == 64 && k->group_size == 32))) return KIVI_ERR_UNSUPPORTED;
     if (bf16 && meta16(k)) return KIVI_ERR_UNSUPPORTED;        // bfloat16 stores keep binary32 metadata
     if (B == 0) return KIVI_OK;
     if (!q || !out) return KIVI_ERR_NULL;
@@ -212,10 +214,10 @@ int decode_attend_entry(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
         (res_ring == 0 && res_head != 0) || res_ring >= kMaxAttendTokens) return KIVI_ERR_SHAPE;
     if (n_res > 0) {
         const int64_t rows = res_ring > 0 ? res_ring : n_res;
-        if ((rc = check_f16_tensor(k_res, slabs, rows, res_bh_stride)) != KIVI_OK) return rc;
-        if ((rc = check_f16_tensor(v_res, slabs, rows, res_bh_stride)) != KIVI_OK) return rc;
+        if ((rc = check_f16_tensor(k_res, slabs, rows, res_bh_stride, D)) != KIVI_OK) return rc;
+        if ((rc = check_f16_tensor(v_res, slabs, rows, res_bh_stride, D)) != KIVI_OK) return rc;
     }
-    const kivi::AttendPlan plan = kivi::plan_attend(B, Hq, Hkv, n_quant, n_res, seq_n_quant != nullptr);
+    const kivi::AttendPlan plan = kivi::plan_attend(B, Hq, Hkv, n_quant, n_res, seq_n_quant != nullptr, D);
     if (!workspace || workspace_bytes < plan.workspace_bytes) return KIVI_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KIVI_ERR_ALIGN;
     if (plan.n_split > kMaxBlocks || slabs > 65535 || B * Hq > kMaxBlocks) return KIVI_ERR_SHAPE;
@@ -238,6 +240,7 @@ int decode_attend_entry(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
     a.workspace = workspace; a.bits = k->bits; a.group = k->group_size;
     a.meta16 = meta16(k);
     a.bf16 = bf16;
+    a.head_dim = D;
     return finish(kivi::launch_decode_attend(a, plan, stream));
 }
 

@@ -10,9 +10,10 @@ namespace kivi {
 // Merge the splits of one (sequence, query head), base-2 log-sum-exp:
 // o = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i with M = max_i m_i.
 // WAVES waves per row: wave w takes splits w, w + WAVES, ..., lane l
-// channels 2l and 2l + 1; the waves' sums meet in LDS.  Many splits (small
-// batches, long contexts) get 16 waves, so each walks only a few of them.
-template <int WAVES>
+// channels 2l and 2l + 1 (lanes l < D/2); the waves' sums meet in LDS.  Many
+// splits (small batches, long contexts) get 16 waves, so each walks only a
+// few of them.
+template <int WAVES, int D>
 __global__ __launch_bounds__(64 * WAVES) void attend_combine_kernel(const float* __restrict__ ws_o,
                                                                    const float* __restrict__ ws_ml,
                                                                    int64_t n_split, float* __restrict__ out)
@@ -25,7 +26,8 @@ __global__ __launch_bounds__(64 * WAVES) void attend_combine_kernel(const float*
     const int w = t >> 6;
     const int l = t & 63;
     const float* ml = ws_ml + row * n_split * 2;
-    const float2* o = reinterpret_cast<const float2*>(ws_o + row * n_split * kHeadDim) + l;
+    const float2* o = reinterpret_cast<const float2*>(ws_o + row * n_split * D) + l;
+    const bool has = l < D / 2;                      // the lane has channels (always at D = 128)
 
     float M = -INFINITY;
     for (int64_t i = t; i < n_split; i += 64 * WAVES) M = fmaxf(M, ml[2 * i]);
@@ -50,7 +52,7 @@ __global__ __launch_bounds__(64 * WAVES) void attend_combine_kernel(const float*
         for (int u = 0; u < kU; ++u) {
             const int64_t s = i + u * WAVES;
             mv[u] = *reinterpret_cast<const float2*>(ml + 2 * s);
-            ov[u] = o[s * (kHeadDim / 2)];
+            ov[u] = has ? o[s * (D / 2)] : make_float2(0.0f, 0.0f);
         }
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
@@ -62,7 +64,7 @@ __global__ __launch_bounds__(64 * WAVES) void attend_combine_kernel(const float*
     }
     for (; i < n_split; i += WAVES) {
         const float2 mv = *reinterpret_cast<const float2*>(ml + 2 * i);
-        const float2 ov = o[i * (kHeadDim / 2)];
+        const float2 ov = has ? o[i * (D / 2)] : make_float2(0.0f, 0.0f);
         const float e = exp2f(mv.x - M);
         L = __builtin_fmaf(e, mv.y, L);
         acc.x = __builtin_fmaf(e, ov.x, acc.x);
@@ -83,7 +85,7 @@ __global__ __launch_bounds__(64 * WAVES) void attend_combine_kernel(const float*
         // a sequence with no tokens at all (only possible in a variable-length
         // batch) has every partial empty (m = -inf, l = 0): its output is zero
         const float2 r = Lt > 0.0f ? make_float2(at.x / Lt, at.y / Lt) : make_float2(0.0f, 0.0f);
-        reinterpret_cast<float2*>(out + row * kHeadDim)[l] = r;
+        if (has) reinterpret_cast<float2*>(out + row * D)[l] = r;
     }
 }
 
@@ -92,7 +94,8 @@ __global__ __launch_bounds__(64 * WAVES) void attend_combine_kernel(const float*
 // Larger ones get as few whole rounds of kWaveSlots waves as keep a wave at
 // most kMaxStepsPerWave steps, with the steps spread evenly, so the last
 // round is not a short tail.
-AttendPlan plan_attend(int64_t B, int Hq, int Hkv, int64_t n_quant, int64_t n_res, bool varlen) {
+AttendPlan plan_attend(int64_t B, int Hq, int Hkv, int64_t n_quant, int64_t n_res, bool varlen,
+                       int head_dim) {
     const int64_t pairs = B * Hkv;
     const int64_t steps_q = (n_quant + kStep - 1) / kStep;
     const int64_t steps = steps_q + (n_res + kStep - 1) / kStep;
@@ -121,7 +124,7 @@ AttendPlan plan_attend(int64_t B, int Hq, int Hkv, int64_t n_quant, int64_t n_re
     p.steps_per_wave = spw;
     p.n_split = (steps + spw - 1) / spw;
     const size_t rows = static_cast<size_t>(B) * static_cast<size_t>(Hq) * static_cast<size_t>(p.n_split);
-    const size_t o_bytes = (rows * kHeadDim * sizeof(float) + 255) & ~static_cast<size_t>(255);
+    const size_t o_bytes = (rows * head_dim * sizeof(float) + 255) & ~static_cast<size_t>(255);
     p.workspace_bytes = o_bytes + rows * 2 * sizeof(float);
     return p;
 }
@@ -131,19 +134,22 @@ AttendPlan plan_attend(int64_t B, int Hq, int Hkv, int64_t n_quant, int64_t n_re
 hipError_t launch_decode_attend(const AttendArgs& a, const AttendPlan& p, hipStream_t stream) {
     float* ws_o = static_cast<float*>(a.workspace);
     const size_t rows = static_cast<size_t>(a.B) * a.Hq * p.n_split;
-    const size_t o_bytes = (rows * kHeadDim * sizeof(float) + 255) & ~static_cast<size_t>(255);
+    const size_t o_bytes = (rows * a.head_dim * sizeof(float) + 255) & ~static_cast<size_t>(255);
     float* ws_ml = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + o_bytes);
     hipError_t e;
     if (a.bf16) e = launch_attend_partial_bf16(a, p, ws_o, ws_ml, stream);
     else if (a.meta16) e = launch_partials<2, false>(a, p, ws_o, ws_ml, stream);
     else e = launch_partials<4, false>(a, p, ws_o, ws_ml, stream);
     if (e != hipSuccess) return e;
-    if (p.n_split >= 48)
-        hipLaunchKernelGGL(attend_combine_kernel<16>, dim3(static_cast<uint32_t>(a.B * a.Hq)), dim3(64 * 16), 0,
-                           stream, ws_o, ws_ml, p.n_split, a.out);
-    else
-        hipLaunchKernelGGL(attend_combine_kernel<4>, dim3(static_cast<uint32_t>(a.B * a.Hq)), dim3(64 * 4), 0,
-                           stream, ws_o, ws_ml, p.n_split, a.out);
+    const dim3 rows_grid(static_cast<uint32_t>(a.B * a.Hq));
+    const bool many = p.n_split >= 48;
+    if (a.head_dim == 64) {
+        if (many) hipLaunchKernelGGL((attend_combine_kernel<16, 64>), rows_grid, dim3(64 * 16), 0, stream, ws_o, ws_ml, p.n_split, a.out);
+        else hipLaunchKernelGGL((attend_combine_kernel<4, 64>), rows_grid, dim3(64 * 4), 0, stream, ws_o, ws_ml, p.n_split, a.out);
+    } else {
+        if (many) hipLaunchKernelGGL((attend_combine_kernel<16, 128>), rows_grid, dim3(64 * 16), 0, stream, ws_o, ws_ml, p.n_split, a.out);
+        else hipLaunchKernelGGL((attend_combine_kernel<4, 128>), rows_grid, dim3(64 * 4), 0, stream, ws_o, ws_ml, p.n_split, a.out);
+    }
     return hipGetLastError();
 }
 

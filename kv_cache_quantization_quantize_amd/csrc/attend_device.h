@@ -247,30 +247,49 @@ __device__ __forceinline__ float2 meta_pair(u32x2 v) {
 // QK^T leaves each lane its scores (rows 4q .. 4q+3 of both 16-token blocks).
 __device__ __forceinline__ int pv_token(int q, int s) { return 16 * (s >> 2) + 4 * q + (s & 3); }
 
-template <int BITS, int G, int MB>
+// Channel geometry for head_dim D (128 or 64).  QK^T: lane group q holds
+// channels kCPG*q + 8*kb + slot of key unit kb < kKB.  PV: MFMA i < kPV covers
+// channels kPV*m + i (m = 0..15), so lane (q, n) takes the kPV channels
+// kPV*n .. kPV*n + kPV - 1 of its tokens.
+template <int D> struct Geo {
+    static constexpr int kCPG = D / 4;          // channels per 16-lane group
+    static constexpr int kKB = D / 32;          // QK^T key units (MFMA k-steps)
+    static constexpr int kPV = D / 16;          // PV MFMAs
+};
+
+template <int BITS, int G, int MB, int D>
 __device__ __forceinline__ void issue_step(StepLoad& L, const StoreView& S, const LaneOffsets& O,
                                            uint32_t t0, int n) {
-    constexpr uint32_t kRow = kHeadDim * BITS / 8;          // code bytes per token
+    constexpr uint32_t kRow = D * BITS / 8;                 // code bytes per token
+    constexpr int kMPT = D / G;                             // value groups per token
     const uint32_t ko = O.k + t0 * kRow;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-        if constexpr (BITS == 4) {
+        // the lane group's kCPG channels: kKB words (4-bit) or kKB / 2 (2-bit)
+        if constexpr (BITS == 4 && D == 128) {
             const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(S.kc, ko + 16 * kRow * blk, 0, kStreamLoad);
             L.kw[blk][0] = t.x; L.kw[blk][1] = t.y; L.kw[blk][2] = t.z; L.kw[blk][3] = t.w;
-        } else {
+        } else if constexpr (BITS == 4 || D == 128) {
             const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(S.kc, ko + 16 * kRow * blk, 0, kStreamLoad);
-            L.kw[blk][0] = t.x; L.kw[blk][1] = t.x; L.kw[blk][2] = t.y; L.kw[blk][3] = t.y;
+            if constexpr (BITS == 4) {
+                L.kw[blk][0] = t.x; L.kw[blk][1] = t.y;
+            } else {
+                L.kw[blk][0] = t.x; L.kw[blk][1] = t.x; L.kw[blk][2] = t.y; L.kw[blk][3] = t.y;
+            }
+        } else {
+            const uint32_t t = __builtin_amdgcn_raw_buffer_load_b32(S.kc, ko + 16 * kRow * blk, 0, kStreamLoad);
+            L.kw[blk][0] = t; L.kw[blk][1] = t;
         }
     }
     // key metadata of the step's group (a 32-token step never crosses one):
     // two channels' pairs, 2 * MB bytes
-    const uint32_t kmo = O.km + (t0 / G) * (kHeadDim * MB);
-    // value metadata: 128/G pairs per token; the lane's one or two groups
-    const uint32_t vmo = O.vm + (kHeadDim * MB / G) * t0;
+    const uint32_t kmo = O.km + (t0 / G) * (D * MB);
+    // value metadata: D/G pairs per token; the lane's one or two groups
+    const uint32_t vmo = O.vm + (D * MB / G) * t0;
     if constexpr (MB == 4) {
         L.ks = __builtin_amdgcn_raw_buffer_load_b64(S.ks, kmo, 0, kStreamLoad);
         L.kz = __builtin_amdgcn_raw_buffer_load_b64(S.kz, kmo, 0, kStreamLoad);
-        if constexpr (G == 128) {
+        if constexpr (kMPT == 1) {
             L.vs = u32x2{__builtin_amdgcn_raw_buffer_load_b32(S.vs, vmo, 0, kStreamLoad), 0u};
             L.vz = u32x2{__builtin_amdgcn_raw_buffer_load_b32(S.vz, vmo, 0, kStreamLoad), 0u};
         } else {
@@ -280,7 +299,7 @@ __device__ __forceinline__ void issue_step(StepLoad& L, const StoreView& S, cons
     } else {
         L.ks = u32x2{__builtin_amdgcn_raw_buffer_load_b32(S.ks, kmo, 0, kStreamLoad), 0u};
         L.kz = u32x2{__builtin_amdgcn_raw_buffer_load_b32(S.kz, kmo, 0, kStreamLoad), 0u};
-        if constexpr (G == 128) {
+        if constexpr (kMPT == 1) {
             L.vs = u32x2{static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(S.vs, vmo, 0, kStreamLoad)), 0u};
             L.vz = u32x2{static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(S.vz, vmo, 0, kStreamLoad)), 0u};
         } else {
@@ -289,11 +308,14 @@ __device__ __forceinline__ void issue_step(StepLoad& L, const StoreView& S, cons
         }
     }
     const uint32_t vo = O.v + t0 * kRow;
+    // the lane's kPV channels start at bit kPV * n * BITS of the token row
+    constexpr int kPV = Geo<D>::kPV;
+    const uint32_t shift = (kPV * n * BITS) & 31;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
         const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(S.vc, vo + (16 * (s >> 2) + (s & 3)) * kRow, 0, kStreamLoad);
-        // 2-bit: bring the lane's 8 channels (half of the word) to the low half
-        L.vw[s] = BITS == 4 ? w : (w >> (16 * (n & 1)));
+        // bring the lane's channels to the low bits
+        L.vw[s] = (kPV * BITS == 32) ? w : (w >> shift);
     }
 }
 
@@ -309,17 +331,19 @@ constexpr int kKPad = 4;                      // floats of padding per 32 channe
 constexpr int kVRow = kStep + 4;              // padded row of 32 tokens
 __device__ __forceinline__ int kidx(int ch) { return ch + kKPad * (ch >> 5); }
 
+template <int D>
 struct Smem {
-    alignas(16) float ks[kHeadDim + kKPad * 4];       // key scale of the step's group
-    alignas(16) float kz[kHeadDim + kKPad * 4];       // key zero - 1024 * scale
-    alignas(16) float vs[kHeadDim / kGroup][kVRow];   // value scale, [group][token]
-    alignas(16) float vz[kHeadDim / kGroup][kVRow];   // value zero - 1024 * scale
-    alignas(16) uint4 bq[4][64];                       // QK^T B operand (queries), [unit][lane]
+    alignas(16) float ks[D + kKPad * (D / 32)];       // key scale of the step's group
+    alignas(16) float kz[D + kKPad * (D / 32)];       // key zero - M * scale
+    alignas(16) float vs[D / kGroup][kVRow];          // value scale, [group][token]
+    alignas(16) float vz[D / kGroup][kVRow];          // value zero - M * scale
+    alignas(16) uint4 bq[D / 32][64];                 // QK^T B operand (queries), [unit][lane]
 };
 
 // The QK^T B operand of channel unit kb, kept in LDS rather than in 16
 // registers across the step loop (the registers hold the prefetched loads).
-__device__ __forceinline__ Frag query_frag(const Smem& sm, int kb, int l) {
+template <int D>
+__device__ __forceinline__ Frag query_frag(const Smem<D>& sm, int kb, int l) {
     const uint4 v = sm.bq[kb][l];
     Frag f;
     f.u[0] = v.x; f.u[1] = v.y; f.u[2] = v.z; f.u[3] = v.w;
@@ -397,14 +421,16 @@ __device__ __forceinline__ Frag softmax_any(const float4_t (&acc_s)[2], SoftStat
 }
 
 // One step of store tokens [t0, t0 + 32), tokens at or past n_quant masked.
-template <int BITS, int G, int MB, bool BF>
-__device__ __forceinline__ void store_step(const StepLoad& L, Smem& sm, SoftState& st,
+template <int BITS, int G, int MB, bool BF, int D>
+__device__ __forceinline__ void store_step(const StepLoad& L, Smem<D>& sm, SoftState& st,
                                            int t0, int n_quant, float c2,
                                            int l, int n, int q) {
     // ---- stage this step's metadata in LDS (zero' = zero - M * scale')
     constexpr float kM = kMagicValue<BF>;
+    constexpr int kMPT = D / G;                 // value groups per token
+    constexpr int kCPG = Geo<D>::kCPG, kKB = Geo<D>::kKB, kPV = Geo<D>::kPV;
     lds_order();
-    {
+    if (2 * l < D) {
         // key scale times 2^-e of its channel's code position (code_pairs)
         const float2 ks = meta_pair<MB>(L.ks), kz = meta_pair<MB>(L.kz);
         const float s0 = ks.x * kscale_factor<BITS, BF>(2 * l);
@@ -414,14 +440,14 @@ __device__ __forceinline__ void store_step(const StepLoad& L, Smem& sm, SoftStat
             make_float2(__builtin_fmaf(-kM, s0, kz.x), __builtin_fmaf(-kM, s1, kz.y));
     }
     {
-        // lanes l and l + 32 hold the same token; for G = 64 and 128 they
-        // hold the same groups too and write the same values
+        // lanes l and l + 32 hold the same token; with 2 groups or 1 per
+        // token they hold the same groups too and write the same values
         const float2 vs = meta_pair<MB>(L.vs), vz = meta_pair<MB>(L.vz);
         const int tt = l & 31;
-        const int gg = G == 32 ? (l >> 5) * 2 : 0;
+        const int gg = kMPT == 4 ? (l >> 5) * 2 : 0;
         sm.vs[gg][tt] = vs.x;
         sm.vz[gg][tt] = __builtin_fmaf(-kM, vs.x, vz.x);
-        if constexpr (G != 128) {
+        if constexpr (kMPT != 1) {
             sm.vs[gg + 1][tt] = vs.y;
             sm.vz[gg + 1][tt] = __builtin_fmaf(-kM, vs.y, vz.y);
         }
@@ -431,8 +457,8 @@ __device__ __forceinline__ void store_step(const StepLoad& L, Smem& sm, SoftStat
     // ---- S^T = K Q^T, token t0 + 16*blk + n, channel unit kb of group q
     float4_t acc_s[2] = {float4_t{0.0f, 0.0f, 0.0f, 0.0f}, float4_t{0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-        const int cb = kidx(32 * q + 8 * kb);
+    for (int kb = 0; kb < kKB; ++kb) {
+        const int cb = kidx(kCPG * q + 8 * kb);
         const float4 s0 = *reinterpret_cast<const float4*>(&sm.ks[cb]);
         const float4 s1 = *reinterpret_cast<const float4*>(&sm.ks[cb + 4]);
         const float4 z0 = *reinterpret_cast<const float4*>(&sm.kz[cb]);
@@ -453,9 +479,9 @@ __device__ __forceinline__ void store_step(const StepLoad& L, Smem& sm, SoftStat
 
     const Frag bp = softmax_any<BF>(acc_s, st, c2, n_quant - t0, q);
 
-    // ---- O^T += V^T P^T: MFMA i covers channels 8m + i, m = 0..15.  Slot s of
-    // lane (q, m) is channel 8m + i of step token pv_token(q, s).
-    const int vg = n / (G / 8);                 // value group of the lane's channels 8n .. 8n+7
+    // ---- O^T += V^T P^T: MFMA i covers channels kPV*m + i, m = 0..15.  Slot s
+    // of lane (q, m) is channel kPV*m + i of step token pv_token(q, s).
+    const int vg = (kPV * n) / G;               // value group of the lane's kPV channels
     const float4 vsa = *reinterpret_cast<const float4*>(&sm.vs[vg][4 * q]);
     const float4 vsb = *reinterpret_cast<const float4*>(&sm.vs[vg][16 + 4 * q]);
     const float4 vza = *reinterpret_cast<const float4*>(&sm.vz[vg][4 * q]);
@@ -463,8 +489,8 @@ __device__ __forceinline__ void store_step(const StepLoad& L, Smem& sm, SoftStat
     const float vsc[8] = {vsa.x, vsa.y, vsa.z, vsa.w, vsb.x, vsb.y, vsb.z, vsb.w};
     const float vzp[8] = {vza.x, vza.y, vza.z, vza.w, vzb.x, vzb.y, vzb.z, vzb.w};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        // code of channel i of the lane's 8 (4-bit: nibble i; 2-bit: field i)
+    for (int i = 0; i < kPV; ++i) {
+        // code of channel i of the lane's kPV (4-bit: nibble i; 2-bit: field i)
         constexpr uint32_t kMask = BITS == 4 ? 0x000F000Fu : 0x00030003u;
         const uint32_t byte = BITS == 4 ? (i >> 1) : (i >> 2);
         const uint32_t shift = BITS == 4 ? 4 * (i & 1) : 2 * (i & 3);
@@ -487,24 +513,25 @@ __device__ __forceinline__ int ring_row(int tok, int head, int ring) {
     return r >= ring ? r - ring : r;
 }
 
-template <bool BF>
-__device__ __forceinline__ void residual_step(const uint16_t* kr, const uint16_t* vr, const Smem& sm,
+template <bool BF, int D>
+__device__ __forceinline__ void residual_step(const uint16_t* kr, const uint16_t* vr, const Smem<D>& sm,
                                               SoftState& st, int t0, int n_res, float c2,
                                               int l, int n, int q, int head, int ring) {
+    constexpr int kCPG = Geo<D>::kCPG, kKB = Geo<D>::kKB, kPV = Geo<D>::kPV;
     const int last = n_res - 1;
     float4_t acc_s[2] = {float4_t{0.0f, 0.0f, 0.0f, 0.0f}, float4_t{0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
         const int tok = ring_row(min(t0 + 16 * blk + n, last), head, ring);
-        const uint4* src = reinterpret_cast<const uint4*>(kr + tok * kHeadDim + 32 * q);
-        uint32_t rn[16];
+        const uint4* src = reinterpret_cast<const uint4*>(kr + tok * D + kCPG * q);
+        uint32_t rn[kCPG / 2];                  // the lane group's channels, natural order
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
+        for (int v = 0; v < kCPG / 8; ++v) {
             const uint4 t = src[v];
             rn[4 * v] = t.x; rn[4 * v + 1] = t.y; rn[4 * v + 2] = t.z; rn[4 * v + 3] = t.w;
         }
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
+        for (int kb = 0; kb < kKB; ++kb) {
             Frag ka;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -517,23 +544,26 @@ __device__ __forceinline__ void residual_step(const uint16_t* kr, const uint16_t
         }
     }
     const Frag bp = softmax_any<BF>(acc_s, st, c2, n_res - t0, q);
-    // V rows: lane (q, m=n) takes channels 8n .. 8n+7 of its 8 tokens
-    uint4 vrow[8];
+    // V rows: lane (q, m=n) takes channels kPV*n .. kPV*n + kPV - 1 of its 8 tokens
+    uint32_t vw[8][kPV / 2];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
         const int tok = ring_row(min(t0 + pv_token(q, s), last), head, ring);
-        vrow[s] = *reinterpret_cast<const uint4*>(vr + tok * kHeadDim + 8 * n);
+        const uint16_t* p = vr + tok * D + kPV * n;
+        if constexpr (kPV == 8) {
+            const uint4 t = *reinterpret_cast<const uint4*>(p);
+            vw[s][0] = t.x; vw[s][1] = t.y; vw[s][2] = t.z; vw[s][3] = t.w;
+        } else {
+            const uint2 t = *reinterpret_cast<const uint2*>(p);
+            vw[s][0] = t.x; vw[s][1] = t.y;
+        }
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < kPV; ++i) {
         Frag va;
         const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t* a0 = reinterpret_cast<const uint32_t*>(&vrow[2 * j]);
-            const uint32_t* a1 = reinterpret_cast<const uint32_t*>(&vrow[2 * j + 1]);
-            va.u[j] = __builtin_amdgcn_perm(a1[i >> 1], a0[i >> 1], sel);
-        }
+        for (int j = 0; j < 4; ++j) va.u[j] = __builtin_amdgcn_perm(vw[2 * j + 1][i >> 1], vw[2 * j][i >> 1], sel);
         st.acc_o[i] = mfma<BF>(va, bp, st.acc_o[i]);
     }
 }
@@ -544,12 +574,13 @@ __device__ __forceinline__ void residual_step(const uint16_t* kr, const uint16_t
 // that axis, so one wave may finish the store and start the residual.
 // Offsets within a slab fit in 32 bits: the ABI keeps n_quant and n_res
 // below 2^24 tokens.
-template <int BITS, int GQA, int G, int MB, bool BF>
+template <int BITS, int GQA, int G, int MB, bool BF, int D>
 __global__ __launch_bounds__(64) KIVI_ATTEND_OCCUPANCY void attend_partial_kernel(const AttendArgs a, int spw, int steps_q,
                                                             int64_t n_split, float* __restrict__ ws_o,
                                                             float* __restrict__ ws_ml)
 {
-    __shared__ Smem sm;
+    constexpr int kCPG = Geo<D>::kCPG, kKB = Geo<D>::kKB, kPV = Geo<D>::kPV;
+    __shared__ Smem<D> sm;
     const int l = threadIdx.x;
     const int n = l & 15;
     const int q = l >> 4;
@@ -576,8 +607,8 @@ __global__ __launch_bounds__(64) KIVI_ATTEND_OCCUPANCY void attend_partial_kerne
 
     // Store part: buffer views and the first two steps' loads, issued before
     // the query so the two HBM latencies overlap.
-    constexpr int kWords = kHeadDim * BITS / 32;
-    constexpr int kMetaPerTok = kHeadDim / G;
+    constexpr int kWords = D * BITS / 32;
+    constexpr int kMetaPerTok = D / G;
     StoreView S;
     LaneOffsets O;
     StepLoad buf[kNBuf];
@@ -593,37 +624,39 @@ __global__ __launch_bounds__(64) KIVI_ATTEND_OCCUPANCY void attend_partial_kerne
         const char* kmeta_z = static_cast<const char*>(a.k_zero) + bkv * a.k_meta_bh_stride * MB;
         const char* vmeta_s = static_cast<const char*>(a.v_scale) + bkv * a.v_meta_bh_stride * MB;
         const char* vmeta_z = static_cast<const char*>(a.v_zero) + bkv * a.v_meta_bh_stride * MB;
-        S.ks = make_rsrc(kmeta_s, n_groups * kHeadDim * MB);
-        S.kz = make_rsrc(kmeta_z, n_groups * kHeadDim * MB);
+        S.ks = make_rsrc(kmeta_s, n_groups * D * MB);
+        S.kz = make_rsrc(kmeta_z, n_groups * D * MB);
         S.vc = make_rsrc(a.v_codes + bkv * a.v_codes_bh_stride, static_cast<uint32_t>(nq) * kWords * 4u);
         S.vs = make_rsrc(vmeta_s, static_cast<uint32_t>(nq) * kMetaPerTok * MB);
         S.vz = make_rsrc(vmeta_z, static_cast<uint32_t>(nq) * kMetaPerTok * MB);
-        O.k = static_cast<uint32_t>(n * kWords + (BITS == 4 ? 4 * q : 2 * q)) * 4u;
-        O.v = static_cast<uint32_t>(4 * q * kWords + (BITS == 4 ? n : (n >> 1))) * 4u;
-        O.km = static_cast<uint32_t>(l) * (2u * MB);
-        O.vm = G == 32 ? static_cast<uint32_t>(l & 31) * (4u * MB) + static_cast<uint32_t>(l >> 5) * (2u * MB)
-                       : static_cast<uint32_t>(l & 31) * (kMetaPerTok * MB);
+        // the lane group's channels start at word kCPG * q * BITS / 32 of a
+        // token row; the lane's PV channels at word kPV * n * BITS / 32
+        O.k = static_cast<uint32_t>(n * kWords + kCPG * q * BITS / 32) * 4u;
+        O.v = static_cast<uint32_t>(4 * q * kWords + kPV * n * BITS / 32) * 4u;
+        O.km = static_cast<uint32_t>(l) * (2u * MB);      // lanes past D/2 load but stage nothing
+        O.vm = kMetaPerTok == 4 ? static_cast<uint32_t>(l & 31) * (4u * MB) + static_cast<uint32_t>(l >> 5) * (2u * MB)
+                                : static_cast<uint32_t>(l & 31) * (kMetaPerTok * MB);
 #pragma unroll
-        for (int u = 0; u + 1 < kNBuf; ++u) issue_step<BITS, G, MB>(buf[u], S, O, pref(j0 + u * kStep), n);
+        for (int u = 0; u + 1 < kNBuf; ++u) issue_step<BITS, G, MB, D>(buf[u], S, O, pref(j0 + u * kStep), n);
     }
 
     // B operand of QK^T: q of head n (zero for n >= GQA) in slot order.
     {
-        Frag bq[4];
-        uint32_t qn[16];                      // channels 32q .. 32q+31, natural order
+        Frag bq[kKB];
+        uint32_t qn[kCPG / 2];                // channels kCPG*q .. kCPG*q + kCPG - 1, natural order
         if (n < GQA) {
-            const uint4* src = reinterpret_cast<const uint4*>(a.q + (qrow0 + n) * kHeadDim + 32 * q);
+            const uint4* src = reinterpret_cast<const uint4*>(a.q + (qrow0 + n) * D + kCPG * q);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
+            for (int v = 0; v < kCPG / 8; ++v) {
                 const uint4 t = src[v];
                 qn[4 * v] = t.x; qn[4 * v + 1] = t.y; qn[4 * v + 2] = t.z; qn[4 * v + 3] = t.w;
             }
         } else {
 #pragma unroll
-            for (int v = 0; v < 16; ++v) qn[v] = 0u;
+            for (int v = 0; v < kCPG / 2; ++v) qn[v] = 0u;
         }
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 // slots (2j, 2j+1) = channels (8kb + j, 8kb + j + 4) of the lane's window
@@ -633,7 +666,7 @@ __global__ __launch_bounds__(64) KIVI_ATTEND_OCCUPANCY void attend_partial_kerne
                 bq[kb].u[j] = __builtin_amdgcn_perm(qn[c1 >> 1], qn[c0 >> 1], (s1 << 16) | s0);
             }
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) sm.bq[kb][l] = make_uint4(bq[kb].u[0], bq[kb].u[1], bq[kb].u[2], bq[kb].u[3]);
+        for (int kb = 0; kb < kKB; ++kb) sm.bq[kb][l] = make_uint4(bq[kb].u[0], bq[kb].u[1], bq[kb].u[2], bq[kb].u[3]);
         lds_order();
     }
 
@@ -650,8 +683,8 @@ __global__ __launch_bounds__(64) KIVI_ATTEND_OCCUPANCY void attend_partial_kerne
         for (int t0 = j0; t0 < j1; t0 += kNBuf * kStep) {
 #pragma unroll
             for (int u = 0; u < kNBuf; ++u) {
-                issue_step<BITS, G, MB>(buf[(u + kNBuf - 1) % kNBuf], S, O, pref(t0 + (u + kNBuf - 1) * kStep), n);
-                store_step<BITS, G, MB, BF>(buf[u], sm, st, t0 + u * kStep, j1, c2, l, n, q);
+                issue_step<BITS, G, MB, D>(buf[(u + kNBuf - 1) % kNBuf], S, O, pref(t0 + (u + kNBuf - 1) * kStep), n);
+                store_step<BITS, G, MB, BF, D>(buf[u], sm, st, t0 + u * kStep, j1, c2, l, n, q);
                 if (t0 + (u + 1) * kStep >= j1) goto store_done;
             }
         }
@@ -661,19 +694,21 @@ __global__ __launch_bounds__(64) KIVI_ATTEND_OCCUPANCY void attend_partial_kerne
         const uint16_t* kr = a.k_res + bkv * a.res_bh_stride;
         const uint16_t* vr = a.v_res + bkv * a.res_bh_stride;
         for (int t0 = r0; t0 < r1; t0 += kStep)
-            residual_step<BF>(kr, vr, sm, st, t0, r1, c2, l, n, q, a.res_head, a.res_ring);
+            residual_step<BF, D>(kr, vr, sm, st, t0, r1, c2, l, n, q, a.res_head, a.res_ring);
     }
 
-    // ---- partial (m, l, o) of head n: lane (q, n) holds channels 32q + 8r + i
+    // ---- partial (m, l, o) of head n: lane (q, n) holds channels
+    // kPV * (4q + r) + i (= kCPG q + kPV r + i)
     const float l_tot = rows_sum(st.l_part);
     if (n < GQA) {
-        float* dst = ws_o + ((qrow0 + n) * n_split + split) * kHeadDim + 32 * q;
+        float* dst = ws_o + ((qrow0 + n) * n_split + split) * D + kCPG * q;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            *reinterpret_cast<float4*>(dst + 8 * r) =
+            *reinterpret_cast<float4*>(dst + kPV * r) =
                 make_float4(st.acc_o[0][r], st.acc_o[1][r], st.acc_o[2][r], st.acc_o[3][r]);
-            *reinterpret_cast<float4*>(dst + 8 * r + 4) =
-                make_float4(st.acc_o[4][r], st.acc_o[5][r], st.acc_o[6][r], st.acc_o[7][r]);
+            if constexpr (kPV == 8)
+                *reinterpret_cast<float4*>(dst + kPV * r + 4) =
+                    make_float4(st.acc_o[4][r], st.acc_o[5][r], st.acc_o[6][r], st.acc_o[7][r]);
         }
         if (q == 0) {
             float* ml = ws_ml + ((qrow0 + n) * n_split + split) * 2;
@@ -689,24 +724,24 @@ __global__ __launch_bounds__(64) KIVI_ATTEND_OCCUPANCY void attend_partial_kerne
 // MB and element format BF.  Each translation unit that calls launch_partials
 // instantiates its own set of kernels.
 // ---------------------------------------------------------------------------
-template <int BITS, int GQA, int G, int MB, bool BF>
+template <int BITS, int GQA, int G, int MB, bool BF, int D>
 hipError_t launch_partial(const AttendArgs& a, const AttendPlan& p, float* ws_o, float* ws_ml,
                           hipStream_t stream) {
     const dim3 grid(static_cast<uint32_t>(p.n_split), static_cast<uint32_t>(a.B * a.Hkv));
-    hipLaunchKernelGGL((attend_partial_kernel<BITS, GQA, G, MB, BF>), grid, dim3(64), 0, stream, a,
+    hipLaunchKernelGGL((attend_partial_kernel<BITS, GQA, G, MB, BF, D>), grid, dim3(64), 0, stream, a,
                        static_cast<int>(p.steps_per_wave), static_cast<int>(p.steps_q), p.n_split,
                        ws_o, ws_ml);
     return hipGetLastError();
 }
 
-template <int BITS, int G, int MB, bool BF>
+template <int BITS, int G, int MB, bool BF, int D = 128>
 hipError_t launch_partial_gqa(const AttendArgs& a, const AttendPlan& p, float* ws_o, float* ws_ml,
                               hipStream_t stream) {
     switch (a.Hq / a.Hkv) {
-        case 1: return launch_partial<BITS, 1, G, MB, BF>(a, p, ws_o, ws_ml, stream);
-        case 2: return launch_partial<BITS, 2, G, MB, BF>(a, p, ws_o, ws_ml, stream);
-        case 4: return launch_partial<BITS, 4, G, MB, BF>(a, p, ws_o, ws_ml, stream);
-        default: return launch_partial<BITS, 8, G, MB, BF>(a, p, ws_o, ws_ml, stream);
+        case 1: return launch_partial<BITS, 1, G, MB, BF, D>(a, p, ws_o, ws_ml, stream);
+        case 2: return launch_partial<BITS, 2, G, MB, BF, D>(a, p, ws_o, ws_ml, stream);
+        case 4: return launch_partial<BITS, 4, G, MB, BF, D>(a, p, ws_o, ws_ml, stream);
+        default: return launch_partial<BITS, 8, G, MB, BF, D>(a, p, ws_o, ws_ml, stream);
     }
 }
 
@@ -714,6 +749,12 @@ template <int MB, bool BF>
 hipError_t launch_partials(const AttendArgs& a, const AttendPlan& p, float* ws_o, float* ws_ml,
                            hipStream_t stream) {
     const bool four = a.bits == 4;
+    if constexpr (MB == 4) {
+        // head_dim 64 (groups of 32, binary32 scale/zero)
+        if (a.head_dim == 64)
+            return four ? launch_partial_gqa<4, 32, MB, BF, 64>(a, p, ws_o, ws_ml, stream)
+                        : launch_partial_gqa<2, 32, MB, BF, 64>(a, p, ws_o, ws_ml, stream);
+    }
     switch (a.group) {
         case 64: return four ? launch_partial_gqa<4, 64, MB, BF>(a, p, ws_o, ws_ml, stream)
                              : launch_partial_gqa<2, 64, MB, BF>(a, p, ws_o, ws_ml, stream);

@@ -78,6 +78,7 @@ struct AttendArgs {
     int group;                     // 32, 64 or 128 (keys and values alike)
     bool meta16;                   // binary16 scale/zero (keys and values alike)
     bool bf16;                     // q, residual and the reconstruction in bfloat16
+    int head_dim;                  // 128, or 64 (groups of 32, binary32 scale/zero)
 };
 
 // Split of the token axis chosen for an attend shape; the workspace holds
@@ -88,7 +89,8 @@ struct AttendPlan {
     int64_t n_split;               // waves per (sequence, kv head)
     size_t workspace_bytes;
 };
-AttendPlan plan_attend(int64_t B, int Hq, int Hkv, int64_t n_quant, int64_t n_res, bool varlen);
+AttendPlan plan_attend(int64_t B, int Hq, int Hkv, int64_t n_quant, int64_t n_res, bool varlen,
+                       int head_dim = 128);
 
 hipError_t launch_key_flush(const FlushArgs& a, hipStream_t stream);
 hipError_t launch_value_flush(const FlushArgs& a, hipStream_t stream);

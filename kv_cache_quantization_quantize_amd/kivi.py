@@ -157,12 +157,12 @@ def _need_f16(t: torch.Tensor, name: str, allow_bf16: bool = False, D: int = HEA
 def _need_query(q: torch.Tensor) -> None:
     if q.dtype not in (torch.float16, torch.bfloat16) or not q.is_cuda or q.dim() != 3 \
             or not q.is_contiguous():
-        raise ValueError("q must be a contiguous float16 or bfloat16 device tensor [B][Hq][128]")
+        raise ValueError("q must be a contiguous float16 or bfloat16 device tensor [B][Hq][head_dim]")
 
 
 def _need_residual(q: torch.Tensor, k_res: torch.Tensor, v_res: torch.Tensor) -> None:
-    _need_f16(k_res, "k_res", allow_bf16=True)
-    _need_f16(v_res, "v_res", allow_bf16=True)
+    _need_f16(k_res, "k_res", allow_bf16=True, D=q.shape[2])
+    _need_f16(v_res, "v_res", allow_bf16=True, D=q.shape[2])
     if k_res.dtype != q.dtype or v_res.dtype != q.dtype:
         raise TypeError("k_res and v_res must have the dtype of q")
     if k_res.stride(0) != v_res.stride(0):
@@ -272,7 +272,7 @@ def decode_attend(q: torch.Tensor, k_store: Store, v_store: Store, n_quant: int,
     if out is None:
         out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
     if not (out.dtype == torch.float32 and out.is_contiguous() and tuple(out.shape) == (B, Hq, D)):
-        raise ValueError("out must be a contiguous float32 [B][Hq][128] tensor")
+        raise ValueError("out must be a contiguous float32 [B][Hq][head_dim] tensor")
     need = attend_workspace_bytes(B, Hq, Hkv, n_quant, n_res) if B else 0
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
@@ -308,7 +308,7 @@ def decode_attend_varlen(q: torch.Tensor, k_store: Store, v_store: Store, n_quan
     if out is None:
         out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
     if not (out.dtype == torch.float32 and out.is_contiguous() and tuple(out.shape) == (B, Hq, D)):
-        raise ValueError("out must be a contiguous float32 [B][Hq][128] tensor")
+        raise ValueError("out must be a contiguous float32 [B][Hq][head_dim] tensor")
     need = attend_workspace_bytes(B, Hq, Hkv, max_n_quant, max_n_res) if B else 0
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)

@@ -191,8 +191,10 @@ def test_attend_validation():
     assert call(wsb=ws - 4) == -5
     assert call(wsp=None) == -5
     assert call(wsp=FAKE + 16) == -4
-    # the attend reads head_dim 128 only
-    assert call(kk=_store(kivi.KIVI_KEYS, cap=64, D=64), vv=_store(kivi.KIVI_VALUES, cap=64, D=64)) == -3
+    # the attend reads head_dim 128, or 64 with groups of 32; key and value
+    # stores share it
+    assert call(kk=_store(kivi.KIVI_KEYS, cap=64, D=96), vv=_store(kivi.KIVI_VALUES, cap=64, D=96)) == -3
+    assert call(kk=_store(kivi.KIVI_KEYS, cap=64, D=64), vv=_store(kivi.KIVI_VALUES, cap=64, D=128)) == -3
     # key and value stores must share their group size (32, 64 or 128)
     assert call(kk=_store(kivi.KIVI_KEYS, cap=64, G=64), vv=_store(kivi.KIVI_VALUES, cap=64, G=32)) == -3
     assert call(kk=_store(kivi.KIVI_KEYS, cap=64, G=48), vv=_store(kivi.KIVI_VALUES, cap=64, G=48)) == -3
