@@ -168,11 +168,15 @@ int kivi_dequantize_bf16(const kivi_store* src, int64_t BH, int64_t token_begin,
 size_t kivi_decode_attend_workspace_bytes(int64_t B, int32_t Hq, int32_t Hkv,
                                           int64_t n_quant, int64_t n_res) {
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || n_quant < 0 || n_res < 0 || n_quant + n_res == 0) return 0;
-    // the larger of the uniform and the variable-length plans, so one size
-    // serves both calls
-    const size_t u = kivi::plan_attend(B, Hq, Hkv, n_quant, n_res, false).workspace_bytes;
-    const size_t v = kivi::plan_attend(B, Hq, Hkv, n_quant, n_res, true).workspace_bytes;
-    return u > v ? u : v;
+    // the largest of the uniform and variable-length plans, fp16 and
+    // bfloat16, so one size serves every attend call of this shape
+    size_t need = 0;
+    for (int varlen = 0; varlen < 2; ++varlen)
+        for (int bf16 = 0; bf16 < 2; ++bf16) {
+            const size_t b = kivi::plan_attend(B, Hq, Hkv, n_quant, n_res, varlen != 0, 128, bf16 != 0).workspace_bytes;
+            need = b > need ? b : need;
+        }
+    return need;
 }
 
 }  // extern "C"
@@ -217,7 +221,7 @@ int decode_attend_entry(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
         if ((rc = check_f16_tensor(k_res, slabs, rows, res_bh_stride, D)) != KIVI_OK) return rc;
         if ((rc = check_f16_tensor(v_res, slabs, rows, res_bh_stride, D)) != KIVI_OK) return rc;
     }
-    const kivi::AttendPlan plan = kivi::plan_attend(B, Hq, Hkv, n_quant, n_res, seq_n_quant != nullptr, D);
+    const kivi::AttendPlan plan = kivi::plan_attend(B, Hq, Hkv, n_quant, n_res, seq_n_quant != nullptr, D, bf16);
     if (!workspace || workspace_bytes < plan.workspace_bytes) return KIVI_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KIVI_ERR_ALIGN;
     if (plan.n_split > kMaxBlocks || slabs > 65535 || B * Hq > kMaxBlocks) return KIVI_ERR_SHAPE;

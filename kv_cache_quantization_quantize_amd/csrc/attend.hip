@@ -95,18 +95,19 @@ __global__ __launch_bounds__(64 * WAVES) void attend_combine_kernel(const float*
 // most kMaxStepsPerWave steps, with the steps spread evenly, so the last
 // round is not a short tail.
 AttendPlan plan_attend(int64_t B, int Hq, int Hkv, int64_t n_quant, int64_t n_res, bool varlen,
-                       int head_dim) {
+                       int head_dim, bool bf16) {
     const int64_t pairs = B * Hkv;
     const int64_t steps_q = (n_quant + kStep - 1) / kStep;
     const int64_t steps = steps_q + (n_res + kStep - 1) / kStep;
     const int64_t total = pairs * steps;
+    const int64_t slots = bf16 ? kWaveSlotsBF16 : kWaveSlots;
     int64_t spw = 1;
-    if (total > kWaveSlots) {
+    if (total > slots) {
         // A variable-length batch sizes the grid for its longest sequence;
         // the shorter ones leave waves with little or nothing to do, so it
         // gets four times finer splits and the hardware refills the freed
         // slots with the remaining work.
-        const int64_t per_round = varlen ? kWaveSlots * 4 : kWaveSlots;
+        const int64_t per_round = varlen ? slots * 4 : slots;
         const int64_t rounds = (total + per_round * kMaxStepsPerWave - 1) / (per_round * kMaxStepsPerWave);
         spw = (total + rounds * per_round - 1) / (rounds * per_round);
     }

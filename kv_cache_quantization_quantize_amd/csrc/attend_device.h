@@ -70,6 +70,7 @@ __device__ __forceinline__ float4_t mfma(const Frag& a, const Frag& b, float4_t 
 #endif
 #define KIVI_ATTEND_OCCUPANCY __attribute__((amdgpu_waves_per_eu(KIVI_ATTEND_WAVES_PER_SIMD)))
 constexpr int64_t kWaveSlots = 256 * 4 * KIVI_ATTEND_WAVES_PER_SIMD;
+constexpr int64_t kWaveSlotsBF16 = 256 * 4 * 2;       // the bfloat16 instances, 2 per SIMD
 constexpr int kNBuf = KIVI_ATTEND_NBUF;
 
 constexpr int kStep = 32;             // tokens per wave step (one key group)
@@ -574,8 +575,10 @@ __device__ __forceinline__ void residual_step(const uint16_t* kr, const uint16_t
 // that axis, so one wave may finish the store and start the residual.
 // Offsets within a slab fit in 32 bits: the ABI keeps n_quant and n_res
 // below 2^24 tokens.
+// bfloat16 instances run at 2 waves per SIMD: their dequantization needs
+// about 190 VGPRs, and at 3 waves (168) they spilled to scratch.
 template <int BITS, int GQA, int G, int MB, bool BF, int D>
-__global__ __launch_bounds__(64) KIVI_ATTEND_OCCUPANCY void attend_partial_kernel(const AttendArgs a, int spw, int steps_q,
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(BF ? 2 : KIVI_ATTEND_WAVES_PER_SIMD))) void attend_partial_kernel(const AttendArgs a, int spw, int steps_q,
                                                             int64_t n_split, float* __restrict__ ws_o,
                                                             float* __restrict__ ws_ml)
 {

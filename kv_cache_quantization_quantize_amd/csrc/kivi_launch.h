@@ -90,7 +90,7 @@ struct AttendPlan {
     size_t workspace_bytes;
 };
 AttendPlan plan_attend(int64_t B, int Hq, int Hkv, int64_t n_quant, int64_t n_res, bool varlen,
-                       int head_dim = 128);
+                       int head_dim = 128, bool bf16 = false);
 
 hipError_t launch_key_flush(const FlushArgs& a, hipStream_t stream);
 hipError_t launch_value_flush(const FlushArgs& a, hipStream_t stream);
