@@ -81,7 +81,7 @@ typedef struct kivi_cache {
     kivi_cache_config cfg;
     kivi_store k_store;       /* all layers' slabs (BH = layers*batch*kv_heads) */
     kivi_store v_store;
-    uint16_t* k_ring;         /* fp16 [slabs][ring][head_dim]                  */
+    uint16_t* k_ring;         /* 16-bit [slabs][ring][head_dim]                */
     uint16_t* v_ring;
     int64_t ring;             /* R + F rows per slab                           */
     int64_t length;           /* tokens per sequence so far                    */
@@ -101,7 +101,7 @@ size_t kivi_cache_device_bytes(const kivi_cache_config* cfg);
 int kivi_cache_init(kivi_cache* cache, const kivi_cache_config* cfg, void* device, size_t bytes);
 
 /* Prompt of S tokens for every layer and sequence at once, into an empty
- * cache.  k, v: fp16 [layers*batch*kv_heads][S][head_dim] with slab stride
+ * cache.  k, v: 16-bit (the cache's format) [layers*batch*kv_heads][S][head_dim] with slab stride
  * x_bh_stride (slab order as in the device layout).  The oldest Q(S) tokens
  * are flushed into the stores (one launch per tensor over all layers), the
  * other S - Q(S) are copied into the rings (one launch).  Q(S) must fit the
@@ -110,13 +110,13 @@ int kivi_cache_prefill(kivi_cache* cache, const uint16_t* k, const uint16_t* v,
                        int64_t x_bh_stride, int64_t S, hipStream_t stream);
 
 /* Step: append this step's token of every sequence to layer `layer`.
- * k_new, v_new: fp16 [batch*kv_heads][head_dim], contiguous.  Once per layer
+ * k_new, v_new: 16-bit [batch*kv_heads][head_dim], contiguous.  Once per layer
  * per step, before that layer's kivi_cache_attend. */
 int kivi_cache_append(kivi_cache* cache, int32_t layer, const uint16_t* k_new,
                       const uint16_t* v_new, hipStream_t stream);
 
 /* Step: decode attention of layer `layer` after its append: one query token
- * per sequence (q fp16 [batch][Hq][head_dim]) over the layer's quantized
+ * per sequence (q 16-bit [batch][Hq][head_dim]) over the layer's quantized
  * tokens and its fp16 tokens including this step's, as kivi_decode_attend
  * (out fp32 [batch][Hq][head_dim]; workspace of at least
  * kivi_cache_attend_workspace_bytes(cache, Hq) bytes). */

@@ -17,7 +17,7 @@
 
 namespace kivi {
 
-constexpr int kHeadDim = 128;      // the attend's and the cache's head_dim
+constexpr int kHeadDim = 128;      // the decode-loop cache's head_dim (rows it copies)
 constexpr int kGroup = 32;         // the cache's group size; the attend's smallest
 constexpr int kWavesPerBlock = 4;
 constexpr int kBlock = 64 * kWavesPerBlock;
