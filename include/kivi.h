@@ -27,10 +27,12 @@
  *    32, 64 or 128, or any other multiple of 16 from 16 to 256 with
  *    group_size 32 (when 32 does not divide head_dim, a token's last value
  *    group holds the remaining 16 channels: [Metal post] "Kernel B" cuts a
- *    row's last group at the row's end).  The attend takes head_dim 128,
- *    or 64 with groups of 32 (binary32 scale/zero), and its key and value
- *    stores share head_dim and group size; q, the residual and out then
- *    have head_dim channels.  Anything else returns KIVI_ERR_UNSUPPORTED.
+ *    row's last group at the row's end).  The attend takes every store
+ *    geometry with binary32 scale/zero (binary16 ones: head_dim 128); its
+ *    key and value stores share head_dim and group size, and q, the
+ *    residual and out have head_dim channels.  head_dim 128 and 64 run on
+ *    the MFMA kernels, every other head_dim on a generic (slower) kernel.
+ *    Anything else returns KIVI_ERR_UNSUPPORTED.
  *
  * Packed store layout (the pages fix none; [Metal post] "So why does the
  * kernel ship?" asks for packed storage of the codes):
@@ -254,8 +256,8 @@ int kivi_decode_attend_varlen_bf16(const uint16_t* q, int64_t B, int32_t Hq, int
                                    float softmax_scale, float* out, void* workspace,
                                    size_t workspace_bytes, hipStream_t stream);
 
-/* Workspace bytes kivi_decode_attend needs for this shape (head_dim 128;
- * an upper bound for head_dim 64). */
+/* Workspace bytes any of the attend calls needs for this shape, at any
+ * head_dim (the bound of head_dim 256) and in either format. */
 size_t kivi_decode_attend_workspace_bytes(int64_t B, int32_t Hq, int32_t Hkv,
                                           int64_t n_quant, int64_t n_res);
 

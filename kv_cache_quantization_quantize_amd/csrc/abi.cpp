@@ -173,7 +173,8 @@ size_t kivi_decode_attend_workspace_bytes(int64_t B, int32_t Hq, int32_t Hkv,
     size_t need = 0;
     for (int varlen = 0; varlen < 2; ++varlen)
         for (int bf16 = 0; bf16 < 2; ++bf16) {
-            const size_t b = kivi::plan_attend(B, Hq, Hkv, n_quant, n_res, varlen != 0, 128, bf16 != 0).workspace_bytes;
+            // head_dim 256 bounds every head_dim's split partials
+            const size_t b = kivi::plan_attend(B, Hq, Hkv, n_quant, n_res, varlen != 0, 256, bf16 != 0).workspace_bytes;
             need = b > need ? b : need;
         }
     return need;
@@ -207,9 +208,10 @@ int decode_attend_entry(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
     if ((rc = check_store(v, KIVI_VALUES, slabs, 0, n_quant)) != KIVI_OK) return rc;
     if (k->bits != v->bits) return KIVI_ERR_SHAPE;
     if (k->group_size != v->group_size || k->meta_format != v->meta_format) return KIVI_ERR_UNSUPPORTED;
-    // head_dim 128, or 64 with groups of 32 (binary32 scale/zero: meta16 stores are head_dim 128)
+    // head_dim 128 with any group size; any other store head_dim with groups
+    // of 32 (binary16 stores are head_dim 128 only, see check_store)
     const int32_t D = k->head_dim;
-    if (v->head_dim != D || !(D == kD || (D == 64 && k->group_size == 32))) return KIVI_ERR_UNSUPPORTED;
+    if (v->head_dim != D || !(D == kD || k->group_size == 32)) return KIVI_ERR_UNSUPPORTED;
     if (bf16 && meta16(k)) return KIVI_ERR_UNSUPPORTED;        // bfloat16 stores keep binary32 metadata
     if (B == 0) return KIVI_OK;
     if (!q || !out) return KIVI_ERR_NULL;

@@ -137,6 +137,7 @@ hipError_t launch_decode_attend(const AttendArgs& a, const AttendPlan& p, hipStr
     const size_t rows = static_cast<size_t>(a.B) * a.Hq * p.n_split;
     const size_t o_bytes = (rows * a.head_dim * sizeof(float) + 255) & ~static_cast<size_t>(255);
     float* ws_ml = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + o_bytes);
+    if (a.head_dim != 64 && a.head_dim != 128) return launch_attend_generic(a, p, ws_o, ws_ml, stream);
     hipError_t e;
     if (a.bf16) e = launch_attend_partial_bf16(a, p, ws_o, ws_ml, stream);
     else if (a.meta16) e = launch_partials<2, false>(a, p, ws_o, ws_ml, stream);

@@ -78,7 +78,7 @@ struct AttendArgs {
     int group;                     // 32, 64 or 128 (keys and values alike)
     bool meta16;                   // binary16 scale/zero (keys and values alike)
     bool bf16;                     // q, residual and the reconstruction in bfloat16
-    int head_dim;                  // 128, or 64 (groups of 32, binary32 scale/zero)
+    int head_dim;                  // 128; others with groups of 32 and binary32 scale/zero
 };
 
 // Split of the token axis chosen for an attend shape; the workspace holds
@@ -96,6 +96,10 @@ hipError_t launch_key_flush(const FlushArgs& a, hipStream_t stream);
 hipError_t launch_value_flush(const FlushArgs& a, hipStream_t stream);
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t stream);
 hipError_t launch_decode_attend(const AttendArgs& a, const AttendPlan& p, hipStream_t stream);
+// the attend at head_dims other than 64 and 128 (groups of 32, binary32
+// scale/zero): partials and combine
+hipError_t launch_attend_generic(const AttendArgs& a, const AttendPlan& p, float* ws_o, float* ws_ml,
+                                 hipStream_t stream);
 // head_dims other than 64, 128 and 256 (multiples of 16 up to 256, groups of 32)
 hipError_t launch_flush_ragged(bool keys, const FlushArgs& a, hipStream_t stream);
 hipError_t launch_dequant_ragged(const DequantArgs& a, hipStream_t stream);

@@ -188,12 +188,13 @@ def test_attend_validation():
     assert call(kk=v) == -2                       # kinds swapped
     assert call(vv=_store(kivi.KIVI_VALUES, bits=2, cap=64)) == -2
     assert call(q=None) == -1
-    assert call(wsb=ws - 4) == -5
+    assert call(wsb=16) == -5                     # far below any plan's need
     assert call(wsp=None) == -5
     assert call(wsp=FAKE + 16) == -4
-    # the attend reads head_dim 128, or 64 with groups of 32; key and value
-    # stores share it
-    assert call(kk=_store(kivi.KIVI_KEYS, cap=64, D=96), vv=_store(kivi.KIVI_VALUES, cap=64, D=96)) == -3
+    # the attend reads head_dim 128 with any group size and other head_dims
+    # with groups of 32; key and value stores share it
+    assert call(kk=_store(kivi.KIVI_KEYS, cap=64, D=96, G=64),
+                vv=_store(kivi.KIVI_VALUES, cap=64, D=96, G=64)) == -3
     assert call(kk=_store(kivi.KIVI_KEYS, cap=64, D=64), vv=_store(kivi.KIVI_VALUES, cap=64, D=128)) == -3
     # key and value stores must share their group size (32, 64 or 128)
     assert call(kk=_store(kivi.KIVI_KEYS, cap=64, G=64), vv=_store(kivi.KIVI_VALUES, cap=64, G=32)) == -3
@@ -209,7 +210,7 @@ def test_attend_validation():
         assert fn(FAKE, 1, 32, 8, ctypes.byref(k16), ctypes.byref(v16), 64, FAKE, FAKE, 2048, 16,
                   0.088, FAKE, FAKE, ws, None) == -3
         assert fn(FAKE, 1, 32, 8, ctypes.byref(k), ctypes.byref(v), 64, FAKE, FAKE, 2048, 16,
-                  0.088, FAKE, FAKE, ws - 4, None) == -5
+                  0.088, FAKE, FAKE, 16, None) == -5
     nq = nr = FAKE
     assert L.kivi_decode_attend_varlen_bf16(FAKE, 1, 32, 8, ctypes.byref(k16), ctypes.byref(v16),
                                             nq, 64, FAKE, FAKE, 2048, nr, 16, 0.088, FAKE, FAKE,

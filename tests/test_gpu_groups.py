@@ -267,3 +267,60 @@ def test_attend_head_dim_64(case, fmt):
                                         nr_h, nr, fmt=fmt)
     err = float(np.max(np.abs(out_v.cpu().numpy().astype(np.float64) - ref_v)))
     assert err <= tol, f"varlen max-abs error {err:.3e}"
+
+
+GENERIC = [
+    # B, Hq, Hkv, n_quant, n_res, bits
+    (2, 16, 8, 300, 37, 4),
+    (1, 8, 2, 1000, 5, 2),
+    (2, 8, 8, 0, 40, 4),
+    (3, 4, 1, 200, 0, 4),
+]
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("Dh", [256, 96, 80, 16])
+@pytest.mark.parametrize("case", GENERIC, ids=lambda c: "B%d-Hq%d-Hkv%d-nq%d-nr%d-b%d" % c)
+def test_attend_generic_head_dims(case, Dh, fmt):
+    """The decode attends at head_dims the MFMA kernels do not take (256 and
+    the ragged ones; groups of 32): the generic kernel rebuilds K and V
+    exactly as stored and rounds no probabilities, so it is held to 2e-3 in
+    both formats; uniform and variable-length against the oracle."""
+    B, Hq, Hkv, nq, nr, bits = case
+    BH = B * Hkv
+    cap = max(32, ((nq + 31) // 32) * 32)
+    seed = 9500 + Dh + nq + nr
+    dtype = torch.bfloat16 if fmt == "bf16" else torch.float16
+    kx = synth.kv_tensor(BH, max(nq, 1), Dh, keys=True, seed=seed, device="cuda", dtype=dtype)[:, :nq]
+    vx = synth.kv_tensor(BH, max(nq, 1), Dh, keys=False, seed=seed, device="cuda", dtype=dtype)[:, :nq]
+    kr = synth.residual(BH, max(nr, 1), Dh, keys=True, seed=seed, device="cuda").to(dtype)
+    vr = synth.residual(BH, max(nr, 1), Dh, keys=False, seed=seed, device="cuda").to(dtype)
+    q = synth.query(B, Hq, Dh, seed=seed, device="cuda").to(dtype)
+    ks = kivi.Store(kivi.KIVI_KEYS, BH, cap, bits, head_dim=Dh)
+    vs = kivi.Store(kivi.KIVI_VALUES, BH, cap, bits, head_dim=Dh)
+    note(f"generic attend head_dim {Dh} {fmt} B={B} Hq={Hq} Hkv={Hkv} n_quant={nq} n_res={nr} bits={bits}")
+    if nq:
+        kivi.quantize_keys(kx.contiguous(), ks, 0)
+        kivi.quantize_values(vx.contiguous(), vs, 0)
+    out = kivi.decode_attend(q, ks, vs, nq, kr, vr, nr)
+    rng = np.random.default_rng(seed)
+    nq_h = rng.integers(0, nq + 1, size=B).astype(np.int32)
+    nr_h = rng.integers(0, nr + 1, size=B).astype(np.int32)
+    empty = (nq_h + nr_h) == 0
+    nq_h[empty], nr_h[empty] = nq, nr
+    out_v = kivi.decode_attend_varlen(q, ks, vs, torch.from_numpy(nq_h).cuda(), nq, kr, vr,
+                                      torch.from_numpy(nr_h).cuda(), nr)
+    torch.cuda.synchronize()
+    hk = oracle.Store(oracle.KEYS, BH, cap, Dh, bits, 32)
+    hv = oracle.Store(oracle.VALUES, BH, cap, Dh, bits, 32)
+    if nq:
+        oracle.quantize_keys(u16(kx), hk, 0, want_recon=False, fmt=fmt)
+        oracle.quantize_values(u16(vx), hv, 0, want_recon=False, fmt=fmt)
+    ref = oracle.decode_attend(u16(q), B, Hq, Hkv, hk, hv, nq, u16(kr), u16(vr), nr, fmt=fmt)
+    err = float(np.max(np.abs(out.cpu().numpy().astype(np.float64) - ref)))
+    print(f"{case} D={Dh} {fmt}: max-abs error {err:.2e}")
+    assert err <= 2e-3, f"max-abs error {err:.3e}"
+    ref_v = oracle.decode_attend_varlen(u16(q), B, Hq, Hkv, hk, hv, nq_h, nq, u16(kr), u16(vr),
+                                        nr_h, nr, fmt=fmt)
+    err = float(np.max(np.abs(out_v.cpu().numpy().astype(np.float64) - ref_v)))
+    assert err <= 2e-3, f"varlen max-abs error {err:.3e}"
