@@ -61,17 +61,18 @@ __device__ __forceinline__ int ring_at(int tok, int head, int ring) {
 
 }  // namespace
 
-template <bool BF>
+// GQA (query heads per kv head) is a template parameter so that the
+// per-head accumulators stay in registers under unrolled loops.
+template <bool BF, int GQA>
 __global__ __launch_bounds__(64) void attend_generic_kernel(const AttendArgs a, int spw, int steps_q,
                                                             int64_t n_split, float* __restrict__ ws_o,
                                                             float* __restrict__ ws_ml)
 {
     constexpr int kG = 32;
-    __shared__ float q_s[kMaxGQA][kMaxD];
-    __shared__ float p_s[kMaxGQA][64];
+    __shared__ float q_s[GQA][kMaxD];
+    __shared__ float p_s[GQA][64];
     const int l = threadIdx.x;
     const int D = a.head_dim;
-    const int GQA = a.Hq / a.Hkv;
     const int bits = a.bits;
     const uint32_t mask = (1u << bits) - 1u;
     const int per_word = 32 / bits;
@@ -108,9 +109,9 @@ __global__ __launch_bounds__(64) void attend_generic_kernel(const AttendArgs a, 
     const uint16_t* vr = a.v_res + bkv * a.res_bh_stride;
     const float c2 = a.softmax_scale * kLog2eG;
 
-    float m[kMaxGQA], lsum[kMaxGQA], o[kMaxGQA][kMaxD / 64];
+    float m[GQA], lsum[GQA], o[GQA][kMaxD / 64];
 #pragma unroll
-    for (int h = 0; h < kMaxGQA; ++h) {
+    for (int h = 0; h < GQA; ++h) {
         m[h] = -INFINITY;
         lsum[h] = 0.0f;
 #pragma unroll
@@ -125,30 +126,36 @@ __global__ __launch_bounds__(64) void attend_generic_kernel(const AttendArgs a, 
             // ---- scores: lane = token
             const int t = t0 + l;
             const bool live = t < hi;
-            float s[kMaxGQA];
+            float s[GQA];
 #pragma unroll
-            for (int h = 0; h < kMaxGQA; ++h) s[h] = 0.0f;
+            for (int h = 0; h < GQA; ++h) s[h] = 0.0f;
             if (live) {
                 if (store) {
                     const float* sp = ksc + static_cast<int64_t>(t / kG) * D;
                     const float* zp = kze + static_cast<int64_t>(t / kG) * D;
+#pragma unroll 4
                     for (int w = 0; w < W; ++w) {
                         const uint32_t word = kc[static_cast<int64_t>(t) * W + w];
+#pragma unroll 8
                         for (int j = 0; j < per_word; ++j) {
                             const int c = w * per_word + j;
                             const float kv_ = recon_value<BF>((word >> (bits * j)) & mask, sp[c], zp[c]);
+#pragma unroll
                             for (int h = 0; h < GQA; ++h) s[h] = __builtin_fmaf(q_s[h][c], kv_, s[h]);
                         }
                     }
                 } else {
                     const uint16_t* row = kr + static_cast<int64_t>(ring_at(t, a.res_head, a.res_ring)) * D;
+#pragma unroll 8
                     for (int c = 0; c < D; ++c) {
                         const float kv_ = widen16<BF>(row[c]);
+#pragma unroll
                         for (int h = 0; h < GQA; ++h) s[h] = __builtin_fmaf(q_s[h][c], kv_, s[h]);
                     }
                 }
             }
             // ---- online softmax across the wave (the chunk has >= 1 live token)
+#pragma unroll
             for (int h = 0; h < GQA; ++h) {
                 const float sc = live ? s[h] * c2 : -INFINITY;
                 const float m_new = fmaxf(m[h], wave_max(sc));
@@ -167,7 +174,8 @@ __global__ __launch_bounds__(64) void attend_generic_kernel(const AttendArgs a, 
             for (int k = 0; k < kMaxD / 64; ++k) {
                 const int c = l + 64 * k;
                 if (c >= D) continue;
-                for (int i = 0; i < n; ++i) {
+#pragma unroll 8
+                for (int i = 0; i < n; ++i) {              // unrolled: several loads in flight
                     const int tt = t0 + i;
                     float v;
                     if (store) {
@@ -177,6 +185,7 @@ __global__ __launch_bounds__(64) void attend_generic_kernel(const AttendArgs a, 
                     } else {
                         v = widen16<BF>(vr[static_cast<int64_t>(ring_at(tt, a.res_head, a.res_ring)) * D + c]);
                     }
+#pragma unroll
                     for (int h = 0; h < GQA; ++h) o[h][k] = __builtin_fmaf(p_s[h][i], v, o[h][k]);
                 }
             }
@@ -184,6 +193,7 @@ __global__ __launch_bounds__(64) void attend_generic_kernel(const AttendArgs a, 
         }
     }
 
+#pragma unroll
     for (int h = 0; h < GQA; ++h) {
         float* dst = ws_o + ((qrow0 + h) * n_split + split) * D;
 #pragma unroll
@@ -261,12 +271,19 @@ __global__ __launch_bounds__(64 * WAVES) void attend_combine_any_kernel(const fl
 hipError_t launch_attend_generic(const AttendArgs& a, const AttendPlan& p, float* ws_o, float* ws_ml,
                                  hipStream_t stream) {
     const dim3 grid(static_cast<uint32_t>(p.n_split), static_cast<uint32_t>(a.B * a.Hkv));
-    if (a.bf16)
-        hipLaunchKernelGGL(attend_generic_kernel<true>, grid, dim3(64), 0, stream, a,
-                           static_cast<int>(p.steps_per_wave), static_cast<int>(p.steps_q), p.n_split, ws_o, ws_ml);
-    else
-        hipLaunchKernelGGL(attend_generic_kernel<false>, grid, dim3(64), 0, stream, a,
-                           static_cast<int>(p.steps_per_wave), static_cast<int>(p.steps_q), p.n_split, ws_o, ws_ml);
+    const int spw = static_cast<int>(p.steps_per_wave), sq = static_cast<int>(p.steps_q);
+#define KIVI_GENERIC(BFV, G) hipLaunchKernelGGL((attend_generic_kernel<BFV, G>), grid, dim3(64), 0, stream, a, spw, sq, p.n_split, ws_o, ws_ml)
+    switch ((a.Hq / a.Hkv) * 2 + (a.bf16 ? 1 : 0)) {
+        case 2: KIVI_GENERIC(false, 1); break;
+        case 3: KIVI_GENERIC(true, 1); break;
+        case 4: KIVI_GENERIC(false, 2); break;
+        case 5: KIVI_GENERIC(true, 2); break;
+        case 8: KIVI_GENERIC(false, 4); break;
+        case 9: KIVI_GENERIC(true, 4); break;
+        case 16: KIVI_GENERIC(false, 8); break;
+        default: KIVI_GENERIC(true, 8); break;          // 17: the ABI admits only 1, 2, 4 and 8
+    }
+#undef KIVI_GENERIC
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 rows(static_cast<uint32_t>(a.B * a.Hq));
