@@ -12,7 +12,6 @@
 namespace {
 
 constexpr int64_t kD = 128;
-constexpr int64_t kG = 32;
 constexpr int64_t kMaxTokens = int64_t{1} << 24;      // the attend's 32-bit offsets
 constexpr int64_t kMaxSlabs = int64_t{1} << 31;
 
@@ -27,8 +26,10 @@ bool valid(const kivi_cache_config* c) {
     if (!c) return false;
     if (c->layers < 1 || c->layers > KIVI_CACHE_MAX_LAYERS || c->batch < 1 || c->kv_heads < 1) return false;
     if (c->bits != 2 && c->bits != 4) return false;
-    if (c->head_dim != kD || c->group_size != kG) return false;
-    if (c->flush_tokens <= 0 || c->flush_tokens % kG != 0) return false;
+    // head_dim 128 with groups of 32, 64 or 128 (binary16 scale/zero included)
+    if (c->head_dim != kD) return false;
+    if (c->group_size != 32 && c->group_size != 64 && c->group_size != 128) return false;
+    if (c->flush_tokens <= 0 || c->flush_tokens % c->group_size != 0) return false;
     if (c->residual_length < 0 || c->residual_length % c->flush_tokens != 0) return false;
     if (c->store_capacity < 0 || c->store_capacity % c->flush_tokens != 0) return false;
     if (c->meta_format != KIVI_META_F32 && c->meta_format != KIVI_META_F16) return false;
@@ -50,11 +51,12 @@ Layout layout(const kivi_cache_config& c) {
     int64_t off = 0;
     auto take = [&off](int64_t bytes) { const int64_t at = off; off = align256(off + bytes); return at; };
     L.kc = take(L.slabs * cap * L.words * 4);
-    L.ks = take(L.slabs * (cap / kG) * kD * mb);
-    L.kz = take(L.slabs * (cap / kG) * kD * mb);
+    const int64_t G = c.group_size;
+    L.ks = take(L.slabs * (cap / G) * kD * mb);
+    L.kz = take(L.slabs * (cap / G) * kD * mb);
     L.vc = take(L.slabs * cap * L.words * 4);
-    L.vs = take(L.slabs * cap * (kD / kG) * mb);
-    L.vz = take(L.slabs * cap * (kD / kG) * mb);
+    L.vs = take(L.slabs * cap * (kD / G) * mb);
+    L.vz = take(L.slabs * cap * (kD / G) * mb);
     L.kr = take(L.slabs * L.ring * kD * 2);
     L.vr = take(L.slabs * L.ring * kD * 2);
     L.total = off;
@@ -118,10 +120,10 @@ int kivi_cache_init(kivi_cache* cache, const kivi_cache_config* cfg, void* devic
     c.cfg = *cfg;
     const int64_t cap = cfg->store_capacity;
     c.k_store = {reinterpret_cast<uint32_t*>(base + L.kc), base + L.ks, base + L.kz,
-                 cap * L.words, (cap / kG) * kD, cap,
+                 cap * L.words, (cap / cfg->group_size) * kD, cap,
                  cfg->bits, cfg->group_size, cfg->head_dim, KIVI_KEYS, cfg->meta_format};
     c.v_store = {reinterpret_cast<uint32_t*>(base + L.vc), base + L.vs, base + L.vz,
-                 cap * L.words, cap * (kD / kG), cap,
+                 cap * L.words, cap * (kD / cfg->group_size), cap,
                  cfg->bits, cfg->group_size, cfg->head_dim, KIVI_VALUES, cfg->meta_format};
     c.k_ring = reinterpret_cast<uint16_t*>(base + L.kr);
     c.v_ring = reinterpret_cast<uint16_t*>(base + L.vr);

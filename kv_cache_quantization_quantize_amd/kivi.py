@@ -341,13 +341,14 @@ class Cache:
 
     def __init__(self, layers: int, batch: int, kv_heads: int, store_capacity: int, bits: int = 4,
                  residual_length: int = 128, flush_tokens: int = GROUP, device="cuda",
-                 meta: str = "f32", dtype=torch.float16):
+                 meta: str = "f32", dtype=torch.float16, group: int = GROUP):
         if meta not in ("f32", "f16"):
             raise ValueError("meta must be 'f32' or 'f16'")
         if dtype not in (torch.float16, torch.bfloat16):
             raise ValueError("dtype must be torch.float16 or torch.bfloat16")
         self.meta, self.dtype = meta, dtype
-        self.cfg = CCacheConfig(layers, batch, kv_heads, bits, HEAD_DIM, GROUP, residual_length,
+        self.group = group
+        self.cfg = CCacheConfig(layers, batch, kv_heads, bits, HEAD_DIM, group, residual_length,
                                 flush_tokens, store_capacity,
                                 KIVI_META_F16 if meta == "f16" else KIVI_META_F32,
                                 1 if dtype == torch.bfloat16 else 0)
@@ -382,10 +383,11 @@ class Cache:
         out = []
         for cs, kind in ((self.c.k_store, KIVI_KEYS), (self.c.v_store, KIVI_VALUES)):
             cap, words = cs.cap, HEAD_DIM * cs.bits // 32
-            meta = (self.slabs, cap // GROUP, HEAD_DIM) if kind == KIVI_KEYS else \
-                (self.slabs, cap, HEAD_DIM // GROUP)
+            G = self.group
+            meta = (self.slabs, cap // G, HEAD_DIM) if kind == KIVI_KEYS else \
+                (self.slabs, cap, HEAD_DIM // G)
             mdt = torch.float16 if self.meta == "f16" else torch.float32
-            out.append(Store(kind, self.slabs, cap, cs.bits,
+            out.append(Store(kind, self.slabs, cap, cs.bits, group=G,
                              codes=self._view(cs.codes, torch.int32, (self.slabs, cap, words)),
                              scale=self._view(cs.scale, mdt, meta),
                              zero=self._view(cs.zero, mdt, meta), meta=self.meta))

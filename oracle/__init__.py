@@ -373,12 +373,13 @@ class CacheModel:
     order.  Slab s = (layer * batch + b) * kv_heads + h."""
 
     def __init__(self, layers: int, batch: int, kv_heads: int, capacity: int, bits: int = 4,
-                 R: int = 128, F: int = 32, D: int = 128, meta: str = "f32", fmt: str = "f16"):
+                 R: int = 128, F: int = 32, D: int = 128, meta: str = "f32", fmt: str = "f16",
+                 G: int = 32):
         self.layers, self.batch, self.kv_heads, self.R, self.F, self.D = layers, batch, kv_heads, R, F, D
         self.fmt = fmt
         self.slabs = layers * batch * kv_heads
-        self.kstore = Store(KEYS, self.slabs, capacity, D, bits, meta=meta)
-        self.vstore = Store(VALUES, self.slabs, capacity, D, bits, meta=meta)
+        self.kstore = Store(KEYS, self.slabs, capacity, D, bits, G, meta=meta)
+        self.vstore = Store(VALUES, self.slabs, capacity, D, bits, G, meta=meta)
         self.k = np.zeros((self.slabs, 0, D), np.uint16)
         self.v = np.zeros((self.slabs, 0, D), np.uint16)
         self.n_quant = 0

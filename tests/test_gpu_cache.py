@@ -46,6 +46,20 @@ def test_decode_loop_matches_model(case):
     """The last field is the scale/zero format ("f32", "f16") or "bf16" for a
     bfloat16 cache (binary32 scale/zero; tolerance as for the bfloat16
     attend: 2e-3 + 2^-8 max|v|)."""
+    _decode_loop(case, 32)
+
+
+@pytest.mark.parametrize("G,case", [
+    (64, (2, 2, 2, 8, 4, 128, 64, 512, 150, 140, "f32")),
+    (128, (1, 2, 8, 32, 4, 128, 128, 512, 200, 200, "f16")),
+    (64, (2, 1, 2, 8, 2, 64, 64, 256, 70, 90, "bf16")),
+], ids=["G64", "G128-meta16", "G64-bf16"])
+def test_decode_loop_group_sizes(G, case):
+    """Caches with groups of 64 and 128 (flush units multiples of the group)."""
+    _decode_loop(case, G)
+
+
+def _decode_loop(case, G):
     layers, batch, kvh, Hq, bits, R, F, cap, S0, steps, variant = case
     bf16 = variant == "bf16"
     meta = "f32" if bf16 else variant
@@ -56,8 +70,8 @@ def test_decode_loop_matches_model(case):
     per = batch * kvh
     note(f"cache loop layers={layers} batch={batch} kv_heads={kvh} Hq={Hq} bits={bits} R={R} F={F} "
          f"capacity={cap} prompt={S0} steps={steps} meta={meta}")
-    c = kivi.Cache(layers, batch, kvh, cap, bits, R, F, meta=meta, dtype=dtype)
-    m = oracle.CacheModel(layers, batch, kvh, cap, bits, R, F, meta=meta, fmt=fmt)
+    c = kivi.Cache(layers, batch, kvh, cap, bits, R, F, meta=meta, dtype=dtype, group=G)
+    m = oracle.CacheModel(layers, batch, kvh, cap, bits, R, F, meta=meta, fmt=fmt, G=G)
     vmax = 0.0
     if S0:
         k0 = synth.kv_tensor(slabs, S0, keys=True, seed=seed, device="cuda", dtype=dtype)
@@ -94,7 +108,7 @@ def test_decode_loop_matches_model(case):
     Q = c.n_quant
     ks, vs = c.stores()
     torch.cuda.synchronize()
-    g = Q // 32
+    g = Q // G
     assert np.array_equal(ks.codes[:, :Q].cpu().numpy().view(np.uint32), m.kstore.codes[:, :Q])
     assert np.array_equal(vs.codes[:, :Q].cpu().numpy().view(np.uint32), m.vstore.codes[:, :Q])
     assert _meta_equal(ks.scale[:, :g], m.kstore.scale[:, :g])
