@@ -62,8 +62,8 @@ typedef struct kivi_cache_config {
     int32_t batch;            /* sequences B >= 1                              */
     int32_t kv_heads;         /* Hkv >= 1                                      */
     int32_t bits;             /* 2 or 4                                        */
-    int32_t head_dim;         /* 128                                           */
-    int32_t group_size;       /* 32, 64 or 128                                 */
+    int32_t head_dim;         /* 128, or a multiple of 16 from 16 to 256       */
+    int32_t group_size;       /* 32, 64 or 128 at head_dim 128; else 32        */
     int32_t residual_length;  /* R >= 0, a multiple of flush_tokens            */
     int32_t flush_tokens;     /* F > 0, a multiple of group_size               */
     int64_t store_capacity;   /* quantized tokens per sequence, a multiple of F */

@@ -26,7 +26,6 @@ namespace kivi {
 namespace {
 
 constexpr int kMaxD = 256;
-constexpr int kMaxGQA = 8;
 constexpr float kLog2eG = 1.4426950408889634f;
 
 __device__ __forceinline__ float wave_max(float v) {

@@ -11,7 +11,6 @@
 
 namespace {
 
-constexpr int64_t kD = 128;
 constexpr int64_t kMaxTokens = int64_t{1} << 24;      // the attend's 32-bit offsets
 constexpr int64_t kMaxSlabs = int64_t{1} << 31;
 
@@ -26,9 +25,15 @@ bool valid(const kivi_cache_config* c) {
     if (!c) return false;
     if (c->layers < 1 || c->layers > KIVI_CACHE_MAX_LAYERS || c->batch < 1 || c->kv_heads < 1) return false;
     if (c->bits != 2 && c->bits != 4) return false;
-    // head_dim 128 with groups of 32, 64 or 128 (binary16 scale/zero included)
-    if (c->head_dim != kD) return false;
-    if (c->group_size != 32 && c->group_size != 64 && c->group_size != 128) return false;
+    // the store geometries: head_dim 128 with groups of 32, 64 or 128 (binary16
+    // scale/zero included); any other multiple of 16 up to 256 with groups of
+    // 32 and binary32 scale/zero
+    const int32_t D = c->head_dim, G = c->group_size;
+    if (D == 128) {
+        if (G != 32 && G != 64 && G != 128) return false;
+    } else if (D < 16 || D > 256 || D % 16 != 0 || G != 32 || c->meta_format != KIVI_META_F32) {
+        return false;
+    }
     if (c->flush_tokens <= 0 || c->flush_tokens % c->group_size != 0) return false;
     if (c->residual_length < 0 || c->residual_length % c->flush_tokens != 0) return false;
     if (c->store_capacity < 0 || c->store_capacity % c->flush_tokens != 0) return false;
@@ -45,6 +50,7 @@ Layout layout(const kivi_cache_config& c) {
     Layout L;
     L.slabs = int64_t{c.layers} * c.batch * c.kv_heads;
     L.ring = int64_t{c.residual_length} + c.flush_tokens;
+    const int64_t kD = c.head_dim;
     L.words = kD * c.bits / 32;
     const int64_t cap = c.store_capacity;
     const int64_t mb = c.meta_format == KIVI_META_F16 ? 2 : 4;     // bytes per scale/zero entry
@@ -55,8 +61,8 @@ Layout layout(const kivi_cache_config& c) {
     L.ks = take(L.slabs * (cap / G) * kD * mb);
     L.kz = take(L.slabs * (cap / G) * kD * mb);
     L.vc = take(L.slabs * cap * L.words * 4);
-    L.vs = take(L.slabs * cap * (kD / G) * mb);
-    L.vz = take(L.slabs * cap * (kD / G) * mb);
+    L.vs = take(L.slabs * cap * ((kD + G - 1) / G) * mb);
+    L.vz = take(L.slabs * cap * ((kD + G - 1) / G) * mb);
     L.kr = take(L.slabs * L.ring * kD * 2);
     L.vr = take(L.slabs * L.ring * kD * 2);
     L.total = off;
@@ -120,10 +126,10 @@ int kivi_cache_init(kivi_cache* cache, const kivi_cache_config* cfg, void* devic
     c.cfg = *cfg;
     const int64_t cap = cfg->store_capacity;
     c.k_store = {reinterpret_cast<uint32_t*>(base + L.kc), base + L.ks, base + L.kz,
-                 cap * L.words, (cap / cfg->group_size) * kD, cap,
+                 cap * L.words, (cap / cfg->group_size) * cfg->head_dim, cap,
                  cfg->bits, cfg->group_size, cfg->head_dim, KIVI_KEYS, cfg->meta_format};
     c.v_store = {reinterpret_cast<uint32_t*>(base + L.vc), base + L.vs, base + L.vz,
-                 cap * L.words, cap * (kD / cfg->group_size), cap,
+                 cap * L.words, cap * ((cfg->head_dim + cfg->group_size - 1) / cfg->group_size), cap,
                  cfg->bits, cfg->group_size, cfg->head_dim, KIVI_VALUES, cfg->meta_format};
     c.k_ring = reinterpret_cast<uint16_t*>(base + L.kr);
     c.v_ring = reinterpret_cast<uint16_t*>(base + L.vr);
@@ -136,6 +142,7 @@ int kivi_cache_prefill(kivi_cache* cache, const uint16_t* k, const uint16_t* v,
                        int64_t x_bh_stride, int64_t S, hipStream_t stream) {
     if (!cache) return KIVI_ERR_NULL;
     if (!valid(&cache->cfg)) return KIVI_ERR_UNSUPPORTED;
+    const int64_t kD = cache->cfg.head_dim;
     if (S < 0 || cache->length != 0) return KIVI_ERR_SHAPE;
     for (uint64_t w : cache->appended)
         if (w) return KIVI_ERR_SHAPE;                  // a step is in progress
@@ -159,7 +166,7 @@ int kivi_cache_prefill(kivi_cache* cache, const uint16_t* k, const uint16_t* v,
     if (nres > 0) {
         const kivi::RowCopy kc = {k + Q * kD, x_bh_stride, cache->k_ring, cache->ring * kD};
         const kivi::RowCopy vc = {v + Q * kD, x_bh_stride, cache->v_ring, cache->ring * kD};
-        rc = finish(kivi::launch_copy_rows(kc, vc, slabs, nres, stream));
+        rc = finish(kivi::launch_copy_rows(kc, vc, slabs, nres, static_cast<int>(kD), stream));
         if (rc != KIVI_OK) return rc;
     }
     cache->length = S;
@@ -173,6 +180,7 @@ int kivi_cache_append(kivi_cache* cache, int32_t layer, const uint16_t* k_new,
                       const uint16_t* v_new, hipStream_t stream) {
     if (!cache) return KIVI_ERR_NULL;
     if (!valid(&cache->cfg)) return KIVI_ERR_UNSUPPORTED;
+    const int64_t kD = cache->cfg.head_dim;
     if (layer < 0 || layer >= cache->cfg.layers || appended(cache, layer)) return KIVI_ERR_SHAPE;
     if (cache->n_res >= cache->ring) return KIVI_ERR_SHAPE;        // no free ring row
     if (!k_new || !v_new) return KIVI_ERR_NULL;
@@ -183,7 +191,7 @@ int kivi_cache_append(kivi_cache* cache, int32_t layer, const uint16_t* k_new,
     const int64_t rs = cache->ring * kD;
     const kivi::RowCopy kc = {k_new, kD, cache->k_ring + slab0 * rs + row * kD, rs};
     const kivi::RowCopy vc = {v_new, kD, cache->v_ring + slab0 * rs + row * kD, rs};
-    const int rc = finish(kivi::launch_copy_rows(kc, vc, seq_slabs(cache), 1, stream));
+    const int rc = finish(kivi::launch_copy_rows(kc, vc, seq_slabs(cache), 1, static_cast<int>(kD), stream));
     if (rc != KIVI_OK) return rc;
     cache->appended[layer >> 6] |= uint64_t{1} << (layer & 63);
     return KIVI_OK;
@@ -194,6 +202,7 @@ int kivi_cache_attend(const kivi_cache* cache, int32_t layer, const uint16_t* q,
                       hipStream_t stream) {
     if (!cache) return KIVI_ERR_NULL;
     if (!valid(&cache->cfg)) return KIVI_ERR_UNSUPPORTED;
+    const int64_t kD = cache->cfg.head_dim;
     if (layer < 0 || layer >= cache->cfg.layers || !appended(cache, layer)) return KIVI_ERR_SHAPE;
     const int64_t slab0 = layer * seq_slabs(cache);
     const kivi_store ks = layer_store(cache->k_store, slab0);
@@ -223,6 +232,7 @@ size_t kivi_cache_attend_workspace_bytes(const kivi_cache* cache, int32_t Hq) {
 int kivi_cache_end_step(kivi_cache* cache, hipStream_t stream) {
     if (!cache) return KIVI_ERR_NULL;
     if (!valid(&cache->cfg)) return KIVI_ERR_UNSUPPORTED;
+    const int64_t kD = cache->cfg.head_dim;
     for (int l = 0; l < cache->cfg.layers; ++l)
         if (!appended(cache, l)) return KIVI_ERR_SHAPE;
     const int64_t F = cache->cfg.flush_tokens;

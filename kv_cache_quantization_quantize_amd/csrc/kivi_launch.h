@@ -103,7 +103,7 @@ hipError_t launch_attend_generic(const AttendArgs& a, const AttendPlan& p, float
 // head_dims other than 64, 128 and 256 (multiples of 16 up to 256, groups of 32)
 hipError_t launch_flush_ragged(bool keys, const FlushArgs& a, hipStream_t stream);
 hipError_t launch_dequant_ragged(const DequantArgs& a, hipStream_t stream);
-// Copies n_rows token rows (head_dim fp16 each) of every slab from src to
+// Copies n_rows token rows (D 16-bit values each) of every slab from src to
 // dst for keys and values at once (one launch).
 struct RowCopy {
     const uint16_t* src;
@@ -111,7 +111,7 @@ struct RowCopy {
     uint16_t* dst;
     int64_t dst_bh_stride;
 };
-hipError_t launch_copy_rows(const RowCopy& k, const RowCopy& v, int64_t slabs, int64_t n_rows,
+hipError_t launch_copy_rows(const RowCopy& k, const RowCopy& v, int64_t slabs, int64_t n_rows, int D,
                             hipStream_t stream);
 
 // The attend entry point behind kivi_decode_attend(_varlen) and the cache:

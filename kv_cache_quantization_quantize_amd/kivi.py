@@ -341,14 +341,14 @@ class Cache:
 
     def __init__(self, layers: int, batch: int, kv_heads: int, store_capacity: int, bits: int = 4,
                  residual_length: int = 128, flush_tokens: int = GROUP, device="cuda",
-                 meta: str = "f32", dtype=torch.float16, group: int = GROUP):
+                 meta: str = "f32", dtype=torch.float16, group: int = GROUP, head_dim: int = HEAD_DIM):
         if meta not in ("f32", "f16"):
             raise ValueError("meta must be 'f32' or 'f16'")
         if dtype not in (torch.float16, torch.bfloat16):
             raise ValueError("dtype must be torch.float16 or torch.bfloat16")
         self.meta, self.dtype = meta, dtype
-        self.group = group
-        self.cfg = CCacheConfig(layers, batch, kv_heads, bits, HEAD_DIM, group, residual_length,
+        self.group, self.head_dim = group, head_dim
+        self.cfg = CCacheConfig(layers, batch, kv_heads, bits, head_dim, group, residual_length,
                                 flush_tokens, store_capacity,
                                 KIVI_META_F16 if meta == "f16" else KIVI_META_F32,
                                 1 if dtype == torch.bfloat16 else 0)
@@ -382,12 +382,12 @@ class Cache:
         """The key and value stores of all layers (torch views of the buffer)."""
         out = []
         for cs, kind in ((self.c.k_store, KIVI_KEYS), (self.c.v_store, KIVI_VALUES)):
-            cap, words = cs.cap, HEAD_DIM * cs.bits // 32
-            G = self.group
-            meta = (self.slabs, cap // G, HEAD_DIM) if kind == KIVI_KEYS else \
-                (self.slabs, cap, HEAD_DIM // G)
+            D, G = self.head_dim, self.group
+            cap, words = cs.cap, D * cs.bits // 32
+            meta = (self.slabs, cap // G, D) if kind == KIVI_KEYS else \
+                (self.slabs, cap, (D + G - 1) // G)
             mdt = torch.float16 if self.meta == "f16" else torch.float32
-            out.append(Store(kind, self.slabs, cap, cs.bits, group=G,
+            out.append(Store(kind, self.slabs, cap, cs.bits, group=G, head_dim=D,
                              codes=self._view(cs.codes, torch.int32, (self.slabs, cap, words)),
                              scale=self._view(cs.scale, mdt, meta),
                              zero=self._view(cs.zero, mdt, meta), meta=self.meta))
@@ -396,7 +396,7 @@ class Cache:
     def rings(self) -> tuple[torch.Tensor, torch.Tensor]:
         """[slabs][ring][128] residual rings in the cache's dtype (torch views
         of the buffer)."""
-        shape = (self.slabs, self.c.ring, HEAD_DIM)
+        shape = (self.slabs, self.c.ring, self.head_dim)
         return (self._view(self.c.k_ring, self.dtype, shape),
                 self._view(self.c.v_ring, self.dtype, shape))
 
@@ -406,8 +406,8 @@ class Cache:
             raise TypeError(f"{name} must be {self.dtype} for this cache, got {t.dtype}")
 
     def prefill(self, k: torch.Tensor, v: torch.Tensor, stream=None) -> None:
-        _need_f16(k, "k", allow_bf16=True)
-        _need_f16(v, "v", allow_bf16=True)
+        _need_f16(k, "k", allow_bf16=True, D=self.head_dim)
+        _need_f16(v, "v", allow_bf16=True, D=self.head_dim)
         self._need_dtype(k, "k")
         self._need_dtype(v, "v")
         if k.stride(0) != v.stride(0) or k.shape != v.shape:
@@ -419,8 +419,8 @@ class Cache:
         for t, name in ((k_new, "k_new"), (v_new, "v_new")):
             self._need_dtype(t, name)
             if not t.is_cuda or not t.is_contiguous() or \
-                    t.numel() != self.cfg.batch * self.cfg.kv_heads * HEAD_DIM:
-                raise ValueError(f"{name} must be a contiguous device tensor [batch*kv_heads][128]")
+                    t.numel() != self.cfg.batch * self.cfg.kv_heads * self.head_dim:
+                raise ValueError(f"{name} must be a contiguous device tensor [batch*kv_heads][head_dim]")
         _check(lib().kivi_cache_append(ctypes.byref(self.c), layer, k_new.data_ptr(), v_new.data_ptr(),
                                        _stream(stream)), "kivi_cache_append")
 

@@ -222,7 +222,7 @@ def test_cache_rejects_bad_configs():
     L = kivi.lib()
     ok = kivi.CCacheConfig(2, 2, 8, 4, 128, 32, 128, 32, 4096)
     assert L.kivi_cache_device_bytes(ctypes.byref(ok)) > 0
-    for field, bad in (("layers", 0), ("layers", 257), ("bits", 3), ("head_dim", 64),
+    for field, bad in (("layers", 0), ("layers", 257), ("bits", 3), ("head_dim", 72),
                        ("group_size", 48), ("flush_tokens", 48), ("residual_length", 100),
                        ("store_capacity", 4100), ("batch", 0), ("meta_format", 2), ("bf16", 2)):
         cfg = kivi.CCacheConfig(2, 2, 8, 4, 128, 32, 128, 32, 4096)

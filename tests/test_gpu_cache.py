@@ -59,7 +59,18 @@ def test_decode_loop_group_sizes(G, case):
     _decode_loop(case, G)
 
 
-def _decode_loop(case, G):
+@pytest.mark.parametrize("Dh,case", [
+    (64, (2, 2, 2, 8, 4, 64, 32, 256, 100, 90, "f32")),
+    (96, (1, 2, 2, 8, 2, 64, 32, 256, 70, 80, "bf16")),
+    (256, (1, 1, 2, 8, 4, 32, 32, 256, 40, 70, "f32")),
+], ids=["D64", "D96-bf16", "D256"])
+def test_decode_loop_head_dims(Dh, case):
+    """Caches at other head_dims (the attend at 64 on MFMA, at 96 and 256 on
+    the generic kernel)."""
+    _decode_loop(case, 32, Dh)
+
+
+def _decode_loop(case, G, Dh=D):
     layers, batch, kvh, Hq, bits, R, F, cap, S0, steps, variant = case
     bf16 = variant == "bf16"
     meta = "f32" if bf16 else variant
@@ -70,12 +81,12 @@ def _decode_loop(case, G):
     per = batch * kvh
     note(f"cache loop layers={layers} batch={batch} kv_heads={kvh} Hq={Hq} bits={bits} R={R} F={F} "
          f"capacity={cap} prompt={S0} steps={steps} meta={meta}")
-    c = kivi.Cache(layers, batch, kvh, cap, bits, R, F, meta=meta, dtype=dtype, group=G)
-    m = oracle.CacheModel(layers, batch, kvh, cap, bits, R, F, meta=meta, fmt=fmt, G=G)
+    c = kivi.Cache(layers, batch, kvh, cap, bits, R, F, meta=meta, dtype=dtype, group=G, head_dim=Dh)
+    m = oracle.CacheModel(layers, batch, kvh, cap, bits, R, F, D=Dh, meta=meta, fmt=fmt, G=G)
     vmax = 0.0
     if S0:
-        k0 = synth.kv_tensor(slabs, S0, keys=True, seed=seed, device="cuda", dtype=dtype)
-        v0 = synth.kv_tensor(slabs, S0, keys=False, seed=seed, device="cuda", dtype=dtype)
+        k0 = synth.kv_tensor(slabs, S0, Dh, keys=True, seed=seed, device="cuda", dtype=dtype)
+        v0 = synth.kv_tensor(slabs, S0, Dh, keys=False, seed=seed, device="cuda", dtype=dtype)
         vmax = float(v0.float().abs().max())
         c.prefill(k0, v0)
         m.prefill(u16(k0), u16(v0))
@@ -83,13 +94,13 @@ def _decode_loop(case, G):
     ws = torch.empty(c.attend_workspace_bytes(Hq), dtype=torch.uint8, device="cuda")
     worst = 0.0
     for step in range(steps):
-        kn = synth.kv_tensor(slabs, 1, keys=True, seed=seed * 1000 + step, device="cuda",
+        kn = synth.kv_tensor(slabs, 1, Dh, keys=True, seed=seed * 1000 + step, device="cuda",
                              dtype=dtype)[:, 0].contiguous()
-        vn = synth.kv_tensor(slabs, 1, keys=False, seed=seed * 1000 + step, device="cuda",
+        vn = synth.kv_tensor(slabs, 1, Dh, keys=False, seed=seed * 1000 + step, device="cuda",
                              dtype=dtype)[:, 0].contiguous()
         vmax = max(vmax, float(vn.float().abs().max()))
-        q = synth.query(layers * batch, Hq, seed=seed * 1000 + step, device="cuda").to(dtype) \
-            .view(layers, batch, Hq, D)
+        q = synth.query(layers * batch, Hq, Dh, seed=seed * 1000 + step, device="cuda").to(dtype) \
+            .view(layers, batch, Hq, Dh)
         outs = []
         for layer in range(layers):
             c.append(layer, kn[layer * per:(layer + 1) * per], vn[layer * per:(layer + 1) * per])
