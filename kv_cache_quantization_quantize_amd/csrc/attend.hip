@@ -120,6 +120,10 @@ AttendPlan plan_attend(int64_t B, int Hq, int Hkv, int64_t n_quant, int64_t n_re
     // B=4 x 16384: 6 -> 31.2, 9 -> 30.3; B=32 x 2048: 6 -> 31.7, 9 -> 31.4.
     const int64_t longer = (total + 699) / 700;
     spw = std::max(spw, std::min<int64_t>(9, longer));
+    // The generic kernel (head_dims other than 64 and 128) has no fixed cost
+    // to amortize and is latency-bound per lane: one 64-token chunk per wave.
+    // (The workspace query plans head_dim 256, so it bounds this plan too.)
+    if (head_dim != 64 && head_dim != 128) spw = std::min<int64_t>(spw, 2);
     AttendPlan p;
     p.steps_q = steps_q;
     p.steps_per_wave = spw;
