@@ -307,7 +307,17 @@ __device__ __forceinline__ bool fast_scale(float s) { return s >= 0x1p-126f && s
 // is what the store holds and what the codes and reconstruction use.  (The
 // zero of an fp16 group is an fp16 value and needs no rounding.)
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float round_to_f16(float s) { return static_cast<float>(static_cast<_Float16>(s)); }
+//
+// The empty asm keeps s a rounded binary32 value.  Without it the compiler
+// folds the FMA that produces s (the last step of scale_of) and this
+// conversion into one mixed-precision FMA with a binary16 result, which
+// rounds once instead of twice: RN16(x) differs from RN16(RN32(x)) wherever
+// RN32(x) lands exactly on a binary16 midpoint, and the store would then
+// hold a different scale than the reading defines.
+__device__ __forceinline__ float round_to_f16(float s) {
+    __asm__("" : "+v"(s));
+    return static_cast<float>(static_cast<_Float16>(s));
+}
 
 // quant_fast's bounds hold for a normal binary16 scale: it is within 2^-11
 // (relative) of the binary32 one, so t / s <= L (1 + 2^-10) stays below

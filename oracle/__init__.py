@@ -219,7 +219,7 @@ class Store:
         self.words = D * bits // 32
         self.codes = np.full((BH, cap, self.words), fill_codes, np.uint32)
         if kind == KEYS:
-            meta_shape = (BH, cap // G, D)
+            meta_shape = (BH, (cap + G - 1) // G, D)     # a ragged last group has its pair too
         else:
             meta_shape = (BH, cap, (D + G - 1) // G)
         self.scale = np.full(meta_shape, fill_meta, np.float32)

@@ -10,6 +10,7 @@ import torch
 
 import oracle
 from gpu_util import note, u16
+from oracle_pool import pmap
 from kv_cache_quantization_quantize_amd import kivi, synth
 
 pytestmark = [pytest.mark.gpu,
@@ -44,24 +45,36 @@ def _gpu(c):
     return out.cpu().numpy().astype(np.float64)
 
 
+def _host(c):
+    """The case's inputs as host fp16 bits, copied once (the oracle's view)."""
+    if "host" not in c:
+        c["host"] = {k: u16(c[k]) for k in ("kx", "vx", "kr", "vr", "q")}
+    return c["host"]
+
+
 def _oracle(c, b):
     Hkv, nq, nr, bits = c["Hkv"], c["nq"], c["nr"], c["bits"]
+    h = _host(c)
     sl = slice(b * Hkv, (b + 1) * Hkv)
     ks = oracle.Store(oracle.KEYS, Hkv, c["cap"], D, bits)
     vs = oracle.Store(oracle.VALUES, Hkv, c["cap"], D, bits)
     if nq:
-        oracle.quantize_keys(u16(c["kx"][sl]), ks, 0, want_recon=False)
-        oracle.quantize_values(u16(c["vx"][sl]), vs, 0, want_recon=False)
-    return oracle.decode_attend(u16(c["q"][b:b + 1]), 1, c["Hq"], Hkv, ks, vs, nq,
-                                u16(c["kr"][sl]), u16(c["vr"][sl]), nr)[0]
+        oracle.quantize_keys(h["kx"][sl], ks, 0, want_recon=False)
+        oracle.quantize_values(h["vx"][sl], vs, 0, want_recon=False)
+    return oracle.decode_attend(h["q"][b:b + 1], 1, c["Hq"], Hkv, ks, vs, nq,
+                                h["kr"][sl], h["vr"][sl], nr)[0]
 
 
 def _compare(c, samples):
+    """Every sequence in ``samples`` against the oracle (one sequence per
+    task of the oracle thread pool)."""
     got = _gpu(c)
     assert np.all(np.isfinite(got))
+    _host(c)
+    samples = list(samples)
+    refs = pmap(lambda b: _oracle(c, b), samples)
     worst = 0.0
-    for b in samples:
-        ref = _oracle(c, b)
+    for b, ref in zip(samples, refs):
         err = float(np.max(np.abs(got[b] - ref)))
         worst = max(worst, err)
         assert err <= TOL, f"sequence {b}: max-abs error {err:.3e}"
@@ -73,8 +86,7 @@ def _compare(c, samples):
 def test_decode_config(B, S_kv):
     """H_q=32, H_kv=8, 4-bit store of S_kv tokens + 128 fp16 residual tokens."""
     c = _case(B, 32, 8, S_kv, 128, 4, seed=1005 + B)
-    samples = sorted({0, B - 1})
-    err = _compare(c, samples)
+    err = _compare(c, range(B))                 # every sequence of the batch
     print(f"B={B} S_kv={S_kv}: max-abs {err:.2e}")
 
 
@@ -170,17 +182,19 @@ def _varlen_gpu(c, max_nq=None, max_nr=None):
 
 def _varlen_oracle(c, seqs, max_nq, max_nr):
     Hkv, bits, cap = c["Hkv"], c["bits"], c["cap"]
-    res = {}
-    for b in seqs:
+    h = _host(c)
+
+    def one(b):
         sl = slice(b * Hkv, (b + 1) * Hkv)
         ks = oracle.Store(oracle.KEYS, Hkv, cap, D, bits)
         vs = oracle.Store(oracle.VALUES, Hkv, cap, D, bits)
-        oracle.quantize_keys(u16(c["kx"][sl]), ks, 0, want_recon=False)
-        oracle.quantize_values(u16(c["vx"][sl]), vs, 0, want_recon=False)
-        res[b] = oracle.decode_attend_varlen(u16(c["q"][b:b + 1]), 1, c["Hq"], Hkv, ks, vs,
-                                             c["nq_seq"][b:b + 1], max_nq, u16(c["kr"][sl]),
-                                             u16(c["vr"][sl]), c["nr_seq"][b:b + 1], max_nr)[0]
-    return res
+        oracle.quantize_keys(h["kx"][sl], ks, 0, want_recon=False)
+        oracle.quantize_values(h["vx"][sl], vs, 0, want_recon=False)
+        return oracle.decode_attend_varlen(h["q"][b:b + 1], 1, c["Hq"], Hkv, ks, vs,
+                                           c["nq_seq"][b:b + 1], max_nq, h["kr"][sl],
+                                           h["vr"][sl], c["nr_seq"][b:b + 1], max_nr)[0]
+    seqs = list(seqs)
+    return dict(zip(seqs, pmap(one, seqs)))
 
 
 def _varlen_compare(c, seqs, max_nq=None, max_nr=None):
@@ -215,14 +229,15 @@ def test_varlen_2bit_gqa8():
     _varlen_compare(c, range(4))
 
 
-def test_varlen_batch32_long_context_sampled():
-    """B=32 requests of 1..16384 store tokens and 0..128 residual tokens."""
+def test_varlen_batch32_long_context():
+    """B=32 requests of 1..16384 store tokens and 0..128 residual tokens,
+    every sequence against the oracle."""
     rng = np.random.default_rng(13)
     nq = rng.integers(1, 16385, size=32)
     nr = rng.integers(0, 129, size=32)
     nq[0], nq[1] = 16384, 1
     c = _varlen_case(32, 32, 8, 16384, 128, 4, 13, nq, nr)
-    _varlen_compare(c, [0, 1, 7, 31])
+    _varlen_compare(c, range(32))
 
 
 def test_varlen_equal_lengths_match_uniform_call():

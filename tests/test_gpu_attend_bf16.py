@@ -3,23 +3,27 @@ kivi_decode_attend_varlen_bf16) against the oracle's bfloat16 attend over the
 same stores (written by the bfloat16 flushes) and the same bfloat16 query and
 residual rows.
 
-Tolerance: the fp16 attend's 2e-3 plus 2^-8 max|v|.  The kernel rounds the
-softmax probabilities to bfloat16 for PV (relative error at most 2^-9, so at
-most 2^-9 max|v| on an output that is a convex combination of values), and
-its in-register reconstruction can differ from the stored one by one
-bfloat16 rounding where the two roundings straddle a boundary."""
+Tolerance: 2e-3 max-abs, the same bar as the fp16 attend.  The kernel's own
+error sources are the softmax probabilities rounded to bfloat16 for PV
+(relative 2^-9 each) and an in-register reconstruction that can differ from
+the stored one by one bfloat16 rounding where the two roundings straddle a
+boundary; both are independent per token, so on these caches (values of
+order 1) they stay well inside the bar.  Only the test whose values are
+scaled to 1e6 is held to a bound relative to its values."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
 from gpu_util import note, u16
+from oracle_pool import pmap
 from kv_cache_quantization_quantize_amd import kivi, synth
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
 D = 128
+TOL = 2e-3
 
 CASES = [
     # B, Hq, Hkv, n_quant, n_res, bits, G
@@ -36,15 +40,6 @@ CASES = [
 
 def _bf16(t):
     return t.to(torch.bfloat16).contiguous()
-
-
-def _tol(vx, vr, nq, nr):
-    vmax = 0.0
-    if nq:
-        vmax = max(vmax, float(vx.float().abs().max()))
-    if nr:
-        vmax = max(vmax, float(vr[:, :nr].float().abs().max()))
-    return 2e-3 + 2.0 ** -8 * vmax
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "B%d-Hq%d-Hkv%d-nq%d-nr%d-b%d-G%d" % c)
@@ -78,7 +73,7 @@ def test_bf16_attend(case):
     if nq:
         oracle.quantize_keys(u16(kx), hk, 0, want_recon=False, fmt="bf16")
         oracle.quantize_values(u16(vx), hv, 0, want_recon=False, fmt="bf16")
-    tol = _tol(vx, vr, nq, nr)
+    tol = TOL
     ref = oracle.decode_attend(u16(q), B, Hq, Hkv, hk, hv, nq, u16(kr), u16(vr), nr, fmt="bf16")
     err = float(np.max(np.abs(out.cpu().numpy().astype(np.float64) - ref)))
     print(f"{case}: max-abs error {err:.2e} (tolerance {tol:.2e})")
@@ -91,7 +86,9 @@ def test_bf16_attend(case):
 
 def test_bf16_values_outside_fp16_range():
     """A bfloat16 cache whose values exceed fp16's range (1e6): the attend
-    stays in bfloat16 throughout, so the result is finite and matches."""
+    stays in bfloat16 throughout, so the result is finite and matches to
+    2^-8 of the largest value (bfloat16's relative precision; the absolute
+    2e-3 bar is for values of order 1)."""
     B, Hq, Hkv, nq, nr = 1, 8, 2, 256, 16
     BH = B * Hkv
     kx = _bf16(synth.kv_tensor(BH, nq, keys=True, seed=5, device="cuda", dtype=torch.bfloat16))
@@ -113,13 +110,13 @@ def test_bf16_values_outside_fp16_range():
     ref = oracle.decode_attend(u16(q), B, Hq, Hkv, hk, hv, nq, u16(kr), u16(vr), nr, fmt="bf16")
     got = out.cpu().numpy().astype(np.float64)
     assert np.all(np.isfinite(got))
-    tol = _tol(vx, vr, nq, nr)
-    assert float(np.max(np.abs(got - ref))) <= tol
+    vmax = max(float(vx.float().abs().max()), float(vr.float().abs().max()))
+    assert float(np.max(np.abs(got - ref))) <= 2.0 ** -8 * vmax
 
 
-def test_full_size_bf16_attend_sampled():
+def test_full_size_bf16_attend():
     """32 sequences x 32 query heads over 8 kv heads, 16384 store tokens + 128
-    residual, 4-bit: four sampled sequences against the oracle."""
+    residual, 4-bit: every sequence against the oracle."""
     B, Hq, Hkv, nq, nr = 32, 32, 8, 16384, 128
     BH = B * Hkv
     kx = synth.kv_tensor(BH, nq, keys=True, seed=91, device="cuda", dtype=torch.bfloat16)
@@ -134,14 +131,19 @@ def test_full_size_bf16_attend_sampled():
     kivi.quantize_values(vx, vs, 0)
     out = kivi.decode_attend(q, ks, vs, nq, kr, vr, nr)
     torch.cuda.synchronize()
-    for b in (0, 13, 31):
+    got = out.cpu().numpy().astype(np.float64)
+    hkx, hvx, hkr, hvr, hq = u16(kx), u16(vx), u16(kr), u16(vr), u16(q)
+
+    def one(b):
         sl = slice(b * Hkv, (b + 1) * Hkv)
         hk = oracle.Store(oracle.KEYS, Hkv, nq, D, 4, 32)
         hv = oracle.Store(oracle.VALUES, Hkv, nq, D, 4, 32)
-        oracle.quantize_keys(u16(kx[sl]), hk, 0, want_recon=False, fmt="bf16")
-        oracle.quantize_values(u16(vx[sl]), hv, 0, want_recon=False, fmt="bf16")
-        ref = oracle.decode_attend(u16(q[b:b + 1]), 1, Hq, Hkv, hk, hv, nq, u16(kr[sl]), u16(vr[sl]), nr,
-                                   fmt="bf16")
-        tol = _tol(vx[sl], vr[sl], nq, nr)
-        err = float(np.max(np.abs(out[b:b + 1].cpu().numpy().astype(np.float64) - ref)))
-        assert err <= tol, f"sequence {b}: max-abs error {err:.3e} > {tol:.3e}"
+        oracle.quantize_keys(hkx[sl], hk, 0, want_recon=False, fmt="bf16")
+        oracle.quantize_values(hvx[sl], hv, 0, want_recon=False, fmt="bf16")
+        return oracle.decode_attend(hq[b:b + 1], 1, Hq, Hkv, hk, hv, nq, hkr[sl], hvr[sl], nr,
+                                    fmt="bf16")[0]
+    refs = pmap(one, range(B))
+    errs = [float(np.max(np.abs(got[b] - refs[b]))) for b in range(B)]
+    print(f"bf16 full size: max-abs error over all {B} sequences {max(errs):.2e}")
+    for b, err in enumerate(errs):
+        assert err <= TOL, f"sequence {b}: max-abs error {err:.3e} > {TOL:.3e}"

@@ -44,8 +44,7 @@ def _meta_equal(gpu: torch.Tensor, host: np.ndarray) -> bool:
     c[0], c[1], c[2], c[3], c[4], c[5], c[6], c[8], c[10]))
 def test_decode_loop_matches_model(case):
     """The last field is the scale/zero format ("f32", "f16") or "bf16" for a
-    bfloat16 cache (binary32 scale/zero; tolerance as for the bfloat16
-    attend: 2e-3 + 2^-8 max|v|)."""
+    bfloat16 cache (binary32 scale/zero; the same 2e-3 tolerance)."""
     _decode_loop(case, 32)
 
 
@@ -83,11 +82,9 @@ def _decode_loop(case, G, Dh=D):
          f"capacity={cap} prompt={S0} steps={steps} meta={meta}")
     c = kivi.Cache(layers, batch, kvh, cap, bits, R, F, meta=meta, dtype=dtype, group=G, head_dim=Dh)
     m = oracle.CacheModel(layers, batch, kvh, cap, bits, R, F, D=Dh, meta=meta, fmt=fmt, G=G)
-    vmax = 0.0
     if S0:
         k0 = synth.kv_tensor(slabs, S0, Dh, keys=True, seed=seed, device="cuda", dtype=dtype)
         v0 = synth.kv_tensor(slabs, S0, Dh, keys=False, seed=seed, device="cuda", dtype=dtype)
-        vmax = float(v0.float().abs().max())
         c.prefill(k0, v0)
         m.prefill(u16(k0), u16(v0))
     assert (c.length, c.n_quant) == (m.length, m.n_quant)
@@ -98,7 +95,6 @@ def _decode_loop(case, G, Dh=D):
                              dtype=dtype)[:, 0].contiguous()
         vn = synth.kv_tensor(slabs, 1, Dh, keys=False, seed=seed * 1000 + step, device="cuda",
                              dtype=dtype)[:, 0].contiguous()
-        vmax = max(vmax, float(vn.float().abs().max()))
         q = synth.query(layers * batch, Hq, Dh, seed=seed * 1000 + step, device="cuda").to(dtype) \
             .view(layers, batch, Hq, Dh)
         outs = []
@@ -114,8 +110,7 @@ def _decode_loop(case, G, Dh=D):
         for layer in range(layers):
             err = float(np.max(np.abs(outs[layer].cpu().numpy().astype(np.float64) - ref[layer])))
             worst = max(worst, err)
-            tol = TOL + (2.0 ** -8 * vmax if bf16 else 0.0)
-            assert err <= tol, f"step {step} layer {layer}: max-abs error {err:.3e}"
+            assert err <= TOL, f"step {step} layer {layer}: max-abs error {err:.3e}"
     Q = c.n_quant
     ks, vs = c.stores()
     torch.cuda.synchronize()

@@ -221,8 +221,8 @@ ATTEND64 = [
 @pytest.mark.parametrize("case", ATTEND64, ids=lambda c: "B%d-Hq%d-Hkv%d-nq%d-nr%d-b%d" % c)
 def test_attend_head_dim_64(case, fmt):
     """The decode attends (uniform and variable-length) at head_dim 64 with
-    groups of 32, fp16 and bfloat16, against the oracle (tolerance 2e-3, plus
-    2^-8 max|v| for bfloat16 as for the other bfloat16 attends)."""
+    groups of 32, fp16 and bfloat16, against the oracle (tolerance 2e-3 in
+    both formats)."""
     B, Hq, Hkv, nq, nr, bits = case
     Dh = 64
     BH = B * Hkv
@@ -255,10 +255,6 @@ def test_attend_head_dim_64(case, fmt):
         oracle.quantize_keys(u16(kx), hk, 0, want_recon=False, fmt=fmt)
         oracle.quantize_values(u16(vx), hv, 0, want_recon=False, fmt=fmt)
     tol = 2e-3
-    if fmt == "bf16":
-        vmax = max(float(vx.float().abs().max()) if nq else 0.0,
-                   float(vr[:, :nr].float().abs().max()) if nr else 0.0)
-        tol += 2.0 ** -8 * vmax
     ref = oracle.decode_attend(u16(q), B, Hq, Hkv, hk, hv, nq, u16(kr), u16(vr), nr, fmt=fmt)
     err = float(np.max(np.abs(out.cpu().numpy().astype(np.float64) - ref)))
     print(f"{case} {fmt}: max-abs error {err:.2e}")
@@ -276,6 +272,20 @@ GENERIC = [
     (2, 8, 8, 0, 40, 4),
     (3, 4, 1, 200, 0, 4),
 ]
+# plans the small cases above never reach: several steps per wave with a wave
+# that runs from the store into the residual window, and a single sequence
+# with eight query heads per kv head split 65 ways (the 16-wave combine)
+GENERIC_PLANS = [
+    (4, 32, 8, 2048, 128, 4),
+    (1, 8, 1, 2048, 5, 4),
+]
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("Dh", [256, 96])
+@pytest.mark.parametrize("case", GENERIC_PLANS, ids=lambda c: "B%d-Hq%d-Hkv%d-nq%d-nr%d-b%d" % c)
+def test_attend_generic_plans(case, Dh, fmt):
+    test_attend_generic_head_dims(case, Dh, fmt)
 
 
 @pytest.mark.parametrize("fmt", ["f16", "bf16"])

@@ -2,8 +2,10 @@
 arguments are tightest: one slab of n_quant = 2^24 - 1 store tokens (the
 attend's token bound; the last key group is ragged) plus a residual window.
 
-  * the flushes are compared with the oracle on three sampled token windows
-    (the start, the middle and the ragged end);
+  * the flushes are compared with the oracle over the whole slab, in token
+    windows of 2^18 (key windows start on a group, so each window is an
+    independent flush; the oracle runs the windows on a thread pool), the
+    last window ending in the ragged group;
   * the dequantize is compared with the oracle on the same windows;
   * the attend (uniform and variable-length) must equal dense attention in
     float64 over the library's own dequantization of the same store (a
@@ -15,7 +17,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import assert_u16_equal, note, u16
+from gpu_util import note, u16
+from oracle_pool import pmap, threads
 from kv_cache_quantization_quantize_amd import kivi, synth
 
 pytestmark = [pytest.mark.gpu,
@@ -37,24 +40,36 @@ def test_largest_single_slab():
     kivi.quantize_values(vx, vs, 0)
     torch.cuda.synchronize()
 
-    # sampled windows against the oracle (key windows start on a group)
-    for t0, n in ((0, 4096), (1 << 23, 4096), (CAP - 4096, N - (CAP - 4096))):
-        for kind, x, st in ((oracle.KEYS, kx, ks), (oracle.VALUES, vx, vs)):
-            hs = oracle.Store(kind, 1, n + (-n) % 32, D, 4, 32)
-            fn = oracle.quantize_keys if kind == oracle.KEYS else oracle.quantize_values
-            hrec = fn(u16(x[:, t0:t0 + n]), hs, 0, want_recon=True)
-            codes = st.codes[:, t0:t0 + n].cpu().numpy().view(np.uint32)
-            assert np.array_equal(codes, hs.codes[:, :n]), f"codes at [{t0}, {t0 + n})"
-            if kind == oracle.KEYS:
-                g0, g1 = t0 // 32, (t0 + n + 31) // 32
-                assert np.array_equal(st.scale[:, g0:g1].cpu().numpy(), hs.scale[:, :g1 - g0])
-                assert np.array_equal(st.zero[:, g0:g1].cpu().numpy(), hs.zero[:, :g1 - g0])
-            else:
-                assert np.array_equal(st.scale[:, t0:t0 + n].cpu().numpy(), hs.scale[:, :n])
-                assert np.array_equal(st.zero[:, t0:t0 + n].cpu().numpy(), hs.zero[:, :n])
-            out = kivi.dequantize(st, t0, n)
-            torch.cuda.synchronize()
-            assert_u16_equal(u16(out), hrec, f"dequantize [{t0}, {t0 + n})")
+    # the whole slab against the oracle, window by window
+    W = 1 << 18
+    windows = [(t0, min(W, N - t0)) for t0 in range(0, N, W)]
+    for kind, x, st in ((oracle.KEYS, kx, ks), (oracle.VALUES, vx, vs)):
+        fn = oracle.quantize_keys if kind == oracle.KEYS else oracle.quantize_values
+        for i in range(0, len(windows), threads()):
+            part = windows[i:i + threads()]
+            note(f"limits: oracle {'keys' if kind == oracle.KEYS else 'values'} tokens "
+                 f"[{part[0][0]}, {part[-1][0] + part[-1][1]})")
+            host = []
+            for t0, n in part:
+                g0, g1 = (t0 // 32, (t0 + n + 31) // 32) if kind == oracle.KEYS else (t0, t0 + n)
+                host.append((t0, n, u16(x[:, t0:t0 + n]),
+                             st.codes[:, t0:t0 + n].cpu().numpy().view(np.uint32),
+                             st.scale[:, g0:g1].cpu().numpy().view(np.uint32),
+                             st.zero[:, g0:g1].cpu().numpy().view(np.uint32),
+                             u16(kivi.dequantize(st, t0, n))))
+
+            def one(h):
+                t0, n, xh, codes, scale, zero, rec = h
+                hs = oracle.Store(kind, 1, n + (-n) % 32, D, 4, 32)
+                hrec = fn(xh, hs, 0, want_recon=True)
+                m = scale.shape[1]
+                return (t0, np.array_equal(codes, hs.codes[:, :n]),
+                        np.array_equal(scale, hs.scale[:, :m].view(np.uint32)),
+                        np.array_equal(zero, hs.zero[:, :m].view(np.uint32)),
+                        np.array_equal(rec, hrec))
+            for t0, *ok in pmap(one, host):
+                assert all(ok), f"window at token {t0}: codes/scale/zero/dequantize equal {ok}"
+            del host
     del kx, vx
     torch.cuda.empty_cache()
 

@@ -10,6 +10,7 @@ import pytest
 import torch
 
 import oracle
+from oracle_pool import pmap
 from gpu_util import (CODE_SENTINEL, META_SENTINEL, assert_store_equal, assert_u16_equal, note, u16)
 from kv_cache_quantization_quantize_amd import kivi, synth
 
@@ -162,10 +163,10 @@ def test_attend(case, G):
     assert err <= TOL, f"varlen max-abs error {err:.3e}"
 
 
-def test_full_size_attend_sampled():
+def test_full_size_attend():
     """The measured shape (32 sequences x 32 query heads over 8 kv heads,
-    16384 store tokens + 128 residual, 4-bit, groups of 32): four sampled
-    sequences against the oracle."""
+    16384 store tokens + 128 residual, 4-bit, groups of 32): every sequence
+    against the oracle."""
     B, Hq, Hkv, nq, nr = 32, 32, 8, 16384, 128
     BH = B * Hkv
     seed = 777
@@ -181,12 +182,56 @@ def test_full_size_attend_sampled():
     kivi.quantize_values(vx, vs, 0)
     out = kivi.decode_attend(q, ks, vs, nq, kr, vr, nr)
     torch.cuda.synchronize()
-    for b in (0, 9, 22, 31):
+    got = out.cpu().numpy().astype(np.float64)
+    hkx, hvx, hkr, hvr, hq = u16(kx), u16(vx), u16(kr), u16(vr), u16(q)
+
+    def one(b):
         sl = slice(b * Hkv, (b + 1) * Hkv)
         hk = oracle.Store(oracle.KEYS, Hkv, nq, D, 4, 32, meta="f16")
         hv = oracle.Store(oracle.VALUES, Hkv, nq, D, 4, 32, meta="f16")
-        oracle.quantize_keys(u16(kx[sl]), hk, 0, want_recon=False)
-        oracle.quantize_values(u16(vx[sl]), hv, 0, want_recon=False)
-        ref = oracle.decode_attend(u16(q[b:b + 1]), 1, Hq, Hkv, hk, hv, nq, u16(kr[sl]), u16(vr[sl]), nr)
-        err = float(np.max(np.abs(out[b:b + 1].cpu().numpy().astype(np.float64) - ref)))
+        oracle.quantize_keys(hkx[sl], hk, 0, want_recon=False)
+        oracle.quantize_values(hvx[sl], hv, 0, want_recon=False)
+        return oracle.decode_attend(hq[b:b + 1], 1, Hq, Hkv, hk, hv, nq, hkr[sl], hvr[sl], nr)[0]
+    for b, ref in enumerate(pmap(one, range(B))):
+        err = float(np.max(np.abs(got[b] - ref)))
         assert err <= TOL, f"sequence {b}: max-abs error {err:.3e}"
+
+
+@pytest.mark.parametrize("kind", ["keys", "values"])
+def test_hand_worked_groups_on_gpu(kind):
+    """Every hand-worked group of tests/golden/meta16_groups.txt as a real
+    group of the flush (a key channel's 32 tokens, or a token's first value
+    group, padded with copies of its minimum): the stored binary16 scale and
+    zero, the codes and the fused reconstruction equal the fixture's values.
+    The midpoint_scale row is a scale whose binary32 value is a binary16
+    tie, where a single rounding straight to binary16 goes the other way."""
+    from golden_io import hexes, ints, rows
+    for r in rows("meta16_groups.txt"):
+        name, bits, xs = r[0], int(r[1]), hexes(r[2])
+        want_s, want_z = hexes(r[3])[0], hexes(r[4])[0]
+        want_q, want_rec = ints(r[5]), hexes(r[6])
+        n = len(xs)
+        mn = min(xs, key=lambda b: float(np.array([b], np.uint16).view(np.float16)[0]))
+        grp = np.array(xs + [mn] * (32 - n), np.uint16)
+        x = np.zeros((1, 32, D), np.uint16)
+        if kind == "keys":
+            x[0, :, 0] = grp                    # channel 0, tokens 0..31
+        else:
+            x[0, 0, :32] = grp                  # token 0, channels 0..31
+        x_dev = torch.from_numpy(x.view(np.int16)).cuda().view(torch.float16)
+        st, hs = _stores(kind, 1, 32, bits, 32)
+        rec = torch.empty_like(x_dev)
+        note(f"hand-worked binary16 group {name} as {kind}")
+        (kivi.quantize_keys if kind == "keys" else kivi.quantize_values)(x_dev, st, 0, rec)
+        torch.cuda.synchronize()
+        s = int(st.scale.view(torch.int16)[0, 0, 0]) & 0xFFFF
+        z = int(st.zero.view(torch.int16)[0, 0, 0]) & 0xFFFF
+        assert (s, z) == (want_s, want_z), f"{name} {kind}: scale/zero {s:#06x}/{z:#06x}"
+        words = st.codes.cpu().numpy().view(np.uint32)[0]
+        r16 = u16(rec)[0]
+        per_word = 32 // bits
+        for i in range(n):
+            t, c = (i, 0) if kind == "keys" else (0, i)
+            q = (int(words[t, c // per_word]) >> (bits * (c % per_word))) & ((1 << bits) - 1)
+            assert q == want_q[i], f"{name} {kind}: code {i} is {q}, fixture {want_q[i]}"
+            assert int(r16[t, c]) == want_rec[i], f"{name} {kind}: recon {i} {int(r16[t, c]):#06x}"
