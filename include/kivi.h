@@ -82,6 +82,8 @@ enum {
 
 enum { KIVI_KEYS = 0, KIVI_VALUES = 1 };
 enum { KIVI_META_F32 = 0, KIVI_META_F16 = 1 };
+/* flags of kivi_decode_attend_workspace_bytes: which attend call it sizes */
+enum { KIVI_ATTEND_BF16 = 1, KIVI_ATTEND_VARLEN = 2 };
 
 /* A packed store (see the layout above).  The struct itself lives in host
  * memory and is only read during the call; the arrays are device memory. */
@@ -193,10 +195,14 @@ int kivi_dequantize_bf16(const kivi_store* src, int64_t BH, int64_t token_begin,
  *              res_bh_stride; may be NULL when n_res == 0
  *   out        fp32 [B][Hq][head_dim]
  *   workspace  device scratch of at least
- *              kivi_decode_attend_workspace_bytes(B, Hq, Hkv, n_quant, n_res)
- *              bytes, 256-byte aligned; its contents on entry do not matter
+ *              kivi_decode_attend_workspace_bytes(B, Hq, Hkv, n_quant, n_res,
+ *              head_dim, 0) bytes, 256-byte aligned, owned by the caller; its
+ *              contents on entry do not matter.  It holds the per-split
+ *              partials between the call's two kernels, so calls that may
+ *              overlap in time need separate workspaces.
  * n_quant + n_res must be > 0, n_quant and n_res below 2^24, Hq/Hkv one of
- * 1, 2, 4, 8, and softmax_scale finite and > 0 (KIVI_ERR_SHAPE otherwise).
+ * 1, 2, 4, 8, B * Hkv at most 65535, and softmax_scale finite and > 0
+ * (KIVI_ERR_SHAPE otherwise).
  */
 int kivi_decode_attend(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
                        const kivi_store* k, const kivi_store* v, int64_t n_quant,
@@ -219,8 +225,9 @@ int kivi_decode_attend(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
  *              keeps every load inside the store and residual bounds below.
  *   max_n_quant, max_n_res  host bounds on the lengths: the grid, the
  *              workspace (kivi_decode_attend_workspace_bytes(B, Hq, Hkv,
- *              max_n_quant, max_n_res)) and the store/residual validation use
- *              them.  max_n_quant + max_n_res must be > 0.
+ *              max_n_quant, max_n_res, head_dim, KIVI_ATTEND_VARLEN)) and the
+ *              store/residual validation use them.  max_n_quant + max_n_res
+ *              must be > 0.
  * A sequence whose clamped lengths are both 0 gets an all-zero output row.
  * Every other argument and every error is as for kivi_decode_attend.
  */
@@ -237,11 +244,13 @@ int kivi_decode_attend_varlen(const uint16_t* q, int64_t B, int32_t Hq, int32_t 
  * bfloat16 bit patterns, and the stores (written by the _bf16 flushes, with
  * binary32 scale/zero) are reconstructed to bfloat16 in registers, as
  * kivi_dequantize_bf16 would.  QK^T and PV run on bfloat16 MFMA operands
- * with fp32 accumulation; the softmax probabilities are rounded to bfloat16
- * for PV (about 2^-9 relative), so the result is within 2e-3 + 2^-8 max|v|
- * of the float64 definition over the bfloat16 reconstruction.  A store with
- * binary16 scale/zero returns KIVI_ERR_UNSUPPORTED; everything else is as
- * for kivi_decode_attend and kivi_decode_attend_varlen (same workspace).
+ * with fp32 accumulation; the softmax probabilities enter PV as a bfloat16
+ * pair (a truncated high part and the rounded remainder, 2^-16 relative),
+ * so the result is within 2e-3 max-abs of the float64 definition over the
+ * bfloat16 reconstruction for values of order 1.  A store with binary16
+ * scale/zero returns KIVI_ERR_UNSUPPORTED; everything else is as for
+ * kivi_decode_attend and kivi_decode_attend_varlen (workspace sized with
+ * KIVI_ATTEND_BF16 in the flags).
  */
 int kivi_decode_attend_bf16(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
                             const kivi_store* k, const kivi_store* v, int64_t n_quant,
@@ -256,10 +265,13 @@ int kivi_decode_attend_varlen_bf16(const uint16_t* q, int64_t B, int32_t Hq, int
                                    float softmax_scale, float* out, void* workspace,
                                    size_t workspace_bytes, hipStream_t stream);
 
-/* Workspace bytes any of the attend calls needs for this shape, at any
- * head_dim (the bound of head_dim 256) and in either format. */
-size_t kivi_decode_attend_workspace_bytes(int64_t B, int32_t Hq, int32_t Hkv,
-                                          int64_t n_quant, int64_t n_res);
+/* Workspace bytes of one attend call: B, Hq, Hkv, n_quant and n_res as the
+ * call passes them (the _varlen calls: their max_n_quant and max_n_res),
+ * head_dim of its stores, and flags KIVI_ATTEND_BF16 for the _bf16 calls
+ * plus KIVI_ATTEND_VARLEN for the _varlen ones.  Exactly what that call
+ * checks for; 0 for arguments no call accepts. */
+size_t kivi_decode_attend_workspace_bytes(int64_t B, int32_t Hq, int32_t Hkv, int64_t n_quant,
+                                          int64_t n_res, int32_t head_dim, int32_t flags);
 
 /* Static description of a status code. */
 const char* kivi_status_string(int status);

@@ -42,7 +42,8 @@ int64_t meta_rows(const kivi_store* st) {
 // Stores take head_dim 128 with groups of 32, 64 or 128 tokens (keys) or
 // channels (values), and any other multiple of 16 from 16 to 256 with groups
 // of 32 (a token's last value group is ragged when 32 does not divide
-// head_dim).  The attend and the decode-loop cache take head_dim 128.
+// head_dim).  The attend and the decode-loop cache take every such store
+// (binary16 scale/zero at head_dim 128 only, see check_store).
 bool geometry_ok(int32_t D, int32_t G) {
     if (D == 128) return G == 32 || G == 64 || G == 128;
     return D >= 16 && D <= 256 && D % 16 == 0 && G == 32;
@@ -165,19 +166,14 @@ int kivi_dequantize_bf16(const kivi_store* src, int64_t BH, int64_t token_begin,
     return dequantize(true, src, BH, token_begin, n_tokens, out, out_bh_stride, stream);
 }
 
-size_t kivi_decode_attend_workspace_bytes(int64_t B, int32_t Hq, int32_t Hkv,
-                                          int64_t n_quant, int64_t n_res) {
+size_t kivi_decode_attend_workspace_bytes(int64_t B, int32_t Hq, int32_t Hkv, int64_t n_quant,
+                                          int64_t n_res, int32_t head_dim, int32_t flags) {
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || n_quant < 0 || n_res < 0 || n_quant + n_res == 0) return 0;
-    // the largest of the uniform and variable-length plans, fp16 and
-    // bfloat16, so one size serves every attend call of this shape
-    size_t need = 0;
-    for (int varlen = 0; varlen < 2; ++varlen)
-        for (int bf16 = 0; bf16 < 2; ++bf16) {
-            // head_dim 256 bounds every head_dim's split partials
-            const size_t b = kivi::plan_attend(B, Hq, Hkv, n_quant, n_res, varlen != 0, 256, bf16 != 0).workspace_bytes;
-            need = b > need ? b : need;
-        }
-    return need;
+    if (head_dim < 16 || head_dim > 256 || head_dim % 16 != 0) return 0;
+    if ((flags & ~(KIVI_ATTEND_BF16 | KIVI_ATTEND_VARLEN)) != 0) return 0;
+    // exactly the plan the matching call will make
+    return kivi::plan_attend(B, Hq, Hkv, n_quant, n_res, (flags & KIVI_ATTEND_VARLEN) != 0, head_dim,
+                             (flags & KIVI_ATTEND_BF16) != 0).workspace_bytes;
 }
 
 }  // extern "C"
@@ -224,9 +220,9 @@ int decode_attend_entry(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
         if ((rc = check_f16_tensor(v_res, slabs, rows, res_bh_stride, D)) != KIVI_OK) return rc;
     }
     const kivi::AttendPlan plan = kivi::plan_attend(B, Hq, Hkv, n_quant, n_res, seq_n_quant != nullptr, D, bf16);
+    if (plan.n_split > kMaxBlocks || slabs > 65535 || B * Hq > kMaxBlocks) return KIVI_ERR_SHAPE;
     if (!workspace || workspace_bytes < plan.workspace_bytes) return KIVI_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KIVI_ERR_ALIGN;
-    if (plan.n_split > kMaxBlocks || slabs > 65535 || B * Hq > kMaxBlocks) return KIVI_ERR_SHAPE;
 
     kivi::AttendArgs a;
     a.q = q; a.B = B; a.Hq = Hq; a.Hkv = Hkv;
@@ -319,11 +315,40 @@ const char* kivi_status_string(int status) {
 
 int kivi_last_hip_error(void) { return g_last_hip_error; }
 
+// The calibration kernels take one workgroup per 16 KiB: sizes up to
+// 2^31 - 1 workgroups.
+static bool calib_size_ok(size_t n_bytes) { return n_bytes / 16384 < static_cast<size_t>(kMaxBlocks); }
+
 int kivi_calib_copy(const void* src, void* dst, size_t n_bytes, hipStream_t stream) {
     if (!src || !dst) return KIVI_ERR_NULL;
     if (!aligned16(src) || !aligned16(dst) || n_bytes % 16 != 0) return KIVI_ERR_ALIGN;
+    if (!calib_size_ok(n_bytes)) return KIVI_ERR_SHAPE;
     if (n_bytes == 0) return KIVI_OK;
     return finish(kivi::launch_calib_copy(src, dst, n_bytes, stream));
+}
+
+int kivi_calib_read(const void* src, size_t n_bytes, void* sink, hipStream_t stream) {
+    if (!src || !sink) return KIVI_ERR_NULL;
+    if (!aligned16(src) || !aligned16(sink) || n_bytes % 16 != 0) return KIVI_ERR_ALIGN;
+    if (!calib_size_ok(n_bytes)) return KIVI_ERR_SHAPE;
+    if (n_bytes == 0) return KIVI_OK;
+    return finish(kivi::launch_calib_read(src, n_bytes, static_cast<uint32_t*>(sink), stream));
+}
+
+int kivi_calib_write(void* dst, size_t n_bytes, hipStream_t stream) {
+    if (!dst) return KIVI_ERR_NULL;
+    if (!aligned16(dst) || n_bytes % 16 != 0) return KIVI_ERR_ALIGN;
+    if (!calib_size_ok(n_bytes)) return KIVI_ERR_SHAPE;
+    if (n_bytes == 0) return KIVI_OK;
+    return finish(kivi::launch_calib_write(dst, n_bytes, stream));
+}
+
+int kivi_calib_mix(const void* src, size_t n_bytes, void* dst, hipStream_t stream) {
+    if (!src || !dst) return KIVI_ERR_NULL;
+    if (!aligned16(src) || !aligned16(dst) || n_bytes % 16 != 0) return KIVI_ERR_ALIGN;
+    if (!calib_size_ok(n_bytes)) return KIVI_ERR_SHAPE;
+    if (n_bytes == 0) return KIVI_OK;
+    return finish(kivi::launch_calib_mix(src, n_bytes, dst, stream));
 }
 
 }  // extern "C"

@@ -10,14 +10,16 @@ namespace kivi {
 // Merge the splits of one (sequence, query head), base-2 log-sum-exp:
 // o = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i with M = max_i m_i.
 // WAVES waves per row: wave w takes splits w, w + WAVES, ..., lane l
-// channels 2l and 2l + 1 (lanes l < D/2); the waves' sums meet in LDS.  Many
-// splits (small batches, long contexts) get 16 waves, so each walks only a
-// few of them.
+// channels 2l and 2l + 1 (lanes l < D/2); the waves' sums meet in LDS.  The
+// first kU splits of every wave are loaded together with their (m, l)
+// before the maximum is known, so a row of up to kU * WAVES splits costs one
+// memory round trip; only longer rows loop over the rest.
 template <int WAVES, int D>
 __global__ __launch_bounds__(64 * WAVES) void attend_combine_kernel(const float* __restrict__ ws_o,
                                                                    const float* __restrict__ ws_ml,
-                                                                   int64_t n_split, float* __restrict__ out)
+                                                                   int64_t n_part, float* __restrict__ out)
 {
+    constexpr int kU = 4;
     __shared__ float red_m[WAVES];
     __shared__ float red_l[WAVES];
     __shared__ float2 red_o[WAVES][64];
@@ -25,50 +27,45 @@ __global__ __launch_bounds__(64 * WAVES) void attend_combine_kernel(const float*
     const int t = threadIdx.x;
     const int w = t >> 6;
     const int l = t & 63;
-    const float* ml = ws_ml + row * n_split * 2;
-    const float2* o = reinterpret_cast<const float2*>(ws_o + row * n_split * D) + l;
+    const float* ml = ws_ml + row * n_part * 2;
+    const float2* o = reinterpret_cast<const float2*>(ws_o + row * n_part * D) + l;
     const bool has = l < D / 2;                      // the lane has channels (always at D = 128)
 
-    float M = -INFINITY;
-    for (int64_t i = t; i < n_split; i += 64 * WAVES) M = fmaxf(M, ml[2 * i]);
+    float2 mv[kU], ov[kU];
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    if (l == 0) red_m[w] = M;
+    for (int u = 0; u < kU; ++u) {
+        const int64_t i = w + static_cast<int64_t>(u) * WAVES;
+        mv[u] = i < n_part ? *reinterpret_cast<const float2*>(ml + 2 * i) : make_float2(-INFINITY, 0.0f);
+        ov[u] = (i < n_part && has) ? o[i * (D / 2)] : make_float2(0.0f, 0.0f);
+    }
+    float M = mv[0].x;
+#pragma unroll
+    for (int u = 1; u < kU; ++u) M = fmaxf(M, mv[u].x);
+    for (int64_t i = w + static_cast<int64_t>(kU) * WAVES; i < n_part; i += WAVES) M = fmaxf(M, ml[2 * i]);
+    if (l == 0) red_m[w] = M;                        // uniform across the wave
     __syncthreads();
     M = red_m[0];
 #pragma unroll
     for (int i = 1; i < WAVES; ++i) M = fmaxf(M, red_m[i]);
-    // every split empty (a sequence with no tokens): keep the weights finite (0)
+    // every partial empty (a sequence with no tokens): keep the weights finite (0)
     if (M == -INFINITY) M = 0.0f;
 
     float L = 0.0f;
     float2 acc = make_float2(0.0f, 0.0f);
-    int64_t i = w;
-    constexpr int kU = 4;
-    for (; i + (kU - 1) * WAVES < n_split; i += kU * WAVES) {
-        float2 mv[kU];
-        float2 ov[kU];
 #pragma unroll
-        for (int u = 0; u < kU; ++u) {
-            const int64_t s = i + u * WAVES;
-            mv[u] = *reinterpret_cast<const float2*>(ml + 2 * s);
-            ov[u] = has ? o[s * (D / 2)] : make_float2(0.0f, 0.0f);
-        }
-#pragma unroll
-        for (int u = 0; u < kU; ++u) {
-            const float e = exp2f(mv[u].x - M);
-            L = __builtin_fmaf(e, mv[u].y, L);
-            acc.x = __builtin_fmaf(e, ov[u].x, acc.x);
-            acc.y = __builtin_fmaf(e, ov[u].y, acc.y);
-        }
+    for (int u = 0; u < kU; ++u) {
+        const float e = exp2f(mv[u].x - M);
+        L = __builtin_fmaf(e, mv[u].y, L);
+        acc.x = __builtin_fmaf(e, ov[u].x, acc.x);
+        acc.y = __builtin_fmaf(e, ov[u].y, acc.y);
     }
-    for (; i < n_split; i += WAVES) {
-        const float2 mv = *reinterpret_cast<const float2*>(ml + 2 * i);
-        const float2 ov = has ? o[i * (D / 2)] : make_float2(0.0f, 0.0f);
-        const float e = exp2f(mv.x - M);
-        L = __builtin_fmaf(e, mv.y, L);
-        acc.x = __builtin_fmaf(e, ov.x, acc.x);
-        acc.y = __builtin_fmaf(e, ov.y, acc.y);
+    for (int64_t i = w + static_cast<int64_t>(kU) * WAVES; i < n_part; i += WAVES) {
+        const float2 m2 = *reinterpret_cast<const float2*>(ml + 2 * i);
+        const float2 o2 = has ? o[i * (D / 2)] : make_float2(0.0f, 0.0f);
+        const float e = exp2f(m2.x - M);
+        L = __builtin_fmaf(e, m2.y, L);
+        acc.x = __builtin_fmaf(e, o2.x, acc.x);
+        acc.y = __builtin_fmaf(e, o2.y, acc.y);
     }
     red_o[w][l] = acc;
     if (l == 0) red_l[w] = L;
@@ -122,25 +119,21 @@ AttendPlan plan_attend(int64_t B, int Hq, int Hkv, int64_t n_quant, int64_t n_re
     spw = std::max(spw, std::min<int64_t>(9, longer));
     // The generic kernel (head_dims other than 64 and 128) has no fixed cost
     // to amortize and is latency-bound per lane: one 64-token chunk per wave.
-    // (The workspace query plans head_dim 256, so it bounds this plan too.)
     if (head_dim != 64 && head_dim != 128) spw = std::min<int64_t>(spw, 2);
     AttendPlan p;
     p.steps_q = steps_q;
     p.steps_per_wave = spw;
     p.n_split = (steps + spw - 1) / spw;
     const size_t rows = static_cast<size_t>(B) * static_cast<size_t>(Hq) * static_cast<size_t>(p.n_split);
-    const size_t o_bytes = (rows * head_dim * sizeof(float) + 255) & ~static_cast<size_t>(255);
-    p.workspace_bytes = o_bytes + rows * 2 * sizeof(float);
+    p.ml_offset = (rows * head_dim * sizeof(float) + 255) & ~static_cast<size_t>(255);
+    p.workspace_bytes = p.ml_offset + rows * 2 * sizeof(float);
     return p;
 }
 
-// The partial kernel, then the combine.  The workspace holds the o rows
-// (256-byte aligned), then the (m, l) pairs.
+// The partial kernel, then the combine.
 hipError_t launch_decode_attend(const AttendArgs& a, const AttendPlan& p, hipStream_t stream) {
     float* ws_o = static_cast<float*>(a.workspace);
-    const size_t rows = static_cast<size_t>(a.B) * a.Hq * p.n_split;
-    const size_t o_bytes = (rows * a.head_dim * sizeof(float) + 255) & ~static_cast<size_t>(255);
-    float* ws_ml = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + o_bytes);
+    float* ws_ml = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + p.ml_offset);
     if (a.head_dim != 64 && a.head_dim != 128) return launch_attend_generic(a, p, ws_o, ws_ml, stream);
     hipError_t e;
     if (a.bf16) e = launch_attend_partial_bf16(a, p, ws_o, ws_ml, stream);

@@ -140,6 +140,42 @@ __device__ __forceinline__ float kscale_factor(int c) {
     else return __builtin_ldexpf(1.0f, -(BF ? min(2 * (c & 3), 4) : 2 * (c & 3)));
 }
 
+// bfloat16 caches at 4 bits take another route to the key and value
+// operands: the two nibbles of every byte of a code word are split into
+// byte lanes (one AND, and one shift and AND, per word), each byte becomes
+// an fp32 integer c in one v_cvt_f32_ubyte*, and the element is
+// RN32(c s + z) rounded to bfloat16 (no magic offset, so zero is used as
+// stored).  Channels then pair as (2j, 2j+1), so the query and the
+// residual key operands keep their natural channel order on this route.
+template <int BITS, bool BF> constexpr bool kByteCodes = BF && BITS == 4;
+// The offset the staged zero absorbs: M for the magic-number routes, 0 for
+// the byte route.
+template <int BITS, bool BF> constexpr float kCodeOffset = kByteCodes<BITS, BF> ? 0.0f : kMagicValue<BF>;
+
+// Byte k of x as an exact fp32 integer (one v_cvt_f32_ubyte{k}).
+__device__ __forceinline__ float byte_f32(uint32_t x, int k) {
+    return static_cast<float>(static_cast<uint8_t>(x >> (8 * k)));
+}
+
+// The nibbles of a code word split into byte lanes: even nibbles (lo) and
+// odd ones (hi).  The empty asm hides the masks from the optimizer, which
+// would otherwise fold each later byte extraction into a bit-field extract
+// plus a conversion instead of one v_cvt_f32_ubyte{k}.
+__device__ __forceinline__ void split_nibbles(uint32_t w, uint32_t& lo, uint32_t& hi) {
+    lo = w & 0x0F0F0F0Fu;
+    hi = (w >> 4) & 0x0F0F0F0Fu;
+    __asm__("" : "+v"(lo), "+v"(hi));
+}
+
+// Two fp32 values rounded to one bfloat16 pair (v_cvt_pk_bf16_f32).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
+    bf16x2_t r;
+    r[0] = static_cast<__bf16>(a);
+    r[1] = static_cast<__bf16>(b);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
 // code * scale + zero as one mixed-precision FMA with an fp16 result:
 // c16 = 1024 + code exactly and zp = RN32(zero - 1024 s), so the result is
 // code*s + zero up to 2^-24 (|zero| + 1024 s) plus the fp16 rounding (the
@@ -153,11 +189,8 @@ __device__ __forceinline__ float kscale_factor(int c) {
 template <bool BF>
 __device__ __forceinline__ uint32_t deq2(uint32_t pair, float s0, float z0, float s1, float z1) {
     if constexpr (BF) {
-        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-        bf16x2_t r;
-        r[0] = static_cast<__bf16>(__builtin_fmaf(__uint_as_float(pair << 16), s0, z0));
-        r[1] = static_cast<__bf16>(__builtin_fmaf(__uint_as_float(pair & 0xffff0000u), s1, z1));
-        return __builtin_bit_cast(uint32_t, r);
+        return bf16_pair(__builtin_fmaf(__uint_as_float(pair << 16), s0, z0),
+                         __builtin_fmaf(__uint_as_float(pair & 0xffff0000u), s1, z1));
     } else {
         const half2_t c = as_h2(pair);
         half2_t r;
@@ -369,9 +402,14 @@ constexpr float kSlack = 8.0f;
 // MASK, tokens at or past `limit` (step-relative) get probability 0.  The
 // scale c2 = softmax_scale * log2(e) is positive, so the max is taken over
 // the raw scores and scaled once.
+// fp16: P is rounded to fp16 (relative 2^-11) and `lo` is unused.  bfloat16
+// would lose 2^-9 that way, the largest error of the bfloat16 attend, so P
+// is split: the high part is p with its low 16 bits cleared (a bfloat16,
+// truncated), the low part the exact remainder rounded to bfloat16; PV
+// takes one MFMA for each and P keeps 2^-16 relative.
 template <bool MASK, bool BF>
 __device__ __forceinline__ Frag softmax_step(const float4_t (&acc_s)[2], SoftState& st, float c2,
-                                             int limit, int q) {
+                                             int limit, int q, Frag& lo) {
     float sv[8];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
@@ -402,8 +440,10 @@ __device__ __forceinline__ Frag softmax_step(const float4_t (&acc_s)[2], SoftSta
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         if constexpr (BF) {
-            bp.b[2 * j] = static_cast<__bf16>(sv[2 * j]);
-            bp.b[2 * j + 1] = static_cast<__bf16>(sv[2 * j + 1]);
+            const uint32_t u0 = __float_as_uint(sv[2 * j]), u1 = __float_as_uint(sv[2 * j + 1]);
+            bp.u[j] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);        // high halves
+            lo.u[j] = bf16_pair(sv[2 * j] - __uint_as_float(u0 & 0xffff0000u),
+                                sv[2 * j + 1] - __uint_as_float(u1 & 0xffff0000u));
         } else {
             half2_t h;
             h[0] = static_cast<_Float16>(sv[2 * j]);
@@ -416,9 +456,9 @@ __device__ __forceinline__ Frag softmax_step(const float4_t (&acc_s)[2], SoftSta
 
 template <bool BF>
 __device__ __forceinline__ Frag softmax_any(const float4_t (&acc_s)[2], SoftState& st, float c2,
-                                            int limit, int q) {
-    if (limit >= kStep) return softmax_step<false, BF>(acc_s, st, c2, limit, q);
-    return softmax_step<true, BF>(acc_s, st, c2, limit, q);
+                                            int limit, int q, Frag& lo) {
+    if (limit >= kStep) return softmax_step<false, BF>(acc_s, st, c2, limit, q, lo);
+    return softmax_step<true, BF>(acc_s, st, c2, limit, q, lo);
 }
 
 // One step of store tokens [t0, t0 + 32), tokens at or past n_quant masked.
@@ -427,7 +467,7 @@ __device__ __forceinline__ void store_step(const StepLoad& L, Smem<D>& sm, SoftS
                                            int t0, int n_quant, float c2,
                                            int l, int n, int q) {
     // ---- stage this step's metadata in LDS (zero' = zero - M * scale')
-    constexpr float kM = kMagicValue<BF>;
+    constexpr float kM = kCodeOffset<BITS, BF>;
     constexpr int kMPT = D / G;                 // value groups per token
     constexpr int kCPG = Geo<D>::kCPG, kKB = Geo<D>::kKB, kPV = Geo<D>::kPV;
     lds_order();
@@ -469,16 +509,29 @@ __device__ __forceinline__ void store_step(const StepLoad& L, Smem<D>& sm, SoftS
         const Frag bq = query_frag(sm, kb, l);
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
-            uint32_t pr[4];
-            code_pairs<BITS, BF>(L.kw[blk][kb], kb & 1, pr);
             Frag ka;
+            if constexpr (kByteCodes<BITS, BF>) {
+                // channels (2j, 2j+1) of the unit: byte j of the even and odd nibbles
+                uint32_t lo, hi;
+                split_nibbles(L.kw[blk][kb], lo, hi);
+                const float sc[8] = {sl[0], sl[1], sl[2], sl[3], sh[0], sh[1], sh[2], sh[3]};
+                const float zc[8] = {zl[0], zl[1], zl[2], zl[3], zh[0], zh[1], zh[2], zh[3]};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) ka.u[j] = deq2<BF>(pr[j], sl[j], zl[j], sh[j], zh[j]);
+                for (int j = 0; j < 4; ++j)
+                    ka.u[j] = bf16_pair(__builtin_fmaf(byte_f32(lo, j), sc[2 * j], zc[2 * j]),
+                                        __builtin_fmaf(byte_f32(hi, j), sc[2 * j + 1], zc[2 * j + 1]));
+            } else {
+                uint32_t pr[4];
+                code_pairs<BITS, BF>(L.kw[blk][kb], kb & 1, pr);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) ka.u[j] = deq2<BF>(pr[j], sl[j], zl[j], sh[j], zh[j]);
+            }
             acc_s[blk] = mfma<BF>(ka, bq, acc_s[blk]);
         }
     }
 
-    const Frag bp = softmax_any<BF>(acc_s, st, c2, n_quant - t0, q);
+    Frag bp_lo;
+    const Frag bp = softmax_any<BF>(acc_s, st, c2, n_quant - t0, q, bp_lo);
 
     // ---- O^T += V^T P^T: MFMA i covers channels kPV*m + i, m = 0..15.  Slot s
     // of lane (q, m) is channel kPV*m + i of step token pv_token(q, s).
@@ -489,6 +542,27 @@ __device__ __forceinline__ void store_step(const StepLoad& L, Smem<D>& sm, SoftS
     const float4 vzb = *reinterpret_cast<const float4*>(&sm.vz[vg][16 + 4 * q]);
     const float vsc[8] = {vsa.x, vsa.y, vsa.z, vsa.w, vsb.x, vsb.y, vsb.z, vsb.w};
     const float vzp[8] = {vza.x, vza.y, vza.z, vza.w, vzb.x, vzb.y, vzb.z, vzb.w};
+    if constexpr (kByteCodes<BITS, BF>) {
+        // token slot s: the even channels' codes in the bytes of vlo, the odd
+        // ones' in vhi; channel i of the lane's kPV is byte i/2 of one of them
+        uint32_t vlo[8], vhi[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) split_nibbles(L.vw[t], vlo[t], vhi[t]);
+#pragma unroll
+        for (int i = 0; i < kPV; ++i) {
+            Frag va;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t w0 = (i & 1) ? vhi[2 * j] : vlo[2 * j];
+                const uint32_t w1 = (i & 1) ? vhi[2 * j + 1] : vlo[2 * j + 1];
+                va.u[j] = bf16_pair(__builtin_fmaf(byte_f32(w0, i >> 1), vsc[2 * j], vzp[2 * j]),
+                                    __builtin_fmaf(byte_f32(w1, i >> 1), vsc[2 * j + 1], vzp[2 * j + 1]));
+            }
+            st.acc_o[i] = mfma<BF>(va, bp, st.acc_o[i]);
+            st.acc_o[i] = mfma<BF>(va, bp_lo, st.acc_o[i]);
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < kPV; ++i) {
         // code of channel i of the lane's kPV (4-bit: nibble i; 2-bit: field i)
@@ -504,6 +578,7 @@ __device__ __forceinline__ void store_step(const StepLoad& L, Smem<D>& sm, SoftS
             va.u[j] = deq2<BF>(pr, vsc[2 * j], vzp[2 * j], vsc[2 * j + 1], vzp[2 * j + 1]);
         }
         st.acc_o[i] = mfma<BF>(va, bp, st.acc_o[i]);
+        if constexpr (BF) st.acc_o[i] = mfma<BF>(va, bp_lo, st.acc_o[i]);
     }
 }
 
@@ -514,7 +589,7 @@ __device__ __forceinline__ int ring_row(int tok, int head, int ring) {
     return r >= ring ? r - ring : r;
 }
 
-template <bool BF, int D>
+template <int BITS, bool BF, int D>
 __device__ __forceinline__ void residual_step(const uint16_t* kr, const uint16_t* vr, const Smem<D>& sm,
                                               SoftState& st, int t0, int n_res, float c2,
                                               int l, int n, int q, int head, int ring) {
@@ -536,15 +611,20 @@ __device__ __forceinline__ void residual_step(const uint16_t* kr, const uint16_t
             Frag ka;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int c0 = 8 * kb + j, c1 = 8 * kb + j + 4;
-                const uint32_t s0 = (c0 & 1) ? 0x0302u : 0x0100u;
-                const uint32_t s1 = (c1 & 1) ? 0x0706u : 0x0504u;
-                ka.u[j] = __builtin_amdgcn_perm(rn[c1 >> 1], rn[c0 >> 1], (s1 << 16) | s0);
+                if constexpr (kByteCodes<BITS, BF>) {
+                    ka.u[j] = rn[4 * kb + j];             // natural order: channels 8kb + 2j, + 1
+                } else {
+                    const int c0 = 8 * kb + j, c1 = 8 * kb + j + 4;
+                    const uint32_t s0 = (c0 & 1) ? 0x0302u : 0x0100u;
+                    const uint32_t s1 = (c1 & 1) ? 0x0706u : 0x0504u;
+                    ka.u[j] = __builtin_amdgcn_perm(rn[c1 >> 1], rn[c0 >> 1], (s1 << 16) | s0);
+                }
             }
             acc_s[blk] = mfma<BF>(ka, query_frag(sm, kb, l), acc_s[blk]);
         }
     }
-    const Frag bp = softmax_any<BF>(acc_s, st, c2, n_res - t0, q);
+    Frag bp_lo;
+    const Frag bp = softmax_any<BF>(acc_s, st, c2, n_res - t0, q, bp_lo);
     // V rows: lane (q, m=n) takes channels kPV*n .. kPV*n + kPV - 1 of its 8 tokens
     uint32_t vw[8][kPV / 2];
 #pragma unroll
@@ -566,6 +646,7 @@ __device__ __forceinline__ void residual_step(const uint16_t* kr, const uint16_t
 #pragma unroll
         for (int j = 0; j < 4; ++j) va.u[j] = __builtin_amdgcn_perm(vw[2 * j + 1][i >> 1], vw[2 * j][i >> 1], sel);
         st.acc_o[i] = mfma<BF>(va, bp, st.acc_o[i]);
+        if constexpr (BF) st.acc_o[i] = mfma<BF>(va, bp_lo, st.acc_o[i]);
     }
 }
 
@@ -662,11 +743,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(BF ? 2 : KIV
         for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                // slots (2j, 2j+1) = channels (8kb + j, 8kb + j + 4) of the lane's window
-                const int c0 = 8 * kb + j, c1 = 8 * kb + j + 4;
-                const uint32_t s0 = (c0 & 1) ? 0x0302u : 0x0100u;
-                const uint32_t s1 = (c1 & 1) ? 0x0706u : 0x0504u;
-                bq[kb].u[j] = __builtin_amdgcn_perm(qn[c1 >> 1], qn[c0 >> 1], (s1 << 16) | s0);
+                if constexpr (kByteCodes<BITS, BF>) {
+                    // slots (2j, 2j+1) = channels (8kb + 2j, 8kb + 2j + 1)
+                    bq[kb].u[j] = qn[4 * kb + j];
+                } else {
+                    // slots (2j, 2j+1) = channels (8kb + j, 8kb + j + 4) of the lane's window
+                    const int c0 = 8 * kb + j, c1 = 8 * kb + j + 4;
+                    const uint32_t s0 = (c0 & 1) ? 0x0302u : 0x0100u;
+                    const uint32_t s1 = (c1 & 1) ? 0x0706u : 0x0504u;
+                    bq[kb].u[j] = __builtin_amdgcn_perm(qn[c1 >> 1], qn[c0 >> 1], (s1 << 16) | s0);
+                }
             }
 #pragma unroll
         for (int kb = 0; kb < kKB; ++kb) sm.bq[kb][l] = make_uint4(bq[kb].u[0], bq[kb].u[1], bq[kb].u[2], bq[kb].u[3]);
@@ -697,7 +783,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(BF ? 2 : KIV
         const uint16_t* kr = a.k_res + bkv * a.res_bh_stride;
         const uint16_t* vr = a.v_res + bkv * a.res_bh_stride;
         for (int t0 = r0; t0 < r1; t0 += kStep)
-            residual_step<BF, D>(kr, vr, sm, st, t0, r1, c2, l, n, q, a.res_head, a.res_ring);
+            residual_step<BITS, BF, D>(kr, vr, sm, st, t0, r1, c2, l, n, q, a.res_head, a.res_ring);
     }
 
     // ---- partial (m, l, o) of head n: lane (q, n) holds channels
@@ -724,8 +810,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(BF ? 2 : KIV
 // ---------------------------------------------------------------------------
 // Host side: launch the partial kernel of one instantiation, and the dispatch
 // over (bits, group size, query heads per kv head) for one metadata width
-// MB and element format BF.  Each translation unit that calls launch_partials
-// instantiates its own set of kernels.
+// MB and element format BF.  Each translation unit that calls
+// launch_partials instantiates its own set of kernels.
 // ---------------------------------------------------------------------------
 template <int BITS, int GQA, int G, int MB, bool BF, int D>
 hipError_t launch_partial(const AttendArgs& a, const AttendPlan& p, float* ws_o, float* ws_ml,

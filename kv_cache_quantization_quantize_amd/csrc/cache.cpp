@@ -217,15 +217,19 @@ int kivi_cache_attend(const kivi_cache* cache, int32_t layer, const uint16_t* q,
 
 size_t kivi_cache_attend_workspace_bytes(const kivi_cache* cache, int32_t Hq) {
     if (!cache || !valid(&cache->cfg) || Hq <= 0) return 0;
-    // the largest need over every (quantized, fp16) split the cache can reach
+    // An attend plan depends on the token counts only through the number of
+    // 32-token steps, ceil(n_quant / 32) + ceil(n_res / 32).  A cache's
+    // attends have n_quant <= store_capacity and 1 <= n_res <= ring, so the
+    // largest plan over step counts 1 .. steps(capacity) + steps(ring) covers
+    // every call the cache can make: at most 2^19 + 2^19 cheap plans.
+    const int32_t flags = cache->cfg.bf16 ? KIVI_ATTEND_BF16 : 0;
+    const int64_t max_steps = (cache->cfg.store_capacity + 31) / 32 + (cache->ring + 31) / 32;
     size_t need = 0;
-    const int64_t F = cache->cfg.flush_tokens;
-    for (int64_t nq = 0; nq <= cache->cfg.store_capacity; nq += F)
-        for (int64_t nr = 1; nr <= cache->ring; ++nr) {
-            const size_t b = kivi_decode_attend_workspace_bytes(cache->cfg.batch, Hq, cache->cfg.kv_heads,
-                                                                nq, nr);
-            need = b > need ? b : need;
-        }
+    for (int64_t steps = 1; steps <= max_steps; ++steps) {
+        const size_t b = kivi_decode_attend_workspace_bytes(cache->cfg.batch, Hq, cache->cfg.kv_heads,
+                                                            32 * steps, 0, cache->cfg.head_dim, flags);
+        need = b > need ? b : need;
+    }
     return need;
 }
 

@@ -82,11 +82,13 @@ struct AttendArgs {
 };
 
 // Split of the token axis chosen for an attend shape; the workspace holds
-// one (m, l, o[128]) partial per (sequence, query head, split).
+// one (m, l, o[head_dim]) partial per (sequence, query head, split): the o
+// rows first, then the (m, l) pairs at ml_offset.
 struct AttendPlan {
     int64_t steps_q;               // 32-token steps over store tokens [0, n_quant)
     int64_t steps_per_wave;        // consecutive steps of store-then-residual per wave
     int64_t n_split;               // waves per (sequence, kv head)
+    size_t ml_offset;              // bytes from the workspace start to the (m, l) pairs
     size_t workspace_bytes;
 };
 AttendPlan plan_attend(int64_t B, int Hq, int Hkv, int64_t n_quant, int64_t n_res, bool varlen,
@@ -97,7 +99,7 @@ hipError_t launch_value_flush(const FlushArgs& a, hipStream_t stream);
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t stream);
 hipError_t launch_decode_attend(const AttendArgs& a, const AttendPlan& p, hipStream_t stream);
 // the attend at head_dims other than 64 and 128 (groups of 32, binary32
-// scale/zero): partials and combine
+// scale/zero): partials and combine (one wave per workgroup, two launches)
 hipError_t launch_attend_generic(const AttendArgs& a, const AttendPlan& p, float* ws_o, float* ws_ml,
                                  hipStream_t stream);
 // head_dims other than 64, 128 and 256 (multiples of 16 up to 256, groups of 32)
@@ -128,5 +130,8 @@ int decode_attend_entry(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
 int hip_status(hipError_t e);
 
 hipError_t launch_calib_copy(const void* src, void* dst, size_t n_bytes, hipStream_t stream);
+hipError_t launch_calib_read(const void* src, size_t n_bytes, uint32_t* sink, hipStream_t stream);
+hipError_t launch_calib_write(void* dst, size_t n_bytes, hipStream_t stream);
+hipError_t launch_calib_mix(const void* src, size_t n_bytes, void* dst, hipStream_t stream);
 
 }  // namespace kivi

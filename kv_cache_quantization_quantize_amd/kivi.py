@@ -20,6 +20,8 @@ KIVI_KEYS = 0
 KIVI_VALUES = 1
 KIVI_META_F32 = 0
 KIVI_META_F16 = 1
+KIVI_ATTEND_BF16 = 1
+KIVI_ATTEND_VARLEN = 2
 HEAD_DIM = 128
 GROUP = 32
 
@@ -29,7 +31,8 @@ EXPORTS = (
     "kivi_quantize_keys_bf16", "kivi_quantize_values_bf16", "kivi_dequantize_bf16",
     "kivi_decode_attend", "kivi_decode_attend_varlen", "kivi_decode_attend_workspace_bytes",
     "kivi_decode_attend_bf16", "kivi_decode_attend_varlen_bf16",
-    "kivi_status_string", "kivi_last_hip_error", "kivi_calib_copy",
+    "kivi_status_string", "kivi_last_hip_error", "kivi_calib_copy", "kivi_calib_read",
+    "kivi_calib_write", "kivi_calib_mix",
     "kivi_cache_device_bytes", "kivi_cache_init", "kivi_cache_prefill", "kivi_cache_append",
     "kivi_cache_attend", "kivi_cache_attend_workspace_bytes", "kivi_cache_end_step",
 )
@@ -104,12 +107,15 @@ def lib() -> ctypes.CDLL:
                                                 vp, i64, ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
         L.kivi_decode_attend_bf16.argtypes = L.kivi_decode_attend.argtypes
         L.kivi_decode_attend_varlen_bf16.argtypes = L.kivi_decode_attend_varlen.argtypes
-        L.kivi_decode_attend_workspace_bytes.argtypes = [i64, i32, i32, i64, i64]
+        L.kivi_decode_attend_workspace_bytes.argtypes = [i64, i32, i32, i64, i64, i32, i32]
         L.kivi_decode_attend_workspace_bytes.restype = ctypes.c_size_t
         L.kivi_status_string.argtypes = [ctypes.c_int]
         L.kivi_status_string.restype = ctypes.c_char_p
         L.kivi_last_hip_error.argtypes = []
         L.kivi_calib_copy.argtypes = [vp, vp, ctypes.c_size_t, vp]
+        L.kivi_calib_read.argtypes = [vp, ctypes.c_size_t, vp, vp]
+        L.kivi_calib_write.argtypes = [vp, ctypes.c_size_t, vp]
+        L.kivi_calib_mix.argtypes = [vp, ctypes.c_size_t, vp, vp]
         cp, cfgp = ctypes.POINTER(CCache), ctypes.POINTER(CCacheConfig)
         L.kivi_cache_device_bytes.argtypes = [cfgp]
         L.kivi_cache_device_bytes.restype = ctypes.c_size_t
@@ -124,7 +130,8 @@ def lib() -> ctypes.CDLL:
                      "kivi_quantize_keys_bf16", "kivi_quantize_values_bf16", "kivi_dequantize_bf16",
                      "kivi_decode_attend", "kivi_decode_attend_varlen", "kivi_last_hip_error",
                      "kivi_decode_attend_bf16", "kivi_decode_attend_varlen_bf16",
-                     "kivi_calib_copy", "kivi_cache_init", "kivi_cache_prefill", "kivi_cache_append",
+                     "kivi_calib_copy", "kivi_calib_read", "kivi_calib_write", "kivi_calib_mix",
+                     "kivi_cache_init", "kivi_cache_prefill", "kivi_cache_append",
                      "kivi_cache_attend", "kivi_cache_end_step"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -158,6 +165,31 @@ def _need_query(q: torch.Tensor) -> None:
     if q.dtype not in (torch.float16, torch.bfloat16) or not q.is_cuda or q.dim() != 3 \
             or not q.is_contiguous():
         raise ValueError("q must be a contiguous float16 or bfloat16 device tensor [B][Hq][head_dim]")
+
+
+def _kv_heads(q: torch.Tensor, k_store: "Store", v_store: "Store") -> int:
+    """Hkv of an attend call, after checking that q and both stores agree:
+    the C ABI reads q, the residual rows and out at the stores' head_dim and
+    B * Hkv slabs, so a mismatch here would be an out-of-bounds access."""
+    if q.dim() != 3:
+        raise ValueError("q must be [B][Hq][head_dim]")
+    B, Hq, D = q.shape
+    for st, name in ((k_store, "k_store"), (v_store, "v_store")):
+        if st.head_dim != D:
+            raise ValueError(f"q has head_dim {D} but {name} has {st.head_dim}")
+    if k_store.BH != v_store.BH:
+        raise ValueError("k_store and v_store must have the same number of slabs")
+    if B == 0:
+        return 1
+    if k_store.BH % B != 0:
+        raise ValueError(f"the stores' {k_store.BH} slabs are not B={B} sequences of kv heads")
+    return k_store.BH // B
+
+
+def _need_out(out: torch.Tensor, B: int, Hq: int, D: int) -> None:
+    if not (out.dtype == torch.float32 and out.is_cuda and out.is_contiguous()
+            and tuple(out.shape) == (B, Hq, D)):
+        raise ValueError(f"out must be a contiguous float32 device tensor of shape ({B}, {Hq}, {D})")
 
 
 def _need_residual(q: torch.Tensor, k_res: torch.Tensor, v_res: torch.Tensor) -> None:
@@ -253,8 +285,17 @@ def dequantize(store: Store, token_begin: int, n_tokens: int, out: torch.Tensor 
     return out
 
 
-def attend_workspace_bytes(B: int, Hq: int, Hkv: int, n_quant: int, n_res: int) -> int:
-    return int(lib().kivi_decode_attend_workspace_bytes(B, Hq, Hkv, n_quant, n_res))
+def attend_workspace_bytes(B: int, Hq: int, Hkv: int, n_quant: int, n_res: int,
+                           head_dim: int = HEAD_DIM, bf16: bool = False, varlen: bool = False) -> int:
+    """kivi_decode_attend_workspace_bytes for the attend call with these
+    arguments (the varlen calls: their max_n_quant / max_n_res)."""
+    flags = (KIVI_ATTEND_BF16 if bf16 else 0) | (KIVI_ATTEND_VARLEN if varlen else 0)
+    return int(lib().kivi_decode_attend_workspace_bytes(B, Hq, Hkv, n_quant, n_res, head_dim, flags))
+
+
+def attend_workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """A new attend workspace of nbytes (its contents do not matter)."""
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
 def decode_attend(q: torch.Tensor, k_store: Store, v_store: Store, n_quant: int,
@@ -264,18 +305,17 @@ def decode_attend(q: torch.Tensor, k_store: Store, v_store: Store, n_quant: int,
     """kivi_decode_attend: fp32 [B][Hq][128] attention of one query token per
     sequence over store tokens [0, n_quant) then residual tokens [0, n_res)
     (kivi_decode_attend_bf16 when q is bfloat16; the residual then is too)."""
+    Hkv = _kv_heads(q, k_store, v_store)
     _need_query(q)
     B, Hq, D = q.shape
-    Hkv = k_store.BH // B if B else 1
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
-    if not (out.dtype == torch.float32 and out.is_contiguous() and tuple(out.shape) == (B, Hq, D)):
-        raise ValueError("out must be a contiguous float32 [B][Hq][head_dim] tensor")
-    need = attend_workspace_bytes(B, Hq, Hkv, n_quant, n_res) if B else 0
+    _need_out(out, B, Hq, D)
     if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+        need = attend_workspace_bytes(B, Hq, Hkv, n_quant, n_res, D, q.dtype == torch.bfloat16) if B else 0
+        workspace = attend_workspace(need, q.device)
     if n_res > 0:
         _need_residual(q, k_res, v_res)
     ks, vs = k_store.c(), v_store.c()
@@ -297,21 +337,21 @@ def decode_attend_varlen(q: torch.Tensor, k_store: Store, v_store: Store, n_quan
     """kivi_decode_attend_varlen: like decode_attend, with device int32 [B]
     per-sequence lengths n_quant[b] <= max_n_quant and n_res[b] <= max_n_res
     (kivi_decode_attend_varlen_bf16 when q is bfloat16)."""
+    Hkv = _kv_heads(q, k_store, v_store)
     _need_query(q)
     B, Hq, D = q.shape
     for t, name in ((n_quant, "n_quant"), (n_res, "n_res")):
         if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous() or t.numel() != B:
             raise ValueError(f"{name} must be a contiguous int32 device tensor of B elements")
-    Hkv = k_store.BH // B if B else 1
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
-    if not (out.dtype == torch.float32 and out.is_contiguous() and tuple(out.shape) == (B, Hq, D)):
-        raise ValueError("out must be a contiguous float32 [B][Hq][head_dim] tensor")
-    need = attend_workspace_bytes(B, Hq, Hkv, max_n_quant, max_n_res) if B else 0
+    _need_out(out, B, Hq, D)
     if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+        need = attend_workspace_bytes(B, Hq, Hkv, max_n_quant, max_n_res, D, q.dtype == torch.bfloat16,
+                                      varlen=True) if B else 0
+        workspace = attend_workspace(need, q.device)
     if max_n_res > 0:
         _need_residual(q, k_res, v_res)
     ks, vs = k_store.c(), v_store.c()
@@ -326,11 +366,38 @@ def decode_attend_varlen(q: torch.Tensor, k_store: Store, v_store: Store, n_quan
     return out
 
 
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
 def calib_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
     """kivi_calib_copy: device-to-device streaming copy (bandwidth ceiling)."""
-    n = src.numel() * src.element_size()
-    assert dst.numel() * dst.element_size() >= n
+    n = _nbytes(src)
+    if _nbytes(dst) < n:
+        raise ValueError("dst is smaller than src")
     _check(lib().kivi_calib_copy(src.data_ptr(), dst.data_ptr(), n, _stream(stream)), "kivi_calib_copy")
+
+
+def calib_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """kivi_calib_read: read every byte of src (read-only ceiling)."""
+    if _nbytes(sink) < 16:
+        raise ValueError("sink must hold at least 16 bytes")
+    _check(lib().kivi_calib_read(src.data_ptr(), _nbytes(src), sink.data_ptr(), _stream(stream)),
+           "kivi_calib_read")
+
+
+def calib_write(dst: torch.Tensor, stream=None) -> None:
+    """kivi_calib_write: write every byte of dst (write-only ceiling)."""
+    _check(lib().kivi_calib_write(dst.data_ptr(), _nbytes(dst), _stream(stream)), "kivi_calib_write")
+
+
+def calib_mix(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    """kivi_calib_mix: read src, write 3/8 of its size to dst (the 4-bit
+    flush's read:write ratio)."""
+    n = _nbytes(src)
+    if _nbytes(dst) < n * 3 // 8:
+        raise ValueError("dst must hold 3/8 of src's bytes")
+    _check(lib().kivi_calib_mix(src.data_ptr(), n, dst.data_ptr(), _stream(stream)), "kivi_calib_mix")
 
 
 class Cache:
@@ -430,6 +497,9 @@ class Cache:
     def attend(self, layer: int, q: torch.Tensor, out: torch.Tensor | None = None,
                workspace: torch.Tensor | None = None, softmax_scale: float | None = None,
                stream=None) -> torch.Tensor:
+        if q.dim() != 3 or q.shape[0] != self.cfg.batch or q.shape[2] != self.head_dim:
+            raise ValueError(f"q must be [{self.cfg.batch}][Hq][{self.head_dim}] for this cache, "
+                             f"got {tuple(q.shape)}")
         _need_query(q)
         self._need_dtype(q, "q")
         B, Hq, D = q.shape
@@ -437,9 +507,9 @@ class Cache:
             softmax_scale = 1.0 / math.sqrt(D)
         if out is None:
             out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+        _need_out(out, B, Hq, D)
         if workspace is None:
-            workspace = torch.empty(max(self.attend_workspace_bytes(Hq), 256), dtype=torch.uint8,
-                                    device=q.device)
+            workspace = attend_workspace(self.attend_workspace_bytes(Hq), q.device)
         _check(lib().kivi_cache_attend(ctypes.byref(self.c), layer, q.data_ptr(), Hq, float(softmax_scale),
                                        out.data_ptr(), workspace.data_ptr(),
                                        workspace.numel() * workspace.element_size(), _stream(stream)),

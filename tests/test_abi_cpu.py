@@ -253,7 +253,7 @@ def test_cache_init_checks_buffer_and_step_order():
     assert L.kivi_cache_prefill(ctypes.byref(c), FAKE + 8, FAKE, 300 * 128, 300, None) == -4
     assert c.length == 0
     assert L.kivi_cache_attend_workspace_bytes(ctypes.byref(c), 8) >= \
-        L.kivi_decode_attend_workspace_bytes(1, 8, 2, 256, 96)
+        L.kivi_decode_attend_workspace_bytes(1, 8, 2, 256, 96, 128, 0)
 
 
 def test_bf16_cache_config():
@@ -279,3 +279,104 @@ def test_cache_with_binary16_metadata_halves_the_metadata_sections():
     assert L.kivi_cache_init(ctypes.byref(c), ctypes.byref(f16), FAKE, n16) == 0
     assert c.k_store.meta_format == kivi.KIVI_META_F16 == c.v_store.meta_format
     assert c.k_store.meta_bh_stride == 8 * 128 and c.v_store.meta_bh_stride == 256 * 4
+
+
+def test_attend_workspace_is_the_call_s_own_plan():
+    """The query sizes the call it names: head_dim and format are arguments,
+    so a head_dim-128 call is not sized for head_dim 256 (the old bound asked
+    about 49 MB at 32 x 16384 and 277 GB at 2^24 tokens), and the
+    variable-length plan's finer splits are only paid by varlen calls."""
+    L = kivi.lib()
+    f = L.kivi_decode_attend_workspace_bytes
+    c5 = f(32, 32, 8, 16384, 128, 128, 0)
+    assert 0 < c5 < 16 * 2 ** 20                           # partials of a few MB
+    assert f(32, 32, 8, 16384, 128, 64, 0) < c5 < f(32, 32, 8, 16384, 128, 256, 0)
+    assert f(32, 32, 8, 16384, 128, 128, kivi.KIVI_ATTEND_VARLEN) >= c5
+    limit = f(32, 32, 8, (1 << 24) - 1, 128, 128, 0)
+    # at the token limit the call reads 256 x 2^24 x 192 B = 824 GB; its partials
+    # (4 heads x 520 B per wave of at most 64 steps of 6 KiB) are about 0.5% of that
+    assert limit < 5 * 2 ** 30
+    assert f(1, 32, 8, 2048, 128, 128, kivi.KIVI_ATTEND_BF16) > 0
+    for bad in ((32, 32, 8, 16384, 128, 100, 0), (32, 32, 8, 16384, 128, 128, 4),
+                (32, 32, 8, 0, 0, 128, 0), (0, 32, 8, 64, 0, 128, 0)):
+        assert f(*bad) == 0, bad
+    assert kivi.attend_workspace_bytes(32, 32, 8, 16384, 128) == c5
+
+
+def test_attend_rejects_a_workspace_one_byte_short():
+    L = kivi.lib()
+    k = _store(kivi.KIVI_KEYS, cap=64)
+    v = _store(kivi.KIVI_VALUES, cap=64)
+    need = L.kivi_decode_attend_workspace_bytes(1, 32, 8, 64, 16, 128, 0)
+    common = (FAKE, 1, 32, 8, ctypes.byref(k), ctypes.byref(v), 64, FAKE, FAKE, 16 * 128, 16, 0.088, FAKE, FAKE)
+    assert L.kivi_decode_attend(*common, need - 1, None) == -5
+
+
+def test_cache_workspace_query_is_fast_at_the_largest_capacity():
+    import time
+    L = kivi.lib()
+    F = 128
+    cfg = kivi.CCacheConfig(1, 32, 8, 4, 128, 32, 128, F, ((1 << 24) - 1) // F * F)
+    c = kivi.CCache()
+    t0 = time.perf_counter()
+    n = L.kivi_cache_attend_workspace_bytes(ctypes.byref(c), 32)   # not initialised: rejected
+    assert n == 0
+    assert L.kivi_cache_device_bytes(ctypes.byref(cfg)) > 0
+    assert L.kivi_cache_init(ctypes.byref(c), ctypes.byref(cfg), FAKE, 1 << 62) == 0
+    t0 = time.perf_counter()
+    n = L.kivi_cache_attend_workspace_bytes(ctypes.byref(c), 32)
+    dt = time.perf_counter() - t0
+    assert dt < 1.0, dt
+    # it covers the largest call the cache makes, and that call's plan
+    assert n >= L.kivi_decode_attend_workspace_bytes(32, 32, 8, cfg.store_capacity, 256, 128, 0)
+    assert n < 5 * 2 ** 30
+
+
+def test_python_attend_checks_shapes_before_any_launch():
+    """q, the stores and out must agree before anything reaches the C ABI:
+    the kernels read q and the residual rows and write out at the stores'
+    head_dim and B * Hkv slabs.  CPU tensors: the checks come first."""
+    import torch
+    ks = kivi.Store(kivi.KIVI_KEYS, 16, 64, 4, device="cpu")
+    vs = kivi.Store(kivi.KIVI_VALUES, 16, 64, 4, device="cpu")
+    ks64 = kivi.Store(kivi.KIVI_KEYS, 16, 64, 4, device="cpu", head_dim=64)
+    q = torch.zeros((2, 32, 128), dtype=torch.float16)
+    with pytest.raises(ValueError, match="head_dim"):
+        kivi.decode_attend(torch.zeros((2, 32, 64), dtype=torch.float16), ks, vs, 64, None, None, 0)
+    with pytest.raises(ValueError, match="head_dim"):
+        kivi.decode_attend(q, ks64, vs, 64, None, None, 0)
+    with pytest.raises(ValueError, match="slabs"):
+        kivi.decode_attend(torch.zeros((3, 32, 128), dtype=torch.float16), ks, vs, 64, None, None, 0)
+    with pytest.raises(ValueError, match="slabs"):
+        kivi.decode_attend(q, ks, kivi.Store(kivi.KIVI_VALUES, 8, 64, 4, device="cpu"), 64, None, None, 0)
+    with pytest.raises(ValueError, match="slabs"):
+        kivi.decode_attend_varlen(torch.zeros((3, 32, 128), dtype=torch.float16), ks, vs, None, 64,
+                                  None, None, None, 0)
+
+
+def test_python_cache_attend_checks_q_and_out():
+    import torch
+
+    class FakeCache(kivi.Cache):          # the checks only, no device buffer
+        def __init__(self):
+            self.cfg = kivi.CCacheConfig(2, 2, 8, 4, 128, 32, 64, 32, 256)
+            self.head_dim = 128
+            self.dtype = torch.float16
+    c = FakeCache()
+    with pytest.raises(ValueError, match="for this cache"):
+        c.attend(0, torch.zeros((3, 32, 128), dtype=torch.float16))
+    with pytest.raises(ValueError, match="for this cache"):
+        c.attend(0, torch.zeros((2, 32, 64), dtype=torch.float16))
+
+
+def test_calibration_kernels_validate_before_launch():
+    L = kivi.lib()
+    assert L.kivi_calib_read(None, 1024, FAKE, None) == -1
+    assert L.kivi_calib_read(FAKE, 1024, None, None) == -1
+    assert L.kivi_calib_read(FAKE + 8, 1024, FAKE, None) == -4
+    assert L.kivi_calib_write(FAKE, 1000, None) == -4
+    assert L.kivi_calib_mix(FAKE, 1024, FAKE + 4, None) == -4
+    assert L.kivi_calib_copy(FAKE, FAKE, 1 << 46, None) == -2     # past 2^31 - 1 workgroups
+    for fn in (lambda: L.kivi_calib_read(FAKE, 0, FAKE, None), lambda: L.kivi_calib_write(FAKE, 0, None),
+               lambda: L.kivi_calib_mix(FAKE, 0, FAKE, None), lambda: L.kivi_calib_copy(FAKE, FAKE, 0, None)):
+        assert fn() == 0                                          # empty: nothing to launch

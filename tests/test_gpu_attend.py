@@ -114,7 +114,7 @@ def test_edge_shapes(case):
 
 def test_workspace_too_small_is_rejected():
     c = _case(1, 32, 8, 64, 8, 4, seed=1)
-    need = kivi.attend_workspace_bytes(1, 32, 8, 64, 8)     # a bound over every head_dim
+    need = kivi.attend_workspace_bytes(1, 32, 8, 64, 8)     # this call's own plan
     assert need > 1024
     ws = torch.empty(1024, dtype=torch.uint8, device="cuda")   # below any plan's need
     with pytest.raises(kivi.KiviError):
@@ -136,7 +136,7 @@ def test_graph_replays_match_eager():
     x_new = synth.kv_tensor(BH, 32, keys=True, seed=7, device="cuda")
     ks2 = kivi.Store(kivi.KIVI_KEYS, BH, 64, 4)
     out = torch.empty((2, 32, D), dtype=torch.float32, device="cuda")
-    ws = torch.empty(kivi.attend_workspace_bytes(2, 32, 8, 1000, 64), dtype=torch.uint8, device="cuda")
+    ws = kivi.attend_workspace(kivi.attend_workspace_bytes(2, 32, 8, 1000, 64))
 
     def work():
         kivi.quantize_keys(x_new, ks2, 32)
@@ -264,7 +264,7 @@ def test_varlen_graph_replays_follow_device_lengths():
     nq_t = torch.zeros(4, dtype=torch.int32, device="cuda")
     nr_t = torch.zeros(4, dtype=torch.int32, device="cuda")
     out = torch.empty((4, 32, D), dtype=torch.float32, device="cuda")
-    ws = torch.empty(kivi.attend_workspace_bytes(4, 32, 8, 2048, 64), dtype=torch.uint8, device="cuda")
+    ws = kivi.attend_workspace(kivi.attend_workspace_bytes(4, 32, 8, 2048, 64, varlen=True))
 
     def call(o):
         kivi.decode_attend_varlen(c["q"], c["ks"], c["vs"], nq_t, 2048, c["kr"], c["vr"], nr_t, 64,
@@ -296,7 +296,7 @@ def test_varlen_rejects_missing_lengths():
     c = _case(1, 32, 8, 64, 8, 4, seed=16)
     nq = torch.tensor([64], dtype=torch.int32, device="cuda")
     ks, vs = c["ks"].c(), c["vs"].c()
-    ws = torch.empty(kivi.attend_workspace_bytes(1, 32, 8, 64, 8), dtype=torch.uint8, device="cuda")
+    ws = kivi.attend_workspace(kivi.attend_workspace_bytes(1, 32, 8, 64, 8, varlen=True))
     out = torch.empty((1, 32, D), dtype=torch.float32, device="cuda")
     import ctypes
     rc = kivi.lib().kivi_decode_attend_varlen(

@@ -88,7 +88,7 @@ def _decode_loop(case, G, Dh=D):
         c.prefill(k0, v0)
         m.prefill(u16(k0), u16(v0))
     assert (c.length, c.n_quant) == (m.length, m.n_quant)
-    ws = torch.empty(c.attend_workspace_bytes(Hq), dtype=torch.uint8, device="cuda")
+    ws = kivi.attend_workspace(c.attend_workspace_bytes(Hq))
     worst = 0.0
     for step in range(steps):
         kn = synth.kv_tensor(slabs, 1, Dh, keys=True, seed=seed * 1000 + step, device="cuda",

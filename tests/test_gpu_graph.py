@@ -31,7 +31,7 @@ def test_graph_replays_match_eager(bits):
     recon = torch.empty((BH, nq, 128), dtype=torch.float16, device="cuda")
     deq = torch.empty_like(recon)
     out = torch.empty((B, Hq, 128), dtype=torch.float32, device="cuda")
-    ws = torch.empty(kivi.attend_workspace_bytes(B, Hq, Hkv, nq, nr), dtype=torch.uint8, device="cuda")
+    ws = kivi.attend_workspace(kivi.attend_workspace_bytes(B, Hq, Hkv, nq, nr))
 
     def work(stream):
         kivi.quantize_keys(kx, ks, 0, recon, stream=stream)
