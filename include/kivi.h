@@ -211,6 +211,26 @@ int kivi_decode_attend(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * kivi_decode_attend without a workspace argument, for callers that cannot
+ * allocate device memory: code under graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The split partials go to a 32 MiB device
+ * array the library owns (part of its code object: each GPU the library runs
+ * on holds one copy, from load until the process ends); the call allocates
+ * nothing.  A shape whose partials exceed it
+ * (kivi_decode_attend_workspace_bytes(B, Hq, Hkv, n_quant, n_res, head_dim,
+ * 0) > 32 MiB) returns KIVI_ERR_WORKSPACE with nothing launched.  All calls
+ * on one GPU share its array: calls that may overlap in time on one GPU
+ * (several streams or host threads) race, and the caller must keep them
+ * apart.  The first call on each device looks the array's address up
+ * (hipGetSymbolAddress) and must not be made during stream capture.
+ * Everything else (arguments, result, errors) is as for kivi_decode_attend.
+ */
+int kivi_decode_attend_noalloc(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
+                               const kivi_store* k, const kivi_store* v, int64_t n_quant,
+                               const uint16_t* k_res, const uint16_t* v_res, int64_t res_bh_stride,
+                               int64_t n_res, float softmax_scale, float* out, hipStream_t stream);
+
+/*
  * kivi_decode_attend over a batch of sequences of different lengths, in one
  * launch ([Benchmarks] "KV-Cache Kernel Roofline: What Actually Limits
  * Decode": several concurrent requests routed through one fused decode

@@ -190,7 +190,7 @@ int decode_attend_entry(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
                         int64_t n_res, int64_t res_head, int64_t res_ring,
                         const int32_t* seq_n_quant, const int32_t* seq_n_res,
                         float softmax_scale, float* out, void* workspace, size_t workspace_bytes,
-                        hipStream_t stream, bool bf16) {
+                        hipStream_t stream, bool bf16, bool static_scratch) {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || n_quant < 0 || n_res < 0) return KIVI_ERR_SHAPE;
     if (Hq % Hkv != 0) return KIVI_ERR_SHAPE;
     const int group = Hq / Hkv;
@@ -221,6 +221,13 @@ int decode_attend_entry(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
     }
     const kivi::AttendPlan plan = kivi::plan_attend(B, Hq, Hkv, n_quant, n_res, seq_n_quant != nullptr, D, bf16);
     if (plan.n_split > kMaxBlocks || slabs > 65535 || B * Hq > kMaxBlocks) return KIVI_ERR_SHAPE;
+    if (static_scratch) {
+        // the library's own array: a size check, then its device address
+        if (plan.workspace_bytes > kivi::static_attend_scratch_bytes()) return KIVI_ERR_WORKSPACE;
+        const hipError_t e = kivi::static_attend_scratch(&workspace);
+        if (e != hipSuccess) return finish(e);
+        workspace_bytes = kivi::static_attend_scratch_bytes();
+    }
     if (!workspace || workspace_bytes < plan.workspace_bytes) return KIVI_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KIVI_ERR_ALIGN;
 
@@ -258,6 +265,15 @@ int kivi_decode_attend(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
     return kivi::decode_attend_entry(q, B, Hq, Hkv, k, v, n_quant, k_res, v_res, res_bh_stride,
                                      n_res, 0, 0, nullptr, nullptr, softmax_scale, out, workspace,
                                      workspace_bytes, stream);
+}
+
+int kivi_decode_attend_noalloc(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
+                               const kivi_store* k, const kivi_store* v, int64_t n_quant,
+                               const uint16_t* k_res, const uint16_t* v_res, int64_t res_bh_stride,
+                               int64_t n_res, float softmax_scale, float* out, hipStream_t stream) {
+    return kivi::decode_attend_entry(q, B, Hq, Hkv, k, v, n_quant, k_res, v_res, res_bh_stride,
+                                     n_res, 0, 0, nullptr, nullptr, softmax_scale, out, nullptr, 0,
+                                     stream, false, true);
 }
 
 int kivi_decode_attend_varlen(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,

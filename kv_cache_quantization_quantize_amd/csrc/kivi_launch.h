@@ -117,14 +117,21 @@ hipError_t launch_copy_rows(const RowCopy& k, const RowCopy& v, int64_t slabs, i
                             hipStream_t stream);
 
 // The attend entry point behind kivi_decode_attend(_varlen) and the cache:
-// validates on the host, then launches (see abi.cpp).
+// validates on the host, then launches (see abi.cpp).  With static_scratch
+// the workspace arguments are ignored and the library's own device array is
+// used (kivi_decode_attend_noalloc).
 int decode_attend_entry(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
                         const kivi_store* k, const kivi_store* v, int64_t n_quant,
                         const uint16_t* k_res, const uint16_t* v_res, int64_t res_bh_stride,
                         int64_t n_res, int64_t res_head, int64_t res_ring,
                         const int32_t* seq_n_quant, const int32_t* seq_n_res,
                         float softmax_scale, float* out, void* workspace, size_t workspace_bytes,
-                        hipStream_t stream, bool bf16 = false);
+                        hipStream_t stream, bool bf16 = false, bool static_scratch = false);
+
+// The library-owned attend workspace (noalloc.hip): its size, and its device
+// address on the current device (resolved on the first call per device).
+size_t static_attend_scratch_bytes();
+hipError_t static_attend_scratch(void** ptr);
 
 // KIVI_OK, or KIVI_ERR_HIP after recording e for kivi_last_hip_error.
 int hip_status(hipError_t e);

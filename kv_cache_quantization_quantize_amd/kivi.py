@@ -30,7 +30,7 @@ EXPORTS = (
     "kivi_quantize_keys", "kivi_quantize_values", "kivi_dequantize",
     "kivi_quantize_keys_bf16", "kivi_quantize_values_bf16", "kivi_dequantize_bf16",
     "kivi_decode_attend", "kivi_decode_attend_varlen", "kivi_decode_attend_workspace_bytes",
-    "kivi_decode_attend_bf16", "kivi_decode_attend_varlen_bf16",
+    "kivi_decode_attend_bf16", "kivi_decode_attend_varlen_bf16", "kivi_decode_attend_noalloc",
     "kivi_status_string", "kivi_last_hip_error", "kivi_calib_copy", "kivi_calib_read",
     "kivi_calib_write", "kivi_calib_mix",
     "kivi_cache_device_bytes", "kivi_cache_init", "kivi_cache_prefill", "kivi_cache_append",
@@ -106,6 +106,8 @@ def lib() -> ctypes.CDLL:
         L.kivi_decode_attend_varlen.argtypes = [vp, i64, i32, i32, sp, sp, vp, i64, vp, vp, i64,
                                                 vp, i64, ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
         L.kivi_decode_attend_bf16.argtypes = L.kivi_decode_attend.argtypes
+        L.kivi_decode_attend_noalloc.argtypes = [vp, i64, i32, i32, sp, sp, i64, vp, vp, i64, i64,
+                                                 ctypes.c_float, vp, vp]
         L.kivi_decode_attend_varlen_bf16.argtypes = L.kivi_decode_attend_varlen.argtypes
         L.kivi_decode_attend_workspace_bytes.argtypes = [i64, i32, i32, i64, i64, i32, i32]
         L.kivi_decode_attend_workspace_bytes.restype = ctypes.c_size_t
@@ -130,7 +132,7 @@ def lib() -> ctypes.CDLL:
                      "kivi_quantize_keys_bf16", "kivi_quantize_values_bf16", "kivi_dequantize_bf16",
                      "kivi_decode_attend", "kivi_decode_attend_varlen", "kivi_last_hip_error",
                      "kivi_decode_attend_bf16", "kivi_decode_attend_varlen_bf16",
-                     "kivi_calib_copy", "kivi_calib_read", "kivi_calib_write", "kivi_calib_mix",
+                     "kivi_decode_attend_noalloc", "kivi_calib_copy", "kivi_calib_read", "kivi_calib_write", "kivi_calib_mix",
                      "kivi_cache_init", "kivi_cache_prefill", "kivi_cache_append",
                      "kivi_cache_attend", "kivi_cache_end_step"):
             getattr(L, name).restype = ctypes.c_int
@@ -326,6 +328,35 @@ def decode_attend(q: torch.Tensor, k_store: Store, v_store: Store, n_quant: int,
         k_res.stride(0) if n_res > 0 else 0, n_res, float(softmax_scale), out.data_ptr(),
         workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream))
     _check(rc, name)
+    return out
+
+
+def decode_attend_noalloc(q: torch.Tensor, k_store: Store, v_store: Store, n_quant: int,
+                          k_res: torch.Tensor | None, v_res: torch.Tensor | None, n_res: int,
+                          softmax_scale: float | None = None, out: torch.Tensor | None = None,
+                          stream=None) -> torch.Tensor:
+    """kivi_decode_attend_noalloc: decode_attend with the library's own
+    device array as workspace (fp16 caches).  Allocates nothing itself when
+    ``out`` is given."""
+    Hkv = _kv_heads(q, k_store, v_store)
+    _need_query(q)
+    if q.dtype != torch.float16:
+        raise TypeError("kivi_decode_attend_noalloc takes float16 caches")
+    B, Hq, D = q.shape
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    _need_out(out, B, Hq, D)
+    if n_res > 0:
+        _need_residual(q, k_res, v_res)
+    ks, vs = k_store.c(), v_store.c()
+    rc = lib().kivi_decode_attend_noalloc(
+        q.data_ptr(), B, Hq, Hkv, ctypes.byref(ks), ctypes.byref(vs), n_quant,
+        k_res.data_ptr() if n_res > 0 else None, v_res.data_ptr() if n_res > 0 else None,
+        k_res.stride(0) if n_res > 0 else 0, n_res, float(softmax_scale), out.data_ptr(),
+        _stream(stream))
+    _check(rc, "kivi_decode_attend_noalloc")
     return out
 
 
