@@ -37,6 +37,7 @@
  *                            and the configuration's scale/zero format
  *   key ring, value ring     16-bit [slabs][R + F][head_dim] (fp16, or
  *                            bfloat16 for a bfloat16 cache)
+ *   key, value staging       the same shape as the rings
  *
  * The library never allocates: the caller allocates the device buffer and
  * the kivi_cache struct.  Every call validates on the host before it enqueues
@@ -83,6 +84,8 @@ typedef struct kivi_cache {
     kivi_store v_store;
     uint16_t* k_ring;         /* 16-bit [slabs][ring][head_dim]                */
     uint16_t* v_ring;
+    uint16_t* k_stage;        /* 16-bit [slabs][ring][head_dim]: a prompt      */
+    uint16_t* v_stage;        /* chunk's first flush groups are assembled here */
     int64_t ring;             /* R + F rows per slab                           */
     int64_t length;           /* tokens per sequence so far                    */
     int64_t n_quant;          /* of which quantized (in the stores)            */
@@ -100,12 +103,20 @@ size_t kivi_cache_device_bytes(const kivi_cache_config* cfg);
  * nothing and does not touch the device memory. */
 int kivi_cache_init(kivi_cache* cache, const kivi_cache_config* cfg, void* device, size_t bytes);
 
-/* Prompt of S tokens for every layer and sequence at once, into an empty
- * cache.  k, v: 16-bit (the cache's format) [layers*batch*kv_heads][S][head_dim] with slab stride
- * x_bh_stride (slab order as in the device layout).  The oldest Q(S) tokens
- * are flushed into the stores (one launch per tensor over all layers), the
- * other S - Q(S) are copied into the rings (one launch).  Q(S) must fit the
- * store capacity. */
+/* A chunk of S prompt tokens for every layer and sequence at once, appended
+ * to the cache (empty, or holding earlier chunks and decode steps; not in
+ * the middle of a step).  k, v: 16-bit (the cache's format)
+ * [layers*batch*kv_heads][S][head_dim] with slab stride x_bh_stride (slab
+ * order as in the device layout).  After the call the cache holds L + S
+ * tokens of which Q(L + S) are quantized, exactly as if the whole prompt had
+ * arrived at once: the newly flushed tokens [Q(L), Q(L + S)) go into the
+ * stores, the ones whose key groups begin among the fp16 tokens already in
+ * the rings through the staging rows (one gather launch, then one flush
+ * launch per tensor over all layers), the rest straight from k and v (one
+ * flush launch per tensor); the chunk's tokens that stay fp16 are copied
+ * into the rings (one launch).  Long prompts can so be fed in pieces (the
+ * pages' runtime prefills 2048-token chunks: [Metal post] "Four benchmarks
+ * that lied", Lie #1).  Q(L + S) must fit the store capacity. */
 int kivi_cache_prefill(kivi_cache* cache, const uint16_t* k, const uint16_t* v,
                        int64_t x_bh_stride, int64_t S, hipStream_t stream);
 

@@ -5,6 +5,8 @@
 // in cache.hip.  Every call validates everything before its first launch.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "kivi.h"
 #include "kivi_cache.h"
 #include "kivi_launch.h"
@@ -18,7 +20,7 @@ int64_t align256(int64_t x) { return (x + 255) & ~int64_t{255}; }
 
 struct Layout {
     int64_t slabs, ring, words;
-    int64_t kc, ks, kz, vc, vs, vz, kr, vr, total;    // byte offsets / size
+    int64_t kc, ks, kz, vc, vs, vz, kr, vr, kst, vst, total;    // byte offsets / size
 };
 
 bool valid(const kivi_cache_config* c) {
@@ -65,6 +67,8 @@ Layout layout(const kivi_cache_config& c) {
     L.vz = take(L.slabs * cap * ((kD + G - 1) / G) * mb);
     L.kr = take(L.slabs * L.ring * kD * 2);
     L.vr = take(L.slabs * L.ring * kD * 2);
+    L.kst = take(L.slabs * L.ring * kD * 2);      // staging for a prompt chunk's first groups
+    L.vst = take(L.slabs * L.ring * kD * 2);
     L.total = off;
     return L;
 }
@@ -133,6 +137,8 @@ int kivi_cache_init(kivi_cache* cache, const kivi_cache_config* cfg, void* devic
                  cfg->bits, cfg->group_size, cfg->head_dim, KIVI_VALUES, cfg->meta_format};
     c.k_ring = reinterpret_cast<uint16_t*>(base + L.kr);
     c.v_ring = reinterpret_cast<uint16_t*>(base + L.vr);
+    c.k_stage = reinterpret_cast<uint16_t*>(base + L.kst);
+    c.v_stage = reinterpret_cast<uint16_t*>(base + L.vst);
     c.ring = L.ring;
     *cache = c;
     return KIVI_OK;
@@ -143,36 +149,76 @@ int kivi_cache_prefill(kivi_cache* cache, const uint16_t* k, const uint16_t* v,
     if (!cache) return KIVI_ERR_NULL;
     if (!valid(&cache->cfg)) return KIVI_ERR_UNSUPPORTED;
     const int64_t kD = cache->cfg.head_dim;
-    if (S < 0 || cache->length != 0) return KIVI_ERR_SHAPE;
+    const int64_t G = cache->cfg.group_size;
+    if (S < 0) return KIVI_ERR_SHAPE;
     for (uint64_t w : cache->appended)
         if (w) return KIVI_ERR_SHAPE;                  // a step is in progress
-    const int64_t Q = quantized_tokens(cache->cfg, S);
-    const int64_t nres = S - Q;
-    if (Q > cache->cfg.store_capacity || nres > cache->ring) return KIVI_ERR_SHAPE;
+    const int64_t L0 = cache->length, Q0 = cache->n_quant, R0 = cache->n_res;
+    if (S > kMaxTokens || L0 + S >= kMaxTokens) return KIVI_ERR_SHAPE;
+    const int64_t L1 = L0 + S;
+    const int64_t Q1 = quantized_tokens(cache->cfg, L1);
+    if (Q1 > cache->cfg.store_capacity) return KIVI_ERR_SHAPE;
     if (S == 0) return KIVI_OK;
     const int64_t slabs = layout(cache->cfg).slabs;
     if (!k || !v) return KIVI_ERR_NULL;
     if (!aligned16(k) || !aligned16(v) || x_bh_stride % 8 != 0) return KIVI_ERR_ALIGN;
     if (slabs > 1 && x_bh_stride < S * kD) return KIVI_ERR_SHAPE;
-    if ((slabs * ((Q + 31) / 32) + 3) / 4 >= kMaxSlabs) return KIVI_ERR_SHAPE;
-    if (slabs * nres * (kD * 2 / 16) / 256 >= kMaxSlabs) return KIVI_ERR_SHAPE;
+    if ((slabs * ((S + cache->ring + 31) / 32) + 3) / 4 >= kMaxSlabs) return KIVI_ERR_SHAPE;
+    if (slabs * (S + cache->ring) * (kD / 8) / 256 >= kMaxSlabs) return KIVI_ERR_SHAPE;
 
+    // The flush takes tokens [Q0, Q1).  Its first groups may hold fp16
+    // tokens still in the ring (ring rows head, head + 1, ... mod ring) and
+    // the chunk's first tokens: tokens [Q0, A_end) with A_end the first group
+    // boundary at or past L0 are assembled in the staging rows and flushed
+    // from there; the rest, [A_end, Q1), lie in the chunk, start on a group
+    // boundary and are flushed from the caller's buffer.  One launch per
+    // tensor over all layers for each part.
+    uint16_t* kcm = const_cast<uint16_t*>(k);
+    uint16_t* vcm = const_cast<uint16_t*>(v);
+    const int64_t rs = cache->ring * kD;               // ring / staging slab stride
     int rc = KIVI_OK;
-    if (Q > 0) {
-        rc = flush_keys(cache, k, slabs, Q, x_bh_stride, 0, stream);
-        if (rc == KIVI_OK) rc = flush_values(cache, v, slabs, Q, x_bh_stride, 0, stream);
+    if (Q1 > Q0) {
+        const int64_t a_end = std::min(Q1, (L0 + G - 1) / G * G);
+        const int64_t A = a_end - Q0;                  // <= ring: R0 < ring, rounded up to G
+        if (A > 0) {
+            const int64_t from_ring = std::min(A, R0);
+            const kivi::RowGather gk = {{cache->k_stage, rs, 0, 0}, {cache->k_ring, rs, cache->head, cache->ring},
+                                        {kcm, x_bh_stride, 0, 0}, from_ring};
+            const kivi::RowGather gv = {{cache->v_stage, rs, 0, 0}, {cache->v_ring, rs, cache->head, cache->ring},
+                                        {vcm, x_bh_stride, 0, 0}, from_ring};
+            rc = finish(kivi::launch_gather_rows(gk, gv, slabs, A, static_cast<int>(kD), stream));
+            if (rc == KIVI_OK) rc = flush_keys(cache, cache->k_stage, slabs, A, rs, Q0, stream);
+            if (rc == KIVI_OK) rc = flush_values(cache, cache->v_stage, slabs, A, rs, Q0, stream);
+            if (rc != KIVI_OK) return rc;
+        }
+        const int64_t B = Q1 - a_end;
+        if (B > 0) {
+            const int64_t c0 = a_end - L0;             // chunk row of token a_end
+            rc = flush_keys(cache, k + c0 * kD, slabs, B, x_bh_stride, a_end, stream);
+            if (rc == KIVI_OK) rc = flush_values(cache, v + c0 * kD, slabs, B, x_bh_stride, a_end, stream);
+            if (rc != KIVI_OK) return rc;
+        }
+    }
+    // The fp16 tokens are now [Q1, L1).  Those older than the chunk stay in
+    // their ring rows; the ring's head moves past the flushed ones (a
+    // multiple of the flush unit, like the ring, so a later flush never
+    // wraps), and the chunk's fp16 tokens are written after them.
+    const int64_t head1 = (cache->head + (Q1 - Q0)) % cache->ring;
+    const int64_t t0 = std::max(L0, Q1);               // first fp16 token that comes from the chunk
+    const int64_t n_copy = L1 - t0;
+    if (n_copy > 0) {
+        const int64_t dst0 = (head1 + (t0 - Q1)) % cache->ring;
+        const kivi::RowGather gk = {{cache->k_ring, rs, dst0, cache->ring}, {kcm, x_bh_stride, t0 - L0, 0},
+                                    {kcm, x_bh_stride, t0 - L0, 0}, n_copy};
+        const kivi::RowGather gv = {{cache->v_ring, rs, dst0, cache->ring}, {vcm, x_bh_stride, t0 - L0, 0},
+                                    {vcm, x_bh_stride, t0 - L0, 0}, n_copy};
+        rc = finish(kivi::launch_gather_rows(gk, gv, slabs, n_copy, static_cast<int>(kD), stream));
         if (rc != KIVI_OK) return rc;
     }
-    if (nres > 0) {
-        const kivi::RowCopy kc = {k + Q * kD, x_bh_stride, cache->k_ring, cache->ring * kD};
-        const kivi::RowCopy vc = {v + Q * kD, x_bh_stride, cache->v_ring, cache->ring * kD};
-        rc = finish(kivi::launch_copy_rows(kc, vc, slabs, nres, static_cast<int>(kD), stream));
-        if (rc != KIVI_OK) return rc;
-    }
-    cache->length = S;
-    cache->n_quant = Q;
-    cache->n_res = nres;
-    cache->head = 0;
+    cache->length = L1;
+    cache->n_quant = Q1;
+    cache->n_res = L1 - Q1;
+    cache->head = head1;
     return KIVI_OK;
 }
 
@@ -186,12 +232,13 @@ int kivi_cache_append(kivi_cache* cache, int32_t layer, const uint16_t* k_new,
     if (!k_new || !v_new) return KIVI_ERR_NULL;
     if (!aligned16(k_new) || !aligned16(v_new)) return KIVI_ERR_ALIGN;
     const int64_t slab0 = layer * seq_slabs(cache);
-    int64_t row = cache->head + cache->n_res;
-    if (row >= cache->ring) row -= cache->ring;
+    const int64_t row = (cache->head + cache->n_res) % cache->ring;
     const int64_t rs = cache->ring * kD;
-    const kivi::RowCopy kc = {k_new, kD, cache->k_ring + slab0 * rs + row * kD, rs};
-    const kivi::RowCopy vc = {v_new, kD, cache->v_ring + slab0 * rs + row * kD, rs};
-    const int rc = finish(kivi::launch_copy_rows(kc, vc, seq_slabs(cache), 1, static_cast<int>(kD), stream));
+    uint16_t* kn = const_cast<uint16_t*>(k_new);
+    uint16_t* vn = const_cast<uint16_t*>(v_new);
+    const kivi::RowGather gk = {{cache->k_ring + slab0 * rs, rs, row, 0}, {kn, kD, 0, 0}, {kn, kD, 0, 0}, 1};
+    const kivi::RowGather gv = {{cache->v_ring + slab0 * rs, rs, row, 0}, {vn, kD, 0, 0}, {vn, kD, 0, 0}, 1};
+    const int rc = finish(kivi::launch_gather_rows(gk, gv, seq_slabs(cache), 1, static_cast<int>(kD), stream));
     if (rc != KIVI_OK) return rc;
     cache->appended[layer >> 6] |= uint64_t{1} << (layer & 63);
     return KIVI_OK;

@@ -105,16 +105,23 @@ hipError_t launch_attend_generic(const AttendArgs& a, const AttendPlan& p, float
 // head_dims other than 64, 128 and 256 (multiples of 16 up to 256, groups of 32)
 hipError_t launch_flush_ragged(bool keys, const FlushArgs& a, hipStream_t stream);
 hipError_t launch_dequant_ragged(const DequantArgs& a, hipStream_t stream);
-// Copies n_rows token rows (D 16-bit values each) of every slab from src to
-// dst for keys and values at once (one launch).
-struct RowCopy {
-    const uint16_t* src;
-    int64_t src_bh_stride;         // elements between slabs
-    uint16_t* dst;
-    int64_t dst_bh_stride;
+// Row copies of the cache (one launch for keys and values): row r < n_rows
+// of every slab comes from span a (r < n_a) or from span b (row r - n_a) and
+// goes to row r of span dst.  A span's row i is row (first + i) mod ring of
+// the slab for a ring (ring > 0), row first + i otherwise; rows hold D
+// 16-bit values.
+struct RowSpan {
+    uint16_t* base;                // slab 0 (read-only for sources)
+    int64_t bh_stride;             // elements between slabs
+    int64_t first;                 // the span's first row
+    int64_t ring;                  // rows of the ring, or 0 for a linear span
 };
-hipError_t launch_copy_rows(const RowCopy& k, const RowCopy& v, int64_t slabs, int64_t n_rows, int D,
-                            hipStream_t stream);
+struct RowGather {
+    RowSpan dst, a, b;
+    int64_t n_a;
+};
+hipError_t launch_gather_rows(const RowGather& k, const RowGather& v, int64_t slabs, int64_t n_rows, int D,
+                              hipStream_t stream);
 
 // The attend entry point behind kivi_decode_attend(_varlen) and the cache:
 // validates on the host, then launches (see abi.cpp).  With static_scratch

@@ -76,7 +76,8 @@ class CCacheConfig(ctypes.Structure):
 class CCache(ctypes.Structure):
     _fields_ = [
         ("cfg", CCacheConfig), ("k_store", CStore), ("v_store", CStore),
-        ("k_ring", ctypes.c_void_p), ("v_ring", ctypes.c_void_p), ("ring", ctypes.c_int64),
+        ("k_ring", ctypes.c_void_p), ("v_ring", ctypes.c_void_p), ("k_stage", ctypes.c_void_p),
+        ("v_stage", ctypes.c_void_p), ("ring", ctypes.c_int64),
         ("length", ctypes.c_int64), ("n_quant", ctypes.c_int64), ("n_res", ctypes.c_int64),
         ("head", ctypes.c_int64), ("appended", ctypes.c_uint64 * (CACHE_MAX_LAYERS // 64)),
     ]

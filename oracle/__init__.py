@@ -398,8 +398,11 @@ class CacheModel:
             self.n_quant = Q
 
     def prefill(self, k, v):
-        """k, v fp16 [slabs][S][D]: the prompt of every layer and sequence."""
-        self.k, self.v = _as_u16(k).copy(), _as_u16(v).copy()
+        """k, v 16-bit [slabs][S][D]: S more prompt tokens of every layer and
+        sequence (the whole prompt, or the next chunk of it), appended to the
+        tokens the model holds; then the rule flushes what it calls for."""
+        self.k = np.concatenate([self.k, _as_u16(k)], axis=1)
+        self.v = np.concatenate([self.v, _as_u16(v)], axis=1)
         self._flush_to_rule()
 
     def step(self, k_new, v_new, q, Hq: int) -> np.ndarray:

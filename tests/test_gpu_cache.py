@@ -71,46 +71,60 @@ def test_decode_loop_head_dims(Dh, case):
 
 def _decode_loop(case, G, Dh=D):
     layers, batch, kvh, Hq, bits, R, F, cap, S0, steps, variant = case
+    sched = ([("chunk", S0)] if S0 else []) + [("steps", steps)]
+    _run_schedule(layers, batch, kvh, Hq, bits, R, F, cap, variant, sched, G, Dh, seed=9000 + S0 + R)
+    print(f"{case}: ok")
+
+
+def _run_schedule(layers, batch, kvh, Hq, bits, R, F, cap, variant, schedule, G=32, Dh=D, seed=0):
+    """Drive the GPU cache and the oracle's CacheModel through the same
+    schedule of ("chunk", n) prompt chunks and ("steps", n) decode steps:
+    token counts equal after every event, every step's attention within
+    TOL, and at the end the stores bit-exact and the rings' fp16 tokens (in
+    logical order from the head) byte-identical to the model's tail."""
     bf16 = variant == "bf16"
     meta = "f32" if bf16 else variant
     dtype = torch.bfloat16 if bf16 else torch.float16
     fmt = "bf16" if bf16 else "f16"
-    seed = 9000 + S0 + R
     slabs = layers * batch * kvh
     per = batch * kvh
-    note(f"cache loop layers={layers} batch={batch} kv_heads={kvh} Hq={Hq} bits={bits} R={R} F={F} "
-         f"capacity={cap} prompt={S0} steps={steps} meta={meta}")
+    note(f"cache layers={layers} batch={batch} kv_heads={kvh} Hq={Hq} bits={bits} R={R} F={F} "
+         f"capacity={cap} G={G} D={Dh} {variant} schedule={schedule}")
     c = kivi.Cache(layers, batch, kvh, cap, bits, R, F, meta=meta, dtype=dtype, group=G, head_dim=Dh)
     m = oracle.CacheModel(layers, batch, kvh, cap, bits, R, F, D=Dh, meta=meta, fmt=fmt, G=G)
-    if S0:
-        k0 = synth.kv_tensor(slabs, S0, Dh, keys=True, seed=seed, device="cuda", dtype=dtype)
-        v0 = synth.kv_tensor(slabs, S0, Dh, keys=False, seed=seed, device="cuda", dtype=dtype)
-        c.prefill(k0, v0)
-        m.prefill(u16(k0), u16(v0))
-    assert (c.length, c.n_quant) == (m.length, m.n_quant)
     ws = kivi.attend_workspace(c.attend_workspace_bytes(Hq))
     worst = 0.0
-    for step in range(steps):
-        kn = synth.kv_tensor(slabs, 1, Dh, keys=True, seed=seed * 1000 + step, device="cuda",
-                             dtype=dtype)[:, 0].contiguous()
-        vn = synth.kv_tensor(slabs, 1, Dh, keys=False, seed=seed * 1000 + step, device="cuda",
-                             dtype=dtype)[:, 0].contiguous()
-        q = synth.query(layers * batch, Hq, Dh, seed=seed * 1000 + step, device="cuda").to(dtype) \
-            .view(layers, batch, Hq, Dh)
-        outs = []
-        for layer in range(layers):
-            c.append(layer, kn[layer * per:(layer + 1) * per], vn[layer * per:(layer + 1) * per])
-            outs.append(c.attend(layer, q[layer].contiguous(), workspace=ws))
-        before = c.n_quant
-        launches = c.end_step()
-        torch.cuda.synchronize()
-        ref = m.step(u16(kn), u16(vn), u16(q), Hq)
-        assert (c.length, c.n_quant) == (m.length, m.n_quant), step
-        assert launches == (2 if c.n_quant != before else 0)
-        for layer in range(layers):
-            err = float(np.max(np.abs(outs[layer].cpu().numpy().astype(np.float64) - ref[layer])))
-            worst = max(worst, err)
-            assert err <= TOL, f"step {step} layer {layer}: max-abs error {err:.3e}"
+    step = 0
+    for e, (what, n) in enumerate(schedule):
+        if what == "chunk":
+            k0 = synth.kv_tensor(slabs, n, Dh, keys=True, seed=seed + 17 * e, device="cuda", dtype=dtype)
+            v0 = synth.kv_tensor(slabs, n, Dh, keys=False, seed=seed + 17 * e, device="cuda", dtype=dtype)
+            c.prefill(k0, v0)
+            m.prefill(u16(k0), u16(v0))
+            assert (c.length, c.n_quant) == (m.length, m.n_quant), (e, what, n)
+            continue
+        for _ in range(n):
+            kn = synth.kv_tensor(slabs, 1, Dh, keys=True, seed=seed * 1000 + step, device="cuda",
+                                 dtype=dtype)[:, 0].contiguous()
+            vn = synth.kv_tensor(slabs, 1, Dh, keys=False, seed=seed * 1000 + step, device="cuda",
+                                 dtype=dtype)[:, 0].contiguous()
+            q = synth.query(layers * batch, Hq, Dh, seed=seed * 1000 + step, device="cuda").to(dtype) \
+                .view(layers, batch, Hq, Dh)
+            outs = []
+            for layer in range(layers):
+                c.append(layer, kn[layer * per:(layer + 1) * per], vn[layer * per:(layer + 1) * per])
+                outs.append(c.attend(layer, q[layer].contiguous(), workspace=ws))
+            before = c.n_quant
+            launches = c.end_step()
+            torch.cuda.synchronize()
+            ref = m.step(u16(kn), u16(vn), u16(q), Hq)
+            assert (c.length, c.n_quant) == (m.length, m.n_quant), step
+            assert launches == (2 if c.n_quant != before else 0)
+            for layer in range(layers):
+                err = float(np.max(np.abs(outs[layer].cpu().numpy().astype(np.float64) - ref[layer])))
+                worst = max(worst, err)
+                assert err <= TOL, f"step {step} layer {layer}: max-abs error {err:.3e}"
+            step += 1
     Q = c.n_quant
     ks, vs = c.stores()
     torch.cuda.synchronize()
@@ -126,7 +140,40 @@ def _decode_loop(case, G, Dh=D):
     assert c.n_res == m.length - Q
     assert np.array_equal(u16(kr[:, rows]), m.k[:, Q:])
     assert np.array_equal(u16(vr[:, rows]), m.v[:, Q:])
-    print(f"{case}: worst attend error {worst:.2e}, length {c.length}, quantized {Q}")
+    return worst
+
+
+CHUNKED = [
+    # layers, batch, kv_heads, Hq, bits, R, F, capacity, variant, G, head_dim, schedule
+    (2, 2, 2, 8, 4, 64, 32, 1024, "f32", 32, D,
+     [("chunk", 45), ("steps", 3), ("chunk", 1), ("chunk", 100), ("steps", 40), ("chunk", 77),
+      ("chunk", 31), ("steps", 2), ("chunk", 200), ("steps", 5)]),
+    (1, 2, 2, 8, 4, 128, 128, 2048, "f16", 32, D,
+     [("chunk", 300), ("steps", 20), ("chunk", 129), ("chunk", 500), ("steps", 130)]),
+    (2, 1, 2, 4, 2, 0, 32, 512, "bf16", 32, D,
+     [("chunk", 33), ("steps", 1), ("chunk", 64), ("chunk", 95), ("steps", 40), ("chunk", 7)]),
+    (1, 2, 2, 8, 4, 128, 64, 1024, "f32", 64, D,
+     [("chunk", 70), ("steps", 30), ("chunk", 250), ("steps", 3), ("chunk", 65)]),
+    (1, 1, 2, 8, 4, 64, 32, 512, "f32", 32, 96,
+     [("chunk", 50), ("steps", 20), ("chunk", 90), ("steps", 5)]),
+]
+
+
+@pytest.mark.parametrize("case", CHUNKED, ids=["f32", "meta16-F128", "bf16-R0", "G64", "D96"])
+def test_chunked_prefill_matches_model(case):
+    """Prompt chunks fed into a cache that already holds tokens (ragged
+    chunk lengths, decode steps in between): the cache holds exactly what
+    the model holds after the same tokens."""
+    layers, batch, kvh, Hq, bits, R, F, cap, variant, G, Dh, sched = case
+    _run_schedule(layers, batch, kvh, Hq, bits, R, F, cap, variant, sched, G, Dh, seed=7700 + R + G)
+
+
+def test_prefill_of_8209_tokens_in_2048_token_chunks():
+    """The Metal post's Generation 1 prompt of 8209 tokens, fed in 2048-token
+    chunks (Lie #1: the runtime chunks prefill at 2048) with R = G = F = 32:
+    8160 tokens flushed per layer, stores equal to the model's."""
+    _run_schedule(2, 1, 8, 32, 4, 32, 32, 8192, "f32",
+                  [("chunk", 2048)] * 4 + [("chunk", 17), ("steps", 2)], 32, D, seed=8209)
 
 
 def test_full_store_is_reported_and_leaves_state_unchanged():

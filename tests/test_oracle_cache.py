@@ -87,3 +87,43 @@ def test_step_attention_is_sdpa_over_store_then_fp16_tail(orc):
                 want = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt).reshape(Hq, D).numpy()
                 assert np.max(np.abs(got[layer, b] - want)) < 1e-12
     assert m.n_quant == 64                    # flush_count(97, 32, 32)
+
+
+def test_chunked_prompt_matches_the_whole_prompt_and_the_2048_chunking(orc):
+    """An 8209-token prompt fed in 2048-token chunks (the pages' runtime
+    chunks prefill at 2048: [Metal post] "Four benchmarks that lied", Lie #1)
+    flushes 8160 tokens per layer (the Generation 1 flush/layer column with
+    R = G = 32) and builds the same stores as the whole prompt at once; so do
+    ragged chunk lengths that are not multiples of the group size, with
+    decode steps in between."""
+    rng = np.random.default_rng(8209)
+    S, slabs = 8209, 2
+    k = _f16(rng.standard_normal((slabs, S, D)) * 3)
+    v = _f16(rng.standard_normal((slabs, S, D)))
+    whole = orc.CacheModel(1, 1, slabs, capacity=8192, R=32, F=32)
+    whole.prefill(k, v)
+    chunked = orc.CacheModel(1, 1, slabs, capacity=8192, R=32, F=32)
+    counts = []
+    for c0 in range(0, S, 2048):
+        chunked.prefill(k[:, c0:c0 + 2048], v[:, c0:c0 + 2048])
+        counts.append(chunked.n_quant)
+    assert counts == [orc.flush_count(min(S, c0 + 2048), 32, 32) for c0 in range(0, S, 2048)]
+    assert chunked.n_quant == whole.n_quant == 8160
+    for a, b in ((chunked.kstore, whole.kstore), (chunked.vstore, whole.vstore)):
+        assert np.array_equal(a.codes, b.codes)
+        assert np.array_equal(a.scale.view(np.uint32), b.scale.view(np.uint32))
+        assert np.array_equal(a.zero.view(np.uint32), b.zero.view(np.uint32))
+    # ragged chunks with steps between them, R = 64, F = 32
+    m = orc.CacheModel(1, 1, slabs, capacity=1024, R=64, F=32)
+    ref = orc.CacheModel(1, 1, slabs, capacity=1024, R=64, F=32)
+    pos = 0
+    for n in (45, 1, 100, 77, 31, 200):
+        m.prefill(k[:, pos:pos + n], v[:, pos:pos + n])
+        pos += n
+        m.step(k[:, pos], v[:, pos], _f16(rng.standard_normal((1, 1, 4, D))), 4)
+        pos += 1
+        assert m.n_quant == orc.flush_count(pos, 64, 32)
+    ref.prefill(k[:, :pos], v[:, :pos])
+    assert m.n_quant == ref.n_quant
+    assert np.array_equal(m.kstore.codes, ref.kstore.codes)
+    assert np.array_equal(m.vstore.codes, ref.vstore.codes)
