@@ -37,6 +37,7 @@ from __future__ import annotations
 import ctypes
 import os
 import subprocess
+import sys
 
 import numpy as np
 
@@ -79,6 +80,11 @@ def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
+            # building starts gcc as a child process, which a process that has
+            # already set up a GPU must not do: build beforehand instead
+            torch = sys.modules.get("torch")
+            if torch is not None and torch.cuda.is_initialized():
+                raise RuntimeError(f"{LIB_PATH} is not built; run oracle.build() before any GPU work")
             build()
         L = ctypes.CDLL(LIB_PATH)
         L.orc_f16_to_f32.argtypes = [ctypes.c_uint16]
