@@ -27,6 +27,12 @@ namespace {
 constexpr int64_t kD = 128;
 constexpr int64_t kMaxBlocks = (int64_t{1} << 31) - 1;
 constexpr int64_t kMaxAttendTokens = int64_t{1} << 24;   // attend offsets stay 32-bit
+// No buffer reaches past the 47-bit virtual address space a process can map:
+// a tensor or store whose extent would is refused before any product of its
+// sizes is formed, so the size arithmetic below never overflows.
+constexpr int64_t kMaxBytes = int64_t{1} << 47;
+constexpr int64_t kMaxStoreTokens = int64_t{1} << 40;
+constexpr int64_t kMaxAttendSlabs = 65535;               // B * Hkv: the partial kernel's grid y
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -51,6 +57,14 @@ bool geometry_ok(int32_t D, int32_t G) {
 
 bool meta16(const kivi_store* st) { return st->meta_format == KIVI_META_F16; }
 
+// Whether n_slabs slabs of slab_elems elements, stride_elems apart, fit in
+// kMaxBytes (all arguments non-negative; no intermediate overflows).
+bool extent_ok(int64_t n_slabs, int64_t stride_elems, int64_t slab_elems, int64_t elem_bytes) {
+    const int64_t limit = kMaxBytes / elem_bytes;
+    if (n_slabs < 0 || stride_elems < 0 || slab_elems < 0 || slab_elems > limit) return false;
+    return n_slabs <= 1 || stride_elems <= (limit - slab_elems) / (n_slabs - 1);
+}
+
 // Checks a store and that tokens [t0, t0 + n) of slabs [0, BH) lie inside it.
 // Binary16 scale/zero are supported at head_dim 128.
 int check_store(const kivi_store* st, int kind, int64_t BH, int64_t t0, int64_t n) {
@@ -65,11 +79,14 @@ int check_store(const kivi_store* st, int kind, int64_t BH, int64_t t0, int64_t 
     if (!aligned16(st->codes) || !aligned16(st->scale) || !aligned16(st->zero)) return KIVI_ERR_ALIGN;
     // slab strides of whole 16-byte units
     if (st->codes_bh_stride % 4 != 0 || st->meta_bh_stride % (meta16(st) ? 8 : 4) != 0) return KIVI_ERR_ALIGN;
-    if (st->cap < 0 || t0 < 0 || n < 0 || t0 > st->cap - n) return KIVI_ERR_SHAPE;
+    if (st->cap < 0 || st->cap > kMaxStoreTokens || t0 < 0 || n < 0 || t0 > st->cap - n) return KIVI_ERR_SHAPE;
+    if (BH < 0 || st->codes_bh_stride < 0 || st->meta_bh_stride < 0) return KIVI_ERR_SHAPE;
     if (BH > 1) {
         if (st->codes_bh_stride < st->cap * words_per_token(st)) return KIVI_ERR_SHAPE;
         if (st->meta_bh_stride < meta_rows(st)) return KIVI_ERR_SHAPE;
     }
+    if (!extent_ok(BH, st->codes_bh_stride, st->cap * words_per_token(st), 4) ||
+        !extent_ok(BH, st->meta_bh_stride, meta_rows(st), meta16(st) ? 2 : 4)) return KIVI_ERR_SHAPE;
     return KIVI_OK;
 }
 
@@ -77,7 +94,9 @@ int check_store(const kivi_store* st, int kind, int64_t BH, int64_t t0, int64_t 
 int check_f16_tensor(const void* p, int64_t BH, int64_t S, int64_t stride, int64_t D = kD) {
     if (!p) return KIVI_ERR_NULL;
     if (!aligned16(p) || stride % 8 != 0) return KIVI_ERR_ALIGN;
+    if (BH < 0 || S < 0 || stride < 0 || S > kMaxBytes / 2 / D) return KIVI_ERR_SHAPE;
     if (BH > 1 && stride < S * D) return KIVI_ERR_SHAPE;
+    if (!extent_ok(BH, stride, S * D, 2)) return KIVI_ERR_SHAPE;
     return KIVI_OK;
 }
 
@@ -168,7 +187,9 @@ int kivi_dequantize_bf16(const kivi_store* src, int64_t BH, int64_t token_begin,
 
 size_t kivi_decode_attend_workspace_bytes(int64_t B, int32_t Hq, int32_t Hkv, int64_t n_quant,
                                           int64_t n_res, int32_t head_dim, int32_t flags) {
-    if (B <= 0 || Hq <= 0 || Hkv <= 0 || n_quant < 0 || n_res < 0 || n_quant + n_res == 0) return 0;
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || B > kMaxAttendSlabs / Hkv) return 0;
+    if (n_quant < 0 || n_res < 0 || n_quant >= kMaxAttendTokens || n_res >= kMaxAttendTokens ||
+        n_quant + n_res == 0) return 0;
     if (head_dim < 16 || head_dim > 256 || head_dim % 16 != 0) return 0;
     if ((flags & ~(KIVI_ATTEND_BF16 | KIVI_ATTEND_VARLEN)) != 0) return 0;
     // exactly the plan the matching call will make
@@ -195,8 +216,9 @@ int decode_attend_entry(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
     if (Hq % Hkv != 0) return KIVI_ERR_SHAPE;
     const int group = Hq / Hkv;
     if (group != 1 && group != 2 && group != 4 && group != 8) return KIVI_ERR_UNSUPPORTED;
-    if (n_quant + n_res == 0) return KIVI_ERR_SHAPE;
     if (n_quant >= kMaxAttendTokens || n_res >= kMaxAttendTokens) return KIVI_ERR_SHAPE;
+    if (n_quant + n_res == 0) return KIVI_ERR_SHAPE;
+    if (B > kMaxAttendSlabs / Hkv) return KIVI_ERR_SHAPE;              // B * Hkv slabs <= 65535
     if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) return KIVI_ERR_SHAPE;
     const int64_t slabs = B * Hkv;
     int rc = check_store(k, KIVI_KEYS, slabs, 0, n_quant);
@@ -220,7 +242,7 @@ int decode_attend_entry(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
         if ((rc = check_f16_tensor(v_res, slabs, rows, res_bh_stride, D)) != KIVI_OK) return rc;
     }
     const kivi::AttendPlan plan = kivi::plan_attend(B, Hq, Hkv, n_quant, n_res, seq_n_quant != nullptr, D, bf16);
-    if (plan.n_split > kMaxBlocks || slabs > 65535 || B * Hq > kMaxBlocks) return KIVI_ERR_SHAPE;
+    if (plan.n_split > kMaxBlocks || slabs > kMaxAttendSlabs || B * Hq > kMaxBlocks) return KIVI_ERR_SHAPE;
     if (static_scratch) {
         // the library's own array: a size check, then its device address
         if (plan.workspace_bytes > kivi::static_attend_scratch_bytes()) return KIVI_ERR_WORKSPACE;
@@ -332,7 +354,7 @@ const char* kivi_status_string(int status) {
 int kivi_last_hip_error(void) { return g_last_hip_error; }
 
 // The calibration kernels take one workgroup per 16 KiB: sizes up to
-// 2^31 - 1 workgroups.
+// 2^31 - 1 workgroups (below 2^45 bytes, inside the address space).
 static bool calib_size_ok(size_t n_bytes) { return n_bytes / 16384 < static_cast<size_t>(kMaxBlocks); }
 
 int kivi_calib_copy(const void* src, void* dst, size_t n_bytes, hipStream_t stream) {

@@ -58,23 +58,13 @@ __device__ __forceinline__ float4_t mfma(const Frag& a, const Frag& b, float4_t 
     else return __builtin_amdgcn_mfma_f32_16x16x32_f16(a.h, b.h, c, 0, 0, 0);
 }
 
-// Three waves per SIMD (at most 168 VGPRs, which hold three steps of loads
-// in flight without spilling; four would need 128 and spill), so the chip
-// holds 256 CUs x 4 SIMDs x 3 = 3072 of these waves at once.  Each wave
-// keeps KIVI_ATTEND_NBUF - 1 steps of loads in flight while it computes one.
-#ifndef KIVI_ATTEND_WAVES_PER_SIMD
-#define KIVI_ATTEND_WAVES_PER_SIMD 3
-#endif
 #ifndef KIVI_ATTEND_NBUF
 #define KIVI_ATTEND_NBUF 3
 #endif
 #define KIVI_ATTEND_OCCUPANCY __attribute__((amdgpu_waves_per_eu(KIVI_ATTEND_WAVES_PER_SIMD)))
-constexpr int64_t kWaveSlots = 256 * 4 * KIVI_ATTEND_WAVES_PER_SIMD;
-constexpr int64_t kWaveSlotsBF16 = 256 * 4 * 2;       // the bfloat16 instances, 2 per SIMD
 constexpr int kNBuf = KIVI_ATTEND_NBUF;
 
-constexpr int kStep = 32;             // tokens per wave step (one key group)
-constexpr int64_t kMaxStepsPerWave = 64;
+constexpr int kStep = kAttendStep;    // tokens per wave step (one key group)
 constexpr float kLog2e = 1.4426950408889634f;
 // The code-to-float trick: a code masked into the low mantissa bits under the
 // exponent of M reads as M + code exactly.  fp16 (10 fraction bits): M =

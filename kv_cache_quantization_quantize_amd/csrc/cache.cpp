@@ -270,11 +270,17 @@ size_t kivi_cache_attend_workspace_bytes(const kivi_cache* cache, int32_t Hq) {
     // largest plan over step counts 1 .. steps(capacity) + steps(ring) covers
     // every call the cache can make: at most 2^19 + 2^19 cheap plans.
     const int32_t flags = cache->cfg.bf16 ? KIVI_ATTEND_BF16 : 0;
-    const int64_t max_steps = (cache->cfg.store_capacity + 31) / 32 + (cache->ring + 31) / 32;
+    const int64_t steps_store = (cache->cfg.store_capacity + 31) / 32;
+    const int64_t max_steps = steps_store + (cache->ring + 31) / 32;
     size_t need = 0;
     for (int64_t steps = 1; steps <= max_steps; ++steps) {
+        // the same step count as a call with this many store and residual
+        // steps, each count within what a call of this cache can pass
+        const int64_t sq = std::min(steps, steps_store);
         const size_t b = kivi_decode_attend_workspace_bytes(cache->cfg.batch, Hq, cache->cfg.kv_heads,
-                                                            32 * steps, 0, cache->cfg.head_dim, flags);
+                                                            32 * sq, 32 * (steps - sq), cache->cfg.head_dim,
+                                                            flags);
+        if (b == 0) return 0;
         need = b > need ? b : need;
     }
     return need;

@@ -81,6 +81,19 @@ struct AttendArgs {
     int head_dim;                  // 128; others with groups of 32 and binary32 scale/zero
 };
 
+// Three waves per SIMD for the fp16 attend (at most 168 VGPRs, which hold
+// three steps of loads in flight without spilling; four would need 128 and
+// spill), so the chip holds 256 CUs x 4 SIMDs x 3 = 3072 of these waves at
+// once; the bfloat16 instances run two per SIMD.  Each wave keeps
+// KIVI_ATTEND_NBUF - 1 steps of loads in flight while it computes one.
+#ifndef KIVI_ATTEND_WAVES_PER_SIMD
+#define KIVI_ATTEND_WAVES_PER_SIMD 3
+#endif
+constexpr int64_t kWaveSlots = 256 * 4 * KIVI_ATTEND_WAVES_PER_SIMD;
+constexpr int64_t kWaveSlotsBF16 = 256 * 4 * 2;
+constexpr int kAttendStep = 32;                 // tokens per wave step (one key group)
+constexpr int64_t kMaxStepsPerWave = 64;
+
 // Split of the token axis chosen for an attend shape; the workspace holds
 // one (m, l, o[head_dim]) partial per (sequence, query head, split): the o
 // rows first, then the (m, l) pairs at ml_offset.
