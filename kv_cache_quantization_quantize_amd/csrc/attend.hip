@@ -10,33 +10,37 @@ namespace kivi {
 // Merge the splits of one (sequence, query head), base-2 log-sum-exp:
 // o = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i with M = max_i m_i.
 // WAVES waves per row: wave w takes splits w, w + WAVES, ..., lane l
-// channels 2l and 2l + 1 (lanes l < D/2); the waves' sums meet in LDS.  The
-// first kU splits of every wave are loaded together with their (m, l)
-// before the maximum is known, so a row of up to kU * WAVES splits costs one
-// memory round trip; only longer rows loop over the rest.
+// channels 2l and 2l + 1 (lanes l < D/2), and at head_dim 256 also 128 + 2l
+// and 129 + 2l; the waves' sums meet in LDS.  The first kU splits of every
+// wave are loaded together with their (m, l) before the maximum is known, so
+// a row of up to kU * WAVES splits costs one memory round trip; only longer
+// rows loop over the rest.
 template <int WAVES, int D>
 __global__ __launch_bounds__(64 * WAVES) void attend_combine_kernel(const float* __restrict__ ws_o,
                                                                    const float* __restrict__ ws_ml,
                                                                    int64_t n_part, float* __restrict__ out)
 {
     constexpr int kU = 4;
+    constexpr int kV = D > 128 ? D / 128 : 1;        // channel pairs per lane
     __shared__ float red_m[WAVES];
     __shared__ float red_l[WAVES];
-    __shared__ float2 red_o[WAVES][64];
+    __shared__ float2 red_o[WAVES][kV][64];
     const int64_t row = blockIdx.x;                  // b * Hq + h
     const int t = threadIdx.x;
     const int w = t >> 6;
     const int l = t & 63;
     const float* ml = ws_ml + row * n_part * 2;
     const float2* o = reinterpret_cast<const float2*>(ws_o + row * n_part * D) + l;
-    const bool has = l < D / 2;                      // the lane has channels (always at D = 128)
+    const bool has = l < D / 2;                      // the lane has channels (always at D >= 128)
 
-    float2 mv[kU], ov[kU];
+    float2 mv[kU], ov[kU][kV];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
         const int64_t i = w + static_cast<int64_t>(u) * WAVES;
         mv[u] = i < n_part ? *reinterpret_cast<const float2*>(ml + 2 * i) : make_float2(-INFINITY, 0.0f);
-        ov[u] = (i < n_part && has) ? o[i * (D / 2)] : make_float2(0.0f, 0.0f);
+#pragma unroll
+        for (int v = 0; v < kV; ++v)
+            ov[u][v] = (i < n_part && has) ? o[i * (D / 2) + 64 * v] : make_float2(0.0f, 0.0f);
     }
     float M = mv[0].x;
 #pragma unroll
@@ -51,38 +55,51 @@ __global__ __launch_bounds__(64 * WAVES) void attend_combine_kernel(const float*
     if (M == -INFINITY) M = 0.0f;
 
     float L = 0.0f;
-    float2 acc = make_float2(0.0f, 0.0f);
+    float2 acc[kV];
+#pragma unroll
+    for (int v = 0; v < kV; ++v) acc[v] = make_float2(0.0f, 0.0f);
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
         const float e = exp2f(mv[u].x - M);
         L = __builtin_fmaf(e, mv[u].y, L);
-        acc.x = __builtin_fmaf(e, ov[u].x, acc.x);
-        acc.y = __builtin_fmaf(e, ov[u].y, acc.y);
+#pragma unroll
+        for (int v = 0; v < kV; ++v) {
+            acc[v].x = __builtin_fmaf(e, ov[u][v].x, acc[v].x);
+            acc[v].y = __builtin_fmaf(e, ov[u][v].y, acc[v].y);
+        }
     }
     for (int64_t i = w + static_cast<int64_t>(kU) * WAVES; i < n_part; i += WAVES) {
         const float2 m2 = *reinterpret_cast<const float2*>(ml + 2 * i);
-        const float2 o2 = has ? o[i * (D / 2)] : make_float2(0.0f, 0.0f);
         const float e = exp2f(m2.x - M);
         L = __builtin_fmaf(e, m2.y, L);
-        acc.x = __builtin_fmaf(e, o2.x, acc.x);
-        acc.y = __builtin_fmaf(e, o2.y, acc.y);
+#pragma unroll
+        for (int v = 0; v < kV; ++v) {
+            const float2 o2 = has ? o[i * (D / 2) + 64 * v] : make_float2(0.0f, 0.0f);
+            acc[v].x = __builtin_fmaf(e, o2.x, acc[v].x);
+            acc[v].y = __builtin_fmaf(e, o2.y, acc[v].y);
+        }
     }
-    red_o[w][l] = acc;
+#pragma unroll
+    for (int v = 0; v < kV; ++v) red_o[w][v][l] = acc[v];
     if (l == 0) red_l[w] = L;
     __syncthreads();
     if (w == 0) {
         float Lt = red_l[0];
-        float2 at = red_o[0][l];
 #pragma unroll
-        for (int v = 1; v < WAVES; ++v) {
-            Lt += red_l[v];
-            at.x += red_o[v][l].x;
-            at.y += red_o[v][l].y;
+        for (int u = 1; u < WAVES; ++u) Lt += red_l[u];
+#pragma unroll
+        for (int v = 0; v < kV; ++v) {
+            float2 at = red_o[0][v][l];
+#pragma unroll
+            for (int u = 1; u < WAVES; ++u) {
+                at.x += red_o[u][v][l].x;
+                at.y += red_o[u][v][l].y;
+            }
+            // a sequence with no tokens at all (only possible in a variable-length
+            // batch) has every partial empty (m = -inf, l = 0): its output is zero
+            const float2 r = Lt > 0.0f ? make_float2(at.x / Lt, at.y / Lt) : make_float2(0.0f, 0.0f);
+            if (has) reinterpret_cast<float2*>(out + row * D)[l + 64 * v] = r;
         }
-        // a sequence with no tokens at all (only possible in a variable-length
-        // batch) has every partial empty (m = -inf, l = 0): its output is zero
-        const float2 r = Lt > 0.0f ? make_float2(at.x / Lt, at.y / Lt) : make_float2(0.0f, 0.0f);
-        if (has) reinterpret_cast<float2*>(out + row * D)[l] = r;
     }
 }
 
@@ -90,7 +107,8 @@ __global__ __launch_bounds__(64 * WAVES) void attend_combine_kernel(const float*
 hipError_t launch_decode_attend(const AttendArgs& a, const AttendPlan& p, hipStream_t stream) {
     float* ws_o = static_cast<float*>(a.workspace);
     float* ws_ml = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + p.ml_offset);
-    if (a.head_dim != 64 && a.head_dim != 128) return launch_attend_generic(a, p, ws_o, ws_ml, stream);
+    if (a.head_dim != 64 && a.head_dim != 128 && a.head_dim != 256)
+        return launch_attend_generic(a, p, ws_o, ws_ml, stream);
     hipError_t e;
     if (a.bf16) e = launch_attend_partial_bf16(a, p, ws_o, ws_ml, stream);
     else if (a.meta16) e = launch_partials<2, false>(a, p, ws_o, ws_ml, stream);
@@ -98,12 +116,19 @@ hipError_t launch_decode_attend(const AttendArgs& a, const AttendPlan& p, hipStr
     if (e != hipSuccess) return e;
     const dim3 rows_grid(static_cast<uint32_t>(a.B * a.Hq));
     const bool many = p.n_split >= 48;
-    if (a.head_dim == 64) {
-        if (many) hipLaunchKernelGGL((attend_combine_kernel<16, 64>), rows_grid, dim3(64 * 16), 0, stream, ws_o, ws_ml, p.n_split, a.out);
-        else hipLaunchKernelGGL((attend_combine_kernel<4, 64>), rows_grid, dim3(64 * 4), 0, stream, ws_o, ws_ml, p.n_split, a.out);
-    } else {
-        if (many) hipLaunchKernelGGL((attend_combine_kernel<16, 128>), rows_grid, dim3(64 * 16), 0, stream, ws_o, ws_ml, p.n_split, a.out);
-        else hipLaunchKernelGGL((attend_combine_kernel<4, 128>), rows_grid, dim3(64 * 4), 0, stream, ws_o, ws_ml, p.n_split, a.out);
+    const dim3 block(64 * (many ? 16 : 4));
+    switch (a.head_dim) {
+        case 64:
+            if (many) hipLaunchKernelGGL((attend_combine_kernel<16, 64>), rows_grid, block, 0, stream, ws_o, ws_ml, p.n_split, a.out);
+            else hipLaunchKernelGGL((attend_combine_kernel<4, 64>), rows_grid, block, 0, stream, ws_o, ws_ml, p.n_split, a.out);
+            break;
+        case 256:
+            if (many) hipLaunchKernelGGL((attend_combine_kernel<16, 256>), rows_grid, block, 0, stream, ws_o, ws_ml, p.n_split, a.out);
+            else hipLaunchKernelGGL((attend_combine_kernel<4, 256>), rows_grid, block, 0, stream, ws_o, ws_ml, p.n_split, a.out);
+            break;
+        default:
+            if (many) hipLaunchKernelGGL((attend_combine_kernel<16, 128>), rows_grid, block, 0, stream, ws_o, ws_ml, p.n_split, a.out);
+            else hipLaunchKernelGGL((attend_combine_kernel<4, 128>), rows_grid, block, 0, stream, ws_o, ws_ml, p.n_split, a.out);
     }
     return hipGetLastError();
 }

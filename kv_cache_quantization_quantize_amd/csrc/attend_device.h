@@ -243,19 +243,41 @@ struct LaneOffsets {
                             // groups 0, 1 (G = 64) or group 0 (G = 128)
 };
 
+// Channel geometry for head_dim D (64, 128 or 256).  QK^T: lane group q
+// holds channels kCPG*q + 8*kb + slot of key unit kb < kKB.  PV: MFMA i < kPV
+// covers channels kPV*m + i (m = 0..15), so lane (q, n) takes the kPV
+// channels kPV*n .. kPV*n + kPV - 1 of its tokens.  Lane l stages the key
+// scale/zero of kKMC channels (kKMC*l .. kKMC*l + kKMC - 1, lanes past D/kKMC
+// idle) and the value scale/zero of token l & 31, kVMG of its groups.
+template <int D> struct Geo {
+    static constexpr int kCPG = D / 4;          // channels per 16-lane group
+    static constexpr int kKB = D / 32;          // QK^T key units (MFMA k-steps)
+    static constexpr int kPV = D / 16;          // PV MFMAs
+    static constexpr int kKMC = D == 256 ? 4 : 2;
+};
+
+// The words of a lane's scale (or zero) load for staging: four channels or
+// groups at head_dim 256 (binary32 only), two otherwise.
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+template <int N> struct MetaWords { typedef u32x2 type; };
+template <> struct MetaWords<4> { typedef u32x4 type; };
 
 // Loads of one 32-token step of store tokens, issued one step ahead of the
 // compute that uses them.
 // Scale and zero stay as loaded (binary32 pairs, or binary16 pairs in the
 // low word) until the step that uses them, so that issuing a prefetch never
 // waits on an earlier load.
+template <int BITS, int G, int D>
 struct StepLoad {
-    uint32_t kw[2][4];      // key code words of token t0 + 16*blk + n (lane's 32 channels)
-    u32x2 ks, kz;           // key scale / zero of channels 2l, 2l+1 of the step's group
-    u32x2 vs, vz;           // value scale / zero of token t0 + (l & 31), groups 2(l>>5), +1
-    uint32_t vw[8];         // value code word holding the lane's 8 channels, its 8 tokens
+    // value scale/zero pairs a lane stages: the groups of token l & 31 split
+    // over lanes l and l + 32 when a token has 4 or 8 groups
+    static constexpr int kVMG = D / G >= 4 ? D / G / 2 : D / G;
+    static constexpr int kVW = (Geo<D>::kPV * BITS + 31) / 32;   // value code words per token
+    uint32_t kw[2][Geo<D>::kKB];   // key code word of unit kb, token t0 + 16*blk + n
+    typename MetaWords<Geo<D>::kKMC>::type ks, kz;   // key scale / zero of the lane's channels
+    typename MetaWords<kVMG == 4 ? 4 : 2>::type vs, vz;   // value scale / zero, token t0 + (l & 31)
+    uint32_t vw[8][kVW];    // value code words holding the lane's kPV channels, its 8 tokens
 };
 
 // The pair of a StepLoad field as floats: MB = 4 bytes (binary32) or 2
@@ -267,60 +289,72 @@ __device__ __forceinline__ float2 meta_pair(u32x2 v) {
     return make_float2(static_cast<float>(h[0]), static_cast<float>(h[1]));
 }
 
+template <int MB>
+__device__ __forceinline__ float4 meta_quad(u32x4 v) {
+    static_assert(MB == 4, "binary16 scale/zero are head_dim 128 only");
+    return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
+}
+
 // Token (within the step) of PV slot s for lane group q: the order in which
 // QK^T leaves each lane its scores (rows 4q .. 4q+3 of both 16-token blocks).
 __device__ __forceinline__ int pv_token(int q, int s) { return 16 * (s >> 2) + 4 * q + (s & 3); }
 
-// Channel geometry for head_dim D (128 or 64).  QK^T: lane group q holds
-// channels kCPG*q + 8*kb + slot of key unit kb < kKB.  PV: MFMA i < kPV covers
-// channels kPV*m + i (m = 0..15), so lane (q, n) takes the kPV channels
-// kPV*n .. kPV*n + kPV - 1 of its tokens.
-template <int D> struct Geo {
-    static constexpr int kCPG = D / 4;          // channels per 16-lane group
-    static constexpr int kKB = D / 32;          // QK^T key units (MFMA k-steps)
-    static constexpr int kPV = D / 16;          // PV MFMAs
-};
 
 template <int BITS, int G, int MB, int D>
-__device__ __forceinline__ void issue_step(StepLoad& L, const StoreView& S, const LaneOffsets& O,
+__device__ __forceinline__ void issue_step(StepLoad<BITS, G, D>& L, const StoreView& S, const LaneOffsets& O,
                                            uint32_t t0, int n) {
     constexpr uint32_t kRow = D * BITS / 8;                 // code bytes per token
     constexpr int kMPT = D / G;                             // value groups per token
+    constexpr int kKB = Geo<D>::kKB;
+    constexpr int kKBytes = Geo<D>::kCPG * BITS / 8;        // a lane group's key code bytes: 4 .. 32
     const uint32_t ko = O.k + t0 * kRow;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-        // the lane group's kCPG channels: kKB words (4-bit) or kKB / 2 (2-bit)
-        if constexpr (BITS == 4 && D == 128) {
-            const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(S.kc, ko + 16 * kRow * blk, 0, kStreamLoad);
-            L.kw[blk][0] = t.x; L.kw[blk][1] = t.y; L.kw[blk][2] = t.z; L.kw[blk][3] = t.w;
-        } else if constexpr (BITS == 4 || D == 128) {
-            const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(S.kc, ko + 16 * kRow * blk, 0, kStreamLoad);
-            if constexpr (BITS == 4) {
-                L.kw[blk][0] = t.x; L.kw[blk][1] = t.y;
-            } else {
-                L.kw[blk][0] = t.x; L.kw[blk][1] = t.x; L.kw[blk][2] = t.y; L.kw[blk][3] = t.y;
+        // the lane group's kCPG channels: one word per key unit (4-bit) or
+        // per two units (2-bit)
+        const uint32_t off = ko + 16 * kRow * blk;
+        uint32_t w[8];
+        if constexpr (kKBytes >= 16) {
+            const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(S.kc, off, 0, kStreamLoad);
+            w[0] = t.x; w[1] = t.y; w[2] = t.z; w[3] = t.w;
+            if constexpr (kKBytes == 32) {
+                const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(S.kc, off + 16, 0, kStreamLoad);
+                w[4] = u.x; w[5] = u.y; w[6] = u.z; w[7] = u.w;
             }
+        } else if constexpr (kKBytes == 8) {
+            const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(S.kc, off, 0, kStreamLoad);
+            w[0] = t.x; w[1] = t.y;
         } else {
-            const uint32_t t = __builtin_amdgcn_raw_buffer_load_b32(S.kc, ko + 16 * kRow * blk, 0, kStreamLoad);
-            L.kw[blk][0] = t; L.kw[blk][1] = t;
+            w[0] = __builtin_amdgcn_raw_buffer_load_b32(S.kc, off, 0, kStreamLoad);
         }
+#pragma unroll
+        for (int kb = 0; kb < kKB; ++kb) L.kw[blk][kb] = w[BITS == 4 ? kb : kb / 2];
     }
     // key metadata of the step's group (a 32-token step never crosses one):
-    // two channels' pairs, 2 * MB bytes
+    // the lane's kKMC channels' pairs, kKMC * MB bytes
     const uint32_t kmo = O.km + (t0 / G) * (D * MB);
-    // value metadata: D/G pairs per token; the lane's one or two groups
+    // value metadata: D/G pairs per token; the lane's groups
     const uint32_t vmo = O.vm + (D * MB / G) * t0;
     if constexpr (MB == 4) {
-        L.ks = __builtin_amdgcn_raw_buffer_load_b64(S.ks, kmo, 0, kStreamLoad);
-        L.kz = __builtin_amdgcn_raw_buffer_load_b64(S.kz, kmo, 0, kStreamLoad);
+        if constexpr (Geo<D>::kKMC == 4) {
+            L.ks = __builtin_amdgcn_raw_buffer_load_b128(S.ks, kmo, 0, kStreamLoad);
+            L.kz = __builtin_amdgcn_raw_buffer_load_b128(S.kz, kmo, 0, kStreamLoad);
+        } else {
+            L.ks = __builtin_amdgcn_raw_buffer_load_b64(S.ks, kmo, 0, kStreamLoad);
+            L.kz = __builtin_amdgcn_raw_buffer_load_b64(S.kz, kmo, 0, kStreamLoad);
+        }
         if constexpr (kMPT == 1) {
             L.vs = u32x2{__builtin_amdgcn_raw_buffer_load_b32(S.vs, vmo, 0, kStreamLoad), 0u};
             L.vz = u32x2{__builtin_amdgcn_raw_buffer_load_b32(S.vz, vmo, 0, kStreamLoad), 0u};
+        } else if constexpr (kMPT == 8) {
+            L.vs = __builtin_amdgcn_raw_buffer_load_b128(S.vs, vmo, 0, kStreamLoad);
+            L.vz = __builtin_amdgcn_raw_buffer_load_b128(S.vz, vmo, 0, kStreamLoad);
         } else {
             L.vs = __builtin_amdgcn_raw_buffer_load_b64(S.vs, vmo, 0, kStreamLoad);
             L.vz = __builtin_amdgcn_raw_buffer_load_b64(S.vz, vmo, 0, kStreamLoad);
         }
     } else {
+        static_assert(D == 128, "binary16 scale/zero are head_dim 128 only");
         L.ks = u32x2{__builtin_amdgcn_raw_buffer_load_b32(S.ks, kmo, 0, kStreamLoad), 0u};
         L.kz = u32x2{__builtin_amdgcn_raw_buffer_load_b32(S.kz, kmo, 0, kStreamLoad), 0u};
         if constexpr (kMPT == 1) {
@@ -337,9 +371,15 @@ __device__ __forceinline__ void issue_step(StepLoad& L, const StoreView& S, cons
     const uint32_t shift = (kPV * n * BITS) & 31;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-        const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(S.vc, vo + (16 * (s >> 2) + (s & 3)) * kRow, 0, kStreamLoad);
-        // bring the lane's channels to the low bits
-        L.vw[s] = (kPV * BITS == 32) ? w : (w >> shift);
+        const uint32_t off = vo + (16 * (s >> 2) + (s & 3)) * kRow;
+        if constexpr (StepLoad<BITS, G, D>::kVW == 2) {
+            const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(S.vc, off, 0, kStreamLoad);
+            L.vw[s][0] = t.x; L.vw[s][1] = t.y;
+        } else {
+            const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(S.vc, off, 0, kStreamLoad);
+            // bring the lane's channels to the low bits
+            L.vw[s][0] = (kPV * BITS >= 32) ? w : (w >> shift);
+        }
     }
 }
 
@@ -374,11 +414,13 @@ __device__ __forceinline__ Frag query_frag(const Smem<D>& sm, int kb, int l) {
     return f;
 }
 
-// Online-softmax state of one lane: head n, channels 32q + 8r + i of acc_o[i][r].
+// Online-softmax state of one lane: head n, channel kPV (4q + r) + i in
+// acc_o[i][r] (NPV = kPV accumulators).
+template <int NPV>
 struct SoftState {
     float m_run;
     float l_part;
-    float4_t acc_o[8];
+    float4_t acc_o[NPV];
 };
 
 // The running max m only moves when a step's max exceeds it by more than
@@ -397,8 +439,8 @@ constexpr float kSlack = 8.0f;
 // is split: the high part is p with its low 16 bits cleared (a bfloat16,
 // truncated), the low part the exact remainder rounded to bfloat16; PV
 // takes one MFMA for each and P keeps 2^-16 relative.
-template <bool MASK, bool BF>
-__device__ __forceinline__ Frag softmax_step(const float4_t (&acc_s)[2], SoftState& st, float c2,
+template <bool MASK, bool BF, int NPV>
+__device__ __forceinline__ Frag softmax_step(const float4_t (&acc_s)[2], SoftState<NPV>& st, float c2,
                                              int limit, int q, Frag& lo) {
     float sv[8];
 #pragma unroll
@@ -424,7 +466,7 @@ __device__ __forceinline__ Frag softmax_step(const float4_t (&acc_s)[2], SoftSta
     st.l_part = __builtin_fmaf(st.l_part, alpha, psum);
     if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) st.acc_o[i] *= alpha;
+        for (int i = 0; i < NPV; ++i) st.acc_o[i] *= alpha;
     }
     Frag bp;                                  // P^T, slot s <-> step token pv_token(q, s)
 #pragma unroll
@@ -444,8 +486,8 @@ __device__ __forceinline__ Frag softmax_step(const float4_t (&acc_s)[2], SoftSta
     return bp;
 }
 
-template <bool BF>
-__device__ __forceinline__ Frag softmax_any(const float4_t (&acc_s)[2], SoftState& st, float c2,
+template <bool BF, int NPV>
+__device__ __forceinline__ Frag softmax_any(const float4_t (&acc_s)[2], SoftState<NPV>& st, float c2,
                                             int limit, int q, Frag& lo) {
     if (limit >= kStep) return softmax_step<false, BF>(acc_s, st, c2, limit, q, lo);
     return softmax_step<true, BF>(acc_s, st, c2, limit, q, lo);
@@ -453,15 +495,28 @@ __device__ __forceinline__ Frag softmax_any(const float4_t (&acc_s)[2], SoftStat
 
 // One step of store tokens [t0, t0 + 32), tokens at or past n_quant masked.
 template <int BITS, int G, int MB, bool BF, int D>
-__device__ __forceinline__ void store_step(const StepLoad& L, Smem<D>& sm, SoftState& st,
-                                           int t0, int n_quant, float c2,
+__device__ __forceinline__ void store_step(const StepLoad<BITS, G, D>& L, Smem<D>& sm,
+                                           SoftState<Geo<D>::kPV>& st, int t0, int n_quant, float c2,
                                            int l, int n, int q) {
     // ---- stage this step's metadata in LDS (zero' = zero - M * scale')
     constexpr float kM = kCodeOffset<BITS, BF>;
     constexpr int kMPT = D / G;                 // value groups per token
     constexpr int kCPG = Geo<D>::kCPG, kKB = Geo<D>::kKB, kPV = Geo<D>::kPV;
     lds_order();
-    if (2 * l < D) {
+    if constexpr (Geo<D>::kKMC == 4) {
+        // channels 4l .. 4l + 3; key scale times 2^-e of each channel's code
+        // position (code_pairs)
+        const float4 ks = meta_quad<MB>(L.ks), kz = meta_quad<MB>(L.kz);
+        const float sc[4] = {ks.x, ks.y, ks.z, ks.w}, zc[4] = {kz.x, kz.y, kz.z, kz.w};
+        float so[4], zo[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            so[c] = sc[c] * kscale_factor<BITS, BF>(4 * l + c);
+            zo[c] = __builtin_fmaf(-kM, so[c], zc[c]);
+        }
+        *reinterpret_cast<float4*>(&sm.ks[kidx(4 * l)]) = make_float4(so[0], so[1], so[2], so[3]);
+        *reinterpret_cast<float4*>(&sm.kz[kidx(4 * l)]) = make_float4(zo[0], zo[1], zo[2], zo[3]);
+    } else if (2 * l < D) {
         // key scale times 2^-e of its channel's code position (code_pairs)
         const float2 ks = meta_pair<MB>(L.ks), kz = meta_pair<MB>(L.kz);
         const float s0 = ks.x * kscale_factor<BITS, BF>(2 * l);
@@ -470,7 +525,17 @@ __device__ __forceinline__ void store_step(const StepLoad& L, Smem<D>& sm, SoftS
         *reinterpret_cast<float2*>(&sm.kz[kidx(2 * l)]) =
             make_float2(__builtin_fmaf(-kM, s0, kz.x), __builtin_fmaf(-kM, s1, kz.y));
     }
-    {
+    if constexpr (kMPT == 8) {
+        // token l & 31, groups 4 (l >> 5) .. 4 (l >> 5) + 3
+        const float4 vs = meta_quad<MB>(L.vs), vz = meta_quad<MB>(L.vz);
+        const float sv[4] = {vs.x, vs.y, vs.z, vs.w}, zv[4] = {vz.x, vz.y, vz.z, vz.w};
+        const int tt = l & 31, gg = (l >> 5) * 4;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            sm.vs[gg + c][tt] = sv[c];
+            sm.vz[gg + c][tt] = __builtin_fmaf(-kM, sv[c], zv[c]);
+        }
+    } else {
         // lanes l and l + 32 hold the same token; with 2 groups or 1 per
         // token they hold the same groups too and write the same values
         const float2 vs = meta_pair<MB>(L.vs), vz = meta_pair<MB>(L.vz);
@@ -535,18 +600,22 @@ __device__ __forceinline__ void store_step(const StepLoad& L, Smem<D>& sm, SoftS
     if constexpr (kByteCodes<BITS, BF>) {
         // token slot s: the even channels' codes in the bytes of vlo, the odd
         // ones' in vhi; channel i of the lane's kPV is byte i/2 of one of them
-        uint32_t vlo[8], vhi[8];
+        constexpr int kVW = StepLoad<BITS, G, D>::kVW;
+        uint32_t vlo[8][kVW], vhi[8][kVW];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) split_nibbles(L.vw[t], vlo[t], vhi[t]);
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int w = 0; w < kVW; ++w) split_nibbles(L.vw[t][w], vlo[t][w], vhi[t][w]);
 #pragma unroll
         for (int i = 0; i < kPV; ++i) {
+            const int wi = i >> 3, ii = i & 7;          // word and place of channel i
             Frag va;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const uint32_t w0 = (i & 1) ? vhi[2 * j] : vlo[2 * j];
-                const uint32_t w1 = (i & 1) ? vhi[2 * j + 1] : vlo[2 * j + 1];
-                va.u[j] = bf16_pair(__builtin_fmaf(byte_f32(w0, i >> 1), vsc[2 * j], vzp[2 * j]),
-                                    __builtin_fmaf(byte_f32(w1, i >> 1), vsc[2 * j + 1], vzp[2 * j + 1]));
+                const uint32_t w0 = (ii & 1) ? vhi[2 * j][wi] : vlo[2 * j][wi];
+                const uint32_t w1 = (ii & 1) ? vhi[2 * j + 1][wi] : vlo[2 * j + 1][wi];
+                va.u[j] = bf16_pair(__builtin_fmaf(byte_f32(w0, ii >> 1), vsc[2 * j], vzp[2 * j]),
+                                    __builtin_fmaf(byte_f32(w1, ii >> 1), vsc[2 * j + 1], vzp[2 * j + 1]));
             }
             st.acc_o[i] = mfma<BF>(va, bp, st.acc_o[i]);
             st.acc_o[i] = mfma<BF>(va, bp_lo, st.acc_o[i]);
@@ -555,15 +624,18 @@ __device__ __forceinline__ void store_step(const StepLoad& L, Smem<D>& sm, SoftS
     }
 #pragma unroll
     for (int i = 0; i < kPV; ++i) {
-        // code of channel i of the lane's kPV (4-bit: nibble i; 2-bit: field i)
+        // code of channel i of the lane's kPV: word wi, field ii (4-bit:
+        // nibble ii; 2-bit: two-bit field ii)
         constexpr uint32_t kMask = BITS == 4 ? 0x000F000Fu : 0x00030003u;
-        const uint32_t byte = BITS == 4 ? (i >> 1) : (i >> 2);
-        const uint32_t shift = BITS == 4 ? 4 * (i & 1) : 2 * (i & 3);
+        constexpr int kCPW = 32 / BITS;
+        const int wi = i / kCPW, ii = i % kCPW;
+        const uint32_t byte = BITS == 4 ? (ii >> 1) : (ii >> 2);
+        const uint32_t shift = BITS == 4 ? 4 * (ii & 1) : 2 * (ii & 3);
         const uint32_t sel = 0x0C000C00u | ((4u + byte) << 16) | byte;
         Frag va;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const uint32_t x = __builtin_amdgcn_perm(L.vw[2 * j + 1], L.vw[2 * j], sel);
+            const uint32_t x = __builtin_amdgcn_perm(L.vw[2 * j + 1][wi], L.vw[2 * j][wi], sel);
             const uint32_t pr = and_or(x >> shift, kMask, kMagic<BF>);
             va.u[j] = deq2<BF>(pr, vsc[2 * j], vzp[2 * j], vsc[2 * j + 1], vzp[2 * j + 1]);
         }
@@ -581,7 +653,7 @@ __device__ __forceinline__ int ring_row(int tok, int head, int ring) {
 
 template <int BITS, bool BF, int D>
 __device__ __forceinline__ void residual_step(const uint16_t* kr, const uint16_t* vr, const Smem<D>& sm,
-                                              SoftState& st, int t0, int n_res, float c2,
+                                              SoftState<Geo<D>::kPV>& st, int t0, int n_res, float c2,
                                               int l, int n, int q, int head, int ring) {
     constexpr int kCPG = Geo<D>::kCPG, kKB = Geo<D>::kKB, kPV = Geo<D>::kPV;
     const int last = n_res - 1;
@@ -621,9 +693,12 @@ __device__ __forceinline__ void residual_step(const uint16_t* kr, const uint16_t
     for (int s = 0; s < 8; ++s) {
         const int tok = ring_row(min(t0 + pv_token(q, s), last), head, ring);
         const uint16_t* p = vr + tok * D + kPV * n;
-        if constexpr (kPV == 8) {
-            const uint4 t = *reinterpret_cast<const uint4*>(p);
-            vw[s][0] = t.x; vw[s][1] = t.y; vw[s][2] = t.z; vw[s][3] = t.w;
+        if constexpr (kPV >= 8) {
+#pragma unroll
+            for (int v = 0; v < kPV / 8; ++v) {
+                const uint4 t = reinterpret_cast<const uint4*>(p)[v];
+                vw[s][4 * v] = t.x; vw[s][4 * v + 1] = t.y; vw[s][4 * v + 2] = t.z; vw[s][4 * v + 3] = t.w;
+            }
         } else {
             const uint2 t = *reinterpret_cast<const uint2*>(p);
             vw[s][0] = t.x; vw[s][1] = t.y;
@@ -647,9 +722,21 @@ __device__ __forceinline__ void residual_step(const uint16_t* kr, const uint16_t
 // Offsets within a slab fit in 32 bits: the ABI keeps n_quant and n_res
 // below 2^24 tokens.
 // bfloat16 instances run at 2 waves per SIMD: their dequantization needs
-// about 190 VGPRs, and at 3 waves (168) they spilled to scratch.
+// about 190 VGPRs, and at 3 waves (168) they spilled to scratch.  Head_dim
+// 256 doubles every per-lane array (16 PV accumulators, 64 key channels per
+// lane group) and also runs at 2 waves.
+#ifndef KIVI_ATTEND_BF16_D256_WAVES
+#define KIVI_ATTEND_BF16_D256_WAVES 1
+#endif
+#ifndef KIVI_ATTEND_BF16_D256_NBUF
+#define KIVI_ATTEND_BF16_D256_NBUF 3
+#endif
+template <bool BF, int D> constexpr int kWavesPerSimd =
+    (BF && D == 256) ? KIVI_ATTEND_BF16_D256_WAVES : (BF || D == 256) ? 2 : KIVI_ATTEND_WAVES_PER_SIMD;
+template <bool BF, int D> constexpr int kNBufOf = (BF && D == 256) ? KIVI_ATTEND_BF16_D256_NBUF : D == 256 ? 2 : kNBuf;
+
 template <int BITS, int GQA, int G, int MB, bool BF, int D>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(BF ? 2 : KIVI_ATTEND_WAVES_PER_SIMD))) void attend_partial_kernel(const AttendArgs a, int spw, int steps_q,
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<BF, D>))) void attend_partial_kernel(const AttendArgs a, int spw, int steps_q,
                                                             int64_t n_split, float* __restrict__ ws_o,
                                                             float* __restrict__ ws_ml)
 {
@@ -683,9 +770,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(BF ? 2 : KIV
     // the query so the two HBM latencies overlap.
     constexpr int kWords = D * BITS / 32;
     constexpr int kMetaPerTok = D / G;
+    constexpr int kNB = kNBufOf<BF, D>;
     StoreView S;
     LaneOffsets O;
-    StepLoad buf[kNBuf];
+    StepLoad<BITS, G, D> buf[kNB];
     // Every prefetch is issued, also past the split's end (to a token far
     // outside the buffers' extent, which the buffer unit answers with zeros
     // and no memory access): a conditional issue makes the compiler wait for
@@ -707,11 +795,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(BF ? 2 : KIV
         // token row; the lane's PV channels at word kPV * n * BITS / 32
         O.k = static_cast<uint32_t>(n * kWords + kCPG * q * BITS / 32) * 4u;
         O.v = static_cast<uint32_t>(4 * q * kWords + kPV * n * BITS / 32) * 4u;
-        O.km = static_cast<uint32_t>(l) * (2u * MB);      // lanes past D/2 load but stage nothing
-        O.vm = kMetaPerTok == 4 ? static_cast<uint32_t>(l & 31) * (4u * MB) + static_cast<uint32_t>(l >> 5) * (2u * MB)
-                                : static_cast<uint32_t>(l & 31) * (kMetaPerTok * MB);
+        // lanes past D / kKMC load but stage nothing
+        O.km = static_cast<uint32_t>(l) * (Geo<D>::kKMC * MB);
+        O.vm = kMetaPerTok >= 4
+                   ? static_cast<uint32_t>(l & 31) * (kMetaPerTok * MB) +
+                         static_cast<uint32_t>(l >> 5) * (kMetaPerTok / 2 * MB)
+                   : static_cast<uint32_t>(l & 31) * (kMetaPerTok * MB);
 #pragma unroll
-        for (int u = 0; u + 1 < kNBuf; ++u) issue_step<BITS, G, MB, D>(buf[u], S, O, pref(j0 + u * kStep), n);
+        for (int u = 0; u + 1 < kNB; ++u) issue_step<BITS, G, MB, D>(buf[u], S, O, pref(j0 + u * kStep), n);
     }
 
     // B operand of QK^T: q of head n (zero for n >= GQA) in slot order.
@@ -750,19 +841,19 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(BF ? 2 : KIV
     }
 
     const float c2 = a.softmax_scale * kLog2e;
-    SoftState st;
+    SoftState<kPV> st;
     st.m_run = -INFINITY;
     st.l_part = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) st.acc_o[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int i = 0; i < kPV; ++i) st.acc_o[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
     if (has_store) {
-        // kNBuf buffers in rotation: while step t computes, the loads of the
-        // next kNBuf - 1 steps are in flight.
-        for (int t0 = j0; t0 < j1; t0 += kNBuf * kStep) {
+        // kNB buffers in rotation: while step t computes, the loads of the
+        // next kNB - 1 steps are in flight.
+        for (int t0 = j0; t0 < j1; t0 += kNB * kStep) {
 #pragma unroll
-            for (int u = 0; u < kNBuf; ++u) {
-                issue_step<BITS, G, MB, D>(buf[(u + kNBuf - 1) % kNBuf], S, O, pref(t0 + (u + kNBuf - 1) * kStep), n);
+            for (int u = 0; u < kNB; ++u) {
+                issue_step<BITS, G, MB, D>(buf[(u + kNB - 1) % kNB], S, O, pref(t0 + (u + kNB - 1) * kStep), n);
                 store_step<BITS, G, MB, BF, D>(buf[u], sm, st, t0 + u * kStep, j1, c2, l, n, q);
                 if (t0 + (u + 1) * kStep >= j1) goto store_done;
             }
@@ -782,13 +873,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(BF ? 2 : KIV
     if (n < GQA) {
         float* dst = ws_o + ((qrow0 + n) * n_split + split) * D + kCPG * q;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            *reinterpret_cast<float4*>(dst + kPV * r) =
-                make_float4(st.acc_o[0][r], st.acc_o[1][r], st.acc_o[2][r], st.acc_o[3][r]);
-            if constexpr (kPV == 8)
-                *reinterpret_cast<float4*>(dst + kPV * r + 4) =
-                    make_float4(st.acc_o[4][r], st.acc_o[5][r], st.acc_o[6][r], st.acc_o[7][r]);
-        }
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int c = 0; c < kPV / 4; ++c)
+                *reinterpret_cast<float4*>(dst + kPV * r + 4 * c) =
+                    make_float4(st.acc_o[4 * c][r], st.acc_o[4 * c + 1][r], st.acc_o[4 * c + 2][r],
+                                st.acc_o[4 * c + 3][r]);
         if (q == 0) {
             float* ml = ws_ml + ((qrow0 + n) * n_split + split) * 2;
             ml[0] = st.m_run;
@@ -829,10 +919,13 @@ hipError_t launch_partials(const AttendArgs& a, const AttendPlan& p, float* ws_o
                            hipStream_t stream) {
     const bool four = a.bits == 4;
     if constexpr (MB == 4) {
-        // head_dim 64 (groups of 32, binary32 scale/zero)
+        // head_dim 64 and 256 (groups of 32, binary32 scale/zero)
         if (a.head_dim == 64)
             return four ? launch_partial_gqa<4, 32, MB, BF, 64>(a, p, ws_o, ws_ml, stream)
                         : launch_partial_gqa<2, 32, MB, BF, 64>(a, p, ws_o, ws_ml, stream);
+        if (a.head_dim == 256)
+            return four ? launch_partial_gqa<4, 32, MB, BF, 256>(a, p, ws_o, ws_ml, stream)
+                        : launch_partial_gqa<2, 32, MB, BF, 256>(a, p, ws_o, ws_ml, stream);
     }
     switch (a.group) {
         case 64: return four ? launch_partial_gqa<4, 64, MB, BF>(a, p, ws_o, ws_ml, stream)

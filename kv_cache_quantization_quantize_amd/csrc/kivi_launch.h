@@ -90,7 +90,7 @@ struct AttendArgs {
 #define KIVI_ATTEND_WAVES_PER_SIMD 3
 #endif
 constexpr int64_t kWaveSlots = 256 * 4 * KIVI_ATTEND_WAVES_PER_SIMD;
-constexpr int64_t kWaveSlotsBF16 = 256 * 4 * 2;
+constexpr int64_t kWaveSlotsBF16 = 256 * 4 * 2;    // also the head_dim 256 kernels
 constexpr int kAttendStep = 32;                 // tokens per wave step (one key group)
 constexpr int64_t kMaxStepsPerWave = 64;
 

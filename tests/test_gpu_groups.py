@@ -7,6 +7,7 @@ import pytest
 import torch
 
 import oracle
+from oracle_pool import pmap
 from gpu_util import (CODE_SENTINEL, META_SENTINEL, assert_store_equal, assert_u16_equal, note, u16)
 from kv_cache_quantization_quantize_amd import kivi, synth
 
@@ -292,10 +293,11 @@ def test_attend_generic_plans(case, Dh, fmt):
 @pytest.mark.parametrize("Dh", [256, 96, 80, 16])
 @pytest.mark.parametrize("case", GENERIC, ids=lambda c: "B%d-Hq%d-Hkv%d-nq%d-nr%d-b%d" % c)
 def test_attend_generic_head_dims(case, Dh, fmt):
-    """The decode attends at head_dims the MFMA kernels do not take (256 and
-    the ragged ones; groups of 32): the generic kernel rebuilds K and V
-    exactly as stored and rounds no probabilities, so it is held to 2e-3 in
-    both formats; uniform and variable-length against the oracle."""
+    """The decode attends at head_dim 256 (the MFMA kernel, 16 PV
+    accumulators per lane) and at the ragged head_dims (the generic kernel,
+    which rebuilds K and V exactly as stored and rounds no probabilities);
+    groups of 32, held to 2e-3 in both formats; uniform and variable-length
+    against the oracle."""
     B, Hq, Hkv, nq, nr, bits = case
     BH = B * Hkv
     cap = max(32, ((nq + 31) // 32) * 32)
@@ -334,3 +336,39 @@ def test_attend_generic_head_dims(case, Dh, fmt):
                                         nr_h, nr, fmt=fmt)
     err = float(np.max(np.abs(out_v.cpu().numpy().astype(np.float64) - ref_v)))
     assert err <= 2e-3, f"varlen max-abs error {err:.3e}"
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("bits", [4, 2])
+def test_attend_head_dim_256_at_the_bench_shape(fmt, bits):
+    """head_dim 256 at the bench's B=32 x 2048 + 128 shape (32 query heads
+    over 8 kv heads, several steps per wave): sampled sequences against the
+    oracle within 2e-3."""
+    B, Hq, Hkv, nq, nr, Dh = 32, 32, 8, 2048, 128, 256
+    BH = B * Hkv
+    seed = 9700 + bits
+    dtype = torch.bfloat16 if fmt == "bf16" else torch.float16
+    kx = synth.kv_tensor(BH, nq, Dh, keys=True, seed=seed, device="cuda", dtype=dtype)
+    vx = synth.kv_tensor(BH, nq, Dh, keys=False, seed=seed, device="cuda", dtype=dtype)
+    kr = synth.residual(BH, nr, Dh, keys=True, seed=seed, device="cuda").to(dtype)
+    vr = synth.residual(BH, nr, Dh, keys=False, seed=seed, device="cuda").to(dtype)
+    q = synth.query(B, Hq, Dh, seed=seed, device="cuda").to(dtype)
+    ks = kivi.Store(kivi.KIVI_KEYS, BH, nq, bits, head_dim=Dh)
+    vs = kivi.Store(kivi.KIVI_VALUES, BH, nq, bits, head_dim=Dh)
+    note(f"attend head_dim 256 {fmt} bits={bits} B={B} S_kv={nq}+{nr}")
+    kivi.quantize_keys(kx, ks, 0)
+    kivi.quantize_values(vx, vs, 0)
+    out = kivi.decode_attend(q, ks, vs, nq, kr, vr, nr).cpu().numpy()
+    hq, hkx, hvx, hkr, hvr = u16(q), u16(kx), u16(vx), u16(kr), u16(vr)
+
+    def one(b):
+        sl = slice(b * Hkv, (b + 1) * Hkv)
+        hk = oracle.Store(oracle.KEYS, Hkv, nq, Dh, bits, 32)
+        hv = oracle.Store(oracle.VALUES, Hkv, nq, Dh, bits, 32)
+        oracle.quantize_keys(hkx[sl], hk, 0, want_recon=False, fmt=fmt)
+        oracle.quantize_values(hvx[sl], hv, 0, want_recon=False, fmt=fmt)
+        return oracle.decode_attend(hq[b:b + 1], 1, Hq, Hkv, hk, hv, nq, hkr[sl], hvr[sl], nr, fmt=fmt)[0]
+    samples = [0, 13, 31]
+    for b, ref in zip(samples, pmap(one, samples)):
+        err = float(np.max(np.abs(out[b].astype(np.float64) - ref)))
+        assert err <= 2e-3, f"sequence {b}: max-abs error {err:.3e}"
