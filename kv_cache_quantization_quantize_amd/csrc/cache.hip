@@ -5,7 +5,7 @@
 // "What we're actually optimizing": the newest residual_length tokens stay
 // fp16, older ones are flushed in whole groups).
 //
-// One launch moves keys and values (blockIdx.y).  Row r of a slab comes
+// One launch moves keys and values (blockIdx.z).  Row r of a slab comes
 // from span a (rows [0, n_a)) or span b (the rest) and goes to span dst;
 // a span may be a ring, whose row index wraps.  Each lane moves 16 bytes,
 // head_dim/8 lanes one token row (16 lanes at head_dim 128), so a wave
@@ -17,38 +17,57 @@ namespace kivi {
 
 namespace {
 
-__device__ __forceinline__ int64_t span_row(const RowSpan& s, int64_t r) {
-    const int64_t i = s.first + r;
-    return s.ring > 0 ? i % s.ring : i;
+// Row i of a span within one slab (row counts stay below 2^26, so 32-bit
+// arithmetic suffices).
+__device__ __forceinline__ int span_row(int first, int ring, int i) {
+    const int r = first + i;
+    return ring > 0 ? r % ring : r;
 }
 
 }  // namespace
 
+// Grid: x covers the rows x lanes of one slab (lane = 16 bytes of a row),
+// y strides over the slabs, z = 0 keys, 1 values.  LANES = head_dim / 8 for
+// the common head_dims (shifts), 0 for a runtime count.  Each field of the
+// gather is picked on its own (a scalar select), so nothing goes through
+// private memory.
+template <int LANES>
 __global__ __launch_bounds__(256) void gather_rows_kernel(const RowGather k, const RowGather v, int64_t slabs,
-                                                          int64_t n_rows, int D)
+                                                          int n_rows, int lanes_rt)
 {
-    const RowGather& c = blockIdx.y == 0 ? k : v;
-    const int kLanesPerRow = D / 8;                    // head_dim is a multiple of 16
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    const int64_t total = slabs * n_rows * kLanesPerRow;
-    if (i >= total) return;
-    const int64_t lane = i % kLanesPerRow;
-    const int64_t row_all = i / kLanesPerRow;
-    const int64_t slab = row_all / n_rows;
-    const int64_t row = row_all - slab * n_rows;
-    const bool from_a = row < c.n_a;
-    const RowSpan& s = from_a ? c.a : c.b;
-    const int64_t srow = span_row(s, from_a ? row : row - c.n_a);
-    const uint4* src = reinterpret_cast<const uint4*>(s.base + slab * s.bh_stride + srow * D) + lane;
-    uint4* dst = reinterpret_cast<uint4*>(c.dst.base + slab * c.dst.bh_stride + span_row(c.dst, row) * D) + lane;
-    *dst = *src;
+    const bool is_v = blockIdx.z != 0;
+    const int lanes = LANES ? LANES : lanes_rt;
+    const int idx = static_cast<int>(blockIdx.x) * 256 + static_cast<int>(threadIdx.x);
+    if (idx >= n_rows * lanes) return;
+    const int row = LANES ? idx / LANES : idx / lanes;
+    const int lane = idx - row * lanes;
+    const int D = lanes * 8;
+    const int n_a = static_cast<int>(is_v ? v.n_a : k.n_a);
+    const bool from_a = row < n_a;
+    const RowSpan src = is_v ? (from_a ? v.a : v.b) : (from_a ? k.a : k.b);
+    const RowSpan dst = is_v ? v.dst : k.dst;
+    const int64_t srow = span_row(static_cast<int>(src.first), static_cast<int>(src.ring), from_a ? row : row - n_a);
+    const int64_t drow = span_row(static_cast<int>(dst.first), static_cast<int>(dst.ring), row);
+    for (int64_t slab = blockIdx.y; slab < slabs; slab += gridDim.y) {
+        const uint4* from = reinterpret_cast<const uint4*>(src.base + slab * src.bh_stride + srow * D) + lane;
+        uint4* to = reinterpret_cast<uint4*>(dst.base + slab * dst.bh_stride + drow * D) + lane;
+        *to = *from;
+    }
 }
 
 hipError_t launch_gather_rows(const RowGather& k, const RowGather& v, int64_t slabs, int64_t n_rows, int D,
                               hipStream_t stream) {
-    const int64_t total = slabs * n_rows * (D / 8);
-    const dim3 grid(static_cast<uint32_t>((total + 255) / 256), 2);
-    hipLaunchKernelGGL(gather_rows_kernel, grid, dim3(256), 0, stream, k, v, slabs, n_rows, D);
+    const int lanes = D / 8;                           // head_dim is a multiple of 16
+    const int64_t per_slab = n_rows * lanes;           // below 2^31: n_rows < 2^26, lanes <= 32
+    const dim3 grid(static_cast<uint32_t>((per_slab + 255) / 256),
+                    static_cast<uint32_t>(slabs < 65535 ? slabs : 65535), 2);
+    const int nr = static_cast<int>(n_rows);
+    switch (lanes) {
+        case 8: hipLaunchKernelGGL(gather_rows_kernel<8>, grid, dim3(256), 0, stream, k, v, slabs, nr, lanes); break;
+        case 16: hipLaunchKernelGGL(gather_rows_kernel<16>, grid, dim3(256), 0, stream, k, v, slabs, nr, lanes); break;
+        case 32: hipLaunchKernelGGL(gather_rows_kernel<32>, grid, dim3(256), 0, stream, k, v, slabs, nr, lanes); break;
+        default: hipLaunchKernelGGL(gather_rows_kernel<0>, grid, dim3(256), 0, stream, k, v, slabs, nr, lanes);
+    }
     return hipGetLastError();
 }
 
