@@ -4,12 +4,12 @@ same stores (written by the bfloat16 flushes) and the same bfloat16 query and
 residual rows.
 
 Tolerance: 2e-3 max-abs, the same bar as the fp16 attend.  The kernel's own
-error sources are the softmax probabilities rounded to bfloat16 for PV
-(relative 2^-9 each) and an in-register reconstruction that can differ from
-the stored one by one bfloat16 rounding where the two roundings straddle a
-boundary; both are independent per token, so on these caches (values of
-order 1) they stay well inside the bar.  Only the test whose values are
-scaled to 1e6 is held to a bound relative to its values."""
+error sources are the softmax probabilities, which enter PV as a truncated
+bfloat16 high part plus the rounded remainder (relative 2^-16), and an
+in-register reconstruction that can differ from the stored one by one
+bfloat16 rounding where the two roundings straddle a boundary.  The test
+whose values are scaled by 10^6 holds the same bar scaled by 10^6 (every
+error term is relative to the values)."""
 import numpy as np
 import pytest
 import torch
@@ -85,10 +85,10 @@ def test_bf16_attend(case):
 
 
 def test_bf16_values_outside_fp16_range():
-    """A bfloat16 cache whose values exceed fp16's range (1e6): the attend
-    stays in bfloat16 throughout, so the result is finite and matches to
-    2^-8 of the largest value (bfloat16's relative precision; the absolute
-    2e-3 bar is for values of order 1)."""
+    """A bfloat16 cache whose values exceed fp16's range (values of order 1
+    scaled by 10^6): the attend stays in bfloat16 throughout, so the result
+    is finite and within 2e-3 x 10^6 of the oracle (the order-1 bar scaled
+    with the values)."""
     B, Hq, Hkv, nq, nr = 1, 8, 2, 256, 16
     BH = B * Hkv
     kx = _bf16(synth.kv_tensor(BH, nq, keys=True, seed=5, device="cuda", dtype=torch.bfloat16))
@@ -110,8 +110,8 @@ def test_bf16_values_outside_fp16_range():
     ref = oracle.decode_attend(u16(q), B, Hq, Hkv, hk, hv, nq, u16(kr), u16(vr), nr, fmt="bf16")
     got = out.cpu().numpy().astype(np.float64)
     assert np.all(np.isfinite(got))
-    vmax = max(float(vx.float().abs().max()), float(vr.float().abs().max()))
-    assert float(np.max(np.abs(got - ref))) <= 2.0 ** -8 * vmax
+    err = float(np.max(np.abs(got - ref)))
+    assert err <= 2e-3 * 1e6, f"max-abs error {err:.3e}"
 
 
 def test_full_size_bf16_attend():
