@@ -1,6 +1,6 @@
 // attend_generic.hip -- the decode attend at the head_dims the MFMA kernels
-// of attend_device.h do not take: 256 and the multiples of 16 other than 64
-// and 128, with groups of 32 and binary32 scale/zero, for fp16 and bfloat16
+// of attend_device.h do not take: the multiples of 16 other than 64, 128
+// and 256, with groups of 32 and binary32 scale/zero, for fp16 and bfloat16
 // caches.
 //
 // Sources, cited by page title and section:
@@ -209,7 +209,8 @@ __global__ __launch_bounds__(64) void attend_generic_kernel(const AttendArgs a, 
 }
 
 // Merge of the splits for any head_dim <= 256: lane l takes channels l,
-// l + 64, ... (the MFMA kernels' combine takes channel pairs at 64 and 128).
+// l + 64, ... (the MFMA kernels' combine takes channel pairs at 64, 128 and
+// 256).
 template <int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void attend_combine_any_kernel(const float* __restrict__ ws_o,
                                                                        const float* __restrict__ ws_ml,

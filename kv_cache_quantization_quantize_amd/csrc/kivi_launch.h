@@ -111,8 +111,9 @@ hipError_t launch_key_flush(const FlushArgs& a, hipStream_t stream);
 hipError_t launch_value_flush(const FlushArgs& a, hipStream_t stream);
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t stream);
 hipError_t launch_decode_attend(const AttendArgs& a, const AttendPlan& p, hipStream_t stream);
-// the attend at head_dims other than 64 and 128 (groups of 32, binary32
-// scale/zero): partials and combine (one wave per workgroup, two launches)
+// the attend at head_dims other than 64, 128 and 256 (groups of 32,
+// binary32 scale/zero): partials and combine (one wave per workgroup, two
+// launches)
 hipError_t launch_attend_generic(const AttendArgs& a, const AttendPlan& p, float* ws_o, float* ws_ml,
                                  hipStream_t stream);
 // head_dims other than 64, 128 and 256 (multiples of 16 up to 256, groups of 32)
