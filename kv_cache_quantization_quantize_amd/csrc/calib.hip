@@ -9,8 +9,12 @@
 //   mix    read n bytes, write 3n/8 bytes: the 4-bit flush's shape (2 B of
 //          fp16 in for 0.5 B of codes + 0.25 B of scale/zero per element).
 // Workgroup b owns one contiguous chunk; every thread issues all of its
-// 16-byte loads before its first store, with the nontemporal hint (each byte
-// is touched once, as in the flush and the attend).
+// 16-byte loads before its first store.  Each kernel uses the cache hints
+// that measured fastest for its shape on MI355X (interleaved runs, 2 GiB):
+// the nontemporal hint on loads and stores for copy, read and mix (each byte
+// is touched once, as in the flush and the attend; plain stores made the mix
+// 10% slower and plain loads the read 17% slower), plain stores for the
+// write-only kernel (6.0-6.3 TB/s against 5.7-5.8 with the hint).
 #include "kivi_device.h"
 #include "kivi_launch.h"
 
@@ -69,7 +73,7 @@ __global__ __launch_bounds__(kCalibBlock) void calib_write_kernel(v4u* __restric
 #pragma unroll
     for (int u = 0; u < kCalibVecs; ++u) {
         const int64_t i = base + u * kCalibBlock;
-        if (i < n_vec) st_nt(dst + i, v4u{pattern, pattern ^ static_cast<uint32_t>(i), pattern, 0u});
+        if (i < n_vec) dst[i] = v4u{pattern, pattern ^ static_cast<uint32_t>(i), pattern, 0u};
     }
 }
 
