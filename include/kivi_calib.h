@@ -8,8 +8,10 @@
  * a copy (read n, write n), a pure read (the decode attend's shape), a pure
  * write, and a flush-shaped mix (read n, write 3n/8: 2 B in per 0.75 B out,
  * the 4-bit flush's ratio).  Each moves every byte once, with 16-byte
- * accesses and the cache hints that measured fastest for its shape (the
- * nontemporal hint, except plain stores for the pure write); the bytes/s
+ * accesses, and with the cache hints and the number of workgroups resident
+ * per CU that measured fastest for its shape (the nontemporal hint, except
+ * plain stores for the pure write; 3 to 5 workgroups of 4 waves per CU,
+ * held there by LDS each launch reserves and never touches); the bytes/s
  * they reach bound what a kernel with the same read/write mix can reach.
  *
  * Every pointer is device memory, 16-byte aligned; sizes are multiples of
