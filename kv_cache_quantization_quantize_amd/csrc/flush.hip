@@ -395,13 +395,38 @@ __global__ __launch_bounds__(kBlock) void value_flush_kernel(
 // ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
+
+// Workgroups a flush lets reside on one CU (0: as many as its registers
+// allow, 8 for these kernels).  A cap is held by LDS the launch reserves and
+// never touches (160 KiB per CU on gfx950).  Measured on the full 32k cache,
+// interleaved against the uncapped kernels: at fp16 input and head_dim 128
+// the key flush ran 2-3% faster at 5 per CU (4 bits, groups of 32; 5% at 2
+// bits, 7% with binary16 scale/zero) and the value flush whose scale and
+// zero go out through LDS (groups of 32, binary32) 5-6% faster at 4 per CU,
+// as the streaming calibration kernels did; fewer requests in flight at once
+// suit the memory system.  bfloat16 input, head_dim 64 and the
+// reconstructing flushes ran 1-7% slower with a cap, and the other value
+// configurations 2-5% slower, so they keep the full residency.
+template <bool KEYS, bool RECON, bool BF16, int G, int D, typename MT>
+constexpr int kFlushPerCU = (BF16 || RECON || D != 128) ? 0
+                            : KEYS ? 5 : (kGatherMeta<G, D, MT> ? 4 : 0);
+
+// The dynamic LDS bytes that hold a launch to per_cu workgroups per CU, on
+// top of static_bytes of its own (0 for no cap).
+static size_t residency_lds(int per_cu, size_t static_bytes) {
+    if (per_cu <= 0) return 0;
+    const size_t per_block = (size_t{160} * 1024 / static_cast<size_t>(per_cu)) / 1024 * 1024;
+    return per_block > static_bytes ? per_block - static_bytes : 0;
+}
+
 template <int BITS, bool RECON, bool BF16, int G, int D, typename MT>
 static hipError_t launch_keys_t(const FlushArgs& a, hipStream_t stream) {
     const int64_t n_groups = (a.S + G - 1) / G;
     const int64_t n_tiles = a.BH * n_groups;
     const int64_t blocks = (n_tiles + kWavesPerBlock - 1) / kWavesPerBlock;
+    const size_t lds = residency_lds(kFlushPerCU<true, RECON, BF16, G, D, MT>, 0);
     hipLaunchKernelGGL((key_flush_kernel<BITS, RECON, BF16, G, D, MT>), dim3(static_cast<uint32_t>(blocks)),
-                       dim3(kBlock), 0, stream, a.x, a.S, a.x_bh_stride, a.codes,
+                       dim3(kBlock), lds, stream, a.x, a.S, a.x_bh_stride, a.codes,
                        a.codes_bh_stride, static_cast<MT*>(a.scale), static_cast<MT*>(a.zero),
                        a.meta_bh_stride, a.dst_token,
                        a.recon, a.recon_bh_stride, n_groups, n_tiles, 1.0f);
@@ -413,8 +438,10 @@ static hipError_t launch_values_t(const FlushArgs& a, hipStream_t stream) {
     const int64_t tiles_per_bh = (a.S + 31) / 32;
     const int64_t n_tiles = a.BH * tiles_per_bh;
     const int64_t blocks = (n_tiles + kWavesPerBlock - 1) / kWavesPerBlock;
+    const size_t lds = residency_lds(kFlushPerCU<false, RECON, BF16, G, D, MT>,
+                                     sizeof(MT) * kWavesPerBlock * (kGatherMeta<G, D, MT> ? 2 * 32 * (D / G) : 1));
     hipLaunchKernelGGL((value_flush_kernel<BITS, RECON, BF16, G, D, MT>), dim3(static_cast<uint32_t>(blocks)),
-                       dim3(kBlock), 0, stream, a.x, a.S, a.x_bh_stride, a.codes,
+                       dim3(kBlock), lds, stream, a.x, a.S, a.x_bh_stride, a.codes,
                        a.codes_bh_stride, static_cast<MT*>(a.scale), static_cast<MT*>(a.zero),
                        a.meta_bh_stride, a.dst_token,
                        a.recon, a.recon_bh_stride, tiles_per_bh, n_tiles, 1.0f);
