@@ -7,12 +7,14 @@
  * streaming kernels are those ceilings on an MI355X, one per traffic shape:
  * a copy (read n, write n), a pure read (the decode attend's shape), a pure
  * write, and a flush-shaped mix (read n, write 3n/8: 2 B in per 0.75 B out,
- * the 4-bit flush's ratio).  Each moves every byte once, with 16-byte
- * accesses, and with the cache hints and the number of workgroups resident
- * per CU that measured fastest for its shape (the nontemporal hint, except
- * plain stores for the pure write; 3 to 5 workgroups of 4 waves per CU,
- * held there by LDS each launch reserves and never touches); the bytes/s
- * they reach bound what a kernel with the same read/write mix can reach.
+ * the 4-bit flush's ratio, in the flush's own pattern: per 8 KiB tile read,
+ * 2 KiB written to one region and 512 B to each of two others).  Each moves
+ * every byte once, with 16-byte accesses, and with the cache hints and the
+ * number of workgroups resident per CU that measured fastest for its shape
+ * (the nontemporal hint, except plain stores for the pure write; 3 or 4
+ * workgroups of 4 waves per CU, held there by LDS each launch reserves and
+ * never touches); the bytes/s they reach bound what a kernel with the same
+ * read/write mix can reach.
  *
  * Every pointer is device memory, 16-byte aligned; sizes are multiples of
  * 16.  The calls enqueue on `stream` and return KIVI_OK (0) or a negative
@@ -43,8 +45,10 @@ int kivi_calib_read(const void* src, size_t n_bytes, void* sink, hipStream_t str
 /* Write n_bytes of a fixed pattern to dst. */
 int kivi_calib_write(void* dst, size_t n_bytes, hipStream_t stream);
 
-/* Read n_bytes of src and write floor(3 n_bytes / 8 / 16) * 16 bytes to dst
- * (which must hold that many). */
+/* Read n_bytes of src and write floor(3 n / 8) 16-byte vectors to dst (n =
+ * n_bytes / 16; dst must hold that many): vectors [0, floor(n/4)) form the
+ * code region, the next floor(n/16) the scale region and the rest the zero
+ * region, each written in 8 KiB-source-tile order. */
 int kivi_calib_mix(const void* src, size_t n_bytes, void* dst, hipStream_t stream);
 
 #ifdef __cplusplus

@@ -353,7 +353,7 @@ const char* kivi_status_string(int status) {
 
 int kivi_last_hip_error(void) { return g_last_hip_error; }
 
-// The calibration kernels take one workgroup per 16 KiB: sizes up to
+// The calibration kernels take at most one workgroup per 16 KiB: sizes up to
 // 2^31 - 1 workgroups (below 2^45 bytes, inside the address space).
 static bool calib_size_ok(size_t n_bytes) { return n_bytes / 16384 < static_cast<size_t>(kMaxBlocks); }
 

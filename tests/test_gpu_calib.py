@@ -1,10 +1,11 @@
 """The calibration kernels (include/kivi_calib.h) move exactly the bytes
 their traffic shape names, since their rates serve as bandwidth ceilings:
 the copy reproduces its source, the write fills every 16-byte vector with
-its pattern, the mix writes the first 3/8 of the source's size (each vector
-the XOR of one thread's four loads) and nothing past it, and the read leaves
-its sink alone unless a thread's fold equals the sentinel.  Sizes include a
-ragged last workgroup (not a multiple of 16 KiB).  Exact comparisons."""
+its pattern, the mix writes the first 3/8 of the source's size in its three
+regions (each vector the XOR of one lane's eight loads) and nothing past
+it, and the read leaves its sink alone unless a thread's fold equals the
+sentinel.  Sizes include a ragged last workgroup (not a multiple of 16 KiB)
+and ragged last mix tiles.  Exact comparisons."""
 import numpy as np
 import pytest
 import torch
@@ -62,7 +63,32 @@ def test_write_fills_every_vector(n):
     assert bool((dst[n:] == 0xA5).all())
 
 
-@pytest.mark.parametrize("n", SIZES)
+def _mix_expected(src: np.ndarray) -> np.ndarray:
+    """dst of the flush-shaped mix: wave t folds lanes l's loads of source
+    vectors 512t + l + 64u (u < 8) and writes the fold of lane k mod 64 to
+    codes[128t + k], of lane k mod 32 to scale[32t + k] and of lane 32 +
+    (k mod 32) to zero[32t + k], the regions holding n/4, n/16 and the rest
+    of 3n/8 vectors (the last tile's counts absorb a ragged end)."""
+    v = src.view(np.uint32).reshape(-1, 4)
+    n = v.shape[0]
+    tiles = (n + 511) // 512
+    pad = np.zeros((tiles * 512, 4), np.uint32)
+    pad[:n] = v
+    lanes = np.bitwise_xor.reduce(pad.reshape(tiles, 8, 64, 4), axis=1)     # [tile, lane, 4]
+    m, mc, ms = n * 3 // 8, n // 4, n // 16
+    mz = m - mc - ms
+    out = np.zeros((m, 4), np.uint32)
+    for start, size, stride, lane_of in ((0, mc, 128, lambda k: k % 64),              # codes
+                                         (mc, ms, 32, lambda k: k % 32),              # scale
+                                         (mc + ms, mz, 32, lambda k: 32 + k % 32)):   # zero
+        j = np.arange(size)
+        t = np.minimum(j // stride, tiles - 1)          # the last tile takes any overflow
+        k = j - t * stride
+        out[start + j] = lanes[t, lane_of(k)]
+    return out
+
+
+@pytest.mark.parametrize("n", SIZES + [16 * 511, 16 * (512 * 3 + 511)])
 def test_mix_writes_three_eighths(n):
     note(f"calib mix n={n}")
     src_h = _src(n, 2)
@@ -71,17 +97,8 @@ def test_mix_writes_three_eighths(n):
     dst = torch.full((n,), 0xA5, dtype=torch.uint8, device="cuda")
     kivi.calib_mix(src, dst)
     torch.cuda.synchronize()
-    folds = _thread_folds(src_h.numpy())
-    # block b stores vectors [b*CHUNK*3/8, (b+1)*CHUNK*3/8); wave w of it
-    # stores its 3/8 share, vector k of the share from lane k mod 64
-    per_wave = 64 * VECS * 3 // 8
-    k = np.arange(per_wave)
-    want = np.empty((folds.shape[0], BLOCK // 64, per_wave, 4), np.uint32)
-    for w in range(BLOCK // 64):
-        want[:, w] = folds[:, w * 64 + (k % 64)]
-    want = want.reshape(-1, 4)[: n_out // 16]
     got = dst[:n_out].cpu().numpy().view(np.uint32).reshape(-1, 4)
-    assert np.array_equal(got, want)
+    assert np.array_equal(got, _mix_expected(src_h.numpy()))
     assert bool((dst[n_out:] == 0xA5).all())
 
 
