@@ -59,7 +59,7 @@ __device__ __forceinline__ float4_t mfma(const Frag& a, const Frag& b, float4_t 
 }
 
 #ifndef KIVI_ATTEND_NBUF
-#define KIVI_ATTEND_NBUF 3
+#define KIVI_ATTEND_NBUF 2
 #endif
 #define KIVI_ATTEND_OCCUPANCY __attribute__((amdgpu_waves_per_eu(KIVI_ATTEND_WAVES_PER_SIMD)))
 constexpr int kNBuf = KIVI_ATTEND_NBUF;
@@ -721,10 +721,9 @@ __device__ __forceinline__ void residual_step(const uint16_t* kr, const uint16_t
 // that axis, so one wave may finish the store and start the residual.
 // Offsets within a slab fit in 32 bits: the ABI keeps n_quant and n_res
 // below 2^24 tokens.
-// bfloat16 instances run at 2 waves per SIMD: their dequantization needs
-// about 190 VGPRs, and at 3 waves (168) they spilled to scratch.  Head_dim
-// 256 doubles every per-lane array (16 PV accumulators, 64 key channels per
-// lane group) and also runs at 2 waves.
+// Head_dim 256 doubles every per-lane array (16 PV accumulators, 64 key
+// channels per lane group) and runs at 2 waves per SIMD (fp16, two buffers)
+// or 1 (bfloat16, three buffers: its dequantization needs the registers).
 #ifndef KIVI_ATTEND_BF16_D256_WAVES
 #define KIVI_ATTEND_BF16_D256_WAVES 1
 #endif
@@ -732,7 +731,8 @@ __device__ __forceinline__ void residual_step(const uint16_t* kr, const uint16_t
 #define KIVI_ATTEND_BF16_D256_NBUF 3
 #endif
 template <bool BF, int D> constexpr int kWavesPerSimd =
-    (BF && D == 256) ? KIVI_ATTEND_BF16_D256_WAVES : (BF || D == 256) ? 2 : KIVI_ATTEND_WAVES_PER_SIMD;
+    (BF && D == 256) ? KIVI_ATTEND_BF16_D256_WAVES : D == 256 ? 2 : BF ? KIVI_ATTEND_BF16_WAVES
+                                                                    : KIVI_ATTEND_WAVES_PER_SIMD;
 template <bool BF, int D> constexpr int kNBufOf = (BF && D == 256) ? KIVI_ATTEND_BF16_D256_NBUF : D == 256 ? 2 : kNBuf;
 
 template <int BITS, int GQA, int G, int MB, bool BF, int D>

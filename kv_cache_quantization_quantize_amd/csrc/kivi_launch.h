@@ -81,16 +81,26 @@ struct AttendArgs {
     int head_dim;                  // 128; others with groups of 32 and binary32 scale/zero
 };
 
-// Three waves per SIMD for the fp16 attend (at most 168 VGPRs, which hold
-// three steps of loads in flight without spilling; four would need 128 and
-// spill), so the chip holds 256 CUs x 4 SIMDs x 3 = 3072 of these waves at
-// once; the bfloat16 instances run two per SIMD.  Each wave keeps
-// KIVI_ATTEND_NBUF - 1 steps of loads in flight while it computes one.
+// Three waves per SIMD for the attend at head_dim 64 and 128, fp16 and
+// bfloat16 alike (at most 168 VGPRs; four would need 128 and spill), so the
+// chip holds 256 CUs x 4 SIMDs x 3 = 3072 of these waves at once.  Each wave
+// keeps KIVI_ATTEND_NBUF - 1 steps of loads in flight while it computes one:
+// one step (about 6 KiB a wave, 72 KiB a CU) measured faster than two, as
+// the streaming read calibration peaked at about 48 KiB in flight per CU and
+// slowed with more.  Interleaved on MI355X against two steps in flight at 2
+// waves per SIMD: bfloat16 at B=32 x 16384 tokens 164-173 -> 156 us, B=16
+// 90 -> 84 us; fp16 B=32 x 2048 31.0 -> 29.4 us, B=32 x 16384 148 -> 147.
+// The bfloat16 4-bit instances keep 12 bytes per lane in scratch at 168
+// VGPRs and are still faster than at two waves.
 #ifndef KIVI_ATTEND_WAVES_PER_SIMD
 #define KIVI_ATTEND_WAVES_PER_SIMD 3
 #endif
+#ifndef KIVI_ATTEND_BF16_WAVES
+#define KIVI_ATTEND_BF16_WAVES 3
+#endif
 constexpr int64_t kWaveSlots = 256 * 4 * KIVI_ATTEND_WAVES_PER_SIMD;
-constexpr int64_t kWaveSlotsBF16 = 256 * 4 * 2;    // also the head_dim 256 kernels
+constexpr int64_t kWaveSlotsBF16 = 256 * 4 * KIVI_ATTEND_BF16_WAVES;   // bfloat16, head_dim up to 128
+constexpr int64_t kWaveSlotsD256 = 256 * 4 * 2;                         // the head_dim 256 kernels
 constexpr int kAttendStep = 32;                 // tokens per wave step (one key group)
 constexpr int64_t kMaxStepsPerWave = 64;
 

@@ -23,8 +23,7 @@ AttendPlan plan_attend(int64_t B, int Hq, int Hkv, int64_t n_quant, int64_t n_re
     const int64_t steps_q = (n_quant + kAttendStep - 1) / kAttendStep;
     const int64_t steps = steps_q + (n_res + kAttendStep - 1) / kAttendStep;
     const int64_t total = pairs * steps;
-    // the bfloat16 and the head_dim 256 kernels run 2 waves per SIMD
-    const int64_t slots = (bf16 || head_dim == 256) ? kWaveSlotsBF16 : kWaveSlots;
+    const int64_t slots = head_dim == 256 ? kWaveSlotsD256 : bf16 ? kWaveSlotsBF16 : kWaveSlots;
     int64_t spw = 1;
     if (total > slots) {
         // A variable-length batch sizes the grid for its longest sequence;
