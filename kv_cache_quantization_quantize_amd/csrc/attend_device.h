@@ -766,8 +766,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
     const int r1 = min(max(s1 - steps_q, 0) * kStep, nr);
     const bool has_store = j0 < j1;
 
-    // Store part: buffer views and the first two steps' loads, issued before
-    // the query so the two HBM latencies overlap.
+    // Store part: buffer views and the first kNB - 1 steps' loads, issued
+    // before the query so the two HBM latencies overlap.
     constexpr int kWords = D * BITS / 32;
     constexpr int kMetaPerTok = D / G;
     constexpr int kNB = kNBufOf<BF, D>;

@@ -36,11 +36,13 @@ AttendPlan plan_attend(int64_t B, int Hq, int Hkv, int64_t n_quant, int64_t n_re
     }
     // Small and mid-size calls take fewer, longer waves: each wave pays a
     // fixed cost (query load, LDS setup, its partial and its share of the
-    // combine), and about 700 waves with two steps of loads in flight each
-    // already keep these sizes at their best.  Measured per call on MI355X
-    // (steps per wave -> us): B=1 x 16384 tokens 2 -> 19.1, 6 -> 16.1;
-    // B=4 x 2048: 1 -> 13.3, 3 -> 11.9; B=16 x 2048: 3 -> 23.0, 9 -> 19.9;
-    // B=4 x 16384: 6 -> 31.2, 9 -> 30.3; B=32 x 2048: 6 -> 31.7, 9 -> 31.4.
+    // combine), and about 700 waves already keep these sizes at their best.
+    // Measured per call on MI355X, fp16, one step of loads in flight (steps
+    // per wave -> us): B=1 x 16384 tokens 2 -> 22.0, 6 -> 15.9; B=4 x 2048:
+    // 1 -> 13.0, 4 -> 11.9; B=16 x 2048: 3 -> 21.4, 9 -> 17.1; B=4 x 16384:
+    // 6 -> 28.8, 9 -> 26.8.  At every fp16 shape the rule below lands within
+    // 2% of the best; bfloat16 follows it within 2% but at B=4 x 2048 (13.9
+    // against 13.1 us at 3 steps).
     const int64_t longer = (total + 699) / 700;
     spw = std::max(spw, std::min<int64_t>(9, longer));
     // The generic kernel (head_dims other than 64, 128 and 256) has no fixed
