@@ -657,36 +657,19 @@ __device__ __forceinline__ void residual_step(const uint16_t* kr, const uint16_t
                                               int l, int n, int q, int head, int ring) {
     constexpr int kCPG = Geo<D>::kCPG, kKB = Geo<D>::kKB, kPV = Geo<D>::kPV;
     const int last = n_res - 1;
-    float4_t acc_s[2] = {float4_t{0.0f, 0.0f, 0.0f, 0.0f}, float4_t{0.0f, 0.0f, 0.0f, 0.0f}};
+    // Every row of the step is loaded up front (K rows of both 16-token
+    // blocks and the V rows), so a residual step costs one memory round trip.
+    uint32_t rn[2][kCPG / 2];                   // the lane group's key channels, natural order
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
         const int tok = ring_row(min(t0 + 16 * blk + n, last), head, ring);
         const uint4* src = reinterpret_cast<const uint4*>(kr + tok * D + kCPG * q);
-        uint32_t rn[kCPG / 2];                  // the lane group's channels, natural order
 #pragma unroll
         for (int v = 0; v < kCPG / 8; ++v) {
             const uint4 t = src[v];
-            rn[4 * v] = t.x; rn[4 * v + 1] = t.y; rn[4 * v + 2] = t.z; rn[4 * v + 3] = t.w;
-        }
-#pragma unroll
-        for (int kb = 0; kb < kKB; ++kb) {
-            Frag ka;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if constexpr (kByteCodes<BITS, BF>) {
-                    ka.u[j] = rn[4 * kb + j];             // natural order: channels 8kb + 2j, + 1
-                } else {
-                    const int c0 = 8 * kb + j, c1 = 8 * kb + j + 4;
-                    const uint32_t s0 = (c0 & 1) ? 0x0302u : 0x0100u;
-                    const uint32_t s1 = (c1 & 1) ? 0x0706u : 0x0504u;
-                    ka.u[j] = __builtin_amdgcn_perm(rn[c1 >> 1], rn[c0 >> 1], (s1 << 16) | s0);
-                }
-            }
-            acc_s[blk] = mfma<BF>(ka, query_frag(sm, kb, l), acc_s[blk]);
+            rn[blk][4 * v] = t.x; rn[blk][4 * v + 1] = t.y; rn[blk][4 * v + 2] = t.z; rn[blk][4 * v + 3] = t.w;
         }
     }
-    Frag bp_lo;
-    const Frag bp = softmax_any<BF>(acc_s, st, c2, n_res - t0, q, bp_lo);
     // V rows: lane (q, m=n) takes channels kPV*n .. kPV*n + kPV - 1 of its 8 tokens
     uint32_t vw[8][kPV / 2];
 #pragma unroll
@@ -704,6 +687,28 @@ __device__ __forceinline__ void residual_step(const uint16_t* kr, const uint16_t
             vw[s][0] = t.x; vw[s][1] = t.y;
         }
     }
+    float4_t acc_s[2] = {float4_t{0.0f, 0.0f, 0.0f, 0.0f}, float4_t{0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+        for (int kb = 0; kb < kKB; ++kb) {
+            Frag ka;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if constexpr (kByteCodes<BITS, BF>) {
+                    ka.u[j] = rn[blk][4 * kb + j];        // natural order: channels 8kb + 2j, + 1
+                } else {
+                    const int c0 = 8 * kb + j, c1 = 8 * kb + j + 4;
+                    const uint32_t s0 = (c0 & 1) ? 0x0302u : 0x0100u;
+                    const uint32_t s1 = (c1 & 1) ? 0x0706u : 0x0504u;
+                    ka.u[j] = __builtin_amdgcn_perm(rn[blk][c1 >> 1], rn[blk][c0 >> 1], (s1 << 16) | s0);
+                }
+            }
+            acc_s[blk] = mfma<BF>(ka, query_frag(sm, kb, l), acc_s[blk]);
+        }
+    }
+    Frag bp_lo;
+    const Frag bp = softmax_any<BF>(acc_s, st, c2, n_res - t0, q, bp_lo);
 #pragma unroll
     for (int i = 0; i < kPV; ++i) {
         Frag va;
