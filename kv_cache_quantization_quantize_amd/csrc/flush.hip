@@ -216,6 +216,12 @@ __global__ __launch_bounds__(kBlock) void key_flush_kernel(
 // the plain stores, whose partial lines the L2 merges.
 template <int G, int D, typename MT>
 constexpr bool kGatherMeta = (D / G) * static_cast<int>(sizeof(MT)) >= 16;
+// Elements of a wave's LDS row for the gathered scale and zero (one element
+// when nothing is gathered), and the workgroup's static LDS bytes.
+template <int G, int D, typename MT>
+constexpr int kValueLdsRow = kGatherMeta<G, D, MT> ? 2 * 32 * (D / G) : 1;
+template <int G, int D, typename MT>
+constexpr size_t kValueLdsBytes = sizeof(MT) * kWavesPerBlock * kValueLdsRow<G, D, MT>;
 
 // One token's scale (or zero) row, 16 or 32 bytes, from LDS to the store
 // (16-byte aligned: the store's metadata is, and so is a token's row).
@@ -376,7 +382,8 @@ __global__ __launch_bounds__(kBlock) void value_flush_kernel(
     constexpr int kMetaPerTok = D / G;
     const int lane = threadIdx.x & 63;
     const int64_t tile = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
-    __shared__ MT lds_meta[kWavesPerBlock][kGatherMeta<G, D, MT> ? 2 * 32 * kMetaPerTok : 1];
+    __shared__ MT lds_meta[kWavesPerBlock][kValueLdsRow<G, D, MT>];
+    static_assert(sizeof(lds_meta) == kValueLdsBytes<G, D, MT>, "the launcher sizes its LDS cap from this");
     if (tile >= n_tiles) return;                    // uniform across the wave
     const int64_t bh = tile / tiles_per_bh;
     const int64_t s0 = (tile - bh * tiles_per_bh) * 32;
@@ -438,8 +445,7 @@ static hipError_t launch_values_t(const FlushArgs& a, hipStream_t stream) {
     const int64_t tiles_per_bh = (a.S + 31) / 32;
     const int64_t n_tiles = a.BH * tiles_per_bh;
     const int64_t blocks = (n_tiles + kWavesPerBlock - 1) / kWavesPerBlock;
-    const size_t lds = residency_lds(kFlushPerCU<false, RECON, BF16, G, D, MT>,
-                                     sizeof(MT) * kWavesPerBlock * (kGatherMeta<G, D, MT> ? 2 * 32 * (D / G) : 1));
+    const size_t lds = residency_lds(kFlushPerCU<false, RECON, BF16, G, D, MT>, kValueLdsBytes<G, D, MT>);
     hipLaunchKernelGGL((value_flush_kernel<BITS, RECON, BF16, G, D, MT>), dim3(static_cast<uint32_t>(blocks)),
                        dim3(kBlock), lds, stream, a.x, a.S, a.x_bh_stride, a.codes,
                        a.codes_bh_stride, static_cast<MT*>(a.scale), static_cast<MT*>(a.zero),
