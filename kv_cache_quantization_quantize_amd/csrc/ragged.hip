@@ -185,7 +185,10 @@ __global__ __launch_bounds__(kBlock) void key_flush_ragged_kernel(
 
 // Values: one wave per (slab, 32-token tile); a token's groups are chunks
 // 4j .. 4j+3 (the last group of a head_dim that 32 does not divide has 2).
-template <int BITS, bool RECON, bool BF16>
+// QUAD (head_dim a multiple of 32): a row is a whole number of quads, so a
+// group's four chunks are the four lanes of one DPP quad and its min and max
+// meet in two quad exchanges instead of LDS.
+template <int BITS, bool RECON, bool BF16, bool QUAD>
 __global__ __launch_bounds__(kBlock) void value_flush_ragged_kernel(
     const uint16_t* __restrict__ x, int64_t S, int64_t x_bh_stride,
     uint32_t* __restrict__ codes, int64_t codes_bh_stride,
@@ -214,30 +217,32 @@ __global__ __launch_bounds__(kBlock) void value_flush_ragged_kernel(
     const int iters = (kG + nR - 1) / nR;
 
     // every row's chunk min/max into LDS (rows past the tile re-read row 0
-    // and are never used)
+    // and are never used); QUAD reduces each row in the loop below instead
     uint4 raw[kMaxIters];
 #pragma unroll
     for (int i = 0; i < kMaxIters; ++i) {
         const int row = r + nR * i;
         if (i < iters) raw[i] = load_stream(xt + (on && row < n_rows ? row : 0) * D + c * 8);
     }
+    if constexpr (!QUAD) {
 #pragma unroll
-    for (int i = 0; i < kMaxIters; ++i) {
-        if (i >= iters) continue;                   // wave-uniform
-        const int row = r + nR * i;
-        if (on && row < n_rows) {
-            float a = widen(raw[i], 0, BF16), b = a;
+        for (int i = 0; i < kMaxIters; ++i) {
+            if (i >= iters) continue;               // wave-uniform
+            const int row = r + nR * i;
+            if (on && row < n_rows) {
+                float a = widen(raw[i], 0, BF16), b = a;
 #pragma unroll
-            for (int k = 1; k < 8; ++k) {
-                const float v = widen(raw[i], k, BF16);
-                a = fminimum(a, v);
-                b = fmaximum(b, v);
+                for (int k = 1; k < 8; ++k) {
+                    const float v = widen(raw[i], k, BF16);
+                    a = fminimum(a, v);
+                    b = fmaximum(b, v);
+                }
+                sm.mn[row][c] = a;
+                sm.mx[row][c] = b;
             }
-            sm.mn[row][c] = a;
-            sm.mx[row][c] = b;
         }
+        lds_fence();
     }
-    lds_fence();
     uint32_t* ct = codes + bh * codes_bh_stride + (dst_token + s0) * kWords;
     uint16_t* rt = RECON ? recon + bh * recon_bh_stride + s0 * D : nullptr;
 #pragma unroll
@@ -246,7 +251,23 @@ __global__ __launch_bounds__(kBlock) void value_flush_ragged_kernel(
         const int row = r + nR * i;
         const bool live = on && row < n_rows;
         float lo = 0.0f, hi = 0.0f;
-        if (live) {
+        if constexpr (QUAD) {
+            // every lane takes part in the exchanges (idle lanes form their
+            // own quads, rows past the tile hold row 0; neither is stored)
+            lo = widen(raw[i], 0, BF16);
+            hi = lo;
+#pragma unroll
+            for (int k = 1; k < 8; ++k) {
+                const float v = widen(raw[i], k, BF16);
+                lo = fminimum(lo, v);
+                hi = fmaximum(hi, v);
+            }
+            lo = fminimum(lo, __uint_as_float(quad_xor1(__float_as_uint(lo))));
+            hi = fmaximum(hi, __uint_as_float(quad_xor1(__float_as_uint(hi))));
+            lo = fminimum(lo, __uint_as_float(quad_xor2(__float_as_uint(lo))));
+            hi = fmaximum(hi, __uint_as_float(quad_xor2(__float_as_uint(hi))));
+            if (!live) lo = hi = 0.0f;
+        } else if (live) {
             lo = sm.mn[row][4 * j];
             hi = sm.mx[row][4 * j];
             for (int k = 4 * j + 1; k < c_end; ++k) {
@@ -353,8 +374,13 @@ static hipError_t launch_flush_ragged_t(const FlushArgs& a, hipStream_t stream) 
                            dim3(kBlock), 0, stream, a.x, a.S, a.x_bh_stride, a.codes, a.codes_bh_stride,
                            sc, ze, a.meta_bh_stride, a.dst_token, a.recon, a.recon_bh_stride,
                            per_bh, n_tiles, a.head_dim, 1.0f);
+    else if (a.head_dim % kG == 0)
+        hipLaunchKernelGGL((value_flush_ragged_kernel<BITS, RECON, BF16, true>), dim3(static_cast<uint32_t>(blocks)),
+                           dim3(kBlock), 0, stream, a.x, a.S, a.x_bh_stride, a.codes, a.codes_bh_stride,
+                           sc, ze, a.meta_bh_stride, a.dst_token, a.recon, a.recon_bh_stride,
+                           per_bh, n_tiles, a.head_dim, 1.0f);
     else
-        hipLaunchKernelGGL((value_flush_ragged_kernel<BITS, RECON, BF16>), dim3(static_cast<uint32_t>(blocks)),
+        hipLaunchKernelGGL((value_flush_ragged_kernel<BITS, RECON, BF16, false>), dim3(static_cast<uint32_t>(blocks)),
                            dim3(kBlock), 0, stream, a.x, a.S, a.x_bh_stride, a.codes, a.codes_bh_stride,
                            sc, ze, a.meta_bh_stride, a.dst_token, a.recon, a.recon_bh_stride,
                            per_bh, n_tiles, a.head_dim, 1.0f);
