@@ -39,8 +39,13 @@ __device__ __forceinline__ void key_tile(const uint16_t* __restrict__ xt, uint32
     constexpr int kWords = D * BITS / 32;          // code words per token row
     constexpr int kLPR = RowGeo<D>::kLanesPerRow;
     constexpr int kRPW = RowGeo<D>::kRowsPerWave;
+    constexpr int kChunks = RowGeo<D>::kChunks;
     const int c = lane % kLPR;                     // channels 8c .. 8c+7
     const int r = lane / kLPR;                     // token rows r, r + kRPW, ...
+    // lanes past a row's last chunk (head_dims 96, 160, 192, 224) re-read
+    // that chunk and store nothing; their min/max only meet each other's
+    const bool has = kChunks == kLPR || c < kChunks;
+    const int cl = kChunks == kLPR ? c : (c < kChunks ? c : kChunks - 1);
 
     // Load 8 token rows x 8 channels.  Rows past the end of a ragged last
     // group re-read the last real token, which is the edge padding of
@@ -51,7 +56,7 @@ __device__ __forceinline__ void key_tile(const uint16_t* __restrict__ xt, uint32
     for (int i = 0; i < kRows; ++i) {
         int row = r + kRPW * i;
         if constexpr (RAGGED) row = row < n_rows ? row : n_rows - 1;
-        raw[i] = load_stream(xt + row * D + c * 8);
+        raw[i] = load_stream(xt + row * D + cl * 8);
     }
 
     // Per-channel min/max over the lane's rows and then across the 4 row
@@ -131,7 +136,7 @@ __device__ __forceinline__ void key_tile(const uint16_t* __restrict__ xt, uint32
             for (int j = 0; j < 8; ++j) h[j] = f32_to_f16(ze[j]);
             store_stream(zet + c * 8, pack8(h));
         }
-    } else {
+    } else if (has) {
         if (r == 0) {
             store_stream4(sct + c * 8, sc[0], sc[1], sc[2], sc[3]);
             store_stream4(sct + c * 8 + 4, sc[4], sc[5], sc[6], sc[7]);
@@ -158,7 +163,7 @@ __device__ __forceinline__ void key_tile(const uint16_t* __restrict__ xt, uint32
         uint32_t packed = static_cast<uint32_t>(qf[0]);
 #pragma unroll
         for (int j = 1; j < 8; ++j) packed |= static_cast<uint32_t>(qf[j]) << (BITS * j);
-        const bool live = !RAGGED || row < n_rows;
+        const bool live = (!RAGGED || row < n_rows) && has;
         if constexpr (BITS == 4) {
             // the lane's 8 channels are exactly one word
             if (live) store_stream(&ct[row * kWords + c], packed);
@@ -215,7 +220,8 @@ __global__ __launch_bounds__(kBlock) void key_flush_kernel(
 // 128, or binary16 scale/zero) they made it 8-10% slower, and those keep
 // the plain stores, whose partial lines the L2 merges.
 template <int G, int D, typename MT>
-constexpr bool kGatherMeta = (D / G) * static_cast<int>(sizeof(MT)) >= 16;
+constexpr bool kGatherMeta = (D / G) * static_cast<int>(sizeof(MT)) == 16 ||
+                             (D / G) * static_cast<int>(sizeof(MT)) == 32;
 // Elements of a wave's LDS row for the gathered scale and zero (one element
 // when nothing is gathered), and the workgroup's static LDS bytes.
 template <int G, int D, typename MT>
@@ -252,17 +258,23 @@ __device__ __forceinline__ void value_tile(const uint16_t* __restrict__ xt, uint
     constexpr int kLanesPerGroup = G / 8;           // 4, 8 or 16 lanes of 8 channels
     constexpr int kLPR = RowGeo<D>::kLanesPerRow;
     constexpr int kRPW = RowGeo<D>::kRowsPerWave;
+    constexpr int kChunks = RowGeo<D>::kChunks;
     constexpr int kRows = 32 / kRPW;                // token rows per lane in a 32-token tile
     const int c = lane % kLPR;
     const int r = lane / kLPR;
     const int j = c / kLanesPerGroup;               // channel group of this lane
+    // lanes past a row's last chunk (head_dims 96, 160, 192, 224: whole
+    // groups of 4, so they form their own quads) re-read that chunk and
+    // store nothing
+    const bool has = kChunks == kLPR || c < kChunks;
+    const int cl = kChunks == kLPR ? c : (c < kChunks ? c : kChunks - 1);
 
     uint4 raw[kRows];
 #pragma unroll
     for (int i = 0; i < kRows; ++i) {
         int row = r + kRPW * i;
         if constexpr (RAGGED) row = row < n_rows ? row : n_rows - 1;   // keep every lane in the exchange
-        raw[i] = load_stream(xt + row * D + c * 8);
+        raw[i] = load_stream(xt + row * D + cl * 8);
     }
 
 #pragma unroll
@@ -327,7 +339,7 @@ __device__ __forceinline__ void value_tile(const uint16_t* __restrict__ xt, uint
         uint32_t packed = static_cast<uint32_t>(qf[0]);
 #pragma unroll
         for (int k = 1; k < 8; ++k) packed |= static_cast<uint32_t>(qf[k]) << (BITS * k);
-        const bool live = !RAGGED || row < n_rows;
+        const bool live = (!RAGGED || row < n_rows) && has;
         if constexpr (BITS == 4) {
             if (live) store_stream(&ct[row * kWords + c], packed);
         } else {
@@ -473,8 +485,15 @@ static hipError_t launch_flush_g(const FlushArgs& a, hipStream_t stream) {
 // head_dim 128.
 template <bool KEYS, bool BF16>
 static hipError_t launch_flush_fmt(const FlushArgs& a, hipStream_t stream) {
-    if (a.head_dim == 64) return launch_flush_g<KEYS, BF16, 32, 64>(a, stream);
-    if (a.head_dim == 256) return launch_flush_g<KEYS, BF16, 32, 256>(a, stream);
+    switch (a.head_dim) {
+        case 64: return launch_flush_g<KEYS, BF16, 32, 64>(a, stream);
+        case 96: return launch_flush_g<KEYS, BF16, 32, 96>(a, stream);
+        case 160: return launch_flush_g<KEYS, BF16, 32, 160>(a, stream);
+        case 192: return launch_flush_g<KEYS, BF16, 32, 192>(a, stream);
+        case 224: return launch_flush_g<KEYS, BF16, 32, 224>(a, stream);
+        case 256: return launch_flush_g<KEYS, BF16, 32, 256>(a, stream);
+        default: break;
+    }
     if constexpr (!BF16) {
         if (a.meta16) {
             switch (a.group) {
@@ -491,7 +510,12 @@ static hipError_t launch_flush_fmt(const FlushArgs& a, hipStream_t stream) {
     }
 }
 
-static bool tiled_head_dim(int D) { return D == 64 || D == 128 || D == 256; }
+// head_dims on the tiled kernels: rows of whole 16- or 32-lane units (64,
+// 128, 256) or of whole groups of 32 channels with idle lanes at the end
+// (96, 160, 192, 224); the others take the generic kernels of ragged.hip
+static bool tiled_head_dim(int D) {
+    return D == 64 || D == 96 || D == 128 || D == 160 || D == 192 || D == 224 || D == 256;
+}
 
 hipError_t launch_key_flush(const FlushArgs& a, hipStream_t stream) {
     if (!tiled_head_dim(a.head_dim)) return launch_flush_ragged(true, a, stream);

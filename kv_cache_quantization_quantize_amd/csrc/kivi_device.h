@@ -105,12 +105,15 @@ __device__ __forceinline__ uint32_t word_of(const uint4& v, int k) {
 }
 
 // Row geometry of the flush and dequantize for head_dim D: a token row is
-// D/8 lanes of 8 channels, so one wave covers 64/(D/8) rows per load (8, 4
-// or 2 for D = 64, 128, 256).  The lanes that hold the same 8 channels of
-// different rows are lane ^ 8 (D = 64 only), ^ 16 (D <= 128) and ^ 32.
+// D/8 chunks of 8 channels, one per lane, in a row of 8, 16 or 32 lanes (the
+// next power of two; head_dims 96, 160, 192 and 224 leave the last lanes of
+// a row idle), so one wave covers 8, 4 or 2 rows per load.  The lanes that
+// hold the same 8 channels of different rows are lane ^ 8 (rows of 8 only),
+// ^ 16 (rows of 8 or 16) and ^ 32.
 template <int D>
 struct RowGeo {
-    static constexpr int kLanesPerRow = D / 8;
+    static constexpr int kChunks = D / 8;          // lanes of a row that hold channels
+    static constexpr int kLanesPerRow = kChunks <= 8 ? 8 : kChunks <= 16 ? 16 : 32;
     static constexpr int kRowsPerWave = 64 / kLanesPerRow;
 };
 
@@ -122,20 +125,20 @@ __device__ __forceinline__ uint32_t lane_xor8(uint32_t v) {
 // min / max over the rows of a wave for each lane's channel block
 template <int D>
 __device__ __forceinline__ half2_t cross_rows_min(half2_t v) {
-    if constexpr (D == 64) v = hmin(v, as_h2(lane_xor8(as_u32(v))));
-    if constexpr (D <= 128) v = row_pair_min(v);
+    if constexpr (RowGeo<D>::kLanesPerRow == 8) v = hmin(v, as_h2(lane_xor8(as_u32(v))));
+    if constexpr (RowGeo<D>::kLanesPerRow <= 16) v = row_pair_min(v);
     return half_min(v);
 }
 template <int D>
 __device__ __forceinline__ half2_t cross_rows_max(half2_t v) {
-    if constexpr (D == 64) v = hmax(v, as_h2(lane_xor8(as_u32(v))));
-    if constexpr (D <= 128) v = row_pair_max(v);
+    if constexpr (RowGeo<D>::kLanesPerRow == 8) v = hmax(v, as_h2(lane_xor8(as_u32(v))));
+    if constexpr (RowGeo<D>::kLanesPerRow <= 16) v = row_pair_max(v);
     return half_max(v);
 }
 template <int D>
 __device__ __forceinline__ float cross_rows_min_f32(float v) {
-    if constexpr (D == 64) v = fminimum(v, __uint_as_float(lane_xor8(__float_as_uint(v))));
-    if constexpr (D <= 128) {
+    if constexpr (RowGeo<D>::kLanesPerRow == 8) v = fminimum(v, __uint_as_float(lane_xor8(__float_as_uint(v))));
+    if constexpr (RowGeo<D>::kLanesPerRow <= 16) {
         const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
         v = fminimum(__uint_as_float(p[0]), __uint_as_float(p[1]));
     }
@@ -144,8 +147,8 @@ __device__ __forceinline__ float cross_rows_min_f32(float v) {
 }
 template <int D>
 __device__ __forceinline__ float cross_rows_max_f32(float v) {
-    if constexpr (D == 64) v = fmaximum(v, __uint_as_float(lane_xor8(__float_as_uint(v))));
-    if constexpr (D <= 128) {
+    if constexpr (RowGeo<D>::kLanesPerRow == 8) v = fmaximum(v, __uint_as_float(lane_xor8(__float_as_uint(v))));
+    if constexpr (RowGeo<D>::kLanesPerRow <= 16) {
         const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
         v = fmaximum(__uint_as_float(p[0]), __uint_as_float(p[1]));
     }

@@ -164,12 +164,14 @@ def test_other_head_dims(shape, Dh, kind, bits, fmt):
 @pytest.mark.parametrize("fmt", ["f16", "bf16"])
 @pytest.mark.parametrize("bits", [4, 2])
 @pytest.mark.parametrize("kind", ["keys", "values"])
-@pytest.mark.parametrize("Dh", [16, 48, 80, 96, 112, 160, 240])
+@pytest.mark.parametrize("Dh", [16, 48, 80, 96, 112, 160, 192, 224, 240])
 @pytest.mark.parametrize("shape", [(3, 101, 160, 32, 7), (2, 64, 64, 0, 0), (1, 1, 64, 32, 1)],
                          ids=lambda c: "BH%d-S%d-dst%d" % (c[0], c[1], c[3]))
 def test_ragged_head_dims(shape, Dh, kind, bits, fmt):
-    """head_dims other than 64, 128 and 256 (the generic kernels; a token's
-    last value group has 16 channels when 32 does not divide head_dim):
+    """head_dims other than 64, 128 and 256: 96, 160, 192 and 224 on the
+    tiled kernels with idle lanes at the end of each row, the others on the
+    generic kernels (a token's last value group has 16 channels when 32 does
+    not divide head_dim):
     flush with fused reconstruction, and dequantize, bit-exact against the
     oracle, sentinel-filled outputs checking the write window."""
     BH, S, cap, dst_k, dst_v = shape
