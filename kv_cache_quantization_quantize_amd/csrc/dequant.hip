@@ -48,8 +48,12 @@ __device__ __forceinline__ void dequant_tile(const uint32_t* __restrict__ cb, co
     constexpr int kMetaPerTok = D / G;
     constexpr int kLPR = RowGeo<D>::kLanesPerRow;
     constexpr int kRPW = RowGeo<D>::kRowsPerWave;
+    constexpr int kChunks = RowGeo<D>::kChunks;
     const int c = lane % kLPR;
     const int r = lane / kLPR;
+    // lanes past a row's last chunk (head_dims 96, 160, 192, 224) have
+    // nothing to write, and no lane exchanges follow
+    if (kChunks != kLPR && c >= kChunks) return;
     const uint32_t* ct = cb + t_first * kWords;
     float gs[8], gz[8];
     if constexpr (ONE_GROUP) {
@@ -133,8 +137,15 @@ static hipError_t launch_g(const DequantArgs& a, hipStream_t stream) {
 // of 32.  Binary16 metadata: fp16 output at head_dim 128.
 template <bool BF16>
 static hipError_t launch_fmt(const DequantArgs& a, hipStream_t stream) {
-    if (a.head_dim == 64) return launch_g<BF16, 32, 64>(a, stream);
-    if (a.head_dim == 256) return launch_g<BF16, 32, 256>(a, stream);
+    switch (a.head_dim) {
+        case 64: return launch_g<BF16, 32, 64>(a, stream);
+        case 96: return launch_g<BF16, 32, 96>(a, stream);
+        case 160: return launch_g<BF16, 32, 160>(a, stream);
+        case 192: return launch_g<BF16, 32, 192>(a, stream);
+        case 224: return launch_g<BF16, 32, 224>(a, stream);
+        case 256: return launch_g<BF16, 32, 256>(a, stream);
+        default: break;
+    }
     if constexpr (!BF16) {
         if (a.meta16) {
             switch (a.group) {
@@ -152,7 +163,11 @@ static hipError_t launch_fmt(const DequantArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t stream) {
-    if (a.head_dim != 64 && a.head_dim != 128 && a.head_dim != 256) return launch_dequant_ragged(a, stream);
+    // the tiled head_dims of the flush (rows of 16 or 32 lanes, the last ones
+    // idle at 96, 160, 192 and 224); the others take the generic kernel
+    const int D = a.head_dim;
+    if (D != 64 && D != 96 && D != 128 && D != 160 && D != 192 && D != 224 && D != 256)
+        return launch_dequant_ragged(a, stream);
     return a.bf16 ? launch_fmt<true>(a, stream) : launch_fmt<false>(a, stream);
 }
 
