@@ -45,14 +45,14 @@ __device__ __forceinline__ void dequant_tile(const uint32_t* __restrict__ cb, co
 {
     constexpr int kWords = D * BITS / 32;
     constexpr uint32_t kMask = (1u << BITS) - 1u;
-    constexpr int kMetaPerTok = D / G;
+    constexpr int kMetaPerTok = (D + G - 1) / G;   // value groups per token (the last may be short)
     constexpr int kLPR = RowGeo<D>::kLanesPerRow;
     constexpr int kRPW = RowGeo<D>::kRowsPerWave;
     constexpr int kChunks = RowGeo<D>::kChunks;
     const int c = lane % kLPR;
     const int r = lane / kLPR;
-    // lanes past a row's last chunk (head_dims 96, 160, 192, 224) have
-    // nothing to write, and no lane exchanges follow
+    // lanes past a row's last chunk (head_dims that are not 64, 128 or 256)
+    // have nothing to write, and no lane exchanges follow
     if (kChunks != kLPR && c >= kChunks) return;
     const uint32_t* ct = cb + t_first * kWords;
     float gs[8], gz[8];
@@ -138,12 +138,11 @@ static hipError_t launch_g(const DequantArgs& a, hipStream_t stream) {
 template <bool BF16>
 static hipError_t launch_fmt(const DequantArgs& a, hipStream_t stream) {
     switch (a.head_dim) {
-        case 64: return launch_g<BF16, 32, 64>(a, stream);
-        case 96: return launch_g<BF16, 32, 96>(a, stream);
-        case 160: return launch_g<BF16, 32, 160>(a, stream);
-        case 192: return launch_g<BF16, 32, 192>(a, stream);
-        case 224: return launch_g<BF16, 32, 224>(a, stream);
-        case 256: return launch_g<BF16, 32, 256>(a, stream);
+#define KIVI_DEQUANT_D(D) case D: return launch_g<BF16, 32, D>(a, stream);
+        KIVI_DEQUANT_D(16) KIVI_DEQUANT_D(32) KIVI_DEQUANT_D(48) KIVI_DEQUANT_D(64) KIVI_DEQUANT_D(80)
+        KIVI_DEQUANT_D(96) KIVI_DEQUANT_D(112) KIVI_DEQUANT_D(144) KIVI_DEQUANT_D(160) KIVI_DEQUANT_D(176)
+        KIVI_DEQUANT_D(192) KIVI_DEQUANT_D(208) KIVI_DEQUANT_D(224) KIVI_DEQUANT_D(240) KIVI_DEQUANT_D(256)
+#undef KIVI_DEQUANT_D
         default: break;
     }
     if constexpr (!BF16) {
@@ -163,11 +162,9 @@ static hipError_t launch_fmt(const DequantArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t stream) {
-    // the tiled head_dims of the flush (rows of 16 or 32 lanes, the last ones
-    // idle at 96, 160, 192 and 224); the others take the generic kernel
-    const int D = a.head_dim;
-    if (D != 64 && D != 96 && D != 128 && D != 160 && D != 192 && D != 224 && D != 256)
-        return launch_dequant_ragged(a, stream);
+    // every head_dim the ABI admits (multiples of 16 up to 256) on the tiled
+    // kernel, as the flush; the ABI rejects the others before any launch
+    if (a.head_dim < 16 || a.head_dim > 256 || a.head_dim % 16 != 0) return hipErrorInvalidValue;
     return a.bf16 ? launch_fmt<true>(a, stream) : launch_fmt<false>(a, stream);
 }
 

@@ -42,8 +42,9 @@ __device__ __forceinline__ void key_tile(const uint16_t* __restrict__ xt, uint32
     constexpr int kChunks = RowGeo<D>::kChunks;
     const int c = lane % kLPR;                     // channels 8c .. 8c+7
     const int r = lane / kLPR;                     // token rows r, r + kRPW, ...
-    // lanes past a row's last chunk (head_dims 96, 160, 192, 224) re-read
-    // that chunk and store nothing; their min/max only meet each other's
+    // lanes past a row's last chunk (head_dims that are not 64, 128 or 256)
+    // re-read that chunk and store nothing; their min/max only meet each
+    // other's
     const bool has = kChunks == kLPR || c < kChunks;
     const int cl = kChunks == kLPR ? c : (c < kChunks ? c : kChunks - 1);
 
@@ -219,13 +220,16 @@ __global__ __launch_bounds__(kBlock) void key_flush_kernel(
 // ms) and the 2-bit one 5%; with 4 to 8 bytes per token (groups of 64 or
 // 128, or binary16 scale/zero) they made it 8-10% slower, and those keep
 // the plain stores, whose partial lines the L2 merges.
+// Value groups per token: a head_dim that G does not divide ends each token
+// with a shorter group.
+template <int G, int D> constexpr int kGroupsPerTok = (D + G - 1) / G;
 template <int G, int D, typename MT>
-constexpr bool kGatherMeta = (D / G) * static_cast<int>(sizeof(MT)) == 16 ||
-                             (D / G) * static_cast<int>(sizeof(MT)) == 32;
+constexpr bool kGatherMeta = kGroupsPerTok<G, D> * static_cast<int>(sizeof(MT)) == 16 ||
+                             kGroupsPerTok<G, D> * static_cast<int>(sizeof(MT)) == 32;
 // Elements of a wave's LDS row for the gathered scale and zero (one element
 // when nothing is gathered), and the workgroup's static LDS bytes.
 template <int G, int D, typename MT>
-constexpr int kValueLdsRow = kGatherMeta<G, D, MT> ? 2 * 32 * (D / G) : 1;
+constexpr int kValueLdsRow = kGatherMeta<G, D, MT> ? 2 * 32 * kGroupsPerTok<G, D> : 1;
 template <int G, int D, typename MT>
 constexpr size_t kValueLdsBytes = sizeof(MT) * kWavesPerBlock * kValueLdsRow<G, D, MT>;
 
@@ -254,7 +258,7 @@ __device__ __forceinline__ void value_tile(const uint16_t* __restrict__ xt, uint
 {
     constexpr bool MH = sizeof(MT) == 2;            // binary16 scale/zero
     constexpr int kWords = D * BITS / 32;
-    constexpr int kMetaPerTok = D / G;              // channel groups per token
+    constexpr int kMetaPerTok = kGroupsPerTok<G, D>;   // channel groups per token
     constexpr int kLanesPerGroup = G / 8;           // 4, 8 or 16 lanes of 8 channels
     constexpr int kLPR = RowGeo<D>::kLanesPerRow;
     constexpr int kRPW = RowGeo<D>::kRowsPerWave;
@@ -263,9 +267,10 @@ __device__ __forceinline__ void value_tile(const uint16_t* __restrict__ xt, uint
     const int c = lane % kLPR;
     const int r = lane / kLPR;
     const int j = c / kLanesPerGroup;               // channel group of this lane
-    // lanes past a row's last chunk (head_dims 96, 160, 192, 224: whole
-    // groups of 4, so they form their own quads) re-read that chunk and
-    // store nothing
+    // lanes past a row's last chunk (head_dims that are not 64, 128 or 256)
+    // re-read that chunk and store nothing: in a quad they share with a
+    // ragged last group (16 channels) they repeat its last chunk, which
+    // cannot move the group's min or max
     const bool has = kChunks == kLPR || c < kChunks;
     const int cl = kChunks == kLPR ? c : (c < kChunks ? c : kChunks - 1);
 
@@ -348,8 +353,8 @@ __device__ __forceinline__ void value_tile(const uint16_t* __restrict__ xt, uint
         }
         if constexpr (kGatherMeta<G, D, MT>) {
             // to the wave's LDS rows (rows past a ragged end are never copied out)
-            if (c % kLanesPerGroup == 0) lds[row * kMetaPerTok + j] = sc;
-            else if (c % kLanesPerGroup == 1) lds[(32 + row) * kMetaPerTok + j] = ze;
+            if (has && c % kLanesPerGroup == 0) lds[row * kMetaPerTok + j] = sc;
+            else if (has && c % kLanesPerGroup == 1) lds[(32 + row) * kMetaPerTok + j] = ze;
         } else if (live) {
             // plain stores: one instruction writes 16-64 B of a line, which the
             // L2 merges (with the nontemporal hint they reached HBM as partial
@@ -391,7 +396,7 @@ __global__ __launch_bounds__(kBlock) void value_flush_kernel(
     int64_t tiles_per_bh, int64_t n_tiles, float one)
 {
     constexpr int kWords = D * BITS / 32;
-    constexpr int kMetaPerTok = D / G;
+    constexpr int kMetaPerTok = kGroupsPerTok<G, D>;
     const int lane = threadIdx.x & 63;
     const int64_t tile = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
     __shared__ MT lds_meta[kWavesPerBlock][kValueLdsRow<G, D, MT>];
@@ -486,12 +491,11 @@ static hipError_t launch_flush_g(const FlushArgs& a, hipStream_t stream) {
 template <bool KEYS, bool BF16>
 static hipError_t launch_flush_fmt(const FlushArgs& a, hipStream_t stream) {
     switch (a.head_dim) {
-        case 64: return launch_flush_g<KEYS, BF16, 32, 64>(a, stream);
-        case 96: return launch_flush_g<KEYS, BF16, 32, 96>(a, stream);
-        case 160: return launch_flush_g<KEYS, BF16, 32, 160>(a, stream);
-        case 192: return launch_flush_g<KEYS, BF16, 32, 192>(a, stream);
-        case 224: return launch_flush_g<KEYS, BF16, 32, 224>(a, stream);
-        case 256: return launch_flush_g<KEYS, BF16, 32, 256>(a, stream);
+#define KIVI_FLUSH_D(D) case D: return launch_flush_g<KEYS, BF16, 32, D>(a, stream);
+        KIVI_FLUSH_D(16) KIVI_FLUSH_D(32) KIVI_FLUSH_D(48) KIVI_FLUSH_D(64) KIVI_FLUSH_D(80)
+        KIVI_FLUSH_D(96) KIVI_FLUSH_D(112) KIVI_FLUSH_D(144) KIVI_FLUSH_D(160) KIVI_FLUSH_D(176)
+        KIVI_FLUSH_D(192) KIVI_FLUSH_D(208) KIVI_FLUSH_D(224) KIVI_FLUSH_D(240) KIVI_FLUSH_D(256)
+#undef KIVI_FLUSH_D
         default: break;
     }
     if constexpr (!BF16) {
@@ -510,20 +514,18 @@ static hipError_t launch_flush_fmt(const FlushArgs& a, hipStream_t stream) {
     }
 }
 
-// head_dims on the tiled kernels: rows of whole 16- or 32-lane units (64,
-// 128, 256) or of whole groups of 32 channels with idle lanes at the end
-// (96, 160, 192, 224); the others take the generic kernels of ragged.hip
-static bool tiled_head_dim(int D) {
-    return D == 64 || D == 96 || D == 128 || D == 160 || D == 192 || D == 224 || D == 256;
-}
+// Every head_dim the ABI admits (multiples of 16 up to 256) runs on the tiled
+// kernels: rows of 8, 16 or 32 lanes, idle at the end when D/8 is not a
+// power of two.  The ABI rejects other head_dims before any launch.
+static bool tiled_head_dim(int D) { return D >= 16 && D <= 256 && D % 16 == 0; }
 
 hipError_t launch_key_flush(const FlushArgs& a, hipStream_t stream) {
-    if (!tiled_head_dim(a.head_dim)) return launch_flush_ragged(true, a, stream);
+    if (!tiled_head_dim(a.head_dim)) return hipErrorInvalidValue;
     return a.bf16 ? launch_flush_fmt<true, true>(a, stream) : launch_flush_fmt<true, false>(a, stream);
 }
 
 hipError_t launch_value_flush(const FlushArgs& a, hipStream_t stream) {
-    if (!tiled_head_dim(a.head_dim)) return launch_flush_ragged(false, a, stream);
+    if (!tiled_head_dim(a.head_dim)) return hipErrorInvalidValue;
     return a.bf16 ? launch_flush_fmt<false, true>(a, stream) : launch_flush_fmt<false, false>(a, stream);
 }
 

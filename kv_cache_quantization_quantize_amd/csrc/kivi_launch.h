@@ -126,9 +126,6 @@ hipError_t launch_decode_attend(const AttendArgs& a, const AttendPlan& p, hipStr
 // launches)
 hipError_t launch_attend_generic(const AttendArgs& a, const AttendPlan& p, float* ws_o, float* ws_ml,
                                  hipStream_t stream);
-// head_dims other than 64, 128 and 256 (multiples of 16 up to 256, groups of 32)
-hipError_t launch_flush_ragged(bool keys, const FlushArgs& a, hipStream_t stream);
-hipError_t launch_dequant_ragged(const DequantArgs& a, hipStream_t stream);
 // Row copies of the cache (one launch for keys and values): row r < n_rows
 // of every slab comes from span a (r < n_a) or from span b (row r - n_a) and
 // goes to row r of span dst.  A span's row i is row (first + i) mod ring of

@@ -21,6 +21,19 @@ def test_flush_bytes_per_element():
     assert 288 * 32768 * 128 * bench.algo_bytes_per_elem(4) == 3321888768
 
 
+def test_flush_bytes_at_other_head_dims():
+    # head_dim 128: the per-element figure for keys and values alike
+    for keys in (True, False):
+        assert bench.flush_bytes(288, 32768, 128, 4, keys) == 3321888768
+    # head_dim 80, 2 slabs x 64 tokens: 10240 elements, 2 B in and 0.5 B of
+    # codes each; keys 2 token groups x 80 channels x 2 slabs = 320 pairs,
+    # values 3 groups (32, 32, 16 channels) x 128 tokens = 384 pairs
+    assert bench.flush_bytes(2, 64, 80, 4, True) == 10240 * 2.5 + 320 * 8
+    assert bench.flush_bytes(2, 64, 80, 4, False) == 10240 * 2.5 + 384 * 8
+    # a ragged last key group still costs one pair per channel
+    assert bench.flush_bytes(1, 33, 16, 2, True) == 33 * 16 * 2 + 33 * 16 // 4 + 2 * 16 * 8
+
+
 def test_attend_bytes_per_call():
     # per (sequence, kv head): S_kv x 192 B of 4-bit codes and binary32
     # metadata at head_dim 128, plus 128 residual tokens x 512 B

@@ -164,16 +164,15 @@ def test_other_head_dims(shape, Dh, kind, bits, fmt):
 @pytest.mark.parametrize("fmt", ["f16", "bf16"])
 @pytest.mark.parametrize("bits", [4, 2])
 @pytest.mark.parametrize("kind", ["keys", "values"])
-@pytest.mark.parametrize("Dh", [16, 48, 80, 96, 112, 160, 192, 224, 240])
+@pytest.mark.parametrize("Dh", [16, 32, 48, 80, 96, 112, 144, 160, 176, 192, 208, 224, 240])
 @pytest.mark.parametrize("shape", [(3, 101, 160, 32, 7), (2, 64, 64, 0, 0), (1, 1, 64, 32, 1)],
                          ids=lambda c: "BH%d-S%d-dst%d" % (c[0], c[1], c[3]))
-def test_ragged_head_dims(shape, Dh, kind, bits, fmt):
-    """head_dims other than 64, 128 and 256: 96, 160, 192 and 224 on the
-    tiled kernels with idle lanes at the end of each row, the others on the
-    generic kernels (a token's last value group has 16 channels when 32 does
-    not divide head_dim):
-    flush with fused reconstruction, and dequantize, bit-exact against the
-    oracle, sentinel-filled outputs checking the write window."""
+def test_other_head_dims(shape, Dh, kind, bits, fmt):
+    """Every admitted head_dim other than 64, 128 and 256: a row of
+    head_dim/8 chunks in 8, 16 or 32 lanes, the lanes past its last chunk
+    idle (a token's last value group has 16 channels when 32 does not divide
+    head_dim): flush with fused reconstruction, and dequantize, bit-exact
+    against the oracle, sentinel-filled outputs checking the write window."""
     BH, S, cap, dst_k, dst_v = shape
     dst = dst_k if kind == "keys" else dst_v
     dtype = torch.bfloat16 if fmt == "bf16" else torch.float16
@@ -186,7 +185,7 @@ def test_ragged_head_dims(shape, Dh, kind, bits, fmt):
     okind = oracle.KEYS if k == kivi.KIVI_KEYS else oracle.VALUES
     hs = oracle.Store(okind, BH, cap, Dh, bits, 32, fill_codes=CODE_SENTINEL, fill_meta=META_SENTINEL)
     recon_full = torch.full((BH, S + 8, Dh), SENTINEL16, dtype=torch.int16, device="cuda").view(dtype)
-    note(f"ragged head_dim {Dh} {fmt} flush {kind} bits={bits} BH={BH} S={S} cap={cap} dst={dst}")
+    note(f"head_dim {Dh} {fmt} flush {kind} bits={bits} BH={BH} S={S} cap={cap} dst={dst}")
     (kivi.quantize_keys if kind == "keys" else kivi.quantize_values)(x, st, dst, recon_full[:, :S])
     torch.cuda.synchronize()
     ofn = oracle.quantize_keys if kind == "keys" else oracle.quantize_values
