@@ -30,9 +30,10 @@
  *    row's last group at the row's end).  The attend takes every store
  *    geometry with binary32 scale/zero (binary16 ones: head_dim 128); its
  *    key and value stores share head_dim and group size, and q, the
- *    residual and out have head_dim channels.  head_dim 128 and 64 run on
- *    the MFMA kernels, every other head_dim on a generic (slower) kernel.
- *    Anything else returns KIVI_ERR_UNSUPPORTED.
+ *    residual and out have head_dim channels.  Every head_dim runs on the
+ *    MFMA kernels: 64, 128 and 256 on their own channel geometry, the others
+ *    on that of the next of them, with the extra channels computed as zeros
+ *    and never stored.  Anything else returns KIVI_ERR_UNSUPPORTED.
  *
  * Packed store layout (the pages fix none; [Metal post] "So why does the
  * kernel ship?" asks for packed storage of the codes):

@@ -223,10 +223,12 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 // A step start whose every load lies past the buffers' extent: the ABI
 // keeps n_quant below 2^24 tokens, and every buffer's offset for token t is
 // t times its bytes per token (key metadata: per token of the group), so a
-// start at 2^25 lands at twice any buffer's extent.  The largest such
-// offsets are 2^25 x 64 B of codes and 2^25 x 16 B of binary32 metadata;
-// lane and instruction offsets keep all of them below 2^32.
-constexpr uint32_t kFarToken = 1u << 25;
+// start at 1.5 x 2^24 lands at 1.5 times any buffer's largest extent.  The
+// largest such offset is 1.5 x 2^24 x 128 B (the code rows of head_dim 256
+// at 4 bits) = 3 x 2^30, so lane and instruction offsets (under 2^13) keep
+// every one of them below 2^32 (a start of 2^25 wrapped to the slab's first
+// rows there).
+constexpr uint32_t kFarToken = 3u << 23;
 
 struct StoreView {
     rsrc_t kc, ks, kz;      // key codes, scale, zero
@@ -300,11 +302,15 @@ __device__ __forceinline__ float4 meta_quad(u32x4 v) {
 __device__ __forceinline__ int pv_token(int q, int s) { return 16 * (s >> 2) + 4 * q + (s & 3); }
 
 
+// ds is the store's head_dim: D itself, or (padded kernels) a multiple of
+// 16 below D whose rows the lane geometry of D reads.  Lanes whose channels
+// lie past ds load bytes of the next row or, past the slab's extent, zeros;
+// the staging masks them.
 template <int BITS, int G, int MB, int D>
 __device__ __forceinline__ void issue_step(StepLoad<BITS, G, D>& L, const StoreView& S, const LaneOffsets& O,
-                                           uint32_t t0, int n) {
-    constexpr uint32_t kRow = D * BITS / 8;                 // code bytes per token
-    constexpr int kMPT = D / G;                             // value groups per token
+                                           uint32_t t0, int n, int ds) {
+    const uint32_t kRow = static_cast<uint32_t>(ds) * BITS / 8;   // code bytes per token
+    constexpr int kMPT = D / G;                             // value groups per token of D's geometry
     constexpr int kKB = Geo<D>::kKB;
     constexpr int kKBytes = Geo<D>::kCPG * BITS / 8;        // a lane group's key code bytes: 4 .. 32
     const uint32_t ko = O.k + t0 * kRow;
@@ -332,9 +338,9 @@ __device__ __forceinline__ void issue_step(StepLoad<BITS, G, D>& L, const StoreV
     }
     // key metadata of the step's group (a 32-token step never crosses one):
     // the lane's kKMC channels' pairs, kKMC * MB bytes
-    const uint32_t kmo = O.km + (t0 / G) * (D * MB);
-    // value metadata: D/G pairs per token; the lane's groups
-    const uint32_t vmo = O.vm + (D * MB / G) * t0;
+    const uint32_t kmo = O.km + (t0 / G) * (static_cast<uint32_t>(ds) * MB);
+    // value metadata: ceil(ds/G) pairs per token; the lane's groups
+    const uint32_t vmo = O.vm + static_cast<uint32_t>((ds + G - 1) / G * MB) * t0;
     if constexpr (MB == 4) {
         if constexpr (Geo<D>::kKMC == 4) {
             L.ks = __builtin_amdgcn_raw_buffer_load_b128(S.ks, kmo, 0, kStreamLoad);
@@ -494,10 +500,14 @@ __device__ __forceinline__ Frag softmax_any(const float4_t (&acc_s)[2], SoftStat
 }
 
 // One step of store tokens [t0, t0 + 32), tokens at or past n_quant masked.
-template <int BITS, int G, int MB, bool BF, int D>
+// PAD: the store's head_dim ds is below D; the key scale and zero of
+// channels at or past ds are staged as 0, so those channels of K are exactly
+// 0 whatever their codes (the query is 0 there too), and the value channels
+// past ds only reach outputs that are never stored.
+template <int BITS, int G, int MB, bool BF, int D, bool PAD>
 __device__ __forceinline__ void store_step(const StepLoad<BITS, G, D>& L, Smem<D>& sm,
                                            SoftState<Geo<D>::kPV>& st, int t0, int n_quant, float c2,
-                                           int l, int n, int q) {
+                                           int l, int n, int q, int ds) {
     // ---- stage this step's metadata in LDS (zero' = zero - M * scale')
     constexpr float kM = kCodeOffset<BITS, BF>;
     constexpr int kMPT = D / G;                 // value groups per token
@@ -506,7 +516,10 @@ __device__ __forceinline__ void store_step(const StepLoad<BITS, G, D>& L, Smem<D
     if constexpr (Geo<D>::kKMC == 4) {
         // channels 4l .. 4l + 3; key scale times 2^-e of each channel's code
         // position (code_pairs)
-        const float4 ks = meta_quad<MB>(L.ks), kz = meta_quad<MB>(L.kz);
+        float4 ks = meta_quad<MB>(L.ks), kz = meta_quad<MB>(L.kz);
+        if constexpr (PAD) {
+            if (4 * l >= ds) ks = kz = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
         const float sc[4] = {ks.x, ks.y, ks.z, ks.w}, zc[4] = {kz.x, kz.y, kz.z, kz.w};
         float so[4], zo[4];
 #pragma unroll
@@ -518,7 +531,10 @@ __device__ __forceinline__ void store_step(const StepLoad<BITS, G, D>& L, Smem<D
         *reinterpret_cast<float4*>(&sm.kz[kidx(4 * l)]) = make_float4(zo[0], zo[1], zo[2], zo[3]);
     } else if (2 * l < D) {
         // key scale times 2^-e of its channel's code position (code_pairs)
-        const float2 ks = meta_pair<MB>(L.ks), kz = meta_pair<MB>(L.kz);
+        float2 ks = meta_pair<MB>(L.ks), kz = meta_pair<MB>(L.kz);
+        if constexpr (PAD) {
+            if (2 * l >= ds) ks = kz = make_float2(0.0f, 0.0f);
+        }
         const float s0 = ks.x * kscale_factor<BITS, BF>(2 * l);
         const float s1 = ks.y * kscale_factor<BITS, BF>(2 * l + 1);
         *reinterpret_cast<float2*>(&sm.ks[kidx(2 * l)]) = make_float2(s0, s1);
@@ -651,10 +667,13 @@ __device__ __forceinline__ int ring_row(int tok, int head, int ring) {
     return r >= ring ? r - ring : r;
 }
 
-template <int BITS, bool BF, int D>
+// Rows have ds channels (PAD: ds < D); channels at or past ds are not
+// loaded and read as 0 (ds is a multiple of 16, so every 8- or 4-channel
+// load is wholly inside a row or wholly past it).
+template <int BITS, bool BF, int D, bool PAD>
 __device__ __forceinline__ void residual_step(const uint16_t* kr, const uint16_t* vr, const Smem<D>& sm,
                                               SoftState<Geo<D>::kPV>& st, int t0, int n_res, float c2,
-                                              int l, int n, int q, int head, int ring) {
+                                              int l, int n, int q, int head, int ring, int ds) {
     constexpr int kCPG = Geo<D>::kCPG, kKB = Geo<D>::kKB, kPV = Geo<D>::kPV;
     const int last = n_res - 1;
     // Every row of the step is loaded up front (K rows of both 16-token
@@ -663,10 +682,10 @@ __device__ __forceinline__ void residual_step(const uint16_t* kr, const uint16_t
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
         const int tok = ring_row(min(t0 + 16 * blk + n, last), head, ring);
-        const uint4* src = reinterpret_cast<const uint4*>(kr + tok * D + kCPG * q);
+        const uint4* src = reinterpret_cast<const uint4*>(kr + tok * ds + kCPG * q);
 #pragma unroll
         for (int v = 0; v < kCPG / 8; ++v) {
-            const uint4 t = src[v];
+            const uint4 t = (!PAD || kCPG * q + 8 * v < ds) ? src[v] : make_uint4(0u, 0u, 0u, 0u);
             rn[blk][4 * v] = t.x; rn[blk][4 * v + 1] = t.y; rn[blk][4 * v + 2] = t.z; rn[blk][4 * v + 3] = t.w;
         }
     }
@@ -675,15 +694,16 @@ __device__ __forceinline__ void residual_step(const uint16_t* kr, const uint16_t
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
         const int tok = ring_row(min(t0 + pv_token(q, s), last), head, ring);
-        const uint16_t* p = vr + tok * D + kPV * n;
+        const uint16_t* p = vr + tok * ds + kPV * n;
         if constexpr (kPV >= 8) {
 #pragma unroll
             for (int v = 0; v < kPV / 8; ++v) {
-                const uint4 t = reinterpret_cast<const uint4*>(p)[v];
+                const uint4 t = (!PAD || kPV * n + 8 * v < ds) ? reinterpret_cast<const uint4*>(p)[v]
+                                                               : make_uint4(0u, 0u, 0u, 0u);
                 vw[s][4 * v] = t.x; vw[s][4 * v + 1] = t.y; vw[s][4 * v + 2] = t.z; vw[s][4 * v + 3] = t.w;
             }
         } else {
-            const uint2 t = *reinterpret_cast<const uint2*>(p);
+            const uint2 t = (!PAD || kPV * n < ds) ? *reinterpret_cast<const uint2*>(p) : make_uint2(0u, 0u);
             vw[s][0] = t.x; vw[s][1] = t.y;
         }
     }
@@ -740,12 +760,15 @@ template <bool BF, int D> constexpr int kWavesPerSimd =
                                                                     : KIVI_ATTEND_WAVES_PER_SIMD;
 template <bool BF, int D> constexpr int kNBufOf = (BF && D == 256) ? KIVI_ATTEND_BF16_D256_NBUF : D == 256 ? 2 : kNBuf;
 
-template <int BITS, int GQA, int G, int MB, bool BF, int D>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<BF, D>))) void attend_partial_kernel(const AttendArgs a, int spw, int steps_q,
-                                                            int64_t n_split, float* __restrict__ ws_o,
-                                                            float* __restrict__ ws_ml)
+// PAD: the stores, q, the residual rows and the partials have ds =
+// a.head_dim channels, a multiple of 16 below D, and the lanes of D's
+// geometry past ds compute on zeros (see store_step and residual_step).
+template <int BITS, int GQA, int G, int MB, bool BF, int D, bool PAD>
+__device__ __forceinline__ void partial_body(const AttendArgs& a, int spw, int steps_q, int64_t n_split,
+                                             float* __restrict__ ws_o, float* __restrict__ ws_ml)
 {
     constexpr int kCPG = Geo<D>::kCPG, kKB = Geo<D>::kKB, kPV = Geo<D>::kPV;
+    const int ds = PAD ? a.head_dim : D;
     __shared__ Smem<D> sm;
     const int l = threadIdx.x;
     const int n = l & 15;
@@ -773,8 +796,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
 
     // Store part: buffer views and the first kNB - 1 steps' loads, issued
     // before the query so the two HBM latencies overlap.
-    constexpr int kWords = D * BITS / 32;
-    constexpr int kMetaPerTok = D / G;
+    const int words = ds * BITS / 32;                   // code words per token
+    constexpr int kMetaPerTok = D / G;                  // value groups per token of D's geometry
+    const int meta_per_tok = (ds + G - 1) / G;          // ... and of the store
     constexpr int kNB = kNBufOf<BF, D>;
     StoreView S;
     LaneOffsets O;
@@ -786,28 +810,28 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
     const auto pref = [j1](int t) { return t < j1 ? static_cast<uint32_t>(t) : kFarToken; };
     if (has_store) {
         const uint32_t n_groups = static_cast<uint32_t>((nq + G - 1) / G);
-        S.kc = make_rsrc(a.k_codes + bkv * a.k_codes_bh_stride, static_cast<uint32_t>(nq) * kWords * 4u);
+        S.kc = make_rsrc(a.k_codes + bkv * a.k_codes_bh_stride, static_cast<uint32_t>(nq) * words * 4u);
         const char* kmeta_s = static_cast<const char*>(a.k_scale) + bkv * a.k_meta_bh_stride * MB;
         const char* kmeta_z = static_cast<const char*>(a.k_zero) + bkv * a.k_meta_bh_stride * MB;
         const char* vmeta_s = static_cast<const char*>(a.v_scale) + bkv * a.v_meta_bh_stride * MB;
         const char* vmeta_z = static_cast<const char*>(a.v_zero) + bkv * a.v_meta_bh_stride * MB;
-        S.ks = make_rsrc(kmeta_s, n_groups * D * MB);
-        S.kz = make_rsrc(kmeta_z, n_groups * D * MB);
-        S.vc = make_rsrc(a.v_codes + bkv * a.v_codes_bh_stride, static_cast<uint32_t>(nq) * kWords * 4u);
-        S.vs = make_rsrc(vmeta_s, static_cast<uint32_t>(nq) * kMetaPerTok * MB);
-        S.vz = make_rsrc(vmeta_z, static_cast<uint32_t>(nq) * kMetaPerTok * MB);
+        S.ks = make_rsrc(kmeta_s, n_groups * ds * MB);
+        S.kz = make_rsrc(kmeta_z, n_groups * ds * MB);
+        S.vc = make_rsrc(a.v_codes + bkv * a.v_codes_bh_stride, static_cast<uint32_t>(nq) * words * 4u);
+        S.vs = make_rsrc(vmeta_s, static_cast<uint32_t>(nq) * meta_per_tok * MB);
+        S.vz = make_rsrc(vmeta_z, static_cast<uint32_t>(nq) * meta_per_tok * MB);
         // the lane group's channels start at word kCPG * q * BITS / 32 of a
         // token row; the lane's PV channels at word kPV * n * BITS / 32
-        O.k = static_cast<uint32_t>(n * kWords + kCPG * q * BITS / 32) * 4u;
-        O.v = static_cast<uint32_t>(4 * q * kWords + kPV * n * BITS / 32) * 4u;
+        O.k = static_cast<uint32_t>(n * words + kCPG * q * BITS / 32) * 4u;
+        O.v = static_cast<uint32_t>(4 * q * words + kPV * n * BITS / 32) * 4u;
         // lanes past D / kKMC load but stage nothing
         O.km = static_cast<uint32_t>(l) * (Geo<D>::kKMC * MB);
         O.vm = kMetaPerTok >= 4
-                   ? static_cast<uint32_t>(l & 31) * (kMetaPerTok * MB) +
+                   ? static_cast<uint32_t>(l & 31) * (meta_per_tok * MB) +
                          static_cast<uint32_t>(l >> 5) * (kMetaPerTok / 2 * MB)
-                   : static_cast<uint32_t>(l & 31) * (kMetaPerTok * MB);
+                   : static_cast<uint32_t>(l & 31) * (meta_per_tok * MB);
 #pragma unroll
-        for (int u = 0; u + 1 < kNB; ++u) issue_step<BITS, G, MB, D>(buf[u], S, O, pref(j0 + u * kStep), n);
+        for (int u = 0; u + 1 < kNB; ++u) issue_step<BITS, G, MB, D>(buf[u], S, O, pref(j0 + u * kStep), n, ds);
     }
 
     // B operand of QK^T: q of head n (zero for n >= GQA) in slot order.
@@ -815,10 +839,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
         Frag bq[kKB];
         uint32_t qn[kCPG / 2];                // channels kCPG*q .. kCPG*q + kCPG - 1, natural order
         if (n < GQA) {
-            const uint4* src = reinterpret_cast<const uint4*>(a.q + (qrow0 + n) * D + kCPG * q);
+            const uint4* src = reinterpret_cast<const uint4*>(a.q + (qrow0 + n) * ds + kCPG * q);
 #pragma unroll
             for (int v = 0; v < kCPG / 8; ++v) {
-                const uint4 t = src[v];
+                const uint4 t = (!PAD || kCPG * q + 8 * v < ds) ? src[v] : make_uint4(0u, 0u, 0u, 0u);
                 qn[4 * v] = t.x; qn[4 * v + 1] = t.y; qn[4 * v + 2] = t.z; qn[4 * v + 3] = t.w;
             }
         } else {
@@ -858,8 +882,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
         for (int t0 = j0; t0 < j1; t0 += kNB * kStep) {
 #pragma unroll
             for (int u = 0; u < kNB; ++u) {
-                issue_step<BITS, G, MB, D>(buf[(u + kNB - 1) % kNB], S, O, pref(t0 + (u + kNB - 1) * kStep), n);
-                store_step<BITS, G, MB, BF, D>(buf[u], sm, st, t0 + u * kStep, j1, c2, l, n, q);
+                issue_step<BITS, G, MB, D>(buf[(u + kNB - 1) % kNB], S, O, pref(t0 + (u + kNB - 1) * kStep), n, ds);
+                store_step<BITS, G, MB, BF, D, PAD>(buf[u], sm, st, t0 + u * kStep, j1, c2, l, n, q, ds);
                 if (t0 + (u + 1) * kStep >= j1) goto store_done;
             }
         }
@@ -869,27 +893,47 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
         const uint16_t* kr = a.k_res + bkv * a.res_bh_stride;
         const uint16_t* vr = a.v_res + bkv * a.res_bh_stride;
         for (int t0 = r0; t0 < r1; t0 += kStep)
-            residual_step<BITS, BF, D>(kr, vr, sm, st, t0, r1, c2, l, n, q, a.res_head, a.res_ring);
+            residual_step<BITS, BF, D, PAD>(kr, vr, sm, st, t0, r1, c2, l, n, q, a.res_head, a.res_ring, ds);
     }
 
     // ---- partial (m, l, o) of head n: lane (q, n) holds channels
     // kPV * (4q + r) + i (= kCPG q + kPV r + i)
     const float l_tot = rows_sum(st.l_part);
     if (n < GQA) {
-        float* dst = ws_o + ((qrow0 + n) * n_split + split) * D + kCPG * q;
+        float* dst = ws_o + ((qrow0 + n) * n_split + split) * ds + kCPG * q;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
             for (int c = 0; c < kPV / 4; ++c)
-                *reinterpret_cast<float4*>(dst + kPV * r + 4 * c) =
-                    make_float4(st.acc_o[4 * c][r], st.acc_o[4 * c + 1][r], st.acc_o[4 * c + 2][r],
-                                st.acc_o[4 * c + 3][r]);
+                if (!PAD || kCPG * q + kPV * r + 4 * c < ds)
+                    *reinterpret_cast<float4*>(dst + kPV * r + 4 * c) =
+                        make_float4(st.acc_o[4 * c][r], st.acc_o[4 * c + 1][r], st.acc_o[4 * c + 2][r],
+                                    st.acc_o[4 * c + 3][r]);
         if (q == 0) {
             float* ml = ws_ml + ((qrow0 + n) * n_split + split) * 2;
             ml[0] = st.m_run;
             ml[1] = l_tot;
         }
     }
+}
+
+template <int BITS, int GQA, int G, int MB, bool BF, int D>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<BF, D>))) void attend_partial_kernel(const AttendArgs a, int spw, int steps_q,
+                                                            int64_t n_split, float* __restrict__ ws_o,
+                                                            float* __restrict__ ws_ml)
+{
+    partial_body<BITS, GQA, G, MB, BF, D, false>(a, spw, steps_q, n_split, ws_o, ws_ml);
+}
+
+// Store head_dims below D that are not 64 or 128 (multiples of 16, groups
+// of 32, binary32 scale/zero) on D's geometry: 16 .. 48 on 64, 80 .. 112 on
+// 128, 144 .. 240 on 256.
+template <int BITS, int GQA, bool BF, int D>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<BF, D>))) void attend_partial_padded_kernel(const AttendArgs a, int spw, int steps_q,
+                                                            int64_t n_split, float* __restrict__ ws_o,
+                                                            float* __restrict__ ws_ml)
+{
+    partial_body<BITS, GQA, kGroup, 4, BF, D, true>(a, spw, steps_q, n_split, ws_o, ws_ml);
 }
 
 // ---------------------------------------------------------------------------
@@ -945,5 +989,50 @@ hipError_t launch_partials(const AttendArgs& a, const AttendPlan& p, float* ws_o
 // The bfloat16 partials (binary32 scale/zero), compiled in attend_bf16.hip.
 hipError_t launch_attend_partial_bf16(const AttendArgs& a, const AttendPlan& p, float* ws_o,
                                       float* ws_ml, hipStream_t stream);
+
+// The padded partial kernels: a store head_dim ds that is not 64, 128 or
+// 256 runs on the geometry of the next of them (groups of 32, binary32
+// scale/zero).
+template <int BITS, int GQA, bool BF, int D>
+hipError_t launch_padded(const AttendArgs& a, const AttendPlan& p, float* ws_o, float* ws_ml,
+                         hipStream_t stream) {
+    const dim3 grid(static_cast<uint32_t>(p.n_split), static_cast<uint32_t>(a.B * a.Hkv));
+    hipLaunchKernelGGL((attend_partial_padded_kernel<BITS, GQA, BF, D>), grid, dim3(64), 0, stream, a,
+                       static_cast<int>(p.steps_per_wave), static_cast<int>(p.steps_q), p.n_split,
+                       ws_o, ws_ml);
+    return hipGetLastError();
+}
+
+template <int BITS, bool BF, int D>
+hipError_t launch_padded_gqa(const AttendArgs& a, const AttendPlan& p, float* ws_o, float* ws_ml,
+                             hipStream_t stream) {
+    switch (a.Hq / a.Hkv) {
+        case 1: return launch_padded<BITS, 1, BF, D>(a, p, ws_o, ws_ml, stream);
+        case 2: return launch_padded<BITS, 2, BF, D>(a, p, ws_o, ws_ml, stream);
+        case 4: return launch_padded<BITS, 4, BF, D>(a, p, ws_o, ws_ml, stream);
+        default: return launch_padded<BITS, 8, BF, D>(a, p, ws_o, ws_ml, stream);
+    }
+}
+
+template <bool BF>
+hipError_t launch_partials_padded(const AttendArgs& a, const AttendPlan& p, float* ws_o, float* ws_ml,
+                                  hipStream_t stream) {
+    const bool four = a.bits == 4;
+    if (a.head_dim < 64)
+        return four ? launch_padded_gqa<4, BF, 64>(a, p, ws_o, ws_ml, stream)
+                    : launch_padded_gqa<2, BF, 64>(a, p, ws_o, ws_ml, stream);
+    if (a.head_dim < 128)
+        return four ? launch_padded_gqa<4, BF, 128>(a, p, ws_o, ws_ml, stream)
+                    : launch_padded_gqa<2, BF, 128>(a, p, ws_o, ws_ml, stream);
+    return four ? launch_padded_gqa<4, BF, 256>(a, p, ws_o, ws_ml, stream)
+                : launch_padded_gqa<2, BF, 256>(a, p, ws_o, ws_ml, stream);
+}
+
+// Compiled in attend_pad.hip (fp16, which hands bfloat16 calls to the
+// second) and attend_pad_bf16.hip.
+hipError_t launch_attend_partial_padded(const AttendArgs& a, const AttendPlan& p, float* ws_o,
+                                        float* ws_ml, hipStream_t stream);
+hipError_t launch_attend_partial_padded_bf16(const AttendArgs& a, const AttendPlan& p, float* ws_o,
+                                             float* ws_ml, hipStream_t stream);
 
 }  // namespace kivi

@@ -79,6 +79,7 @@ struct AttendArgs {
     bool meta16;                   // binary16 scale/zero (keys and values alike)
     bool bf16;                     // q, residual and the reconstruction in bfloat16
     int head_dim;                  // 128; others with groups of 32 and binary32 scale/zero
+                                   // (q, residual, out and the partials have head_dim channels)
 };
 
 // Three waves per SIMD for the attend at head_dim 64 and 128, fp16 and
@@ -121,11 +122,6 @@ hipError_t launch_key_flush(const FlushArgs& a, hipStream_t stream);
 hipError_t launch_value_flush(const FlushArgs& a, hipStream_t stream);
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t stream);
 hipError_t launch_decode_attend(const AttendArgs& a, const AttendPlan& p, hipStream_t stream);
-// the attend at head_dims other than 64, 128 and 256 (groups of 32,
-// binary32 scale/zero): partials and combine (one wave per workgroup, two
-// launches)
-hipError_t launch_attend_generic(const AttendArgs& a, const AttendPlan& p, float* ws_o, float* ws_ml,
-                                 hipStream_t stream);
 // Row copies of the cache (one launch for keys and values): row r < n_rows
 // of every slab comes from span a (r < n_a) or from span b (row r - n_a) and
 // goes to row r of span dst.  A span's row i is row (first + i) mod ring of

@@ -23,7 +23,9 @@ AttendPlan plan_attend(int64_t B, int Hq, int Hkv, int64_t n_quant, int64_t n_re
     const int64_t steps_q = (n_quant + kAttendStep - 1) / kAttendStep;
     const int64_t steps = steps_q + (n_res + kAttendStep - 1) / kAttendStep;
     const int64_t total = pairs * steps;
-    const int64_t slots = head_dim == 256 ? kWaveSlotsD256 : bf16 ? kWaveSlotsBF16 : kWaveSlots;
+    // head_dims other than 64, 128 and 256 run on the kernels of the next of
+    // them, with their occupancy
+    const int64_t slots = head_dim > 128 ? kWaveSlotsD256 : bf16 ? kWaveSlotsBF16 : kWaveSlots;
     int64_t spw = 1;
     if (total > slots) {
         // A variable-length batch sizes the grid for its longest sequence;
@@ -45,10 +47,6 @@ AttendPlan plan_attend(int64_t B, int Hq, int Hkv, int64_t n_quant, int64_t n_re
     // against 13.1 us at 3 steps).
     const int64_t longer = (total + 699) / 700;
     spw = std::max(spw, std::min<int64_t>(9, longer));
-    // The generic kernel (head_dims other than 64, 128 and 256) has no fixed
-    // cost to amortize and is latency-bound per lane: one 64-token chunk per
-    // wave.
-    if (head_dim != 64 && head_dim != 128 && head_dim != 256) spw = std::min<int64_t>(spw, 2);
     AttendPlan p;
     p.steps_q = steps_q;
     p.steps_per_wave = spw;

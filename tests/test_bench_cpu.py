@@ -50,6 +50,9 @@ def test_attend_bytes_per_call():
     assert bench.attend_bytes(1, 1, 0, 4, group=128) == 144
     # head_dim 256: twice the codes and metadata
     assert bench.attend_bytes(1, 1, 0, 4, head_dim=256) == 384
+    # head_dim 80: 2 x 40 B of codes, 20 B of key metadata per token, and
+    # three value groups (32, 32 and 16 channels) of 8 B
+    assert bench.attend_bytes(1, 1, 0, 4, head_dim=80) == 124
 
 
 def test_stats_are_order_statistics():

@@ -64,8 +64,8 @@ def test_decode_loop_group_sizes(G, case):
     (256, (1, 1, 2, 8, 4, 32, 32, 256, 40, 70, "f32")),
 ], ids=["D64", "D96-bf16", "D256"])
 def test_decode_loop_head_dims(Dh, case):
-    """Caches at other head_dims (the attend at 64 on MFMA, at 96 and 256 on
-    the generic kernel)."""
+    """Caches at other head_dims (the attend at 64 and 256 on their own MFMA
+    geometry, at 96 padded onto the 128-channel one)."""
     _decode_loop(case, 32, Dh)
 
 

@@ -267,7 +267,7 @@ def test_attend_head_dim_64(case, fmt):
     assert err <= tol, f"varlen max-abs error {err:.3e}"
 
 
-GENERIC = [
+ATTEND_CASES = [
     # B, Hq, Hkv, n_quant, n_res, bits
     (2, 16, 8, 300, 37, 4),
     (1, 8, 2, 1000, 5, 2),
@@ -277,28 +277,32 @@ GENERIC = [
 # plans the small cases above never reach: several steps per wave with a wave
 # that runs from the store into the residual window, and a single sequence
 # with eight query heads per kv head split 65 ways (the 16-wave combine)
-GENERIC_PLANS = [
+ATTEND_PLANS = [
     (4, 32, 8, 2048, 128, 4),
     (1, 8, 1, 2048, 5, 4),
 ]
+# every admitted head_dim but 128: 64 and 256 on their own MFMA geometry, the
+# others padded to the next of 64, 128 and 256
+OTHER_DIMS = [16, 32, 48, 64, 80, 96, 112, 144, 160, 176, 192, 208, 224, 240, 256]
 
 
 @pytest.mark.parametrize("fmt", ["f16", "bf16"])
-@pytest.mark.parametrize("Dh", [256, 96])
-@pytest.mark.parametrize("case", GENERIC_PLANS, ids=lambda c: "B%d-Hq%d-Hkv%d-nq%d-nr%d-b%d" % c)
-def test_attend_generic_plans(case, Dh, fmt):
-    test_attend_generic_head_dims(case, Dh, fmt)
+@pytest.mark.parametrize("Dh", [256, 96, 48, 176])
+@pytest.mark.parametrize("case", ATTEND_PLANS, ids=lambda c: "B%d-Hq%d-Hkv%d-nq%d-nr%d-b%d" % c)
+def test_attend_other_head_dim_plans(case, Dh, fmt):
+    test_attend_other_head_dims(case, Dh, fmt)
 
 
 @pytest.mark.parametrize("fmt", ["f16", "bf16"])
-@pytest.mark.parametrize("Dh", [256, 96, 80, 16])
-@pytest.mark.parametrize("case", GENERIC, ids=lambda c: "B%d-Hq%d-Hkv%d-nq%d-nr%d-b%d" % c)
-def test_attend_generic_head_dims(case, Dh, fmt):
-    """The decode attends at head_dim 256 (the MFMA kernel, 16 PV
-    accumulators per lane) and at the ragged head_dims (the generic kernel,
-    which rebuilds K and V exactly as stored and rounds no probabilities);
-    groups of 32, held to 2e-3 in both formats; uniform and variable-length
-    against the oracle."""
+@pytest.mark.parametrize("Dh", OTHER_DIMS)
+@pytest.mark.parametrize("case", ATTEND_CASES, ids=lambda c: "B%d-Hq%d-Hkv%d-nq%d-nr%d-b%d" % c)
+def test_attend_other_head_dims(case, Dh, fmt):
+    """The decode attends at head_dim 256 (16 PV accumulators per lane) and
+    at the head_dims padded onto the 64-, 128- or 256-channel MFMA geometry
+    (the channels past head_dim dequantized with zero scale and zero, zero
+    queries and residual rows there, and never stored); groups of 32, held
+    to 2e-3 in both formats; uniform and variable-length against the
+    oracle."""
     B, Hq, Hkv, nq, nr, bits = case
     BH = B * Hkv
     cap = max(32, ((nq + 31) // 32) * 32)
@@ -311,7 +315,7 @@ def test_attend_generic_head_dims(case, Dh, fmt):
     q = synth.query(B, Hq, Dh, seed=seed, device="cuda").to(dtype)
     ks = kivi.Store(kivi.KIVI_KEYS, BH, cap, bits, head_dim=Dh)
     vs = kivi.Store(kivi.KIVI_VALUES, BH, cap, bits, head_dim=Dh)
-    note(f"generic attend head_dim {Dh} {fmt} B={B} Hq={Hq} Hkv={Hkv} n_quant={nq} n_res={nr} bits={bits}")
+    note(f"attend head_dim {Dh} {fmt} B={B} Hq={Hq} Hkv={Hkv} n_quant={nq} n_res={nr} bits={bits}")
     if nq:
         kivi.quantize_keys(kx.contiguous(), ks, 0)
         kivi.quantize_values(vx.contiguous(), vs, 0)
@@ -341,13 +345,14 @@ def test_attend_generic_head_dims(case, Dh, fmt):
 
 @pytest.mark.parametrize("fmt", ["f16", "bf16"])
 @pytest.mark.parametrize("bits", [4, 2])
-def test_attend_head_dim_256_at_the_bench_shape(fmt, bits):
-    """head_dim 256 at the bench's B=32 x 2048 + 128 shape (32 query heads
-    over 8 kv heads, several steps per wave): sampled sequences against the
-    oracle within 2e-3."""
-    B, Hq, Hkv, nq, nr, Dh = 32, 32, 8, 2048, 128, 256
+@pytest.mark.parametrize("Dh", [256, 96])
+def test_attend_head_dims_at_the_bench_shape(Dh, fmt, bits):
+    """head_dims 256 and 96 (padded to 128) at the bench's B=32 x 2048 + 128
+    shape (32 query heads over 8 kv heads, several steps per wave): sampled
+    sequences against the oracle within 2e-3."""
+    B, Hq, Hkv, nq, nr = 32, 32, 8, 2048, 128
     BH = B * Hkv
-    seed = 9700 + bits
+    seed = 9700 + bits + Dh
     dtype = torch.bfloat16 if fmt == "bf16" else torch.float16
     kx = synth.kv_tensor(BH, nq, Dh, keys=True, seed=seed, device="cuda", dtype=dtype)
     vx = synth.kv_tensor(BH, nq, Dh, keys=False, seed=seed, device="cuda", dtype=dtype)
@@ -356,7 +361,7 @@ def test_attend_head_dim_256_at_the_bench_shape(fmt, bits):
     q = synth.query(B, Hq, Dh, seed=seed, device="cuda").to(dtype)
     ks = kivi.Store(kivi.KIVI_KEYS, BH, nq, bits, head_dim=Dh)
     vs = kivi.Store(kivi.KIVI_VALUES, BH, nq, bits, head_dim=Dh)
-    note(f"attend head_dim 256 {fmt} bits={bits} B={B} S_kv={nq}+{nr}")
+    note(f"attend head_dim {Dh} {fmt} bits={bits} B={B} S_kv={nq}+{nr}")
     kivi.quantize_keys(kx, ks, 0)
     kivi.quantize_values(vx, vs, 0)
     out = kivi.decode_attend(q, ks, vs, nq, kr, vr, nr).cpu().numpy()
