@@ -243,7 +243,16 @@ struct LaneOffsets {
     uint32_t km;            // key scale / zero of channels 2l, 2l+1
     uint32_t vm;            // value scale / zero of token l & 31: groups 2(l>>5), +1 (G = 32),
                             // groups 0, 1 (G = 64) or group 0 (G = 128)
+    // Padded kernels: whether the lane's key code, value code and key
+    // metadata channels reach below the store's head_dim.  The loads of a
+    // lane that holds only padded channels go to kDeadOffset instead.
+    bool k_live = true, v_live = true, km_live = true;
 };
+
+// A buffer offset past every extent (the ABI keeps extents below 2^31): a
+// load there returns zeros without a memory access.  Instruction offsets of
+// at most 16 keep it below 2^32.
+constexpr uint32_t kDeadOffset = 0xFFFFFF00u;
 
 // Channel geometry for head_dim D (64, 128 or 256).  QK^T: lane group q
 // holds channels kCPG*q + 8*kb + slot of key unit kb < kKB.  PV: MFMA i < kPV
@@ -306,9 +315,11 @@ __device__ __forceinline__ int pv_token(int q, int s) { return 16 * (s >> 2) + 4
 // 16 below D whose rows the lane geometry of D reads.  Lanes whose channels
 // lie past ds load bytes of the next row or, past the slab's extent, zeros;
 // the staging masks them.
-template <int BITS, int G, int MB, int D>
+template <int BITS, int G, int MB, int D, bool PAD>
 __device__ __forceinline__ void issue_step(StepLoad<BITS, G, D>& L, const StoreView& S, const LaneOffsets& O,
                                            uint32_t t0, int n, int ds) {
+    // a lane holding only channels past ds loads nothing (padded kernels)
+    const auto lane_off = [](bool live, uint32_t off) { return (!PAD || live) ? off : kDeadOffset; };
     const uint32_t kRow = static_cast<uint32_t>(ds) * BITS / 8;   // code bytes per token
     constexpr int kMPT = D / G;                             // value groups per token of D's geometry
     constexpr int kKB = Geo<D>::kKB;
@@ -318,7 +329,7 @@ __device__ __forceinline__ void issue_step(StepLoad<BITS, G, D>& L, const StoreV
     for (int blk = 0; blk < 2; ++blk) {
         // the lane group's kCPG channels: one word per key unit (4-bit) or
         // per two units (2-bit)
-        const uint32_t off = ko + 16 * kRow * blk;
+        const uint32_t off = lane_off(O.k_live, ko + 16 * kRow * blk);
         uint32_t w[8];
         if constexpr (kKBytes >= 16) {
             const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(S.kc, off, 0, kStreamLoad);
@@ -338,7 +349,7 @@ __device__ __forceinline__ void issue_step(StepLoad<BITS, G, D>& L, const StoreV
     }
     // key metadata of the step's group (a 32-token step never crosses one):
     // the lane's kKMC channels' pairs, kKMC * MB bytes
-    const uint32_t kmo = O.km + (t0 / G) * (static_cast<uint32_t>(ds) * MB);
+    const uint32_t kmo = lane_off(O.km_live, O.km + (t0 / G) * (static_cast<uint32_t>(ds) * MB));
     // value metadata: ceil(ds/G) pairs per token; the lane's groups
     const uint32_t vmo = O.vm + static_cast<uint32_t>((ds + G - 1) / G * MB) * t0;
     if constexpr (MB == 4) {
@@ -377,7 +388,7 @@ __device__ __forceinline__ void issue_step(StepLoad<BITS, G, D>& L, const StoreV
     const uint32_t shift = (kPV * n * BITS) & 31;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-        const uint32_t off = vo + (16 * (s >> 2) + (s & 3)) * kRow;
+        const uint32_t off = lane_off(O.v_live, vo + (16 * (s >> 2) + (s & 3)) * kRow);
         if constexpr (StepLoad<BITS, G, D>::kVW == 2) {
             const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(S.vc, off, 0, kStreamLoad);
             L.vw[s][0] = t.x; L.vw[s][1] = t.y;
@@ -830,8 +841,13 @@ __device__ __forceinline__ void partial_body(const AttendArgs& a, int spw, int s
                    ? static_cast<uint32_t>(l & 31) * (meta_per_tok * MB) +
                          static_cast<uint32_t>(l >> 5) * (kMetaPerTok / 2 * MB)
                    : static_cast<uint32_t>(l & 31) * (meta_per_tok * MB);
+        if constexpr (PAD) {
+            O.k_live = kCPG * q < ds;
+            O.v_live = kPV * n < ds;
+            O.km_live = Geo<D>::kKMC * l < ds;
+        }
 #pragma unroll
-        for (int u = 0; u + 1 < kNB; ++u) issue_step<BITS, G, MB, D>(buf[u], S, O, pref(j0 + u * kStep), n, ds);
+        for (int u = 0; u + 1 < kNB; ++u) issue_step<BITS, G, MB, D, PAD>(buf[u], S, O, pref(j0 + u * kStep), n, ds);
     }
 
     // B operand of QK^T: q of head n (zero for n >= GQA) in slot order.
@@ -882,7 +898,7 @@ __device__ __forceinline__ void partial_body(const AttendArgs& a, int spw, int s
         for (int t0 = j0; t0 < j1; t0 += kNB * kStep) {
 #pragma unroll
             for (int u = 0; u < kNB; ++u) {
-                issue_step<BITS, G, MB, D>(buf[(u + kNB - 1) % kNB], S, O, pref(t0 + (u + kNB - 1) * kStep), n, ds);
+                issue_step<BITS, G, MB, D, PAD>(buf[(u + kNB - 1) % kNB], S, O, pref(t0 + (u + kNB - 1) * kStep), n, ds);
                 store_step<BITS, G, MB, BF, D, PAD>(buf[u], sm, st, t0 + u * kStep, j1, c2, l, n, q, ds);
                 if (t0 + (u + 1) * kStep >= j1) goto store_done;
             }

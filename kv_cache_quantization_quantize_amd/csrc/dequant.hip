@@ -14,6 +14,16 @@
 
 namespace kivi {
 
+// Workgroups per CU a dequantize launch is held to by LDS it reserves and
+// never touches (160 KiB per CU on gfx950; 0: no cap).  Measured on the
+// full 32k cache, interleaved against full residency: 5 per CU ran the fp16
+// dequantizes 1-3% faster at 4 bits and 5-11% faster at 2 bits and at
+// head_dim 96; bfloat16 values gained 1-2% at 4 per CU and bfloat16 keys
+// lost 1-2% with any cap.  Before every row's loads were issued ahead of the
+// first store, a cap of 3 or 4 per CU had doubled the value dequantize's
+// time (one memory round trip per row, hidden only by many waves).
+template <bool KEYS, bool BF16> constexpr int kDequantPerCU = BF16 ? (KEYS ? 0 : 4) : 5;
+
 // Eight consecutive scale (or zero) entries as floats: binary32, or binary16
 // widened exactly.  p is 16-byte aligned (the ABI's slab stride and head_dim
 // rows keep it so).
@@ -60,27 +70,40 @@ __device__ __forceinline__ void dequant_tile(const uint32_t* __restrict__ cb, co
         load_meta8(scb + (t_first / G) * D + c * 8, gs);
         load_meta8(zeb + (t_first / G) * D + c * 8, gz);
     }
+    constexpr int kIters = 32 / kRPW;
+    // Every row's code word (and, for values, its group's scale and zero) is
+    // loaded before the first store, rows past n_rows re-reading the last
+    // one, so a tile costs one memory round trip rather than one per row.
+    uint32_t wv[kIters];
+    float vs[kIters], vz[kIters];
 #pragma unroll
-    for (int i = 0; i < 32 / kRPW; ++i) {
+    for (int i = 0; i < kIters; ++i) {
+        const int k = min(r + kRPW * i, n_rows - 1);
+        if constexpr (BITS == 4) wv[i] = ct[k * kWords + c];
+        else wv[i] = ct[k * kWords + (c >> 1)] >> (16 * (c & 1));
+        if constexpr (!KEYS) {
+            const int64_t t = t_first + k;
+            vs[i] = meta_value(scb[t * kMetaPerTok + c / (G / 8)]);
+            vz[i] = meta_value(zeb[t * kMetaPerTok + c / (G / 8)]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kIters; ++i) {
         const int k = r + kRPW * i;                    // output row
         if (!ONE_GROUP && k >= n_rows) continue;
-        uint32_t w;
-        if constexpr (BITS == 4) w = ct[k * kWords + c];
-        else w = ct[k * kWords + (c >> 1)] >> (16 * (c & 1));
+        const uint32_t w = wv[i];
         float sc[8], ze[8];
         if constexpr (ONE_GROUP) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) { sc[j] = gs[j]; ze[j] = gz[j]; }
         } else if constexpr (KEYS) {
+            // a tile that straddles key groups (an unaligned window)
             const int64_t t = t_first + k;
             load_meta8(scb + (t / G) * D + c * 8, sc);
             load_meta8(zeb + (t / G) * D + c * 8, ze);
         } else {
-            const int64_t t = t_first + k;
-            const float s = meta_value(scb[t * kMetaPerTok + c / (G / 8)]);
-            const float z = meta_value(zeb[t * kMetaPerTok + c / (G / 8)]);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) { sc[j] = s; ze[j] = z; }
+            for (int j = 0; j < 8; ++j) { sc[j] = vs[i]; ze[j] = vz[i]; }
         }
         uint32_t h[8];
 #pragma unroll
@@ -119,8 +142,10 @@ static hipError_t launch_t(const DequantArgs& a, hipStream_t stream) {
     const int64_t tiles_per_bh = (a.n + 31) / 32;
     const int64_t n_tiles = a.BH * tiles_per_bh;
     const int64_t blocks = (n_tiles + kWavesPerBlock - 1) / kWavesPerBlock;
+    constexpr int kPerCU = kDequantPerCU<KEYS, BF16>;
+    const size_t lds = kPerCU > 0 ? (size_t{160} * 1024 / kPerCU) / 1024 * 1024 : 0;
     hipLaunchKernelGGL((dequant_kernel<BITS, KEYS, BF16, G, D, MT>), dim3(static_cast<uint32_t>(blocks)),
-                       dim3(kBlock), 0, stream, a.codes, a.codes_bh_stride,
+                       dim3(kBlock), lds, stream, a.codes, a.codes_bh_stride,
                        static_cast<const MT*>(a.scale), static_cast<const MT*>(a.zero),
                        a.meta_bh_stride, a.t0, a.n, a.out, a.out_bh_stride, tiles_per_bh, n_tiles);
     return hipGetLastError();
