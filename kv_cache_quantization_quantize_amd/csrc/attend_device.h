@@ -229,6 +229,9 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 // every one of them below 2^32 (a start of 2^25 wrapped to the slab's first
 // rows there).
 constexpr uint32_t kFarToken = 3u << 23;
+static_assert(kFarToken > (1u << 24), "a far step must start past every extent (n_quant < 2^24)");
+static_assert(uint64_t{kFarToken} * 128 + (1u << 13) < (uint64_t{1} << 32),
+              "far offsets of 128-byte code rows plus lane offsets must not wrap");
 
 struct StoreView {
     rsrc_t kc, ks, kz;      // key codes, scale, zero
@@ -253,6 +256,8 @@ struct LaneOffsets {
 // load there returns zeros without a memory access.  Instruction offsets of
 // at most 16 keep it below 2^32.
 constexpr uint32_t kDeadOffset = 0xFFFFFF00u;
+static_assert(uint64_t{kDeadOffset} + 32 < (uint64_t{1} << 32) && kDeadOffset > (1u << 31),
+              "dead loads must stay past every extent without wrapping");
 
 // Channel geometry for head_dim D (64, 128 or 256).  QK^T: lane group q
 // holds channels kCPG*q + 8*kb + slot of key unit kb < kKB.  PV: MFMA i < kPV

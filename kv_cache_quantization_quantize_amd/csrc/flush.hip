@@ -431,8 +431,14 @@ __global__ __launch_bounds__(kBlock) void value_flush_kernel(
 // suit the memory system.  bfloat16 input, head_dim 64 and the
 // reconstructing flushes ran 1-7% slower with a cap, and the other value
 // configurations 2-5% slower, so they keep the full residency.
+// At head_dim 256 (16 KiB of input per wave) 3 per CU ran the key flush 3%
+// and the value flush 2% faster than the 4 its registers allow; the head_dims
+// with idle lanes at the end of each row ran 5-90% slower with a cap of 3
+// or 4 and keep the full residency.
 template <bool KEYS, bool RECON, bool BF16, int G, int D, typename MT>
-constexpr int kFlushPerCU = (BF16 || RECON || D != 128) ? 0
+constexpr int kFlushPerCU = (BF16 || RECON) ? 0
+                            : D == 256 ? 3
+                            : D != 128 ? 0
                             : KEYS ? 5 : (kGatherMeta<G, D, MT> ? 4 : 0);
 
 // The dynamic LDS bytes that hold a launch to per_cu workgroups per CU, on
