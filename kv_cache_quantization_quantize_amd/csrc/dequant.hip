@@ -158,8 +158,8 @@ static hipError_t launch_g(const DequantArgs& a, hipStream_t stream) {
     return keys ? launch_t<2, true, BF16, G, D, MT>(a, stream) : launch_t<2, false, BF16, G, D, MT>(a, stream);
 }
 
-// head_dim 128 with groups of 32, 64 or 128; head_dim 64 and 256 with groups
-// of 32.  Binary16 metadata: fp16 output at head_dim 128.
+// head_dim 128 with groups of 32, 64 or 128; every other multiple of 16 up
+// to 256 with groups of 32.  Binary16 metadata: fp16 output at head_dim 128.
 template <bool BF16>
 static hipError_t launch_fmt(const DequantArgs& a, hipStream_t stream) {
     switch (a.head_dim) {

@@ -511,9 +511,9 @@ static hipError_t launch_flush_g(const FlushArgs& a, hipStream_t stream) {
     }
 }
 
-// head_dim 128 with groups of 32, 64 or 128; head_dim 64 and 256 with groups
-// of 32 (the ABI admits no other pair).  Binary16 metadata: fp16 input at
-// head_dim 128.
+// head_dim 128 with groups of 32, 64 or 128; every other multiple of 16 up
+// to 256 with groups of 32 (the ABI admits no other pair).  Binary16
+// metadata: fp16 input at head_dim 128.
 template <bool KEYS, bool BF16>
 static hipError_t launch_flush_fmt(const FlushArgs& a, hipStream_t stream) {
     switch (a.head_dim) {
