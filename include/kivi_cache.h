@@ -135,6 +135,19 @@ int kivi_cache_attend(const kivi_cache* cache, int32_t layer, const uint16_t* q,
                       float softmax_scale, float* out, void* workspace, size_t workspace_bytes,
                       hipStream_t stream);
 
+/* Step, fused: kivi_cache_append then kivi_cache_attend of layer `layer` in
+ * one kernel launch pair instead of three launches.  The attend reads this
+ * step's token from k_new / v_new directly, and the wave that holds it also
+ * writes it into the layer's rings, so the cache afterwards is as if both
+ * calls had run; out is bit-identical to theirs.  Arguments, workspace and
+ * errors as the two calls (the layer must not have appended this step;
+ * nothing is launched and the layer stays un-appended on error).  k_new and
+ * v_new are read during the launch only. */
+int kivi_cache_append_attend(kivi_cache* cache, int32_t layer, const uint16_t* k_new,
+                             const uint16_t* v_new, const uint16_t* q, int32_t Hq,
+                             float softmax_scale, float* out, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
 /* Workspace bytes that serve kivi_cache_attend at every length the cache can
  * reach (so one allocation, or one captured graph, covers the whole loop). */
 size_t kivi_cache_attend_workspace_bytes(const kivi_cache* cache, int32_t Hq);

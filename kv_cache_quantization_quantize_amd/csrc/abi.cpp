@@ -211,7 +211,8 @@ int decode_attend_entry(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
                         int64_t n_res, int64_t res_head, int64_t res_ring,
                         const int32_t* seq_n_quant, const int32_t* seq_n_res,
                         float softmax_scale, float* out, void* workspace, size_t workspace_bytes,
-                        hipStream_t stream, bool bf16, bool static_scratch) {
+                        hipStream_t stream, bool bf16, bool static_scratch,
+                        const uint16_t* k_new, const uint16_t* v_new, int64_t new_row) {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || n_quant < 0 || n_res < 0) return KIVI_ERR_SHAPE;
     if (Hq % Hkv != 0) return KIVI_ERR_SHAPE;
     const int group = Hq / Hkv;
@@ -240,6 +241,16 @@ int decode_attend_entry(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
         const int64_t rows = res_ring > 0 ? res_ring : n_res;
         if ((rc = check_f16_tensor(k_res, slabs, rows, res_bh_stride, D)) != KIVI_OK) return rc;
         if ((rc = check_f16_tensor(v_res, slabs, rows, res_bh_stride, D)) != KIVI_OK) return rc;
+    }
+    if (k_new || v_new) {
+        // a fused append: token n_res - 1 comes from row s of k_new / v_new and
+        // is written to ring row new_row, which must not hold one of the
+        // other n_res - 1 tokens (uniform batches, a ring window only)
+        if (!k_new || !v_new) return KIVI_ERR_NULL;
+        if (seq_n_quant || seq_n_res || res_ring == 0 || n_res < 1) return KIVI_ERR_SHAPE;
+        if (new_row != (res_head + n_res - 1) % res_ring) return KIVI_ERR_SHAPE;
+        if ((rc = check_f16_tensor(k_new, slabs, 1, D, D)) != KIVI_OK) return rc;
+        if ((rc = check_f16_tensor(v_new, slabs, 1, D, D)) != KIVI_OK) return rc;
     }
     const kivi::AttendPlan plan = kivi::plan_attend(B, Hq, Hkv, n_quant, n_res, seq_n_quant != nullptr, D, bf16);
     if (plan.n_split > kMaxBlocks || slabs > kMaxAttendSlabs || B * Hq > kMaxBlocks) return KIVI_ERR_SHAPE;
@@ -272,6 +283,9 @@ int decode_attend_entry(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
     a.meta16 = meta16(k);
     a.bf16 = bf16;
     a.head_dim = D;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.new_row = static_cast<int32_t>(new_row);
     return finish(kivi::launch_decode_attend(a, plan, stream));
 }
 

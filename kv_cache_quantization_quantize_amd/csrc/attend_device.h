@@ -686,19 +686,23 @@ __device__ __forceinline__ int ring_row(int tok, int head, int ring) {
 // Rows have ds channels (PAD: ds < D); channels at or past ds are not
 // loaded and read as 0 (ds is a multiple of 16, so every 8- or 4-channel
 // load is wholly inside a row or wholly past it).
+// Token new_tok (a fused append; -1 if none) is read from the rows knew /
+// vnew instead of the window.
 template <int BITS, bool BF, int D, bool PAD>
 __device__ __forceinline__ void residual_step(const uint16_t* kr, const uint16_t* vr, const Smem<D>& sm,
                                               SoftState<Geo<D>::kPV>& st, int t0, int n_res, float c2,
-                                              int l, int n, int q, int head, int ring, int ds) {
+                                              int l, int n, int q, int head, int ring, int ds,
+                                              int new_tok, const uint16_t* knew, const uint16_t* vnew) {
     constexpr int kCPG = Geo<D>::kCPG, kKB = Geo<D>::kKB, kPV = Geo<D>::kPV;
     const int last = n_res - 1;
+    const auto krow = [&](int tok) { return tok == new_tok ? knew : kr + ring_row(tok, head, ring) * ds; };
+    const auto vrow = [&](int tok) { return tok == new_tok ? vnew : vr + ring_row(tok, head, ring) * ds; };
     // Every row of the step is loaded up front (K rows of both 16-token
     // blocks and the V rows), so a residual step costs one memory round trip.
     uint32_t rn[2][kCPG / 2];                   // the lane group's key channels, natural order
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-        const int tok = ring_row(min(t0 + 16 * blk + n, last), head, ring);
-        const uint4* src = reinterpret_cast<const uint4*>(kr + tok * ds + kCPG * q);
+        const uint4* src = reinterpret_cast<const uint4*>(krow(min(t0 + 16 * blk + n, last)) + kCPG * q);
 #pragma unroll
         for (int v = 0; v < kCPG / 8; ++v) {
             const uint4 t = (!PAD || kCPG * q + 8 * v < ds) ? src[v] : make_uint4(0u, 0u, 0u, 0u);
@@ -709,8 +713,7 @@ __device__ __forceinline__ void residual_step(const uint16_t* kr, const uint16_t
     uint32_t vw[8][kPV / 2];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-        const int tok = ring_row(min(t0 + pv_token(q, s), last), head, ring);
-        const uint16_t* p = vr + tok * ds + kPV * n;
+        const uint16_t* p = vrow(min(t0 + pv_token(q, s), last)) + kPV * n;
         if constexpr (kPV >= 8) {
 #pragma unroll
             for (int v = 0; v < kPV / 8; ++v) {
@@ -913,8 +916,26 @@ __device__ __forceinline__ void partial_body(const AttendArgs& a, int spw, int s
     if (r0 < r1) {
         const uint16_t* kr = a.k_res + bkv * a.res_bh_stride;
         const uint16_t* vr = a.v_res + bkv * a.res_bh_stride;
+        // a fused append's token: the last of the window (uniform batches only)
+        const int new_tok = a.k_new ? nr - 1 : -1;
+        const uint16_t* knew = a.k_new ? a.k_new + bkv * ds : kr;
+        const uint16_t* vnew = a.k_new ? a.v_new + bkv * ds : vr;
         for (int t0 = r0; t0 < r1; t0 += kStep)
-            residual_step<BITS, BF, D, PAD>(kr, vr, sm, st, t0, r1, c2, l, n, q, a.res_head, a.res_ring, ds);
+            residual_step<BITS, BF, D, PAD>(kr, vr, sm, st, t0, r1, c2, l, n, q, a.res_head, a.res_ring, ds,
+                                            new_tok, knew, vnew);
+        if (a.k_new && r1 == nr) {
+            // this wave holds the new token: it writes the token's K and V
+            // rows into the window's row new_row (ds / 8 lanes of 16 bytes
+            // each), which no other wave of this launch reads
+            const int chunks = ds / 8;
+            if (l < 2 * chunks) {
+                const bool val = l >= chunks;
+                const int c = val ? l - chunks : l;
+                const uint4 row = *reinterpret_cast<const uint4*>((val ? vnew : knew) + c * 8);
+                uint16_t* dst = const_cast<uint16_t*>(val ? vr : kr) + a.new_row * ds + c * 8;
+                *reinterpret_cast<uint4*>(dst) = row;
+            }
+        }
     }
 
     // ---- partial (m, l, o) of head n: lane (q, n) holds channels

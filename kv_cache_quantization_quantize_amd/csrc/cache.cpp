@@ -262,6 +262,32 @@ int kivi_cache_attend(const kivi_cache* cache, int32_t layer, const uint16_t* q,
                                      workspace_bytes, stream, cache->cfg.bf16 != 0);
 }
 
+int kivi_cache_append_attend(kivi_cache* cache, int32_t layer, const uint16_t* k_new,
+                             const uint16_t* v_new, const uint16_t* q, int32_t Hq,
+                             float softmax_scale, float* out, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+    if (!cache) return KIVI_ERR_NULL;
+    if (!valid(&cache->cfg)) return KIVI_ERR_UNSUPPORTED;
+    const int64_t kD = cache->cfg.head_dim;
+    if (layer < 0 || layer >= cache->cfg.layers || appended(cache, layer)) return KIVI_ERR_SHAPE;
+    if (cache->n_res >= cache->ring) return KIVI_ERR_SHAPE;        // no free ring row
+    if (!k_new || !v_new) return KIVI_ERR_NULL;
+    const int64_t slab0 = layer * seq_slabs(cache);
+    const kivi_store ks = layer_store(cache->k_store, slab0);
+    const kivi_store vs = layer_store(cache->v_store, slab0);
+    const int64_t rs = cache->ring * kD;
+    const int64_t row = (cache->head + cache->n_res) % cache->ring;
+    const int rc = kivi::decode_attend_entry(q, cache->cfg.batch, Hq, cache->cfg.kv_heads, &ks, &vs,
+                                             cache->n_quant, cache->k_ring + slab0 * rs,
+                                             cache->v_ring + slab0 * rs, rs, cache->n_res + 1, cache->head,
+                                             cache->ring, nullptr, nullptr, softmax_scale, out, workspace,
+                                             workspace_bytes, stream, cache->cfg.bf16 != 0, false,
+                                             k_new, v_new, row);
+    if (rc != KIVI_OK) return rc;
+    cache->appended[layer >> 6] |= uint64_t{1} << (layer & 63);
+    return KIVI_OK;
+}
+
 size_t kivi_cache_attend_workspace_bytes(const kivi_cache* cache, int32_t Hq) {
     if (!cache || !valid(&cache->cfg) || Hq <= 0) return 0;
     // An attend plan depends on the token counts only through the number of

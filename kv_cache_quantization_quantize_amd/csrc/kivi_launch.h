@@ -80,6 +80,15 @@ struct AttendArgs {
     bool bf16;                     // q, residual and the reconstruction in bfloat16
     int head_dim;                  // 128; others with groups of 32 and binary32 scale/zero
                                    // (q, residual, out and the partials have head_dim channels)
+    // Fused append (the decode-loop cache): residual token n_res - 1 of slab s
+    // is read from row s of k_new / v_new (head_dim elements each) instead of
+    // from the residual window, and the wave that holds that token writes
+    // both rows into row new_row of the slab's window (k_res / v_res, which
+    // are then the cache's own rings).  No other wave of the launch reads
+    // that row.  k_new null: no fused append.
+    const uint16_t* k_new = nullptr;
+    const uint16_t* v_new = nullptr;
+    int32_t new_row = 0;
 };
 
 // Three waves per SIMD for the attend at head_dim 64 and 128, fp16 and
@@ -150,7 +159,9 @@ int decode_attend_entry(const uint16_t* q, int64_t B, int32_t Hq, int32_t Hkv,
                         int64_t n_res, int64_t res_head, int64_t res_ring,
                         const int32_t* seq_n_quant, const int32_t* seq_n_res,
                         float softmax_scale, float* out, void* workspace, size_t workspace_bytes,
-                        hipStream_t stream, bool bf16 = false, bool static_scratch = false);
+                        hipStream_t stream, bool bf16 = false, bool static_scratch = false,
+                        const uint16_t* k_new = nullptr, const uint16_t* v_new = nullptr,
+                        int64_t new_row = 0);
 
 // The library-owned attend workspace (noalloc.hip): its size, and its device
 // address on the current device (resolved on the first call per device).

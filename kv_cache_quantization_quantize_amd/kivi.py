@@ -35,6 +35,7 @@ EXPORTS = (
     "kivi_calib_write", "kivi_calib_mix",
     "kivi_cache_device_bytes", "kivi_cache_init", "kivi_cache_prefill", "kivi_cache_append",
     "kivi_cache_attend", "kivi_cache_attend_workspace_bytes", "kivi_cache_end_step",
+    "kivi_cache_append_attend",
 )
 CACHE_MAX_LAYERS = 256
 
@@ -126,6 +127,8 @@ def lib() -> ctypes.CDLL:
         L.kivi_cache_prefill.argtypes = [cp, vp, vp, i64, i64, vp]
         L.kivi_cache_append.argtypes = [cp, i32, vp, vp, vp]
         L.kivi_cache_attend.argtypes = [cp, i32, vp, i32, ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
+        L.kivi_cache_append_attend.argtypes = [cp, i32, vp, vp, vp, i32, ctypes.c_float, vp, vp,
+                                               ctypes.c_size_t, vp]
         L.kivi_cache_attend_workspace_bytes.argtypes = [cp, i32]
         L.kivi_cache_attend_workspace_bytes.restype = ctypes.c_size_t
         L.kivi_cache_end_step.argtypes = [cp, vp]
@@ -135,7 +138,7 @@ def lib() -> ctypes.CDLL:
                      "kivi_decode_attend_bf16", "kivi_decode_attend_varlen_bf16",
                      "kivi_decode_attend_noalloc", "kivi_calib_copy", "kivi_calib_read", "kivi_calib_write", "kivi_calib_mix",
                      "kivi_cache_init", "kivi_cache_prefill", "kivi_cache_append",
-                     "kivi_cache_attend", "kivi_cache_end_step"):
+                     "kivi_cache_attend", "kivi_cache_end_step", "kivi_cache_append_attend"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -546,6 +549,35 @@ class Cache:
                                        out.data_ptr(), workspace.data_ptr(),
                                        workspace.numel() * workspace.element_size(), _stream(stream)),
                "kivi_cache_attend")
+        return out
+
+    def append_attend(self, layer: int, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                      out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                      softmax_scale: float | None = None, stream=None) -> torch.Tensor:
+        """kivi_cache_append_attend: append then attend in one launch pair
+        (the same cache state and a bit-identical out)."""
+        for t, name in ((k_new, "k_new"), (v_new, "v_new")):
+            self._need_dtype(t, name)
+            if not t.is_cuda or not t.is_contiguous() or \
+                    t.numel() != self.cfg.batch * self.cfg.kv_heads * self.head_dim:
+                raise ValueError(f"{name} must be a contiguous device tensor [batch*kv_heads][head_dim]")
+        if q.dim() != 3 or q.shape[0] != self.cfg.batch or q.shape[2] != self.head_dim:
+            raise ValueError(f"q must be [{self.cfg.batch}][Hq][{self.head_dim}] for this cache, "
+                             f"got {tuple(q.shape)}")
+        _need_query(q)
+        self._need_dtype(q, "q")
+        B, Hq, D = q.shape
+        if softmax_scale is None:
+            softmax_scale = 1.0 / math.sqrt(D)
+        if out is None:
+            out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+        _need_out(out, B, Hq, D)
+        if workspace is None:
+            workspace = attend_workspace(self.attend_workspace_bytes(Hq), q.device)
+        _check(lib().kivi_cache_append_attend(ctypes.byref(self.c), layer, k_new.data_ptr(), v_new.data_ptr(),
+                                              q.data_ptr(), Hq, float(softmax_scale), out.data_ptr(),
+                                              workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                              _stream(stream)), "kivi_cache_append_attend")
         return out
 
     def end_step(self, stream=None) -> int:

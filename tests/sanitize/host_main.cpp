@@ -340,8 +340,13 @@ void on_attend(const kivi::AttendArgs& a) {
         const int64_t slab = g_loop.layer * per + s;
         for (int64_t i = 0; i < a.n_res; ++i) {
             const int64_t row = (a.res_head + i) % a.res_ring;
-            CHECK(is_label(a.k_res + s * a.res_bh_stride + row * D, slab, c->n_quant + i, 0, D));
-            CHECK(is_label(a.v_res + s * a.res_bh_stride + row * D, slab, c->n_quant + i, 1, D));
+            // a fused append's token is read from the new rows, not yet the ring
+            const bool fresh = a.k_new && i == a.n_res - 1;
+            CHECK(is_label(fresh ? a.k_new + s * D : a.k_res + s * a.res_bh_stride + row * D, slab,
+                           c->n_quant + i, 0, D));
+            CHECK(is_label(fresh ? a.v_new + s * D : a.v_res + s * a.res_bh_stride + row * D, slab,
+                           c->n_quant + i, 1, D));
+            if (fresh) CHECK(row == a.new_row);
         }
     }
     ++g_loop.attends;
@@ -416,10 +421,21 @@ void run_cache(const kivi_cache_config& cfg, const std::vector<int64_t>& schedul
                         label(vn + s * D, l * per + s, c.length, 1, D);
                     }
                     CHECK(kivi_cache_attend(&c, l, q, Hq, 0.1f, out, ws, wsb, nullptr) == KIVI_ERR_SHAPE);
-                    CHECK(kivi_cache_append(&c, l, kn, vn, nullptr) == KIVI_OK);
-                    CHECK(kivi_cache_append(&c, l, kn, vn, nullptr) == KIVI_ERR_SHAPE);
                     g_loop.layer = l;
-                    CHECK(kivi_cache_attend(&c, l, q, Hq, 0.1f, out, ws, wsb, nullptr) == KIVI_OK);
+                    if (l % 2 == 0) {
+                        CHECK(kivi_cache_append(&c, l, kn, vn, nullptr) == KIVI_OK);
+                        CHECK(kivi_cache_append(&c, l, kn, vn, nullptr) == KIVI_ERR_SHAPE);
+                        CHECK(kivi_cache_append_attend(&c, l, kn, vn, q, Hq, 0.1f, out, ws, wsb, nullptr) ==
+                              KIVI_ERR_SHAPE);
+                        CHECK(kivi_cache_attend(&c, l, q, Hq, 0.1f, out, ws, wsb, nullptr) == KIVI_OK);
+                    } else {
+                        // the fused call: a too-small workspace leaves the layer un-appended
+                        CHECK(kivi_cache_append_attend(&c, l, kn, vn, q, Hq, 0.1f, out, ws, 16, nullptr) ==
+                              KIVI_ERR_WORKSPACE);
+                        CHECK(kivi_cache_append_attend(&c, l, kn, vn, q, Hq, 0.1f, out, ws, wsb, nullptr) ==
+                              KIVI_OK);
+                        CHECK(kivi_cache_append(&c, l, kn, vn, nullptr) == KIVI_ERR_SHAPE);
+                    }
                     if (l + 1 < cfg.layers) CHECK(kivi_cache_end_step(&c, nullptr) == KIVI_ERR_SHAPE);
                 }
                 const int64_t q0 = c.n_quant;

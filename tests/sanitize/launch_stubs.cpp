@@ -117,6 +117,16 @@ hipError_t launch_decode_attend(const AttendArgs& a, const AttendPlan& p, hipStr
             touch(a.k_res + s * a.res_bh_stride + row * D, D * 2);
             touch(a.v_res + s * a.res_bh_stride + row * D, D * 2);
         }
+        if (a.k_new) {
+            // a fused append: the new rows are read and copied into ring row
+            // new_row, as the kernel does
+            touch(a.k_new + s * D, D * 2);
+            touch(a.v_new + s * D, D * 2);
+            uint16_t* kd = const_cast<uint16_t*>(a.k_res) + s * a.res_bh_stride + int64_t{a.new_row} * D;
+            uint16_t* vd = const_cast<uint16_t*>(a.v_res) + s * a.res_bh_stride + int64_t{a.new_row} * D;
+            std::memcpy(kd, a.k_new + s * D, static_cast<size_t>(D) * 2);
+            std::memcpy(vd, a.v_new + s * D, static_cast<size_t>(D) * 2);
+        }
     }
     return hipSuccess;
 }
