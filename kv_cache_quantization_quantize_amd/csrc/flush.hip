@@ -257,10 +257,11 @@ __device__ __forceinline__ void meta_row_out(const void* src, void* dst) {
 // Value rows.  A value group of 32 channels is one DPP quad and no exchange
 // crosses token rows, so a row needs whole quads, not a power-of-two lane
 // count: head_dims 80 and 96 can take rows of 12 lanes (5 tokens a wave
-// instead of 4), 144 and 160 rows of 20 (3 instead of 2).  Measured on 1.2e9
-// elements against RowGeo's rows: 144 19%, 160 14% and 80 12% faster, 96 11%
-// faster for bfloat16 caches but 5% slower for fp16 ones, which keep
-// RowGeo's 16-lane rows; the other head_dims gain no rows.
+// instead of 4), 144 and 160 rows of 20 (3 instead of 2).  Measured against
+// RowGeo's rows: 144 19-20% and 160 14% faster; 80 12% faster over 256
+// slabs of 32768 tokens and level over 460; 96 11% faster for bfloat16
+// caches but 5% slower for fp16 ones, which keep RowGeo's 16-lane rows; the
+// other head_dims gain no rows.
 template <int D, bool BF16> struct ValueRowGeo {
     static constexpr int kChunks = D / 8;
     static constexpr int kQuadLanes = (kChunks + 3) / 4 * 4;
