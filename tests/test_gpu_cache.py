@@ -196,26 +196,29 @@ def test_full_store_is_reported_and_leaves_state_unchanged():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("Dh,variant", [(128, "f32"), (128, "f16"), (96, "bf16"), (64, "f32")])
-def test_fused_append_attend_matches_the_two_calls(Dh, variant):
+@pytest.mark.parametrize("Dh,variant,S0", [(128, "f32", 70), (128, "f16", 70), (96, "bf16", 70), (64, "f32", 70),
+                                           (128, "f32", 0)])
+def test_fused_append_attend_matches_the_two_calls(Dh, variant, S0):
     """kivi_cache_append_attend against kivi_cache_append + kivi_cache_attend
-    on two caches fed the same prompt and tokens, through ring wraps and
-    cross-layer flushes: every step's output bit-identical, and at the end
-    the two device buffers (both zeroed before use) byte-identical, so the
-    fused call wrote each token into its ring row exactly as the append."""
-    layers, batch, kvh, Hq, bits, R, F, cap, S0, steps = 3, 2, 2, 8, 4, 64, 32, 256, 70, 75
+    on two caches fed the same prompt (or none: the first step attends over
+    its own token only) and tokens, through ring wraps and cross-layer
+    flushes: every step's output bit-identical, and at the end the two device
+    buffers (both zeroed before use) byte-identical, so the fused call wrote
+    each token into its ring row exactly as the append."""
+    layers, batch, kvh, Hq, bits, R, F, cap, steps = 3, 2, 2, 8, 4, 64, 32, 256, 75
     bf16 = variant == "bf16"
     meta = "f32" if bf16 else variant
     dtype = torch.bfloat16 if bf16 else torch.float16
     slabs, per = layers * batch * kvh, batch * kvh
-    note(f"fused append+attend D={Dh} {variant} layers={layers} R={R} F={F} steps={steps}")
+    note(f"fused append+attend D={Dh} {variant} prompt={S0} layers={layers} R={R} F={F} steps={steps}")
     two = [kivi.Cache(layers, batch, kvh, cap, bits, R, F, meta=meta, dtype=dtype, head_dim=Dh) for _ in range(2)]
     for c in two:
         c.buffer.zero_()
-    k0 = synth.kv_tensor(slabs, S0, Dh, keys=True, seed=9900 + Dh, device="cuda", dtype=dtype)
-    v0 = synth.kv_tensor(slabs, S0, Dh, keys=False, seed=9900 + Dh, device="cuda", dtype=dtype)
-    for c in two:
-        c.prefill(k0, v0)
+    k0 = synth.kv_tensor(slabs, max(S0, 1), Dh, keys=True, seed=9900 + Dh, device="cuda", dtype=dtype)[:, :S0]
+    v0 = synth.kv_tensor(slabs, max(S0, 1), Dh, keys=False, seed=9900 + Dh, device="cuda", dtype=dtype)[:, :S0]
+    if S0:
+        for c in two:
+            c.prefill(k0, v0)
     ws = [kivi.attend_workspace(c.attend_workspace_bytes(Hq)) for c in two]
     for step in range(steps):
         kn = synth.kv_tensor(slabs, 1, Dh, keys=True, seed=9950 + step, device="cuda", dtype=dtype)[:, 0].contiguous()
@@ -232,7 +235,7 @@ def test_fused_append_attend_matches_the_two_calls(Dh, variant):
         assert launches[0] == launches[1]
         assert (two[0].length, two[0].n_quant) == (two[1].length, two[1].n_quant)
     torch.cuda.synchronize()
-    assert two[0].n_quant > 0 and two[0].length == S0 + steps
+    assert two[0].length == S0 + steps and two[0].n_quant == (S0 + steps - R) // F * F
     assert torch.equal(two[0].buffer, two[1].buffer)
     # a second fused call on a layer that already appended this step is refused
     kn = torch.zeros((per, Dh), dtype=dtype, device="cuda")
