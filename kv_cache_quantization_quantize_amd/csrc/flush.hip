@@ -151,15 +151,34 @@ __device__ __forceinline__ void key_tile(const uint16_t* __restrict__ xt, uint32
     for (int i = 0; i < kRows; ++i) {
         const int row = r + kRPW * i;
         float t[8], qf[8];
-        float dev = 0.0f;
+        if constexpr (BF16) {
+            // bfloat16: each element whose quotient lies within 2^-16 of a tie
+            // is recomputed with the IEEE quotient (the proof at quant_fast is
+            // per element).  A wave runs such a branch only when one of its
+            // lanes needs it; bfloat16's coarser grid makes ties about 8 times
+            // likelier than fp16's (2e-3 of the elements of the synthetic
+            // cache), so a whole-row recompute ran in 65% of a wave's rows.
+            float dv[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            t[j] = sub_elem<BF16>(raw[i], j, one, ze[j]);
-            qf[j] = quant_fast(t[j], rc[j], dev);
-        }
-        if (dev > kNearTie || slow) {              // rare: within 2^-16 of a tie
+            for (int j = 0; j < 8; ++j) {
+                t[j] = sub_elem<BF16>(raw[i], j, one, ze[j]);
+                dv[j] = 0.0f;
+                qf[j] = quant_fast(t[j], rc[j], dv[j]);
+            }
 #pragma unroll
-            for (int j = 0; j < 8; ++j) qf[j] = quant_exact(t[j], sc[j], static_cast<float>((1 << BITS) - 1));
+            for (int j = 0; j < 8; ++j)
+                if (dv[j] > kNearTie || slow) qf[j] = quant_exact(t[j], sc[j], static_cast<float>((1 << BITS) - 1));
+        } else {
+            float dev = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                t[j] = sub_elem<BF16>(raw[i], j, one, ze[j]);
+                qf[j] = quant_fast(t[j], rc[j], dev);
+            }
+            if (dev > kNearTie || slow) {          // rare: within 2^-16 of a tie
+#pragma unroll
+                for (int j = 0; j < 8; ++j) qf[j] = quant_exact(t[j], sc[j], static_cast<float>((1 << BITS) - 1));
+            }
         }
         uint32_t packed = static_cast<uint32_t>(qf[0]);
 #pragma unroll
@@ -357,15 +376,30 @@ __device__ __forceinline__ void value_tile(const uint16_t* __restrict__ xt, uint
         const float rc = recip_clamped(sc);
 
         float t[8], qf[8];
-        float dev = 0.0f;
+        if constexpr (BF16) {
+            // per element, as in key_tile
+            const bool slow = !fast_scale(sc);
+            float dv[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            t[k] = sub_elem<BF16>(raw[i], k, one, ze);
-            qf[k] = quant_fast(t[k], rc, dev);
-        }
-        if (dev > kNearTie || (BF16 && !fast_scale(sc)) || (MH && slow_scale16(sc, hi - lo))) {
+            for (int k = 0; k < 8; ++k) {
+                t[k] = sub_elem<BF16>(raw[i], k, one, ze);
+                dv[k] = 0.0f;
+                qf[k] = quant_fast(t[k], rc, dv[k]);
+            }
 #pragma unroll
-            for (int k = 0; k < 8; ++k) qf[k] = quant_exact(t[k], sc, static_cast<float>((1 << BITS) - 1));
+            for (int k = 0; k < 8; ++k)
+                if (dv[k] > kNearTie || slow) qf[k] = quant_exact(t[k], sc, static_cast<float>((1 << BITS) - 1));
+        } else {
+            float dev = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                t[k] = sub_elem<BF16>(raw[i], k, one, ze);
+                qf[k] = quant_fast(t[k], rc, dev);
+            }
+            if (dev > kNearTie || (MH && slow_scale16(sc, hi - lo))) {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) qf[k] = quant_exact(t[k], sc, static_cast<float>((1 << BITS) - 1));
+            }
         }
         uint32_t packed = static_cast<uint32_t>(qf[0]);
 #pragma unroll
