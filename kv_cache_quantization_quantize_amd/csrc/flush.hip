@@ -27,35 +27,61 @@ namespace kivi {
 // ---------------------------------------------------------------------------
 // Keys: group = (bh, token group g, channel d) over tokens [32g, min(32g+32, S))
 // ---------------------------------------------------------------------------
+// Key rows of fp16 caches.  Where head_dim/8 is not a power of two, a row of
+// exactly head_dim/8 lanes can fit more tokens in a wave than RowGeo's padded
+// rows; it is taken where that needs fewer passes over a group of 32 tokens
+// (head_dims 80, 96, 144 and 160: 6, 7, 11 and 11 passes instead of 8, 8, 16
+// and 16), and the rows' per-channel min/max then meet through the wave's LDS
+// instead of lane exchanges.  Measured on MI355X (4-bit fp16 keys, 32768
+// tokens, one flush): 80 -16%, 96 -3.5%, 144 -9%, 160 -3%; head_dim 48 (4
+// passes either way) took 4% longer and bfloat16 rows (min/max in fp32,
+// twice the exchange and 150-195 registers) 9% longer, so both keep RowGeo's
+// rows.  Groups of 32 only (the other group sizes are head_dim 128).
+template <int D, bool BF16> struct KeyRowGeo {
+    static constexpr int kChunks = D / 8;
+    static constexpr int kPackedRows = 64 / kChunks;
+    static constexpr bool kPack = !BF16 && (kChunks & (kChunks - 1)) != 0 &&
+                                  (32 + kPackedRows - 1) / kPackedRows < 32 / RowGeo<D>::kRowsPerWave;
+    static constexpr int kLanesPerRow = kPack ? kChunks : RowGeo<D>::kLanesPerRow;
+    static constexpr int kRowsPerWave = 64 / kLanesPerRow;
+};
+
 // One tile.  xt, ct, rt point at token s0 of the slab (input, codes, recon);
 // n_rows = min(32, S - s0) real rows.  RAGGED tiles clamp loads to the last
 // real row and guard stores; full tiles do neither.
 template <int BITS, bool RECON, bool RAGGED, bool BF16, int G, int D, typename MT>
 __device__ __forceinline__ void key_tile(const uint16_t* __restrict__ xt, uint32_t* __restrict__ ct,
                                          MT* __restrict__ sct, MT* __restrict__ zet,
-                                         uint16_t* __restrict__ rt, int n_rows, int lane, float one)
+                                         uint16_t* __restrict__ rt, int n_rows, int lane, float one,
+                                         uint4* __restrict__ xl)
 {
     constexpr bool MH = sizeof(MT) == 2;            // binary16 scale/zero
     constexpr int kWords = D * BITS / 32;          // code words per token row
-    constexpr int kLPR = RowGeo<D>::kLanesPerRow;
-    constexpr int kRPW = RowGeo<D>::kRowsPerWave;
+    constexpr bool kPack = KeyRowGeo<D, BF16>::kPack;
+    static_assert(G == 32 || !kPack, "packed key rows hold groups of 32 only");
+    constexpr int kLPR = KeyRowGeo<D, BF16>::kLanesPerRow;
+    constexpr int kRPW = KeyRowGeo<D, BF16>::kRowsPerWave;
     constexpr int kChunks = RowGeo<D>::kChunks;
     const int c = lane % kLPR;                     // channels 8c .. 8c+7
-    const int r = lane / kLPR;                     // token rows r, r + kRPW, ...
+    // lanes past the wave's last whole row (packed rows) take row 0's place
+    // and store nothing
+    const bool in_row = kLPR * kRPW == 64 || lane < kLPR * kRPW;
+    const int r = in_row ? lane / kLPR : 0;        // token rows r, r + kRPW, ...
     // lanes past a row's last chunk (head_dims that are not 64, 128 or 256)
     // re-read that chunk and store nothing; their min/max only meet each
     // other's
-    const bool has = kChunks == kLPR || c < kChunks;
+    const bool has = (kChunks == kLPR || c < kChunks) && in_row;
     const int cl = kChunks == kLPR ? c : (c < kChunks ? c : kChunks - 1);
 
-    // Load 8 token rows x 8 channels.  Rows past the end of a ragged last
+    // Load the lane's token rows x 8 channels.  Rows past the end of a ragged last
     // group re-read the last real token, which is the edge padding of
     // "Three ways to be off by one bit", item 3, and cannot move min or max.
-    constexpr int kRows = G / kRPW;                // token rows per lane: the tile is one group
+    constexpr int kRows = (G + kRPW - 1) / kRPW;   // token rows per lane: the tile is one group
     uint4 raw[kRows];
 #pragma unroll
     for (int i = 0; i < kRows; ++i) {
         int row = r + kRPW * i;
+        if constexpr (G % kRPW != 0) row = row < G ? row : G - 1;   // a last pass past the group
         if constexpr (RAGGED) row = row < n_rows ? row : n_rows - 1;
         raw[i] = load_stream(xt + row * D + cl * 8);
     }
@@ -65,6 +91,7 @@ __device__ __forceinline__ void key_tile(const uint16_t* __restrict__ xt, uint32
     // monotone), bfloat16 widened exactly to fp32 (no packed bfloat16 form).
     float mnf[8], mxf[8];
     if constexpr (!BF16) {
+        half2_t mnw[4], mxw[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             half2_t mn = as_h2(word_of(raw[0], k)), mx = mn;
@@ -80,10 +107,39 @@ __device__ __forceinline__ void key_tile(const uint16_t* __restrict__ xt, uint32
                     mx = hmax(mx, a);
                 }
             }
-            mn = cross_rows_min<D>(mn);
-            mx = cross_rows_max<D>(mx);
-            mnf[2 * k] = static_cast<float>(mn[0]); mnf[2 * k + 1] = static_cast<float>(mn[1]);
-            mxf[2 * k] = static_cast<float>(mx[0]); mxf[2 * k + 1] = static_cast<float>(mx[1]);
+            if constexpr (!kPack) {
+                mn = cross_rows_min<D>(mn);
+                mx = cross_rows_max<D>(mx);
+                mnf[2 * k] = static_cast<float>(mn[0]); mnf[2 * k + 1] = static_cast<float>(mn[1]);
+                mxf[2 * k] = static_cast<float>(mx[0]); mxf[2 * k + 1] = static_cast<float>(mx[1]);
+            }
+            mnw[k] = mn;
+            mxw[k] = mx;
+        }
+        if constexpr (kPack) {
+            // every lane posts its 8 channels' min and max in its own LDS
+            // slots; then each folds in the kRPW rows' slots of its chunk (a
+            // wave's LDS instructions run in order; the fences keep the
+            // compiler from moving them)
+            xl[2 * lane] = make_uint4(as_u32(mnw[0]), as_u32(mnw[1]), as_u32(mnw[2]), as_u32(mnw[3]));
+            xl[2 * lane + 1] = make_uint4(as_u32(mxw[0]), as_u32(mxw[1]), as_u32(mxw[2]), as_u32(mxw[3]));
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+#pragma unroll
+            for (int rr = 0; rr < kRPW; ++rr) {
+                const uint4 a = xl[2 * (rr * kLPR + c)], b = xl[2 * (rr * kLPR + c) + 1];
+                const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    mnw[k] = rr == 0 ? as_h2(av[k]) : hmin(mnw[k], as_h2(av[k]));
+                    mxw[k] = rr == 0 ? as_h2(bv[k]) : hmax(mxw[k], as_h2(bv[k]));
+                }
+            }
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                mnf[2 * k] = static_cast<float>(mnw[k][0]); mnf[2 * k + 1] = static_cast<float>(mnw[k][1]);
+                mxf[2 * k] = static_cast<float>(mxw[k][0]); mxf[2 * k + 1] = static_cast<float>(mxw[k][1]);
+            }
         }
     } else {
 #pragma unroll
@@ -183,7 +239,7 @@ __device__ __forceinline__ void key_tile(const uint16_t* __restrict__ xt, uint32
         uint32_t packed = static_cast<uint32_t>(qf[0]);
 #pragma unroll
         for (int j = 1; j < 8; ++j) packed |= static_cast<uint32_t>(qf[j]) << (BITS * j);
-        const bool live = (!RAGGED || row < n_rows) && has;
+        const bool live = (!RAGGED || row < n_rows) && has && (G % kRPW == 0 || row < G);
         if constexpr (BITS == 4) {
             // the lane's 8 channels are exactly one word
             if (live) store_stream(&ct[row * kWords + c], packed);
@@ -221,10 +277,17 @@ __global__ __launch_bounds__(kBlock) void key_flush_kernel(
     const int64_t moff = bh * meta_bh_stride + (dst_token / G + g) * D;
     uint16_t* rt = RECON ? recon + bh * recon_bh_stride + s0 * D : nullptr;
     const int64_t rows = S - s0;
+    uint4* xl = nullptr;
+    if constexpr (KeyRowGeo<D, BF16>::kPack) {
+        // the wave's min/max exchange of packed rows (static LDS only where
+        // rows are packed, so the capped head_dim-128 launches keep theirs)
+        __shared__ uint4 key_xchg[kWavesPerBlock][128];   // a lane's min and max: 2 slots
+        xl = key_xchg[threadIdx.x >> 6];
+    }
     if (rows >= G)
-        key_tile<BITS, RECON, false, BF16, G, D, MT>(xt, ct, scale + moff, zero + moff, rt, G, lane, one);
+        key_tile<BITS, RECON, false, BF16, G, D, MT>(xt, ct, scale + moff, zero + moff, rt, G, lane, one, xl);
     else
-        key_tile<BITS, RECON, true, BF16, G, D, MT>(xt, ct, scale + moff, zero + moff, rt, static_cast<int>(rows), lane, one);
+        key_tile<BITS, RECON, true, BF16, G, D, MT>(xt, ct, scale + moff, zero + moff, rt, static_cast<int>(rows), lane, one, xl);
 }
 
 // ---------------------------------------------------------------------------
