@@ -159,3 +159,46 @@ def test_decode_incremental_flush():
         res = pmap(one, range(0, BH, per_task))
         bad = [i * per_task for i, r in enumerate(res) if not all(r)]
         assert not bad, f"{name}: slabs from {bad[:5]} differ from the oracle"
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("kind", ["keys", "values"])
+@pytest.mark.parametrize("Dh", [80, 96, 144, 160])
+def test_other_head_dims_at_full_size(Dh, kind, fmt):
+    """The head_dims whose rows are packed (fp16 key rows of head_dim/8
+    lanes, value rows of whole DPP quads) at the element count of the full
+    cache: 288 * 128 / head_dim slabs of 32768 tokens in one launch, as the
+    benchmark's head_dim rows time them.  Six slabs (both ends and the
+    middle) are compared whole with the oracle: codes, scale, zero, and the
+    dequantize kernel's output."""
+    S, bits = 32768, 4
+    BH = LAYERS * HKV * D // Dh
+    k = kivi.KIVI_KEYS if kind == "keys" else kivi.KIVI_VALUES
+    okind = oracle.KEYS if kind == "keys" else oracle.VALUES
+    ofn = oracle.quantize_keys if kind == "keys" else oracle.quantize_values
+    dtype = torch.bfloat16 if fmt == "bf16" else torch.float16
+    note(f"full-size head_dim {Dh} {fmt} {kind}: generating {BH}x{S}x{Dh}")
+    x = synth.kv_tensor(BH, S, Dh, keys=(kind == "keys"), seed=1009, device="cuda", dtype=dtype)
+    st = kivi.Store(k, BH, S, bits, head_dim=Dh)
+    note(f"full-size head_dim {Dh} {fmt} {kind}: flush (one launch)")
+    (kivi.quantize_keys if kind == "keys" else kivi.quantize_values)(x, st, 0)
+    torch.cuda.synchronize()
+    sample = [0, 1, BH // 3, BH // 2, BH - 2, BH - 1]
+    idx = torch.tensor(sample, device="cuda")
+    sub = kivi.Store(k, len(sample), S, bits, head_dim=Dh, codes=st.codes[idx], scale=st.scale[idx],
+                     zero=st.zero[idx])
+    rec = u16(kivi.dequantize(sub, 0, S, dtype=dtype))
+    xh = u16(x[idx])
+    codes = sub.codes.cpu().numpy().view(np.uint32)
+    scale = sub.scale.cpu().numpy().view(np.uint32)
+    zero = sub.zero.cpu().numpy().view(np.uint32)
+    del x, st
+    note(f"full-size head_dim {Dh} {fmt} {kind}: oracle over slabs {sample}")
+
+    def one(i):
+        hs = oracle.Store(okind, 1, S, Dh, bits)
+        hrec = ofn(xh[i:i + 1], hs, 0, want_recon=True, fmt=fmt)
+        return (_first_diff(codes[i], hs.codes[0]), _first_diff(scale[i], hs.scale[0].view(np.uint32)),
+                _first_diff(zero[i], hs.zero[0].view(np.uint32)), _first_diff(rec[i], hrec[0]))
+    for bh, r in zip(sample, pmap(one, range(len(sample)))):
+        assert r == ("equal",) * 4, f"D={Dh} {fmt} {kind} slab {bh}: codes/scale/zero/dequantize {r}"
