@@ -27,20 +27,21 @@ namespace kivi {
 // ---------------------------------------------------------------------------
 // Keys: group = (bh, token group g, channel d) over tokens [32g, min(32g+32, S))
 // ---------------------------------------------------------------------------
-// Key rows of fp16 caches.  Where head_dim/8 is not a power of two, a row of
-// exactly head_dim/8 lanes can fit more tokens in a wave than RowGeo's padded
-// rows; it is taken where that needs fewer passes over a group of 32 tokens
+// Key rows.  Where head_dim/8 is not a power of two, a row of exactly
+// head_dim/8 lanes can fit more tokens in a wave than RowGeo's padded rows;
+// it is taken where that needs fewer passes over a group of 32 tokens
 // (head_dims 80, 96, 144 and 160: 6, 7, 11 and 11 passes instead of 8, 8, 16
 // and 16), and the rows' per-channel min/max then meet through the wave's LDS
-// instead of lane exchanges.  Measured on MI355X (4-bit fp16 keys, 32768
-// tokens, one flush): 80 -16%, 96 -3.5%, 144 -9%, 160 -3%; head_dim 48 (4
-// passes either way) took 4% longer and bfloat16 rows (min/max in fp32,
-// twice the exchange and 150-195 registers) 9% longer, so both keep RowGeo's
-// rows.  Groups of 32 only (the other group sizes are head_dim 128).
-template <int D, bool BF16> struct KeyRowGeo {
+// instead of lane exchanges.  Measured on MI355X (4-bit keys, 32768 tokens
+// per slab, one flush), fp16: 80 -16%, 96 -3.5%, 144 -9%, 160 -3%;
+// bfloat16: 80 -7%, 96 -2%, 144 and 160 -37% (its padded 32-lane rows held
+// only two tokens a wave).  Head_dim 48 (4 passes either way) took 4%
+// longer and keeps RowGeo's rows.  Groups of 32 only (the other group sizes
+// are head_dim 128).
+template <int D> struct KeyRowGeo {
     static constexpr int kChunks = D / 8;
     static constexpr int kPackedRows = 64 / kChunks;
-    static constexpr bool kPack = !BF16 && (kChunks & (kChunks - 1)) != 0 &&
+    static constexpr bool kPack = (kChunks & (kChunks - 1)) != 0 &&
                                   (32 + kPackedRows - 1) / kPackedRows < 32 / RowGeo<D>::kRowsPerWave;
     static constexpr int kLanesPerRow = kPack ? kChunks : RowGeo<D>::kLanesPerRow;
     static constexpr int kRowsPerWave = 64 / kLanesPerRow;
@@ -57,10 +58,10 @@ __device__ __forceinline__ void key_tile(const uint16_t* __restrict__ xt, uint32
 {
     constexpr bool MH = sizeof(MT) == 2;            // binary16 scale/zero
     constexpr int kWords = D * BITS / 32;          // code words per token row
-    constexpr bool kPack = KeyRowGeo<D, BF16>::kPack;
+    constexpr bool kPack = KeyRowGeo<D>::kPack;
     static_assert(G == 32 || !kPack, "packed key rows hold groups of 32 only");
-    constexpr int kLPR = KeyRowGeo<D, BF16>::kLanesPerRow;
-    constexpr int kRPW = KeyRowGeo<D, BF16>::kRowsPerWave;
+    constexpr int kLPR = KeyRowGeo<D>::kLanesPerRow;
+    constexpr int kRPW = KeyRowGeo<D>::kRowsPerWave;
     constexpr int kChunks = RowGeo<D>::kChunks;
     const int c = lane % kLPR;                     // channels 8c .. 8c+7
     // lanes past the wave's last whole row (packed rows) take row 0's place
@@ -161,8 +162,35 @@ __device__ __forceinline__ void key_tile(const uint16_t* __restrict__ xt, uint32
                     mx = fmaximum(mx, a);
                 }
             }
-            mnf[j] = cross_rows_min_f32<D>(mn);
-            mxf[j] = cross_rows_max_f32<D>(mx);
+            if constexpr (!kPack) {
+                mn = cross_rows_min_f32<D>(mn);
+                mx = cross_rows_max_f32<D>(mx);
+            }
+            mnf[j] = mn;
+            mxf[j] = mx;
+        }
+        if constexpr (kPack) {
+            // as for fp16: the min and max of bfloat16 elements are bfloat16
+            // values, so they travel as bfloat16 pairs, 2 slots a lane
+            const auto pair = [](float lo, float hi) {
+                return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+            };
+            xl[2 * lane] = make_uint4(pair(mnf[0], mnf[1]), pair(mnf[2], mnf[3]), pair(mnf[4], mnf[5]), pair(mnf[6], mnf[7]));
+            xl[2 * lane + 1] = make_uint4(pair(mxf[0], mxf[1]), pair(mxf[2], mxf[3]), pair(mxf[4], mxf[5]), pair(mxf[6], mxf[7]));
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+#pragma unroll
+            for (int rr = 0; rr < kRPW; ++rr) {
+                const uint4 a = xl[2 * (rr * kLPR + c)], b = xl[2 * (rr * kLPR + c) + 1];
+                const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float va = (j & 1) ? bf16_hi(av[j >> 1]) : bf16_lo(av[j >> 1]);
+                    const float vb = (j & 1) ? bf16_hi(bv[j >> 1]) : bf16_lo(bv[j >> 1]);
+                    mnf[j] = rr == 0 ? va : fminimum(mnf[j], va);
+                    mxf[j] = rr == 0 ? vb : fmaximum(mxf[j], vb);
+                }
+            }
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
         }
     }
 
@@ -278,7 +306,7 @@ __global__ __launch_bounds__(kBlock) void key_flush_kernel(
     uint16_t* rt = RECON ? recon + bh * recon_bh_stride + s0 * D : nullptr;
     const int64_t rows = S - s0;
     uint4* xl = nullptr;
-    if constexpr (KeyRowGeo<D, BF16>::kPack) {
+    if constexpr (KeyRowGeo<D>::kPack) {
         // the wave's min/max exchange of packed rows (static LDS only where
         // rows are packed, so the capped head_dim-128 launches keep theirs)
         __shared__ uint4 key_xchg[kWavesPerBlock][128];   // a lane's min and max: 2 slots
