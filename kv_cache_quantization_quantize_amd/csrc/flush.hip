@@ -286,7 +286,7 @@ __device__ __forceinline__ void key_tile(const uint16_t* __restrict__ xt, uint32
 }
 
 template <int BITS, bool RECON, bool BF16, int G, int D, typename MT>
-__global__ __launch_bounds__(kBlock) void key_flush_kernel(
+__device__ __forceinline__ void key_flush_body(
     const uint16_t* __restrict__ x, int64_t S, int64_t x_bh_stride,
     uint32_t* __restrict__ codes, int64_t codes_bh_stride,
     MT* __restrict__ scale, MT* __restrict__ zero, int64_t meta_bh_stride,
@@ -316,6 +316,38 @@ __global__ __launch_bounds__(kBlock) void key_flush_kernel(
         key_tile<BITS, RECON, false, BF16, G, D, MT>(xt, ct, scale + moff, zero + moff, rt, G, lane, one, xl);
     else
         key_tile<BITS, RECON, true, BF16, G, D, MT>(xt, ct, scale + moff, zero + moff, rt, static_cast<int>(rows), lane, one, xl);
+}
+
+template <int BITS, bool RECON, bool BF16, int G, int D, typename MT>
+__global__ __launch_bounds__(kBlock) void key_flush_kernel(
+    const uint16_t* __restrict__ x, int64_t S, int64_t x_bh_stride,
+    uint32_t* __restrict__ codes, int64_t codes_bh_stride,
+    MT* __restrict__ scale, MT* __restrict__ zero, int64_t meta_bh_stride,
+    int64_t dst_token, uint16_t* __restrict__ recon, int64_t recon_bh_stride,
+    int64_t n_groups, int64_t n_tiles, float one)
+{
+    key_flush_body<BITS, RECON, BF16, G, D, MT>(x, S, x_bh_stride, codes, codes_bh_stride, scale, zero, meta_bh_stride, dst_token, recon, recon_bh_stride, n_groups, n_tiles, one);
+}
+
+// bfloat16 keys with more than 8 token rows per lane held about 200
+// registers (2 waves per SIMD) at head_dims above 160 and about 150 (3) in
+// the packed rows of 144 and 160.  This entry caps the registers: 3 waves
+// for the 32-lane rows (a few spills), 4 for the packed rows.  Interleaved
+// A/B on MI355X, 4-bit bfloat16 keys, 32768 tokens per slab: 176, 192 and
+// 224 -23 to -25%, 256 -16%, 144 -13%, 160 -9%; a cap of 4 on the 32-lane
+// rows spilled 330-400 bytes a lane and doubled their time.
+template <int D> constexpr int kKeyWavesBF16 =
+    (32 + KeyRowGeo<D>::kRowsPerWave - 1) / KeyRowGeo<D>::kRowsPerWave <= 8 ? 0 : KeyRowGeo<D>::kPack ? 4 : 3;
+template <int BITS, bool RECON, bool BF16, int G, int D, typename MT>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kKeyWavesBF16<D>)))
+void key_flush_capped_kernel(
+    const uint16_t* __restrict__ x, int64_t S, int64_t x_bh_stride,
+    uint32_t* __restrict__ codes, int64_t codes_bh_stride,
+    MT* __restrict__ scale, MT* __restrict__ zero, int64_t meta_bh_stride,
+    int64_t dst_token, uint16_t* __restrict__ recon, int64_t recon_bh_stride,
+    int64_t n_groups, int64_t n_tiles, float one)
+{
+    key_flush_body<BITS, RECON, BF16, G, D, MT>(x, S, x_bh_stride, codes, codes_bh_stride, scale, zero, meta_bh_stride, dst_token, recon, recon_bh_stride, n_groups, n_tiles, one);
 }
 
 // ---------------------------------------------------------------------------
@@ -622,11 +654,18 @@ static hipError_t launch_keys_t(const FlushArgs& a, hipStream_t stream) {
     const int64_t n_tiles = a.BH * n_groups;
     const int64_t blocks = (n_tiles + kWavesPerBlock - 1) / kWavesPerBlock;
     const size_t lds = residency_lds(kFlushPerCU<true, RECON, BF16, G, D, MT>, 0);
-    hipLaunchKernelGGL((key_flush_kernel<BITS, RECON, BF16, G, D, MT>), dim3(static_cast<uint32_t>(blocks)),
-                       dim3(kBlock), lds, stream, a.x, a.S, a.x_bh_stride, a.codes,
-                       a.codes_bh_stride, static_cast<MT*>(a.scale), static_cast<MT*>(a.zero),
-                       a.meta_bh_stride, a.dst_token,
-                       a.recon, a.recon_bh_stride, n_groups, n_tiles, 1.0f);
+    if constexpr (BF16 && kKeyWavesBF16<D> > 0)
+        hipLaunchKernelGGL((key_flush_capped_kernel<BITS, RECON, BF16, G, D, MT>), dim3(static_cast<uint32_t>(blocks)),
+                           dim3(kBlock), lds, stream, a.x, a.S, a.x_bh_stride, a.codes,
+                           a.codes_bh_stride, static_cast<MT*>(a.scale), static_cast<MT*>(a.zero),
+                           a.meta_bh_stride, a.dst_token,
+                           a.recon, a.recon_bh_stride, n_groups, n_tiles, 1.0f);
+    else
+        hipLaunchKernelGGL((key_flush_kernel<BITS, RECON, BF16, G, D, MT>), dim3(static_cast<uint32_t>(blocks)),
+                           dim3(kBlock), lds, stream, a.x, a.S, a.x_bh_stride, a.codes,
+                           a.codes_bh_stride, static_cast<MT*>(a.scale), static_cast<MT*>(a.zero),
+                           a.meta_bh_stride, a.dst_token,
+                           a.recon, a.recon_bh_stride, n_groups, n_tiles, 1.0f);
     return hipGetLastError();
 }
 
